@@ -1,0 +1,243 @@
+"""The MoE feed-forward block in float64 -- plain, slow and direct.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Steps, in the order the pages give them:
+
+1. Router: one logit per expert, l[t, e] = sum_j x[t, j] * Wr[j, e] + b[e]
+   (superteams.ai "Llama 4", section "Mixture of Experts: Why Total and
+   Active Parameters Diverge", the routing sketch: "one logit per expert").
+   The bias b is optional (zero when absent); the pages name none, the
+   skewed workloads need one.
+2. Top-1: the expert with the largest logit, ties to the lowest index
+   (same sketch: argmax; KerasFormers "Llama 4", section "What is unusual
+   about the block": Scout routes 1 of 16, Maverick 1 of 128;
+   llm-architectures-explained "Llama 4 Maverick", table "Every
+   architecture field", ffns.moe.active = 1).
+3. Gate: g = sigmoid(l[t, e*]) of the selected logit, applied to the
+   token's input of the routed expert only (KerasFormers "Llama 4", "What is
+   unusual about the block": routed with a sigmoid gate on the scaled input).
+   No softmax, no renormalisation.  Because the expert's first layer is
+   linear, g * (x W) = (g x) W; the oracle uses the former.
+4. Routed expert e*: SwiGLU MLP, h = SiLU(u Wg) * (u Wu), y = h Wd, with
+   Wg / Wu the column halves [0, f) / [f, 2f) of W_gate_up[e*] and
+   SiLU(z) = z / (1 + exp(-z)) (llm-architectures-explained "Llama 4
+   Maverick", "Every architecture field": experts are gated MLPs of width
+   intermediate_size = 8192).
+5. Shared expert: the same SwiGLU form of width fs on every token, no gate
+   (same table: ffns.moe.shared = 1, d_shared = 8192; torchtune
+   llama4_decoder, Parameters: use_shared_expert).
+6. Combine: out = shared(x) + routed (superteams.ai routing sketch; the
+   other experts contribute nothing).
+
+Rounding points of the reduced-precision variants (the pages fix none; they
+follow the data types of the workloads):
+  R1 (bf16 weights): the SwiGLU output h is rounded to bf16 (RNE, from its
+     float32 value) before the down projection.
+  R0 (e4m3 weights): per token, s_x = fp32(max_j |x[t, j]|) / 448 in float32
+     (1 for an all-zero row), q = e4m3(fp32(x) / s_x); the shared expert sees
+     q * s_x and the routed expert q * (g * s_x).
+  R1 (e4m3 weights): h is first rounded to bf16 as above, then quantised per
+     token exactly like R0 (scale from the bf16 row's max magnitude).
+  The output itself is returned unrounded in float64.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Optional
+
+import numpy as np
+import torch
+
+from .numerics import bf16_round, e4m3_round, e4m3_decode
+
+NEAR_TIE = 1e-3   # top-2 logit margin below which either choice is accepted
+
+
+# ------------------------------------------------------------ input decoding
+
+def to_f64(t) -> np.ndarray:
+    """fp32 / bf16 torch tensor (or numpy array) -> exact float64 numpy array."""
+    if isinstance(t, torch.Tensor):
+        return t.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def dequant_cols(codes, scale) -> np.ndarray:
+    """e4m3 codes [K, N] (uint8) with one fp32 scale per column N -> float64 values."""
+    c = codes.numpy() if isinstance(codes, torch.Tensor) else np.asarray(codes)
+    s = to_f64(scale)
+    return e4m3_decode(c) * s[None, :]
+
+
+def weight_f64(w, scale=None) -> np.ndarray:
+    if scale is None:
+        return to_f64(w)
+    return dequant_cols(w, scale)
+
+
+# ------------------------------------------------------------ routing
+
+@dataclasses.dataclass
+class Routing:
+    logits: np.ndarray   # [T, E] float64
+    idx: np.ndarray      # [T] int64, chosen expert
+    gate: np.ndarray     # [T] float64, sigmoid of the chosen logit
+    margin: np.ndarray   # [T] float64, chosen logit minus best other (inf if E == 1)
+    counts: np.ndarray   # [E] int64
+    offsets: np.ndarray  # [E + 1] int64
+    perm: np.ndarray     # [T] int64, tokens grouped by expert, ascending within a group
+    inv: np.ndarray      # [T] int64, inverse of perm
+
+
+def router_logits(x, wr, bias=None) -> np.ndarray:
+    lg = to_f64(x) @ to_f64(wr)
+    if bias is not None:
+        lg = lg + to_f64(bias)[None, :]
+    return lg
+
+
+def top1(logits: np.ndarray):
+    """Lowest index among the maxima of each row, and the top-2 margin."""
+    T, E = logits.shape
+    mx = logits.max(axis=1) if E else np.zeros(T)
+    idx = np.argmax(logits == mx[:, None], axis=1).astype(np.int64)
+    if E == 1:
+        margin = np.full(T, np.inf)
+    else:
+        others = logits.copy()
+        others[np.arange(T), idx] = -np.inf
+        margin = mx - others.max(axis=1)
+    return idx, margin
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def routing_record(idx: np.ndarray, E: int):
+    counts = np.bincount(idx, minlength=E).astype(np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    perm = np.argsort(idx, kind="stable").astype(np.int64)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(len(perm), dtype=np.int64)
+    return counts, offsets, perm, inv
+
+
+def route(x, wr, bias=None) -> Routing:
+    lg = router_logits(x, wr, bias)
+    idx, margin = top1(lg)
+    gate = sigmoid(lg[np.arange(lg.shape[0]), idx])
+    counts, offsets, perm, inv = routing_record(idx, lg.shape[1])
+    return Routing(lg, idx, gate, margin, counts, offsets, perm, inv)
+
+
+# ------------------------------------------------------------ experts
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(a: np.ndarray, width: int) -> np.ndarray:
+    return silu(a[:, :width]) * a[:, width:]
+
+
+def quant_rows_e4m3(v32: np.ndarray):
+    """Per-row e4m3 quantisation of float32-valued rows -> (values q*s as float64, s)."""
+    v32 = np.asarray(v32, dtype=np.float32)
+    amax = np.abs(v32).max(axis=1) if v32.shape[1] else np.zeros(v32.shape[0], np.float32)
+    s = (amax.astype(np.float32) / np.float32(448.0)).astype(np.float32)
+    s = np.where(amax > 0, s, np.float32(1.0)).astype(np.float32)
+    q = e4m3_round((v32 / s[:, None]).astype(np.float32))
+    return q * s.astype(np.float64)[:, None], s
+
+
+def round_h(h: np.ndarray, mode: str) -> np.ndarray:
+    """Rounding point R1 applied to SwiGLU outputs (rows = tokens)."""
+    if mode == "f32":
+        return h
+    hb = bf16_round(h.astype(np.float32))
+    if mode == "bf16":
+        return hb
+    if mode == "e4m3":
+        return quant_rows_e4m3(hb.astype(np.float32))[0]
+    raise ValueError(mode)
+
+
+def swiglu_mlp(u: np.ndarray, wgu: np.ndarray, wd: np.ndarray, width: int, mode: str,
+               row_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    a = u @ wgu
+    if row_scale is not None:
+        a = a * row_scale[:, None]
+    h = round_h(swiglu(a, width), mode)
+    return h @ wd
+
+
+# ------------------------------------------------------------ the block
+
+class Weights:
+    """Access to the block's weights as torch CPU tensors.
+
+    router() -> (w_router [d,E], bias [E] | None)
+    expert(e) -> (w_gate_up [d,2f], s_gate_up | None, w_down [f,d], s_down | None)
+    shared() -> (ws_gate_up [d,2fs], ss_gate_up | None, ws_down [fs,d], ss_down | None)
+    """
+
+    def __init__(self, router: Callable, expert: Callable, shared: Callable):
+        self.router, self.expert, self.shared = router, expert, shared
+
+    @staticmethod
+    def from_dict(inp: dict) -> "Weights":
+        def ex(e):
+            s = inp.get("s_gate_up")
+            sd = inp.get("s_down")
+            return (inp["w_gate_up"][e], None if s is None else s[e],
+                    inp["w_down"][e], None if sd is None else sd[e])
+        return Weights(lambda: (inp["w_router"], inp.get("router_bias")), ex,
+                       lambda: (inp["ws_gate_up"], inp.get("ss_gate_up"),
+                                inp["ws_down"], inp.get("ss_down")))
+
+
+def expert_input(x, mode: str):
+    """The expert path's view of x: (float64 values, per-token scale or None)."""
+    x64 = to_f64(x)
+    if mode != "e4m3":
+        return x64, None
+    xq, s = quant_rows_e4m3(x64.astype(np.float32))
+    return xq, s
+
+
+def combine(x, idx: np.ndarray, gate: np.ndarray, w: Weights, f: int, fs: int,
+            mode: str) -> np.ndarray:
+    """out[t] = shared(x[t]) + expert_{idx[t]}(gate[t] * x[t]) for given choices."""
+    xin, _ = expert_input(x, mode)
+    T = xin.shape[0]
+    wsgu, ssgu, wsd, ssd = w.shared()
+    out = swiglu_mlp(xin, weight_f64(wsgu, ssgu), weight_f64(wsd, ssd), fs, mode)
+    for e in np.unique(idx):
+        rows = np.nonzero(idx == e)[0]
+        wgu, sgu, wd, sd = w.expert(int(e))
+        out[rows] += swiglu_mlp(xin[rows], weight_f64(wgu, sgu), weight_f64(wd, sd), f, mode,
+                                row_scale=gate[rows])
+    assert out.shape[0] == T
+    return out
+
+
+def forward(x, w: Weights, f: int, fs: int, mode: str):
+    """Whole block: returns (out float64 [T, d], Routing)."""
+    wr, b = w.router()
+    r = route(x, wr, b)
+    out = combine(x, r.idx, r.gate, w, f, fs, mode)
+    return out, r
+
+
+def rel_err(got, ref) -> float:
+    """max |got - ref| / RMS(ref)."""
+    g = to_f64(got)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = np.sqrt(np.mean(ref * ref))
+    if rms == 0:
+        return float(np.max(np.abs(g - ref)))
+    return float(np.max(np.abs(g - ref)) / rms)

@@ -1,0 +1,75 @@
+"""oracle.numerics against torch's bf16 / float8_e4m3fn casts (library routines)."""
+import numpy as np
+import torch
+
+from oracle import numerics
+
+
+def _all_bf16_as_f32():
+    bits = np.arange(65536, dtype=np.uint32) << 16
+    v = bits.view(np.float32)
+    return v[np.isfinite(v)]
+
+
+def _random_f32(n, seed):
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+    v = bits.view(np.float32)
+    return v[np.isfinite(v)]
+
+
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([
+        _random_f32(500_000, 1),
+        rng.standard_normal(500_000).astype(np.float32),
+        _all_bf16_as_f32(),
+        # exact ties: bf16 value + half an ulp
+        (_all_bf16_as_f32().view(np.uint32) + np.uint32(0x8000)).view(np.float32),
+    ])
+    v = v[np.isfinite(v) & (np.abs(v) < 3.0e38)]
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = numerics.bf16_round(v)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3_decode_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = numerics.e4m3_decode_table()
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_e4m3_round_matches_torch_in_range():
+    rng = np.random.default_rng(2)
+    v = np.concatenate([
+        _all_bf16_as_f32(),
+        _random_f32(400_000, 3),
+        (rng.standard_normal(400_000) * 100).astype(np.float32),
+        (rng.standard_normal(100_000) * 1e-2).astype(np.float32),
+    ])
+    v = v[np.abs(v) <= 448.0]  # torch's cast does not saturate; compare inside the range
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = numerics.e4m3_round(v)
+    np.testing.assert_array_equal(got, ref)
+    codes = numerics.e4m3_encode(v)
+    ref_codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # -0 vs +0 may differ only for zero; compare values through the decode table elsewhere
+    nz = v != 0
+    np.testing.assert_array_equal(codes[nz], ref_codes[nz])
+
+
+def test_e4m3_saturates():
+    v = np.array([448.0, 449.0, 463.9, 464.0, 470.0, 1e6, -1e30, -500.0], dtype=np.float32)
+    got = numerics.e4m3_round(v)
+    np.testing.assert_array_equal(got, [448, 448, 448, 448, 448, 448, -448, -448])
+
+
+def test_e4m3_ties_to_even():
+    # 1 + 1/16 is halfway between 1 and 1.125: ties to the even mantissa (1.0)
+    # 1 + 3/16 halfway between 1.125 and 1.25: ties to 1.25
+    v = np.array([1.0625, 1.1875, 2 ** -10, 3 * 2 ** -10], dtype=np.float32)
+    np.testing.assert_array_equal(numerics.e4m3_round(v), [1.0, 1.25, 0.0, 2 ** -8])
