@@ -1,0 +1,207 @@
+"""Benchmark of the Llama 4 MoE feed-forward block on one MI355X.
+
+One step = one moe_forward over one batch of synthetic tokens: router GEMM,
+top-1 + sigmoid gate, histogram / scan / permutation, grouped gate/up GEMM
+with the SwiGLU epilogue (routed + shared), shared down GEMM, routed down
+GEMM with un-permute + combine.  Inputs are generated on the GPU by the
+seeded generator before timing and stay resident in HBM.
+
+Prints ONE JSON line (rank 0, N = 1):
+  value       tokens/s of the whole block
+  roofline    the dominant stage (largest average duration, timed with HIP
+              events recorded by the library on its stream) against the MFMA
+              or HBM roofline, using algorithmic FLOPs / bytes of that stage
+  cpu_baseline  the fp64 CPU oracle timed on a bounded token sample
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2516.6e12, "e4m3": 5033.2e12, "f32": 157.3e12}   # dense MFMA, FLOP/s
+HBM_PEAK = 8.0e12                                                 # bytes/s
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def esize(dt: str) -> int:
+    return {"f32": 4, "bf16": 2, "e4m3": 1}[dt]
+
+
+def stage_work(cfg, counts):
+    """Algorithmic (FLOPs, bytes) per launch of each stage."""
+    T, d, E, f, fs = cfg.T, cfg.d, cfg.E, cfg.f, cfg.fs
+    xb, wb = esize(cfg.x_dtype), esize(cfg.w_dtype)
+    hb = 4 if cfg.w_dtype == "f32" else 2
+    ob = esize(cfg.out_dtype)
+    touched = sum(1 for c in counts if c > 0)
+    sc = 4 if cfg.w_dtype == "e4m3" else 0     # fp32 column scales per weight column
+    xin = 1 if cfg.w_dtype == "e4m3" else xb   # gate/up reads the e4m3 copy of x
+    return {
+        "route": (2 * T * d * E, T * d * xb + d * E * xb + (4 * E if cfg.has_bias else 0) + T * 8),
+        "gate_up": (4 * T * d * (f + fs),
+                    touched * (d * 2 * f * wb + 2 * f * sc) + d * 2 * fs * wb + 2 * fs * sc
+                    + T * d * xin + T * (f + fs) * hb),
+        "down_shared": (2 * T * fs * d, fs * d * wb + d * sc + T * fs * hb + T * d * 4),
+        "down_routed": (2 * T * f * d, touched * (f * d * wb + d * sc) + T * f * hb + T * d * 4 + T * d * ob),
+    }
+
+
+def block_work(cfg, counts):
+    """Whole-block algorithmic FLOPs and bytes (touched weights + x + out)."""
+    T, d, E, f, fs = cfg.T, cfg.d, cfg.E, cfg.f, cfg.fs
+    wb = esize(cfg.w_dtype)
+    sc = 4 if cfg.w_dtype == "e4m3" else 0
+    touched = sum(1 for c in counts if c > 0)
+    flops = 2 * T * (d * E + 3 * d * f + 3 * d * fs)
+    byts = (touched * (3 * d * f * wb + (2 * f + d) * sc) + 3 * d * fs * wb + (2 * fs + d) * sc
+            + d * E * esize(cfg.x_dtype) + T * d * esize(cfg.x_dtype) + T * d * esize(cfg.out_dtype))
+    return flops, byts
+
+
+def cpu_baseline(cfg, g, sample):
+    """Time the fp64 oracle on the first `sample` tokens (weights copied per expert)."""
+    import numpy as np
+    import torch
+    from oracle import block
+
+    xs = g["x"][:sample].cpu()
+
+    def ex(e):
+        s = g["s_gate_up"]
+        sd = g["s_down"]
+        return (g["w_gate_up"][e].cpu(), None if s is None else s[e].cpu(),
+                g["w_down"][e].cpu(), None if sd is None else sd[e].cpu())
+
+    shared = tuple(None if g[k] is None else g[k].cpu() for k in ("ws_gate_up", "ss_gate_up", "ws_down", "ss_down"))
+    router = (g["w_router"].cpu(), None if g["router_bias"] is None else g["router_bias"].cpu())
+    w = block.Weights(lambda: router, ex, lambda: shared)
+    t0 = time.perf_counter()
+    out, r = block.forward(xs, w, cfg.f, cfg.fs, cfg.w_dtype)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"first {sample} of {cfg.T} tokens, full fp64 block (routing + every touched expert "
+                      f"+ shared), {int(np.count_nonzero(r.counts))} experts touched, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="scout_prefill_bf16")
+    ap.add_argument("--cpu-sample", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the block is measured at one "
+                                   "GPU's share with no collectives; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import synth
+    from sparse_moe_transformer_llama4_amd import moe
+
+    dev = torch.device("cuda:0")
+    cfg = synth.get_config(args.config)
+    print(f"[bench] generating {cfg.name} on {dev}", file=sys.stderr, flush=True)
+    g = synth.make_inputs(cfg, dev)
+    torch.cuda.synchronize()
+    plan = moe.Plan.for_shape(cfg)
+    ws = torch.empty(max(moe.moe_workspace_size(plan, cfg.T), 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.T, cfg.d), dtype=moe._TORCH_DT[moe._DT[cfg.out_dtype]], device=dev)
+    routing = moe.new_routing(plan, cfg.T, dev)
+    events = [moe.StageEvents() for _ in range(args.steps)]
+    warm_ev = moe.StageEvents()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        moe.moe_forward_timed(plan, g["x"], g, warm_ev, out, ws, routing)
+    torch.cuda.synchronize()
+    counts = routing["counts"].cpu().tolist()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        moe.moe_forward_timed(plan, g["x"], g, events[k], out, ws, routing)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+
+    per_stage = [ev.durations_ms() for ev in events]
+    avg = [sum(s[i] for s in per_stage) / len(per_stage) for i in range(moe.MOE_NUM_STAGES)]
+    stage_ms = dict(zip(moe.STAGES, avg))
+    work = stage_work(cfg, counts)
+    dom = max(stage_ms, key=stage_ms.get)
+    fl, by = work[dom]
+    peak_f = PEAK[cfg.w_dtype]
+    ridge = peak_f / HBM_PEAK
+    t_dom = stage_ms[dom] * 1e-3
+    if fl / by >= ridge:
+        roof = {"bound": "mfma", "achieved": fl / t_dom / 1e12, "peak": peak_f / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": by / t_dom / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = dom
+    roof["ms"] = stage_ms[dom]
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        tr = json.load(open(PROFILE_TRAFFIC)).get(cfg.name, {}).get(dom)
+        if tr and tr.get("source_hash") == _kernel_source_hash():
+            traffic = tr["bytes"]
+    roof["traffic"] = traffic
+
+    F, B = block_work(cfg, counts)
+    t = ms * 1e-3
+    result = {
+        "metric": "MoE-layer tokens/s + % MFMA peak (prefill), % HBM BW (decode)",
+        "value": cfg.T / t,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.w_dtype,
+        "data": "synthetic (seeded counter-based generator, random-init weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "f": cfg.f, "f_shared": cfg.fs,
+                   "x_dtype": cfg.x_dtype, "w_dtype": cfg.w_dtype, "out_dtype": cfg.out_dtype,
+                   "routing": cfg.bias, "experts_touched": sum(1 for c in counts if c > 0)},
+        "block_tflops": F / t / 1e12,
+        "block_gbps": B / t / 1e9,
+        "mfma_frac": F / t / peak_f,
+        "hbm_frac": B / t / HBM_PEAK,
+        "stage_ms": stage_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or min(cfg.T, 512 if cfg.E <= 16 else 192)
+        print(f"[bench] cpu oracle on {sample} tokens", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, g, sample)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def _kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_transformer_llama4_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * moe.h -- C ABI of the Llama 4 mixture-of-experts feed-forward block on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The block (KerasFormers "Llama 4", section "What is unusual about the
+ * block"; superteams.ai "Llama 4", section "Mixture of Experts: Why Total
+ * and Active Parameters Diverge"; llm-architectures-explained "Llama 4
+ * Maverick", table "Every architecture field"):
+ *
+ *   logit[t,e] = sum_j x[t,j] * W_router[j,e] (+ bias[e])      one logit per expert
+ *   e*(t)      = lowest index among the maxima of logit[t,:]    top-1 (argmax)
+ *   g(t)       = 1 / (1 + exp(-logit[t,e*]))                    sigmoid gate on the input
+ *   routed(t)  = SwiGLU_{e*}(g(t) * x[t])                       gated MLP of width f
+ *   shared(t)  = SwiGLU_s(x[t])                                 shared gated MLP of width f_shared
+ *   out[t]     = shared(t) + routed(t)                          the other experts contribute nothing
+ *   SwiGLU_W(u) = (SiLU(u Wg) * (u Wu)) Wd,  SiLU(z) = z / (1 + exp(-z)),
+ *                Wg / Wu = columns [0,f) / [f,2f) of W_gate_up.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer (HBM) owned by the caller;
+ *     the library never allocates, frees or keeps device memory.  Scratch
+ *     space is the caller's workspace, sized by moe_workspace_size.
+ *   - All work is enqueued asynchronously on `stream` (hipStream_t; NULL =
+ *     the default stream).  No host synchronisation, no device-to-host copy.
+ *   - Arguments, shapes, alignment and workspace size are checked on the
+ *     host BEFORE anything is enqueued; a failed check enqueues nothing.
+ *   - Row-major layouts throughout.  Pointers must be 16-byte aligned.
+ *   - Inputs must be finite; NaN / Inf inputs are outside the contract.
+ *   - A plan is immutable after creation and may be shared by threads and
+ *     streams; concurrent calls need distinct workspaces.
+ */
+#ifndef MOE355_MOE_H
+#define MOE355_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = -1, /* null / misaligned pointer, missing fp8 scale, bad abi_version */
+  MOE_ERR_UNSUPPORTED = -2,      /* top_k != 1, d / f / f_shared not multiples of 64 (128 for
+                                    E4M3 weights), E outside [1,256], dtype combination not
+                                    implemented */
+  MOE_ERR_SHAPE = -3,            /* T < 0 or T > max_tokens */
+  MOE_ERR_WORKSPACE = -4,        /* workspace smaller than moe_workspace_size */
+  MOE_ERR_HIP = -5               /* a HIP launch failed; see moe_last_hip_error */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_E4M3 = 2 /* OCP 8-bit float E4M3 "fn": max 448, no infinities; stored as uint8 codes */
+} moe_dtype;
+
+/*
+ * Block configuration (KerasFormers "Llama 4", Llama4Model arguments
+ * embed_dim / mlp_dim / num_experts / num_experts_per_tok; torchtune
+ * llama4_decoder parameters num_experts, experts_per_token,
+ * use_shared_expert).  Supported dtype triples (x, w, out):
+ *   F32 / F32 / F32      fp32 everywhere, fp32 MFMA
+ *   BF16 / BF16 / F32    bf16 MFMA, fp32 accumulate, h rounded to bf16, fp32 output
+ *   BF16 / BF16 / BF16   as above with the output rounded to bf16
+ *   BF16 / E4M3 / BF16   router in bf16; x and h quantised to e4m3 per token;
+ *                        e4m3 weights with one fp32 scale per output column
+ */
+typedef struct moe_config {
+  int32_t abi_version;     /* MOE_ABI_VERSION */
+  int32_t d;               /* model width, multiple of 64 (128 for E4M3 weights) */
+  int32_t n_experts;       /* E, 1..256 */
+  int32_t f;               /* routed expert width, multiple of 64 (128 for E4M3) */
+  int32_t f_shared;        /* shared expert width, multiple of 64 (128 for E4M3) */
+  int32_t top_k;           /* must be 1 */
+  int32_t x_dtype;         /* moe_dtype of x and W_router */
+  int32_t w_dtype;         /* moe_dtype of the expert and shared weights */
+  int32_t out_dtype;       /* moe_dtype of out */
+  int32_t has_router_bias; /* 0 / 1 */
+  int64_t max_tokens;      /* largest T accepted by this plan (>= 1) */
+} moe_config;
+
+typedef struct moe_plan_s* moe_plan_t;
+
+/*
+ * Weights: all resident in device memory (KerasFormers "Llama 4": all
+ * experts stay resident).  Scale pointers are required when w_dtype is
+ * E4M3 and ignored otherwise: one fp32 scale per output column n of the
+ * [K, N] matrix, value = code * scale[n].
+ */
+typedef struct moe_weights {
+  const void* w_router;     /* [d, E]         x_dtype */
+  const float* router_bias; /* [E] fp32, or NULL when has_router_bias == 0 */
+  const void* w_gate_up;    /* [E, d, 2f]     columns [0,f) feed SiLU, [f,2f) the linear branch */
+  const float* s_gate_up;   /* [E, 2f] */
+  const void* w_down;       /* [E, f, d] */
+  const float* s_down;      /* [E, d] */
+  const void* ws_gate_up;   /* [d, 2 f_shared] shared expert */
+  const float* ss_gate_up;  /* [2 f_shared] */
+  const void* ws_down;      /* [f_shared, d] */
+  const float* ss_down;     /* [d] */
+} moe_weights;
+
+/*
+ * Routing record (device buffers owned by the caller).
+ *   expert_idx[t] = e*(t);  gate[t] = g(t) (fp32, from the fp32 logit);
+ *   counts[e] = #tokens routed to e;  offsets[0] = 0,
+ *   offsets[e+1] = offsets[e] + counts[e];
+ *   perm[offsets[e] + r] = the r-th smallest token index routed to e
+ *   (a stable grouping of tokens by expert).
+ */
+typedef struct moe_routing {
+  int32_t* expert_idx; /* [T] */
+  float* gate;         /* [T] */
+  int32_t* counts;     /* [E] */
+  int32_t* offsets;    /* [E + 1] */
+  int32_t* perm;       /* [T] */
+} moe_routing;
+
+/* Validate `cfg` and create a host-side plan (no device call is made).
+ * Returns MOE_ERR_UNSUPPORTED / MOE_ERR_INVALID_ARGUMENT for bad configs; *out
+ * is set to NULL on failure. */
+moe_status moe_plan(const moe_config* cfg, moe_plan_t* out);
+
+/* Release a plan (NULL is ignored).  Does not touch device memory. */
+void moe_plan_destroy(moe_plan_t plan);
+
+/* Bytes of device workspace moe_route / moe_forward need for T tokens. */
+moe_status moe_workspace_size(moe_plan_t plan, int64_t T, size_t* bytes);
+
+/*
+ * Router, top-1, gate and the stable expert grouping only (superteams.ai
+ * "Llama 4", routing sketch: one logit per expert, argmax).  Fills every
+ * pointer of *out.  T == 0 zeroes counts and offsets and enqueues nothing else.
+ */
+moe_status moe_route(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w,
+                     moe_routing* out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * The whole block: out[T, d] (out_dtype) = shared(x) + routed(x).
+ * x: [T, d] x_dtype.  routing_out may be NULL; when given, the routing
+ * record is written there as by moe_route.  Each output row is written
+ * exactly once (no atomics), so results are deterministic.
+ */
+moe_status moe_forward(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w,
+                       void* out, moe_routing* routing_out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_forward with stage timing: records events[0..MOE_NUM_STAGES] on
+ * `stream` at the stage boundaries
+ *   [0] routing (router GEMM, top-1, gate, scan, permutation; e4m3: x quantisation)
+ *   [1] grouped gate/up GEMM with the SwiGLU epilogue (routed groups + shared)
+ *   [2] shared-expert down GEMM (e4m3: preceded by h quantisation)
+ *   [3] routed down GEMM with un-permute + combine
+ * so hipEventElapsedTime(events[i], events[i+1]) is the duration of stage i.
+ * Events are created by the caller; everything else is as moe_forward.
+ */
+#define MOE_NUM_STAGES 4
+moe_status moe_forward_timed(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w,
+                             void* out, moe_routing* routing_out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* hipError_t value behind the last MOE_ERR_HIP returned for this plan (0 if none). */
+int moe_last_hip_error(moe_plan_t plan);
+
+/* Library identity, e.g. "moe355 1 gfx950". */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE355_MOE_H */

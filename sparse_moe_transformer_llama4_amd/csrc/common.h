@@ -1,0 +1,62 @@
+// Internal definitions shared by the HIP translation units of libmoe355.
+// gfx950 (CDNA4) only: 64-lane wavefronts, MFMA matrix cores, 160 KiB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// Tile heights the device-side scheduler publishes tile tables for.
+constexpr int kNumBM = 5;
+__host__ __device__ constexpr int bm_of(int i) { return 16 << i; }  // 16, 32, 64, 128, 256
+__host__ __device__ constexpr int bm_index(int bm) {
+  return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : 4;
+}
+
+// Tokens handled by one router workgroup (4 waves x 16 tokens).
+constexpr int kRouteTokens = 64;
+
+enum Dtype : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+// ------------------------------------------------------------------ scalars
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// ------------------------------------------------------------------ workspace
+
+// Byte offsets of the scratch buffers inside the caller's workspace.  All
+// offsets are multiples of 256.  Sizes depend on T (tokens) and the plan.
+struct WsLayout {
+  size_t idx, gate, counts, offsets, perm;  // routing record (used when the caller passes none)
+  size_t hist;                              // int32 [nblocks_route][E] -> per-block bases
+  size_t tiles;                             // int32 [kNumBM][E + 2] tile tables
+  size_t h_r, h_s;                          // SwiGLU outputs (bf16 / f32; bf16 staging for e4m3)
+  size_t hq_r, hq_s;                        // e4m3 codes of h (e4m3 only)
+  size_t sh_r, sh_s;                        // per-row fp32 scales of h (e4m3 only)
+  size_t amax_r, amax_s;                    // per-row max |h| as uint bits (e4m3 only)
+  size_t y_s;                               // fp32 [T][d] shared-expert output
+  size_t xq, sx;                            // e4m3 x codes [T][d] and fp32 scales [T] (e4m3 only)
+  size_t total;
+};
+
+}  // namespace moe

@@ -1,0 +1,72 @@
+// Kernel argument blocks and host-side launchers (internal to libmoe355).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouterArgs {
+  const void* x;      // [T][d] x dtype
+  const void* wr;     // [d][E] x dtype
+  const float* bias;  // [E] or nullptr
+  int T, d, E;
+  int32_t* idx;       // [T]
+  float* gate;        // [T]
+  int32_t* hist;      // [nblocks][E]
+};
+
+struct ScanArgs {
+  int32_t* hist;  // [nblocks][E], replaced by per-block bases
+  int nblocks, E, T;
+  int32_t* counts;   // [E]
+  int32_t* offsets;  // [E + 1]
+  int32_t* tiles;    // [kNumBM][E + 2]
+};
+
+enum GemmMode : int {
+  MODE_GATEUP = 0,       // groups 0..E-1 routed (+ group E = shared): h = SiLU(g*acc_gate) * (g*acc_up)
+  MODE_DOWN_SHARED = 1,  // y_s = h_s W_down_shared (fp32)
+  MODE_DOWN_ROUTED = 2   // out[perm[r]] = h_r[r] W_down[e] + y_s[perm[r]]
+};
+
+struct GemmArgs {
+  const void* A;         // routed A: x / x codes (GATEUP, gathered through perm) or h_r (DOWN)
+  const void* A_shared;  // shared A: x / x codes (GATEUP) or h_s (DOWN_SHARED)
+  const void* B;         // routed weights [E][K][Nb]
+  const void* B_shared;  // shared weights [K][Nb]
+  const float* sB;       // e4m3: routed column scales [E][Nb]
+  const float* sB_shared;
+  const float* sA;       // e4m3: per-row scale of A (x scale by token, or h scale by row)
+  const float* sA_shared;
+  int K;
+  int N;                 // GATEUP: routed half width f; DOWN: d
+  int N_shared;          // GATEUP: shared half width fs
+  int T, E;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* tiles;  // tile table row for this launch's BM ([E + 2])
+  const float* gate;     // [T] by token
+  void* C;               // GATEUP: h_r [T][f]; DOWN_ROUTED: out [T][d]; DOWN_SHARED: y_s
+  void* C_shared;        // GATEUP: h_s [T][fs]
+  const float* Y;        // DOWN_ROUTED: y_s [T][d]
+  uint32_t* amax;        // e4m3 GATEUP: per-row max |h| bits (routed rows)
+  uint32_t* amax_shared;
+  int out_bf16;          // DOWN_ROUTED: output dtype bf16 (else fp32)
+};
+
+hipError_t launch_router(const RouterArgs& a, int x_dtype, hipStream_t s);
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+hipError_t launch_perm(const int32_t* idx, const int32_t* base, int T, int E, int32_t* perm,
+                       hipStream_t s);
+hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* sx, hipStream_t s);
+hipError_t launch_quant_h(const uint16_t* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
+                          float* sh, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+
+// Grouped GEMM launch.  `grid_m` is an upper bound of M tiles; surplus
+// workgroups exit after reading the tile table.
+hipError_t launch_gemm(int mode, int w_dtype, const GemmArgs& a, int grid_m_tokens, hipStream_t s,
+                       const int32_t* tiles_all);
+
+}  // namespace moe

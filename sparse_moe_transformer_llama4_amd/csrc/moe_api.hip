@@ -1,0 +1,339 @@
+// Host side of libmoe355: the C ABI declared in include/moe.h.
+// Validation happens before any enqueue; the launch sequence is
+//   router -> scan -> permutation -> grouped gate/up GEMM (+ shared) ->
+//   [e4m3: quantise h] -> shared down GEMM -> routed down GEMM + combine,
+// all on the caller's stream, with no host synchronisation.
+#include <cstring>
+#include <new>
+
+#include "common.h"
+#include "launch.h"
+#include "moe.h"
+
+using namespace moe;
+
+struct moe_plan_s {
+  moe_config cfg;
+  int last_hip_error;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool config_dtypes_ok(const moe_config& c) {
+  if (c.x_dtype == MOE_F32 && c.w_dtype == MOE_F32 && c.out_dtype == MOE_F32) return true;
+  if (c.x_dtype == MOE_BF16 && c.w_dtype == MOE_BF16 && (c.out_dtype == MOE_F32 || c.out_dtype == MOE_BF16))
+    return true;
+  if (c.x_dtype == MOE_BF16 && c.w_dtype == MOE_E4M3 && c.out_dtype == MOE_BF16) return true;
+  return false;
+}
+
+int k_multiple(const moe_config& c) { return c.w_dtype == MOE_E4M3 ? 128 : 64; }
+
+WsLayout layout_for(const moe_config& c, int64_t T) {
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t E = static_cast<size_t>(c.n_experts);
+  const size_t t = static_cast<size_t>(T);
+  const size_t nb = (t + kRouteTokens - 1) / kRouteTokens;
+  const bool fp8 = c.w_dtype == MOE_E4M3;
+  const size_t hsz = c.w_dtype == MOE_F32 ? 4 : 2;
+  L.idx = take(t * 4);
+  L.gate = take(t * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(t * 4);
+  L.hist = take(nb * E * 4);
+  L.tiles = take(kNumBM * (E + 2) * 4);
+  L.h_r = take(t * c.f * hsz);
+  L.h_s = take(t * c.f_shared * hsz);
+  L.y_s = take(t * c.d * 4);
+  if (fp8) {
+    L.hq_r = take(t * c.f);
+    L.hq_s = take(t * c.f_shared);
+    L.sh_r = take(t * 4);
+    L.sh_s = take(t * 4);
+    L.amax_r = take(t * 4);
+    L.amax_s = take(t * 4);
+    L.xq = take(t * c.d);
+    L.sx = take(t * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+moe_status hip_fail(moe_plan_t p, hipError_t e) {
+  p->last_hip_error = static_cast<int>(e);
+  return MOE_ERR_HIP;
+}
+
+moe_status check_common(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* ws,
+                        size_t ws_bytes) {
+  if (!plan || !w) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config& c = plan->cfg;
+  if (T < 0 || T > c.max_tokens) return MOE_ERR_SHAPE;
+  if (T > 0 && (!x || !aligned16(x))) return MOE_ERR_INVALID_ARGUMENT;
+  if (!w->w_router || !aligned16(w->w_router)) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.has_router_bias && (!w->router_bias || !aligned16(w->router_bias))) return MOE_ERR_INVALID_ARGUMENT;
+  if (layout_for(c, T).total > ws_bytes) return MOE_ERR_WORKSPACE;
+  if (T > 0 && (!ws || !aligned16(ws))) return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+moe_status check_expert_weights(const moe_config& c, const moe_weights* w) {
+  const void* req[] = {w->w_gate_up, w->w_down, w->ws_gate_up, w->ws_down};
+  for (const void* p : req)
+    if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.w_dtype == MOE_E4M3) {
+    const void* sc[] = {w->s_gate_up, w->s_down, w->ss_gate_up, w->ss_down};
+    for (const void* p : sc)
+      if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  return MOE_OK;
+}
+
+moe_status check_routing(const moe_routing* r) {
+  const void* ps[] = {r->expert_idx, r->gate, r->counts, r->offsets, r->perm};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+// Pointers of the routing record: the caller's, or workspace-backed.
+struct Route {
+  int32_t *idx, *counts, *offsets, *perm, *hist, *tiles;
+  float* gate;
+};
+
+Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
+  Route o;
+  o.idx = r ? r->expert_idx : reinterpret_cast<int32_t*>(ws + L.idx);
+  o.gate = r ? r->gate : reinterpret_cast<float*>(ws + L.gate);
+  o.counts = r ? r->counts : reinterpret_cast<int32_t*>(ws + L.counts);
+  o.offsets = r ? r->offsets : reinterpret_cast<int32_t*>(ws + L.offsets);
+  o.perm = r ? r->perm : reinterpret_cast<int32_t*>(ws + L.perm);
+  o.hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  o.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  return o;
+}
+
+// Router + scan + permutation.
+hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_weights* w, const Route& R,
+                         hipStream_t s) {
+  hipError_t e;
+  if (T > 0) {
+    RouterArgs ra{x, w->w_router, c.has_router_bias ? w->router_bias : nullptr, T, c.d, c.n_experts,
+                  R.idx, R.gate, R.hist};
+    if ((e = launch_router(ra, c.x_dtype, s)) != hipSuccess) return e;
+  }
+  ScanArgs sa{R.hist, (T + kRouteTokens - 1) / kRouteTokens, c.n_experts, T, R.counts, R.offsets, R.tiles};
+  if ((e = launch_scan(sa, s)) != hipSuccess) return e;
+  if (T > 0 && (e = launch_perm(R.idx, R.hist, T, c.n_experts, R.perm, s)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_SHAPE: return "token count out of range";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* moe_version(void) { return "moe355 1 gfx950"; }
+
+moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
+  if (!out) return MOE_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (!cfg || cfg->abi_version != MOE_ABI_VERSION) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config& c = *cfg;
+  if (c.top_k != 1) return MOE_ERR_UNSUPPORTED;
+  if (c.n_experts < 1 || c.n_experts > 256) return MOE_ERR_UNSUPPORTED;
+  if (!config_dtypes_ok(c)) return MOE_ERR_UNSUPPORTED;
+  const int km = k_multiple(c);
+  if (c.d <= 0 || c.f <= 0 || c.f_shared <= 0 || c.d % km || c.f % km || c.f_shared % km)
+    return MOE_ERR_UNSUPPORTED;
+  if (c.has_router_bias != 0 && c.has_router_bias != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.max_tokens < 1 || c.max_tokens > (int64_t{1} << 30)) return MOE_ERR_SHAPE;
+  moe_plan_s* p = new (std::nothrow) moe_plan_s;
+  if (!p) return MOE_ERR_INVALID_ARGUMENT;
+  p->cfg = c;
+  p->last_hip_error = 0;
+  *out = p;
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan_t plan) { delete plan; }
+
+int moe_last_hip_error(moe_plan_t plan) { return plan ? plan->last_hip_error : 0; }
+
+moe_status moe_workspace_size(moe_plan_t plan, int64_t T, size_t* bytes) {
+  if (!plan || !bytes) return MOE_ERR_INVALID_ARGUMENT;
+  if (T < 0 || T > plan->cfg.max_tokens) return MOE_ERR_SHAPE;
+  *bytes = layout_for(plan->cfg, T).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, moe_routing* out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_common(plan, x, T, w, workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_routing(out)) != MOE_OK) return st;
+  const WsLayout L = layout_for(plan->cfg, T);
+  const Route R = route_ptrs(static_cast<uint8_t*>(workspace), L, out);
+  const hipError_t e = enqueue_route(plan->cfg, x, static_cast<int>(T), w, R, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
+}
+
+static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
+                               moe_routing* routing_out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, hipEvent_t* ev) {
+  moe_status st = check_common(plan, x, T, w, workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
+  const moe_config& c = plan->cfg;
+  if ((st = check_expert_weights(c, w)) != MOE_OK) return st;
+  if (T > 0 && (!out || !aligned16(out))) return MOE_ERR_INVALID_ARGUMENT;
+  if (routing_out && (st = check_routing(routing_out)) != MOE_OK) return st;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const WsLayout L = layout_for(c, T);
+  const Route R = route_ptrs(ws, L, routing_out);
+  const int Ti = static_cast<int>(T);
+  hipError_t e;
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  if ((e = mark(0)) != hipSuccess) return hip_fail(plan, e);
+  e = enqueue_route(c, x, Ti, w, R, stream);
+  if (e != hipSuccess) return hip_fail(plan, e);
+  if (T == 0) {
+    for (int i = 1; i <= MOE_NUM_STAGES; ++i)
+      if ((e = mark(i)) != hipSuccess) return hip_fail(plan, e);
+    return MOE_OK;
+  }
+
+  const bool fp8 = c.w_dtype == MOE_E4M3;
+  const void* a_x = x;
+  float* sx = nullptr;
+  uint32_t *amax_r = nullptr, *amax_s = nullptr;
+  if (fp8) {
+    uint8_t* xq = ws + L.xq;
+    sx = reinterpret_cast<float*>(ws + L.sx);
+    if ((e = launch_quant_x(static_cast<const uint16_t*>(x), Ti, c.d, xq, sx, stream)) != hipSuccess)
+      return hip_fail(plan, e);
+    a_x = xq;
+    amax_r = reinterpret_cast<uint32_t*>(ws + L.amax_r);
+    amax_s = reinterpret_cast<uint32_t*>(ws + L.amax_s);
+    if ((e = launch_fill_u32(amax_r, T, 0u, stream)) != hipSuccess) return hip_fail(plan, e);
+    if ((e = launch_fill_u32(amax_s, T, 0u, stream)) != hipSuccess) return hip_fail(plan, e);
+  }
+  if ((e = mark(1)) != hipSuccess) return hip_fail(plan, e);
+
+  // gate/up (routed groups + shared group) with the SwiGLU epilogue
+  GemmArgs g1{};
+  g1.A = a_x;
+  g1.A_shared = a_x;
+  g1.B = w->w_gate_up;
+  g1.B_shared = w->ws_gate_up;
+  g1.sB = fp8 ? w->s_gate_up : nullptr;
+  g1.sB_shared = fp8 ? w->ss_gate_up : nullptr;
+  g1.sA = sx;
+  g1.sA_shared = sx;
+  g1.K = c.d;
+  g1.N = c.f;
+  g1.N_shared = c.f_shared;
+  g1.T = Ti;
+  g1.E = c.n_experts;
+  g1.offsets = R.offsets;
+  g1.perm = R.perm;
+  g1.gate = R.gate;
+  g1.C = ws + L.h_r;
+  g1.C_shared = ws + L.h_s;
+  g1.amax = amax_r;
+  g1.amax_shared = amax_s;
+  if ((e = launch_gemm(MODE_GATEUP, c.w_dtype, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
+  if ((e = mark(2)) != hipSuccess) return hip_fail(plan, e);
+
+  const void* h_r = ws + L.h_r;
+  const void* h_s = ws + L.h_s;
+  float *sh_r = nullptr, *sh_s = nullptr;
+  if (fp8) {
+    sh_r = reinterpret_cast<float*>(ws + L.sh_r);
+    sh_s = reinterpret_cast<float*>(ws + L.sh_s);
+    if ((e = launch_quant_h(reinterpret_cast<const uint16_t*>(ws + L.h_r), amax_r, Ti, c.f, ws + L.hq_r, sh_r,
+                            stream)) != hipSuccess)
+      return hip_fail(plan, e);
+    if ((e = launch_quant_h(reinterpret_cast<const uint16_t*>(ws + L.h_s), amax_s, Ti, c.f_shared, ws + L.hq_s,
+                            sh_s, stream)) != hipSuccess)
+      return hip_fail(plan, e);
+    h_r = ws + L.hq_r;
+    h_s = ws + L.hq_s;
+  }
+
+  float* y_s = reinterpret_cast<float*>(ws + L.y_s);
+  GemmArgs g2{};
+  g2.A_shared = h_s;
+  g2.B_shared = w->ws_down;
+  g2.sB_shared = fp8 ? w->ss_down : nullptr;
+  g2.sA_shared = sh_s;
+  g2.K = c.f_shared;
+  g2.N = c.d;
+  g2.T = Ti;
+  g2.E = c.n_experts;
+  g2.offsets = R.offsets;
+  g2.C_shared = y_s;
+  if ((e = launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles)) != hipSuccess)
+    return hip_fail(plan, e);
+  if ((e = mark(3)) != hipSuccess) return hip_fail(plan, e);
+
+  GemmArgs g3{};
+  g3.A = h_r;
+  g3.B = w->w_down;
+  g3.sB = fp8 ? w->s_down : nullptr;
+  g3.sA = sh_r;
+  g3.K = c.f;
+  g3.N = c.d;
+  g3.T = Ti;
+  g3.E = c.n_experts;
+  g3.offsets = R.offsets;
+  g3.perm = R.perm;
+  g3.C = out;
+  g3.Y = y_s;
+  g3.out_bf16 = c.out_dtype == MOE_BF16;
+  if ((e = launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles)) != hipSuccess)
+    return hip_fail(plan, e);
+  if ((e = mark(4)) != hipSuccess) return hip_fail(plan, e);
+  return MOE_OK;
+}
+
+moe_status moe_forward(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
+                       moe_routing* routing_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return forward_impl(plan, x, T, w, out, routing_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status moe_forward_timed(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
+                             moe_routing* routing_out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, hipEvent_t* events) {
+  if (!events) return MOE_ERR_INVALID_ARGUMENT;
+  return forward_impl(plan, x, T, w, out, routing_out, workspace, workspace_bytes, stream, events);
+}
+
+}  // extern "C"

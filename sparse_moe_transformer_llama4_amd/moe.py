@@ -1,0 +1,292 @@
+"""ctypes binding of libmoe355 (include/moe.h): argument marshalling only.
+
+Every step of the block runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or a call fails, this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libmoe355.so")
+
+MOE_ABI_VERSION = 1
+MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3}
+_TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.uint8}
+
+# names declared in include/moe.h
+symbols = ("moe_plan", "moe_plan_destroy", "moe_workspace_size", "moe_route", "moe_forward",
+           "moe_forward_timed", "moe_status_string", "moe_last_hip_error", "moe_version")
+MOE_NUM_STAGES = 4
+STAGES = ("route", "gate_up", "down_shared", "down_routed")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{what}: {moe_status_string(status)} ({status})"
+        if hip_error:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg)
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("d", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("f", ctypes.c_int32), ("f_shared", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("x_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("has_router_bias", ctypes.c_int32), ("max_tokens", ctypes.c_int64)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_router", "router_bias", "w_gate_up", "s_gate_up", "w_down", "s_down",
+        "ws_gate_up", "ss_gate_up", "ws_down", "ss_down")]
+
+
+class _Routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("expert_idx", "gate", "counts", "offsets", "perm")]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmoe355.so (built in-tree by sparse_moe_transformer_llama4_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libmoe355 not built: {path} is missing "
+                          "(run python -m sparse_moe_transformer_llama4_amd.build)")
+    lib = ctypes.CDLL(path)
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.moe_plan.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(P)]
+    lib.moe_plan.restype = ctypes.c_int
+    lib.moe_plan_destroy.argtypes = [P]
+    lib.moe_plan_destroy.restype = None
+    lib.moe_workspace_size.argtypes = [P, I64, ctypes.POINTER(SZ)]
+    lib.moe_workspace_size.restype = ctypes.c_int
+    lib.moe_route.argtypes = [P, P, I64, ctypes.POINTER(_Weights), ctypes.POINTER(_Routing), P, SZ, P]
+    lib.moe_route.restype = ctypes.c_int
+    lib.moe_forward.argtypes = [P, P, I64, ctypes.POINTER(_Weights), P, ctypes.POINTER(_Routing), P, SZ, P]
+    lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_timed.argtypes = [P, P, I64, ctypes.POINTER(_Weights), P, ctypes.POINTER(_Routing), P, SZ,
+                                      P, ctypes.POINTER(P)]
+    lib.moe_forward_timed.restype = ctypes.c_int
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_hip_error.argtypes = [P]
+    lib.moe_last_hip_error.restype = ctypes.c_int
+    lib.moe_version.argtypes = []
+    lib.moe_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def moe_status_string(status: int) -> str:
+    return load_library().moe_status_string(int(status)).decode()
+
+
+def moe_version() -> str:
+    return load_library().moe_version().decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+class Plan:
+    """Owns a moe_plan_t.  Shapes: d, E, f, fs; dtypes as "f32" / "bf16" / "e4m3"."""
+
+    def __init__(self, d: int, E: int, f: int, fs: int, x_dtype="bf16", w_dtype="bf16",
+                 out_dtype="f32", has_bias=False, max_tokens=65536, top_k=1):
+        lib = load_library()
+        self.cfg = _Config(MOE_ABI_VERSION, d, E, f, fs, top_k, _DT[x_dtype], _DT[w_dtype], _DT[out_dtype],
+                           int(bool(has_bias)), max_tokens)
+        self.d, self.E, self.f, self.fs = d, E, f, fs
+        self.x_dtype, self.w_dtype, self.out_dtype = x_dtype, w_dtype, out_dtype
+        self.has_bias = bool(has_bias)
+        self.handle = ctypes.c_void_p()
+        st = lib.moe_plan(ctypes.byref(self.cfg), ctypes.byref(self.handle))
+        if st != 0:
+            raise MoeError(st, "moe_plan")
+
+    @staticmethod
+    def for_shape(shape, max_tokens=None) -> "Plan":
+        return Plan(shape.d, shape.E, shape.f, shape.fs, shape.x_dtype, shape.w_dtype, shape.out_dtype,
+                    shape.has_bias, max_tokens or max(shape.T, 1))
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.moe_plan_destroy(h)
+            self.handle = None
+
+    def _err(self, st, what):
+        return MoeError(st, what, load_library().moe_last_hip_error(self.handle) if st == -5 else 0)
+
+
+def moe_plan(shape_or_kwargs, **kw) -> Plan:
+    """Create a plan from an object with d, E, f, fs, x_dtype, w_dtype, out_dtype, has_bias, T."""
+    if kw:
+        return Plan(**kw)
+    return Plan.for_shape(shape_or_kwargs)
+
+
+def moe_workspace_size(plan: Plan, T: int) -> int:
+    n = ctypes.c_size_t()
+    st = load_library().moe_workspace_size(plan.handle, int(T), ctypes.byref(n))
+    if st != 0:
+        raise plan._err(st, "moe_workspace_size")
+    return n.value
+
+
+def _weights(w: dict) -> _Weights:
+    return _Weights(*[_ptr(w.get(k)) for k in (
+        "w_router", "router_bias", "w_gate_up", "s_gate_up", "w_down", "s_down",
+        "ws_gate_up", "ss_gate_up", "ws_down", "ss_down")])
+
+
+def new_routing(plan: Plan, T: int, device) -> dict:
+    z = lambda n, dt: torch.empty(max(n, 1), dtype=dt, device=device)
+    return {"expert_idx": z(T, torch.int32), "gate": z(T, torch.float32),
+            "counts": z(plan.E, torch.int32), "offsets": z(plan.E + 1, torch.int32),
+            "perm": z(T, torch.int32)}
+
+
+def _routing(r: Optional[dict]):
+    if r is None:
+        return None
+    return _Routing(*[_ptr(r[k]) for k in ("expert_idx", "gate", "counts", "offsets", "perm")])
+
+
+def _workspace(plan: Plan, T: int, ws: Optional[torch.Tensor], device):
+    need = moe_workspace_size(plan, T)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws
+
+
+def _check_tensor(t: torch.Tensor, name: str, dtype):
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype:
+        raise ValueError(f"{name}: need a contiguous {dtype} device tensor, got {t.dtype} "
+                         f"on {t.device} (contiguous={t.is_contiguous()})")
+
+
+def _check_inputs(plan: Plan, x: torch.Tensor, w: dict):
+    _check_tensor(x, "x", _TORCH_DT[_DT[plan.x_dtype]])
+    if x.dim() != 2 or x.shape[1] != plan.d:
+        raise ValueError(f"x must be [T, {plan.d}]")
+    _check_tensor(w["w_router"], "w_router", _TORCH_DT[_DT[plan.x_dtype]])
+    if tuple(w["w_router"].shape) != (plan.d, plan.E):
+        raise ValueError("w_router shape")
+
+
+def moe_route(plan: Plan, x: torch.Tensor, w: dict, routing: Optional[dict] = None,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Router + top-1 + gate + stable expert grouping; returns the routing dict."""
+    _check_inputs(plan, x, w)
+    T = x.shape[0]
+    routing = routing or new_routing(plan, T, x.device)
+    ws = _workspace(plan, T, workspace, x.device)
+    r = _routing(routing)
+    st = load_library().moe_route(plan.handle, _ptr(x), T, ctypes.byref(_weights(w)), ctypes.byref(r),
+                                  _ptr(ws), ws.numel(), _stream(stream))
+    if st != 0:
+        raise plan._err(st, "moe_route")
+    return routing
+
+
+def moe_forward(plan: Plan, x: torch.Tensor, w: dict, out: Optional[torch.Tensor] = None,
+                routing: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """The whole block: out = shared(x) + routed(x)."""
+    _check_inputs(plan, x, w)
+    T = x.shape[0]
+    wdt = _TORCH_DT[_DT[plan.w_dtype]]
+    for k in ("w_gate_up", "w_down", "ws_gate_up", "ws_down"):
+        _check_tensor(w[k], k, wdt)
+    if out is None:
+        out = torch.empty((T, plan.d), dtype=_TORCH_DT[_DT[plan.out_dtype]], device=x.device)
+    _check_tensor(out, "out", _TORCH_DT[_DT[plan.out_dtype]])
+    ws = _workspace(plan, T, workspace, x.device)
+    r = _routing(routing)
+    st = load_library().moe_forward(plan.handle, _ptr(x), T, ctypes.byref(_weights(w)), _ptr(out),
+                                    ctypes.byref(r) if r is not None else None, _ptr(ws), ws.numel(),
+                                    _stream(stream))
+    if st != 0:
+        raise plan._err(st, "moe_forward")
+    return out
+
+
+# ------------------------------------------------------------------ stage timing
+
+_hip = None
+
+
+def _hip_runtime():
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        _hip = h
+    return _hip
+
+
+class StageEvents:
+    """MOE_NUM_STAGES + 1 hipEvents for moe_forward_timed."""
+
+    def __init__(self):
+        h = _hip_runtime()
+        self.ev = (ctypes.c_void_p * (MOE_NUM_STAGES + 1))()
+        for i in range(MOE_NUM_STAGES + 1):
+            e = ctypes.c_void_p()
+            if h.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev[i] = e
+        self.h = h
+
+    def durations_ms(self):
+        """Per-stage durations of the last recorded call (synchronises on the last event)."""
+        self.h.hipEventSynchronize(self.ev[MOE_NUM_STAGES])
+        out = []
+        for i in range(MOE_NUM_STAGES):
+            ms = ctypes.c_float()
+            self.h.hipEventElapsedTime(ctypes.byref(ms), self.ev[i], self.ev[i + 1])
+            out.append(ms.value)
+        return out
+
+    def __del__(self):
+        for i in range(MOE_NUM_STAGES + 1):
+            if self.ev[i]:
+                self.h.hipEventDestroy(self.ev[i])
+
+
+def moe_forward_timed(plan: Plan, x: torch.Tensor, w: dict, events: StageEvents, out: torch.Tensor,
+                      workspace: torch.Tensor, routing: Optional[dict] = None, stream=None) -> torch.Tensor:
+    """moe_forward that records `events` at the stage boundaries."""
+    T = x.shape[0]
+    r = _routing(routing)
+    st = load_library().moe_forward_timed(plan.handle, _ptr(x), T, ctypes.byref(_weights(w)), _ptr(out),
+                                          ctypes.byref(r) if r is not None else None, _ptr(workspace),
+                                          workspace.numel(), _stream(stream), events.ev)
+    if st != 0:
+        raise plan._err(st, "moe_forward_timed")
+    return out

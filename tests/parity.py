@@ -1,0 +1,73 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI
+and compare it with the oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+from oracle import block
+
+TOL = {"f32": 1e-4, "bf16": 1e-2, "e4m3": 5e-2}
+
+
+def to_device(inp: dict, device) -> dict:
+    return {k: (None if v is None else v.to(device)) for k, v in inp.items()}
+
+
+def run_gpu(plan, x, w, poison_ws=True, T=None):
+    from sparse_moe_transformer_llama4_amd import moe
+    T = x.shape[0] if T is None else T
+    routing = moe.new_routing(plan, T, x.device)
+    for v in routing.values():
+        v.fill_(-7 if v.dtype == torch.int32 else float("nan"))
+    ws = torch.empty(max(moe.moe_workspace_size(plan, T), 256), dtype=torch.uint8, device=x.device)
+    if poison_ws:
+        ws.fill_(0xFF)  # NaN for every float view, -1 for int32
+    out = moe.moe_forward(plan, x, w, routing=routing, workspace=ws)
+    torch.cuda.synchronize()
+    return out, routing
+
+
+def check_routing(cfg, r_or: block.Routing, routing: dict, rows=None):
+    """Bit-exact routing rules: GPU record self-consistent, and equal to the
+    oracle on every token whose top-2 margin exceeds 1e-3."""
+    T, E = len(r_or.idx), cfg.E
+    idx = routing["expert_idx"][:T].cpu().numpy().astype(np.int64)
+    assert ((idx >= 0) & (idx < E)).all()
+    counts, offsets, perm, _ = block.routing_record(idx, E)
+    np.testing.assert_array_equal(routing["counts"][:E].cpu().numpy(), counts)
+    np.testing.assert_array_equal(routing["offsets"][:E + 1].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(routing["perm"][:T].cpu().numpy(), perm)
+    far = r_or.margin > block.NEAR_TIE
+    np.testing.assert_array_equal(idx[far], r_or.idx[far])
+    mx = r_or.logits.max(axis=1)
+    chosen = r_or.logits[np.arange(T), idx]
+    assert (chosen >= mx - block.NEAR_TIE).all()
+    if far.all():
+        np.testing.assert_array_equal(counts, r_or.counts)
+        np.testing.assert_array_equal(perm, r_or.perm)
+    gate = routing["gate"][:T].cpu().double().numpy()
+    np.testing.assert_allclose(gate, block.sigmoid(chosen), rtol=0, atol=2e-6)
+    return idx
+
+
+def output_error(cfg, out_gpu, ref):
+    """max over elements of (|gpu - ref| - half a bf16 ulp of ref for bf16 outputs) / RMS(ref)."""
+    g = out_gpu.detach().cpu().double().numpy()
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    slack = np.abs(ref) * 2.0 ** -9 if cfg.out_dtype == "bf16" else 0.0
+    return float(np.max(np.maximum(np.abs(g - ref) - slack, 0.0)) / rms)
+
+
+def check_forward(cfg, inp_cpu: dict, out_gpu, routing, tol=None):
+    w = block.Weights.from_dict(inp_cpu)
+    wr, b = w.router()
+    r = block.route(inp_cpu["x"], wr, b)
+    idx = check_routing(cfg, r, routing)
+    gate = block.sigmoid(r.logits[np.arange(len(idx)), idx])
+    ref = block.combine(inp_cpu["x"], idx, gate, w, cfg.f, cfg.fs, cfg.w_dtype)
+    err = output_error(cfg, out_gpu, ref)
+    assert err <= (tol or TOL[cfg.w_dtype]), f"{cfg.name}: max|err|/RMS = {err:.3e}"
+    return err, r

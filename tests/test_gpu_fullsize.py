@@ -1,0 +1,82 @@
+"""The five workloads at full size, in the launch configuration bench.py times.
+
+Routing is compared with the oracle on every token (bit-exact rules); the
+output is compared on sampled tokens that the oracle computes one by one:
+tokens of the hottest expert and of the expert of token 0, plus the shared
+expert for each.  Inputs are generated on the GPU for the HIP path and on
+the CPU for the oracle by the same counter-based generator."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import block
+from parity import TOL, check_routing, output_error
+
+pytestmark = pytest.mark.gpu
+
+
+def test_generator_gpu_equals_cpu(gpu):
+    for name in ("small_bf16", "small_fp8", "small_fp32", "small_bf16_bias"):
+        cfg = synth.get_config(name)
+        a = synth.make_inputs(cfg, "cpu")
+        b = synth.make_inputs(cfg, gpu)
+        for k, v in a.items():
+            if v is None:
+                assert b[k] is None
+            else:
+                assert torch.equal(v, b[k].cpu()), (name, k)
+    cfg = synth.CONFIGS["maverick_prefill_fp8"]
+    assert torch.equal(synth.gen_x(cfg, "cpu", rows=slice(5000, 5004)),
+                       synth.gen_x(cfg, gpu, rows=slice(5000, 5004)).cpu())
+    w_c = synth.gen_expert(cfg, 77, "cpu")
+    w_g = synth.gen_expert(cfg, 77, gpu)
+    for u, v in zip(w_c, w_g):
+        assert torch.equal(u, v.cpu())
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "scout_decode_bf16", "scout_prefill_bf16",
+                                  "maverick_prefill_bf16", "maverick_prefill_fp8"])
+def test_fullsize_sampled(gpu, name):
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = synth.get_config(name)
+    print(f"[full] {name}: generating on GPU", flush=True)
+    g = synth.make_inputs(cfg, gpu)
+    plan = moe.Plan.for_shape(cfg)
+    routing = moe.new_routing(plan, cfg.T, gpu)
+    ws = torch.full((moe.moe_workspace_size(plan, cfg.T),), 0xFF, dtype=torch.uint8, device=gpu)
+    out = moe.moe_forward(plan, g["x"], g, routing=routing, workspace=ws)
+    torch.cuda.synchronize()
+    out_cpu = out.cpu()
+    routing = {k: v.cpu() for k, v in routing.items()}
+    del g, ws, out
+    gc.collect()
+    torch.cuda.empty_cache()
+
+    print(f"[full] {name}: oracle routing on all {cfg.T} tokens", flush=True)
+    x = synth.gen_x(cfg, "cpu")
+    r = block.route(x, synth.gen_router(cfg, "cpu"), synth.gen_bias(cfg))
+    idx = check_routing(cfg, r, routing)
+
+    counts = np.bincount(idx, minlength=cfg.E)
+    experts = [int(np.argmax(counts)), int(idx[0])]
+    if experts[0] == experts[1]:
+        nz = np.nonzero(counts)[0]
+        experts[1] = int(nz[np.argmin(counts[nz])])
+    toks = []
+    for e in experts:
+        grp = np.nonzero(idx == e)[0]
+        toks += sorted(set([grp[0], grp[len(grp) // 2], grp[-1]]))
+    toks = np.array(sorted(set(toks)))
+    print(f"[full] {name}: oracle output on tokens {toks.tolist()} (experts {experts})", flush=True)
+    cache = {e: synth.gen_expert(cfg, e, "cpu") for e in experts}
+    shared = synth.gen_shared(cfg, "cpu")
+    w = block.Weights(lambda: None, lambda e: cache[e], lambda: shared)
+    gate = block.sigmoid(r.logits[toks, idx[toks]])
+    ref = block.combine(x[toks], idx[toks], gate, w, cfg.f, cfg.fs, cfg.w_dtype)
+    err = output_error(cfg, out_cpu[toks], ref)
+    print(f"[full] {name}: sampled max|err|/RMS = {err:.3e}", flush=True)
+    assert err <= TOL[cfg.w_dtype]
+    assert torch.isfinite(out_cpu.float()).all()

@@ -1,0 +1,137 @@
+"""HIP path vs the oracle, element by element, through the C ABI (needs a GPU)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import block
+from parity import check_forward, run_gpu, to_device, output_error
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = ["tiny_fp32", "small_fp32", "small_bf16", "small_bf16_bias", "small_bf16_out16",
+          "decode_like_bf16", "small_fp8"]
+
+
+def _plan(cfg, **kw):
+    from sparse_moe_transformer_llama4_amd import moe
+    return moe.Plan.for_shape(cfg, **kw)
+
+
+@pytest.mark.parametrize("name", SHAPES)
+def test_forward_matches_oracle(gpu, name):
+    cfg = synth.get_config(name)
+    print(f"[parity] {name} T={cfg.T} d={cfg.d} E={cfg.E} f={cfg.f} fs={cfg.fs} {cfg.w_dtype}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    err, _ = check_forward(cfg, inp, out, routing)
+    print(f"[parity] {name} max|err|/RMS = {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "small_fp32", "small_fp8"])
+def test_deterministic(gpu, name):
+    cfg = synth.get_config(name)
+    inp = to_device(synth.make_inputs(cfg), gpu)
+    p = _plan(cfg)
+    o1, r1 = run_gpu(p, inp["x"], inp)
+    o2, r2 = run_gpu(p, inp["x"], inp, poison_ws=False)
+    assert torch.equal(o1, o2)
+    for k in r1:
+        assert torch.equal(r1[k], r2[k])
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 63, 64, 65, 129])
+def test_ragged_token_counts(gpu, T):
+    cfg = dataclasses.replace(synth.get_config("small_bf16"), T=T, name=f"ragged{T}")
+    print(f"[parity] ragged T={T}", flush=True)
+    inp = synth.make_inputs(cfg)
+    out, routing = run_gpu(_plan(cfg), inp["x"].to(gpu), to_device(inp, gpu))
+    check_forward(cfg, inp, out, routing)
+
+
+def test_zero_tokens(gpu):
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = synth.get_config("small_bf16")
+    inp = to_device(synth.make_inputs(cfg), gpu)
+    p = _plan(cfg)
+    x0 = inp["x"][:0]
+    routing = moe.new_routing(p, 0, gpu)
+    routing["counts"].fill_(5)
+    routing["offsets"].fill_(5)
+    out = moe.moe_forward(p, x0, inp, routing=routing)
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.d)
+    assert (routing["counts"] == 0).all() and (routing["offsets"] == 0).all()
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32", "e4m3"])
+def test_all_tokens_to_one_expert(gpu, dt):
+    base = {"bf16": "small_bf16", "f32": "small_fp32", "e4m3": "small_fp8"}[dt]
+    cfg = dataclasses.replace(synth.get_config(base), bias="cold", n_cold=0)
+    inp = synth.make_inputs(cfg)
+    hot = cfg.E - 2
+    inp["router_bias"] = torch.full((cfg.E,), -50.0)
+    inp["router_bias"][hot] = 50.0
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    check_forward(cfg, inp, out, routing)
+    assert int(routing["counts"][hot]) == cfg.T
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32", "e4m3"])
+def test_idle_experts_nan_poisoned(gpu, dt):
+    base = {"bf16": "small_bf16", "f32": "small_fp32", "e4m3": "small_fp8"}[dt]
+    cfg = dataclasses.replace(synth.get_config(base), bias="cold", n_cold=0)
+    inp = synth.make_inputs(cfg)
+    bias = torch.full((cfg.E,), -40.0)
+    bias[1] = bias[3] = 0.0
+    inp["router_bias"] = bias
+    g = to_device(inp, gpu)
+    p = _plan(cfg)
+    out1, r1 = run_gpu(p, g["x"], g)
+    used = set(torch.unique(r1["expert_idx"][:cfg.T]).tolist())
+    assert used <= {1, 3}
+    for e in range(cfg.E):
+        if e not in used:
+            if dt == "e4m3":
+                g["w_gate_up"][e].fill_(0x7F); g["w_down"][e].fill_(0x7F)
+            else:
+                g["w_gate_up"][e].fill_(float("nan")); g["w_down"][e].fill_(float("nan"))
+    out2, _ = run_gpu(p, g["x"], g)
+    assert torch.equal(out1, out2)
+    check_forward(cfg, inp, out2, r1)
+
+
+def test_zero_router_gate_half_expert0(gpu):
+    cfg = synth.get_config("small_bf16")
+    inp = synth.make_inputs(cfg)
+    inp["w_router"].zero_()
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    assert (routing["expert_idx"][:cfg.T] == 0).all()
+    assert (routing["gate"][:cfg.T] == 0.5).all()
+    check_forward(cfg, inp, out, routing)
+
+
+def test_single_expert(gpu):
+    cfg = dataclasses.replace(synth.get_config("small_bf16"), E=1, name="e1")
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    check_forward(cfg, inp, out, routing)
+
+
+def test_route_only_entry_point(gpu):
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = synth.get_config("small_bf16_bias")
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    r = moe.moe_route(_plan(cfg), g["x"], g)
+    torch.cuda.synchronize()
+    w = block.Weights.from_dict(inp)
+    ro = block.route(inp["x"], *w.router())
+    from parity import check_routing
+    check_routing(cfg, ro, r)
