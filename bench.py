@@ -185,7 +185,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or min(cfg.T, 512 if cfg.E <= 16 else 192)
+        sample = args.cpu_sample or min(cfg.T, 4096 if cfg.E <= 16 else 512)
         print(f"[bench] cpu oracle on {sample} tokens", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, g, sample)
     else:

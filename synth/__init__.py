@@ -95,7 +95,7 @@ TEST_SHAPES = {
                                 bias="zipf", zipf_alpha=0.6, seed=13),
     "small_bf16_out16": MoEShape("small_bf16_out16", T=257, d=256, E=4, f=128, fs=192,
                                  out_dtype="bf16", seed=14),
-    "small_fp8": MoEShape("small_fp8", T=650, d=512, E=8, f=256, fs=384,
+    "small_fp8": MoEShape("small_fp8", T=650, d=1024, E=8, f=8192, fs=8064,
                           w_dtype="e4m3", out_dtype="bf16", seed=15),
     "decode_like_bf16": MoEShape("decode_like_bf16", T=32, d=1024, E=16, f=512, fs=512,
                                  bias="cold", seed=16),
