@@ -37,8 +37,11 @@ follow the data types of the workloads):
   R0 (e4m3 weights): per token, s_x = fp32(max_j |x[t, j]|) / 448 in float32
      (1 for an all-zero row), q = e4m3(fp32(x) / s_x); the shared expert sees
      q * s_x and the routed expert q * (g * s_x).
-  R1 (e4m3 weights): h is first rounded to bf16 as above, then quantised per
-     token exactly like R0 (scale from the bf16 row's max magnitude).
+  R1 (e4m3 weights): h is quantised per token exactly like R0, from its
+     float32 value: s_h = fp32(max_j |h[t, j]|) / 448, code = e4m3(fp32(h) / s_h).
+     (A bf16 intermediate is deliberately absent: a scale taken from a
+     bf16-rounded row lets a one-ulp difference in the row's largest element
+     re-round every code of that row.)
   The output itself is returned unrounded in float64.
 """
 from __future__ import annotations
@@ -156,11 +159,10 @@ def round_h(h: np.ndarray, mode: str) -> np.ndarray:
     """Rounding point R1 applied to SwiGLU outputs (rows = tokens)."""
     if mode == "f32":
         return h
-    hb = bf16_round(h.astype(np.float32))
     if mode == "bf16":
-        return hb
+        return bf16_round(h.astype(np.float32))
     if mode == "e4m3":
-        return quant_rows_e4m3(hb.astype(np.float32))[0]
+        return quant_rows_e4m3(h.astype(np.float32))[0]
     raise ValueError(mode)
 
 

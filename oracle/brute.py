@@ -60,10 +60,10 @@ def _swiglu_mlp(u, wgu, wd, width, mode, scale=1.0):
     for j in range(width):
         z = a[j]
         h.append(z / (1.0 + math.exp(-z)) * a[width + j])
-    if mode in ("bf16", "e4m3"):
+    if mode == "bf16":
         h = [_bf16(v) for v in h]
     if mode == "e4m3":
-        h, _ = _quant_row(h)
+        h, _ = _quant_row([_f32(v) for v in h])
     return _matvec(h, wd)
 
 
