@@ -100,10 +100,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     rows = T;
     if (m0 >= T) return;
   } else {
-    const int G = GATEUP ? E + 1 : E;
-    const int mt = blockIdx.x;
-    if (mt >= p.tiles[G]) return;
-    int lo = 0, hi = G - 1;
+    const int mt = blockIdx.x + p.tiles[p.group_lo];
+    if (mt >= p.tiles[p.group_hi]) return;
+    int lo = p.group_lo, hi = p.group_hi - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
@@ -265,12 +264,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
           if (valid) {
             void* C = shared ? p.C_shared : p.C;
             const int64_t o = static_cast<int64_t>(orow) * NH + col;
-            if constexpr (DT == DT_F32) {
-              reinterpret_cast<float*>(C)[o] = h;
+            if constexpr (DT == DT_BF16) {
+              reinterpret_cast<uint16_t*>(C)[o] = f32_to_bf16(h);
             } else {
-              const uint16_t hb = f32_to_bf16(h);
-              reinterpret_cast<uint16_t*>(C)[o] = hb;
-              rmax = fmaxf(rmax, fabsf(bf16_to_f32(hb)));
+              // fp32 h; e4m3 rows are quantised afterwards from these values
+              reinterpret_cast<float*>(C)[o] = h;
+              rmax = fmaxf(rmax, fabsf(h));
             }
           }
         }
@@ -323,15 +322,17 @@ static hipError_t launch_one(const GemmArgs& a0, int grid_m_tokens, hipStream_t 
   a.tiles = tiles_all + bm_index(BM) * (a.E + 2);
   int gm, nmax;
   constexpr int BNH = MODE == MODE_GATEUP ? BN / 2 : BN;
+  const bool has_routed = a.group_lo < a.E;
+  const bool has_shared = a.group_hi > a.E;
+  const int mt_tok = (grid_m_tokens + BM - 1) / BM;
   if constexpr (MODE == MODE_DOWN_SHARED) {
-    gm = (grid_m_tokens + BM - 1) / BM;
+    gm = mt_tok;
     nmax = a.N;
-  } else if constexpr (MODE == MODE_GATEUP) {
-    gm = 2 * ((grid_m_tokens + BM - 1) / BM) + a.E;  // >= sum_g ceil(n_g/BM) + ceil(T/BM)
-    nmax = a.N > a.N_shared ? a.N : a.N_shared;
   } else {
-    gm = (grid_m_tokens + BM - 1) / BM + a.E;
+    // sum over routed groups of ceil(n_g / BM) <= ceil(T / BM) + E; the shared group adds ceil(T / BM)
+    gm = (has_routed ? mt_tok + a.E : 0) + (has_shared ? mt_tok : 0);
     nmax = a.N;
+    if (MODE == MODE_GATEUP) nmax = max(has_routed ? a.N : 0, has_shared ? a.N_shared : 0);
   }
   const int gn = (nmax + BNH - 1) / BNH;
   if (gm <= 0 || gn <= 0) return hipSuccess;

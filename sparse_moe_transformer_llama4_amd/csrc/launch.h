@@ -53,6 +53,7 @@ struct GemmArgs {
   uint32_t* amax;        // e4m3 GATEUP: per-row max |h| bits (routed rows)
   uint32_t* amax_shared;
   int out_bf16;          // DOWN_ROUTED: output dtype bf16 (else fp32)
+  int group_lo, group_hi;  // groups [lo, hi) handled by this launch (group E = shared expert)
 };
 
 hipError_t launch_router(const RouterArgs& a, int x_dtype, hipStream_t s);
@@ -60,7 +61,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_perm(const int32_t* idx, const int32_t* base, int T, int E, int32_t* perm,
                        hipStream_t s);
 hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* sx, hipStream_t s);
-hipError_t launch_quant_h(const uint16_t* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
+hipError_t launch_quant_h(const float* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
                           float* sh, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 
@@ -68,5 +69,10 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 // workgroups exit after reading the tile table.
 hipError_t launch_gemm(int mode, int w_dtype, const GemmArgs& a, int grid_m_tokens, hipStream_t s,
                        const int32_t* tiles_all);
+
+// bf16 prefill tiling (BM in {64, 128, 256} rows x 256 weight columns).
+bool bf16_v2_supported(int K, int N, int N_shared);
+hipError_t launch_gemm_bf16_v2(int mode, int bm, const GemmArgs& a, int T, hipStream_t s,
+                               const int32_t* tiles_all);
 
 }  // namespace moe

@@ -47,7 +47,7 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   const size_t t = static_cast<size_t>(T);
   const size_t nb = (t + kRouteTokens - 1) / kRouteTokens;
   const bool fp8 = c.w_dtype == MOE_E4M3;
-  const size_t hsz = c.w_dtype == MOE_F32 ? 4 : 2;
+  const size_t hsz = c.w_dtype == MOE_BF16 ? 2 : 4;  // e4m3: fp32 staging before quantisation
   L.idx = take(t * 4);
   L.gate = take(t * 4);
   L.counts = take(E * 4);
@@ -125,6 +125,17 @@ Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
   o.hist = reinterpret_cast<int32_t*>(ws + L.hist);
   o.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   return o;
+}
+
+// Token counts from which the bf16 prefill tiling is used.
+constexpr int64_t kPrefillTokens = 256;
+
+// Tile height for the routed groups: the mean group size decides between
+// 256-, 128- and 64-row tiles (a taller tile reuses each weight tile for more
+// rows; a shorter one wastes fewer MFMA rows on ragged group tails).
+int routed_tile_rows(int64_t T, int E) {
+  const int64_t mean = T / E;
+  return mean >= 192 ? 256 : mean >= 96 ? 128 : 64;
 }
 
 // Router + scan + permutation.
@@ -268,7 +279,23 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g1.C_shared = ws + L.h_s;
   g1.amax = amax_r;
   g1.amax_shared = amax_s;
-  if ((e = launch_gemm(MODE_GATEUP, c.w_dtype, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
+  const bool v2 = c.w_dtype == MOE_BF16 && T >= kPrefillTokens && bf16_v2_supported(c.d, c.f, c.f_shared) &&
+                  bf16_v2_supported(c.f, c.d, c.d) && bf16_v2_supported(c.f_shared, c.d, c.d);
+  const int bm_routed = routed_tile_rows(T, c.n_experts);
+  if (v2) {
+    g1.group_lo = 0;
+    g1.group_hi = c.n_experts;
+    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_routed, g1, Ti, stream, R.tiles)) != hipSuccess)
+      return hip_fail(plan, e);
+    g1.group_lo = c.n_experts;
+    g1.group_hi = c.n_experts + 1;
+    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, 256, g1, Ti, stream, R.tiles)) != hipSuccess)
+      return hip_fail(plan, e);
+  } else {
+    g1.group_lo = 0;
+    g1.group_hi = c.n_experts + 1;
+    if ((e = launch_gemm(MODE_GATEUP, c.w_dtype, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
+  }
   if ((e = mark(2)) != hipSuccess) return hip_fail(plan, e);
 
   const void* h_r = ws + L.h_r;
@@ -277,10 +304,10 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   if (fp8) {
     sh_r = reinterpret_cast<float*>(ws + L.sh_r);
     sh_s = reinterpret_cast<float*>(ws + L.sh_s);
-    if ((e = launch_quant_h(reinterpret_cast<const uint16_t*>(ws + L.h_r), amax_r, Ti, c.f, ws + L.hq_r, sh_r,
+    if ((e = launch_quant_h(reinterpret_cast<const float*>(ws + L.h_r), amax_r, Ti, c.f, ws + L.hq_r, sh_r,
                             stream)) != hipSuccess)
       return hip_fail(plan, e);
-    if ((e = launch_quant_h(reinterpret_cast<const uint16_t*>(ws + L.h_s), amax_s, Ti, c.f_shared, ws + L.hq_s,
+    if ((e = launch_quant_h(reinterpret_cast<const float*>(ws + L.h_s), amax_s, Ti, c.f_shared, ws + L.hq_s,
                             sh_s, stream)) != hipSuccess)
       return hip_fail(plan, e);
     h_r = ws + L.hq_r;
@@ -299,8 +326,11 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g2.E = c.n_experts;
   g2.offsets = R.offsets;
   g2.C_shared = y_s;
-  if ((e = launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles)) != hipSuccess)
-    return hip_fail(plan, e);
+  g2.group_lo = c.n_experts;
+  g2.group_hi = c.n_experts + 1;
+  e = v2 ? launch_gemm_bf16_v2(MODE_DOWN_SHARED, 256, g2, Ti, stream, R.tiles)
+         : launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles);
+  if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(plan, e);
 
   GemmArgs g3{};
@@ -317,8 +347,11 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g3.C = out;
   g3.Y = y_s;
   g3.out_bf16 = c.out_dtype == MOE_BF16;
-  if ((e = launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles)) != hipSuccess)
-    return hip_fail(plan, e);
+  g3.group_lo = 0;
+  g3.group_hi = c.n_experts;
+  e = v2 ? launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_routed, g3, Ti, stream, R.tiles)
+         : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
+  if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(4)) != hipSuccess) return hip_fail(plan, e);
   return MOE_OK;
 }

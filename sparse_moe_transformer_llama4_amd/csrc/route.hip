@@ -194,8 +194,9 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* x, int T, 
   }
 }
 
-// Per-row e4m3 quantisation of bf16 h rows with a precomputed row max.
-__global__ __launch_bounds__(256) void quant_h_kernel(const uint16_t* h, const uint32_t* amax, int rows,
+// Per-row e4m3 quantisation of fp32 h rows with a precomputed row max:
+// s = max|h| / 448 (1 for a zero row), code = e4m3(h / s).
+__global__ __launch_bounds__(256) void quant_h_kernel(const float* h, const uint32_t* amax, int rows,
                                                       int n, uint8_t* hq, float* sh) {
   const int r = blockIdx.x;
   if (r >= rows) return;
@@ -204,16 +205,13 @@ __global__ __launch_bounds__(256) void quant_h_kernel(const uint16_t* h, const u
   if (blockIdx.y == 0 && threadIdx.x == 0) sh[r] = s;
   const int k = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (k >= n) return;
-  const uint4 v = *reinterpret_cast<const uint4*>(h + static_cast<int64_t>(r) * n + k);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    lo |= f32_to_e4m3(__uint_as_float(w[i] << 16) / s) << (16 * i);
-    lo |= f32_to_e4m3(__uint_as_float(w[i] & 0xFFFF0000u) / s) << (16 * i + 8);
-    hi |= f32_to_e4m3(__uint_as_float(w[i + 2] << 16) / s) << (16 * i);
-    hi |= f32_to_e4m3(__uint_as_float(w[i + 2] & 0xFFFF0000u) / s) << (16 * i + 8);
-  }
+  const float* src = h + static_cast<int64_t>(r) * n + k;
+  const float4 v0 = *reinterpret_cast<const float4*>(src);
+  const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+  const uint32_t lo = f32_to_e4m3(v0.x / s) | (f32_to_e4m3(v0.y / s) << 8) | (f32_to_e4m3(v0.z / s) << 16) |
+                      (f32_to_e4m3(v0.w / s) << 24);
+  const uint32_t hi = f32_to_e4m3(v1.x / s) | (f32_to_e4m3(v1.y / s) << 8) | (f32_to_e4m3(v1.z / s) << 16) |
+                      (f32_to_e4m3(v1.w / s) << 24);
   *reinterpret_cast<uint2*>(hq + static_cast<int64_t>(r) * n + k) = make_uint2(lo, hi);
 }
 
@@ -325,7 +323,7 @@ hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* s
   return hipGetLastError();
 }
 
-hipError_t launch_quant_h(const uint16_t* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
+hipError_t launch_quant_h(const float* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
                           float* sh, hipStream_t s) {
   hipLaunchKernelGGL(quant_h_kernel, dim3(rows, (n + 2047) / 2048), dim3(256), 0, s, h, amax, rows, n,
                      hq, sh);
