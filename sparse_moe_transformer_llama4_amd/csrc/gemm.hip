@@ -157,25 +157,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     b_src[i] = bbase + (static_cast<int64_t>(k) * ldb + (b_ok[i] ? gc : 0)) * ES;
   }
 
-  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
+  i32x4 ra[A_CHUNKS], rb[B_CHUNKS];   // native vectors stay in VGPRs
   auto load_tiles = [&](int kt) {
     const int64_t koff = static_cast<int64_t>(kt) * kKBytes;
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + koff);
+    for (int i = 0; i < A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const i32x4*>(a_src[i] + koff);
     const int64_t kboff = static_cast<int64_t>(kt) * BK * ldb * ES;
 #pragma unroll
     for (int i = 0; i < B_CHUNKS; ++i)
-      rb[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(b_src[i] + kboff) : make_uint4(0, 0, 0, 0);
+      rb[i] = b_ok[i] ? *reinterpret_cast<const i32x4*>(b_src[i] + kboff) : i32x4{0, 0, 0, 0};
   };
   auto store_tiles = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
       const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(&As[buf][(c >> 3) * kPitch + (c & 7) * 16]) = ra[i];
+      *reinterpret_cast<i32x4*>(&As[buf][(c >> 3) * kPitch + (c & 7) * 16]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_CHUNKS; ++i) {
-      const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
+      const uint32_t w[4] = {static_cast<uint32_t>(rb[i][0]), static_cast<uint32_t>(rb[i][1]),
+                             static_cast<uint32_t>(rb[i][2]), static_cast<uint32_t>(rb[i][3])};
       uint8_t* dst = &Bs[buf][b_col[i] * kPitch + b_k[i] * ES];
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {

@@ -48,8 +48,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int FN = BN / WN / 16;
   constexpr bool GATEUP = MODE == MODE_GATEUP;
   constexpr int BNH = GATEUP ? BN / 2 : BN;
-  constexpr int A_CH = BM * BK * 2 / 16 / 256;   // 16-byte chunks per thread
-  constexpr int B_CH = BK * BN * 2 / 16 / 256;
+  constexpr int A_CH = BM * BK * 2 / 16 / 256;   // 16-byte chunks per thread (rows tid/8 + 32 i)
+  constexpr int B_CH = BK * BN * 2 / 16 / 256;   // (K rows tid/32 + 8 i)
+  static_assert(B_CH == 8, "weight chunk layout");
   static_assert(WM * WN == 4, "4 waves");
   static_assert(!GATEUP || FN % 2 == 0, "gate/up fragment pairs");
 
@@ -86,89 +87,71 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   const int row_base = shared ? 0 : p.offsets[g];
   const int ldb = GATEUP ? 2 * NH : NH;
 
-  // ---- global sources
-  const uint8_t* a_src[A_CH];
+  // ---- global sources.  A: 8 chunks of 16 bytes per row, rows (tid>>3) + 32*i
+  // (gathered through perm for the routed gate/up groups), kept as 32-bit
+  // element offsets.  Weights: every chunk of this thread sits in the same
+  // tile column, rows (tid>>5) + 8*i, so one base address and a row stride
+  // serve all of them.
+  const uint16_t* abase;
+  if constexpr (GATEUP) abase = reinterpret_cast<const uint16_t*>(shared ? p.A_shared : p.A);
+  else if constexpr (MODE == MODE_DOWN_SHARED) abase = reinterpret_cast<const uint16_t*>(p.A_shared);
+  else abase = reinterpret_cast<const uint16_t*>(p.A);
+  uint32_t a_off[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * 256;
-    const int r = min(m0 + (c >> 3), rows - 1);
-    int64_t arow;
-    const uint8_t* base;
-    if constexpr (GATEUP) {
-      arow = shared ? r : p.perm[row_base + r];
-      base = reinterpret_cast<const uint8_t*>(shared ? p.A_shared : p.A);
-    } else if constexpr (MODE == MODE_DOWN_SHARED) {
-      arow = r;
-      base = reinterpret_cast<const uint8_t*>(p.A_shared);
-    } else {
-      arow = row_base + r;
-      base = reinterpret_cast<const uint8_t*>(p.A);
-    }
-    a_src[i] = base + arow * static_cast<int64_t>(K) * 2 + (c & 7) * 16;
+    const int r = min(m0 + (tid >> 3) + 32 * i, rows - 1);
+    int arow;
+    if constexpr (GATEUP) arow = shared ? r : p.perm[row_base + r];
+    else if constexpr (MODE == MODE_DOWN_SHARED) arow = r;
+    else arow = row_base + r;
+    a_off[i] = static_cast<uint32_t>(arow) * static_cast<uint32_t>(K) + (tid & 7) * 8;
   }
-  const uint8_t* bbase = reinterpret_cast<const uint8_t*>(shared ? p.B_shared : p.B) +
-                         (shared ? 0 : static_cast<int64_t>(g) * K * ldb * 2);
-  const uint8_t* b_src[B_CH];
-  bool b_ok[B_CH];
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * 256;
-    const int k = c >> 5;              // 32 chunks of 8 columns per K row
-    const int lc = (c & 31) * 8;       // tile column
-    int gc;
-    if constexpr (GATEUP) gc = lc < BNH ? n0 + lc : NH + n0 + (lc - BNH);
-    else gc = n0 + lc;
-    b_ok[i] = n0 + (GATEUP ? lc % BNH : lc) < NH;
-    b_src[i] = bbase + (static_cast<int64_t>(k) * ldb + (b_ok[i] ? gc : 0)) * 2;
-  }
+  const int lcB = (tid & 31) * 8;   // tile column of this thread's weight chunks
+  int gcB;
+  if constexpr (GATEUP) gcB = lcB < BNH ? n0 + lcB : NH + n0 + (lcB - BNH);
+  else gcB = n0 + lcB;
+  const bool b_ok = n0 + (GATEUP ? lcB % BNH : lcB) < NH;
+  const uint16_t* bptr = reinterpret_cast<const uint16_t*>(shared ? p.B_shared : p.B) +
+                         (shared ? 0 : static_cast<int64_t>(g) * K * ldb) +
+                         static_cast<int64_t>(tid >> 5) * ldb + (b_ok ? gcB : 0);
+  const int64_t b_rstride = static_cast<int64_t>(8) * ldb;     // 8 K rows between this thread's chunks
+  const int64_t b_kstride = static_cast<int64_t>(BK) * ldb;    // one K stage
 
-  uint4 ra[A_CH], rb[B_CH];
-  const int64_t b_kstride = static_cast<int64_t>(BK) * ldb * 2;
-  auto load_tiles = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + kt * (BK * 2));
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i)
-      rb[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(b_src[i] + kt * b_kstride) : make_uint4(0, 0, 0, 0);
-  };
-  auto store_tiles = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(&As[buf][(c >> 3) * A_PITCH + (c & 7) * 16]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(&Bs[buf][(c >> 5) * B_PITCH + (c & 31) * 16]) = rb[i];
-    }
-  };
-
+  i32x4 ra[A_CH], rb[B_CH];   // native vectors: kept in VGPRs (HIP's uint4 struct is not)
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // tile column of this wave's fragment j
-  auto frag_col = [&](int j) -> int {
-    if constexpr (GATEUP) {
-      constexpr int HF = FN / 2;
-      return (j < HF ? 0 : BNH) + wn * (BNH / WN) + (j % HF) * 16;
-    } else {
-      return wn * (BN / WN) + j * 16;
-    }
-  };
-
   const int nk = K / BK;
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
   const int lrow = lane & 15;
   const int lkb = (lane >> 4) * 8;   // this lane's K offset inside a 32-wide MFMA step
+  uint8_t* const a_st = &As[0][(tid >> 3) * A_PITCH + (tid & 7) * 16];
+  uint8_t* const b_st = &Bs[0][(tid >> 5) * B_PITCH + (tid & 31) * 16];
+
+#define MOE_LOAD_STAGE(kt)                                                                     \
+  do {                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                           \
+      ra[i] = *reinterpret_cast<const i32x4*>(abase + a_off[i] + (kt) * BK);                   \
+    const uint16_t* bp_ = bptr + (kt) * b_kstride;                                             \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                           \
+      rb[i] = b_ok ? *reinterpret_cast<const i32x4*>(bp_ + i * b_rstride) : i32x4{0, 0, 0, 0};     \
+  } while (0)
+#define MOE_STORE_STAGE(buf)                                                                   \
+  do {                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                           \
+      *reinterpret_cast<i32x4*>(a_st + (buf) * (BM * A_PITCH) + i * 32 * A_PITCH) = ra[i];     \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                           \
+      *reinterpret_cast<i32x4*>(b_st + (buf) * (BK * B_PITCH) + i * 8 * B_PITCH) = rb[i];      \
+  } while (0)
+
+  MOE_LOAD_STAGE(0);
+  MOE_STORE_STAGE(0);
+  __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_tiles(kt + 1);
+    if (kt + 1 < nk) MOE_LOAD_STAGE(kt + 1);
     const uint8_t* as = As[cur];
     const uint8_t* bs = Bs[cur];
 #pragma unroll
@@ -178,16 +161,27 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
       for (int i = 0; i < FM; ++i)
         af[i] = *reinterpret_cast<const bf16x8*>(as + (wm * (BM / WM) + i * 16 + lrow) * A_PITCH + (ks + lkb) * 2);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bf[j] = read_b_frag(bs, ks + lkb, frag_col(j), lane);
+      for (int j = 0; j < FN; ++j) {
+        int col;
+        if constexpr (GATEUP) {
+          constexpr int HF = FN / 2;
+          col = (j < HF ? 0 : BNH) + wn * (BNH / WN) + (j % HF) * 16;
+        } else {
+          col = wn * (BN / WN) + j * 16;
+        }
+        bf[j] = read_b_frag(bs, ks + lkb, col, lane);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tiles(cur ^ 1);
+    if (kt + 1 < nk) MOE_STORE_STAGE(cur ^ 1);
     __syncthreads();
   }
+#undef MOE_LOAD_STAGE
+#undef MOE_STORE_STAGE
 
   // ---- epilogue (16x16 accumulator: lane holds rows 4*(lane/16)+q of column lane%16)
   const int lcol = lane & 15;
