@@ -3,19 +3,26 @@
 // Same three launches and epilogues as gemm.hip (gate/up with the SwiGLU
 // epilogue over routed groups plus the shared expert; shared down; routed
 // down with un-permute + combine), with a tiling sized for CDNA4:
-//   * workgroup tile BM x 256 (BM = 64 / 128 / 256), K staged 64 at a time,
-//     4 waves; at BM = 256 each wave owns a 128 x 128 accumulator block, so
-//     LDS traffic per MFMA stays at half of what 64 x 64 blocks would need;
-//   * both operands are written to LDS exactly as they sit in memory (A rows
-//     K-contiguous, the weight tile N-contiguous) with 16-byte stores;
-//   * the weight operand is read back with the gfx950 LDS transpose read
+//   * workgroup tile BM x 256 (BM = 64 / 128 / 256), 4 waves; at BM = 256
+//     each wave owns a 128 x 128 accumulator block (256 AGPRs), so LDS
+//     traffic per MFMA is half of what 64 x 64 blocks would need;
+//   * operands travel global -> LDS with the gfx950 direct-to-LDS load
+//     (global_load_lds_dwordx4): no staging registers, so a 4-deep ring of
+//     K = 32 stages keeps about two stages of MFMA work in front of memory
+//     latency at no VGPR cost;
+//   * the DMA writes 16 bytes per lane at base + 16 * lane, so the LDS layout
+//     is dense; bank conflicts are avoided with XOR swizzles applied on the
+//     global side (each lane fetches the chunk that belongs at its slot):
+//     A rows (64 B): chunk c of row r sits at c ^ ((r >> 2) & 3);
+//     weight rows (512 B): 16-byte chunk c of row r sits at c ^ (2 * (r & 3));
+//   * the weight operand is read with the gfx950 LDS transpose read
 //     (ds_read_b64_tr_b16): each 16-lane group reads a 4 (K) x 16 (N) block
 //     and every lane receives one column's 4 K values -- the MFMA operand
-//     layout -- so no transpose is done in registers or with scalar stores;
-//   * the weight rows are padded to 544 bytes so the four rows a 16-lane
-//     group reads fall into disjoint LDS banks;
-//   * double-buffered LDS: the next K stage is fetched into registers while
-//     the current one feeds the MFMAs, one barrier per stage.
+//     layout -- so the N-contiguous weight tile needs no transpose anywhere;
+//   * the next stage's MFMA operands are read from LDS while the current
+//     stage's MFMAs run (register double buffer, loop unrolled by two), one
+//     explicit vmcnt wait + s_barrier per stage, and scheduling-group hints
+//     interleave the memory operations with the MFMAs.
 #include "common.h"
 #include "launch.h"
 
@@ -26,17 +33,53 @@ namespace {
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int BN = 256;               // weight columns per tile (gate/up: 128 + 128)
-constexpr int BK = 64;                // K per stage (bf16 elements)
-constexpr int A_PITCH = BK * 2 + 16;  // bytes per A row in LDS
-constexpr int B_PITCH = BN * 2 + 32;  // bytes per weight row in LDS
+constexpr int BN = 256;   // weight columns per tile (gate/up: 128 + 128)
+constexpr int BK = 32;    // K per pipeline stage (bf16) = one MFMA step
+constexpr int NBUF = 4;   // LDS ring depth
+constexpr int A_ROWB = BK * 2;    // bytes per A row in LDS (dense, swizzled)
+constexpr int B_ROWB = BN * 2;    // bytes per weight row in LDS (dense, swizzled)
+constexpr int B_STAGE = BK * B_ROWB;
 
-__device__ __forceinline__ bf16x8 read_b_frag(const uint8_t* bs, int kb, int col, int lane) {
-  // lane s of the 16-lane group points at row kb + s/4, columns col + 4*(s%4)
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Scheduling-group hints (masks: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read):
+// N groups of (one op of class M, S MFMAs).
+template <int N, int M, int S>
+__device__ __forceinline__ void sched_pairs() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(M, 1, 0);
+    if constexpr (S > 0) __builtin_amdgcn_sched_group_barrier(0x008, S, 0);
+    sched_pairs<N - 1, M, S>();
+  }
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in [3:0] and
+// [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15 -> no wait on those).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Direct-to-LDS 16-byte load: every lane fetches 16 bytes from `g`; they
+// land at LDS byte address m0 + 16 * lane.  Written as inline asm on purpose:
+// the instruction writes no VGPR, and the stage pipeline below orders it with
+// explicit vmcnt waits and barriers, whereas the compiler would otherwise
+// wait for every in-flight stage before each LDS transpose read.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory", "m0");
+}
+
+// Weight fragment of 16 columns x 8 K rows (rows kb..kb+7) for this lane:
+// lane s of each 16-lane group points at row kb + s/4 (and kb + 4 + s/4),
+// bytes [2*(col + 4*(s%4)), +8) of the logical row, mapped through the swizzle.
+__device__ __forceinline__ bf16x8 read_b_frag(const lds_u8* bs, int kb, int col, int lane) {
   const int s = lane & 15;
-  const uint8_t* p0 = bs + (kb + (s >> 2)) * B_PITCH + (col + 4 * (s & 3)) * 2;
+  const int lbyte = (col + 4 * (s & 3)) * 2;                 // logical byte in the row
+  const int r = kb + (s >> 2);                                // (r & 3) == (s >> 2) & 3
+  const int pbyte = ((lbyte >> 4) ^ (2 * (r & 3))) * 16 + (lbyte & 15);
+  const lds_u8* p0 = bs + r * B_ROWB + pbyte;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * B_PITCH));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * B_ROWB));
   typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
   const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
@@ -48,14 +91,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int FN = BN / WN / 16;
   constexpr bool GATEUP = MODE == MODE_GATEUP;
   constexpr int BNH = GATEUP ? BN / 2 : BN;
-  constexpr int A_CH = BM * BK * 2 / 16 / 256;   // 16-byte chunks per thread (rows tid/8 + 32 i)
-  constexpr int B_CH = BK * BN * 2 / 16 / 256;   // (K rows tid/32 + 8 i)
-  static_assert(B_CH == 8, "weight chunk layout");
+  constexpr int A_STAGE = BM * A_ROWB;
+  constexpr int A_INS = A_STAGE / 1024 / 4;   // 1 KB DMA instructions per wave per stage (A)
+  constexpr int B_INS = B_STAGE / 1024 / 4;   // (weights)
+  constexpr int LOADS = A_INS + B_INS;        // VMEM instructions per wave per stage
   static_assert(WM * WN == 4, "4 waves");
   static_assert(!GATEUP || FN % 2 == 0, "gate/up fragment pairs");
+  static_assert(A_INS >= 1 && B_INS == 4, "stage layout");
 
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * A_PITCH];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BK * B_PITCH];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * (A_STAGE + B_STAGE)];
+  lds_u8* const As = (lds_u8*)(smem);
+  lds_u8* const Bs = As + NBUF * A_STAGE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -87,101 +133,127 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   const int row_base = shared ? 0 : p.offsets[g];
   const int ldb = GATEUP ? 2 * NH : NH;
 
-  // ---- global sources.  A: 8 chunks of 16 bytes per row, rows (tid>>3) + 32*i
-  // (gathered through perm for the routed gate/up groups), kept as 32-bit
-  // element offsets.  Weights: every chunk of this thread sits in the same
-  // tile column, rows (tid>>5) + 8*i, so one base address and a row stride
-  // serve all of them.
+  // ---- DMA sources.  A: instruction i of this wave fills tile rows
+  // 16*(wave*A_INS + i) + lane/4; the lane fetches the logical chunk that the
+  // swizzle places at its slot.  Rows past the group's end repeat its last
+  // row (their results are never stored).
   const uint16_t* abase;
   if constexpr (GATEUP) abase = reinterpret_cast<const uint16_t*>(shared ? p.A_shared : p.A);
   else if constexpr (MODE == MODE_DOWN_SHARED) abase = reinterpret_cast<const uint16_t*>(p.A_shared);
   else abase = reinterpret_cast<const uint16_t*>(p.A);
-  uint32_t a_off[A_CH];
+  uint32_t a_off[A_INS];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int r = min(m0 + (tid >> 3) + 32 * i, rows - 1);
+  for (int i = 0; i < A_INS; ++i) {
+    const int tr = 16 * (wave * A_INS + i) + (lane >> 2);        // tile row
+    const int c = (lane & 3) ^ ((tr >> 2) & 3);                  // logical 16-byte chunk
+    const int r = min(m0 + tr, rows - 1);
     int arow;
     if constexpr (GATEUP) arow = shared ? r : p.perm[row_base + r];
     else if constexpr (MODE == MODE_DOWN_SHARED) arow = r;
     else arow = row_base + r;
-    a_off[i] = static_cast<uint32_t>(arow) * static_cast<uint32_t>(K) + (tid & 7) * 8;
+    a_off[i] = static_cast<uint32_t>(arow) * static_cast<uint32_t>(K) + c * 8;
   }
-  const int lcB = (tid & 31) * 8;   // tile column of this thread's weight chunks
-  int gcB;
-  if constexpr (GATEUP) gcB = lcB < BNH ? n0 + lcB : NH + n0 + (lcB - BNH);
-  else gcB = n0 + lcB;
-  const bool b_ok = n0 + (GATEUP ? lcB % BNH : lcB) < NH;
-  const uint16_t* bptr = reinterpret_cast<const uint16_t*>(shared ? p.B_shared : p.B) +
-                         (shared ? 0 : static_cast<int64_t>(g) * K * ldb) +
-                         static_cast<int64_t>(tid >> 5) * ldb + (b_ok ? gcB : 0);
-  const int64_t b_rstride = static_cast<int64_t>(8) * ldb;     // 8 K rows between this thread's chunks
-  const int64_t b_kstride = static_cast<int64_t>(BK) * ldb;    // one K stage
+  // weights: instruction i fills K rows 2*(wave*4 + i) + lane/32 of the stage;
+  // the lane's slot is 16-byte chunk lane%32 of that row
+  const uint16_t* bbase = reinterpret_cast<const uint16_t*>(shared ? p.B_shared : p.B) +
+                          (shared ? 0 : static_cast<int64_t>(g) * K * ldb);
+  int64_t b_off[B_INS];
+#pragma unroll
+  for (int i = 0; i < B_INS; ++i) {
+    const int kr = 2 * (wave * B_INS + i) + (lane >> 5);
+    const int c = (lane & 31) ^ (2 * (kr & 3));
+    const int lc = c * 8;                                        // tile column
+    int gc;
+    if constexpr (GATEUP) gc = lc < BNH ? n0 + lc : NH + n0 + (lc - BNH);
+    else gc = n0 + lc;
+    const bool ok = n0 + (GATEUP ? lc % BNH : lc) < NH;
+    b_off[i] = static_cast<int64_t>(kr) * ldb + (ok ? gc : 0);  // clamped columns: valid, discarded
+  }
+  const int64_t b_kstride = static_cast<int64_t>(BK) * ldb;
+  const int nk = K / BK;   // even: K is a multiple of 64
 
-  i32x4 ra[A_CH], rb[B_CH];   // native vectors: kept in VGPRs (HIP's uint4 struct is not)
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
   const int lrow = lane & 15;
-  const int lkb = (lane >> 4) * 8;   // this lane's K offset inside a 32-wide MFMA step
-  uint8_t* const a_st = &As[0][(tid >> 3) * A_PITCH + (tid & 7) * 16];
-  uint8_t* const b_st = &Bs[0][(tid >> 5) * B_PITCH + (tid & 31) * 16];
+  const int kg = lane >> 4;         // this lane's 8-wide K group inside the stage
+  // A fragment i: logical row wm*(BM/WM) + 16 i + lrow, chunk kg; (row >> 2) & 3 == lrow >> 2
+  const int a_rd = (wm * (BM / WM) + lrow) * A_ROWB + ((kg ^ (lrow >> 2)) << 4);
 
-#define MOE_LOAD_STAGE(kt)                                                                     \
+  // Operands in registers: the weight fragments of a stage (FN x 4 VGPRs) are
+  // double-buffered across stages; A fragments stream one 16-row block ahead
+  // (2 x 4 VGPRs), the next A block read while the current one's FN MFMAs run.
+  bf16x8 fb0[FN], fb1[FN], fa[2];
+  // wave-uniform LDS byte addresses of this wave's first DMA slot (A / weights)
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t a_lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(As)) + wave_u * (A_INS * 1024);
+  const uint32_t b_lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(Bs)) + wave_u * (B_INS * 1024);
+
+#define MOE_ISSUE(st)                                                                          \
   do {                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                           \
-      ra[i] = *reinterpret_cast<const i32x4*>(abase + a_off[i] + (kt) * BK);                   \
-    const uint16_t* bp_ = bptr + (kt) * b_kstride;                                             \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                           \
-      rb[i] = b_ok ? *reinterpret_cast<const i32x4*>(bp_ + i * b_rstride) : i32x4{0, 0, 0, 0};     \
+    const int s_ = min((st), nk - 1);                                                          \
+    const uint32_t b_ = static_cast<uint32_t>((st) % NBUF);                                    \
+    _Pragma("unroll") for (int i = 0; i < A_INS; ++i)                                          \
+      dma16(abase + a_off[i] + s_ * BK, a_lds0 + b_ * A_STAGE + i * 1024);                     \
+    _Pragma("unroll") for (int i = 0; i < B_INS; ++i)                                          \
+      dma16(bbase + b_off[i] + s_ * b_kstride, b_lds0 + b_ * B_STAGE + i * 1024);              \
   } while (0)
-#define MOE_STORE_STAGE(buf)                                                                   \
+#define MOE_BFRAG(FB, j, st)                                                                   \
   do {                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                           \
-      *reinterpret_cast<i32x4*>(a_st + (buf) * (BM * A_PITCH) + i * 32 * A_PITCH) = ra[i];     \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                           \
-      *reinterpret_cast<i32x4*>(b_st + (buf) * (BK * B_PITCH) + i * 8 * B_PITCH) = rb[i];      \
+    int col_;                                                                                  \
+    if constexpr (GATEUP) col_ = ((j) < FN / 2 ? 0 : BNH) + wn * (BNH / WN) + ((j) % (FN / 2)) * 16; \
+    else col_ = wn * (BN / WN) + (j) * 16;                                                     \
+    FB[j] = read_b_frag(Bs + ((st) % NBUF) * B_STAGE, kg * 8, col_, lane);                     \
+  } while (0)
+#define MOE_AFRAG(dst, i, st)                                                                  \
+  dst = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(                    \
+      As + ((st) % NBUF) * A_STAGE + a_rd + (i) * 16 * A_ROWB)
+  // One stage: DMA of stage kt+3; weight fragments of stage kt+1 into FB2;
+  // FM blocks of FN MFMAs on stage kt (A block i+1 read during block i, the
+  // last one reading block 0 of stage kt+1); then publish stage kt+2 (this
+  // wave's DMA for it done, only kt+3's may be in flight) with a barrier that
+  // also keeps every wave's reads ahead of the next overwrite.
+#define MOE_STEP(kt, FB, FB2)                                                                  \
+  do {                                                                                         \
+    MOE_ISSUE((kt) + 3);                                                                       \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) MOE_BFRAG(FB2, j, (kt) + 1);               \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                           \
+      if (i + 1 < FM) MOE_AFRAG(fa[(i + 1) & 1], i + 1, (kt));                                 \
+      else MOE_AFRAG(fa[(i + 1) & 1], 0, (kt) + 1);                                            \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i & 1], FB[j], acc[i][j], 0, 0, 0); \
+    }                                                                                          \
+    if constexpr (FM * FN >= 2 * (LOADS + FM + 2 * FN)) {                                      \
+      sched_pairs<LOADS, 0x020, 1>();                                                          \
+      sched_pairs<FM + 2 * FN, 0x100, 1>();                                                    \
+    }                                                                                          \
+    wait_vmcnt<LOADS>();                                                                       \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                                       \
+    __builtin_amdgcn_s_barrier();                                                              \
   } while (0)
 
-  MOE_LOAD_STAGE(0);
-  MOE_STORE_STAGE(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) MOE_LOAD_STAGE(kt + 1);
-    const uint8_t* as = As[cur];
-    const uint8_t* bs = Bs[cur];
+  // prologue: stages 0..2 in flight, wait for stage 0, read its weight
+  // fragments and A block 0
+  MOE_ISSUE(0);
+  MOE_ISSUE(1);
+  MOE_ISSUE(2);
+  wait_vmcnt<2 * LOADS>();
+  __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 32) {
-      bf16x8 af[FM], bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(as + (wm * (BM / WM) + i * 16 + lrow) * A_PITCH + (ks + lkb) * 2);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        int col;
-        if constexpr (GATEUP) {
-          constexpr int HF = FN / 2;
-          col = (j < HF ? 0 : BNH) + wn * (BNH / WN) + (j % HF) * 16;
-        } else {
-          col = wn * (BN / WN) + j * 16;
-        }
-        bf[j] = read_b_frag(bs, ks + lkb, col, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) MOE_STORE_STAGE(cur ^ 1);
-    __syncthreads();
+  for (int j = 0; j < FN; ++j) MOE_BFRAG(fb0, j, 0);
+  MOE_AFRAG(fa[0], 0, 0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    MOE_STEP(kt, fb0, fb1);
+    MOE_STEP(kt + 1, fb1, fb0);
   }
-#undef MOE_LOAD_STAGE
-#undef MOE_STORE_STAGE
+  wait_vmcnt<0>();
+#undef MOE_BFRAG
+#undef MOE_AFRAG
+#undef MOE_ISSUE
+#undef MOE_STEP
 
   // ---- epilogue (16x16 accumulator: lane holds rows 4*(lane/16)+q of column lane%16)
   const int lcol = lane & 15;
