@@ -95,9 +95,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int A_INS = A_STAGE / 1024 / 4;   // 1 KB DMA instructions per wave per stage (A)
   constexpr int B_INS = B_STAGE / 1024 / 4;   // (weights)
   constexpr int LOADS = A_INS + B_INS;        // VMEM instructions per wave per stage
+  constexpr int JPB = FN / FM;                 // next-stage weight fragments read per A block
   static_assert(WM * WN == 4, "4 waves");
   static_assert(!GATEUP || FN % 2 == 0, "gate/up fragment pairs");
   static_assert(A_INS >= 1 && B_INS == 4, "stage layout");
+  static_assert(FN % FM == 0, "weight fragments spread evenly over the A blocks");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * (A_STAGE + B_STAGE)];
   lds_u8* const As = (lds_u8*)(smem);
@@ -219,28 +221,29 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
 #define MOE_STEP(kt, FB, FB2)                                                                  \
   do {                                                                                         \
     MOE_ISSUE((kt) + 3);                                                                       \
-    _Pragma("unroll") for (int j = 0; j < FN; ++j) MOE_BFRAG(FB2, j, (kt) + 1);               \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                           \
+      /* reads for the next block: A block i+1 (or block 0 of stage kt+1) and */               \
+      /* JPB of stage kt+1's weight fragments; then block i's MFMAs          */               \
       if (i + 1 < FM) MOE_AFRAG(fa[(i + 1) & 1], i + 1, (kt));                                 \
       else MOE_AFRAG(fa[(i + 1) & 1], 0, (kt) + 1);                                            \
+      _Pragma("unroll") for (int jj = 0; jj < JPB; ++jj) MOE_BFRAG(FB2, i * JPB + jj, (kt) + 1); \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
       _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i & 1], FB[j], acc[i][j], 0, 0, 0); \
-    }                                                                                          \
-    if constexpr (FM * FN >= 2 * (LOADS + FM + 2 * FN)) {                                      \
-      sched_pairs<LOADS, 0x020, 1>();                                                          \
-      sched_pairs<FM + 2 * FN, 0x100, 1>();                                                    \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
     }                                                                                          \
     wait_vmcnt<LOADS>();                                                                       \
     __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                                       \
     __builtin_amdgcn_s_barrier();                                                              \
   } while (0)
 
-  // prologue: stages 0..2 in flight, wait for stage 0, read its weight
-  // fragments and A block 0
+  // prologue: stages 0..2 in flight.  Iteration kt reads stage kt+1's
+  // operands, so stages 0 and 1 must have landed (only stage 2's DMA may
+  // still be in flight) before the barrier that publishes them.
   MOE_ISSUE(0);
   MOE_ISSUE(1);
   MOE_ISSUE(2);
-  wait_vmcnt<2 * LOADS>();
+  wait_vmcnt<LOADS>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int j = 0; j < FN; ++j) MOE_BFRAG(fb0, j, 0);

@@ -75,4 +75,10 @@ bool bf16_v2_supported(int K, int N, int N_shared);
 hipError_t launch_gemm_bf16_v2(int mode, int bm, const GemmArgs& a, int T, hipStream_t s,
                                const int32_t* tiles_all);
 
+// bf16 weight-streaming tiling for decode-sized T (16- or 32-row tiles,
+// 128 weight columns, K split over the 4 waves; K must be a multiple of 128).
+bool decode_supported(int K);
+hipError_t launch_gemm_decode(int mode, bool rows32, const GemmArgs& a, int T, hipStream_t s,
+                              const int32_t* tiles_all);
+
 }  // namespace moe

@@ -127,8 +127,10 @@ Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
   return o;
 }
 
-// Token counts from which the bf16 prefill tiling is used.
+// Token counts from which the bf16 prefill tiling is used, and up to which
+// the weight-streaming decode tiling is used.
 constexpr int64_t kPrefillTokens = 256;
+constexpr int64_t kDecodeTokens = 64;
 
 // Tile height for the routed groups: the mean group size decides between
 // 256-, 128- and 64-row tiles (a taller tile reuses each weight tile for more
@@ -281,8 +283,19 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g1.amax_shared = amax_s;
   const bool v2 = c.w_dtype == MOE_BF16 && T >= kPrefillTokens && bf16_v2_supported(c.d, c.f, c.f_shared) &&
                   bf16_v2_supported(c.f, c.d, c.d) && bf16_v2_supported(c.f_shared, c.d, c.d);
+  const bool dec = c.w_dtype == MOE_BF16 && T <= kDecodeTokens && decode_supported(c.d) &&
+                   decode_supported(c.f) && decode_supported(c.f_shared);
   const int bm_routed = routed_tile_rows(T, c.n_experts);
-  if (v2) {
+  if (dec) {
+    g1.group_lo = 0;
+    g1.group_hi = c.n_experts;
+    if ((e = launch_gemm_decode(MODE_GATEUP, false, g1, Ti, stream, R.tiles)) != hipSuccess)
+      return hip_fail(plan, e);
+    g1.group_lo = c.n_experts;
+    g1.group_hi = c.n_experts + 1;
+    if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles)) != hipSuccess)
+      return hip_fail(plan, e);
+  } else if (v2) {
     g1.group_lo = 0;
     g1.group_hi = c.n_experts;
     if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_routed, g1, Ti, stream, R.tiles)) != hipSuccess)
@@ -328,8 +341,9 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g2.C_shared = y_s;
   g2.group_lo = c.n_experts;
   g2.group_hi = c.n_experts + 1;
-  e = v2 ? launch_gemm_bf16_v2(MODE_DOWN_SHARED, 256, g2, Ti, stream, R.tiles)
-         : launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles);
+  e = dec  ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
+      : v2 ? launch_gemm_bf16_v2(MODE_DOWN_SHARED, 256, g2, Ti, stream, R.tiles)
+           : launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(plan, e);
 
@@ -349,8 +363,9 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g3.out_bf16 = c.out_dtype == MOE_BF16;
   g3.group_lo = 0;
   g3.group_hi = c.n_experts;
-  e = v2 ? launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_routed, g3, Ti, stream, R.tiles)
-         : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
+  e = dec  ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
+      : v2 ? launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_routed, g3, Ti, stream, R.tiles)
+           : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(4)) != hipSuccess) return hip_fail(plan, e);
   return MOE_OK;

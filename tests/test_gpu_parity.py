@@ -135,3 +135,30 @@ def test_route_only_entry_point(gpu):
     ro = block.route(inp["x"], *w.router())
     from parity import check_routing
     check_routing(cfg, ro, r)
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 31, 33, 64])
+def test_decode_path_ragged(gpu, T):
+    # decode-sized token counts on widths the weight-streaming kernels take
+    cfg = dataclasses.replace(synth.get_config("decode_like_bf16"), T=T, name=f"decode{T}")
+    print(f"[parity] decode T={T}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    check_forward(cfg, inp, out, routing)
+
+
+def test_decode_path_one_hot_and_idle_nan(gpu):
+    # all 40 tokens to one expert (several 16-row tiles of one group) and every
+    # other expert's weights NaN
+    cfg = dataclasses.replace(synth.get_config("decode_like_bf16"), T=40, bias="cold", n_cold=0, name="dec_hot")
+    inp = synth.make_inputs(cfg)
+    inp["router_bias"] = torch.full((cfg.E,), -60.0)
+    inp["router_bias"][5] = 60.0
+    g = to_device(inp, gpu)
+    for e in range(cfg.E):
+        if e != 5:
+            g["w_gate_up"][e].fill_(float("nan")); g["w_down"][e].fill_(float("nan"))
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    assert int(routing["counts"][5]) == cfg.T
+    check_forward(cfg, inp, out, routing)
