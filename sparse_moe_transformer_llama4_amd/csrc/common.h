@@ -49,6 +49,7 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 struct WsLayout {
   size_t idx, gate, counts, offsets, perm;  // routing record (used when the caller passes none)
   size_t hist;                              // int32 [nblocks_route][E] -> per-block bases
+  size_t logits;                            // fp32 [router splits][T][E] partial router logits
   size_t tiles;                             // int32 [kNumBM][E + 2] tile tables
   size_t h_r, h_s;                          // SwiGLU outputs (bf16 / f32; bf16 staging for e4m3)
   size_t hq_r, hq_s;                        // e4m3 codes of h (e4m3 only)

@@ -56,7 +56,15 @@ struct GemmArgs {
   int group_lo, group_hi;  // groups [lo, hi) handled by this launch (group E = shared expert)
 };
 
-hipError_t launch_router(const RouterArgs& a, int x_dtype, hipStream_t s);
+// Router in two launches: partial logits over K slices of d (the slice count
+// grows for few tokens so the GPU fills), then a fixed-order sum + top-1 +
+// gate + histogram.  `part` holds router_splits(T, d) * T * E floats.
+int router_splits(int T, int d, int x_dtype);
+hipError_t launch_router(const RouterArgs& a, int x_dtype, float* part, hipStream_t s);
+// T <= 64: partial logits, then one workgroup does top-1, gate, counts,
+// offsets, tile tables and the stable permutation.
+hipError_t launch_route_small(const RouterArgs& a, int x_dtype, float* part, int32_t* counts, int32_t* offsets,
+                              int32_t* tiles, int32_t* perm, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_perm(const int32_t* idx, const int32_t* base, int T, int E, int32_t* perm,
                        hipStream_t s);

@@ -54,6 +54,7 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   L.offsets = take((E + 1) * 4);
   L.perm = take(t * 4);
   L.hist = take(nb * E * 4);
+  L.logits = take(static_cast<size_t>(router_splits(static_cast<int>(T), c.d, c.x_dtype)) * t * E * 4);
   L.tiles = take(kNumBM * (E + 2) * 4);
   L.h_r = take(t * c.f * hsz);
   L.h_s = take(t * c.f_shared * hsz);
@@ -112,7 +113,7 @@ moe_status check_routing(const moe_routing* r) {
 // Pointers of the routing record: the caller's, or workspace-backed.
 struct Route {
   int32_t *idx, *counts, *offsets, *perm, *hist, *tiles;
-  float* gate;
+  float *gate, *logits;
 };
 
 Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
@@ -124,6 +125,7 @@ Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
   o.perm = r ? r->perm : reinterpret_cast<int32_t*>(ws + L.perm);
   o.hist = reinterpret_cast<int32_t*>(ws + L.hist);
   o.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  o.logits = reinterpret_cast<float*>(ws + L.logits);
   return o;
 }
 
@@ -140,14 +142,27 @@ int routed_tile_rows(int64_t T, int E) {
   return mean >= 192 ? 256 : mean >= 96 ? 128 : 64;
 }
 
+// Tile height for a down GEMM (N = d columns in 256-wide tiles) over `rows`
+// tokens in `groups` groups: 256-row tiles only when they still give at
+// least ~3 full rounds of workgroups over the GPU's CUs, else 128 (fewer
+// idle CUs in the last round outweigh the lower per-tile efficiency).
+int down_tile_rows(int64_t rows, int groups, int d, int bm_max) {
+  const int64_t ntile = (d + 255) / 256;
+  const int64_t t256 = ((rows + 255) / 256 + (groups > 1 ? groups / 2 : 0)) * ntile;
+  if (bm_max >= 256 && t256 >= 3 * 256) return 256;
+  return bm_max >= 128 ? 128 : bm_max;
+}
+
 // Router + scan + permutation.
 hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_weights* w, const Route& R,
                          hipStream_t s) {
   hipError_t e;
+  RouterArgs ra{x, w->w_router, c.has_router_bias ? w->router_bias : nullptr, T, c.d, c.n_experts,
+                R.idx, R.gate, R.hist};
+  if (T > 0 && T <= kRouteTokens)
+    return launch_route_small(ra, c.x_dtype, R.logits, R.counts, R.offsets, R.tiles, R.perm, s);
   if (T > 0) {
-    RouterArgs ra{x, w->w_router, c.has_router_bias ? w->router_bias : nullptr, T, c.d, c.n_experts,
-                  R.idx, R.gate, R.hist};
-    if ((e = launch_router(ra, c.x_dtype, s)) != hipSuccess) return e;
+    if ((e = launch_router(ra, c.x_dtype, R.logits, s)) != hipSuccess) return e;
   }
   ScanArgs sa{R.hist, (T + kRouteTokens - 1) / kRouteTokens, c.n_experts, T, R.counts, R.offsets, R.tiles};
   if ((e = launch_scan(sa, s)) != hipSuccess) return e;
@@ -342,7 +357,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g2.group_lo = c.n_experts;
   g2.group_hi = c.n_experts + 1;
   e = dec  ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
-      : v2 ? launch_gemm_bf16_v2(MODE_DOWN_SHARED, 256, g2, Ti, stream, R.tiles)
+      : v2 ? launch_gemm_bf16_v2(MODE_DOWN_SHARED, down_tile_rows(T, 1, c.d, 256), g2, Ti, stream, R.tiles)
            : launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(plan, e);
@@ -364,7 +379,8 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g3.group_lo = 0;
   g3.group_hi = c.n_experts;
   e = dec  ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
-      : v2 ? launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_routed, g3, Ti, stream, R.tiles)
+      : v2 ? launch_gemm_bf16_v2(MODE_DOWN_ROUTED, down_tile_rows(T, c.n_experts, c.d, bm_routed), g3, Ti, stream,
+                                 R.tiles)
            : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(4)) != hipSuccess) return hip_fail(plan, e);

@@ -40,34 +40,33 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
 
 // ---------------------------------------------------------------- router
 
-template <int DT> struct RouterT;
-template <> struct RouterT<DT_BF16> {
-  static constexpr int KC = 64;     // K elements staged per chunk
-  static constexpr int KSTEP = 32;  // K of one MFMA
-};
-template <> struct RouterT<DT_F32> {
-  static constexpr int KC = 32;
-  static constexpr int KSTEP = 4;
-};
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short r_s16x4;
+typedef __attribute__((address_space(3))) r_s16x4 r_lds_s16x4;
 
-// One workgroup = 4 waves = 64 tokens; each wave computes a 16 x Ep logit
-// tile with 16x16 MFMAs (Ep = E rounded up to 16).  The router weight chunk
-// [KC x E] is staged in LDS transposed to [E][KC] so that every lane reads
-// its K-contiguous MFMA operand with one LDS access.
+// Partial logits of 64 tokens x all experts over one K slice of d.
+// Workgroup = 4 waves x 16 tokens; grid = (token blocks, K slices).  The
+// router weight rows of each 64-deep K chunk are staged in LDS as they sit in
+// memory ([K][E], expert-contiguous, rows padded by 32 bytes); bf16 operands
+// are read back with the LDS transpose read (one expert column's 4 K values
+// per lane), fp32 ones with plain 4-byte reads (one K value per lane).
+// Tokens come straight from global memory into the MFMA registers.
 template <int DT>
-__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  using R = RouterT<DT>;
-  constexpr int KC = R::KC;
-  constexpr int PITCH = KC + 8;  // elements per LDS row (padding breaks bank aliasing)
+__global__ __launch_bounds__(256) void router_partial_kernel(RouterArgs a, int kslice, float* part) {
   using Elem = typename std::conditional<DT == DT_BF16, uint16_t, float>::type;
-  __shared__ Elem wt[256 * PITCH];
+  constexpr int ES = sizeof(Elem);
+  constexpr int KC = DT == DT_BF16 ? 64 : 32;          // K rows per staged chunk
+  constexpr int KSTEP = DT == DT_BF16 ? 32 : 4;        // K per MFMA
+  __shared__ __attribute__((aligned(16))) uint8_t wt[KC * (256 * 4 + 32)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, d = a.d, T = a.T;
   const int Ep = (E + 15) & ~15;
   const int nf = Ep >> 4;
+  const int pitch = Ep * ES + 32;                       // bytes per staged row
   const int t0 = blockIdx.x * kRouteTokens + wave * 16;
   const int trow = min(t0 + (lane & 15), T - 1);
+  const int ks0 = blockIdx.y * kslice;
+  const int ks1 = min(d, ks0 + kslice);
   const Elem* xrow = reinterpret_cast<const Elem*>(a.x) + static_cast<int64_t>(trow) * d;
   const Elem* wr = reinterpret_cast<const Elem*>(a.wr);
 
@@ -75,26 +74,40 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // zero the padding rows E..Ep-1 once
-  for (int i = tid; i < (Ep - E) * PITCH; i += 256) wt[E * PITCH + i] = Elem(0);
-
-  for (int k0 = 0; k0 < d; k0 += KC) {
+  const int chunk_elems = KC * E;                       // contiguous in [d][E]
+  const bool vec_ok = (E * ES) % 16 == 0;
+  for (int k0 = ks0; k0 < ks1; k0 += KC) {
     __syncthreads();
-    for (int i = tid; i < KC * E; i += 256) {
-      const int k = i / E, e = i - k * E;
-      wt[e * PITCH + k] = wr[static_cast<int64_t>(k0 + k) * E + e];
+    const Elem* src = wr + static_cast<int64_t>(k0) * E;
+    if (vec_ok) {
+      const int rowv = E * ES / 16;                     // 16-byte pieces per row
+      for (int i = tid; i < KC * rowv; i += 256) {
+        const int r = i / rowv, c = i - r * rowv;
+        *reinterpret_cast<i32x4*>(&wt[r * pitch + c * 16]) =
+            *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(src) + (static_cast<int64_t>(r) * E * ES + c * 16));
+      }
+    } else {
+      for (int i = tid; i < chunk_elems; i += 256) {
+        const int r = i / E, c = i - r * E;
+        *reinterpret_cast<Elem*>(&wt[r * pitch + c * ES]) = src[i];
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < KC; ks += R::KSTEP) {
+    for (int ks = 0; ks < KC; ks += KSTEP) {
       if constexpr (DT == DT_BF16) {
         const int kk = ks + (lane >> 4) * 8;
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(xrow + k0 + kk);
+        const int s = lane & 15;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           if (j < nf) {
-            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&wt[(j * 16 + (lane & 15)) * PITCH + kk]);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[j], 0, 0, 0);
+            const uint8_t* p0 = &wt[(kk + (s >> 2)) * pitch + (j * 16 + 4 * (s & 3)) * 2];
+            const r_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((r_lds_s16x4*)(p0));
+            const r_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((r_lds_s16x4*)(p0 + 4 * pitch));
+            typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+            const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, v), acc[j], 0, 0, 0);
           }
         }
       } else {
@@ -103,57 +116,53 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           if (j < nf) {
-            const float bv = wt[(j * 16 + (lane & 15)) * PITCH + kk];
+            const float bv = *reinterpret_cast<const float*>(&wt[kk * pitch + (j * 16 + (lane & 15)) * 4]);
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[j], 0, 0, 0);
           }
         }
       }
     }
   }
-
-  // Lane holds logits of rows 4*(lane/16)+q, column j*16 + lane%16.
-  // Per row: best (value, index) over this lane's columns (ascending), then
-  // across the 16 lanes of the row group; ties go to the lower index.
-  const int col0 = lane & 15;
+  // partial logits: lane holds rows 4*(lane/16)+q of column j*16 + lane%16
+  float* out = part + static_cast<int64_t>(blockIdx.y) * T * E;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float best = -INFINITY;
-    int bi = 0x7fffffff;
+  for (int j = 0; j < 16; ++j) {
+    if (j < nf) {
+      const int e = j * 16 + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j < nf) {
-        const int e = j * 16 + col0;
-        if (e < E) {
-          float v = acc[j][q];
-          if (a.bias) v += a.bias[e];
-          if (v > best) { best = v; bi = e; }
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + 4 * (lane >> 4) + q;
+        if (e < E && t < T) out[static_cast<int64_t>(t) * E + e] = acc[j][q];
       }
     }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      const float ov = __shfl_xor(best, m, 64);
-      const int oi = __shfl_xor(bi, m, 64);
-      if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+  }
+}
+
+// Sum of the K-slice partials in slice order (deterministic), bias, top-1
+// with ties to the lowest index, sigmoid gate, and the per-workgroup expert
+// histogram (64 tokens per workgroup, the blocking the permutation uses).
+__global__ __launch_bounds__(64) void router_finish_kernel(RouterArgs a, int nsplit, const float* part) {
+  __shared__ int hist[256];
+  const int E = a.E, T = a.T;
+  for (int e = threadIdx.x; e < E; e += 64) hist[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kRouteTokens + threadIdx.x;
+  if (t < T) {
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int e = 0; e < E; ++e) {
+      float v = 0.f;
+      for (int s = 0; s < nsplit; ++s) v += part[(static_cast<int64_t>(s) * T + t) * E + e];
+      if (a.bias) v += a.bias[e];
+      if (v > best) { best = v; bi = e; }
     }
     bi = min(bi, E - 1);  // only reachable with non-finite logits (outside the contract)
-    const int t = t0 + 4 * (lane >> 4) + q;
-    if (col0 == 0 && t < T) {
-      a.idx[t] = bi;
-      a.gate[t] = 1.0f / (1.0f + expf(-best));
-    }
-  }
-
-  // per-workgroup histogram
-  __shared__ int hist[256];
-  for (int e = tid; e < E; e += 256) hist[e] = 0;
-  __syncthreads();
-  if (tid < kRouteTokens) {
-    const int t = blockIdx.x * kRouteTokens + tid;
-    if (t < T) atomicAdd(&hist[a.idx[t]], 1);
+    a.idx[t] = bi;
+    a.gate[t] = 1.0f / (1.0f + expf(-best));
+    atomicAdd(&hist[bi], 1);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) a.hist[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
+  for (int e = threadIdx.x; e < E; e += 64) a.hist[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
 }
 
 // Per-token e4m3 quantisation of x (bf16): s = fp32(max|x_t|) / 448 (1 for
@@ -222,30 +231,74 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
 
 // ---------------------------------------------------------------- scan
 
-// Block-wide exclusive scan of one int per thread (256 threads).
-__device__ int block_exclusive_scan(int v, int* sm, int* total) {
-  const int tid = threadIdx.x;
-  sm[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int o = tid >= off ? sm[tid - off] : 0;
-    __syncthreads();
-    sm[tid] += o;
-    __syncthreads();
+// Exclusive scans over a 256-thread workgroup of NV values per thread at
+// once (wave shuffles, one barrier): v[i] -> exclusive prefix, tot[i] -> total.
+template <int NV>
+__device__ void block_exclusive_scan(int (&v)[NV], int (&tot)[NV], int* sm /* [NV][4] */) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int x[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) x[i] = v[i];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int n = __shfl_up(x[i], o, 64);
+      if (lane >= o) x[i] += n;
+    }
   }
-  const int incl = sm[tid];
-  if (total) *total = sm[255];
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sm[i * 4 + w] = x[i];
+  }
   __syncthreads();
-  return incl - v;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    int off = 0, t = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sj = sm[i * 4 + j];
+      off += j < w ? sj : 0;
+      t += sj;
+    }
+    tot[i] = t;
+    v[i] = x[i] - v[i] + off;
+  }
+}
+
+// Writes counts, offsets[E + 1] and the tile tables from per-expert counts
+// held one per thread (thread e < E); group E of every table is the shared
+// expert (T rows) and entry E + 1 the total.
+__device__ void offsets_and_tiles(int cnt, int E, int T, int32_t* counts, int32_t* offsets, int32_t* tiles,
+                                  int* sm) {
+  const int e = threadIdx.x;
+  int v[1 + kNumBM], tot[1 + kNumBM];
+  v[0] = cnt;
+#pragma unroll
+  for (int i = 0; i < kNumBM; ++i) v[1 + i] = (cnt + bm_of(i) - 1) / bm_of(i);
+  block_exclusive_scan<1 + kNumBM>(v, tot, sm);
+  if (e < E) {
+    counts[e] = cnt;
+    offsets[e] = v[0];
+#pragma unroll
+    for (int i = 0; i < kNumBM; ++i) tiles[i * (E + 2) + e] = v[1 + i];
+  }
+  if (e == 0) {
+    offsets[E] = tot[0];
+#pragma unroll
+    for (int i = 0; i < kNumBM; ++i) {
+      tiles[i * (E + 2) + E] = tot[1 + i];   // the shared group follows the routed ones
+      tiles[i * (E + 2) + E + 1] = tot[1 + i] + (T + bm_of(i) - 1) / bm_of(i);
+    }
+  }
 }
 
 // One workgroup: column scan of the per-workgroup histograms.
 //   hist[b][e] <- offsets[e] + sum_{b' < b} hist[b'][e]   (base of block b in group e)
-//   counts[e], offsets[e]
-//   tiles[i][g] = sum_{g' < g} ceil(n_g' / BM_i) for g = 0..E+1, where group E
-//   is the shared expert (n_E = T) and entry E+1 is the total.
+//   counts[e], offsets[e], and the tile tables tiles[i][g] = sum_{g' < g}
+//   ceil(n_g' / BM_i) for g = 0..E+1 (group E = the shared expert, n_E = T).
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
-  __shared__ int sm[256];
+  __shared__ int sm[(1 + kNumBM) * 4];
   const int e = threadIdx.x;
   const int E = a.E;
   int running = 0;
@@ -258,25 +311,51 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     }
   }
   const int cnt = e < E ? running : 0;
-  int total = 0;
-  const int off = block_exclusive_scan(cnt, sm, &total);
+  offsets_and_tiles(cnt, E, a.T, a.counts, a.offsets, a.tiles, sm);
   if (e < E) {
-    a.counts[e] = cnt;
-    a.offsets[e] = off;
+    const int off = a.offsets[e];
     for (int b = 0; b < a.nblocks; ++b) a.hist[static_cast<int64_t>(b) * E + e] += off;
   }
-  if (e == 0) a.offsets[E] = total;
-  for (int i = 0; i < kNumBM; ++i) {
-    const int bm = bm_of(i);
-    const int mt = (cnt + bm - 1) / bm;
-    int tot = 0;
-    const int start = block_exclusive_scan(mt, sm, &tot);
-    int* tt = a.tiles + i * (E + 2);
-    if (e < E) tt[e] = start;
-    if (e == 0) {
-      tt[E] = tot;                            // the shared group follows the routed ones
-      tt[E + 1] = tot + (a.T + bm - 1) / bm;
+}
+
+// Routing of at most 64 tokens in one workgroup: sum of the K-slice partial
+// logits, bias, top-1 (lowest index), gate, counts, offsets, tile tables and
+// the stable permutation, without a histogram pass.
+__global__ __launch_bounds__(256) void route_small_kernel(RouterArgs a, int nsplit, const float* part,
+                                                          int32_t* counts, int32_t* offsets, int32_t* tiles,
+                                                          int32_t* perm) {
+  __shared__ int cnt_s[256];
+  __shared__ int ids[kRouteTokens];
+  __shared__ int sm[(1 + kNumBM) * 4];
+  const int tid = threadIdx.x, E = a.E, T = a.T;
+  cnt_s[tid] = 0;
+  __syncthreads();
+  if (tid < T) {
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int e = 0; e < E; ++e) {
+      float v = 0.f;
+      for (int s = 0; s < nsplit; ++s) v += part[(static_cast<int64_t>(s) * T + tid) * E + e];
+      if (a.bias) v += a.bias[e];
+      if (v > best) { best = v; bi = e; }
     }
+    bi = min(bi, E - 1);  // only reachable with non-finite logits (outside the contract)
+    a.idx[tid] = bi;
+    a.gate[tid] = 1.0f / (1.0f + expf(-best));
+    ids[tid] = bi;
+    atomicAdd(&cnt_s[bi], 1);
+  }
+  __syncthreads();
+  offsets_and_tiles(tid < E ? cnt_s[tid] : 0, E, T, counts, offsets, tiles, sm);
+  __shared__ int off_s[256];
+  __syncthreads();
+  if (tid < E) off_s[tid] = offsets[tid];
+  __syncthreads();
+  if (tid < T) {
+    const int e = ids[tid];
+    int rank = 0;
+    for (int j = 0; j < tid; ++j) rank += ids[j] == e;
+    perm[off_s[e] + rank] = tid;
   }
 }
 
@@ -297,12 +376,39 @@ __global__ __launch_bounds__(64) void perm_kernel(const int32_t* idx, const int3
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_router(const RouterArgs& a, int x_dtype, hipStream_t s) {
+int router_splits(int T, int d, int x_dtype) {
+  const int kc = x_dtype == DT_BF16 ? 64 : 32;
+  const int nb = (T + kRouteTokens - 1) / kRouteTokens;
+  int ns = 1;
+  while (nb * ns < 256 && (d / kc) % (ns * 2) == 0 && d / (ns * 2) >= 2 * kc) ns *= 2;
+  return ns;
+}
+
+static hipError_t launch_partials(const RouterArgs& a, int x_dtype, float* part, int ns, hipStream_t s) {
   const int nb = (a.T + kRouteTokens - 1) / kRouteTokens;
+  const int kslice = a.d / ns;
   if (x_dtype == DT_BF16)
-    hipLaunchKernelGGL(router_kernel<DT_BF16>, dim3(nb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(router_partial_kernel<DT_BF16>, dim3(nb, ns), dim3(256), 0, s, a, kslice, part);
   else
-    hipLaunchKernelGGL(router_kernel<DT_F32>, dim3(nb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(router_partial_kernel<DT_F32>, dim3(nb, ns), dim3(256), 0, s, a, kslice, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const RouterArgs& a, int x_dtype, float* part, hipStream_t s) {
+  const int nb = (a.T + kRouteTokens - 1) / kRouteTokens;
+  const int ns = router_splits(a.T, a.d, x_dtype);
+  hipError_t e = launch_partials(a, x_dtype, part, ns, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(router_finish_kernel, dim3(nb), dim3(kRouteTokens), 0, s, a, ns, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_small(const RouterArgs& a, int x_dtype, float* part, int32_t* counts, int32_t* offsets,
+                              int32_t* tiles, int32_t* perm, hipStream_t s) {
+  const int ns = router_splits(a.T, a.d, x_dtype);
+  hipError_t e = launch_partials(a, x_dtype, part, ns, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(256), 0, s, a, ns, part, counts, offsets, tiles, perm);
   return hipGetLastError();
 }
 
