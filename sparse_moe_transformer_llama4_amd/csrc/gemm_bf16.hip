@@ -109,16 +109,33 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   const int wm = wave / WN, wn = wave % WN;
   const int E = p.E, T = p.T, K = p.K;
 
-  // ---- tile lookup
+  // ---- tile lookup with an XCD-aware order.  Workgroup ids go round-robin
+  // over the 8 XCDs (each with its own L2): XCD x = id % 8 takes the N-tiles
+  // [x*gn/8, (x+1)*gn/8) for every M-tile, so each weight panel is fetched by
+  // one XCD, and walks them M-major so the workgroups it runs together share
+  // an A panel.  Ids beyond the real tile count exit.
+  const int nmt = (MODE == MODE_DOWN_SHARED) ? (T + BM - 1) / BM : p.tiles[p.group_hi] - p.tiles[p.group_lo];
+  const int gn = p.n_tiles;
+  const int lid = blockIdx.x;
+  int mt_rel, nt;
+  if (gn >= 8) {
+    const int x = lid & 7, local = lid >> 3;
+    const int nt_lo = (x * gn) >> 3, w = (((x + 1) * gn) >> 3) - nt_lo;
+    if (local >= nmt * w) return;
+    mt_rel = local / w;
+    nt = nt_lo + (local - mt_rel * w);
+  } else {
+    if (lid >= nmt * gn) return;
+    mt_rel = lid / gn;
+    nt = lid - mt_rel * gn;
+  }
   int g, m0, rows;
   if constexpr (MODE == MODE_DOWN_SHARED) {
     g = 0;
-    m0 = blockIdx.x * BM;
+    m0 = mt_rel * BM;
     rows = T;
-    if (m0 >= T) return;
   } else {
-    const int mt = blockIdx.x + p.tiles[p.group_lo];
-    if (mt >= p.tiles[p.group_hi]) return;
+    const int mt = mt_rel + p.tiles[p.group_lo];
     int lo = p.group_lo, hi = p.group_hi - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -130,7 +147,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   }
   const bool shared = (MODE == MODE_DOWN_SHARED) || (GATEUP && g == E);
   const int NH = (GATEUP && shared) ? p.N_shared : p.N;
-  const int n0 = blockIdx.y * BNH;
+  const int n0 = nt * BNH;
   if (n0 >= NH) return;
   const int row_base = shared ? 0 : p.offsets[g];
   const int ldb = GATEUP ? 2 * NH : NH;
@@ -329,7 +346,10 @@ hipError_t launch_v2(const GemmArgs& a0, int T, hipStream_t s, const int32_t* ti
   }
   if (gm <= 0) return hipSuccess;
   const int gn = (nmax + BNH - 1) / BNH;
-  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, BM, WM, WN>), dim3(gm, gn), dim3(256), 0, s, a);
+  a.n_tiles = gn;
+  // 1-D grid: enough ids for the largest per-XCD share of (M-tile bound x N-tiles)
+  const int64_t nblk = gn >= 8 ? 8 * static_cast<int64_t>(gm) * ((gn + 7) / 8) : static_cast<int64_t>(gm) * gn;
+  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, BM, WM, WN>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

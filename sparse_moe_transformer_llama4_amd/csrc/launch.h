@@ -54,6 +54,7 @@ struct GemmArgs {
   uint32_t* amax_shared;
   int out_bf16;          // DOWN_ROUTED: output dtype bf16 (else fp32)
   int group_lo, group_hi;  // groups [lo, hi) handled by this launch (group E = shared expert)
+  int n_tiles;             // N-tiles per M-tile of this launch (set by the launcher)
 };
 
 // Router in two launches: partial logits over K slices of d (the slice count
