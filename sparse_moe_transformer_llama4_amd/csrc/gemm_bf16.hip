@@ -35,7 +35,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int BN = 256;   // weight columns per tile (gate/up: 128 + 128)
 constexpr int BK = 32;    // K per pipeline stage (bf16) = one MFMA step
-constexpr int NBUF = 4;   // LDS ring depth
 constexpr int A_ROWB = BK * 2;    // bytes per A row in LDS (dense, swizzled)
 constexpr int B_ROWB = BN * 2;    // bytes per weight row in LDS (dense, swizzled)
 constexpr int B_STAGE = BK * B_ROWB;
@@ -92,6 +91,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr bool GATEUP = MODE == MODE_GATEUP;
   constexpr int BNH = GATEUP ? BN / 2 : BN;
   constexpr int A_STAGE = BM * A_ROWB;
+  // LDS ring depth 4 (NBUF - 2 = 2 stages in flight ahead of the MFMAs).
+  // Deeper rings measured slower: at BM = 64 they cost the second resident
+  // workgroup per CU (4 x 20 KB lets two share the 160 KB LDS).
+  constexpr int NBUF = 4;
   constexpr int A_INS = A_STAGE / 1024 / 4;   // 1 KB DMA instructions per wave per stage (A)
   constexpr int B_INS = B_STAGE / 1024 / 4;   // (weights)
   constexpr int LOADS = A_INS + B_INS;        // VMEM instructions per wave per stage
@@ -99,6 +102,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   static_assert(WM * WN == 4, "4 waves");
   static_assert(!GATEUP || FN % 2 == 0, "gate/up fragment pairs");
   static_assert(A_INS >= 1 && B_INS == 4, "stage layout");
+  static_assert(NBUF >= 4, "pipeline depth");
   static_assert(FN % FM == 0, "weight fragments spread evenly over the A blocks");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * (A_STAGE + B_STAGE)];
@@ -230,14 +234,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
 #define MOE_AFRAG(dst, i, st)                                                                  \
   dst = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(                    \
       As + ((st) % NBUF) * A_STAGE + a_rd + (i) * 16 * A_ROWB)
-  // One stage: DMA of stage kt+3; weight fragments of stage kt+1 into FB2;
-  // FM blocks of FN MFMAs on stage kt (A block i+1 read during block i, the
-  // last one reading block 0 of stage kt+1); then publish stage kt+2 (this
-  // wave's DMA for it done, only kt+3's may be in flight) with a barrier that
-  // also keeps every wave's reads ahead of the next overwrite.
+  // One stage: DMA of stage kt+NBUF-1; weight fragments of stage kt+1 into
+  // FB2; FM blocks of FN MFMAs on stage kt (A block i+1 read during block i,
+  // the last one reading block 0 of stage kt+1); then publish stage kt+2 (this
+  // wave's DMA for it done, only later stages' may be in flight) with a
+  // barrier that also keeps every wave's reads ahead of the next overwrite.
 #define MOE_STEP(kt, FB, FB2)                                                                  \
   do {                                                                                         \
-    MOE_ISSUE((kt) + 3);                                                                       \
+    MOE_ISSUE((kt) + NBUF - 1);                                                                \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                           \
       /* reads for the next block: A block i+1 (or block 0 of stage kt+1) and */               \
       /* JPB of stage kt+1's weight fragments; then block i's MFMAs          */               \
@@ -249,18 +253,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i & 1], FB[j], acc[i][j], 0, 0, 0); \
       __builtin_amdgcn_sched_barrier(0);                                                       \
     }                                                                                          \
-    wait_vmcnt<LOADS>();                                                                       \
+    wait_vmcnt<(NBUF - 3) * LOADS>();                                                          \
     __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                                       \
     __builtin_amdgcn_s_barrier();                                                              \
   } while (0)
 
-  // prologue: stages 0..2 in flight.  Iteration kt reads stage kt+1's
-  // operands, so stages 0 and 1 must have landed (only stage 2's DMA may
-  // still be in flight) before the barrier that publishes them.
-  MOE_ISSUE(0);
-  MOE_ISSUE(1);
-  MOE_ISSUE(2);
-  wait_vmcnt<LOADS>();
+  // prologue: stages 0 .. NBUF-2 in flight.  Iteration kt reads stage kt+1's
+  // operands, so stages 0 and 1 must have landed (only the later stages' DMA
+  // may still be in flight) before the barrier that publishes them.
+#pragma unroll
+  for (int st = 0; st < NBUF - 1; ++st) MOE_ISSUE(st);
+  wait_vmcnt<(NBUF - 3) * LOADS>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int j = 0; j < FN; ++j) MOE_BFRAG(fb0, j, 0);
