@@ -1,0 +1,338 @@
+// fp8 (OCP e4m3fn) grouped GEMMs for prefill-sized token counts (gfx950).
+//
+// The same three launches as the bf16 kernels, on e4m3 codes with fp32
+// scales: the gate/up GEMM multiplies per-token-quantised x by per-column-
+// quantised W_gate_up and applies (gate x token scale x column scale) to the
+// fp32 accumulator before the SwiGLU epilogue; the down GEMMs multiply the
+// per-row-quantised h by per-column-quantised W_down.  MFMA:
+// v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales), 32 K bytes per lane.
+//   * workgroup tile 128 x 256 (gate/up: 128 gate + 128 up columns), 4 waves
+//     of 64 x 128 accumulators; one pipeline stage = K 128 (one MFMA step);
+//   * direct-to-LDS loads into a 3-deep ring of 48 KB stages;
+//   * A rows (128 B) are stored with 16-byte chunk k of row r at
+//     k ^ ((r >> 1) & 7): a 16-lane group then reads 16 rows x 16 B from 16
+//     distinct bank slots;
+//   * weight rows (256 B) are stored with 16-byte chunk c of row r at
+//     c ^ (r & 7) and read with the gfx950 byte transpose read
+//     (ds_read_b64_tr_b8): each 16-lane group reads 8 K rows x 16 columns and
+//     every lane receives its column's 8 K bytes; four reads give the 32 K
+//     bytes of the MFMA operand;
+//   * XCD-aware tile order and one explicit vmcnt wait + s_barrier per stage,
+//     as in the bf16 kernels.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+constexpr int BM = 128, BN = 256, WM = 2, WN = 2;
+constexpr int BK = 128;                  // K bytes per stage = one MFMA step
+constexpr int NBUF = 3;
+constexpr int A_ROWB = BK;               // 128 B per A row
+constexpr int B_ROWB = BN;               // 256 B per weight row
+constexpr int A_STAGE = BM * A_ROWB;     // 16 KB
+constexpr int B_STAGE = BK * B_ROWB;     // 32 KB
+constexpr int A_INS = A_STAGE / 1024 / 4;
+constexpr int B_INS = B_STAGE / 1024 / 4;
+constexpr int LOADS = A_INS + B_INS;
+constexpr int FM = BM / WM / 16;         // 4
+constexpr int FN = BN / WN / 16;         // 8
+constexpr int JPB = FN / FM;             // weight fragments read per A block
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Direct-to-LDS 16-byte load into m0 + 16 * lane (inline asm: it writes no
+// VGPR; the stage ring orders it with explicit vmcnt waits and barriers).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory", "m0");
+}
+
+// 32 K bytes (rows 32*(lane/16) .. +31) of tile column col + lane%16.
+__device__ __forceinline__ i32x8 read_b_frag(const lds_u8* bs, int col, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const int pchunk = (col >> 4) ^ ((s >> 1) & 7);       // rows of one read share (row & 7) = s/2
+  const lds_u8* p = bs + (32 * g + (s >> 1)) * B_ROWB + pchunk * 16 + 8 * (s & 1);
+  i32x8 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 8 * q * B_ROWB));
+    r[2 * q] = v[0];
+    r[2 * q + 1] = v[1];
+  }
+  return r;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
+  constexpr bool GATEUP = MODE == MODE_GATEUP;
+  constexpr int BNH = GATEUP ? BN / 2 : BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * (A_STAGE + B_STAGE)];
+  lds_u8* const As = (lds_u8*)(smem);
+  lds_u8* const Bs = As + NBUF * A_STAGE;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int E = p.E, T = p.T, K = p.K;
+
+  // ---- XCD-aware tile lookup (as in the bf16 kernels)
+  const int nmt = (MODE == MODE_DOWN_SHARED) ? (T + BM - 1) / BM : p.tiles[p.group_hi] - p.tiles[p.group_lo];
+  const int gn = p.n_tiles;
+  const int lid = blockIdx.x;
+  int mt_rel, nt;
+  if (gn >= 8) {
+    const int x = lid & 7, local = lid >> 3;
+    const int nt_lo = (x * gn) >> 3, w = (((x + 1) * gn) >> 3) - nt_lo;
+    if (local >= nmt * w) return;
+    mt_rel = local / w;
+    nt = nt_lo + (local - mt_rel * w);
+  } else {
+    if (lid >= nmt * gn) return;
+    mt_rel = lid / gn;
+    nt = lid - mt_rel * gn;
+  }
+  int g, m0, rows;
+  if constexpr (MODE == MODE_DOWN_SHARED) {
+    g = 0;
+    m0 = mt_rel * BM;
+    rows = T;
+  } else {
+    const int mt = mt_rel + p.tiles[p.group_lo];
+    int lo = p.group_lo, hi = p.group_hi - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    m0 = (mt - p.tiles[g]) * BM;
+    rows = (g == E) ? T : p.offsets[g + 1] - p.offsets[g];
+  }
+  const bool shared = (MODE == MODE_DOWN_SHARED) || (GATEUP && g == E);
+  const int NH = (GATEUP && shared) ? p.N_shared : p.N;
+  const int n0 = nt * BNH;
+  if (n0 >= NH) return;
+  const int row_base = shared ? 0 : p.offsets[g];
+  const int ldb = GATEUP ? 2 * NH : NH;   // weight row length in bytes
+
+  // ---- DMA sources.  A: instruction i fills tile rows 8*(wave*A_INS + i) + lane/8,
+  // the lane fetching the logical chunk its slot holds under the swizzle.
+  const uint8_t* abase;
+  if constexpr (GATEUP) abase = reinterpret_cast<const uint8_t*>(shared ? p.A_shared : p.A);
+  else if constexpr (MODE == MODE_DOWN_SHARED) abase = reinterpret_cast<const uint8_t*>(p.A_shared);
+  else abase = reinterpret_cast<const uint8_t*>(p.A);
+  uint32_t a_off[A_INS];
+#pragma unroll
+  for (int i = 0; i < A_INS; ++i) {
+    const int tr = 8 * (wave * A_INS + i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((tr >> 1) & 7);
+    const int r = min(m0 + tr, rows - 1);
+    int arow;
+    if constexpr (GATEUP) arow = shared ? r : p.perm[row_base + r];
+    else if constexpr (MODE == MODE_DOWN_SHARED) arow = r;
+    else arow = row_base + r;
+    a_off[i] = static_cast<uint32_t>(arow) * static_cast<uint32_t>(K) + c * 16;
+  }
+  // weights: instruction i fills K rows 4*(wave*B_INS + i) + lane/16; slot = chunk lane%16
+  const uint8_t* bbase = reinterpret_cast<const uint8_t*>(shared ? p.B_shared : p.B) +
+                         (shared ? 0 : static_cast<int64_t>(g) * K * ldb);
+  int64_t b_off[B_INS];
+#pragma unroll
+  for (int i = 0; i < B_INS; ++i) {
+    const int kr = 4 * (wave * B_INS + i) + (lane >> 4);
+    const int c = (lane & 15) ^ (kr & 7);
+    const int lc = c * 16;
+    int gc;
+    if constexpr (GATEUP) gc = lc < BNH ? n0 + lc : NH + n0 + (lc - BNH);
+    else gc = n0 + lc;
+    const bool ok = n0 + (GATEUP ? lc % BNH : lc) < NH;
+    b_off[i] = static_cast<int64_t>(kr) * ldb + (ok ? gc : 0);   // clamped columns are never stored
+  }
+  const int64_t b_kstride = static_cast<int64_t>(BK) * ldb;
+  const int nk = K / BK;
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int lrow = lane & 15, kg = lane >> 4;
+  // A fragment: row wm*64 + 16 i + lrow, logical chunks 2 kg, 2 kg + 1; (row >> 1) & 7 == lrow >> 1
+  const int a_rd0 = (wm * (BM / WM) + lrow) * A_ROWB + (((2 * kg) ^ (lrow >> 1)) << 4);
+  const int a_rd1 = (wm * (BM / WM) + lrow) * A_ROWB + (((2 * kg + 1) ^ (lrow >> 1)) << 4);
+
+  i32x8 fb0[FN], fb1[FN], fa[2];
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t a_lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(As)) + wave_u * (A_INS * 1024);
+  const uint32_t b_lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(Bs)) + wave_u * (B_INS * 1024);
+
+#define F8_ISSUE(st)                                                                           \
+  do {                                                                                         \
+    const int s_ = min((st), nk - 1);                                                          \
+    const uint32_t b_ = static_cast<uint32_t>((st) % NBUF);                                    \
+    _Pragma("unroll") for (int i = 0; i < A_INS; ++i)                                          \
+      dma16(abase + a_off[i] + s_ * BK, a_lds0 + b_ * A_STAGE + i * 1024);                     \
+    _Pragma("unroll") for (int i = 0; i < B_INS; ++i)                                          \
+      dma16(bbase + b_off[i] + s_ * b_kstride, b_lds0 + b_ * B_STAGE + i * 1024);              \
+  } while (0)
+#define F8_BFRAG(FB, j, st)                                                                    \
+  do {                                                                                         \
+    int col_;                                                                                  \
+    if constexpr (GATEUP) col_ = ((j) < FN / 2 ? 0 : BNH) + wn * (BNH / WN) + ((j) % (FN / 2)) * 16; \
+    else col_ = wn * (BN / WN) + (j) * 16;                                                     \
+    FB[j] = read_b_frag(Bs + ((st) % NBUF) * B_STAGE, col_, lane);                             \
+  } while (0)
+#define F8_AFRAG(dst, i, st)                                                                   \
+  do {                                                                                         \
+    const lds_u8* ab_ = As + ((st) % NBUF) * A_STAGE + (i) * 16 * A_ROWB;                      \
+    const i32x4 lo_ = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(ab_ + a_rd0); \
+    const i32x4 hi_ = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(ab_ + a_rd1); \
+    dst = i32x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};               \
+  } while (0)
+  // One stage (K 128): DMA of stage kt+2; weight fragments of stage kt+1;
+  // FM blocks of FN MFMAs on stage kt with the next A block read ahead; then
+  // publish stage kt+2 (with a 3-deep ring every DMA issued so far).
+#define F8_STEP(kt, FB, FB2)                                                                   \
+  do {                                                                                         \
+    F8_ISSUE((kt) + 2);                                                                        \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                           \
+      if (i + 1 < FM) F8_AFRAG(fa[(i + 1) & 1], i + 1, (kt));                                  \
+      else F8_AFRAG(fa[(i + 1) & 1], 0, (kt) + 1);                                             \
+      _Pragma("unroll") for (int jj = 0; jj < JPB; ++jj) F8_BFRAG(FB2, i * JPB + jj, (kt) + 1); \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i & 1], FB[j], acc[i][j], 0, 0, 0, \
+                                                                      127, 0, 127);             \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+    }                                                                                          \
+    wait_vmcnt<0>();                                                                           \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                                       \
+    __builtin_amdgcn_s_barrier();                                                              \
+  } while (0)
+
+  // prologue: stages 0 and 1 landed and published; operands of stage 0 read
+  F8_ISSUE(0);
+  F8_ISSUE(1);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int j = 0; j < FN; ++j) F8_BFRAG(fb0, j, 0);
+  F8_AFRAG(fa[0], 0, 0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    F8_STEP(kt, fb0, fb1);
+    F8_STEP(kt + 1, fb1, fb0);
+  }
+  if (kt < nk) F8_STEP(kt, fb0, fb1);
+  wait_vmcnt<0>();
+#undef F8_ISSUE
+#undef F8_BFRAG
+#undef F8_AFRAG
+#undef F8_STEP
+
+  // ---- epilogue (16x16 accumulator: lane holds rows 4*(lane/16)+q of column lane%16)
+  const int lcol = lane & 15;
+  const int rq = 4 * (lane >> 4);
+  if constexpr (GATEUP) {
+    constexpr int HF = FN / 2;
+    const float* sB = shared ? p.sB_shared : p.sB + static_cast<int64_t>(g) * 2 * NH;
+    float* C = reinterpret_cast<float*>(shared ? p.C_shared : p.C);
+    uint32_t* amax = shared ? p.amax_shared : p.amax;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + wm * (BM / WM) + i * 16 + rq + q;
+        const bool valid = r < rows;
+        const int orow = row_base + min(r, rows - 1);
+        const int tok = shared ? min(r, rows - 1) : p.perm[orow];
+        const float scale = (shared ? 1.0f : p.gate[tok]) * (shared ? p.sA_shared : p.sA)[tok];
+        float rmax = 0.f;
+#pragma unroll
+        for (int j = 0; j < HF; ++j) {
+          const int col = n0 + wn * (BNH / WN) + j * 16 + lcol;
+          if (valid && col < NH) {
+            const float gv = acc[i][j][q] * scale * sB[col];
+            const float uv = acc[i][j + HF][q] * scale * sB[NH + col];
+            const float h = silu_f(gv) * uv;
+            C[static_cast<int64_t>(orow) * NH + col] = h;
+            rmax = fmaxf(rmax, fabsf(h));
+          }
+        }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, m, 64));
+        if (valid && lcol == 0) atomicMax(&amax[orow], __float_as_uint(rmax));
+      }
+    }
+  } else {
+    const float* sB = (MODE == MODE_DOWN_ROUTED) ? p.sB + static_cast<int64_t>(g) * NH : p.sB_shared;
+    const float* sA = (MODE == MODE_DOWN_ROUTED) ? p.sA : p.sA_shared;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + wm * (BM / WM) + i * 16 + rq + q;
+        if (r >= rows) continue;
+        const int arow = row_base + r;
+        const int orow = (MODE == MODE_DOWN_ROUTED) ? p.perm[arow] : r;
+        const float rs = sA[arow];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + wn * (BN / WN) + j * 16 + lcol;
+          if (col >= NH) continue;
+          const int64_t o = static_cast<int64_t>(orow) * NH + col;
+          const float v = acc[i][j][q] * rs * sB[col];
+          if constexpr (MODE == MODE_DOWN_SHARED) {
+            reinterpret_cast<float*>(p.C_shared)[o] = v;
+          } else {
+            const float y = v + p.Y[o];
+            if (p.out_bf16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16(y);
+            else reinterpret_cast<float*>(p.C)[o] = y;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MODE>
+hipError_t launch_f8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* tiles_all) {
+  GemmArgs a = a0;
+  a.tiles = tiles_all + bm_index(BM) * (a.E + 2);
+  constexpr int BNH = MODE == MODE_GATEUP ? BN / 2 : BN;
+  const bool has_routed = a.group_lo < a.E;
+  const bool has_shared = a.group_hi > a.E;
+  int gm, nmax = a.N;
+  if constexpr (MODE == MODE_DOWN_SHARED) {
+    gm = (T + BM - 1) / BM;
+  } else {
+    gm = (has_routed ? (T + BM - 1) / BM + a.E : 0) + (has_shared ? (T + BM - 1) / BM : 0);
+    if (MODE == MODE_GATEUP) nmax = max(has_routed ? a.N : 0, has_shared ? a.N_shared : 0);
+  }
+  if (gm <= 0) return hipSuccess;
+  const int gn = (nmax + BNH - 1) / BNH;
+  a.n_tiles = gn;
+  const int64_t nblk = gn >= 8 ? 8 * static_cast<int64_t>(gm) * ((gn + 7) / 8) : static_cast<int64_t>(gm) * gn;
+  hipLaunchKernelGGL((gemm_fp8_kernel<MODE>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_fp8(int mode, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all) {
+  switch (mode) {
+    case MODE_GATEUP: return launch_f8<MODE_GATEUP>(a, T, s, tiles_all);
+    case MODE_DOWN_SHARED: return launch_f8<MODE_DOWN_SHARED>(a, T, s, tiles_all);
+    case MODE_DOWN_ROUTED: return launch_f8<MODE_DOWN_ROUTED>(a, T, s, tiles_all);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

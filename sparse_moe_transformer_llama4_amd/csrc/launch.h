@@ -84,6 +84,9 @@ bool bf16_v2_supported(int K, int N, int N_shared);
 hipError_t launch_gemm_bf16_v2(int mode, int bm, const GemmArgs& a, int T, hipStream_t s,
                                const int32_t* tiles_all);
 
+// fp8 prefill tiling (128 x 256 tiles, K 128 per stage; K multiple of 128).
+hipError_t launch_gemm_fp8(int mode, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all);
+
 // bf16 weight-streaming tiling for decode-sized T (16- or 32-row tiles,
 // 128 weight columns, K split over the 4 waves; K must be a multiple of 128).
 bool decode_supported(int K);

@@ -300,8 +300,13 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
                   bf16_v2_supported(c.f, c.d, c.d) && bf16_v2_supported(c.f_shared, c.d, c.d);
   const bool dec = c.w_dtype == MOE_BF16 && T <= kDecodeTokens && decode_supported(c.d) &&
                    decode_supported(c.f) && decode_supported(c.f_shared);
+  const bool f8 = fp8 && T >= kPrefillTokens;
   const int bm_routed = routed_tile_rows(T, c.n_experts);
-  if (dec) {
+  if (f8) {
+    g1.group_lo = 0;
+    g1.group_hi = c.n_experts + 1;
+    if ((e = launch_gemm_fp8(MODE_GATEUP, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
+  } else if (dec) {
     g1.group_lo = 0;
     g1.group_hi = c.n_experts;
     if ((e = launch_gemm_decode(MODE_GATEUP, false, g1, Ti, stream, R.tiles)) != hipSuccess)
@@ -356,7 +361,8 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g2.C_shared = y_s;
   g2.group_lo = c.n_experts;
   g2.group_hi = c.n_experts + 1;
-  e = dec  ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
+  e = f8   ? launch_gemm_fp8(MODE_DOWN_SHARED, g2, Ti, stream, R.tiles)
+      : dec  ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
       : v2 ? launch_gemm_bf16_v2(MODE_DOWN_SHARED, down_tile_rows(T, 1, c.d, 256), g2, Ti, stream, R.tiles)
            : launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
@@ -378,7 +384,8 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g3.out_bf16 = c.out_dtype == MOE_BF16;
   g3.group_lo = 0;
   g3.group_hi = c.n_experts;
-  e = dec  ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
+  e = f8   ? launch_gemm_fp8(MODE_DOWN_ROUTED, g3, Ti, stream, R.tiles)
+      : dec  ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
       : v2 ? launch_gemm_bf16_v2(MODE_DOWN_ROUTED, down_tile_rows(T, c.n_experts, c.d, bm_routed), g3, Ti, stream,
                                  R.tiles)
            : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
