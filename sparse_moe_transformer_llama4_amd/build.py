@@ -26,13 +26,21 @@ FLAGS = [
 ]
 
 
+# Per-unit code generation.  The 64- and 128-row bf16 GEMM tiles keep their
+# accumulators in VGPRs (VGPR-form MFMAs): with the AGPR form the register
+# allocator copied them between registers on every main-loop iteration.
+UNIT_FLAGS = {
+    "gemm_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, objdir: str, extra) -> str:
     obj = os.path.join(objdir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *UNIT_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
   constexpr int DNBUF = FMMAX == 1 ? 4 : 3;     // per-wave ring depth (LDS: 4 x 4 x 9 KB / 4 x 3 x 10 KB)
   constexpr int LOADS = INS + FMMAX;            // DMA instructions per stage per wave
   constexpr int PART = 4 * DBM * DBN * 4;       // bytes of the final partial sums
-  constexpr int SMEM = 4 * DNBUF * STAGE > PART ? 4 * DNBUF * STAGE : PART;
+  constexpr int RING = 4 * DNBUF * STAGE;
+  constexpr int SMEM = RING > PART + 4 * DBM ? RING : PART + 4 * DBM;   // + per-row table after PART
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -108,6 +109,20 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
   const int nvalid = min(DBM, rows - m0);
   const int fm = (nvalid + 15) >> 4;            // fragments with valid rows (uniform)
 
+  // Per-row metadata for the epilogue (the routed gate/up's gate scale, the
+  // routed down's output row), one tile row per thread, loaded now so its
+  // latency hides behind the main loop.
+  float row_scale = 1.0f;
+  int row_out = 0;
+  if (tid < DBM) {
+    const int r = min(m0 + tid, rows - 1);
+    if constexpr (GATEUP) {
+      if (!shared) row_scale = p.gate[p.perm[row_base + r]];
+    } else if constexpr (MODE == MODE_DOWN_ROUTED) {
+      row_out = p.perm[row_base + r];
+    }
+  }
+
   // ---- this wave's K quarter
   const int kq = K >> 2;                        // multiple of 32
   const int k0 = wave * kq;
@@ -132,7 +147,8 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
   const int64_t w_kstride = static_cast<int64_t>(DBK) * ldb;
 
   // activations: DMA instruction f fills rows 16f .. 16f+15 (64 B each) of the
-  // stage's activation block; lane -> row 16f + lane/4, chunk lane%4
+  // stage's activation block; lane -> row 16f + lane/4, slot lane%4, which
+  // holds logical chunk slot ^ ((row >> 1) & 3) (conflict-free fragment reads)
   const uint16_t* abase;
   if constexpr (GATEUP) abase = reinterpret_cast<const uint16_t*>(shared ? p.A_shared : p.A);
   else if constexpr (MODE == MODE_DOWN_SHARED) abase = reinterpret_cast<const uint16_t*>(p.A_shared);
@@ -145,14 +161,14 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
     if constexpr (GATEUP) arow = shared ? r : p.perm[row_base + r];
     else if constexpr (MODE == MODE_DOWN_SHARED) arow = r;
     else arow = row_base + r;
-    a_off[f] = static_cast<int64_t>(arow) * K + k0 + (lane & 3) * 8;
+    a_off[f] = static_cast<int64_t>(arow) * K + k0 + (((lane & 3) ^ ((lane >> 3) & 3)) * 8);
   }
 
   const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem)) +
                         __builtin_amdgcn_readfirstlane(wave) * (DNBUF * STAGE);
   const lds_u8* ring_p = (const lds_u8*)smem + wave * (DNBUF * STAGE);
   // this lane's A fragment slot: row lane%16 of the fragment, K chunk lane/16
-  const int a_rd = WSTAGE + (lane & 15) * 64 + (lane >> 4) * 16;
+  const int a_rd = WSTAGE + (lane & 15) * 64 + (((lane >> 4) ^ ((lane >> 1) & 3)) << 4);
 
   f32x4 acc[FMMAX][FN];
 #pragma unroll
@@ -214,40 +230,61 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
           part[(wave * DBM + 16 * f + rq + q) * DBN + j * 16 + lcol] = acc[f][j][q];
     }
   }
+  if (tid < DBM) {
+    if constexpr (GATEUP) reinterpret_cast<float*>(smem + PART)[tid] = row_scale;
+    else reinterpret_cast<int*>(smem + PART)[tid] = row_out;
+  }
   __syncthreads();
   auto total = [&](int r, int c) -> float {
     return part[(0 * DBM + r) * DBN + c] + part[(1 * DBM + r) * DBN + c] + part[(2 * DBM + r) * DBN + c] +
            part[(3 * DBM + r) * DBN + c];
   };
 
-  // ---- epilogue: thread -> (row, column) pairs, columns fastest
+  // ---- epilogue: thread -> (row, column) pairs, columns fastest.  Fixed
+  // trip count, fully unrolled, every global load ahead of the stores (the
+  // compiler must assume stores through C may alias the loaded arrays, so a
+  // load between stores would wait a full round trip).
+  constexpr int NIT = DBM * BNH / 256;
   if constexpr (GATEUP) {
     void* C = shared ? p.C_shared : p.C;
-    for (int e = tid; e < nvalid * BNH; e += 256) {
+    const float* sct = reinterpret_cast<const float*>(smem + PART);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int e = tid + 256 * it;
       const int r = e / BNH, c = e % BNH;
       const int col = n0 + c;
-      if (col >= NH) continue;
+      if (r >= nvalid || col >= NH) continue;
       const int orow = row_base + m0 + r;
-      const float scale = shared ? 1.0f : p.gate[p.perm[orow]];
-      const float gv = total(r, c) * scale;
-      const float uv = total(r, BNH + c) * scale;
+      const float gv = total(r, c) * sct[r];
+      const float uv = total(r, BNH + c) * sct[r];
       reinterpret_cast<uint16_t*>(C)[static_cast<int64_t>(orow) * NH + col] = f32_to_bf16(silu_f(gv) * uv);
     }
   } else {
-    for (int e = tid; e < nvalid * BNH; e += 256) {
+    const int* ot = reinterpret_cast<const int*>(smem + PART);
+    float y[NIT];
+    if constexpr (MODE == MODE_DOWN_ROUTED) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int e = tid + 256 * it;
+        const int r = e / BNH, col = n0 + e % BNH;
+        y[it] = (r < nvalid && col < NH) ? p.Y[static_cast<int64_t>(ot[r]) * NH + col] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int e = tid + 256 * it;
       const int r = e / BNH, c = e % BNH;
       const int col = n0 + c;
-      if (col >= NH) continue;
-      const int arow = row_base + m0 + r;
-      const int orow = (MODE == MODE_DOWN_ROUTED) ? p.perm[arow] : m0 + r;
+      if (r >= nvalid || col >= NH) continue;
+      const int orow = (MODE == MODE_DOWN_ROUTED) ? ot[r] : m0 + r;
       const int64_t o = static_cast<int64_t>(orow) * NH + col;
       const float v = total(r, c);
       if constexpr (MODE == MODE_DOWN_SHARED) {
         reinterpret_cast<float*>(p.C_shared)[o] = v;
       } else {
-        const float y = v + p.Y[o];
-        if (p.out_bf16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16(y);
-        else reinterpret_cast<float*>(p.C)[o] = y;
+        const float yv = v + y[it];
+        if (p.out_bf16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16(yv);
+        else reinterpret_cast<float*>(p.C)[o] = yv;
       }
     }
   }

@@ -10,10 +10,14 @@
 //     of 64 x 128 accumulators; one pipeline stage = K 128 (one MFMA step);
 //   * direct-to-LDS loads into a 3-deep ring of 48 KB stages;
 //   * A rows (128 B) are stored with 16-byte chunk k of row r at
-//     k ^ ((r >> 1) & 7): a 16-lane group then reads 16 rows x 16 B from 16
-//     distinct bank slots;
+//     k ^ a_swz(r & 15), a permutation found by measuring LDS read rates: the
+//     fragment reads (16 rows x 16 B per 16-lane group) run at the full
+//     ds_read_b128 rate, where k ^ ((r >> 1) & 7) or k ^ (r & 7) run at half;
 //   * weight rows (256 B) are stored with 16-byte chunk c of row r at
-//     c ^ (r & 7) and read with the gfx950 byte transpose read
+//     c ^ (r & 7) ^ (8 * ((r >> 5) & 1)) (the last term keeps the two 16-lane
+//     groups that one transpose read serves together, 32 rows apart, on
+//     different banks; without it the reads run at 60 % of the rate) and read
+//     with the gfx950 byte transpose read
 //     (ds_read_b64_tr_b8): each 16-lane group reads 8 K rows x 16 columns and
 //     every lane receives its column's 8 K bytes; four reads give the 32 K
 //     bytes of the MFMA operand;
@@ -44,6 +48,12 @@ constexpr int FM = BM / WM / 16;         // 4
 constexpr int FN = BN / WN / 16;         // 8
 constexpr int JPB = FN / FM;             // weight fragments read per A block
 
+// Chunk permutation of an A row (see the header comment): XOR of 5, 7 and 1
+// selected by bits 0, 1 and 3 of the row.
+__device__ __forceinline__ int a_swz(int r) {
+  return ((r & 1) ? 5 : 0) ^ ((r & 2) ? 7 : 0) ^ ((r & 8) ? 1 : 0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
@@ -58,7 +68,8 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
 // 32 K bytes (rows 32*(lane/16) .. +31) of tile column col + lane%16.
 __device__ __forceinline__ i32x8 read_b_frag(const lds_u8* bs, int col, int lane) {
   const int s = lane & 15, g = lane >> 4;
-  const int pchunk = (col >> 4) ^ ((s >> 1) & 7);       // rows of one read share (row & 7) = s/2
+  // rows of one read: 32 g + s/2 (+ 8 q), so (row & 7) = s/2 and (row >> 5) & 1 = g & 1
+  const int pchunk = (col >> 4) ^ ((s >> 1) & 7) ^ ((g & 1) << 3);
   const lds_u8* p = bs + (32 * g + (s >> 1)) * B_ROWB + pchunk * 16 + 8 * (s & 1);
   i32x8 r;
 #pragma unroll
@@ -121,6 +132,25 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
   const int row_base = shared ? 0 : p.offsets[g];
   const int ldb = GATEUP ? 2 * NH : NH;   // weight row length in bytes
 
+  // Per-row metadata for the epilogue, one tile row per thread, loaded now so
+  // its latency hides behind the main loop: the row's scale (gate/up: the
+  // routing gate times the token's activation scale; down: the scale of h)
+  // and, for the routed down, the token the row belongs to.
+  float row_scale = 1.0f;
+  int row_out = 0;
+  if (tid < BM) {
+    const int r = min(m0 + tid, rows - 1);
+    if constexpr (GATEUP) {
+      const int tok = shared ? r : p.perm[row_base + r];
+      row_scale = (shared ? 1.0f : p.gate[tok]) * (shared ? p.sA_shared : p.sA)[tok];
+    } else if constexpr (MODE == MODE_DOWN_SHARED) {
+      row_scale = p.sA_shared[r];
+    } else {
+      row_scale = p.sA[row_base + r];
+      row_out = p.perm[row_base + r];
+    }
+  }
+
   // ---- DMA sources.  A: instruction i fills tile rows 8*(wave*A_INS + i) + lane/8,
   // the lane fetching the logical chunk its slot holds under the swizzle.
   const uint8_t* abase;
@@ -131,7 +161,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
     const int tr = 8 * (wave * A_INS + i) + (lane >> 3);
-    const int c = (lane & 7) ^ ((tr >> 1) & 7);
+    const int c = (lane & 7) ^ a_swz(tr & 15);
     const int r = min(m0 + tr, rows - 1);
     int arow;
     if constexpr (GATEUP) arow = shared ? r : p.perm[row_base + r];
@@ -146,7 +176,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
     const int kr = 4 * (wave * B_INS + i) + (lane >> 4);
-    const int c = (lane & 15) ^ (kr & 7);
+    const int c = (lane & 15) ^ (kr & 7) ^ (((kr >> 5) & 1) << 3);
     const int lc = c * 16;
     int gc;
     if constexpr (GATEUP) gc = lc < BNH ? n0 + lc : NH + n0 + (lc - BNH);
@@ -164,9 +194,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int lrow = lane & 15, kg = lane >> 4;
-  // A fragment: row wm*64 + 16 i + lrow, logical chunks 2 kg, 2 kg + 1; (row >> 1) & 7 == lrow >> 1
-  const int a_rd0 = (wm * (BM / WM) + lrow) * A_ROWB + (((2 * kg) ^ (lrow >> 1)) << 4);
-  const int a_rd1 = (wm * (BM / WM) + lrow) * A_ROWB + (((2 * kg + 1) ^ (lrow >> 1)) << 4);
+  // A fragment: row wm*64 + 16 i + lrow, logical chunks 2 kg, 2 kg + 1; row & 15 == lrow
+  const int a_rd0 = (wm * (BM / WM) + lrow) * A_ROWB + (((2 * kg) ^ a_swz(lrow)) << 4);
+  const int a_rd1 = (wm * (BM / WM) + lrow) * A_ROWB + (((2 * kg + 1) ^ a_swz(lrow)) << 4);
 
   i32x8 fb0[FN], fb1[FN], fa[2];
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -225,42 +255,67 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
 #pragma unroll
   for (int j = 0; j < FN; ++j) F8_BFRAG(fb0, j, 0);
   F8_AFRAG(fa[0], 0, 0);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
+  // one stage per iteration: unrolled by two, the register allocator moved
+  // the accumulators between the halves with v_accvgpr copies
+  for (int kt = 0; kt < nk; ++kt) {
     F8_STEP(kt, fb0, fb1);
-    F8_STEP(kt + 1, fb1, fb0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb0[j] = fb1[j];
   }
-  if (kt < nk) F8_STEP(kt, fb0, fb1);
   wait_vmcnt<0>();
 #undef F8_ISSUE
 #undef F8_BFRAG
 #undef F8_AFRAG
 #undef F8_STEP
 
-  // ---- epilogue (16x16 accumulator: lane holds rows 4*(lane/16)+q of column lane%16)
+  // ---- epilogue (16x16 accumulator: lane holds rows 4*(lane/16)+q of column
+  // lane%16).  No global load sits between two stores through C (the compiler
+  // must assume they may alias, so each would wait a full round trip): the
+  // column scales are loaded first, the row metadata comes through LDS (the
+  // ring is free once every wave's DMA has landed) and the shared expert's
+  // output is loaded one fragment block ahead of the stores that consume it.
   const int lcol = lane & 15;
   const int rq = 4 * (lane >> 4);
+  const int wrow = wm * (BM / WM) + rq;   // tile row of fragment 0, q = 0
+  constexpr int BNW = BNH / WN;           // output columns per wave
+  float csc[FN];                          // column scales of this lane's fragments
+  {
+    const float* sB = GATEUP ? (shared ? p.sB_shared : p.sB + static_cast<int64_t>(g) * 2 * NH)
+                             : (MODE == MODE_DOWN_ROUTED ? p.sB + static_cast<int64_t>(g) * NH : p.sB_shared);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int jj = GATEUP ? j % (FN / 2) : j;
+      const int col = n0 + wn * BNW + jj * 16 + lcol;
+      csc[j] = col < NH ? sB[(GATEUP && j >= FN / 2 ? NH : 0) + col] : 0.0f;
+    }
+  }
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+  __syncthreads();
+  if (tid < BM) {
+    reinterpret_cast<__attribute__((address_space(3))) float*>(As)[tid] = row_scale;
+    reinterpret_cast<__attribute__((address_space(3))) int*>(As)[BM + tid] = row_out;
+  }
+  __syncthreads();
   if constexpr (GATEUP) {
     constexpr int HF = FN / 2;
-    const float* sB = shared ? p.sB_shared : p.sB + static_cast<int64_t>(g) * 2 * NH;
     float* C = reinterpret_cast<float*>(shared ? p.C_shared : p.C);
     uint32_t* amax = shared ? p.amax_shared : p.amax;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = m0 + wm * (BM / WM) + i * 16 + rq + q;
+        const int r = m0 + wrow + i * 16 + q;
         const bool valid = r < rows;
         const int orow = row_base + min(r, rows - 1);
-        const int tok = shared ? min(r, rows - 1) : p.perm[orow];
-        const float scale = (shared ? 1.0f : p.gate[tok]) * (shared ? p.sA_shared : p.sA)[tok];
         float rmax = 0.f;
 #pragma unroll
         for (int j = 0; j < HF; ++j) {
-          const int col = n0 + wn * (BNH / WN) + j * 16 + lcol;
+          const int col = n0 + wn * BNW + j * 16 + lcol;
           if (valid && col < NH) {
-            const float gv = acc[i][j][q] * scale * sB[col];
-            const float uv = acc[i][j + HF][q] * scale * sB[NH + col];
+            const float gv = acc[i][j][q] * sc[q] * csc[j];
+            const float uv = acc[i][j + HF][q] * sc[q] * csc[j + HF];
             const float h = silu_f(gv) * uv;
             C[static_cast<int64_t>(orow) * NH + col] = h;
             rmax = fmaxf(rmax, fabsf(h));
@@ -271,34 +326,60 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
         if (valid && lcol == 0) atomicMax(&amax[orow], __float_as_uint(rmax));
       }
     }
-  } else {
-    const float* sB = (MODE == MODE_DOWN_ROUTED) ? p.sB + static_cast<int64_t>(g) * NH : p.sB_shared;
-    const float* sA = (MODE == MODE_DOWN_ROUTED) ? p.sA : p.sA_shared;
+  } else if constexpr (MODE == MODE_DOWN_SHARED) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = m0 + wm * (BM / WM) + i * 16 + rq + q;
+        const int r = m0 + wrow + i * 16 + q;
         if (r >= rows) continue;
-        const int arow = row_base + r;
-        const int orow = (MODE == MODE_DOWN_ROUTED) ? p.perm[arow] : r;
-        const float rs = sA[arow];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * (BN / WN) + j * 16 + lcol;
+          const int col = n0 + wn * BNW + j * 16 + lcol;
           if (col >= NH) continue;
-          const int64_t o = static_cast<int64_t>(orow) * NH + col;
-          const float v = acc[i][j][q] * rs * sB[col];
-          if constexpr (MODE == MODE_DOWN_SHARED) {
-            reinterpret_cast<float*>(p.C_shared)[o] = v;
-          } else {
-            const float y = v + p.Y[o];
-            if (p.out_bf16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16(y);
-            else reinterpret_cast<float*>(p.C)[o] = y;
-          }
+          reinterpret_cast<float*>(p.C_shared)[static_cast<int64_t>(r) * NH + col] = acc[i][j][q] * sc[q] * csc[j];
         }
       }
     }
+  } else {
+    int orow[FM][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const i32x4 o4 = *(const lds_i32x4*)(As + 4 * (BM + wrow + 16 * i));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) orow[i][q] = o4[q];
+    }
+    float y[2][4][FN];
+#define F8_LOAD_Y(b, i)                                                                        \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                            \
+      const bool ok_ = m0 + wrow + (i) * 16 + q < rows;                                        \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                         \
+        const int col_ = n0 + wn * BNW + j * 16 + lcol;                                        \
+        y[b][q][j] = (ok_ && col_ < NH) ? p.Y[static_cast<int64_t>(orow[i][q]) * NH + col_] : 0.0f; \
+      }                                                                                        \
+    }
+    F8_LOAD_Y(0, 0)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i + 1 < FM) { F8_LOAD_Y((i + 1) & 1, i + 1) }
+      const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + wrow + i * 16 + q;
+        if (r >= rows) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + wn * BNW + j * 16 + lcol;
+          if (col >= NH) continue;
+          const int64_t o = static_cast<int64_t>(orow[i][q]) * NH + col;
+          const float v = acc[i][j][q] * sc[q] * csc[j] + y[i & 1][q][j];
+          if (p.out_bf16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16(v);
+          else reinterpret_cast<float*>(p.C)[o] = v;
+        }
+      }
+    }
+#undef F8_LOAD_Y
   }
 }
 

@@ -83,6 +83,8 @@ hipError_t launch_gemm(int mode, int w_dtype, const GemmArgs& a, int grid_m_toke
 bool bf16_v2_supported(int K, int N, int N_shared);
 hipError_t launch_gemm_bf16_v2(int mode, int bm, const GemmArgs& a, int T, hipStream_t s,
                                const int32_t* tiles_all);
+// The 256-row tiles of launch_gemm_bf16_v2 (separate unit: AGPR-form MFMAs).
+hipError_t launch_gemm_bf16_tall(int mode, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all);
 
 // fp8 prefill tiling (128 x 256 tiles, K 128 per stage; K multiple of 128).
 hipError_t launch_gemm_fp8(int mode, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all);
