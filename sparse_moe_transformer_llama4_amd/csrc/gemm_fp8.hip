@@ -8,7 +8,9 @@
 // v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales), 32 K bytes per lane.
 //   * workgroup tile 128 x 256 (gate/up: 128 gate + 128 up columns), 4 waves
 //     of 64 x 128 accumulators; one pipeline stage = K 128 (one MFMA step);
-//   * direct-to-LDS loads into a 3-deep ring of 48 KB stages;
+//   * direct-to-LDS loads (scalar-base form) into a 3-deep ring of 48 KB
+//     stages; a slot is refilled as soon as its stage's fragments are in
+//     registers, so two stages are always in flight;
 //   * A rows (128 B) are stored with 16-byte chunk k of row r at
 //     k ^ a_swz(r & 15), a permutation found by measuring LDS read rates: the
 //     fragment reads (16 rows x 16 B per 16-lane group) run at the full
@@ -21,8 +23,9 @@
 //     (ds_read_b64_tr_b8): each 16-lane group reads 8 K rows x 16 columns and
 //     every lane receives its column's 8 K bytes; four reads give the 32 K
 //     bytes of the MFMA operand;
-//   * XCD-aware tile order and one explicit vmcnt wait + s_barrier per stage,
-//     as in the bf16 kernels.
+//   * XCD-aware tile order, one explicit vmcnt wait + s_barrier per stage,
+//     and the MFMA stream with the next stage's LDS reads and the DMA
+//     threaded through it, as in the bf16 kernels.
 #include "common.h"
 #include "launch.h"
 
@@ -46,7 +49,6 @@ constexpr int B_INS = B_STAGE / 1024 / 4;
 constexpr int LOADS = A_INS + B_INS;
 constexpr int FM = BM / WM / 16;         // 4
 constexpr int FN = BN / WN / 16;         // 8
-constexpr int JPB = FN / FM;             // weight fragments read per A block
 
 // Chunk permutation of an A row (see the header comment): XOR of 5, 7 and 1
 // selected by bits 0, 1 and 3 of the row.
@@ -61,25 +63,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Direct-to-LDS 16-byte load into m0 + 16 * lane (inline asm: it writes no
 // VGPR; the stage ring orders it with explicit vmcnt waits and barriers).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory", "m0");
+// Scalar-base form: `sbase` is wave-uniform and each lane adds its own 32-bit
+// byte offset, so advancing along K is one scalar add per stage.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory", "m0");
 }
 
-// 32 K bytes (rows 32*(lane/16) .. +31) of tile column col + lane%16.
-__device__ __forceinline__ i32x8 read_b_frag(const lds_u8* bs, int col, int lane) {
-  const int s = lane & 15, g = lane >> 4;
-  // rows of one read: 32 g + s/2 (+ 8 q), so (row & 7) = s/2 and (row >> 5) & 1 = g & 1
-  const int pchunk = (col >> 4) ^ ((s >> 1) & 7) ^ ((g & 1) << 3);
-  const lds_u8* p = bs + (32 * g + (s >> 1)) * B_ROWB + pchunk * 16 + 8 * (s & 1);
-  i32x8 r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 8 * q * B_ROWB));
-    r[2 * q] = v[0];
-    r[2 * q + 1] = v[1];
-  }
-  return r;
-}
 
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
@@ -153,11 +143,11 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
 
   // ---- DMA sources.  A: instruction i fills tile rows 8*(wave*A_INS + i) + lane/8,
   // the lane fetching the logical chunk its slot holds under the swizzle.
-  const uint8_t* abase;
-  if constexpr (GATEUP) abase = reinterpret_cast<const uint8_t*>(shared ? p.A_shared : p.A);
-  else if constexpr (MODE == MODE_DOWN_SHARED) abase = reinterpret_cast<const uint8_t*>(p.A_shared);
-  else abase = reinterpret_cast<const uint8_t*>(p.A);
-  uint32_t a_off[A_INS];
+  const uint8_t* a_src;
+  if constexpr (GATEUP) a_src = reinterpret_cast<const uint8_t*>(shared ? p.A_shared : p.A);
+  else if constexpr (MODE == MODE_DOWN_SHARED) a_src = reinterpret_cast<const uint8_t*>(p.A_shared);
+  else a_src = reinterpret_cast<const uint8_t*>(p.A);
+  uint32_t a_voff[A_INS];   // byte offsets (the caller guarantees T * K < 2^31)
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
     const int tr = 8 * (wave * A_INS + i) + (lane >> 3);
@@ -167,12 +157,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
     if constexpr (GATEUP) arow = shared ? r : p.perm[row_base + r];
     else if constexpr (MODE == MODE_DOWN_SHARED) arow = r;
     else arow = row_base + r;
-    a_off[i] = static_cast<uint32_t>(arow) * static_cast<uint32_t>(K) + c * 16;
+    a_voff[i] = static_cast<uint32_t>(arow) * static_cast<uint32_t>(K) + c * 16;
   }
   // weights: instruction i fills K rows 4*(wave*B_INS + i) + lane/16; slot = chunk lane%16
-  const uint8_t* bbase = reinterpret_cast<const uint8_t*>(shared ? p.B_shared : p.B) +
+  const uint8_t* b_src = reinterpret_cast<const uint8_t*>(shared ? p.B_shared : p.B) +
                          (shared ? 0 : static_cast<int64_t>(g) * K * ldb);
-  int64_t b_off[B_INS];
+  uint32_t b_voff[B_INS];
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
     const int kr = 4 * (wave * B_INS + i) + (lane >> 4);
@@ -182,9 +172,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
     if constexpr (GATEUP) gc = lc < BNH ? n0 + lc : NH + n0 + (lc - BNH);
     else gc = n0 + lc;
     const bool ok = n0 + (GATEUP ? lc % BNH : lc) < NH;
-    b_off[i] = static_cast<int64_t>(kr) * ldb + (ok ? gc : 0);   // clamped columns are never stored
+    b_voff[i] = static_cast<uint32_t>(kr * ldb + (ok ? gc : 0));   // clamped columns are never stored
   }
-  const int64_t b_kstride = static_cast<int64_t>(BK) * ldb;
+  const int64_t b_kstep = static_cast<int64_t>(BK) * ldb;
   const int nk = K / BK;
 
   f32x4 acc[FM][FN];
@@ -193,79 +183,136 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // ---- LDS read addresses: per-lane bases, slot and fragment offsets as
+  // immediates.
+  const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(As));
   const int lrow = lane & 15, kg = lane >> 4;
-  // A fragment: row wm*64 + 16 i + lrow, logical chunks 2 kg, 2 kg + 1; row & 15 == lrow
-  const int a_rd0 = (wm * (BM / WM) + lrow) * A_ROWB + (((2 * kg) ^ a_swz(lrow)) << 4);
-  const int a_rd1 = (wm * (BM / WM) + lrow) * A_ROWB + (((2 * kg + 1) ^ a_swz(lrow)) << 4);
-
-  i32x8 fb0[FN], fb1[FN], fa[2];
+  // A fragment i of slot sl: row wm*64 + 16 i + lrow, logical chunks 2 kg and
+  // 2 kg + 1 (row & 15 == lrow) at a_rd0/1 + sl*A_STAGE + i*16*A_ROWB
+  const uint32_t a_rd0 = ring + (wm * (BM / WM) + lrow) * A_ROWB + (((2 * kg) ^ a_swz(lrow)) << 4);
+  const uint32_t a_rd1 = ring + (wm * (BM / WM) + lrow) * A_ROWB + (((2 * kg + 1) ^ a_swz(lrow)) << 4);
+  // weight fragment j of slot sl (32 K bytes of one column per lane): four
+  // byte-transpose reads at b_rd[j] + sl*B_STAGE + 8 q rows.  Lane s of
+  // 16-lane group g points at row 32 g + s/2 (+ 8 q), 8 bytes of the 16-byte
+  // chunk holding its column block; rows of one read share (row & 7) = s/2
+  // and (row >> 5) & 1 = g & 1.
+  uint32_t b_rd[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    int col;
+    if constexpr (GATEUP) col = (j < FN / 2 ? 0 : BNH) + wn * (BNH / WN) + (j % (FN / 2)) * 16;
+    else col = wn * (BN / WN) + j * 16;
+    const int s = lane & 15, g = lane >> 4;
+    const int pchunk = (col >> 4) ^ ((s >> 1) & 7) ^ ((g & 1) << 3);
+    b_rd[j] = ring + NBUF * A_STAGE + (32 * g + (s >> 1)) * B_ROWB + pchunk * 16 + 8 * (s & 1);
+  }
+  typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+#define F8_AREAD(FA, i, SL)                                                                    \
+  do {                                                                                         \
+    const i32x4 lo_ = *(const lds_i32x4*)((const lds_u8*)(uintptr_t)a_rd0 + (SL) * A_STAGE + (i) * 16 * A_ROWB); \
+    const i32x4 hi_ = *(const lds_i32x4*)((const lds_u8*)(uintptr_t)a_rd1 + (SL) * A_STAGE + (i) * 16 * A_ROWB); \
+    FA[i] = i32x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};             \
+  } while (0)
+#define F8_BREAD(FB, j, SL)                                                                    \
+  do {                                                                                         \
+    const lds_u8* q_ = (const lds_u8*)(uintptr_t)b_rd[j] + (SL) * B_STAGE;                     \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                            \
+      const i32x2 v_ = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(q_ + 8 * q * B_ROWB)); \
+      FB[j][2 * q] = v_[0];                                                                    \
+      FB[j][2 * q + 1] = v_[1];                                                                \
+    }                                                                                          \
+  } while (0)
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t a_lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(As)) + wave_u * (A_INS * 1024);
-  const uint32_t b_lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(Bs)) + wave_u * (B_INS * 1024);
+  const uint32_t a_lds0 = ring + wave_u * (A_INS * 1024);
+  const uint32_t b_lds0 = ring + NBUF * A_STAGE + wave_u * (B_INS * 1024);
+#define F8_DMA_A(i, st, SL)                                                                    \
+  dma16(a_src + static_cast<int64_t>(min((st), nk - 1)) * BK, a_voff[i], a_lds0 + (SL) * A_STAGE + (i) * 1024)
+#define F8_DMA_B(i, st, SL)                                                                    \
+  dma16(b_src + static_cast<int64_t>(min((st), nk - 1)) * b_kstep, b_voff[i], b_lds0 + (SL) * B_STAGE + (i) * 1024)
 
-#define F8_ISSUE(st)                                                                           \
+  // Operands in registers: all of a stage's fragments double-buffered.
+  i32x8 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
+  constexpr int NMF = FM * FN;
+  constexpr int NOPS = FM + FN + A_INS + B_INS;
+  // One stage (step kt + R, slot R % NBUF free, operands FA/FB): the MFMA
+  // stream starts right after the previous barrier; the reads of the next
+  // stage's fragments and then the DMA of stage kt + R + NBUF into the free
+  // slot are threaded through it; the end waits for stage kt + R + 2 and the
+  // reads, and the barrier publishes that stage and frees the next slot.
+#define F8_STEP(R, FA, FB, FA2, FB2)                                                           \
   do {                                                                                         \
-    const int s_ = min((st), nk - 1);                                                          \
-    const uint32_t b_ = static_cast<uint32_t>((st) % NBUF);                                    \
-    _Pragma("unroll") for (int i = 0; i < A_INS; ++i)                                          \
-      dma16(abase + a_off[i] + s_ * BK, a_lds0 + b_ * A_STAGE + i * 1024);                     \
-    _Pragma("unroll") for (int i = 0; i < B_INS; ++i)                                          \
-      dma16(bbase + b_off[i] + s_ * b_kstride, b_lds0 + b_ * B_STAGE + i * 1024);              \
-  } while (0)
-#define F8_BFRAG(FB, j, st)                                                                    \
-  do {                                                                                         \
-    int col_;                                                                                  \
-    if constexpr (GATEUP) col_ = ((j) < FN / 2 ? 0 : BNH) + wn * (BNH / WN) + ((j) % (FN / 2)) * 16; \
-    else col_ = wn * (BN / WN) + (j) * 16;                                                     \
-    FB[j] = read_b_frag(Bs + ((st) % NBUF) * B_STAGE, col_, lane);                             \
-  } while (0)
-#define F8_AFRAG(dst, i, st)                                                                   \
-  do {                                                                                         \
-    const lds_u8* ab_ = As + ((st) % NBUF) * A_STAGE + (i) * 16 * A_ROWB;                      \
-    const i32x4 lo_ = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(ab_ + a_rd0); \
-    const i32x4 hi_ = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(ab_ + a_rd1); \
-    dst = i32x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};               \
-  } while (0)
-  // One stage (K 128): DMA of stage kt+2; weight fragments of stage kt+1;
-  // FM blocks of FN MFMAs on stage kt with the next A block read ahead; then
-  // publish stage kt+2 (with a 3-deep ring every DMA issued so far).
-#define F8_STEP(kt, FB, FB2)                                                                   \
-  do {                                                                                         \
-    F8_ISSUE((kt) + 2);                                                                        \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                           \
-      if (i + 1 < FM) F8_AFRAG(fa[(i + 1) & 1], i + 1, (kt));                                  \
-      else F8_AFRAG(fa[(i + 1) & 1], 0, (kt) + 1);                                             \
-      _Pragma("unroll") for (int jj = 0; jj < JPB; ++jj) F8_BFRAG(FB2, i * JPB + jj, (kt) + 1); \
-      __builtin_amdgcn_sched_barrier(0);                                                       \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i & 1], FB[j], acc[i][j], 0, 0, 0, \
-                                                                      127, 0, 127);             \
+    constexpr int sl_ = (R) % NBUF, nsl_ = ((R) + 1) % NBUF;                                   \
+    const int sd_ = kt + (R) + NBUF;                                                           \
+    _Pragma("unroll") for (int m_ = 0; m_ < NMF; ++m_) {                                       \
+      acc[m_ / FN][m_ % FN] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(               \
+          FA[m_ / FN], FB[m_ % FN], acc[m_ / FN][m_ % FN], 0, 0, 0, 127, 0, 127);              \
+      _Pragma("unroll") for (int o_ = 0; o_ < NOPS; ++o_) {                                    \
+        if (o_ * NMF / NOPS == m_) {                                                           \
+          if (o_ < FM) F8_AREAD(FA2, o_, nsl_);                                                \
+          else if (o_ < FM + FN) F8_BREAD(FB2, o_ - FM, nsl_);                                 \
+          else if (o_ < FM + FN + A_INS) F8_DMA_A(o_ - FM - FN, sd_, sl_);                     \
+          else F8_DMA_B(o_ - FM - FN - A_INS, sd_, sl_);                                       \
+        }                                                                                      \
+      }                                                                                        \
       __builtin_amdgcn_sched_barrier(0);                                                       \
     }                                                                                          \
-    wait_vmcnt<0>();                                                                           \
+    wait_vmcnt<(NBUF - 2) * LOADS>();                                                          \
     __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                                       \
     __builtin_amdgcn_s_barrier();                                                              \
   } while (0)
 
-  // prologue: stages 0 and 1 landed and published; operands of stage 0 read
-  F8_ISSUE(0);
-  F8_ISSUE(1);
-  wait_vmcnt<0>();
+  // prologue: stages 0 .. NBUF-1 in flight; 0 and 1 landed and published;
+  // stage 0's fragments in registers and its slot released
+#pragma unroll
+  for (int st = 0; st < NBUF; ++st) {
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) F8_DMA_A(i, st, st);
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) F8_DMA_B(i, st, st);
+  }
+  wait_vmcnt<(NBUF - 2) * LOADS>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int j = 0; j < FN; ++j) F8_BFRAG(fb0, j, 0);
-  F8_AFRAG(fa[0], 0, 0);
-  // one stage per iteration: unrolled by two, the register allocator moved
-  // the accumulators between the halves with v_accvgpr copies
-  for (int kt = 0; kt < nk; ++kt) {
-    F8_STEP(kt, fb0, fb1);
+  for (int i = 0; i < FM; ++i) F8_AREAD(fa0, i, 0);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb0[j] = fb1[j];
+  for (int j = 0; j < FN; ++j) F8_BREAD(fb0, j, 0);
+  __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */
+  __builtin_amdgcn_s_barrier();
+  // unrolled by 6 = ring depth x register parity: slots and buffers are
+  // compile-time; the accumulators are pinned to AGPRs at each iteration
+  // (otherwise the register allocator rotates them with v_accvgpr copies)
+  static_assert(NBUF == 3, "the loop below is unrolled by 2 x the ring depth");
+  int kt = 0;
+  for (; kt + 6 <= nk; kt += 6) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+    F8_STEP(0, fa0, fb0, fa1, fb1);
+    F8_STEP(1, fa1, fb1, fa0, fb0);
+    F8_STEP(2, fa0, fb0, fa1, fb1);
+    F8_STEP(3, fa1, fb1, fa0, fb0);
+    F8_STEP(4, fa0, fb0, fa1, fb1);
+    F8_STEP(5, fa1, fb1, fa0, fb0);
+  }
+  if (kt < nk) {
+    F8_STEP(0, fa0, fb0, fa1, fb1);
+    if (kt + 1 < nk) {
+      F8_STEP(1, fa1, fb1, fa0, fb0);
+      if (kt + 2 < nk) {
+        F8_STEP(2, fa0, fb0, fa1, fb1);
+        if (kt + 3 < nk) {
+          F8_STEP(3, fa1, fb1, fa0, fb0);
+          if (kt + 4 < nk) F8_STEP(4, fa0, fb0, fa1, fb1);
+        }
+      }
+    }
   }
   wait_vmcnt<0>();
-#undef F8_ISSUE
-#undef F8_BFRAG
-#undef F8_AFRAG
+#undef F8_AREAD
+#undef F8_BREAD
+#undef F8_DMA_A
+#undef F8_DMA_B
 #undef F8_STEP
 
   // ---- epilogue (16x16 accumulator: lane holds rows 4*(lane/16)+q of column
