@@ -3,6 +3,7 @@
 //   router -> scan -> permutation -> grouped gate/up GEMM (+ shared) ->
 //   [e4m3: quantise h] -> shared down GEMM -> routed down GEMM + combine,
 // all on the caller's stream, with no host synchronisation.
+#include <algorithm>
 #include <cstring>
 #include <new>
 
@@ -134,22 +135,24 @@ Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
 constexpr int64_t kPrefillTokens = 256;
 constexpr int64_t kDecodeTokens = 64;
 
-// Tile height for the routed groups: the mean group size decides between
-// 256-, 128- and 64-row tiles (a taller tile reuses each weight tile for more
-// rows; a shorter one wastes fewer MFMA rows on ragged group tails).
+// Tile height for the routed groups: 256 rows when the mean group holds at
+// least 192 tokens, else 128 (a taller tile reuses each weight tile for more
+// rows; a shorter one wastes fewer MFMA rows on ragged group tails).  64-row
+// tiles lost to 128-row ones even at 64 tokens per expert with skewed routing.
 int routed_tile_rows(int64_t T, int E) {
   const int64_t mean = T / E;
-  return mean >= 192 ? 256 : mean >= 96 ? 128 : 64;
+  return mean >= 192 ? 256 : 128;
 }
 
 // Tile height for a down GEMM (N = d columns in 256-wide tiles) over `rows`
-// tokens in `groups` groups: 256-row tiles only when they still give at
-// least ~3 full rounds of workgroups over the GPU's CUs, else 128 (fewer
-// idle CUs in the last round outweigh the lower per-tile efficiency).
+// tokens in `groups` groups: 256-row tiles when they still give at least
+// ~1.5 rounds of workgroups over the GPU's 256 CUs, else 128 (fewer idle CUs
+// in the last round outweigh the lower per-tile efficiency).  Measured on the
+// Scout- and Maverick-shaped prefill layers.
 int down_tile_rows(int64_t rows, int groups, int d, int bm_max) {
   const int64_t ntile = (d + 255) / 256;
   const int64_t t256 = ((rows + 255) / 256 + (groups > 1 ? groups / 2 : 0)) * ntile;
-  if (bm_max >= 256 && t256 >= 3 * 256) return 256;
+  if (bm_max >= 256 && t256 >= 384) return 256;
   return bm_max >= 128 ? 128 : bm_max;
 }
 
@@ -296,11 +299,14 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g1.C_shared = ws + L.h_s;
   g1.amax = amax_r;
   g1.amax_shared = amax_s;
-  const bool v2 = c.w_dtype == MOE_BF16 && T >= kPrefillTokens && bf16_v2_supported(c.d, c.f, c.f_shared) &&
+  // the prefill kernels address activations with 32-bit byte offsets
+  const int64_t kmax = std::max(std::max(c.d, c.f), c.f_shared);
+  const bool offsets32 = T * kmax * 2 < (int64_t{1} << 31);
+  const bool v2 = c.w_dtype == MOE_BF16 && T >= kPrefillTokens && offsets32 && bf16_v2_supported(c.d, c.f, c.f_shared) &&
                   bf16_v2_supported(c.f, c.d, c.d) && bf16_v2_supported(c.f_shared, c.d, c.d);
   const bool dec = c.w_dtype == MOE_BF16 && T <= kDecodeTokens && decode_supported(c.d) &&
                    decode_supported(c.f) && decode_supported(c.f_shared);
-  const bool f8 = fp8 && T >= kPrefillTokens;
+  const bool f8 = fp8 && T >= kPrefillTokens && offsets32;
   const int bm_routed = routed_tile_rows(T, c.n_experts);
   if (f8) {
     g1.group_lo = 0;

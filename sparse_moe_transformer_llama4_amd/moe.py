@@ -255,8 +255,9 @@ class StageEvents:
 
     def __init__(self):
         h = _hip_runtime()
-        self.ev = (ctypes.c_void_p * (MOE_NUM_STAGES + 1))()
-        for i in range(MOE_NUM_STAGES + 1):
+        self.n = MOE_NUM_STAGES + 1
+        self.ev = (ctypes.c_void_p * self.n)()
+        for i in range(self.n):
             e = ctypes.c_void_p()
             if h.hipEventCreate(ctypes.byref(e)) != 0:
                 raise RuntimeError("hipEventCreate failed")
@@ -274,9 +275,14 @@ class StageEvents:
         return out
 
     def __del__(self):
-        for i in range(MOE_NUM_STAGES + 1):
-            if self.ev[i]:
-                self.h.hipEventDestroy(self.ev[i])
+        # uses only instance attributes: module globals may already be gone
+        # when this runs at interpreter exit
+        ev, h = getattr(self, "ev", None), getattr(self, "h", None)
+        if ev is None or h is None:
+            return
+        for i in range(getattr(self, "n", 0)):
+            if ev[i]:
+                h.hipEventDestroy(ev[i])
 
 
 def moe_forward_timed(plan: Plan, x: torch.Tensor, w: dict, events: StageEvents, out: torch.Tensor,
