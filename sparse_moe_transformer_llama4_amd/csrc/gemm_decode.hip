@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
   constexpr int DBM = 16 * FMMAX;               // rows per tile
   constexpr int ASTAGE = FMMAX * 1024;          // activation bytes per stage (16 rows x 64 B per KB)
   constexpr int STAGE = WSTAGE + ASTAGE;
-  constexpr int DNBUF = FMMAX == 1 ? 4 : 3;     // per-wave ring depth (LDS: 4 x 4 x 9 KB / 4 x 3 x 10 KB)
+  constexpr int DNBUF = 4;                      // per-wave ring depth (LDS: 4 x 4 x 9 KB / 4 x 4 x 10 KB)
   constexpr int LOADS = INS + FMMAX;            // DMA instructions per stage per wave
   constexpr int PART = 4 * DBM * DBN * 4;       // bytes of the final partial sums
   constexpr int RING = 4 * DNBUF * STAGE;
@@ -123,9 +123,12 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
     }
   }
 
-  // ---- this wave's K quarter
-  const int kq = K >> 2;                        // multiple of 32
-  const int k0 = wave * kq;
+  // ---- this block's K range (split over blockIdx.z for the shared down
+  // GEMM, whose single M-tile would otherwise leave most CUs idle) and this
+  // wave's quarter of it
+  const int nsplit = gridDim.z;
+  const int kq = (K / nsplit) >> 2;             // multiple of 32
+  const int k0 = static_cast<int>(blockIdx.z) * (K / nsplit) + wave * kq;
   const int ns = kq / DBK;
 
   // weights: DMA instruction i fills K rows 4i .. 4i+3 of the stage; lane ->
@@ -263,11 +266,27 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
     const int* ot = reinterpret_cast<const int*>(smem + PART);
     float y[NIT];
     if constexpr (MODE == MODE_DOWN_ROUTED) {
+      // the shared expert's output, as y_parts K-split partials summed in order
+      const int nparts = p.y_parts > 1 ? p.y_parts : 1;
+      const int64_t pstride = static_cast<int64_t>(T) * NH;
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int e = tid + 256 * it;
-        const int r = e / BNH, col = n0 + e % BNH;
-        y[it] = (r < nvalid && col < NH) ? p.Y[static_cast<int64_t>(ot[r]) * NH + col] : 0.0f;
+      for (int it = 0; it < NIT; ++it) y[it] = 0.0f;
+      for (int s0 = 0; s0 < nparts; s0 += 4) {
+        float yv[4][NIT];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            const int e = tid + 256 * it;
+            const int r = e / BNH, col = n0 + e % BNH;
+            yv[u][it] = (s0 + u < nparts && r < nvalid && col < NH)
+                            ? p.Y[(s0 + u) * pstride + static_cast<int64_t>(ot[r]) * NH + col] : 0.0f;
+          }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int it = 0; it < NIT; ++it)
+            if (s0 + u < nparts) y[it] += yv[u][it];
       }
     }
 #pragma unroll
@@ -280,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
       const int64_t o = static_cast<int64_t>(orow) * NH + col;
       const float v = total(r, c);
       if constexpr (MODE == MODE_DOWN_SHARED) {
-        reinterpret_cast<float*>(p.C_shared)[o] = v;
+        reinterpret_cast<float*>(p.C_shared)[static_cast<int64_t>(blockIdx.z) * T * NH + o] = v;
       } else {
         const float yv = v + y[it];
         if (p.out_bf16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16(yv);
@@ -308,7 +327,9 @@ hipError_t launch_dec(const GemmArgs& a0, int T, hipStream_t s, const int32_t* t
   }
   if (gm <= 0) return hipSuccess;
   const int gn = (nmax + BNH - 1) / BNH;
-  hipLaunchKernelGGL((gemm_decode_kernel<MODE, FMMAX>), dim3(gm, gn), dim3(256), 0, s, a);
+  const int ks = (MODE == MODE_DOWN_SHARED && a.ksplit > 1) ? a.ksplit : 1;
+  if (a.K % (128 * ks) != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_decode_kernel<MODE, FMMAX>), dim3(gm, gn, ks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

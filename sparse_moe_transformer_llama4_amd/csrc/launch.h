@@ -55,6 +55,8 @@ struct GemmArgs {
   int out_bf16;          // DOWN_ROUTED: output dtype bf16 (else fp32)
   int group_lo, group_hi;  // groups [lo, hi) handled by this launch (group E = shared expert)
   int n_tiles;             // N-tiles per M-tile of this launch (set by the launcher)
+  int ksplit;              // decode DOWN_SHARED: K split over blocks; partial s at C_shared + s*T*N (0 = 1)
+  int y_parts;             // decode DOWN_ROUTED: Y holds this many partials, summed in order (0 = 1)
 };
 
 // Router in two launches: partial logits over K slices of d (the slice count

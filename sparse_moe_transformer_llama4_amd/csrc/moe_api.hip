@@ -36,6 +36,18 @@ bool config_dtypes_ok(const moe_config& c) {
 
 int k_multiple(const moe_config& c) { return c.w_dtype == MOE_E4M3 ? 128 : 64; }
 
+constexpr int64_t kDecodeTokensMax = 64;
+
+// Decode-sized calls split the shared down GEMM over K (its single M-tile
+// would leave most CUs idle): the number of partial shared outputs, summed in
+// order by the routed down GEMM.  1 for every other path.
+int decode_y_parts(const moe_config& c, int64_t T) {
+  if (T > kDecodeTokensMax || c.w_dtype != MOE_BF16) return 1;
+  for (int s = 8; s > 1; s >>= 1)
+    if (c.f_shared % (128 * s) == 0) return s;
+  return 1;
+}
+
 WsLayout layout_for(const moe_config& c, int64_t T) {
   WsLayout L{};
   size_t off = 0;
@@ -59,7 +71,7 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   L.tiles = take(kNumBM * (E + 2) * 4);
   L.h_r = take(t * c.f * hsz);
   L.h_s = take(t * c.f_shared * hsz);
-  L.y_s = take(t * c.d * 4);
+  L.y_s = take(t * c.d * 4 * static_cast<size_t>(decode_y_parts(c, T)));
   if (fp8) {
     L.hq_r = take(t * c.f);
     L.hq_s = take(t * c.f_shared);
@@ -133,7 +145,7 @@ Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
 // Token counts from which the bf16 prefill tiling is used, and up to which
 // the weight-streaming decode tiling is used.
 constexpr int64_t kPrefillTokens = 256;
-constexpr int64_t kDecodeTokens = 64;
+constexpr int64_t kDecodeTokens = kDecodeTokensMax;
 
 // Tile height for the routed groups: 256 rows when the mean group holds at
 // least 192 tokens, else 128 (a taller tile reuses each weight tile for more
@@ -313,11 +325,8 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     g1.group_hi = c.n_experts + 1;
     if ((e = launch_gemm_fp8(MODE_GATEUP, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
   } else if (dec) {
+    // routed groups and the shared expert in one launch of 32-row tiles
     g1.group_lo = 0;
-    g1.group_hi = c.n_experts;
-    if ((e = launch_gemm_decode(MODE_GATEUP, false, g1, Ti, stream, R.tiles)) != hipSuccess)
-      return hip_fail(plan, e);
-    g1.group_lo = c.n_experts;
     g1.group_hi = c.n_experts + 1;
     if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles)) != hipSuccess)
       return hip_fail(plan, e);
@@ -365,6 +374,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g2.E = c.n_experts;
   g2.offsets = R.offsets;
   g2.C_shared = y_s;
+  g2.ksplit = dec ? decode_y_parts(c, T) : 1;
   g2.group_lo = c.n_experts;
   g2.group_hi = c.n_experts + 1;
   e = f8   ? launch_gemm_fp8(MODE_DOWN_SHARED, g2, Ti, stream, R.tiles)
@@ -387,6 +397,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   g3.perm = R.perm;
   g3.C = out;
   g3.Y = y_s;
+  g3.y_parts = dec ? decode_y_parts(c, T) : 1;
   g3.out_bf16 = c.out_dtype == MOE_BF16;
   g3.group_lo = 0;
   g3.group_hi = c.n_experts;

@@ -327,16 +327,33 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouterArgs a, int nspl
   __shared__ int cnt_s[256];
   __shared__ int ids[kRouteTokens];
   __shared__ int sm[(1 + kNumBM) * 4];
+  __shared__ float lg[kRouteTokens * 256];
   const int tid = threadIdx.x, E = a.E, T = a.T;
   cnt_s[tid] = 0;
+  // logits of every (token, expert) pair, the K-slice partials summed in
+  // slice order; the loads of a pair are issued together (a dependent chain
+  // of global loads per token took tens of microseconds)
+  for (int i = tid; i < T * E; i += 256) {
+    const int t = i / E, e = i - t * E;
+    float v = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += 16) {
+      float pv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        pv[u] = s0 + u < nsplit ? part[(static_cast<int64_t>(s0 + u) * T + t) * E + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (s0 + u < nsplit) v += pv[u];
+    }
+    if (a.bias) v += a.bias[e];
+    lg[i] = v;
+  }
   __syncthreads();
   if (tid < T) {
     float best = -INFINITY;
     int bi = 0x7fffffff;
     for (int e = 0; e < E; ++e) {
-      float v = 0.f;
-      for (int s = 0; s < nsplit; ++s) v += part[(static_cast<int64_t>(s) * T + tid) * E + e];
-      if (a.bias) v += a.bias[e];
+      const float v = lg[tid * E + e];
       if (v > best) { best = v; bi = e; }
     }
     bi = min(bi, E - 1);  // only reachable with non-finite logits (outside the contract)
