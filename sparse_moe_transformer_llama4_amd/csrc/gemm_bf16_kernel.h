@@ -76,11 +76,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr bool GATEUP = MODE == MODE_GATEUP;
   constexpr int BNH = GATEUP ? BN / 2 : BN;
   constexpr int A_STAGE = BM * A_ROWB;
-  // LDS ring of 4 stages.  A stage's slot is refilled as soon as its
-  // fragments are in registers, so three stages are always in flight; the
+  // LDS ring of NBUF stages.  A stage's slot is refilled as soon as its
+  // fragments are in registers, so NBUF - 1 stages are always in flight; the
   // main loop is unrolled by the ring depth so that slot indices (and the
-  // register double buffer's parity) are compile-time constants.
-  constexpr int NBUF = 4;
+  // register double buffer's parity) are compile-time constants.  Fetches
+  // that miss L2 take thousands of cycles under load: 128-row tiles, which
+  // consume a stage every ~570 cycles, keep 5 in flight (6 x 24 KB); 256-row
+  // tiles (~1250 cycles per stage) keep 3 (4 x 32 KB); 64-row tiles keep 3
+  // per workgroup with two workgroups per CU (2 x 4 x 20 KB).
+  constexpr int NBUF = BM == 128 ? 6 : 4;
   constexpr int A_INS = A_STAGE / 1024 / 4;   // 1 KB DMA instructions per wave per stage (A)
   constexpr int B_INS = B_STAGE / 1024 / 4;   // (weights)
   constexpr int LOADS = A_INS + B_INS;        // VMEM instructions per wave per stage
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   for (int j = 0; j < FN; ++j) MOE_BREAD(fb0, j, 0);
   __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */
   __builtin_amdgcn_s_barrier();
-  static_assert(NBUF == 4, "the loop below is unrolled by the ring depth");
+  static_assert(NBUF == 4 || NBUF == 6, "the loop below is unrolled by the ring depth");
   int kt = 0;
   for (; kt + NBUF <= nk; kt += NBUF) {
     // 256-row tiles keep their accumulators in AGPRs: pinning them there at
@@ -318,12 +322,24 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
     MOE_STEP(1, fa1, fb1, fa0, fb0);
     MOE_STEP(2, fa0, fb0, fa1, fb1);
     MOE_STEP(3, fa1, fb1, fa0, fb0);
+    if constexpr (NBUF == 6) {
+      MOE_STEP(4, fa0, fb0, fa1, fb1);
+      MOE_STEP(5, fa1, fb1, fa0, fb0);
+    }
   }
   if (kt < nk) {
     MOE_STEP(0, fa0, fb0, fa1, fb1);
     if (kt + 1 < nk) {
       MOE_STEP(1, fa1, fb1, fa0, fb0);
-      if (kt + 2 < nk) MOE_STEP(2, fa0, fb0, fa1, fb1);
+      if (kt + 2 < nk) {
+        MOE_STEP(2, fa0, fb0, fa1, fb1);
+        if constexpr (NBUF == 6) {
+          if (kt + 3 < nk) {
+            MOE_STEP(3, fa1, fb1, fa0, fb0);
+            if (kt + 4 < nk) MOE_STEP(4, fa0, fb0, fa1, fb1);
+          }
+        }
+      }
     }
   }
   wait_vmcnt<0>();

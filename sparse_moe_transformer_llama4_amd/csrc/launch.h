@@ -69,8 +69,11 @@ hipError_t launch_router(const RouterArgs& a, int x_dtype, float* part, hipStrea
 hipError_t launch_route_small(const RouterArgs& a, int x_dtype, float* part, int32_t* counts, int32_t* offsets,
                               int32_t* tiles, int32_t* perm, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
-hipError_t launch_perm(const int32_t* idx, const int32_t* base, int T, int E, int32_t* perm,
-                       hipStream_t s);
+hipError_t launch_perm(const int32_t* idx, const int32_t* base, const int32_t* offsets, int T, int E,
+                       int32_t* perm, hipStream_t s);
+// The fixed-order finish of launch_router over `nsplit` partial logit slices
+// (used with nsplit = 1 when the logits come from the prefill GEMM).
+hipError_t launch_router_finish(const RouterArgs& a, int nsplit, const float* part, hipStream_t s);
 hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* sx, hipStream_t s);
 hipError_t launch_quant_h(const float* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
                           float* sh, hipStream_t s);

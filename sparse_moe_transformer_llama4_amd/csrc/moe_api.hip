@@ -176,12 +176,32 @@ hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_we
                 R.idx, R.gate, R.hist};
   if (T > 0 && T <= kRouteTokens)
     return launch_route_small(ra, c.x_dtype, R.logits, R.counts, R.offsets, R.tiles, R.perm, s);
-  if (T > 0) {
+  // Prefill-sized bf16 calls with E a multiple of 64: the logits x·W_router
+  // come from the pipelined bf16 GEMM (its fp32 [T][N] mode), then the
+  // fixed-order finish; otherwise the dedicated router kernels.
+  const bool gemm_router = c.x_dtype == MOE_BF16 && T >= kPrefillTokens && c.n_experts % 64 == 0 &&
+                           bf16_v2_supported(c.d, c.n_experts, c.n_experts) &&
+                           static_cast<int64_t>(T) * c.d * 2 < (int64_t{1} << 31);
+  if (T > 0 && gemm_router) {
+    GemmArgs g{};
+    g.A_shared = x;
+    g.B_shared = w->w_router;
+    g.K = c.d;
+    g.N = c.n_experts;
+    g.N_shared = c.n_experts;
+    g.T = T;
+    g.E = c.n_experts;
+    g.C_shared = R.logits;
+    g.group_lo = c.n_experts;
+    g.group_hi = c.n_experts + 1;
+    if ((e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, 64, g, T, s, R.tiles)) != hipSuccess) return e;
+    if ((e = launch_router_finish(ra, 1, R.logits, s)) != hipSuccess) return e;
+  } else if (T > 0) {
     if ((e = launch_router(ra, c.x_dtype, R.logits, s)) != hipSuccess) return e;
   }
   ScanArgs sa{R.hist, (T + kRouteTokens - 1) / kRouteTokens, c.n_experts, T, R.counts, R.offsets, R.tiles};
   if ((e = launch_scan(sa, s)) != hipSuccess) return e;
-  if (T > 0 && (e = launch_perm(R.idx, R.hist, T, c.n_experts, R.perm, s)) != hipSuccess) return e;
+  if (T > 0 && (e = launch_perm(R.idx, R.hist, R.offsets, T, c.n_experts, R.perm, s)) != hipSuccess) return e;
   return hipSuccess;
 }
 

@@ -294,28 +294,35 @@ __device__ void offsets_and_tiles(int cnt, int E, int T, int32_t* counts, int32_
 }
 
 // One workgroup: column scan of the per-workgroup histograms.
-//   hist[b][e] <- offsets[e] + sum_{b' < b} hist[b'][e]   (base of block b in group e)
+//   hist[b][e] <- sum_{b' < b} hist[b'][e]   (rank base of block b inside group e;
+//                                          the permutation adds offsets[e])
 //   counts[e], offsets[e], and the tile tables tiles[i][g] = sum_{g' < g}
 //   ceil(n_g' / BM_i) for g = 0..E+1 (group E = the shared expert, n_E = T).
+// Each thread owns one expert's column and walks it in chunks whose loads
+// are all issued before the chunk's stores (a load after a store to the same
+// array would wait a full round trip).
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   __shared__ int sm[(1 + kNumBM) * 4];
   const int e = threadIdx.x;
   const int E = a.E;
   int running = 0;
   if (e < E) {
-    for (int b = 0; b < a.nblocks; ++b) {
-      int* p = a.hist + static_cast<int64_t>(b) * E + e;
-      const int c = *p;
-      *p = running;
-      running += c;
+    constexpr int CH = 32;
+    for (int b0 = 0; b0 < a.nblocks; b0 += CH) {
+      int c[CH];
+#pragma unroll
+      for (int u = 0; u < CH; ++u)
+        c[u] = b0 + u < a.nblocks ? a.hist[static_cast<int64_t>(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        if (b0 + u < a.nblocks) {
+          a.hist[static_cast<int64_t>(b0 + u) * E + e] = running;
+          running += c[u];
+        }
+      }
     }
   }
-  const int cnt = e < E ? running : 0;
-  offsets_and_tiles(cnt, E, a.T, a.counts, a.offsets, a.tiles, sm);
-  if (e < E) {
-    const int off = a.offsets[e];
-    for (int b = 0; b < a.nblocks; ++b) a.hist[static_cast<int64_t>(b) * E + e] += off;
-  }
+  offsets_and_tiles(e < E ? running : 0, E, a.T, a.counts, a.offsets, a.tiles, sm);
 }
 
 // Routing of at most 64 tokens in one workgroup: sum of the K-slice partial
@@ -376,10 +383,11 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouterArgs a, int nspl
   }
 }
 
-// Stable position of every token: perm[base[b][e] + rank] = t, where rank
-// counts earlier tokens of the same workgroup routed to the same expert.
-__global__ __launch_bounds__(64) void perm_kernel(const int32_t* idx, const int32_t* base, int T, int E,
-                                                  int32_t* perm) {
+// Stable position of every token: perm[offsets[e] + base[b][e] + rank] = t,
+// where rank counts earlier tokens of the same workgroup routed to the same
+// expert.
+__global__ __launch_bounds__(64) void perm_kernel(const int32_t* idx, const int32_t* base,
+                                                  const int32_t* offsets, int T, int E, int32_t* perm) {
   __shared__ int ids[kRouteTokens];
   const int t = blockIdx.x * kRouteTokens + threadIdx.x;
   ids[threadIdx.x] = t < T ? idx[t] : -1;
@@ -388,7 +396,7 @@ __global__ __launch_bounds__(64) void perm_kernel(const int32_t* idx, const int3
   const int e = ids[threadIdx.x];
   int rank = 0;
   for (int j = 0; j < static_cast<int>(threadIdx.x); ++j) rank += ids[j] == e;
-  perm[base[static_cast<int64_t>(blockIdx.x) * E + e] + rank] = t;
+  perm[offsets[e] + base[static_cast<int64_t>(blockIdx.x) * E + e] + rank] = t;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -408,6 +416,12 @@ static hipError_t launch_partials(const RouterArgs& a, int x_dtype, float* part,
     hipLaunchKernelGGL(router_partial_kernel<DT_BF16>, dim3(nb, ns), dim3(256), 0, s, a, kslice, part);
   else
     hipLaunchKernelGGL(router_partial_kernel<DT_F32>, dim3(nb, ns), dim3(256), 0, s, a, kslice, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_finish(const RouterArgs& a, int nsplit, const float* part, hipStream_t s) {
+  const int nb = (a.T + kRouteTokens - 1) / kRouteTokens;
+  hipLaunchKernelGGL(router_finish_kernel, dim3(nb), dim3(kRouteTokens), 0, s, a, nsplit, part);
   return hipGetLastError();
 }
 
@@ -434,10 +448,10 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_perm(const int32_t* idx, const int32_t* base, int T, int E, int32_t* perm,
-                       hipStream_t s) {
-  const int nb = (T + kRouteTokens - 1) / kRouteTokens;
-  hipLaunchKernelGGL(perm_kernel, dim3(nb), dim3(kRouteTokens), 0, s, idx, base, T, E, perm);
+hipError_t launch_perm(const int32_t* idx, const int32_t* base, const int32_t* offsets, int T, int E,
+                       int32_t* perm, hipStream_t s) {
+  hipLaunchKernelGGL(perm_kernel, dim3((T + kRouteTokens - 1) / kRouteTokens), dim3(kRouteTokens), 0, s, idx, base,
+                     offsets, T, E, perm);
   return hipGetLastError();
 }
 
