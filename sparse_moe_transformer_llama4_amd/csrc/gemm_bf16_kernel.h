@@ -350,23 +350,32 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
 #undef MOE_STEP
 
   // ---- epilogue (16x16 accumulator: lane holds rows 4*(lane/16)+q of column
-  // lane%16).  No global load sits between two stores through C: the compiler
-  // must assume they may alias, so each such load would wait a full memory
-  // round trip.  The row metadata comes through LDS (the ring is free once
-  // every wave's DMA has landed); the shared expert's output is loaded one
-  // fragment block ahead of the stores that consume it.
+  // lane%16).  The tile goes through LDS (the ring is free once every wave's
+  // DMA has landed) so that global memory sees 16-byte row chunks instead of
+  // 2- or 4-byte scattered stores; the per-row metadata comes through LDS too.
+  // No global load sits between two stores through C (the compiler must
+  // assume they may alias, so such a load would wait a full round trip): the
+  // shared expert's output is loaded for 16 chunks at a time before they are
+  // stored.
   __syncthreads();
   typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
   typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+  typedef __attribute__((address_space(3))) float lds_f32;
+  typedef __attribute__((address_space(3))) int lds_i32;
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
   if (tid < BM) {
-    if constexpr (GATEUP) reinterpret_cast<__attribute__((address_space(3))) float*>(As)[tid] = row_scale;
-    else reinterpret_cast<__attribute__((address_space(3))) int*>(As)[tid] = row_out;
+    if constexpr (GATEUP) reinterpret_cast<lds_f32*>(As)[tid] = row_scale;
+    else reinterpret_cast<lds_i32*>(As)[tid] = row_out;
   }
   __syncthreads();
+  lds_u8* const stage = As + 1024;        // staging area after the row table (BM * 4 <= 1 KB)
   const int lcol = lane & 15;
   const int rq = 4 * (lane >> 4);
   const int wrow = wm * (BM / WM) + rq;   // tile row of fragment 0, q = 0
-  if constexpr (GATEUP) {
+  if constexpr (GATEUP && BM == 256) {
+    // 256-row tiles store straight from the accumulators: the staged
+    // version below upsets their register allocation (accumulator copies in
+    // the main loop)
     constexpr int HF = FN / 2;
     void* C = shared ? p.C_shared : p.C;
 #pragma unroll
@@ -387,58 +396,95 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
         }
       }
     }
-  } else if constexpr (MODE == MODE_DOWN_SHARED) {
+  } else if constexpr (GATEUP) {
+    // h tile [BM][BNH] bf16, row pitch HP bytes
+    constexpr int HF = FN / 2;
+    constexpr int HP = BNH * 2 + 16;
+    static_assert(1024 + BM * HP <= NBUF * (A_STAGE + B_STAGE), "h staging fits the ring");
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = m0 + wrow + i * 16 + q;
-        if (r >= rows) continue;
+        const int rt = wrow + i * 16 + q;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * (BN / WN) + j * 16 + lcol;
-          if (col >= NH) continue;
-          reinterpret_cast<float*>(p.C_shared)[static_cast<int64_t>(r) * NH + col] = acc[i][j][q];
+        for (int j = 0; j < HF; ++j) {
+          const int ct = wn * (BNH / WN) + j * 16 + lcol;
+          const float gv = acc[i][j][q] * sc[q];
+          const float uv = acc[i][j + HF][q] * sc[q];
+          *(lds_u16*)(stage + rt * HP + ct * 2) = f32_to_bf16(silu_f(gv) * uv);
         }
       }
+    }
+    __syncthreads();
+    constexpr int CPR = BNH / 8;          // 16-byte chunks per row
+    uint16_t* C = reinterpret_cast<uint16_t*>(shared ? p.C_shared : p.C);
+    for (int k = tid; k < BM * CPR; k += 256) {
+      const int r = k / CPR, cc = k - r * CPR;
+      const int col = n0 + cc * 8;
+      if (m0 + r < rows && col < NH)      // NH % 8 == 0: a chunk is wholly in or out
+        *reinterpret_cast<i32x4*>(C + static_cast<int64_t>(row_base + m0 + r) * NH + col) =
+            *(const lds_i32x4*)(stage + r * HP + cc * 16);
     }
   } else {
-    int orow[FM][4];
+    // fp32 tile in passes of PR rows, [PR][BN] with row pitch FPB bytes
+    constexpr int PR = BM == 128 ? 128 : 64;
+    constexpr int FPB = BN * 4 + 16;
+    static_assert(1024 + PR * FPB <= NBUF * (A_STAGE + B_STAGE), "fp32 staging fits the ring");
+    constexpr int CPR = BN / 4;           // 16-byte chunks per row
+    constexpr int NB = 16;                // chunks per thread per batch
+    static_assert((PR * CPR) % (256 * NB) == 0, "whole batches per pass");
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const i32x4 o4 = *(const lds_i32x4*)(As + 4 * (wrow + 16 * i));
+    for (int pass = 0; pass < BM / PR; ++pass) {
+      if (pass > 0) __syncthreads();      // the previous pass's chunks are read
 #pragma unroll
-      for (int q = 0; q < 4; ++q) orow[i][q] = o4[q];
-    }
-    float y[2][4][FN];
-#define MOE_LOAD_Y(b, i)                                                                       \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                            \
-      const bool ok_ = m0 + wrow + (i) * 16 + q < rows;                                        \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                         \
-        const int col_ = n0 + wn * (BN / WN) + j * 16 + lcol;                                  \
-        y[b][q][j] = (ok_ && col_ < NH) ? p.Y[static_cast<int64_t>(orow[i][q]) * NH + col_] : 0.0f; \
-      }                                                                                        \
-    }
-    MOE_LOAD_Y(0, 0)
+      for (int i = 0; i < FM; ++i) {
+        const int rt0 = wm * (BM / WM) + i * 16;          // first tile row of fragment i (uniform)
+        if (rt0 / PR != pass) continue;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (i + 1 < FM) { MOE_LOAD_Y((i + 1) & 1, i + 1) }
+        for (int q = 0; q < 4; ++q) {
+          const int rp = rt0 + rq + q - pass * PR;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = m0 + wrow + i * 16 + q;
-        if (r >= rows) continue;
+          for (int j = 0; j < FN; ++j)
+            *(lds_f32*)(stage + rp * FPB + (wn * (BN / WN) + j * 16 + lcol) * 4) = acc[i][j][q];
+        }
+      }
+      __syncthreads();
+      for (int k0 = tid; k0 < PR * CPR; k0 += 256 * NB) {
+        f32x4 y[NB];
+        int orow[NB];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * (BN / WN) + j * 16 + lcol;
-          if (col >= NH) continue;
-          const int64_t o = static_cast<int64_t>(orow[i][q]) * NH + col;
-          const float v = acc[i][j][q] + y[i & 1][q][j];
-          if (p.out_bf16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16(v);
-          else reinterpret_cast<float*>(p.C)[o] = v;
+        for (int u = 0; u < NB; ++u) {
+          const int k = k0 + u * 256;
+          const int r = k / CPR, cc = k - r * CPR;
+          const int rt = pass * PR + r;
+          if constexpr (MODE == MODE_DOWN_ROUTED) orow[u] = reinterpret_cast<const lds_i32*>(As)[rt];
+          else orow[u] = m0 + rt;
+          const bool ok = m0 + rt < rows && n0 + cc * 4 < NH;
+          y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (MODE == MODE_DOWN_ROUTED)
+            if (ok) y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int k = k0 + u * 256;
+          const int r = k / CPR, cc = k - r * CPR;
+          const int rt = pass * PR + r;
+          if (m0 + rt >= rows || n0 + cc * 4 >= NH) continue;
+          const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
+          const int64_t o = static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4;
+          if constexpr (MODE == MODE_DOWN_SHARED) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + o) = v;
+          } else if (p.out_bf16) {
+            const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+            const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + o) = v;
+          }
         }
       }
     }
-#undef MOE_LOAD_Y
   }
 }
 
