@@ -318,9 +318,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
   // ---- epilogue (16x16 accumulator: lane holds rows 4*(lane/16)+q of column
   // lane%16).  No global load sits between two stores through C (the compiler
   // must assume they may alias, so each would wait a full round trip): the
-  // column scales are loaded first, the row metadata comes through LDS (the
-  // ring is free once every wave's DMA has landed) and the shared expert's
-  // output is loaded one fragment block ahead of the stores that consume it.
+  // column scales are loaded first and the row metadata comes through LDS
+  // (the ring is free once every wave's DMA has landed).
   const int lcol = lane & 15;
   const int rq = 4 * (lane >> 4);
   const int wrow = wm * (BM / WM) + rq;   // tile row of fragment 0, q = 0
@@ -344,89 +343,100 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
     reinterpret_cast<__attribute__((address_space(3))) int*>(As)[BM + tid] = row_out;
   }
   __syncthreads();
+  // The tile goes through LDS (after the 1 KB of row tables) so that global
+  // memory sees 16-byte row chunks instead of scattered 4-byte stores.
+  typedef __attribute__((address_space(3))) float lds_f32;
+  typedef __attribute__((address_space(3))) int lds_i32;
+  lds_u8* const stage = As + 1024;
   if constexpr (GATEUP) {
+    // h tile [BM][BNH] fp32 (row pitch HP bytes), then 16-byte chunks with the
+    // per-row max |h| reduced over the lanes that share a row
     constexpr int HF = FN / 2;
-    float* C = reinterpret_cast<float*>(shared ? p.C_shared : p.C);
-    uint32_t* amax = shared ? p.amax_shared : p.amax;
+    constexpr int HP = BNH * 4 + 16;
+    static_assert(1024 + BM * HP <= NBUF * (A_STAGE + B_STAGE), "h staging fits the ring");
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = m0 + wrow + i * 16 + q;
-        const bool valid = r < rows;
-        const int orow = row_base + min(r, rows - 1);
-        float rmax = 0.f;
+        const int rt = wrow + i * 16 + q;
 #pragma unroll
         for (int j = 0; j < HF; ++j) {
-          const int col = n0 + wn * BNW + j * 16 + lcol;
-          if (valid && col < NH) {
-            const float gv = acc[i][j][q] * sc[q] * csc[j];
-            const float uv = acc[i][j + HF][q] * sc[q] * csc[j + HF];
-            const float h = silu_f(gv) * uv;
-            C[static_cast<int64_t>(orow) * NH + col] = h;
-            rmax = fmaxf(rmax, fabsf(h));
-          }
+          const float gv = acc[i][j][q] * sc[q] * csc[j];
+          const float uv = acc[i][j + HF][q] * sc[q] * csc[j + HF];
+          *(lds_f32*)(stage + rt * HP + (wn * BNW + j * 16 + lcol) * 4) = silu_f(gv) * uv;
         }
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, m, 64));
-        if (valid && lcol == 0) atomicMax(&amax[orow], __float_as_uint(rmax));
       }
     }
-  } else if constexpr (MODE == MODE_DOWN_SHARED) {
+    __syncthreads();
+    constexpr int CPR = BNH / 4;          // 16-byte chunks per row (32)
+    static_assert(CPR == 32 && (BM * CPR) % 256 == 0, "a row's chunks are 32 consecutive lanes");
+    float* C = reinterpret_cast<float*>(shared ? p.C_shared : p.C);
+    uint32_t* amax = shared ? p.amax_shared : p.amax;
+    for (int k = tid; k < BM * CPR; k += 256) {
+      const int r = k / CPR, cc = k - r * CPR;
+      const int col = n0 + cc * 4;
+      const bool ok = m0 + r < rows && col < NH;
+      const f32x4 v = *(const lds_f32x4*)(stage + r * HP + cc * 16);
+      float m = ok ? fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))) : 0.f;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = m0 + wrow + i * 16 + q;
-        if (r >= rows) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * BNW + j * 16 + lcol;
-          if (col >= NH) continue;
-          reinterpret_cast<float*>(p.C_shared)[static_cast<int64_t>(r) * NH + col] = acc[i][j][q] * sc[q] * csc[j];
-        }
-      }
+      for (int sh = 1; sh < 32; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
+      if (ok) *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row_base + m0 + r) * NH + col) = v;
+      if (cc == 0 && m0 + r < rows) atomicMax(&amax[row_base + m0 + r], __float_as_uint(m));
     }
   } else {
-    int orow[FM][4];
+    // scaled fp32 tile [BM][BN] (row pitch FPB bytes), then 16-byte chunks:
+    // shared down stores them; routed down adds the shared expert's output,
+    // loaded for 16 chunks at a time before they are stored
+    constexpr int FPB = BN * 4 + 16;
+    static_assert(1024 + BM * FPB <= NBUF * (A_STAGE + B_STAGE), "fp32 staging fits the ring");
+    constexpr int CPR = BN / 4;
+    constexpr int NB = 16;
+    static_assert((BM * CPR) % (256 * NB) == 0, "whole batches");
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const i32x4 o4 = *(const lds_i32x4*)(As + 4 * (BM + wrow + 16 * i));
-#pragma unroll
-      for (int q = 0; q < 4; ++q) orow[i][q] = o4[q];
-    }
-    float y[2][4][FN];
-#define F8_LOAD_Y(b, i)                                                                        \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                            \
-      const bool ok_ = m0 + wrow + (i) * 16 + q < rows;                                        \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                         \
-        const int col_ = n0 + wn * BNW + j * 16 + lcol;                                        \
-        y[b][q][j] = (ok_ && col_ < NH) ? p.Y[static_cast<int64_t>(orow[i][q]) * NH + col_] : 0.0f; \
-      }                                                                                        \
-    }
-    F8_LOAD_Y(0, 0)
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (i + 1 < FM) { F8_LOAD_Y((i + 1) & 1, i + 1) }
       const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = m0 + wrow + i * 16 + q;
-        if (r >= rows) continue;
+        const int rt = wrow + i * 16 + q;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * BNW + j * 16 + lcol;
-          if (col >= NH) continue;
-          const int64_t o = static_cast<int64_t>(orow[i][q]) * NH + col;
-          const float v = acc[i][j][q] * sc[q] * csc[j] + y[i & 1][q][j];
-          if (p.out_bf16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16(v);
-          else reinterpret_cast<float*>(p.C)[o] = v;
+        for (int j = 0; j < FN; ++j)
+          *(lds_f32*)(stage + rt * FPB + (wn * BNW + j * 16 + lcol) * 4) = acc[i][j][q] * sc[q] * csc[j];
+      }
+    }
+    __syncthreads();
+    for (int k0 = tid; k0 < BM * CPR; k0 += 256 * NB) {
+      f32x4 y[NB];
+      int orow[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int k = k0 + u * 256;
+        const int r = k / CPR, cc = k - r * CPR;
+        if constexpr (MODE == MODE_DOWN_ROUTED) orow[u] = reinterpret_cast<const lds_i32*>(As)[BM + r];
+        else orow[u] = m0 + r;
+        y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (MODE == MODE_DOWN_ROUTED)
+          if (m0 + r < rows && n0 + cc * 4 < NH)
+            y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int k = k0 + u * 256;
+        const int r = k / CPR, cc = k - r * CPR;
+        if (m0 + r >= rows || n0 + cc * 4 >= NH) continue;
+        const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
+        const int64_t o = static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4;
+        if constexpr (MODE == MODE_DOWN_SHARED) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + o) = v;
+        } else if (p.out_bf16) {
+          const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+          const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + o) = v;
         }
       }
     }
-#undef F8_LOAD_Y
   }
 }
 
