@@ -82,9 +82,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   // register double buffer's parity) are compile-time constants.  Fetches
   // that miss L2 take thousands of cycles under load: 128-row tiles, which
   // consume a stage every ~570 cycles, keep 5 in flight (6 x 24 KB); 256-row
-  // tiles (~1250 cycles per stage) keep 3 (4 x 32 KB); 64-row tiles keep 3
-  // per workgroup with two workgroups per CU (2 x 4 x 20 KB).
-  constexpr int NBUF = BM == 128 ? 6 : 4;
+  // tiles keep 4 (5 x 32 KB, the whole LDS); 64-row tiles keep 3 per
+  // workgroup with two workgroups per CU (2 x 4 x 20 KB).
+  constexpr int NBUF = BM == 128 ? 6 : BM == 256 ? 5 : 4;
   constexpr int A_INS = A_STAGE / 1024 / 4;   // 1 KB DMA instructions per wave per stage (A)
   constexpr int B_INS = B_STAGE / 1024 / 4;   // (weights)
   constexpr int LOADS = A_INS + B_INS;        // VMEM instructions per wave per stage
@@ -260,17 +260,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NMF = FM * FN;                       // MFMAs per stage
   constexpr int NOPS = FM + FN + A_INS + B_INS;      // other operations per stage
 
-  // One stage (step kt + SL, operands FA/FB in registers, its slot SL free):
+  // One stage (step kt + R, operands FA/FB in registers, its slot R % NBUF free):
   // the MFMA stream starts right after the previous barrier, and the stage's
   // other work is threaded through it in a fixed order -- first the reads of
   // stage kt+SL+1's fragments into FA2/FB2 (they must land before the stage
   // ends), then the DMA of stage kt+SL+NBUF into slot SL.  The end waits for
   // stage kt+SL+2 (this wave's part; later stages may be in flight) and for
   // the reads, and the barrier publishes that stage and frees slot SL+1.
-#define MOE_STEP(SL, FA, FB, FA2, FB2)                                                         \
+#define MOE_STEP(R, FA, FB, FA2, FB2)                                                          \
   do {                                                                                         \
-    constexpr int nsl_ = ((SL) + 1) % NBUF;                                                    \
-    const int sd_ = kt + (SL) + NBUF;                                                          \
+    constexpr int sl_ = (R) % NBUF, nsl_ = ((R) + 1) % NBUF;                                   \
+    const int sd_ = kt + (R) + NBUF;                                                           \
     _Pragma("unroll") for (int m_ = 0; m_ < NMF; ++m_) {                                       \
       acc[m_ / FN][m_ % FN] =                                                                  \
           __builtin_amdgcn_mfma_f32_16x16x32_bf16(FA[m_ / FN], FB[m_ % FN], acc[m_ / FN][m_ % FN], 0, 0, 0); \
@@ -278,8 +278,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
         if (o_ * NMF / NOPS == m_) {                                                           \
           if (o_ < FM) MOE_AREAD(FA2, o_, nsl_);                                               \
           else if (o_ < FM + FN) MOE_BREAD(FB2, o_ - FM, nsl_);                                \
-          else if (o_ < FM + FN + A_INS) MOE_DMA_A(o_ - FM - FN, sd_, (SL));                   \
-          else MOE_DMA_B(o_ - FM - FN - A_INS, sd_, (SL));                                     \
+          else if (o_ < FM + FN + A_INS) MOE_DMA_A(o_ - FM - FN, sd_, sl_);                    \
+          else MOE_DMA_B(o_ - FM - FN - A_INS, sd_, sl_);                                      \
         }                                                                                      \
       }                                                                                        \
       __builtin_amdgcn_sched_barrier(0);                                                       \
@@ -306,9 +306,20 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   for (int j = 0; j < FN; ++j) MOE_BREAD(fb0, j, 0);
   __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */
   __builtin_amdgcn_s_barrier();
-  static_assert(NBUF == 4 || NBUF == 6, "the loop below is unrolled by the ring depth");
+  // Unrolled by U = lcm(NBUF, 2) so that ring slots and the register
+  // buffers' parity are compile-time; the tail runs the first steps of one
+  // more group.
+  constexpr int U = NBUF % 2 == 0 ? NBUF : 2 * NBUF;
+  static_assert(U <= 10, "unrolled steps below");
+#define MOE_STEPR(R)                                                                           \
+  do {                                                                                         \
+    if constexpr ((R) < U) {                                                                   \
+      if constexpr ((R) % 2 == 0) MOE_STEP((R), fa0, fb0, fa1, fb1);                           \
+      else MOE_STEP((R), fa1, fb1, fa0, fb0);                                                  \
+    }                                                                                          \
+  } while (0)
   int kt = 0;
-  for (; kt + NBUF <= nk; kt += NBUF) {
+  for (; kt + U <= nk; kt += U) {
     // 256-row tiles keep their accumulators in AGPRs: pinning them there at
     // each iteration keeps the register allocator from moving them between
     // AGPRs and VGPRs across iterations (hundreds of v_accvgpr copies otherwise)
@@ -318,30 +329,20 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
     }
-    MOE_STEP(0, fa0, fb0, fa1, fb1);
-    MOE_STEP(1, fa1, fb1, fa0, fb0);
-    MOE_STEP(2, fa0, fb0, fa1, fb1);
-    MOE_STEP(3, fa1, fb1, fa0, fb0);
-    if constexpr (NBUF == 6) {
-      MOE_STEP(4, fa0, fb0, fa1, fb1);
-      MOE_STEP(5, fa1, fb1, fa0, fb0);
-    }
+    MOE_STEPR(0); MOE_STEPR(1); MOE_STEPR(2); MOE_STEPR(3); MOE_STEPR(4);
+    MOE_STEPR(5); MOE_STEPR(6); MOE_STEPR(7); MOE_STEPR(8); MOE_STEPR(9);
   }
-  if (kt < nk) {
-    MOE_STEP(0, fa0, fb0, fa1, fb1);
-    if (kt + 1 < nk) {
-      MOE_STEP(1, fa1, fb1, fa0, fb0);
-      if (kt + 2 < nk) {
-        MOE_STEP(2, fa0, fb0, fa1, fb1);
-        if constexpr (NBUF == 6) {
-          if (kt + 3 < nk) {
-            MOE_STEP(3, fa1, fb1, fa0, fb0);
-            if (kt + 4 < nk) MOE_STEP(4, fa0, fb0, fa1, fb1);
-          }
-        }
-      }
-    }
-  }
+  const int left = nk - kt;   // 0 .. U-1
+  if (left > 0) { MOE_STEPR(0);
+  if (left > 1) { MOE_STEPR(1);
+  if (left > 2) { MOE_STEPR(2);
+  if (left > 3) { MOE_STEPR(3);
+  if (left > 4) { MOE_STEPR(4);
+  if (left > 5) { MOE_STEPR(5);
+  if (left > 6) { MOE_STEPR(6);
+  if (left > 7) { MOE_STEPR(7);
+  if (left > 8) { MOE_STEPR(8); } } } } } } } } }
+#undef MOE_STEPR
   wait_vmcnt<0>();
 #undef MOE_AREAD
 #undef MOE_BREAD
