@@ -22,12 +22,20 @@
  *     space is the caller's workspace, sized by moe_workspace_size.
  *   - All work is enqueued asynchronously on `stream` (hipStream_t; NULL =
  *     the default stream).  No host synchronisation, no device-to-host copy.
+ *     Decode-sized bf16 forward calls (T <= 64) also use a side stream that
+ *     the plan creates for the current device on first use (non-blocking,
+ *     default priority): it waits for `stream` before its first kernel and
+ *     `stream` waits for it before the call's last kernel, so for the caller
+ *     the whole call is still ordered in `stream`.  If `stream` belongs to
+ *     another device than the current one, the call runs on `stream` alone.
  *   - Arguments, shapes, alignment and workspace size are checked on the
  *     host BEFORE anything is enqueued; a failed check enqueues nothing.
  *   - Row-major layouts throughout.  Pointers must be 16-byte aligned.
  *   - Inputs must be finite; NaN / Inf inputs are outside the contract.
- *   - A plan is immutable after creation and may be shared by threads and
- *     streams; concurrent calls need distinct workspaces.
+ *   - A plan may be shared by threads and streams (its side streams are
+ *     created and used under a lock); concurrent calls need distinct
+ *     workspaces.  Calls on one plan captured into a HIP graph must not
+ *     overlap in time with uncaptured calls on the same plan.
  */
 #ifndef MOE355_MOE_H
 #define MOE355_MOE_H
@@ -121,12 +129,14 @@ typedef struct moe_routing {
   int32_t* perm;       /* [T] */
 } moe_routing;
 
-/* Validate `cfg` and create a host-side plan (no device call is made).
+/* Validate `cfg` and create a host-side plan (no device call is made; the
+ * side stream of the decode schedule is created by the first call that uses it).
  * Returns MOE_ERR_UNSUPPORTED / MOE_ERR_INVALID_ARGUMENT for bad configs; *out
  * is set to NULL on failure. */
 moe_status moe_plan(const moe_config* cfg, moe_plan_t* out);
 
-/* Release a plan (NULL is ignored).  Does not touch device memory. */
+/* Release a plan and the side streams and events it created (NULL is
+ * ignored).  Does not touch device memory; work already enqueued completes. */
 void moe_plan_destroy(moe_plan_t plan);
 
 /* Bytes of device workspace moe_route / moe_forward need for T tokens. */
@@ -159,7 +169,9 @@ moe_status moe_forward(moe_plan_t plan, const void* x, int64_t T, const moe_weig
  *   [2] shared-expert down GEMM (e4m3: preceded by h quantisation)
  *   [3] routed down GEMM with un-permute + combine
  * so hipEventElapsedTime(events[i], events[i+1]) is the duration of stage i.
- * Events are created by the caller; everything else is as moe_forward.
+ * The stages run one after another on `stream` alone (no side stream), so a
+ * decode-sized timed call can take longer than moe_forward.  Events are
+ * created by the caller; everything else is as moe_forward.
  */
 #define MOE_NUM_STAGES 4
 moe_status moe_forward_timed(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w,

@@ -429,8 +429,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
     }
   } else {
     // fp32 tile in passes of PR rows, [PR][BN] with row pitch FPB bytes
-    constexpr int PR = BM == 128 ? 128 : 64;
     constexpr int FPB = BN * 4 + 16;
+    constexpr int PR = (1024 + 128 * FPB <= NBUF * (A_STAGE + B_STAGE) && BM >= 128) ? 128 : 64;
     static_assert(1024 + PR * FPB <= NBUF * (A_STAGE + B_STAGE), "fp32 staging fits the ring");
     constexpr int CPR = BN / 4;           // 16-byte chunks per row
     constexpr int NB = 16;                // chunks per thread per batch

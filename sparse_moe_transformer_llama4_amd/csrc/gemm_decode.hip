@@ -22,6 +22,8 @@
 //   * the four K-quarter partial sums are added through LDS once at the end,
 //     followed by the same epilogues as the prefill kernels (SwiGLU with the
 //     gate on routed rows; fp32 shared output; un-permute + combine).
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -50,6 +52,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory", "m0");
 }
+// The same with the non-temporal hint, for the weights: each weight byte is
+// read once per call, and the streaming policy lifts the rate of these
+// 128/256-byte row segments by ~8 % (measured: 5.6 -> 6.0 TB/s for the
+// gate/up tiles' two 128-byte segments per row).
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_base), "v"(g) : "memory", "m0");
+}
 
 __device__ __forceinline__ bf16x8 read_w_frag(const lds_u8* st, int kb, int col, int lane) {
   const int s = lane & 15;
@@ -64,10 +73,228 @@ __device__ __forceinline__ bf16x8 read_w_frag(const lds_u8* st, int kb, int col,
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// ---------------------------------------------------------------- gate/up
+//
+// Tile = 128 gate columns + the matching 128 up columns, i.e. two 256-byte
+// segments per weight row (a streaming probe: 256-byte segments ~7 % faster
+// than 128-byte ones when the workgroups fill whole rounds).  With 512-byte
+// weight rows a stage holds 16 K rows (8 KB) and feeds the 16x16x16 MFMA, so
+// the 4-deep per-wave ring still fits in 144 KB.  A launch over the shared
+// group alone (group_lo == E) addresses its tiles directly, without the tile
+// table, so it can run before the routing has finished.
+constexpr int GBN = 256;               // weight columns per tile
+constexpr int GBNH = GBN / 2;          // output columns per tile
+constexpr int GBK = 16;                // K rows per stage
+constexpr int GROWB = GBN * 2;         // bytes per weight row in LDS
+constexpr int GWSTAGE = GBK * GROWB;   // 8 KB of weights per stage
+constexpr int GINS = GWSTAGE / 1024;   // weight DMA instructions per stage per wave (8)
+constexpr int GFN = GBN / 16;          // weight fragments (16 columns each)
+constexpr int GSTAGE = GWSTAGE + 1024; // + 32 activation rows x 16 K values
+constexpr int GPP = GBN + 16;          // floats per row of the partial-sum buffer (padded)
+
+// B fragment of the 16x16x16 MFMA for columns col .. col+15: lane gets column
+// col + lane%16, K rows 4 (lane/16) .. +3 of the stage.  The 16 lanes of a
+// group address 4 rows x 4 columns each; the transposing read returns every
+// lane its column's 4 values.  16-byte chunk c of row r sits at c ^ 2 (r & 7).
+__device__ __forceinline__ s16x4 read_w_frag16(const lds_u8* st, int col, int lane) {
+  const int s = lane & 15;
+  const int r = 4 * (lane >> 4) + (s >> 2);
+  const int lbyte = (col + 4 * (s & 3)) * 2;
+  const int pbyte = ((lbyte >> 4) ^ (2 * (r & 7))) * 16 + (lbyte & 15);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + r * GROWB + pbyte));
+}
+
+template <int FMMAX>
+__global__ __launch_bounds__(256, 1) void gemm_decode_gateup_kernel(GemmArgs p) {
+  constexpr int DBM = 16 * FMMAX;              // rows per tile
+  constexpr int DNBUF = 4;                     // per-wave ring depth
+  constexpr int LOADS = GINS + 1;              // DMA instructions per stage per wave
+  constexpr int PART = 4 * DBM * GPP * 4;      // the four waves' partial sums
+  constexpr int RING = 4 * DNBUF * GSTAGE;
+  constexpr int TAB = PART;                    // per-row gate scales
+  constexpr int SMEM = RING > TAB + 4 * DBM ? RING : TAB + 4 * DBM;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.E, K = p.K;
+
+  // ---- tile lookup (DBM-row tiles over groups group_lo .. group_hi - 1)
+  int g, m0;
+  if (p.group_lo == E) {
+    g = E;
+    m0 = blockIdx.x * DBM;
+    if (m0 >= p.T) return;
+  } else {
+    const int mt = blockIdx.x + p.tiles[p.group_lo];
+    if (mt >= p.tiles[p.group_hi]) return;
+    int lo = p.group_lo, hi = p.group_hi - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    m0 = (mt - p.tiles[g]) * DBM;
+  }
+  const int rows = (g == E) ? p.T : p.offsets[g + 1] - p.offsets[g];
+  const bool shared = g == E;
+  const int NH = shared ? p.N_shared : p.N;
+  const int n0 = blockIdx.y * GBNH;
+  if (n0 >= NH) return;
+  const int row_base = shared ? 0 : p.offsets[g];
+  const int ldb = 2 * NH;
+  const int nvalid = min(DBM, rows - m0);
+  const int fm = (nvalid + 15) >> 4;           // fragments with valid rows (uniform)
+
+  // the routed rows' gate scale, loaded now so its latency hides behind the loop
+  float row_scale = 1.0f;
+  if (tid < DBM && !shared) row_scale = p.gate[p.perm[row_base + min(m0 + tid, rows - 1)]];
+
+  // ---- this wave's quarter of K
+  const int kq = K >> 2;                       // multiple of GBK
+  const int k0 = wave * kq;
+  const int ns = kq / GBK;
+
+  // weights: DMA instruction i fills K rows 2i, 2i+1 of the stage; lane ->
+  // row 2i + lane/32, physical chunk lane%32 holding logical chunk
+  // c = (lane%32) ^ 2 (row & 7); logical chunks 0..15 are the gate columns
+  // n0 + 8c, 16..31 the up columns NH + n0 + 8 (c - 16)
+  const uint16_t* wbase = reinterpret_cast<const uint16_t*>(shared ? p.B_shared : p.B) +
+                          (shared ? 0 : static_cast<int64_t>(g) * K * ldb);
+  int64_t w_off[GINS];
+#pragma unroll
+  for (int i = 0; i < GINS; ++i) {
+    const int kr = 2 * i + (lane >> 5);
+    const int c = (lane & 31) ^ (2 * (kr & 7));
+    const int lc = (c & 15) * 8;
+    const int gc = (c < 16 ? n0 : NH + n0) + lc;
+    w_off[i] = static_cast<int64_t>(k0 + kr) * ldb + (n0 + lc < NH ? gc : 0);
+  }
+  const int64_t w_kstride = static_cast<int64_t>(GBK) * ldb;
+
+  // activations: one DMA instruction per stage; lane -> tile row lane/2,
+  // physical chunk lane%2 holding logical chunk (lane%2) ^ ((row >> 3) & 1)
+  // (8 K values); rows past the group are clamped to its last row
+  const uint16_t* abase = reinterpret_cast<const uint16_t*>(shared ? p.A_shared : p.A);
+  int64_t a_off;
+  {
+    const int ar = lane >> 1;
+    const int r = min(m0 + ar, rows - 1);
+    const int arow = shared ? r : p.perm[row_base + r];
+    a_off = static_cast<int64_t>(arow) * K + k0 + (((lane & 1) ^ ((ar >> 3) & 1)) * 8);
+  }
+
+  const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem)) +
+                        __builtin_amdgcn_readfirstlane(wave) * (DNBUF * GSTAGE);
+  const lds_u8* ring_p = (const lds_u8*)smem + wave * (DNBUF * GSTAGE);
+  // A fragment f: row 16f + lane%16, K values 4 (lane/16) .. +3 = logical
+  // chunk lane/32, bytes 8 ((lane/16) & 1) of it
+  int a_rd[FMMAX];
+#pragma unroll
+  for (int f = 0; f < FMMAX; ++f) {
+    const int r = 16 * f + (lane & 15);
+    a_rd[f] = GWSTAGE + r * 32 + (((lane >> 5) ^ ((r >> 3) & 1)) << 4) + (((lane >> 4) & 1) << 3);
+  }
+
+  f32x4 acc[FMMAX][GFN];
+#pragma unroll
+  for (int f = 0; f < FMMAX; ++f)
+#pragma unroll
+    for (int j = 0; j < GFN; ++j) acc[f][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#define GU_ISSUE(st)                                                                           \
+  do {                                                                                         \
+    const int s_ = min((st), ns - 1);                                                          \
+    const uint32_t b_ = ring + static_cast<uint32_t>(((st) % DNBUF) * GSTAGE);                 \
+    _Pragma("unroll") for (int i = 0; i < GINS; ++i)                                           \
+      dma16_nt(wbase + w_off[i] + s_ * w_kstride, b_ + i * 1024);                              \
+    dma16(abase + a_off + s_ * GBK, b_ + GWSTAGE);                                             \
+  } while (0)
+  // Stage kt: its DMA is complete once only the later stages' DMAs remain.
+#define GU_STEP(kt)                                                                            \
+  do {                                                                                         \
+    GU_ISSUE((kt) + DNBUF - 1);                                                                \
+    wait_vmcnt<(DNBUF - 1) * LOADS>();                                                         \
+    const lds_u8* st_ = ring_p + ((kt) % DNBUF) * GSTAGE;                                      \
+    s16x4 wf[GFN], af[FMMAX];                                                                  \
+    _Pragma("unroll") for (int j = 0; j < GFN; ++j)                                            \
+      wf[j] = read_w_frag16(st_, (j < GFN / 2 ? 0 : GBNH) + (j % (GFN / 2)) * 16, lane);       \
+    _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
+      af[f] = *reinterpret_cast<const lds_s16x4*>(st_ + a_rd[f]);                              \
+    _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
+      if (f < fm)                                                                              \
+        _Pragma("unroll") for (int j = 0; j < GFN; ++j)                                        \
+          acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(af[f], wf[j], acc[f][j], 0, 0, 0); \
+    /* this stage's slot is refilled DNBUF-1 steps later: reads must be done */                \
+    __builtin_amdgcn_s_waitcnt(0xC07F);                                                        \
+  } while (0)
+
+#pragma unroll
+  for (int st = 0; st < DNBUF - 1; ++st) GU_ISSUE(st);
+  for (int kt = 0; kt < ns; ++kt) GU_STEP(kt);
+  wait_vmcnt<0>();
+#undef GU_ISSUE
+#undef GU_STEP
+
+  // ---- the four waves' partial sums through LDS ([row][GPP] fp32 each)
+  __syncthreads();
+  float* part = reinterpret_cast<float*>(smem);
+  float* tab = reinterpret_cast<float*>(smem + TAB);
+  const int lcol = lane & 15, rq = 4 * (lane >> 4);
+#pragma unroll
+  for (int f = 0; f < FMMAX; ++f) {
+    if (f < fm) {
+#pragma unroll
+      for (int j = 0; j < GFN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          part[(wave * DBM + 16 * f + rq + q) * GPP + j * 16 + lcol] = acc[f][j][q];
+    }
+  }
+  if (tid < DBM) tab[tid] = row_scale;
+  __syncthreads();
+  // thread -> quads of 4 consecutive columns of a row; sum in wave order
+  constexpr int C4 = GBN / 4;
+  constexpr int NQ = DBM * C4 / 256;
+  f32x4 tq[NQ];
+#pragma unroll
+  for (int it = 0; it < NQ; ++it) {
+    const int e = tid + 256 * it;
+    const int r = e / C4, c = (e % C4) * 4;
+    const f32x4* p0 = reinterpret_cast<const f32x4*>(part + r * GPP + c);
+    constexpr int WS = DBM * GPP / 4;            // one wave's buffer in quads
+    tq[it] = ((p0[0] + p0[WS]) + p0[2 * WS]) + p0[3 * WS];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < NQ; ++it) {
+    const int e = tid + 256 * it;
+    const int r = e / C4, c = (e % C4) * 4;
+    *reinterpret_cast<f32x4*>(part + r * GPP + c) = tq[it];
+  }
+  __syncthreads();
+
+  // ---- SwiGLU epilogue: h = SiLU(s acc_gate) * (s acc_up), s = the token's
+  // gate on routed rows, 1 on shared rows; columns fastest
+  constexpr int NIT = DBM * GBNH / 256;
+  uint16_t* C = reinterpret_cast<uint16_t*>(shared ? p.C_shared : p.C);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int e = tid + 256 * it;
+    const int r = e / GBNH, c = e % GBNH;
+    const int col = n0 + c;
+    if (r >= nvalid || col >= NH) continue;
+    const float sc = tab[r];
+    const float gv = part[r * GPP + c] * sc;
+    const float uv = part[r * GPP + GBNH + c] * sc;
+    C[static_cast<int64_t>(row_base + m0 + r) * NH + col] = f32_to_bf16(silu_f(gv) * uv);
+  }
+}
+
+// ---------------------------------------------------------------- down
+
 template <int MODE, int FMMAX>
 __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
-  constexpr bool GATEUP = MODE == MODE_GATEUP;
-  constexpr int BNH = GATEUP ? DBN / 2 : DBN;   // output columns per tile
+  static_assert(MODE == MODE_DOWN_SHARED || MODE == MODE_DOWN_ROUTED, "down modes only");
   constexpr int DBM = 16 * FMMAX;               // rows per tile
   constexpr int ASTAGE = FMMAX * 1024;          // activation bytes per stage (16 rows x 64 B per KB)
   constexpr int STAGE = WSTAGE + ASTAGE;
@@ -98,30 +325,21 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
     }
     g = lo;
     m0 = (mt - p.tiles[g]) * DBM;
-    rows = (g == E) ? T : p.offsets[g + 1] - p.offsets[g];
+    rows = p.offsets[g + 1] - p.offsets[g];
   }
-  const bool shared = (MODE == MODE_DOWN_SHARED) || (GATEUP && g == E);
-  const int NH = (GATEUP && shared) ? p.N_shared : p.N;
-  const int n0 = blockIdx.y * BNH;
+  constexpr bool shared = MODE == MODE_DOWN_SHARED;
+  const int NH = p.N;
+  const int n0 = blockIdx.y * DBN;
   if (n0 >= NH) return;
   const int row_base = shared ? 0 : p.offsets[g];
-  const int ldb = GATEUP ? 2 * NH : NH;
+  const int ldb = NH;
   const int nvalid = min(DBM, rows - m0);
   const int fm = (nvalid + 15) >> 4;            // fragments with valid rows (uniform)
 
-  // Per-row metadata for the epilogue (the routed gate/up's gate scale, the
-  // routed down's output row), one tile row per thread, loaded now so its
-  // latency hides behind the main loop.
-  float row_scale = 1.0f;
+  // the routed down's output row (un-permutation), one tile row per thread,
+  // loaded now so its latency hides behind the main loop
   int row_out = 0;
-  if (tid < DBM) {
-    const int r = min(m0 + tid, rows - 1);
-    if constexpr (GATEUP) {
-      if (!shared) row_scale = p.gate[p.perm[row_base + r]];
-    } else if constexpr (MODE == MODE_DOWN_ROUTED) {
-      row_out = p.perm[row_base + r];
-    }
-  }
+  if (MODE == MODE_DOWN_ROUTED && tid < DBM) row_out = p.perm[row_base + min(m0 + tid, rows - 1)];
 
   // ---- this block's K range (split over blockIdx.z for the shared down
   // GEMM, whose single M-tile would otherwise leave most CUs idle) and this
@@ -141,29 +359,19 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
     const int kr = 4 * i + (lane >> 4);
     const int c = (lane & 15) ^ (2 * (kr & 3));
     const int lc = c * 8;
-    int gc;
-    if constexpr (GATEUP) gc = lc < BNH ? n0 + lc : NH + n0 + (lc - BNH);
-    else gc = n0 + lc;
-    const bool ok = n0 + (GATEUP ? lc % BNH : lc) < NH;
-    w_off[i] = static_cast<int64_t>(k0 + kr) * ldb + (ok ? gc : 0);
+    w_off[i] = static_cast<int64_t>(k0 + kr) * ldb + (n0 + lc < NH ? n0 + lc : 0);
   }
   const int64_t w_kstride = static_cast<int64_t>(DBK) * ldb;
 
   // activations: DMA instruction f fills rows 16f .. 16f+15 (64 B each) of the
   // stage's activation block; lane -> row 16f + lane/4, slot lane%4, which
   // holds logical chunk slot ^ ((row >> 1) & 3) (conflict-free fragment reads)
-  const uint16_t* abase;
-  if constexpr (GATEUP) abase = reinterpret_cast<const uint16_t*>(shared ? p.A_shared : p.A);
-  else if constexpr (MODE == MODE_DOWN_SHARED) abase = reinterpret_cast<const uint16_t*>(p.A_shared);
-  else abase = reinterpret_cast<const uint16_t*>(p.A);
+  const uint16_t* abase = reinterpret_cast<const uint16_t*>(shared ? p.A_shared : p.A);
   int64_t a_off[FMMAX];
 #pragma unroll
   for (int f = 0; f < FMMAX; ++f) {
     const int r = min(m0 + 16 * f + (lane >> 2), rows - 1);
-    int arow;
-    if constexpr (GATEUP) arow = shared ? r : p.perm[row_base + r];
-    else if constexpr (MODE == MODE_DOWN_SHARED) arow = r;
-    else arow = row_base + r;
+    const int arow = row_base + r;
     a_off[f] = static_cast<int64_t>(arow) * K + k0 + (((lane & 3) ^ ((lane >> 3) & 3)) * 8);
   }
 
@@ -184,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
     const int s_ = min((st), ns - 1);                                                          \
     const uint32_t b_ = ring + static_cast<uint32_t>(((st) % DNBUF) * STAGE);                  \
     _Pragma("unroll") for (int i = 0; i < INS; ++i)                                            \
-      dma16(wbase + w_off[i] + s_ * w_kstride, b_ + i * 1024);                                 \
+      dma16_nt(wbase + w_off[i] + s_ * w_kstride, b_ + i * 1024);                                 \
     _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
       dma16(abase + a_off[f] + s_ * DBK, b_ + WSTAGE + f * 1024);                              \
   } while (0)
@@ -195,12 +403,8 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
     wait_vmcnt<(DNBUF - 1) * LOADS>();                                                         \
     const lds_u8* st_ = ring_p + ((kt) % DNBUF) * STAGE;                                       \
     bf16x8 wf[FN], af[FMMAX];                                                                  \
-    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                           \
-      int col_;                                                                                \
-      if constexpr (GATEUP) col_ = (j < FN / 2 ? 0 : BNH) + (j % (FN / 2)) * 16;               \
-      else col_ = j * 16;                                                                      \
-      wf[j] = read_w_frag(st_, (lane >> 4) * 8, col_, lane);                                   \
-    }                                                                                          \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
+      wf[j] = read_w_frag(st_, (lane >> 4) * 8, j * 16, lane);                                 \
     _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
       af[f] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(st_ + a_rd + f * 1024); \
     _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
@@ -233,10 +437,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
           part[(wave * DBM + 16 * f + rq + q) * DBN + j * 16 + lcol] = acc[f][j][q];
     }
   }
-  if (tid < DBM) {
-    if constexpr (GATEUP) reinterpret_cast<float*>(smem + PART)[tid] = row_scale;
-    else reinterpret_cast<int*>(smem + PART)[tid] = row_out;
-  }
+  if (tid < DBM) reinterpret_cast<int*>(smem + PART)[tid] = row_out;
   __syncthreads();
   auto total = [&](int r, int c) -> float {
     return part[(0 * DBM + r) * DBN + c] + part[(1 * DBM + r) * DBN + c] + part[(2 * DBM + r) * DBN + c] +
@@ -247,22 +448,8 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
   // trip count, fully unrolled, every global load ahead of the stores (the
   // compiler must assume stores through C may alias the loaded arrays, so a
   // load between stores would wait a full round trip).
-  constexpr int NIT = DBM * BNH / 256;
-  if constexpr (GATEUP) {
-    void* C = shared ? p.C_shared : p.C;
-    const float* sct = reinterpret_cast<const float*>(smem + PART);
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int e = tid + 256 * it;
-      const int r = e / BNH, c = e % BNH;
-      const int col = n0 + c;
-      if (r >= nvalid || col >= NH) continue;
-      const int orow = row_base + m0 + r;
-      const float gv = total(r, c) * sct[r];
-      const float uv = total(r, BNH + c) * sct[r];
-      reinterpret_cast<uint16_t*>(C)[static_cast<int64_t>(orow) * NH + col] = f32_to_bf16(silu_f(gv) * uv);
-    }
-  } else {
+  constexpr int NIT = DBM * DBN / 256;
+  {
     const int* ot = reinterpret_cast<const int*>(smem + PART);
     float y[NIT];
     if constexpr (MODE == MODE_DOWN_ROUTED) {
@@ -278,7 +465,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
 #pragma unroll
           for (int it = 0; it < NIT; ++it) {
             const int e = tid + 256 * it;
-            const int r = e / BNH, col = n0 + e % BNH;
+            const int r = e / DBN, col = n0 + e % DBN;
             yv[u][it] = (s0 + u < nparts && r < nvalid && col < NH)
                             ? p.Y[(s0 + u) * pstride + static_cast<int64_t>(ot[r]) * NH + col] : 0.0f;
           }
@@ -292,7 +479,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int e = tid + 256 * it;
-      const int r = e / BNH, c = e % BNH;
+      const int r = e / DBN, c = e % DBN;
       const int col = n0 + c;
       if (r >= nvalid || col >= NH) continue;
       const int orow = (MODE == MODE_DOWN_ROUTED) ? ot[r] : m0 + r;
@@ -314,22 +501,30 @@ hipError_t launch_dec(const GemmArgs& a0, int T, hipStream_t s, const int32_t* t
   constexpr int DBM = 16 * FMMAX;
   GemmArgs a = a0;
   a.tiles = tiles_all + bm_index(DBM) * (a.E + 2);
-  constexpr int BNH = MODE == MODE_GATEUP ? DBN / 2 : DBN;
-  const bool has_routed = a.group_lo < a.E;
-  const bool has_shared = a.group_hi > a.E;
   const int mt_tok = (T + DBM - 1) / DBM;
-  int gm, nmax = a.N;
-  if constexpr (MODE == MODE_DOWN_SHARED) {
-    gm = mt_tok;
-  } else {
-    gm = (has_routed ? mt_tok + a.E : 0) + (has_shared ? mt_tok : 0);
-    if (MODE == MODE_GATEUP) nmax = max(has_routed ? a.N : 0, has_shared ? a.N_shared : 0);
-  }
+  const int gm = MODE == MODE_DOWN_SHARED ? mt_tok : mt_tok + a.E;
   if (gm <= 0) return hipSuccess;
-  const int gn = (nmax + BNH - 1) / BNH;
+  const int gn = (a.N + DBN - 1) / DBN;
   const int ks = (MODE == MODE_DOWN_SHARED && a.ksplit > 1) ? a.ksplit : 1;
   if (a.K % (128 * ks) != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_decode_kernel<MODE, FMMAX>), dim3(gm, gn, ks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FMMAX>
+hipError_t launch_dec_gateup(const GemmArgs& a0, int T, hipStream_t s, const int32_t* tiles_all) {
+  constexpr int DBM = 16 * FMMAX;
+  GemmArgs a = a0;
+  a.tiles = tiles_all + bm_index(DBM) * (a.E + 2);
+  const bool has_routed = a.group_lo < a.E;
+  const bool has_shared = a.group_hi > a.E;
+  const int mt_tok = (T + DBM - 1) / DBM;
+  const int gm = (has_routed ? mt_tok + a.E : 0) + (has_shared ? mt_tok : 0);
+  const int nmax = std::max(has_routed ? a.N : 0, has_shared ? a.N_shared : 0);
+  const int gn = (nmax + GBNH - 1) / GBNH;
+  if (gm <= 0 || gn <= 0) return hipSuccess;
+  if (a.K % (4 * GBK) != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_decode_gateup_kernel<FMMAX>), dim3(gm, gn), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -342,13 +537,13 @@ hipError_t launch_gemm_decode(int mode, bool rows32, const GemmArgs& a, int T, h
                               const int32_t* tiles_all) {
   if (rows32) {
     switch (mode) {
-      case MODE_GATEUP: return launch_dec<MODE_GATEUP, 2>(a, T, s, tiles_all);
+      case MODE_GATEUP: return launch_dec_gateup<2>(a, T, s, tiles_all);
       case MODE_DOWN_SHARED: return launch_dec<MODE_DOWN_SHARED, 2>(a, T, s, tiles_all);
       case MODE_DOWN_ROUTED: return launch_dec<MODE_DOWN_ROUTED, 2>(a, T, s, tiles_all);
     }
   } else {
     switch (mode) {
-      case MODE_GATEUP: return launch_dec<MODE_GATEUP, 1>(a, T, s, tiles_all);
+      case MODE_GATEUP: return launch_dec_gateup<1>(a, T, s, tiles_all);
       case MODE_DOWN_SHARED: return launch_dec<MODE_DOWN_SHARED, 1>(a, T, s, tiles_all);
       case MODE_DOWN_ROUTED: return launch_dec<MODE_DOWN_ROUTED, 1>(a, T, s, tiles_all);
     }

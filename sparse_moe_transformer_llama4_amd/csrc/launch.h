@@ -94,8 +94,10 @@ hipError_t launch_gemm_bf16_tall(int mode, const GemmArgs& a, int T, hipStream_t
 // fp8 prefill tiling (128 x 256 tiles, K 128 per stage; K multiple of 128).
 hipError_t launch_gemm_fp8(int mode, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all);
 
-// bf16 weight-streaming tiling for decode-sized T (16- or 32-row tiles,
-// 128 weight columns, K split over the 4 waves; K must be a multiple of 128).
+// bf16 weight-streaming tiling for decode-sized T (16- or 32-row tiles, K
+// split over the 4 waves; K must be a multiple of 128).  Gate/up tiles are 128
+// gate + 128 up columns, down tiles 128 columns.  A gate/up or shared down
+// launch over the shared group alone does not read the routing tables.
 bool decode_supported(int K);
 hipError_t launch_gemm_decode(int mode, bool rows32, const GemmArgs& a, int T, hipStream_t s,
                               const int32_t* tiles_all);

@@ -2,9 +2,12 @@
 // Validation happens before any enqueue; the launch sequence is
 //   router -> scan -> permutation -> grouped gate/up GEMM (+ shared) ->
 //   [e4m3: quantise h] -> shared down GEMM -> routed down GEMM + combine,
-// all on the caller's stream, with no host synchronisation.
+// on the caller's stream, with no host synchronisation.  Decode-sized bf16
+// calls run the shared expert's two GEMMs on a side stream forked from and
+// joined back into the caller's stream.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "common.h"
@@ -13,9 +16,19 @@
 
 using namespace moe;
 
+// Side stream of one device for the decode schedule, with its fork / join
+// events (no timing).  Created on first use, default priority.
+struct AuxStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 16;
+
 struct moe_plan_s {
   moe_config cfg;
   int last_hip_error;
+  std::mutex mu;               // guards aux and each fork / join enqueue sequence
+  AuxStream aux[kMaxDevices];  // by device id
 };
 
 namespace {
@@ -46,6 +59,12 @@ int decode_y_parts(const moe_config& c, int64_t T) {
   for (int s = 8; s > 1; s >>= 1)
     if (c.f_shared % (128 * s) == 0) return s;
   return 1;
+}
+
+// The weight-streaming decode tiling serves bf16 calls of at most 64 tokens.
+bool use_decode(const moe_config& c, int64_t T) {
+  return c.w_dtype == MOE_BF16 && T > 0 && T <= kDecodeTokensMax && decode_supported(c.d) &&
+         decode_supported(c.f) && decode_supported(c.f_shared);
 }
 
 WsLayout layout_for(const moe_config& c, int64_t T) {
@@ -142,10 +161,8 @@ Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
   return o;
 }
 
-// Token counts from which the bf16 prefill tiling is used, and up to which
-// the weight-streaming decode tiling is used.
+// Token count from which the bf16 prefill tiling is used.
 constexpr int64_t kPrefillTokens = 256;
-constexpr int64_t kDecodeTokens = kDecodeTokensMax;
 
 // Tile height for the routed groups: 256 rows when the mean group holds at
 // least 192 tokens, else 128 (a taller tile reuses each weight tile for more
@@ -205,6 +222,133 @@ hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_we
   return hipSuccess;
 }
 
+GemmArgs gateup_args(const moe_config& c, const moe_weights* w, uint8_t* ws, const WsLayout& L, const Route& R,
+                     const void* a_x, float* sx, uint32_t* amax_r, uint32_t* amax_s, int T) {
+  const bool fp8 = c.w_dtype == MOE_E4M3;
+  GemmArgs g{};
+  g.A = a_x;
+  g.A_shared = a_x;
+  g.B = w->w_gate_up;
+  g.B_shared = w->ws_gate_up;
+  g.sB = fp8 ? w->s_gate_up : nullptr;
+  g.sB_shared = fp8 ? w->ss_gate_up : nullptr;
+  g.sA = sx;
+  g.sA_shared = sx;
+  g.K = c.d;
+  g.N = c.f;
+  g.N_shared = c.f_shared;
+  g.T = T;
+  g.E = c.n_experts;
+  g.offsets = R.offsets;
+  g.perm = R.perm;
+  g.gate = R.gate;
+  g.C = ws + L.h_r;
+  g.C_shared = ws + L.h_s;
+  g.amax = amax_r;
+  g.amax_shared = amax_s;
+  return g;
+}
+
+GemmArgs down_shared_args(const moe_config& c, const moe_weights* w, uint8_t* ws, const WsLayout& L,
+                          const Route& R, const void* h_s, const float* sh_s, int T, int ksplit) {
+  const bool fp8 = c.w_dtype == MOE_E4M3;
+  GemmArgs g{};
+  g.A_shared = h_s;
+  g.B_shared = w->ws_down;
+  g.sB_shared = fp8 ? w->ss_down : nullptr;
+  g.sA_shared = sh_s;
+  g.K = c.f_shared;
+  g.N = c.d;
+  g.T = T;
+  g.E = c.n_experts;
+  g.offsets = R.offsets;
+  g.C_shared = reinterpret_cast<float*>(ws + L.y_s);
+  g.ksplit = ksplit;
+  g.group_lo = c.n_experts;
+  g.group_hi = c.n_experts + 1;
+  return g;
+}
+
+GemmArgs down_routed_args(const moe_config& c, const moe_weights* w, uint8_t* ws, const WsLayout& L,
+                          const Route& R, const void* h_r, const float* sh_r, void* out, int T, int y_parts) {
+  const bool fp8 = c.w_dtype == MOE_E4M3;
+  GemmArgs g{};
+  g.A = h_r;
+  g.B = w->w_down;
+  g.sB = fp8 ? w->s_down : nullptr;
+  g.sA = sh_r;
+  g.K = c.f;
+  g.N = c.d;
+  g.T = T;
+  g.E = c.n_experts;
+  g.offsets = R.offsets;
+  g.perm = R.perm;
+  g.C = out;
+  g.Y = reinterpret_cast<const float*>(ws + L.y_s);
+  g.y_parts = y_parts;
+  g.out_bf16 = c.out_dtype == MOE_BF16;
+  g.group_lo = 0;
+  g.group_hi = c.n_experts;
+  return g;
+}
+
+// The plan's side stream of the calling device (created on first use), or
+// null when the caller's stream belongs to another device than the current
+// one.  Called with plan->mu held.
+const AuxStream* aux_for(moe_plan_t plan, hipStream_t stream, hipError_t* err) {
+  *err = hipSuccess;
+  int cur = 0;
+  hipDevice_t sdev = 0;
+  if ((*err = hipGetDevice(&cur)) != hipSuccess) return nullptr;
+  if ((*err = hipStreamGetDevice(stream, &sdev)) != hipSuccess) return nullptr;
+  if (sdev != cur || cur < 0 || cur >= kMaxDevices) return nullptr;
+  AuxStream& a = plan->aux[cur];
+  if (!a.stream) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if ((*err = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return nullptr;
+    if ((*err = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess ||
+        (*err = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) {
+      if (f) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(st);
+      return nullptr;
+    }
+    a.stream = st;
+    a.fork = f;
+    a.join = j;
+  }
+  return &a;
+}
+
+// Decode-sized bf16 schedule with the shared expert on a side stream: the
+// shared gate/up and down GEMMs depend on x alone, so they run while the
+// routing and the routed gate/up proceed on `stream`; the routed down GEMM,
+// which adds the shared output, waits for them.  Same kernels and arguments
+// as the serial schedule, hence the same results.
+hipError_t enqueue_decode_overlapped(const moe_config& c, const void* x, int T, const moe_weights* w, void* out,
+                                     uint8_t* ws, const WsLayout& L, const Route& R, const AuxStream& aux,
+                                     hipStream_t stream) {
+  hipError_t e;
+  const int ys = decode_y_parts(c, T);
+  if ((e = hipEventRecord(aux.fork, stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(aux.stream, aux.fork, 0)) != hipSuccess) return e;
+  GemmArgs g1 = gateup_args(c, w, ws, L, R, x, nullptr, nullptr, nullptr, T);
+  g1.group_lo = c.n_experts;
+  g1.group_hi = c.n_experts + 1;
+  if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, T, aux.stream, R.tiles)) != hipSuccess) return e;
+  const GemmArgs g2 = down_shared_args(c, w, ws, L, R, ws + L.h_s, nullptr, T, ys);
+  if ((e = launch_gemm_decode(MODE_DOWN_SHARED, true, g2, T, aux.stream, R.tiles)) != hipSuccess) return e;
+  if ((e = hipEventRecord(aux.join, aux.stream)) != hipSuccess) return e;
+
+  if ((e = enqueue_route(c, x, T, w, R, stream)) != hipSuccess) return e;
+  g1.group_lo = 0;
+  g1.group_hi = c.n_experts;
+  if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, T, stream, R.tiles)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(stream, aux.join, 0)) != hipSuccess) return e;
+  const GemmArgs g3 = down_routed_args(c, w, ws, L, R, ws + L.h_r, nullptr, out, T, ys);
+  return launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, T, stream, R.tiles);
+}
+
 }  // namespace
 
 extern "C" {
@@ -244,7 +388,15 @@ moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
   return MOE_OK;
 }
 
-void moe_plan_destroy(moe_plan_t plan) { delete plan; }
+void moe_plan_destroy(moe_plan_t plan) {
+  if (!plan) return;
+  for (AuxStream& a : plan->aux) {
+    if (a.fork) (void)hipEventDestroy(a.fork);
+    if (a.join) (void)hipEventDestroy(a.join);
+    if (a.stream) (void)hipStreamDestroy(a.stream);
+  }
+  delete plan;
+}
 
 int moe_last_hip_error(moe_plan_t plan) { return plan ? plan->last_hip_error : 0; }
 
@@ -281,7 +433,19 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   const WsLayout L = layout_for(c, T);
   const Route R = route_ptrs(ws, L, routing_out);
   const int Ti = static_cast<int>(T);
+  const bool dec = use_decode(c, T);
   hipError_t e;
+
+  if (dec && !ev) {
+    std::lock_guard<std::mutex> lock(plan->mu);
+    const AuxStream* aux = aux_for(plan, stream, &e);
+    if (e != hipSuccess) return hip_fail(plan, e);
+    if (aux) {
+      e = enqueue_decode_overlapped(c, x, Ti, w, out, ws, L, R, *aux, stream);
+      return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
+    }
+  }
+
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return hip_fail(plan, e);
   e = enqueue_route(c, x, Ti, w, R, stream);
@@ -310,34 +474,12 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   if ((e = mark(1)) != hipSuccess) return hip_fail(plan, e);
 
   // gate/up (routed groups + shared group) with the SwiGLU epilogue
-  GemmArgs g1{};
-  g1.A = a_x;
-  g1.A_shared = a_x;
-  g1.B = w->w_gate_up;
-  g1.B_shared = w->ws_gate_up;
-  g1.sB = fp8 ? w->s_gate_up : nullptr;
-  g1.sB_shared = fp8 ? w->ss_gate_up : nullptr;
-  g1.sA = sx;
-  g1.sA_shared = sx;
-  g1.K = c.d;
-  g1.N = c.f;
-  g1.N_shared = c.f_shared;
-  g1.T = Ti;
-  g1.E = c.n_experts;
-  g1.offsets = R.offsets;
-  g1.perm = R.perm;
-  g1.gate = R.gate;
-  g1.C = ws + L.h_r;
-  g1.C_shared = ws + L.h_s;
-  g1.amax = amax_r;
-  g1.amax_shared = amax_s;
+  GemmArgs g1 = gateup_args(c, w, ws, L, R, a_x, sx, amax_r, amax_s, Ti);
   // the prefill kernels address activations with 32-bit byte offsets
   const int64_t kmax = std::max(std::max(c.d, c.f), c.f_shared);
   const bool offsets32 = T * kmax * 2 < (int64_t{1} << 31);
   const bool v2 = c.w_dtype == MOE_BF16 && T >= kPrefillTokens && offsets32 && bf16_v2_supported(c.d, c.f, c.f_shared) &&
                   bf16_v2_supported(c.f, c.d, c.d) && bf16_v2_supported(c.f_shared, c.d, c.d);
-  const bool dec = c.w_dtype == MOE_BF16 && T <= kDecodeTokens && decode_supported(c.d) &&
-                   decode_supported(c.f) && decode_supported(c.f_shared);
   const bool f8 = fp8 && T >= kPrefillTokens && offsets32;
   const int bm_routed = routed_tile_rows(T, c.n_experts);
   if (f8) {
@@ -382,21 +524,8 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     h_s = ws + L.hq_s;
   }
 
-  float* y_s = reinterpret_cast<float*>(ws + L.y_s);
-  GemmArgs g2{};
-  g2.A_shared = h_s;
-  g2.B_shared = w->ws_down;
-  g2.sB_shared = fp8 ? w->ss_down : nullptr;
-  g2.sA_shared = sh_s;
-  g2.K = c.f_shared;
-  g2.N = c.d;
-  g2.T = Ti;
-  g2.E = c.n_experts;
-  g2.offsets = R.offsets;
-  g2.C_shared = y_s;
-  g2.ksplit = dec ? decode_y_parts(c, T) : 1;
-  g2.group_lo = c.n_experts;
-  g2.group_hi = c.n_experts + 1;
+  const int ys = dec ? decode_y_parts(c, T) : 1;
+  const GemmArgs g2 = down_shared_args(c, w, ws, L, R, h_s, sh_s, Ti, ys);
   e = f8   ? launch_gemm_fp8(MODE_DOWN_SHARED, g2, Ti, stream, R.tiles)
       : dec  ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
       : v2 ? launch_gemm_bf16_v2(MODE_DOWN_SHARED, down_tile_rows(T, 1, c.d, 256), g2, Ti, stream, R.tiles)
@@ -404,23 +533,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(plan, e);
 
-  GemmArgs g3{};
-  g3.A = h_r;
-  g3.B = w->w_down;
-  g3.sB = fp8 ? w->s_down : nullptr;
-  g3.sA = sh_r;
-  g3.K = c.f;
-  g3.N = c.d;
-  g3.T = Ti;
-  g3.E = c.n_experts;
-  g3.offsets = R.offsets;
-  g3.perm = R.perm;
-  g3.C = out;
-  g3.Y = y_s;
-  g3.y_parts = dec ? decode_y_parts(c, T) : 1;
-  g3.out_bf16 = c.out_dtype == MOE_BF16;
-  g3.group_lo = 0;
-  g3.group_hi = c.n_experts;
+  const GemmArgs g3 = down_routed_args(c, w, ws, L, R, h_r, sh_r, out, Ti, ys);
   e = f8   ? launch_gemm_fp8(MODE_DOWN_ROUTED, g3, Ti, stream, R.tiles)
       : dec  ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
       : v2 ? launch_gemm_bf16_v2(MODE_DOWN_ROUTED, down_tile_rows(T, c.n_experts, c.d, bm_routed), g3, Ti, stream,

@@ -162,3 +162,42 @@ def test_decode_path_one_hot_and_idle_nan(gpu):
     out, routing = run_gpu(_plan(cfg), g["x"], g)
     assert int(routing["counts"][5]) == cfg.T
     check_forward(cfg, inp, out, routing)
+
+
+def test_decode_side_stream_matches_serial_schedule(gpu):
+    # Decode-sized bf16 calls run the shared expert's GEMMs on a side stream.
+    # Same kernels and arguments as the serial schedule (moe_forward_timed):
+    # results must be identical bit for bit, also for back-to-back calls with
+    # different inputs on a non-default stream, sharing one workspace, with no
+    # host synchronisation in between (the fork of a call must wait for the
+    # previous call's routed down GEMM, which reads the shared output).
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = dataclasses.replace(synth.get_config("decode_like_bf16"), T=33, name="dec_stream")
+    p = _plan(cfg)
+    w = to_device(synth.make_inputs(cfg), gpu)
+    xs = [w["x"], torch.roll(w["x"], 5, 0).contiguous(), (w["x"] * 0.5).contiguous(),
+          torch.flip(w["x"], (0,)).contiguous()]
+    ws = torch.empty(moe.moe_workspace_size(p, cfg.T), dtype=torch.uint8, device=gpu)
+    odt = torch.float32 if cfg.out_dtype == "f32" else torch.bfloat16
+    ev = moe.StageEvents()
+    ref = []
+    for x in xs:
+        o = torch.empty((cfg.T, cfg.d), dtype=odt, device=gpu)
+        moe.moe_forward_timed(p, x, w, ev, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        ref.append(o.clone())
+    outs = [torch.full((cfg.T, cfg.d), float("nan"), dtype=odt, device=gpu) for _ in xs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for rep in range(2):
+            for x, o in zip(xs, outs):
+                moe.moe_forward(p, x, w, out=o, workspace=ws, stream=s)
+    s.synchronize()
+    for i, (r, o) in enumerate(zip(ref, outs)):
+        assert torch.equal(r, o), f"call {i}: side-stream schedule differs from the serial one"
+    # and the serial result is the oracle's
+    inp = synth.make_inputs(cfg)
+    out, routing = run_gpu(p, w["x"], w)
+    assert torch.equal(out, ref[0])
+    check_forward(cfg, inp, out, routing)
