@@ -16,6 +16,21 @@ __host__ __device__ constexpr int bm_index(int bm) {
   return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : 4;
 }
 
+// Tile tables published by the routing stage, each [E + 2] int32 (entry g =
+// first tile of group g, group E = the shared expert, entry E + 1 = total):
+//   table_all(bm):   every group in bm-row tiles;
+//   table_large(bm): only the routed groups of more than kSmallGroup tokens
+//                    (and the shared group) in bm-row tiles;
+//   kTableSmall:     only the routed groups of 1 .. kSmallGroup tokens, one
+//                    32-row tile each (no shared group).
+// The small groups are weight streams; they can take the 32-row
+// weight-streaming tiles while the MFMA tiles serve the rest.
+constexpr int kSmallGroup = 32;
+constexpr int kNumTables = 2 * kNumBM + 1;
+constexpr int kTableSmall = 2 * kNumBM;
+__host__ __device__ constexpr int table_all(int bm) { return bm_index(bm); }
+__host__ __device__ constexpr int table_large(int bm) { return kNumBM + bm_index(bm); }
+
 // Tokens handled by one router workgroup (4 waves x 16 tokens).
 constexpr int kRouteTokens = 64;
 
@@ -50,7 +65,7 @@ struct WsLayout {
   size_t idx, gate, counts, offsets, perm;  // routing record (used when the caller passes none)
   size_t hist;                              // int32 [nblocks_route][E] -> per-block bases
   size_t logits;                            // fp32 [router splits][T][E] partial router logits
-  size_t tiles;                             // int32 [kNumBM][E + 2] tile tables
+  size_t tiles;                             // int32 [kNumTables][E + 2] tile tables
   size_t h_r, h_s;                          // SwiGLU outputs (bf16 / f32; bf16 staging for e4m3)
   size_t hq_r, hq_s;                        // e4m3 codes of h (e4m3 only)
   size_t sh_r, sh_s;                        // per-row fp32 scales of h (e4m3 only)

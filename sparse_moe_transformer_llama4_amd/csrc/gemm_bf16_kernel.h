@@ -105,7 +105,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   // [x*gn/8, (x+1)*gn/8) for every M-tile, so each weight panel is fetched by
   // one XCD, and walks them M-major so the workgroups it runs together share
   // an A panel.  Ids beyond the real tile count exit.
-  const int nmt = (MODE == MODE_DOWN_SHARED) ? (T + BM - 1) / BM : p.tiles[p.group_hi] - p.tiles[p.group_lo];
+  // a launch over the shared group alone addresses its tiles directly (it
+  // does not read the routing tables, so it may run before routing ends)
+  const bool shared_only = MODE == MODE_DOWN_SHARED || (GATEUP && p.group_lo == E);
+  const int nmt = shared_only ? (T + BM - 1) / BM : p.tiles[p.group_hi] - p.tiles[p.group_lo];
   const int gn = p.n_tiles;
   const int lid = blockIdx.x;
   int mt_rel, nt;
@@ -121,8 +124,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
     nt = lid - mt_rel * gn;
   }
   int g, m0, rows;
-  if constexpr (MODE == MODE_DOWN_SHARED) {
-    g = 0;
+  if (shared_only) {
+    g = MODE == MODE_DOWN_SHARED ? 0 : E;
     m0 = mt_rel * BM;
     rows = T;
   } else {

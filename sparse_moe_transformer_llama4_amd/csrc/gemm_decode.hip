@@ -532,6 +532,26 @@ hipError_t launch_dec_gateup(const GemmArgs& a0, int T, hipStream_t s, const int
 
 bool decode_supported(int K) { return K % 128 == 0 && K >= 128; }
 
+hipError_t launch_gemm_decode_small(int mode, const GemmArgs& a0, hipStream_t s, const int32_t* tiles_all) {
+  GemmArgs a = a0;
+  a.tiles = tiles_all + kTableSmall * (a.E + 2);
+  a.group_lo = 0;
+  a.group_hi = a.E;
+  const int gm = a.E;   // one 32-row tile per small group at most
+  if (gm <= 0 || a.N <= 0) return hipSuccess;
+  if (mode == MODE_GATEUP) {
+    if (a.K % (4 * GBK) != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_decode_gateup_kernel<2>), dim3(gm, (a.N + GBNH - 1) / GBNH), dim3(256), 0, s, a);
+  } else if (mode == MODE_DOWN_ROUTED) {
+    if (a.K % 128 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_decode_kernel<MODE_DOWN_ROUTED, 2>), dim3(gm, (a.N + DBN - 1) / DBN, 1), dim3(256), 0,
+                       s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // rows32: 32-row tiles (for groups that may exceed 16 rows), else 16-row tiles.
 hipError_t launch_gemm_decode(int mode, bool rows32, const GemmArgs& a, int T, hipStream_t s,
                               const int32_t* tiles_all) {

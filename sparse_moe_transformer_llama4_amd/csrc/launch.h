@@ -21,7 +21,7 @@ struct ScanArgs {
   int nblocks, E, T;
   int32_t* counts;   // [E]
   int32_t* offsets;  // [E + 1]
-  int32_t* tiles;    // [kNumBM][E + 2]
+  int32_t* tiles;    // [kNumTables][E + 2]
 };
 
 enum GemmMode : int {
@@ -101,5 +101,10 @@ hipError_t launch_gemm_fp8(int mode, const GemmArgs& a, int T, hipStream_t s, co
 bool decode_supported(int K);
 hipError_t launch_gemm_decode(int mode, bool rows32, const GemmArgs& a, int T, hipStream_t s,
                               const int32_t* tiles_all);
+// The routed groups of 1 .. kSmallGroup tokens (table kTableSmall, one 32-row
+// tile each) on the weight-streaming tiles: MODE_GATEUP (SwiGLU epilogue) or
+// MODE_DOWN_ROUTED (un-permute + combine with the y_parts shared partials).
+// The other groups are left to launches over the table_large tables.
+hipError_t launch_gemm_decode_small(int mode, const GemmArgs& a, hipStream_t s, const int32_t* tiles_all);
 
 }  // namespace moe

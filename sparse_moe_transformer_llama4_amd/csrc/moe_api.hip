@@ -87,7 +87,7 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   L.perm = take(t * 4);
   L.hist = take(nb * E * 4);
   L.logits = take(static_cast<size_t>(router_splits(static_cast<int>(T), c.d, c.x_dtype)) * t * E * 4);
-  L.tiles = take(kNumBM * (E + 2) * 4);
+  L.tiles = take(kNumTables * (E + 2) * 4);
   L.h_r = take(t * c.f * hsz);
   L.h_s = take(t * c.f_shared * hsz);
   L.y_s = take(t * c.d * 4 * static_cast<size_t>(decode_y_parts(c, T)));
@@ -434,16 +434,52 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   const Route R = route_ptrs(ws, L, routing_out);
   const int Ti = static_cast<int>(T);
   const bool dec = use_decode(c, T);
+  const bool fp8 = c.w_dtype == MOE_E4M3;
+  // the prefill kernels address activations with 32-bit byte offsets
+  const int64_t kmax = std::max(std::max(c.d, c.f), c.f_shared);
+  const bool offsets32 = T * kmax * 2 < (int64_t{1} << 31);
+  const bool v2 = c.w_dtype == MOE_BF16 && T >= kPrefillTokens && offsets32 && bf16_v2_supported(c.d, c.f, c.f_shared) &&
+                  bf16_v2_supported(c.f, c.d, c.d) && bf16_v2_supported(c.f_shared, c.d, c.d);
+  const bool f8 = fp8 && T >= kPrefillTokens && offsets32;
+  const int bm_routed = routed_tile_rows(T, c.n_experts);
+  // bf16 prefill with few tokens per expert: the groups of at most
+  // kSmallGroup tokens take the weight-streaming tiles, the others the MFMA
+  // tiles (tables table_large / kTableSmall from the routing stage)
+  const bool split = v2 && bm_routed == 128 && decode_supported(c.d) && decode_supported(c.f);
+  const int32_t* tiles_routed = split ? R.tiles + kNumBM * (c.n_experts + 2) : R.tiles;
   hipError_t e;
 
-  if (dec && !ev) {
-    std::lock_guard<std::mutex> lock(plan->mu);
-    const AuxStream* aux = aux_for(plan, stream, &e);
+  // decode-sized and bf16 prefill calls use the plan's side stream (not the
+  // stage-timed variant, which keeps every stage on `stream`)
+  std::unique_lock<std::mutex> lock(plan->mu, std::defer_lock);
+  const AuxStream* aux = nullptr;
+  if (!ev && T > 0 && (dec || v2)) {
+    lock.lock();
+    aux = aux_for(plan, stream, &e);
     if (e != hipSuccess) return hip_fail(plan, e);
-    if (aux) {
-      e = enqueue_decode_overlapped(c, x, Ti, w, out, ws, L, R, *aux, stream);
-      return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
-    }
+  }
+  if (dec && aux) {
+    e = enqueue_decode_overlapped(c, x, Ti, w, out, ws, L, R, *aux, stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
+  }
+  // bf16 prefill: the shared expert's gate/up and down GEMMs depend on x
+  // alone and are MFMA-bound; on the side stream they overlap the routing and
+  // the routed gate/up (weight-streaming-bound when the groups are small).
+  // The routed down GEMM, which adds the shared output, waits for them.
+  const bool shared_side = v2 && aux;
+  if (shared_side) {
+    if ((e = hipEventRecord(aux->fork, stream)) != hipSuccess) return hip_fail(plan, e);
+    if ((e = hipStreamWaitEvent(aux->stream, aux->fork, 0)) != hipSuccess) return hip_fail(plan, e);
+    GemmArgs gs = gateup_args(c, w, ws, L, R, x, nullptr, nullptr, nullptr, Ti);
+    gs.group_lo = c.n_experts;
+    gs.group_hi = c.n_experts + 1;
+    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, Ti, aux->stream, R.tiles)) != hipSuccess)
+      return hip_fail(plan, e);
+    const GemmArgs g2s = down_shared_args(c, w, ws, L, R, ws + L.h_s, nullptr, Ti, 1);
+    if ((e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, down_tile_rows(T, 1, c.d, 256), g2s, Ti, aux->stream,
+                                 R.tiles)) != hipSuccess)
+      return hip_fail(plan, e);
+    if ((e = hipEventRecord(aux->join, aux->stream)) != hipSuccess) return hip_fail(plan, e);
   }
 
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
@@ -456,7 +492,6 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     return MOE_OK;
   }
 
-  const bool fp8 = c.w_dtype == MOE_E4M3;
   const void* a_x = x;
   float* sx = nullptr;
   uint32_t *amax_r = nullptr, *amax_s = nullptr;
@@ -475,13 +510,8 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
 
   // gate/up (routed groups + shared group) with the SwiGLU epilogue
   GemmArgs g1 = gateup_args(c, w, ws, L, R, a_x, sx, amax_r, amax_s, Ti);
-  // the prefill kernels address activations with 32-bit byte offsets
-  const int64_t kmax = std::max(std::max(c.d, c.f), c.f_shared);
-  const bool offsets32 = T * kmax * 2 < (int64_t{1} << 31);
-  const bool v2 = c.w_dtype == MOE_BF16 && T >= kPrefillTokens && offsets32 && bf16_v2_supported(c.d, c.f, c.f_shared) &&
-                  bf16_v2_supported(c.f, c.d, c.d) && bf16_v2_supported(c.f_shared, c.d, c.d);
-  const bool f8 = fp8 && T >= kPrefillTokens && offsets32;
-  const int bm_routed = routed_tile_rows(T, c.n_experts);
+  if (split && (e = launch_gemm_decode_small(MODE_GATEUP, g1, stream, R.tiles)) != hipSuccess)
+    return hip_fail(plan, e);
   if (f8) {
     g1.group_lo = 0;
     g1.group_hi = c.n_experts + 1;
@@ -495,11 +525,11 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   } else if (v2) {
     g1.group_lo = 0;
     g1.group_hi = c.n_experts;
-    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_routed, g1, Ti, stream, R.tiles)) != hipSuccess)
+    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_routed, g1, Ti, stream, tiles_routed)) != hipSuccess)
       return hip_fail(plan, e);
     g1.group_lo = c.n_experts;
     g1.group_hi = c.n_experts + 1;
-    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, 256, g1, Ti, stream, R.tiles)) != hipSuccess)
+    if (!shared_side && (e = launch_gemm_bf16_v2(MODE_GATEUP, 256, g1, Ti, stream, R.tiles)) != hipSuccess)
       return hip_fail(plan, e);
   } else {
     g1.group_lo = 0;
@@ -526,18 +556,23 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
 
   const int ys = dec ? decode_y_parts(c, T) : 1;
   const GemmArgs g2 = down_shared_args(c, w, ws, L, R, h_s, sh_s, Ti, ys);
-  e = f8   ? launch_gemm_fp8(MODE_DOWN_SHARED, g2, Ti, stream, R.tiles)
-      : dec  ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
+  e = shared_side ? hipSuccess
+      : f8        ? launch_gemm_fp8(MODE_DOWN_SHARED, g2, Ti, stream, R.tiles)
+      : dec       ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
       : v2 ? launch_gemm_bf16_v2(MODE_DOWN_SHARED, down_tile_rows(T, 1, c.d, 256), g2, Ti, stream, R.tiles)
            : launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(plan, e);
 
+  // the routed down GEMMs add the shared output: on the side stream's join
+  if (shared_side && (e = hipStreamWaitEvent(stream, aux->join, 0)) != hipSuccess) return hip_fail(plan, e);
   const GemmArgs g3 = down_routed_args(c, w, ws, L, R, h_r, sh_r, out, Ti, ys);
+  if (split && (e = launch_gemm_decode_small(MODE_DOWN_ROUTED, g3, stream, R.tiles)) != hipSuccess)
+    return hip_fail(plan, e);
   e = f8   ? launch_gemm_fp8(MODE_DOWN_ROUTED, g3, Ti, stream, R.tiles)
       : dec  ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
       : v2 ? launch_gemm_bf16_v2(MODE_DOWN_ROUTED, down_tile_rows(T, c.n_experts, c.d, bm_routed), g3, Ti, stream,
-                                 R.tiles)
+                                 tiles_routed)
            : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(4)) != hipSuccess) return hip_fail(plan, e);

@@ -266,29 +266,37 @@ __device__ void block_exclusive_scan(int (&v)[NV], int (&tot)[NV], int* sm /* [N
   }
 }
 
-// Writes counts, offsets[E + 1] and the tile tables from per-expert counts
-// held one per thread (thread e < E); group E of every table is the shared
+// Writes counts, offsets[E + 1] and the tile tables (see table_all /
+// table_large / kTableSmall) from per-expert counts held one per thread
+// (thread e < E); group E of every table but the small one is the shared
 // expert (T rows) and entry E + 1 the total.
 __device__ void offsets_and_tiles(int cnt, int E, int T, int32_t* counts, int32_t* offsets, int32_t* tiles,
                                   int* sm) {
   const int e = threadIdx.x;
-  int v[1 + kNumBM], tot[1 + kNumBM];
+  int v[1 + kNumTables], tot[1 + kNumTables];
   v[0] = cnt;
+  const bool large = cnt > kSmallGroup;
 #pragma unroll
-  for (int i = 0; i < kNumBM; ++i) v[1 + i] = (cnt + bm_of(i) - 1) / bm_of(i);
-  block_exclusive_scan<1 + kNumBM>(v, tot, sm);
+  for (int i = 0; i < kNumBM; ++i) {
+    const int t = (cnt + bm_of(i) - 1) / bm_of(i);
+    v[1 + i] = t;
+    v[1 + kNumBM + i] = large ? t : 0;
+  }
+  v[1 + kTableSmall] = (cnt > 0 && !large) ? 1 : 0;
+  block_exclusive_scan<1 + kNumTables>(v, tot, sm);
   if (e < E) {
     counts[e] = cnt;
     offsets[e] = v[0];
 #pragma unroll
-    for (int i = 0; i < kNumBM; ++i) tiles[i * (E + 2) + e] = v[1 + i];
+    for (int i = 0; i < kNumTables; ++i) tiles[i * (E + 2) + e] = v[1 + i];
   }
   if (e == 0) {
     offsets[E] = tot[0];
 #pragma unroll
-    for (int i = 0; i < kNumBM; ++i) {
+    for (int i = 0; i < kNumTables; ++i) {
+      const int shared = i == kTableSmall ? 0 : (T + bm_of(i % kNumBM) - 1) / bm_of(i % kNumBM);
       tiles[i * (E + 2) + E] = tot[1 + i];   // the shared group follows the routed ones
-      tiles[i * (E + 2) + E + 1] = tot[1 + i] + (T + bm_of(i) - 1) / bm_of(i);
+      tiles[i * (E + 2) + E + 1] = tot[1 + i] + shared;
     }
   }
 }
@@ -302,7 +310,7 @@ __device__ void offsets_and_tiles(int cnt, int E, int T, int32_t* counts, int32_
 // are all issued before the chunk's stores (a load after a store to the same
 // array would wait a full round trip).
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
-  __shared__ int sm[(1 + kNumBM) * 4];
+  __shared__ int sm[(1 + kNumTables) * 4];
   const int e = threadIdx.x;
   const int E = a.E;
   int running = 0;
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouterArgs a, int nspl
                                                           int32_t* perm) {
   __shared__ int cnt_s[256];
   __shared__ int ids[kRouteTokens];
-  __shared__ int sm[(1 + kNumBM) * 4];
+  __shared__ int sm[(1 + kNumTables) * 4];
   __shared__ float lg[kRouteTokens * 256];
   const int tid = threadIdx.x, E = a.E, T = a.T;
   cnt_s[tid] = 0;

@@ -99,6 +99,10 @@ TEST_SHAPES = {
                           w_dtype="e4m3", out_dtype="bf16", seed=15),
     "decode_like_bf16": MoEShape("decode_like_bf16", T=32, d=1024, E=16, f=512, fs=512,
                                  bias="cold", seed=16),
+    # skewed routing over 32 experts: 25 groups of 1..32 tokens (6 of them
+    # 17..32) next to 7 larger ones
+    "small_bf16_split": MoEShape("small_bf16_split", T=1200, d=512, E=32, f=384, fs=256,
+                                 bias="zipf", zipf_alpha=0.3, seed=17),
 }
 
 

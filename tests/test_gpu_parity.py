@@ -12,7 +12,7 @@ from parity import check_forward, run_gpu, to_device, output_error
 pytestmark = pytest.mark.gpu
 
 SHAPES = ["tiny_fp32", "small_fp32", "small_bf16", "small_bf16_bias", "small_bf16_out16",
-          "decode_like_bf16", "small_fp8"]
+          "decode_like_bf16", "small_fp8", "small_bf16_split"]
 
 
 def _plan(cfg, **kw):
@@ -164,15 +164,20 @@ def test_decode_path_one_hot_and_idle_nan(gpu):
     check_forward(cfg, inp, out, routing)
 
 
-def test_decode_side_stream_matches_serial_schedule(gpu):
-    # Decode-sized bf16 calls run the shared expert's GEMMs on a side stream.
-    # Same kernels and arguments as the serial schedule (moe_forward_timed):
-    # results must be identical bit for bit, also for back-to-back calls with
-    # different inputs on a non-default stream, sharing one workspace, with no
-    # host synchronisation in between (the fork of a call must wait for the
-    # previous call's routed down GEMM, which reads the shared output).
+@pytest.mark.parametrize("name,T", [("decode_like_bf16", 33), ("small_bf16_split", None)])
+def test_side_stream_matches_serial_schedule(gpu, name, T):
+    # Decode-sized bf16 calls run the shared expert's GEMMs, and bf16 prefill
+    # calls with few tokens per expert the small groups' GEMMs, on a side
+    # stream.  Same kernels and arguments as the serial schedule
+    # (moe_forward_timed): results must be identical bit for bit, also for
+    # back-to-back calls with different inputs on a non-default stream,
+    # sharing one workspace, with no host synchronisation in between (each
+    # call's fork must wait for the previous call's reads of the workspace).
     from sparse_moe_transformer_llama4_amd import moe
-    cfg = dataclasses.replace(synth.get_config("decode_like_bf16"), T=33, name="dec_stream")
+    cfg = synth.get_config(name)
+    if T is not None:
+        cfg = dataclasses.replace(cfg, T=T, name=f"{name}_T{T}")
+    print(f"[parity] side stream {cfg.name}", flush=True)
     p = _plan(cfg)
     w = to_device(synth.make_inputs(cfg), gpu)
     xs = [w["x"], torch.roll(w["x"], 5, 0).contiguous(), (w["x"] * 0.5).contiguous(),
