@@ -18,18 +18,19 @@ __host__ __device__ constexpr int bm_index(int bm) {
 
 // Tile tables published by the routing stage, each [E + 2] int32 (entry g =
 // first tile of group g, group E = the shared expert, entry E + 1 = total):
-//   table_all(bm):   every group in bm-row tiles;
-//   table_large(bm): only the routed groups of more than kSmallGroup tokens
-//                    (and the shared group) in bm-row tiles;
-//   kTableSmall:     only the routed groups of 1 .. kSmallGroup tokens, one
-//                    32-row tile each (no shared group).
-// The small groups are weight streams; they can take the 32-row
-// weight-streaming tiles while the MFMA tiles serve the rest.
-constexpr int kSmallGroup = 32;
-constexpr int kNumTables = 2 * kNumBM + 1;
-constexpr int kTableSmall = 2 * kNumBM;
+//   table_all(bm):  every group in bm-row tiles;
+//   table_main(bm): the routed groups' bm-row tiles without their tails (and
+//                   the shared group): a group whose last bm-row tile would
+//                   hold only 1..kTailRows rows gets floor(n / bm) tiles;
+//   table_tail(bm): those tails, one kTailRows-row tile each (rows
+//                   bm * floor(n / bm) .. n - 1; no shared group).
+// A group of 1..kTailRows tokens is all tail.  Tails are weight streams: they
+// take the 32-row weight-streaming tiles while the MFMA tiles do the rest.
+constexpr int kTailRows = 32;
+constexpr int kNumTables = 3 * kNumBM;
 __host__ __device__ constexpr int table_all(int bm) { return bm_index(bm); }
-__host__ __device__ constexpr int table_large(int bm) { return kNumBM + bm_index(bm); }
+__host__ __device__ constexpr int table_main(int bm) { return kNumBM + bm_index(bm); }
+__host__ __device__ constexpr int table_tail(int bm) { return 2 * kNumBM + bm_index(bm); }
 
 // Tokens handled by one router workgroup (4 waves x 16 tokens).
 constexpr int kRouteTokens = 64;

@@ -4,17 +4,20 @@
 // expert's W_gate_up and W_down are read once from HBM and each weight is
 // used by a handful of rows.  The kernels therefore optimise bytes in
 // flight, not MFMA reuse:
-//   * workgroup tile = (group, 16 or 32 rows, 128 weight columns); gate/up
-//     tiles pair 64 gate columns with the matching 64 up columns;
+//   * workgroup tile = (group, 16 or 32 rows, 128 weight columns; gate/up:
+//     128 gate + the matching 128 up columns), grid (row tile, column tile)
+//     with the row tile fastest: the workgroups running together read many
+//     different weight matrices (measured faster than walking one matrix's
+//     columns together);
 //   * wave-level split-K: each of the 4 waves streams its own quarter of K
-//     through a private LDS ring (4 deep for 16-row tiles, 3 deep for 32-row
-//     tiles) fed by direct-to-LDS loads (global_load_lds_dwordx4), so the
+//     through a private 4-deep LDS ring fed by direct-to-LDS loads
+//     (global_load_lds_dwordx4, weights with the non-temporal hint), so the
 //     main loop needs no workgroup barrier -- each wave only waits for its
-//     own DMA (vmcnt) -- and 80-108 KB per CU are in flight against HBM
+//     own DMA (vmcnt) -- and ~108 KB per CU are in flight against HBM
 //     latency;
-//   * weight rows are 256 B in LDS; 16-byte chunk c of row r is stored at
-//     c ^ (2 * (r & 3)) so the LDS transpose reads (ds_read_b64_tr_b16) of
-//     four consecutive rows hit disjoint banks;
+//   * down tiles keep 256-byte weight rows in LDS (16-byte chunk c of row r
+//     at c ^ 2 (r & 3)), gate/up tiles 512-byte rows (c ^ 2 (r & 7)), so the
+//     LDS transpose reads (ds_read_b64_tr_b16) hit disjoint banks;
 //   * the activation rows of each stage travel through the same per-wave
 //     DMA ring (1-2 KB per stage), so every load in the loop is ordered by
 //     the explicit waits and none by compiler-inserted ones;
@@ -118,14 +121,17 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_gateup_kernel(GemmArgs p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E, K = p.K;
 
-  // ---- tile lookup (DBM-row tiles over groups group_lo .. group_hi - 1)
+  // ---- tile lookup (DBM-row tiles over groups group_lo .. group_hi - 1);
+  // grid (row tile, column tile), or (column tile, row tile) for tail launches
+  const int bi_m = p.tail_bm > 0 ? blockIdx.y : blockIdx.x;
+  const int bi_n = p.tail_bm > 0 ? blockIdx.x : blockIdx.y;
   int g, m0;
   if (p.group_lo == E) {
     g = E;
-    m0 = blockIdx.x * DBM;
+    m0 = bi_m * DBM;
     if (m0 >= p.T) return;
   } else {
-    const int mt = blockIdx.x + p.tiles[p.group_lo];
+    const int mt = bi_m + p.tiles[p.group_lo];
     if (mt >= p.tiles[p.group_hi]) return;
     int lo = p.group_lo, hi = p.group_hi - 1;
     while (lo < hi) {
@@ -136,9 +142,11 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_gateup_kernel(GemmArgs p) 
     m0 = (mt - p.tiles[g]) * DBM;
   }
   const int rows = (g == E) ? p.T : p.offsets[g + 1] - p.offsets[g];
+  // tail launches: the tile starts after the group's full tail_bm-row tiles
+  if (p.tail_bm > 0 && g < E) m0 += (rows / p.tail_bm) * p.tail_bm;
   const bool shared = g == E;
   const int NH = shared ? p.N_shared : p.N;
-  const int n0 = blockIdx.y * GBNH;
+  const int n0 = bi_n * GBNH;
   if (n0 >= NH) return;
   const int row_base = shared ? 0 : p.offsets[g];
   const int ldb = 2 * NH;
@@ -308,15 +316,18 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E, T = p.T, K = p.K;
 
-  // ---- tile lookup (DBM-row tiles)
+  // ---- tile lookup (DBM-row tiles); grid (row tile, column tile, K part),
+  // or (column tile, row tile) for tail launches
+  const int bi_m = p.tail_bm > 0 ? blockIdx.y : blockIdx.x;
+  const int bi_n = p.tail_bm > 0 ? blockIdx.x : blockIdx.y;
   int g, m0, rows;
   if constexpr (MODE == MODE_DOWN_SHARED) {
     g = 0;
-    m0 = blockIdx.x * DBM;
+    m0 = bi_m * DBM;
     rows = T;
     if (m0 >= T) return;
   } else {
-    const int mt = blockIdx.x + p.tiles[p.group_lo];
+    const int mt = bi_m + p.tiles[p.group_lo];
     if (mt >= p.tiles[p.group_hi]) return;
     int lo = p.group_lo, hi = p.group_hi - 1;
     while (lo < hi) {
@@ -326,10 +337,11 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
     g = lo;
     m0 = (mt - p.tiles[g]) * DBM;
     rows = p.offsets[g + 1] - p.offsets[g];
+    if (p.tail_bm > 0) m0 += (rows / p.tail_bm) * p.tail_bm;   // tail launches
   }
   constexpr bool shared = MODE == MODE_DOWN_SHARED;
   const int NH = p.N;
-  const int n0 = blockIdx.y * DBN;
+  const int n0 = bi_n * DBN;
   if (n0 >= NH) return;
   const int row_base = shared ? 0 : p.offsets[g];
   const int ldb = NH;
@@ -532,19 +544,26 @@ hipError_t launch_dec_gateup(const GemmArgs& a0, int T, hipStream_t s, const int
 
 bool decode_supported(int K) { return K % 128 == 0 && K >= 128; }
 
-hipError_t launch_gemm_decode_small(int mode, const GemmArgs& a0, hipStream_t s, const int32_t* tiles_all) {
+hipError_t launch_gemm_decode_tail(int mode, const GemmArgs& a0, int bm_main, hipStream_t s,
+                                   const int32_t* tiles_all) {
+  static_assert(kTailRows == 32, "tails are single 32-row tiles");
   GemmArgs a = a0;
-  a.tiles = tiles_all + kTableSmall * (a.E + 2);
+  a.tiles = tiles_all + table_tail(bm_main) * (a.E + 2);
+  a.tail_bm = bm_main;
   a.group_lo = 0;
   a.group_hi = a.E;
-  const int gm = a.E;   // one 32-row tile per small group at most
+  // one tail tile per group at most.  Grid (column tile, row tile), column
+  // tile fastest: a group's workgroups spread over the 8 XCDs (ids go
+  // round-robin) whichever groups have tails, and run together on adjacent
+  // segments of the same weight rows, which the group's main tiles also read
+  const int gm = a.E;
   if (gm <= 0 || a.N <= 0) return hipSuccess;
   if (mode == MODE_GATEUP) {
     if (a.K % (4 * GBK) != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_decode_gateup_kernel<2>), dim3(gm, (a.N + GBNH - 1) / GBNH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_decode_gateup_kernel<2>), dim3((a.N + GBNH - 1) / GBNH, gm), dim3(256), 0, s, a);
   } else if (mode == MODE_DOWN_ROUTED) {
     if (a.K % 128 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_decode_kernel<MODE_DOWN_ROUTED, 2>), dim3(gm, (a.N + DBN - 1) / DBN, 1), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_decode_kernel<MODE_DOWN_ROUTED, 2>), dim3((a.N + DBN - 1) / DBN, gm, 1), dim3(256), 0,
                        s, a);
   } else {
     return hipErrorInvalidValue;

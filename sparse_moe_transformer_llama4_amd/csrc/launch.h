@@ -57,6 +57,7 @@ struct GemmArgs {
   int n_tiles;             // N-tiles per M-tile of this launch (set by the launcher)
   int ksplit;              // decode DOWN_SHARED: K split over blocks; partial s at C_shared + s*T*N (0 = 1)
   int y_parts;             // decode DOWN_ROUTED: Y holds this many partials, summed in order (0 = 1)
+  int tail_bm;             // weight-streaming tail launches: rows of the groups' full main tiles (0 = none)
 };
 
 // Router in two launches: partial logits over K slices of d (the slice count
@@ -101,10 +102,12 @@ hipError_t launch_gemm_fp8(int mode, const GemmArgs& a, int T, hipStream_t s, co
 bool decode_supported(int K);
 hipError_t launch_gemm_decode(int mode, bool rows32, const GemmArgs& a, int T, hipStream_t s,
                               const int32_t* tiles_all);
-// The routed groups of 1 .. kSmallGroup tokens (table kTableSmall, one 32-row
-// tile each) on the weight-streaming tiles: MODE_GATEUP (SwiGLU epilogue) or
-// MODE_DOWN_ROUTED (un-permute + combine with the y_parts shared partials).
-// The other groups are left to launches over the table_large tables.
-hipError_t launch_gemm_decode_small(int mode, const GemmArgs& a, hipStream_t s, const int32_t* tiles_all);
+// The tails of the routed groups for main tiles of bm_main rows (table
+// table_tail(bm_main): one 32-row tile per group, starting after the group's
+// full bm_main-row tiles) on the weight-streaming tiles: MODE_GATEUP (SwiGLU
+// epilogue) or MODE_DOWN_ROUTED (un-permute + combine with the y_parts shared
+// partials).  The rest is left to launches over table_main(bm_main).
+hipError_t launch_gemm_decode_tail(int mode, const GemmArgs& a, int bm_main, hipStream_t s,
+                                   const int32_t* tiles_all);
 
 }  // namespace moe

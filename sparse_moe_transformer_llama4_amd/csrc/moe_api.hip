@@ -20,7 +20,9 @@ using namespace moe;
 // events (no timing).  Created on first use, default priority.
 struct AuxStream {
   hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;  // side stream starts after / main stream resumes after
+  hipEvent_t routed = nullptr;                // routing done (main stream)
+  hipEvent_t shared = nullptr;                // shared expert's output done (side stream)
 };
 constexpr int kMaxDevices = 16;
 
@@ -305,17 +307,21 @@ const AuxStream* aux_for(moe_plan_t plan, hipStream_t stream, hipError_t* err) {
   AuxStream& a = plan->aux[cur];
   if (!a.stream) {
     hipStream_t st = nullptr;
-    hipEvent_t f = nullptr, j = nullptr;
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     if ((*err = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return nullptr;
-    if ((*err = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess ||
-        (*err = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) {
-      if (f) (void)hipEventDestroy(f);
-      (void)hipStreamDestroy(st);
-      return nullptr;
+    for (hipEvent_t& x : ev) {
+      if ((*err = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) {
+        for (hipEvent_t y : ev)
+          if (y) (void)hipEventDestroy(y);
+        (void)hipStreamDestroy(st);
+        return nullptr;
+      }
     }
     a.stream = st;
-    a.fork = f;
-    a.join = j;
+    a.fork = ev[0];
+    a.join = ev[1];
+    a.routed = ev[2];
+    a.shared = ev[3];
   }
   return &a;
 }
@@ -347,6 +353,73 @@ hipError_t enqueue_decode_overlapped(const moe_config& c, const void* x, int T, 
   if ((e = hipStreamWaitEvent(stream, aux.join, 0)) != hipSuccess) return e;
   const GemmArgs g3 = down_routed_args(c, w, ws, L, R, ws + L.h_r, nullptr, out, T, ys);
   return launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, T, stream, R.tiles);
+}
+
+// bf16 prefill.  Routed groups: main tiles of bm_r rows (gate/up) and bm_d
+// rows (down) on the MFMA kernels over table_main; the tails (the 1..32 rows
+// past a group's last full main tile, or all of a group of at most 32
+// tokens) on the 32-row weight-streaming tiles over table_tail.  With a side
+// stream:
+//   side: shared gate/up -> [routing done] -> tail gate/up -> shared down ->
+//         (shared output done) -> tail down -> (join)
+//   main: routing -> routed main gate/up -> [shared output done] ->
+//         routed main down -> [join]
+// The shared expert depends on x alone and the tails are weight streams;
+// both overlap the MFMA-bound main tiles.  Without a side stream (the
+// stage-timed variant) the same launches run in stage order on `stream`.
+hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const moe_weights* w, void* out,
+                                uint8_t* ws, const WsLayout& L, const Route& R, const AuxStream* aux,
+                                hipStream_t stream, hipEvent_t* ev) {
+  hipError_t e;
+  const int E = c.n_experts;
+  const int bm_r = routed_tile_rows(T, E);
+  const int bm_d = down_tile_rows(T, E, c.d, bm_r);
+  const int bm_sd = down_tile_rows(T, 1, c.d, 256);
+  const bool tails = decode_supported(c.d) && decode_supported(c.f);
+  const int32_t* tiles_main = tails ? R.tiles + kNumBM * (E + 2) : R.tiles;
+  GemmArgs g1 = gateup_args(c, w, ws, L, R, x, nullptr, nullptr, nullptr, T);
+  GemmArgs gs = g1;
+  gs.group_lo = E;
+  gs.group_hi = E + 1;
+  g1.group_lo = 0;
+  g1.group_hi = E;
+  const GemmArgs g2 = down_shared_args(c, w, ws, L, R, ws + L.h_s, nullptr, T, 1);
+  const GemmArgs g3 = down_routed_args(c, w, ws, L, R, ws + L.h_r, nullptr, out, T, 1);
+
+  if (aux) {
+    const hipStream_t a = aux->stream;
+    if ((e = hipEventRecord(aux->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(a, aux->fork, 0)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, T, a, R.tiles)) != hipSuccess) return e;
+    if ((e = enqueue_route(c, x, T, w, R, stream)) != hipSuccess) return e;
+    if (tails) {
+      if ((e = hipEventRecord(aux->routed, stream)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(a, aux->routed, 0)) != hipSuccess) return e;
+      if ((e = launch_gemm_decode_tail(MODE_GATEUP, g1, bm_r, a, R.tiles)) != hipSuccess) return e;
+    }
+    if ((e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, bm_sd, g2, T, a, R.tiles)) != hipSuccess) return e;
+    if ((e = hipEventRecord(aux->shared, a)) != hipSuccess) return e;
+    if (tails && (e = launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3, bm_d, a, R.tiles)) != hipSuccess) return e;
+    if ((e = hipEventRecord(aux->join, a)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_r, g1, T, stream, tiles_main)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, aux->shared, 0)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3, T, stream, tiles_main)) != hipSuccess) return e;
+    return hipStreamWaitEvent(stream, aux->join, 0);
+  }
+
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  if ((e = mark(0)) != hipSuccess) return e;
+  if ((e = enqueue_route(c, x, T, w, R, stream)) != hipSuccess) return e;
+  if ((e = mark(1)) != hipSuccess) return e;
+  if (tails && (e = launch_gemm_decode_tail(MODE_GATEUP, g1, bm_r, stream, R.tiles)) != hipSuccess) return e;
+  if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_r, g1, T, stream, tiles_main)) != hipSuccess) return e;
+  if ((e = launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, T, stream, R.tiles)) != hipSuccess) return e;
+  if ((e = mark(2)) != hipSuccess) return e;
+  if ((e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, bm_sd, g2, T, stream, R.tiles)) != hipSuccess) return e;
+  if ((e = mark(3)) != hipSuccess) return e;
+  if (tails && (e = launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3, bm_d, stream, R.tiles)) != hipSuccess) return e;
+  if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3, T, stream, tiles_main)) != hipSuccess) return e;
+  return mark(4);
 }
 
 }  // namespace
@@ -391,8 +464,8 @@ moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
 void moe_plan_destroy(moe_plan_t plan) {
   if (!plan) return;
   for (AuxStream& a : plan->aux) {
-    if (a.fork) (void)hipEventDestroy(a.fork);
-    if (a.join) (void)hipEventDestroy(a.join);
+    for (hipEvent_t ev : {a.fork, a.join, a.routed, a.shared})
+      if (ev) (void)hipEventDestroy(ev);
     if (a.stream) (void)hipStreamDestroy(a.stream);
   }
   delete plan;
@@ -441,12 +514,6 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   const bool v2 = c.w_dtype == MOE_BF16 && T >= kPrefillTokens && offsets32 && bf16_v2_supported(c.d, c.f, c.f_shared) &&
                   bf16_v2_supported(c.f, c.d, c.d) && bf16_v2_supported(c.f_shared, c.d, c.d);
   const bool f8 = fp8 && T >= kPrefillTokens && offsets32;
-  const int bm_routed = routed_tile_rows(T, c.n_experts);
-  // bf16 prefill with few tokens per expert: the groups of at most
-  // kSmallGroup tokens take the weight-streaming tiles, the others the MFMA
-  // tiles (tables table_large / kTableSmall from the routing stage)
-  const bool split = v2 && bm_routed == 128 && decode_supported(c.d) && decode_supported(c.f);
-  const int32_t* tiles_routed = split ? R.tiles + kNumBM * (c.n_experts + 2) : R.tiles;
   hipError_t e;
 
   // decode-sized and bf16 prefill calls use the plan's side stream (not the
@@ -462,26 +529,10 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     e = enqueue_decode_overlapped(c, x, Ti, w, out, ws, L, R, *aux, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
   }
-  // bf16 prefill: the shared expert's gate/up and down GEMMs depend on x
-  // alone and are MFMA-bound; on the side stream they overlap the routing and
-  // the routed gate/up (weight-streaming-bound when the groups are small).
-  // The routed down GEMM, which adds the shared output, waits for them.
-  const bool shared_side = v2 && aux;
-  if (shared_side) {
-    if ((e = hipEventRecord(aux->fork, stream)) != hipSuccess) return hip_fail(plan, e);
-    if ((e = hipStreamWaitEvent(aux->stream, aux->fork, 0)) != hipSuccess) return hip_fail(plan, e);
-    GemmArgs gs = gateup_args(c, w, ws, L, R, x, nullptr, nullptr, nullptr, Ti);
-    gs.group_lo = c.n_experts;
-    gs.group_hi = c.n_experts + 1;
-    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, Ti, aux->stream, R.tiles)) != hipSuccess)
-      return hip_fail(plan, e);
-    const GemmArgs g2s = down_shared_args(c, w, ws, L, R, ws + L.h_s, nullptr, Ti, 1);
-    if ((e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, down_tile_rows(T, 1, c.d, 256), g2s, Ti, aux->stream,
-                                 R.tiles)) != hipSuccess)
-      return hip_fail(plan, e);
-    if ((e = hipEventRecord(aux->join, aux->stream)) != hipSuccess) return hip_fail(plan, e);
+  if (v2) {
+    e = enqueue_bf16_prefill(c, x, Ti, w, out, ws, L, R, aux, stream, ev);
+    return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
   }
-
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return hip_fail(plan, e);
   e = enqueue_route(c, x, Ti, w, R, stream);
@@ -510,8 +561,6 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
 
   // gate/up (routed groups + shared group) with the SwiGLU epilogue
   GemmArgs g1 = gateup_args(c, w, ws, L, R, a_x, sx, amax_r, amax_s, Ti);
-  if (split && (e = launch_gemm_decode_small(MODE_GATEUP, g1, stream, R.tiles)) != hipSuccess)
-    return hip_fail(plan, e);
   if (f8) {
     g1.group_lo = 0;
     g1.group_hi = c.n_experts + 1;
@@ -521,15 +570,6 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     g1.group_lo = 0;
     g1.group_hi = c.n_experts + 1;
     if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles)) != hipSuccess)
-      return hip_fail(plan, e);
-  } else if (v2) {
-    g1.group_lo = 0;
-    g1.group_hi = c.n_experts;
-    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_routed, g1, Ti, stream, tiles_routed)) != hipSuccess)
-      return hip_fail(plan, e);
-    g1.group_lo = c.n_experts;
-    g1.group_hi = c.n_experts + 1;
-    if (!shared_side && (e = launch_gemm_bf16_v2(MODE_GATEUP, 256, g1, Ti, stream, R.tiles)) != hipSuccess)
       return hip_fail(plan, e);
   } else {
     g1.group_lo = 0;
@@ -556,24 +596,16 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
 
   const int ys = dec ? decode_y_parts(c, T) : 1;
   const GemmArgs g2 = down_shared_args(c, w, ws, L, R, h_s, sh_s, Ti, ys);
-  e = shared_side ? hipSuccess
-      : f8        ? launch_gemm_fp8(MODE_DOWN_SHARED, g2, Ti, stream, R.tiles)
-      : dec       ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
-      : v2 ? launch_gemm_bf16_v2(MODE_DOWN_SHARED, down_tile_rows(T, 1, c.d, 256), g2, Ti, stream, R.tiles)
-           : launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles);
+  e = f8    ? launch_gemm_fp8(MODE_DOWN_SHARED, g2, Ti, stream, R.tiles)
+      : dec ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
+            : launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(plan, e);
 
-  // the routed down GEMMs add the shared output: on the side stream's join
-  if (shared_side && (e = hipStreamWaitEvent(stream, aux->join, 0)) != hipSuccess) return hip_fail(plan, e);
   const GemmArgs g3 = down_routed_args(c, w, ws, L, R, h_r, sh_r, out, Ti, ys);
-  if (split && (e = launch_gemm_decode_small(MODE_DOWN_ROUTED, g3, stream, R.tiles)) != hipSuccess)
-    return hip_fail(plan, e);
-  e = f8   ? launch_gemm_fp8(MODE_DOWN_ROUTED, g3, Ti, stream, R.tiles)
-      : dec  ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
-      : v2 ? launch_gemm_bf16_v2(MODE_DOWN_ROUTED, down_tile_rows(T, c.n_experts, c.d, bm_routed), g3, Ti, stream,
-                                 tiles_routed)
-           : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
+  e = f8    ? launch_gemm_fp8(MODE_DOWN_ROUTED, g3, Ti, stream, R.tiles)
+      : dec ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
+            : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(4)) != hipSuccess) return hip_fail(plan, e);
   return MOE_OK;

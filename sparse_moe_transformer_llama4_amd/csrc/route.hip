@@ -267,22 +267,23 @@ __device__ void block_exclusive_scan(int (&v)[NV], int (&tot)[NV], int* sm /* [N
 }
 
 // Writes counts, offsets[E + 1] and the tile tables (see table_all /
-// table_large / kTableSmall) from per-expert counts held one per thread
-// (thread e < E); group E of every table but the small one is the shared
-// expert (T rows) and entry E + 1 the total.
+// table_main / table_tail) from per-expert counts held one per thread
+// (thread e < E); group E of the all / main tables is the shared expert
+// (T rows) and entry E + 1 the total.
 __device__ void offsets_and_tiles(int cnt, int E, int T, int32_t* counts, int32_t* offsets, int32_t* tiles,
                                   int* sm) {
   const int e = threadIdx.x;
   int v[1 + kNumTables], tot[1 + kNumTables];
   v[0] = cnt;
-  const bool large = cnt > kSmallGroup;
 #pragma unroll
   for (int i = 0; i < kNumBM; ++i) {
-    const int t = (cnt + bm_of(i) - 1) / bm_of(i);
-    v[1 + i] = t;
-    v[1 + kNumBM + i] = large ? t : 0;
+    const int bm = bm_of(i);
+    const int r = cnt % bm;
+    const bool tail = r > 0 && r <= kTailRows;
+    v[1 + i] = (cnt + bm - 1) / bm;
+    v[1 + kNumBM + i] = tail ? cnt / bm : (cnt + bm - 1) / bm;
+    v[1 + 2 * kNumBM + i] = tail ? 1 : 0;
   }
-  v[1 + kTableSmall] = (cnt > 0 && !large) ? 1 : 0;
   block_exclusive_scan<1 + kNumTables>(v, tot, sm);
   if (e < E) {
     counts[e] = cnt;
@@ -294,7 +295,7 @@ __device__ void offsets_and_tiles(int cnt, int E, int T, int32_t* counts, int32_
     offsets[E] = tot[0];
 #pragma unroll
     for (int i = 0; i < kNumTables; ++i) {
-      const int shared = i == kTableSmall ? 0 : (T + bm_of(i % kNumBM) - 1) / bm_of(i % kNumBM);
+      const int shared = i >= 2 * kNumBM ? 0 : (T + bm_of(i % kNumBM) - 1) / bm_of(i % kNumBM);
       tiles[i * (E + 2) + E] = tot[1 + i];   // the shared group follows the routed ones
       tiles[i * (E + 2) + E + 1] = tot[1 + i] + shared;
     }

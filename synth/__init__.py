@@ -103,6 +103,9 @@ TEST_SHAPES = {
     # 17..32) next to 7 larger ones
     "small_bf16_split": MoEShape("small_bf16_split", T=1200, d=512, E=32, f=384, fs=256,
                                  bias="zipf", zipf_alpha=0.3, seed=17),
+    # ~275 tokens per expert (256-row routed tiles): four groups end in a
+    # 3..27-row tail past a full 256-row tile, two in a 38- / 50-row one
+    "small_bf16_tall": MoEShape("small_bf16_tall", T=2200, d=512, E=8, f=384, fs=256, seed=22),
 }
 
 
