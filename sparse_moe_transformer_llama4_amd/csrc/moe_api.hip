@@ -374,7 +374,9 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
   const int E = c.n_experts;
   const int bm_r = routed_tile_rows(T, E);
   const int bm_d = down_tile_rows(T, E, c.d, bm_r);
-  const int bm_sd = down_tile_rows(T, 1, c.d, 256);
+  // the shared down GEMM: 256-row tiles when it overlaps the routed work on
+  // the side stream (per-FLOP efficiency over full rounds), else by rounds
+  const int bm_sd = aux ? 256 : down_tile_rows(T, 1, c.d, 256);
   const bool tails = decode_supported(c.d) && decode_supported(c.f);
   const int32_t* tiles_main = tails ? R.tiles + kNumBM * (E + 2) : R.tiles;
   GemmArgs g1 = gateup_args(c, w, ws, L, R, x, nullptr, nullptr, nullptr, T);
