@@ -467,7 +467,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
           const bool ok = m0 + rt < rows && n0 + cc * 4 < NH;
           y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
           if constexpr (MODE == MODE_DOWN_ROUTED)
-            if (ok) y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
+            if (ok && p.Y) y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
@@ -475,7 +475,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
           const int r = k / CPR, cc = k - r * CPR;
           const int rt = pass * PR + r;
           if (m0 + rt >= rows || n0 + cc * 4 >= NH) continue;
-          const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
+          // routed rows without a shared output (Y null) are stored as summed
+          const f32x4 acc4 = *(const lds_f32x4*)(stage + r * FPB + cc * 16);
+          const f32x4 v = (MODE == MODE_DOWN_ROUTED && !p.Y) ? acc4 : acc4 + y[u];
           const int64_t o = static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4;
           if constexpr (MODE == MODE_DOWN_SHARED) {
             *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + o) = v;

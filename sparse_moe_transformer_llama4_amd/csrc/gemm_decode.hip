@@ -466,7 +466,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
     float y[NIT];
     if constexpr (MODE == MODE_DOWN_ROUTED) {
       // the shared expert's output, as y_parts K-split partials summed in order
-      const int nparts = p.y_parts > 1 ? p.y_parts : 1;
+      const int nparts = !p.Y ? 0 : p.y_parts > 1 ? p.y_parts : 1;
       const int64_t pstride = static_cast<int64_t>(T) * NH;
 #pragma unroll
       for (int it = 0; it < NIT; ++it) y[it] = 0.0f;
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
       if constexpr (MODE == MODE_DOWN_SHARED) {
         reinterpret_cast<float*>(p.C_shared)[static_cast<int64_t>(blockIdx.z) * T * NH + o] = v;
       } else {
-        const float yv = v + y[it];
+        const float yv = p.Y ? v + y[it] : v;
         if (p.out_bf16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16(yv);
         else reinterpret_cast<float*>(p.C)[o] = yv;
       }

@@ -52,6 +52,8 @@ bool config_dtypes_ok(const moe_config& c) {
 int k_multiple(const moe_config& c) { return c.w_dtype == MOE_E4M3 ? 128 : 64; }
 
 constexpr int64_t kDecodeTokensMax = 64;
+// Token count from which the bf16 prefill tiling is used.
+constexpr int64_t kPrefillTokens = 256;
 
 // Decode-sized calls split the shared down GEMM over K (its single M-tile
 // would leave most CUs idle): the number of partial shared outputs, summed in
@@ -93,6 +95,7 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   L.h_r = take(t * c.f * hsz);
   L.h_s = take(t * c.f_shared * hsz);
   L.y_s = take(t * c.d * 4 * static_cast<size_t>(decode_y_parts(c, T)));
+  if (c.w_dtype == MOE_BF16 && T >= kPrefillTokens) L.r_out = take(t * c.d * 4);
   if (fp8) {
     L.hq_r = take(t * c.f);
     L.hq_s = take(t * c.f_shared);
@@ -163,8 +166,6 @@ Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
   return o;
 }
 
-// Token count from which the bf16 prefill tiling is used.
-constexpr int64_t kPrefillTokens = 256;
 
 // Tile height for the routed groups: 256 rows when the mean group holds at
 // least 192 tokens, else 128 (a taller tile reuses each weight tile for more
@@ -361,12 +362,14 @@ hipError_t enqueue_decode_overlapped(const moe_config& c, const void* x, int T, 
 // tokens) on the 32-row weight-streaming tiles over table_tail.  With a side
 // stream:
 //   side: shared gate/up -> [routing done] -> tail gate/up -> shared down ->
-//         (shared output done) -> tail down -> (join)
-//   main: routing -> routed main gate/up -> [shared output done] ->
-//         routed main down -> [join]
+//         tail down (into r_out) -> (join)
+//   main: routing -> routed main gate/up -> routed main down (into r_out) ->
+//         [join] -> combine out = r_out + y_s
 // The shared expert depends on x alone and the tails are weight streams;
-// both overlap the MFMA-bound main tiles.  Without a side stream (the
-// stage-timed variant) the same launches run in stage order on `stream`.
+// both overlap the MFMA-bound main tiles, and neither down GEMM waits for
+// the other.  Without a side stream (the stage-timed variant) the same GEMMs
+// run in stage order on `stream`, the routed down epilogue adding y_s itself
+// (the same fp32 addition as the combine's).
 hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const moe_weights* w, void* out,
                                 uint8_t* ws, const WsLayout& L, const Route& R, const AuxStream* aux,
                                 hipStream_t stream, hipEvent_t* ev) {
@@ -399,14 +402,21 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
       if ((e = hipStreamWaitEvent(a, aux->routed, 0)) != hipSuccess) return e;
       if ((e = launch_gemm_decode_tail(MODE_GATEUP, g1, bm_r, a, R.tiles)) != hipSuccess) return e;
     }
+    // the routed down GEMMs store their sums (fp32, token order) in r_out
+    // and the combine adds the shared output at the end, so neither down
+    // GEMM waits for the other
+    GemmArgs g3r = g3;
+    g3r.C = ws + L.r_out;
+    g3r.Y = nullptr;
+    g3r.out_bf16 = 0;
     if ((e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, bm_sd, g2, T, a, R.tiles)) != hipSuccess) return e;
-    if ((e = hipEventRecord(aux->shared, a)) != hipSuccess) return e;
-    if (tails && (e = launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3, bm_d, a, R.tiles)) != hipSuccess) return e;
+    if (tails && (e = launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3r, bm_d, a, R.tiles)) != hipSuccess) return e;
     if ((e = hipEventRecord(aux->join, a)) != hipSuccess) return e;
     if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_r, g1, T, stream, tiles_main)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(stream, aux->shared, 0)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3, T, stream, tiles_main)) != hipSuccess) return e;
-    return hipStreamWaitEvent(stream, aux->join, 0);
+    if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3r, T, stream, tiles_main)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, aux->join, 0)) != hipSuccess) return e;
+    return launch_combine(reinterpret_cast<const float*>(ws + L.r_out), reinterpret_cast<const float*>(ws + L.y_s),
+                          out, static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream);
   }
 
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
