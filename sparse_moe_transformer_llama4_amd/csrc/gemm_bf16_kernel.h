@@ -139,7 +139,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
     m0 = (mt - p.tiles[g]) * BM;
     rows = (g == E) ? T : p.offsets[g + 1] - p.offsets[g];
   }
-  const bool shared = (MODE == MODE_DOWN_SHARED) || (GATEUP && g == E);
+  // the shared group: its own launch (DOWN_SHARED), or group E of a gate/up
+  // or routed down launch over groups .. E (the routed down then writes the
+  // shared output in token order to C_shared, the routed rows to C; the
+  // caller guarantees the same K, f == f_shared, for that launch)
+  const bool shared = (MODE == MODE_DOWN_SHARED) || g == E;
   const int NH = (GATEUP && shared) ? p.N_shared : p.N;
   const int n0 = nt * BNH;
   if (n0 >= NH) return;
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
     if constexpr (GATEUP) {
       if (!shared) row_scale = p.gate[p.perm[row_base + r]];
     } else if constexpr (MODE == MODE_DOWN_ROUTED) {
-      row_out = p.perm[row_base + r];
+      row_out = shared ? r : p.perm[row_base + r];
     }
   }
 
@@ -167,8 +171,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   // stored).  The caller guarantees T * K * 2 < 2^31.
   const uint8_t* a_src;
   if constexpr (GATEUP) a_src = reinterpret_cast<const uint8_t*>(shared ? p.A_shared : p.A);
-  else if constexpr (MODE == MODE_DOWN_SHARED) a_src = reinterpret_cast<const uint8_t*>(p.A_shared);
-  else a_src = reinterpret_cast<const uint8_t*>(p.A);
+  else a_src = reinterpret_cast<const uint8_t*>(shared ? p.A_shared : p.A);
   uint32_t a_voff[A_INS];
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
@@ -467,7 +470,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
           const bool ok = m0 + rt < rows && n0 + cc * 4 < NH;
           y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
           if constexpr (MODE == MODE_DOWN_ROUTED)
-            if (ok && p.Y) y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
+            if (ok && p.Y && !shared)
+              y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
@@ -477,9 +481,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
           if (m0 + rt >= rows || n0 + cc * 4 >= NH) continue;
           // routed rows without a shared output (Y null) are stored as summed
           const f32x4 acc4 = *(const lds_f32x4*)(stage + r * FPB + cc * 16);
-          const f32x4 v = (MODE == MODE_DOWN_ROUTED && !p.Y) ? acc4 : acc4 + y[u];
+          const f32x4 v = (MODE == MODE_DOWN_ROUTED && (!p.Y || shared)) ? acc4 : acc4 + y[u];
           const int64_t o = static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4;
-          if constexpr (MODE == MODE_DOWN_SHARED) {
+          if (shared) {
             *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + o) = v;
           } else if (p.out_bf16) {
             const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
@@ -512,6 +516,10 @@ hipError_t launch_v2(const GemmArgs& a0, int T, hipStream_t s, const int32_t* ti
     if (MODE == MODE_GATEUP) nmax = max(has_routed ? a.N : 0, has_shared ? a.N_shared : 0);
   }
   if (gm <= 0) return hipSuccess;
+  // a routed down launch that includes the shared group reads h_s and the
+  // shared weights with the routed K: the caller passes the shared K in
+  // N_shared, and it must match
+  if (MODE == MODE_DOWN_ROUTED && has_shared && a.N_shared != a.K) return hipErrorInvalidValue;
   const int gn = (nmax + BNH - 1) / BNH;
   a.n_tiles = gn;
   // 1-D grid: enough ids for the largest per-XCD share of (M-tile bound x N-tiles)

@@ -41,7 +41,7 @@ struct GemmArgs {
   const float* sA_shared;
   int K;
   int N;                 // GATEUP: routed half width f; DOWN: d
-  int N_shared;          // GATEUP: shared half width fs
+  int N_shared;          // GATEUP: shared half width fs; DOWN_ROUTED over groups .. E: fs (must equal K)
   int T, E;
   const int32_t* offsets;
   const int32_t* perm;

@@ -361,9 +361,10 @@ hipError_t enqueue_decode_overlapped(const moe_config& c, const void* x, int T, 
 // past a group's last full main tile, or all of a group of at most 32
 // tokens) on the 32-row weight-streaming tiles over table_tail.  With a side
 // stream:
-//   side: shared gate/up -> [routing done] -> tail gate/up -> shared down ->
+//   side: shared gate/up -> (h_s done) -> [routing done] -> tail gate/up ->
 //         tail down (into r_out) -> (join)
-//   main: routing -> routed main gate/up -> routed main down (into r_out) ->
+//   main: routing -> routed main gate/up -> [h_s done] -> one down launch:
+//         routed main tiles (into r_out) + shared tiles (into y_s) ->
 //         [join] -> combine out = r_out + y_s
 // The shared expert depends on x alone and the tails are weight streams;
 // both overlap the MFMA-bound main tiles, and neither down GEMM waits for
@@ -377,9 +378,7 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
   const int E = c.n_experts;
   const int bm_r = routed_tile_rows(T, E);
   const int bm_d = down_tile_rows(T, E, c.d, bm_r);
-  // the shared down GEMM: 256-row tiles when it overlaps the routed work on
-  // the side stream (per-FLOP efficiency over full rounds), else by rounds
-  const int bm_sd = aux ? 256 : down_tile_rows(T, 1, c.d, 256);
+  const int bm_sd = down_tile_rows(T, 1, c.d, 256);
   const bool tails = decode_supported(c.d) && decode_supported(c.f);
   const int32_t* tiles_main = tails ? R.tiles + kNumBM * (E + 2) : R.tiles;
   GemmArgs g1 = gateup_args(c, w, ws, L, R, x, nullptr, nullptr, nullptr, T);
@@ -393,27 +392,42 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
 
   if (aux) {
     const hipStream_t a = aux->stream;
+    // the routed down GEMMs store their sums (fp32, token order) in r_out and
+    // the combine adds the shared output at the end.  The main tiles of the
+    // routed groups and the shared group's tiles (group E, into y_s) form one
+    // down launch
+    GemmArgs g3r = g3;
+    g3r.C = ws + L.r_out;
+    g3r.Y = nullptr;
+    g3r.out_bf16 = 0;
+    // (when both take 256-row tiles and one K, f == f_shared; else the
+    // shared down GEMM runs in 256-row tiles on the side stream after the
+    // shared gate/up: in a 128-row launch it lost more than the merge gains)
+    const bool merge_down = c.f == c.f_shared && bm_d == 256;
+    GemmArgs g3m = g3r;
+    if (merge_down) {
+      g3m.A_shared = ws + L.h_s;
+      g3m.B_shared = w->ws_down;
+      g3m.C_shared = ws + L.y_s;
+      g3m.N_shared = c.f_shared;
+      g3m.group_hi = E + 1;
+    }
     if ((e = hipEventRecord(aux->fork, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(a, aux->fork, 0)) != hipSuccess) return e;
     if ((e = launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, T, a, R.tiles)) != hipSuccess) return e;
+    if (!merge_down && (e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, 256, g2, T, a, R.tiles)) != hipSuccess) return e;
+    if ((e = hipEventRecord(aux->shared, a)) != hipSuccess) return e;
     if ((e = enqueue_route(c, x, T, w, R, stream)) != hipSuccess) return e;
     if (tails) {
       if ((e = hipEventRecord(aux->routed, stream)) != hipSuccess) return e;
       if ((e = hipStreamWaitEvent(a, aux->routed, 0)) != hipSuccess) return e;
       if ((e = launch_gemm_decode_tail(MODE_GATEUP, g1, bm_r, a, R.tiles)) != hipSuccess) return e;
+      if ((e = launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3r, bm_d, a, R.tiles)) != hipSuccess) return e;
     }
-    // the routed down GEMMs store their sums (fp32, token order) in r_out
-    // and the combine adds the shared output at the end, so neither down
-    // GEMM waits for the other
-    GemmArgs g3r = g3;
-    g3r.C = ws + L.r_out;
-    g3r.Y = nullptr;
-    g3r.out_bf16 = 0;
-    if ((e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, bm_sd, g2, T, a, R.tiles)) != hipSuccess) return e;
-    if (tails && (e = launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3r, bm_d, a, R.tiles)) != hipSuccess) return e;
     if ((e = hipEventRecord(aux->join, a)) != hipSuccess) return e;
     if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_r, g1, T, stream, tiles_main)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3r, T, stream, tiles_main)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, aux->shared, 0)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3m, T, stream, tiles_main)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(stream, aux->join, 0)) != hipSuccess) return e;
     return launch_combine(reinterpret_cast<const float*>(ws + L.r_out), reinterpret_cast<const float*>(ws + L.y_s),
                           out, static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream);

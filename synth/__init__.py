@@ -100,12 +100,18 @@ TEST_SHAPES = {
     "decode_like_bf16": MoEShape("decode_like_bf16", T=32, d=1024, E=16, f=512, fs=512,
                                  bias="cold", seed=16),
     # skewed routing over 32 experts: 25 groups of 1..32 tokens (6 of them
-    # 17..32) next to 7 larger ones
-    "small_bf16_split": MoEShape("small_bf16_split", T=1200, d=512, E=32, f=384, fs=256,
+    # 17..32) next to 7 larger ones; f == fs (one down launch for the routed
+    # main tiles and the shared expert)
+    "small_bf16_split": MoEShape("small_bf16_split", T=1200, d=512, E=32, f=384, fs=384,
                                  bias="zipf", zipf_alpha=0.3, seed=17),
     # ~275 tokens per expert (256-row routed tiles): four groups end in a
-    # 3..27-row tail past a full 256-row tile, two in a 38- / 50-row one
-    "small_bf16_tall": MoEShape("small_bf16_tall", T=2200, d=512, E=8, f=384, fs=256, seed=22),
+    # 3..27-row tail past a full 256-row tile, two in a 38- / 50-row one;
+    # f == fs
+    "small_bf16_tall": MoEShape("small_bf16_tall", T=2200, d=512, E=8, f=384, fs=384, seed=22),
+    # Scout-like tiling at a narrow f: d = 5120 and ~512 tokens per expert give
+    # 256-row routed and down tiles, so the routed main tiles and the shared
+    # expert share one down launch (f == fs)
+    "wide_bf16_tall": MoEShape("wide_bf16_tall", T=4096, d=5120, E=8, f=256, fs=256, seed=23),
 }
 
 

@@ -12,7 +12,7 @@ from parity import check_forward, run_gpu, to_device, output_error
 pytestmark = pytest.mark.gpu
 
 SHAPES = ["tiny_fp32", "small_fp32", "small_bf16", "small_bf16_bias", "small_bf16_out16",
-          "decode_like_bf16", "small_fp8", "small_bf16_split", "small_bf16_tall"]
+          "decode_like_bf16", "small_fp8", "small_bf16_split", "small_bf16_tall", "wide_bf16_tall"]
 
 
 def _plan(cfg, **kw):
@@ -165,7 +165,7 @@ def test_decode_path_one_hot_and_idle_nan(gpu):
 
 
 @pytest.mark.parametrize("name,T", [("decode_like_bf16", 33), ("small_bf16_split", None),
-                                    ("small_bf16_tall", None)])
+                                    ("small_bf16_tall", None), ("wide_bf16_tall", None)])
 def test_side_stream_matches_serial_schedule(gpu, name, T):
     # Decode-sized bf16 calls run the shared expert's GEMMs, and bf16 prefill
     # calls the shared expert and the routed groups' tails, on a side stream.  Same kernels and arguments as the serial schedule
