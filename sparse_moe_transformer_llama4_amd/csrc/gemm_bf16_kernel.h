@@ -70,7 +70,7 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 
 
 template <int MODE, int BM, int WM, int WN>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int FM = BM / WM / 16;
   constexpr int FN = BN / WN / 16;
   constexpr bool GATEUP = MODE == MODE_GATEUP;
@@ -85,12 +85,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   // tiles keep 4 (5 x 32 KB, the whole LDS); 64-row tiles keep 3 per
   // workgroup with two workgroups per CU (2 x 4 x 20 KB).
   constexpr int NBUF = BM == 128 ? 6 : BM == 256 ? 5 : 4;
-  constexpr int A_INS = A_STAGE / 1024 / 4;   // 1 KB DMA instructions per wave per stage (A)
-  constexpr int B_INS = B_STAGE / 1024 / 4;   // (weights)
+  constexpr int NW = WM * WN;                 // waves per workgroup
+  constexpr int NT = 64 * NW;                 // threads per workgroup
+  constexpr int A_INS = A_STAGE / 1024 / NW;  // 1 KB DMA instructions per wave per stage (A)
+  constexpr int B_INS = B_STAGE / 1024 / NW;  // (weights)
   constexpr int LOADS = A_INS + B_INS;        // VMEM instructions per wave per stage
-  static_assert(WM * WN == 4, "4 waves");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(!GATEUP || FN % 2 == 0, "gate/up fragment pairs");
-  static_assert(A_INS >= 1 && B_INS == 4, "stage layout");
+  static_assert(A_INS >= 1 && B_INS >= 1 && A_INS * NW * 1024 == A_STAGE && B_INS * NW * 1024 == B_STAGE,
+                "stage layout");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * (A_STAGE + B_STAGE)];
   lds_u8* const As = (lds_u8*)(smem);
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
     __syncthreads();
     constexpr int CPR = BNH / 8;          // 16-byte chunks per row
     uint16_t* C = reinterpret_cast<uint16_t*>(shared ? p.C_shared : p.C);
-    for (int k = tid; k < BM * CPR; k += 256) {
+    for (int k = tid; k < BM * CPR; k += NT) {
       const int r = k / CPR, cc = k - r * CPR;
       const int col = n0 + cc * 8;
       if (m0 + r < rows && col < NH)      // NH % 8 == 0: a chunk is wholly in or out
@@ -440,7 +443,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
     static_assert(1024 + PR * FPB <= NBUF * (A_STAGE + B_STAGE), "fp32 staging fits the ring");
     constexpr int CPR = BN / 4;           // 16-byte chunks per row
     constexpr int NB = 16;                // chunks per thread per batch
-    static_assert((PR * CPR) % (256 * NB) == 0, "whole batches per pass");
+    static_assert((PR * CPR) % (NT * NB) == 0, "whole batches per pass");
 #pragma unroll
     for (int pass = 0; pass < BM / PR; ++pass) {
       if (pass > 0) __syncthreads();      // the previous pass's chunks are read
@@ -457,12 +460,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
         }
       }
       __syncthreads();
-      for (int k0 = tid; k0 < PR * CPR; k0 += 256 * NB) {
+      for (int k0 = tid; k0 < PR * CPR; k0 += NT * NB) {
         f32x4 y[NB];
         int orow[NB];
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-          const int k = k0 + u * 256;
+          const int k = k0 + u * NT;
           const int r = k / CPR, cc = k - r * CPR;
           const int rt = pass * PR + r;
           if constexpr (MODE == MODE_DOWN_ROUTED) orow[u] = reinterpret_cast<const lds_i32*>(As)[rt];
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-          const int k = k0 + u * 256;
+          const int k = k0 + u * NT;
           const int r = k / CPR, cc = k - r * CPR;
           const int rt = pass * PR + r;
           if (m0 + rt >= rows || n0 + cc * 4 >= NH) continue;
@@ -524,7 +527,8 @@ hipError_t launch_v2(const GemmArgs& a0, int T, hipStream_t s, const int32_t* ti
   a.n_tiles = gn;
   // 1-D grid: enough ids for the largest per-XCD share of (M-tile bound x N-tiles)
   const int64_t nblk = gn >= 8 ? 8 * static_cast<int64_t>(gm) * ((gn + 7) / 8) : static_cast<int64_t>(gm) * gn;
-  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, BM, WM, WN>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, BM, WM, WN>), dim3(static_cast<unsigned>(nblk)), dim3(64 * WM * WN), 0, s,
+                     a);
   return hipGetLastError();
 }
 
