@@ -22,12 +22,14 @@
  *     space is the caller's workspace, sized by moe_workspace_size.
  *   - All work is enqueued asynchronously on `stream` (hipStream_t; NULL =
  *     the default stream).  No host synchronisation, no device-to-host copy.
- *     Decode-sized bf16 forward calls (T <= 64) also use a side stream that
- *     the plan creates for the current device on first use (non-blocking,
- *     default priority): it waits for `stream` before its first kernel and
- *     `stream` waits for it before the call's last kernel, so for the caller
- *     the whole call is still ordered in `stream`.  If `stream` belongs to
- *     another device than the current one, the call runs on `stream` alone.
+ *     moe_forward also uses a side stream for decode-sized bf16 calls
+ *     (T <= 64) and for bf16 prefill-sized calls (T >= 256).  The plan
+ *     creates it for the current device on first use (non-blocking, default
+ *     priority): it waits for `stream` before its first kernel and `stream`
+ *     waits for it before the call's last kernel, so for the caller the whole
+ *     call is still ordered in `stream` (and it can be captured into a HIP
+ *     graph from `stream`).  If `stream` belongs to another device than the
+ *     current one, the call runs on `stream` alone.
  *   - Arguments, shapes, alignment and workspace size are checked on the
  *     host BEFORE anything is enqueued; a failed check enqueues nothing.
  *   - Row-major layouts throughout.  Pointers must be 16-byte aligned.
