@@ -79,12 +79,23 @@ typedef enum moe_dtype {
  *   BF16 / BF16 / BF16   as above with the output rounded to bf16
  *   BF16 / E4M3 / BF16   router in bf16; x and h quantised to e4m3 per token;
  *                        e4m3 weights with one fp32 scale per output column
+ *
+ * n_experts == 0 configures a dense layer (llm-architectures-explained
+ * "Llama 4 Maverick", table "Every architecture field": the layers between
+ * the MoE layers have a plain gated MLP of width d_ff = 16384): out =
+ * SwiGLU_s(x) with the shared weights and f_shared = d_ff, no router, no
+ * routed experts.  It takes BF16 / BF16 / {F32, BF16}, f == 0, no router
+ * bias, d and f_shared multiples of 128, and max_tokens * max(d, f_shared)
+ * * 2 < 2^31; anything else is MOE_ERR_UNSUPPORTED (MOE_ERR_SHAPE for
+ * max_tokens).  The router and routed-expert pointers may then be NULL,
+ * moe_route returns MOE_ERR_UNSUPPORTED and moe_forward's routing_out must
+ * be NULL (MOE_ERR_INVALID_ARGUMENT otherwise).
  */
 typedef struct moe_config {
   int32_t abi_version;     /* MOE_ABI_VERSION */
   int32_t d;               /* model width, multiple of 64 (128 for E4M3 weights) */
-  int32_t n_experts;       /* E, 1..256 */
-  int32_t f;               /* routed expert width, multiple of 64 (128 for E4M3) */
+  int32_t n_experts;       /* E, 1..256; 0 = a dense layer (see below) */
+  int32_t f;               /* routed expert width, multiple of 64 (128 for E4M3); 0 when E == 0 */
   int32_t f_shared;        /* shared expert width, multiple of 64 (128 for E4M3) */
   int32_t top_k;           /* must be 1 */
   int32_t x_dtype;         /* moe_dtype of x and W_router */

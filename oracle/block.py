@@ -225,6 +225,17 @@ def combine(x, idx: np.ndarray, gate: np.ndarray, w: Weights, f: int, fs: int,
     return out
 
 
+def dense(x, w: Weights, fs: int, mode: str) -> np.ndarray:
+    """A dense layer (llm-architectures-explained "Llama 4 Maverick", table
+    "Every architecture field": the non-MoE layers' FFN is a gated MLP of
+    width d_ff, 16384): out = SwiGLU(x) with the shared weights and width fs,
+    no router and no gate.  The same computation as combine() with no routed
+    token."""
+    xin, _ = expert_input(x, mode)
+    wsgu, ssgu, wsd, ssd = w.shared()
+    return swiglu_mlp(xin, weight_f64(wsgu, ssgu), weight_f64(wsd, ssd), fs, mode)
+
+
 def forward(x, w: Weights, f: int, fs: int, mode: str):
     """Whole block: returns (out float64 [T, d], Routing)."""
     wr, b = w.router()

@@ -79,9 +79,12 @@ hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* s
 hipError_t launch_quant_h(const float* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
                           float* sh, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
-// out = r + y element by element (n fp32 values, n % 4 == 0), stored as bf16
-// when out_bf16: the combine of the two down GEMMs when they run unordered.
-hipError_t launch_combine(const float* r, const float* y, void* out, int64_t n, int out_bf16, hipStream_t s);
+// out = r + y[0] + y[1] + ... + y[parts-1] element by element, in that order
+// (n fp32 values per array, n % 4 == 0; r may be null), stored as bf16 when
+// out_bf16: the combine of the two down GEMMs when they run unordered, and the
+// sum of a dense layer's K-split partials.
+hipError_t launch_combine(const float* r, const float* y, int parts, void* out, int64_t n, int out_bf16,
+                          hipStream_t s);
 
 // Grouped GEMM launch.  `grid_m` is an upper bound of M tiles; surplus
 // workgroups exit after reading the tile table.

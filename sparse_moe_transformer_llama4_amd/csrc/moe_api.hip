@@ -121,7 +121,7 @@ moe_status check_common(moe_plan_t plan, const void* x, int64_t T, const moe_wei
   const moe_config& c = plan->cfg;
   if (T < 0 || T > c.max_tokens) return MOE_ERR_SHAPE;
   if (T > 0 && (!x || !aligned16(x))) return MOE_ERR_INVALID_ARGUMENT;
-  if (!w->w_router || !aligned16(w->w_router)) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.n_experts > 0 && (!w->w_router || !aligned16(w->w_router))) return MOE_ERR_INVALID_ARGUMENT;
   if (c.has_router_bias && (!w->router_bias || !aligned16(w->router_bias))) return MOE_ERR_INVALID_ARGUMENT;
   if (layout_for(c, T).total > ws_bytes) return MOE_ERR_WORKSPACE;
   if (T > 0 && (!ws || !aligned16(ws))) return MOE_ERR_INVALID_ARGUMENT;
@@ -129,9 +129,9 @@ moe_status check_common(moe_plan_t plan, const void* x, int64_t T, const moe_wei
 }
 
 moe_status check_expert_weights(const moe_config& c, const moe_weights* w) {
-  const void* req[] = {w->w_gate_up, w->w_down, w->ws_gate_up, w->ws_down};
-  for (const void* p : req)
-    if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  const void* req[] = {w->ws_gate_up, w->ws_down, w->w_gate_up, w->w_down};
+  for (int i = 0; i < (c.n_experts > 0 ? 4 : 2); ++i)    // a dense layer has no routed experts
+    if (!req[i] || !aligned16(req[i])) return MOE_ERR_INVALID_ARGUMENT;
   if (c.w_dtype == MOE_E4M3) {
     const void* sc[] = {w->s_gate_up, w->s_down, w->ss_gate_up, w->ss_down};
     for (const void* p : sc)
@@ -429,7 +429,7 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
     if ((e = hipStreamWaitEvent(stream, aux->shared, 0)) != hipSuccess) return e;
     if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3m, T, stream, tiles_main)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(stream, aux->join, 0)) != hipSuccess) return e;
-    return launch_combine(reinterpret_cast<const float*>(ws + L.r_out), reinterpret_cast<const float*>(ws + L.y_s),
+    return launch_combine(reinterpret_cast<const float*>(ws + L.r_out), reinterpret_cast<const float*>(ws + L.y_s), 1,
                           out, static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream);
   }
 
@@ -445,6 +445,43 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
   if ((e = mark(3)) != hipSuccess) return e;
   if (tails && (e = launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3, bm_d, stream, R.tiles)) != hipSuccess) return e;
   if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3, T, stream, tiles_main)) != hipSuccess) return e;
+  return mark(4);
+}
+
+// A dense layer (n_experts == 0; llm-architectures-explained "Llama 4
+// Maverick", table "Every architecture field": every other layer's FFN is a
+// gated MLP of width d_ff = 16384): out = SwiGLU_s(x), the shared group
+// alone, with no routing.  Up to 64 tokens on the weight-streaming tiles
+// (the down GEMM split over K, its partials summed in order), else on the
+// prefill tiles; both address the shared group without tile tables.
+hipError_t enqueue_dense(const moe_config& c, const void* x, int T, const moe_weights* w, void* out, uint8_t* ws,
+                         const WsLayout& L, const Route& R, hipStream_t stream, hipEvent_t* ev) {
+  hipError_t e;
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  if ((e = mark(0)) != hipSuccess || (e = mark(1)) != hipSuccess) return e;   // no routing stage
+  if (T == 0) {
+    for (int i = 2; i <= MOE_NUM_STAGES; ++i)
+      if ((e = mark(i)) != hipSuccess) return e;
+    return hipSuccess;
+  }
+  const bool small = T <= kDecodeTokensMax;
+  GemmArgs g1 = gateup_args(c, w, ws, L, R, x, nullptr, nullptr, nullptr, T);
+  g1.group_lo = 0;   // == E: the shared group alone
+  g1.group_hi = 1;
+  e = small ? launch_gemm_decode(MODE_GATEUP, true, g1, T, stream, R.tiles)
+            : launch_gemm_bf16_v2(MODE_GATEUP, 256, g1, T, stream, R.tiles);
+  if (e != hipSuccess || (e = mark(2)) != hipSuccess) return e;
+  const int parts = small ? decode_y_parts(c, T) : 1;
+  GemmArgs g2 = down_shared_args(c, w, ws, L, R, ws + L.h_s, nullptr, T, parts);
+  const bool direct = !small && c.out_dtype == MOE_F32;   // fp32 output straight from the GEMM
+  if (direct) g2.C_shared = out;
+  e = small ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, T, stream, R.tiles)
+            : launch_gemm_bf16_v2(MODE_DOWN_SHARED, down_tile_rows(T, 1, c.d, 256), g2, T, stream, R.tiles);
+  if (e != hipSuccess || (e = mark(3)) != hipSuccess) return e;
+  if (!direct &&
+      (e = launch_combine(nullptr, reinterpret_cast<const float*>(ws + L.y_s), parts, out,
+                          static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream)) != hipSuccess)
+    return e;
   return mark(4);
 }
 
@@ -472,13 +509,21 @@ moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
   if (!cfg || cfg->abi_version != MOE_ABI_VERSION) return MOE_ERR_INVALID_ARGUMENT;
   const moe_config& c = *cfg;
   if (c.top_k != 1) return MOE_ERR_UNSUPPORTED;
-  if (c.n_experts < 1 || c.n_experts > 256) return MOE_ERR_UNSUPPORTED;
+  if (c.n_experts < 0 || c.n_experts > 256) return MOE_ERR_UNSUPPORTED;
   if (!config_dtypes_ok(c)) return MOE_ERR_UNSUPPORTED;
-  const int km = k_multiple(c);
-  if (c.d <= 0 || c.f <= 0 || c.f_shared <= 0 || c.d % km || c.f % km || c.f_shared % km)
-    return MOE_ERR_UNSUPPORTED;
   if (c.has_router_bias != 0 && c.has_router_bias != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c.max_tokens < 1 || c.max_tokens > (int64_t{1} << 30)) return MOE_ERR_SHAPE;
+  if (c.n_experts == 0) {
+    // a dense layer: the shared gated MLP alone, bf16 weights, widths that
+    // the weight-streaming and prefill tilings both take
+    if (c.x_dtype != MOE_BF16 || c.w_dtype != MOE_BF16 || c.has_router_bias || c.f != 0) return MOE_ERR_UNSUPPORTED;
+    if (c.d <= 0 || c.f_shared <= 0 || c.d % 128 || c.f_shared % 128) return MOE_ERR_UNSUPPORTED;
+    if (c.max_tokens * std::max(c.d, c.f_shared) * 2 >= (int64_t{1} << 31)) return MOE_ERR_SHAPE;
+  } else {
+    const int km = k_multiple(c);
+    if (c.d <= 0 || c.f <= 0 || c.f_shared <= 0 || c.d % km || c.f % km || c.f_shared % km)
+      return MOE_ERR_UNSUPPORTED;
+  }
   moe_plan_s* p = new (std::nothrow) moe_plan_s;
   if (!p) return MOE_ERR_INVALID_ARGUMENT;
   p->cfg = c;
@@ -510,6 +555,7 @@ moe_status moe_route(moe_plan_t plan, const void* x, int64_t T, const moe_weight
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_common(plan, x, T, w, workspace, workspace_bytes);
   if (st != MOE_OK) return st;
+  if (plan->cfg.n_experts == 0) return MOE_ERR_UNSUPPORTED;   // a dense layer routes nothing
   if (!out) return MOE_ERR_INVALID_ARGUMENT;
   if ((st = check_routing(out)) != MOE_OK) return st;
   const WsLayout L = layout_for(plan->cfg, T);
@@ -526,12 +572,17 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   const moe_config& c = plan->cfg;
   if ((st = check_expert_weights(c, w)) != MOE_OK) return st;
   if (T > 0 && (!out || !aligned16(out))) return MOE_ERR_INVALID_ARGUMENT;
+  if (routing_out && c.n_experts == 0) return MOE_ERR_INVALID_ARGUMENT;   // a dense layer routes nothing
   if (routing_out && (st = check_routing(routing_out)) != MOE_OK) return st;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const WsLayout L = layout_for(c, T);
   const Route R = route_ptrs(ws, L, routing_out);
   const int Ti = static_cast<int>(T);
+  if (c.n_experts == 0) {
+    const hipError_t e = enqueue_dense(c, x, Ti, w, out, ws, L, R, stream, ev);
+    return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
+  }
   const bool dec = use_decode(c, T);
   const bool fp8 = c.w_dtype == MOE_E4M3;
   // the prefill kernels address activations with 32-bit byte offsets

@@ -191,6 +191,8 @@ def _check_inputs(plan: Plan, x: torch.Tensor, w: dict):
     _check_tensor(x, "x", _TORCH_DT[_DT[plan.x_dtype]])
     if x.dim() != 2 or x.shape[1] != plan.d:
         raise ValueError(f"x must be [T, {plan.d}]")
+    if plan.E == 0:          # a dense layer: no router
+        return
     _check_tensor(w["w_router"], "w_router", _TORCH_DT[_DT[plan.x_dtype]])
     if tuple(w["w_router"].shape) != (plan.d, plan.E):
         raise ValueError("w_router shape")
@@ -218,7 +220,7 @@ def moe_forward(plan: Plan, x: torch.Tensor, w: dict, out: Optional[torch.Tensor
     _check_inputs(plan, x, w)
     T = x.shape[0]
     wdt = _TORCH_DT[_DT[plan.w_dtype]]
-    for k in ("w_gate_up", "w_down", "ws_gate_up", "ws_down"):
+    for k in ("w_gate_up", "w_down", "ws_gate_up", "ws_down") if plan.E > 0 else ("ws_gate_up", "ws_down"):
         _check_tensor(w[k], k, wdt)
     if out is None:
         out = torch.empty((T, plan.d), dtype=_TORCH_DT[_DT[plan.out_dtype]], device=x.device)

@@ -85,6 +85,15 @@ CONFIGS = {
                                      fs=8192, w_dtype="e4m3", out_dtype="bf16", seed=4),
 }
 
+# Workloads beyond the five: Maverick's dense layers (every other layer: a
+# gated MLP of width d_ff = 16384, no experts), prefill and decode.
+EXTRA_CONFIGS = {
+    "maverick_dense_prefill_bf16": MoEShape("maverick_dense_prefill_bf16", T=8192, d=5120, E=0, f=0,
+                                            fs=16384, seed=5),
+    "maverick_dense_decode_bf16": MoEShape("maverick_dense_decode_bf16", T=32, d=5120, E=0, f=0,
+                                           fs=16384, seed=6),
+}
+
 # Smaller shapes for element-by-element parity: several tiles in every
 # dimension plus ragged tails, small enough for the fp64 oracle in seconds.
 TEST_SHAPES = {
@@ -108,6 +117,8 @@ TEST_SHAPES = {
     # 3..27-row tail past a full 256-row tile, two in a 38- / 50-row one;
     # f == fs
     "small_bf16_tall": MoEShape("small_bf16_tall", T=2200, d=512, E=8, f=384, fs=384, seed=22),
+    # a dense layer (no routed experts): the shared gated MLP alone
+    "small_dense_bf16": MoEShape("small_dense_bf16", T=300, d=512, E=0, f=0, fs=384, seed=24),
     # Scout-like tiling at a narrow f: d = 5120 and ~512 tokens per expert give
     # 256-row routed and down tiles, so the routed main tiles and the shared
     # expert share one down launch (f == fs)
@@ -118,6 +129,8 @@ TEST_SHAPES = {
 def get_config(name: str) -> MoEShape:
     if name in CONFIGS:
         return CONFIGS[name]
+    if name in EXTRA_CONFIGS:
+        return EXTRA_CONFIGS[name]
     return TEST_SHAPES[name]
 
 
@@ -294,6 +307,11 @@ def make_inputs(cfg: MoEShape, device="cpu") -> dict:
     dev = torch.device(device)
     wdt = torch.uint8 if cfg.w_dtype == "e4m3" else DTYPES[cfg.w_dtype]
     E, d, f, fs = cfg.E, cfg.d, cfg.f, cfg.fs
+    if E == 0:   # a dense layer: the shared gated MLP alone
+        wsgu, ssgu, wsd, ssd = gen_shared(cfg, dev)
+        return {"x": gen_x(cfg, dev), "w_router": None, "router_bias": None, "w_gate_up": None, "w_down": None,
+                "s_gate_up": None, "s_down": None,
+                "ws_gate_up": wsgu, "ss_gate_up": ssgu, "ws_down": wsd, "ss_down": ssd}
     out = {
         "x": gen_x(cfg, dev),
         "w_router": gen_router(cfg, dev),

@@ -61,6 +61,16 @@ def _plan(**kw):
     ({"abi_version": 2}, INVALID),
     ({"has_router_bias": 3}, INVALID),
     ({"max_tokens": 0}, SHAPE),
+    # a dense layer (no routed experts): bf16, f == 0, no bias, widths % 128
+    ({"n_experts": 0, "f": 0}, OK),
+    ({"n_experts": 0, "f": 0, "out_dtype": 1}, OK),
+    ({"n_experts": 0, "f": 0, "w_dtype": 2, "out_dtype": 1}, UNSUPPORTED),
+    ({"n_experts": 0, "f": 0, "x_dtype": 0, "w_dtype": 0, "out_dtype": 0}, UNSUPPORTED),
+    ({"n_experts": 0, "f": 0, "has_router_bias": 1}, UNSUPPORTED),
+    ({"n_experts": 0, "f": 0, "d": 320}, UNSUPPORTED),
+    ({"n_experts": 0, "f": 0, "f_shared": 192}, UNSUPPORTED),
+    ({"n_experts": 0, "f": 0, "max_tokens": 1 << 20}, OK),
+    ({"n_experts": 0, "f": 0, "max_tokens": 1 << 21}, SHAPE),
 ])
 def test_plan_validation(kw, status):
     st, h = _plan(**kw)
@@ -112,6 +122,25 @@ def test_forward_rejects_before_enqueue():
     r = moe._Routing(P, P, P, None, P)
     assert lib.moe_route(h, P, 64, ctypes.byref(w), ctypes.byref(r), P, n.value, None) == INVALID
     assert lib.moe_route(h, P, 64, ctypes.byref(w), None, P, n.value, None) == INVALID
+    lib.moe_plan_destroy(h)
+
+
+def test_dense_layer_rejects_before_enqueue():
+    """A dense plan (n_experts == 0): no routing entry point, no routing record,
+    the shared weights required, the router and routed weights not."""
+    lib = moe.load_library()
+    st, h = _plan(n_experts=0, f=0, max_tokens=64)
+    assert st == OK
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(h, 64, ctypes.byref(n)) == OK
+    P = 0x10000
+    w = moe._Weights(None, None, None, None, None, None, P, None, P, None)   # shared weights only
+    r = moe._Routing(P, P, P, P, P)
+    assert lib.moe_route(h, P, 64, ctypes.byref(w), ctypes.byref(r), P, n.value, None) == UNSUPPORTED
+    assert lib.moe_forward(h, P, 64, ctypes.byref(w), P, ctypes.byref(r), P, n.value, None) == INVALID
+    bad = moe._Weights(None, None, None, None, None, None, P, None, None, None)
+    assert lib.moe_forward(h, P, 64, ctypes.byref(bad), P, None, P, n.value, None) == INVALID
+    assert lib.moe_forward(h, P, 65, ctypes.byref(w), P, None, P, n.value, None) == SHAPE
     lib.moe_plan_destroy(h)
 
 

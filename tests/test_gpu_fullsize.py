@@ -80,3 +80,31 @@ def test_fullsize_sampled(gpu, name):
     print(f"[full] {name}: sampled max|err|/RMS = {err:.3e}", flush=True)
     assert err <= TOL[cfg.w_dtype]
     assert torch.isfinite(out_cpu.float()).all()
+
+
+@pytest.mark.parametrize("name", ["maverick_dense_decode_bf16", "maverick_dense_prefill_bf16"])
+def test_fullsize_dense_sampled(gpu, name):
+    # Maverick's dense layers (gated MLP of width 16384, no experts) at full
+    # size; the oracle computes sampled tokens one by one
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = synth.get_config(name)
+    print(f"[full] {name}: generating on GPU", flush=True)
+    g = synth.make_inputs(cfg, gpu)
+    plan = moe.Plan.for_shape(cfg)
+    ws = torch.full((moe.moe_workspace_size(plan, cfg.T),), 0xFF, dtype=torch.uint8, device=gpu)
+    out = moe.moe_forward(plan, g["x"], g, workspace=ws)
+    torch.cuda.synchronize()
+    out_cpu = out.cpu()
+    del g, ws, out
+    gc.collect()
+    torch.cuda.empty_cache()
+    toks = np.array(sorted({0, 1, cfg.T // 2, cfg.T - 1}))
+    print(f"[full] {name}: oracle output on tokens {toks.tolist()}", flush=True)
+    x = synth.gen_x(cfg, "cpu")
+    shared = synth.gen_shared(cfg, "cpu")
+    w = block.Weights(lambda: None, lambda e: None, lambda: shared)
+    ref = block.dense(x[toks], w, cfg.fs, cfg.w_dtype)
+    err = output_error(cfg, out_cpu[toks], ref)
+    print(f"[full] {name}: sampled max|err|/RMS = {err:.3e}", flush=True)
+    assert err <= TOL[cfg.w_dtype]
+    assert torch.isfinite(out_cpu.float()).all()

@@ -239,3 +239,28 @@ def test_graph_capture_replays_match_eager(gpu, name):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out_g, ref), f"replay {rep} differs from the eager call"
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 33, 64, 65, 300])
+def test_dense_layer_matches_oracle(gpu, T, out_dtype):
+    # a dense layer (n_experts == 0): the shared gated MLP alone.  T <= 64
+    # takes the weight-streaming tiles (down GEMM split over K, partials summed
+    # in order), larger T the prefill tiles
+    from parity import TOL
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = dataclasses.replace(synth.get_config("small_dense_bf16"), T=T, out_dtype=out_dtype,
+                              name=f"dense{T}_{out_dtype}")
+    print(f"[parity] dense T={T} out={out_dtype}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    p = _plan(cfg)
+    ws = torch.full((max(moe.moe_workspace_size(p, T), 256),), 0xFF, dtype=torch.uint8, device=gpu)
+    out = moe.moe_forward(p, g["x"], g, workspace=ws)
+    torch.cuda.synchronize()
+    ref = block.dense(inp["x"], block.Weights.from_dict(inp), cfg.fs, cfg.w_dtype)
+    err = output_error(cfg, out, ref)
+    print(f"[parity] dense T={T} max|err|/RMS = {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    with pytest.raises(Exception):
+        moe.moe_forward(p, g["x"], g, workspace=ws, routing=moe.new_routing(p, T, gpu))

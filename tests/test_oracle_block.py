@@ -57,6 +57,31 @@ def test_oracle_matches_brute_force(T, d, E, f, fs, mode):
     assert np.max(np.abs(out - bo)) <= 1e-12 * scale
 
 
+@pytest.mark.parametrize("T,d,fs,mode", [(0, 8, 8, "bf16"), (5, 16, 8, "bf16"), (7, 8, 16, "f32"),
+                                         (3, 16, 4, "e4m3")])
+def test_dense_matches_brute_force(T, d, fs, mode):
+    # a dense layer: the shared gated MLP alone, token by token in plain Python
+    cfg = synth.MoEShape("dense", T=T, d=d, E=0, f=0, fs=fs, x_dtype="f32" if mode == "f32" else "bf16",
+                         w_dtype=mode, out_dtype="f32", seed=T * 7 + fs, w_std=0.3)
+    inp = synth.make_inputs(cfg)
+    assert inp["w_router"] is None and inp["w_gate_up"] is None
+    w = block.Weights.from_dict(inp)
+    out = block.dense(inp["x"], w, fs, mode)
+    assert out.shape == (T, d)
+    if T == 0:
+        return
+    sh = w.shared()
+    wsgu = block.weight_f64(sh[0], sh[1]).tolist()
+    wsd = block.weight_f64(sh[2], sh[3]).tolist()
+    xin = block.expert_input(inp["x"], mode)[0].tolist() if mode == "e4m3" else block.to_f64(inp["x"]).tolist()
+    bo = np.array([brute._swiglu_mlp(xin[t], wsgu, wsd, fs, mode) for t in range(T)])
+    scale = np.sqrt(np.mean(bo * bo))
+    assert np.max(np.abs(out - bo)) <= 1e-12 * scale
+    # and it is the block with no routed token
+    ref = block.combine(inp["x"], np.zeros(0, dtype=np.int64), np.zeros(0), w, 0, fs, mode)
+    np.testing.assert_array_equal(out, ref)
+
+
 def test_brute_force_with_bias_and_ties():
     # bias makes expert 2 win for every token; equal logits must pick the lowest index
     cfg, inp = _tiny(5, 8, 4, 4, 4, "f32", seed=3, bias=[0.0, 0.0, 50.0, 50.0])
