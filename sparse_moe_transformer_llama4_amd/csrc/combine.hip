@@ -32,7 +32,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const f32x4* r, const f32x
   }
 }
 
+// SwiGLU over summed K-split partials of the gate/up GEMM (the same SiLU and
+// products as the gate/up epilogue): thread -> 4 consecutive columns.
+__global__ __launch_bounds__(256) void swiglu_parts_kernel(const float* gu, int parts, int T, int N, uint16_t* h) {
+  const int n4 = N / 4;
+  const int64_t total = static_cast<int64_t>(T) * n4;
+  const int64_t pstride = static_cast<int64_t>(T) * 2 * N;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = i / n4;
+    const int c = static_cast<int>(i - t * n4) * 4;
+    const float* g0 = gu + t * 2 * N + c;
+    f32x4 g = *reinterpret_cast<const f32x4*>(g0);
+    f32x4 u = *reinterpret_cast<const f32x4*>(g0 + N);
+    for (int q = 1; q < parts; ++q) {
+      g += *reinterpret_cast<const f32x4*>(g0 + q * pstride);
+      u += *reinterpret_cast<const f32x4*>(g0 + q * pstride + N);
+    }
+    uint16_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = f32_to_bf16(silu_f(g[j]) * u[j]);
+    *reinterpret_cast<uint2*>(h + t * N + c) =
+        make_uint2(v[0] | (static_cast<uint32_t>(v[1]) << 16), v[2] | (static_cast<uint32_t>(v[3]) << 16));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_swiglu_parts(const float* gu, int parts, int T, int N, uint16_t* h, hipStream_t s) {
+  if (N % 4 != 0 || parts < 1) return hipErrorInvalidValue;
+  const int64_t total = static_cast<int64_t>(T) * (N / 4);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(swiglu_parts_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, gu, parts, T, N, h);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const float* r, const float* y, int parts, void* out, int64_t n, int out_bf16,
                           hipStream_t s) {

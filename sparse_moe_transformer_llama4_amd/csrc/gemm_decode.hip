@@ -158,8 +158,10 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_gateup_kernel(GemmArgs p) 
   if (tid < DBM && !shared) row_scale = p.gate[p.perm[row_base + min(m0 + tid, rows - 1)]];
 
   // ---- this wave's quarter of K
-  const int kq = K >> 2;                       // multiple of GBK
-  const int k0 = wave * kq;
+  // K split over gridDim.z (launches that write pre-activation partials)
+  const int kz = K / static_cast<int>(gridDim.z);
+  const int kq = kz >> 2;                      // multiple of GBK
+  const int k0 = static_cast<int>(blockIdx.z) * kz + wave * kq;
   const int ns = kq / GBK;
 
   // weights: DMA instruction i fills K rows 2i, 2i+1 of the stage; lane ->
@@ -272,6 +274,21 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_gateup_kernel(GemmArgs p) 
     constexpr int WS = DBM * GPP / 4;            // one wave's buffer in quads
     tq[it] = ((p0[0] + p0[WS]) + p0[2 * WS]) + p0[3 * WS];
   }
+  if (p.gu_part) {
+    // pre-activation partial of this K part: [z][row][2 NH] fp32, gate
+    // columns at n0.., up columns at NH + n0.. (the SwiGLU runs after the
+    // parts are summed)
+    float* dst = p.gu_part + static_cast<int64_t>(blockIdx.z) * p.T * (2 * NH);
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + 256 * it;
+      const int r = e / C4, c = (e % C4) * 4;
+      const int gcol = c < GBNH ? n0 + c : NH + n0 + (c - GBNH);
+      if (r < nvalid && n0 + (c % GBNH) < NH)
+        *reinterpret_cast<f32x4*>(dst + static_cast<int64_t>(row_base + m0 + r) * (2 * NH) + gcol) = tq[it];
+    }
+    return;
+  }
   __syncthreads();
 #pragma unroll
   for (int it = 0; it < NQ; ++it) {
@@ -355,11 +372,16 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
 
   // ---- this block's K range (split over blockIdx.z for the shared down
   // GEMM, whose single M-tile would otherwise leave most CUs idle) and this
-  // wave's quarter of it
+  // wave's quarter of it.  K is cut into 128-row units, part z taking units
+  // [z U / nsplit, (z+1) U / nsplit): parts differ by one unit at most when
+  // nsplit does not divide U
   const int nsplit = gridDim.z;
-  const int kq = (K / nsplit) >> 2;             // multiple of 32
-  const int k0 = static_cast<int>(blockIdx.z) * (K / nsplit) + wave * kq;
-  const int ns = kq / DBK;
+  const int units = K >> 7;
+  const int u0 = static_cast<int>(blockIdx.z) * units / nsplit;
+  const int u1 = (static_cast<int>(blockIdx.z) + 1) * units / nsplit;
+  const int ns = u1 - u0;                       // DBK-row stages per wave
+  const int kq = ns * DBK;
+  const int k0 = u0 * 128 + wave * kq;
 
   // weights: DMA instruction i fills K rows 4i .. 4i+3 of the stage; lane ->
   // row 4i + lane/16, physical chunk lane%16 holds logical chunk c
@@ -518,7 +540,7 @@ hipError_t launch_dec(const GemmArgs& a0, int T, hipStream_t s, const int32_t* t
   if (gm <= 0) return hipSuccess;
   const int gn = (a.N + DBN - 1) / DBN;
   const int ks = (MODE == MODE_DOWN_SHARED && a.ksplit > 1) ? a.ksplit : 1;
-  if (a.K % (128 * ks) != 0) return hipErrorInvalidValue;
+  if (a.K % 128 != 0 || a.K / 128 < ks) return hipErrorInvalidValue;   // >= one 128-row unit per part
   hipLaunchKernelGGL((gemm_decode_kernel<MODE, FMMAX>), dim3(gm, gn, ks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -535,8 +557,12 @@ hipError_t launch_dec_gateup(const GemmArgs& a0, int T, hipStream_t s, const int
   const int nmax = std::max(has_routed ? a.N : 0, has_shared ? a.N_shared : 0);
   const int gn = (nmax + GBNH - 1) / GBNH;
   if (gm <= 0 || gn <= 0) return hipSuccess;
-  if (a.K % (4 * GBK) != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_decode_gateup_kernel<FMMAX>), dim3(gm, gn), dim3(256), 0, s, a);
+  // partial mode (gu_part): K split over ksplit workgroups, no SwiGLU (and
+  // no gate scale) here: the shared group alone
+  if (a.gu_part && has_routed) return hipErrorInvalidValue;
+  const int ks = (a.gu_part && a.ksplit > 1) ? a.ksplit : 1;
+  if (a.K % (4 * GBK * ks) != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_decode_gateup_kernel<FMMAX>), dim3(gm, gn, ks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -55,9 +55,13 @@ struct GemmArgs {
   int out_bf16;          // DOWN_ROUTED: output dtype bf16 (else fp32)
   int group_lo, group_hi;  // groups [lo, hi) handled by this launch (group E = shared expert)
   int n_tiles;             // N-tiles per M-tile of this launch (set by the launcher)
-  int ksplit;              // decode DOWN_SHARED: K split over blocks; partial s at C_shared + s*T*N (0 = 1)
+  int ksplit;              // decode DOWN_SHARED (and GATEUP with gu_part): K split over blocks; partial s at
+                           // C_shared + s*T*N (0 = 1).  DOWN_SHARED: parts take K/128-row units in turn, not
+                           // necessarily equal counts (ksplit <= K/128); GATEUP: ksplit must divide K/64
   int y_parts;             // decode DOWN_ROUTED: Y holds this many partials, summed in order (0 = 1)
   int tail_bm;             // weight-streaming tail launches: rows of the groups' full main tiles (0 = none)
+  float* gu_part;          // weight-streaming GATEUP: write fp32 pre-activation partials [ksplit][T][2 N] here
+                           // instead of h (K split over ksplit workgroups; null = normal epilogue)
 };
 
 // Router in two launches: partial logits over K slices of d (the slice count
@@ -85,6 +89,9 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 // sum of a dense layer's K-split partials.
 hipError_t launch_combine(const float* r, const float* y, int parts, void* out, int64_t n, int out_bf16,
                           hipStream_t s);
+// h[t][c] = bf16(SiLU(g) * u), g = sum over the parts of gu[q][t][c], u of
+// gu[q][t][N + c], in order (parts of a K-split gate/up GEMM; N % 4 == 0).
+hipError_t launch_swiglu_parts(const float* gu, int parts, int T, int N, uint16_t* h, hipStream_t s);
 
 // Grouped GEMM launch.  `grid_m` is an upper bound of M tiles; surplus
 // workgroups exit after reading the tile table.

@@ -71,6 +71,27 @@ bool use_decode(const moe_config& c, int64_t T) {
          decode_supported(c.f) && decode_supported(c.f_shared);
 }
 
+// A dense layer's gate/up GEMM at decode sizes has one row tile per 128
+// output columns, too few workgroups for the GPU: its K is split into this
+// many parts (at most 4, until there are >= 256 workgroups), whose fp32
+// pre-activation partials are summed before the SwiGLU.  1 otherwise.
+int dense_gateup_parts(const moe_config& c, int64_t T) {
+  if (c.n_experts != 0 || T < 1 || T > kDecodeTokensMax) return 1;
+  const int64_t wg = ((T + 31) / 32) * (c.f_shared / 128);
+  int ks = 1;
+  while (ks < 4 && wg * ks < 256 && c.d % (128 * ks) == 0) ks *= 2;
+  return ks;
+}
+
+// The same layer's down GEMM (the shared group alone, d / 128 column tiles
+// per 32-row tile): K parts for about one workgroup per CU, 1..8.
+int dense_down_parts(const moe_config& c, int64_t T) {
+  if (c.n_experts != 0 || T < 1 || T > kDecodeTokensMax) return 1;
+  const int64_t wg = ((T + 31) / 32) * ((c.d + 127) / 128);
+  const int64_t ks = std::min<int64_t>({8, std::max<int64_t>(1, 256 / wg), c.f_shared / 128});
+  return static_cast<int>(ks);
+}
+
 WsLayout layout_for(const moe_config& c, int64_t T) {
   WsLayout L{};
   size_t off = 0;
@@ -94,8 +115,10 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   L.tiles = take(kNumTables * (E + 2) * 4);
   L.h_r = take(t * c.f * hsz);
   L.h_s = take(t * c.f_shared * hsz);
-  L.y_s = take(t * c.d * 4 * static_cast<size_t>(decode_y_parts(c, T)));
+  L.y_s = take(t * c.d * 4 * static_cast<size_t>(std::max(decode_y_parts(c, T), dense_down_parts(c, T))));
   if (c.w_dtype == MOE_BF16 && T >= kPrefillTokens) L.r_out = take(t * c.d * 4);
+  if (dense_gateup_parts(c, T) > 1)
+    L.gu_part = take(static_cast<size_t>(dense_gateup_parts(c, T)) * t * 2 * c.f_shared * 4);
   if (fp8) {
     L.hq_r = take(t * c.f);
     L.hq_s = take(t * c.f_shared);
@@ -452,7 +475,7 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
 // Maverick", table "Every architecture field": every other layer's FFN is a
 // gated MLP of width d_ff = 16384): out = SwiGLU_s(x), the shared group
 // alone, with no routing.  Up to 64 tokens on the weight-streaming tiles
-// (the down GEMM split over K, its partials summed in order), else on the
+// (both GEMMs split over K, their partials summed in order), else on the
 // prefill tiles; both address the shared group without tile tables.
 hipError_t enqueue_dense(const moe_config& c, const void* x, int T, const moe_weights* w, void* out, uint8_t* ws,
                          const WsLayout& L, const Route& R, hipStream_t stream, hipEvent_t* ev) {
@@ -468,10 +491,18 @@ hipError_t enqueue_dense(const moe_config& c, const void* x, int T, const moe_we
   GemmArgs g1 = gateup_args(c, w, ws, L, R, x, nullptr, nullptr, nullptr, T);
   g1.group_lo = 0;   // == E: the shared group alone
   g1.group_hi = 1;
+  const int gp = dense_gateup_parts(c, T);
+  if (gp > 1) {      // K-split gate/up partials, then the SwiGLU over their sum
+    g1.gu_part = reinterpret_cast<float*>(ws + L.gu_part);
+    g1.ksplit = gp;
+  }
   e = small ? launch_gemm_decode(MODE_GATEUP, true, g1, T, stream, R.tiles)
             : launch_gemm_bf16_v2(MODE_GATEUP, 256, g1, T, stream, R.tiles);
+  if (e == hipSuccess && gp > 1)
+    e = launch_swiglu_parts(reinterpret_cast<const float*>(ws + L.gu_part), gp, T, c.f_shared,
+                            reinterpret_cast<uint16_t*>(ws + L.h_s), stream);
   if (e != hipSuccess || (e = mark(2)) != hipSuccess) return e;
-  const int parts = small ? decode_y_parts(c, T) : 1;
+  const int parts = small ? dense_down_parts(c, T) : 1;
   GemmArgs g2 = down_shared_args(c, w, ws, L, R, ws + L.h_s, nullptr, T, parts);
   const bool direct = !small && c.out_dtype == MOE_F32;   // fp32 output straight from the GEMM
   if (direct) g2.C_shared = out;

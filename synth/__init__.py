@@ -119,6 +119,9 @@ TEST_SHAPES = {
     "small_bf16_tall": MoEShape("small_bf16_tall", T=2200, d=512, E=8, f=384, fs=384, seed=22),
     # a dense layer (no routed experts): the shared gated MLP alone
     "small_dense_bf16": MoEShape("small_dense_bf16", T=300, d=512, E=0, f=0, fs=384, seed=24),
+    # a wider dense layer at decode sizes: d / 128 = 16 column tiles, so both
+    # GEMMs split K (the down GEMM into 8 parts over 10 units of 128 rows)
+    "wide_dense_bf16": MoEShape("wide_dense_bf16", T=40, d=2048, E=0, f=0, fs=1280, seed=25),
     # Scout-like tiling at a narrow f: d = 5120 and ~512 tokens per expert give
     # 256-row routed and down tiles, so the routed main tiles and the shared
     # expert share one down launch (f == fs)

@@ -242,16 +242,19 @@ def test_graph_capture_replays_match_eager(gpu, name):
 
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("T", [1, 33, 64, 65, 300])
-def test_dense_layer_matches_oracle(gpu, T, out_dtype):
+@pytest.mark.parametrize("shape,T", [("small_dense_bf16", 1), ("small_dense_bf16", 33), ("small_dense_bf16", 64),
+                                     ("small_dense_bf16", 65), ("small_dense_bf16", 300), ("wide_dense_bf16", 5),
+                                     ("wide_dense_bf16", 40)])
+def test_dense_layer_matches_oracle(gpu, shape, T, out_dtype):
     # a dense layer (n_experts == 0): the shared gated MLP alone.  T <= 64
-    # takes the weight-streaming tiles (down GEMM split over K, partials summed
-    # in order), larger T the prefill tiles
+    # takes the weight-streaming tiles (both GEMMs split over K, partials
+    # summed in order; the wide shape's down GEMM in unequal parts), larger T
+    # the prefill tiles
     from parity import TOL
     from sparse_moe_transformer_llama4_amd import moe
-    cfg = dataclasses.replace(synth.get_config("small_dense_bf16"), T=T, out_dtype=out_dtype,
-                              name=f"dense{T}_{out_dtype}")
-    print(f"[parity] dense T={T} out={out_dtype}", flush=True)
+    cfg = dataclasses.replace(synth.get_config(shape), T=T, out_dtype=out_dtype,
+                              name=f"{shape}{T}_{out_dtype}")
+    print(f"[parity] dense {shape} T={T} out={out_dtype}", flush=True)
     inp = synth.make_inputs(cfg)
     g = to_device(inp, gpu)
     p = _plan(cfg)
