@@ -49,8 +49,13 @@ def stage_work(cfg, counts):
     touched = sum(1 for c in counts if c > 0)
     sc = 4 if cfg.w_dtype == "e4m3" else 0     # fp32 column scales per weight column
     xin = 1 if cfg.w_dtype == "e4m3" else xb   # gate/up reads the e4m3 copy of x
+    # RMSNorm in front of the block: x read, the normalised rows written (and
+    # their e4m3 codes + scales for e4m3 weights), the gain read
+    norm = 0
+    if cfg.norm_eps is not None:
+        norm = 2 * T * d * xb + d * xb + ((T * d + 4 * T) if cfg.w_dtype == "e4m3" else 0)
     return {
-        "route": (2 * T * d * E, T * d * xb + d * E * xb + (4 * E if cfg.has_bias else 0) + T * 8),
+        "route": (2 * T * d * E, T * d * xb + d * E * xb + (4 * E if cfg.has_bias else 0) + T * 8 + norm),
         "gate_up": (4 * T * d * (f + fs),
                     touched * (d * 2 * f * wb + 2 * f * sc) + d * 2 * fs * wb + 2 * fs * sc
                     + T * d * xin + T * (f + fs) * hb),
@@ -78,6 +83,7 @@ def cpu_baseline(cfg, g, sample):
     from oracle import block
 
     xs = g["x"][:sample].cpu()
+    nw = None if g.get("norm_weight") is None else g["norm_weight"].cpu()
 
     def ex(e):
         s = g["s_gate_up"]
@@ -89,11 +95,18 @@ def cpu_baseline(cfg, g, sample):
     router = (g["w_router"].cpu(), None if g["router_bias"] is None else g["router_bias"].cpu())
     w = block.Weights(lambda: router, ex, lambda: shared)
     t0 = time.perf_counter()
-    out, r = block.forward(xs, w, cfg.f, cfg.fs, cfg.w_dtype)
+    if nw is not None:
+        xs = block.rmsnorm(xs, nw, float(np.float32(cfg.norm_eps)), cfg.x_dtype)
+    if cfg.E == 0:
+        out = block.dense(xs, w, cfg.fs, cfg.w_dtype)
+        what = "dense gated MLP"
+    else:
+        out, r = block.forward(xs, w, cfg.f, cfg.fs, cfg.w_dtype)
+        what = (f"routing + every touched expert + shared), {int(np.count_nonzero(r.counts))} experts touched")
     dt = time.perf_counter() - t0
+    norm = "RMSNorm + " if nw is not None else ""
     return {"value": sample / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"first {sample} of {cfg.T} tokens, full fp64 block (routing + every touched expert "
-                      f"+ shared), {int(np.count_nonzero(r.counts))} experts touched, {dt:.1f} s"}
+            "sample": f"first {sample} of {cfg.T} tokens, full fp64 block ({norm}{what}, {dt:.1f} s"}
 
 
 def main():
@@ -136,7 +149,7 @@ def main():
     plan = moe.Plan.for_shape(cfg)
     ws = torch.empty(max(moe.moe_workspace_size(plan, cfg.T), 256), dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.T, cfg.d), dtype=moe._TORCH_DT[moe._DT[cfg.out_dtype]], device=dev)
-    routing = moe.new_routing(plan, cfg.T, dev)
+    routing = moe.new_routing(plan, cfg.T, dev) if cfg.E > 0 else None   # a dense layer routes nothing
     events = [moe.StageEvents() for _ in range(args.steps)]
     warm_ev = moe.StageEvents()
 
@@ -145,7 +158,7 @@ def main():
         moe.moe_forward(plan, g["x"], g, out=out, routing=routing, workspace=ws)
         moe.moe_forward_timed(plan, g["x"], g, warm_ev, out, ws, routing)
     torch.cuda.synchronize()
-    counts = routing["counts"].cpu().tolist()
+    counts = routing["counts"].cpu().tolist() if routing is not None else []
 
     # timed region 1: the library call itself (tokens/s)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
@@ -223,7 +236,8 @@ def main():
         "data": "synthetic (seeded counter-based generator, random-init weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "f": cfg.f, "f_shared": cfg.fs,
                    "x_dtype": cfg.x_dtype, "w_dtype": cfg.w_dtype, "out_dtype": cfg.out_dtype,
-                   "routing": cfg.bias, "experts_touched": sum(1 for c in counts if c > 0)},
+                   "routing": cfg.bias, "experts_touched": sum(1 for c in counts if c > 0),
+                   "rmsnorm_eps": cfg.norm_eps},
         "block_tflops": F / t / 1e12,
         "block_gbps": B / t / 1e9,
         "mfma_frac": F / t / peak_f,

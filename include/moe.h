@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -90,6 +90,14 @@ typedef enum moe_dtype {
  * max_tokens).  The router and routed-expert pointers may then be NULL,
  * moe_route returns MOE_ERR_UNSUPPORTED and moe_forward's routing_out must
  * be NULL (MOE_ERR_INVALID_ARGUMENT otherwise).
+ *
+ * has_norm == 1 puts the RMSNorm that precedes the feed-forward block
+ * (llm-architectures-explained "Llama 4 Maverick", table "Every
+ * architecture field": RMSNorm before the MLP; KerasFormers "Llama 4",
+ * Llama4Model argument norm_eps) in front of every entry point that reads x:
+ *   xn[t, j] = x[t, j] / sqrt(mean_j x[t, j]^2 + norm_eps) * norm_weight[j],
+ * computed in fp32 and rounded to x_dtype; routing and both experts then
+ * read xn in place of x (x itself is not modified).  Any config may have it.
  */
 typedef struct moe_config {
   int32_t abi_version;     /* MOE_ABI_VERSION */
@@ -103,6 +111,8 @@ typedef struct moe_config {
   int32_t out_dtype;       /* moe_dtype of out */
   int32_t has_router_bias; /* 0 / 1 */
   int64_t max_tokens;      /* largest T accepted by this plan (>= 1) */
+  int32_t has_norm;        /* 0 / 1: the block starts with the RMSNorm below */
+  float norm_eps;          /* RMSNorm epsilon (1e-5 in Llama 4), finite and >= 0; read when has_norm */
 } moe_config;
 
 typedef struct moe_plan_s* moe_plan_t;
@@ -124,6 +134,7 @@ typedef struct moe_weights {
   const float* ss_gate_up;  /* [2 f_shared] */
   const void* ws_down;      /* [f_shared, d] */
   const float* ss_down;     /* [d] */
+  const void* norm_weight;  /* [d] x_dtype RMSNorm gain, or NULL when has_norm == 0 */
 } moe_weights;
 
 /*
@@ -177,7 +188,8 @@ moe_status moe_forward(moe_plan_t plan, const void* x, int64_t T, const moe_weig
 /*
  * moe_forward with stage timing: records events[0..MOE_NUM_STAGES] on
  * `stream` at the stage boundaries
- *   [0] routing (router GEMM, top-1, gate, scan, permutation; e4m3: x quantisation)
+ *   [0] routing (RMSNorm if configured, router GEMM, top-1, gate, scan, permutation;
+ *       e4m3: x quantisation)
  *   [1] grouped gate/up GEMM with the SwiGLU epilogue (routed groups + shared)
  *   [2] shared-expert down GEMM (e4m3: preceded by h quantisation)
  *   [3] routed down GEMM with un-permute + combine
@@ -197,7 +209,7 @@ const char* moe_status_string(moe_status s);
 /* hipError_t value behind the last MOE_ERR_HIP returned for this plan (0 if none). */
 int moe_last_hip_error(moe_plan_t plan);
 
-/* Library identity, e.g. "moe355 1 gfx950". */
+/* Library identity, e.g. "moe355 2 gfx950". */
 const char* moe_version(void);
 
 #ifdef __cplusplus

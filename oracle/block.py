@@ -30,6 +30,15 @@ Steps, in the order the pages give them:
 6. Combine: out = shared(x) + routed (superteams.ai routing sketch; the
    other experts contribute nothing).
 
+Optional step 0, the RMSNorm in front of the block (llm-architectures-explained
+"Llama 4 Maverick", table "Every architecture field": RMSNorm before the MLP;
+KerasFormers "Llama 4", Llama4Model arguments: norm_eps 1e-5): each row is
+divided by the root of its mean square plus eps and multiplied by the gain,
+xn = x / sqrt(mean(x^2) + eps) * w, exactly in float64 and rounded once
+(RNE) to the dtype of x; steps 1-6 then take xn in place of x.  The pages
+name the norm and its eps, not its formula: this is the standard RMSNorm
+(root-mean-square layer normalisation with a learned per-feature gain).
+
 Rounding points of the reduced-precision variants (the pages fix none; they
 follow the data types of the workloads):
   R1 (bf16 weights): the SwiGLU output h is rounded to bf16 (RNE, from its
@@ -52,7 +61,7 @@ from typing import Callable, Optional
 import numpy as np
 import torch
 
-from .numerics import bf16_round, e4m3_round, e4m3_decode
+from .numerics import bf16_round, e4m3_round, e4m3_decode, round_f64_to
 
 NEAR_TIE = 1e-3   # top-2 logit margin below which either choice is accepted
 
@@ -91,6 +100,16 @@ class Routing:
     offsets: np.ndarray  # [E + 1] int64
     perm: np.ndarray     # [T] int64, tokens grouped by expert, ascending within a group
     inv: np.ndarray      # [T] int64, inverse of perm
+
+
+def rmsnorm(x, w, eps: float, dtype: str) -> np.ndarray:
+    """Step 0: xn[t, j] = x[t, j] / sqrt(mean_j x[t, j]^2 + eps) * w[j] in
+    float64, rounded once to `dtype` ("bf16" / "f32"); float64 values out."""
+    x64 = to_f64(x)
+    w64 = to_f64(w)
+    ms = np.mean(x64 * x64, axis=1) if x64.shape[1] else np.zeros(x64.shape[0])
+    y = x64 / np.sqrt(ms + float(eps))[:, None] * w64[None, :]
+    return round_f64_to(y, dtype)
 
 
 def router_logits(x, wr, bias=None) -> np.ndarray:

@@ -37,6 +37,16 @@ def bf16_round(v) -> np.ndarray:
     return _round_sig(v, 8, -133)
 
 
+def round_f64_to(v, dtype: str) -> np.ndarray:
+    """Round exact float64 values ONCE to bf16 or fp32 (RNE), with no float32
+    step in between (bf16_round above takes float32 inputs); returns float64."""
+    if dtype == "bf16":
+        return _round_sig(v, 8, -133)
+    if dtype == "f32":
+        return _round_sig(v, 24, -149)
+    raise ValueError(dtype)
+
+
 def e4m3_round(v) -> np.ndarray:
     """Round float32 values to e4m3fn values (RNE, saturating at +-448); returns float64."""
     v = np.asarray(v, dtype=np.float32).astype(np.float64)

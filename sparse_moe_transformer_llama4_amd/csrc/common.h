@@ -74,6 +74,7 @@ struct WsLayout {
   size_t y_s;                               // fp32 [T][d] shared-expert output
   size_t r_out;                             // fp32 [T][d] routed output before the combine (bf16 prefill)
   size_t gu_part;                           // fp32 [parts][T][2 fs] gate/up partials (dense decode)
+  size_t x_n;                               // x's rows after the RMSNorm (x dtype), when the block has one
   size_t xq, sx;                            // e4m3 x codes [T][d] and fp32 scales [T] (e4m3 only)
   size_t total;
 };

@@ -80,6 +80,10 @@ hipError_t launch_perm(const int32_t* idx, const int32_t* base, const int32_t* o
 // (used with nsplit = 1 when the logits come from the prefill GEMM).
 hipError_t launch_router_finish(const RouterArgs& a, int nsplit, const float* part, hipStream_t s);
 hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* sx, hipStream_t s);
+// RMSNorm of x's rows into xn (x's dtype, DT_BF16 or DT_F32); with xq / sx
+// (bf16 only) also xn's per-token e4m3 codes and scales.
+hipError_t launch_rmsnorm(int x_dtype, const void* x, const void* w, int T, int d, float eps, void* xn,
+                          uint8_t* xq, float* sx, hipStream_t s);
 hipError_t launch_quant_h(const float* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
                           float* sh, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);

@@ -119,6 +119,7 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   if (c.w_dtype == MOE_BF16 && T >= kPrefillTokens) L.r_out = take(t * c.d * 4);
   if (dense_gateup_parts(c, T) > 1)
     L.gu_part = take(static_cast<size_t>(dense_gateup_parts(c, T)) * t * 2 * c.f_shared * 4);
+  if (c.has_norm) L.x_n = take(t * c.d * (c.x_dtype == MOE_F32 ? 4 : 2));
   if (fp8) {
     L.hq_r = take(t * c.f);
     L.hq_s = take(t * c.f_shared);
@@ -146,6 +147,7 @@ moe_status check_common(moe_plan_t plan, const void* x, int64_t T, const moe_wei
   if (T > 0 && (!x || !aligned16(x))) return MOE_ERR_INVALID_ARGUMENT;
   if (c.n_experts > 0 && (!w->w_router || !aligned16(w->w_router))) return MOE_ERR_INVALID_ARGUMENT;
   if (c.has_router_bias && (!w->router_bias || !aligned16(w->router_bias))) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.has_norm && (!w->norm_weight || !aligned16(w->norm_weight))) return MOE_ERR_INVALID_ARGUMENT;
   if (layout_for(c, T).total > ws_bytes) return MOE_ERR_WORKSPACE;
   if (T > 0 && (!ws || !aligned16(ws))) return MOE_ERR_INVALID_ARGUMENT;
   return MOE_OK;
@@ -456,7 +458,7 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
                           out, static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream);
   }
 
-  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return e;
   if ((e = enqueue_route(c, x, T, w, R, stream)) != hipSuccess) return e;
   if ((e = mark(1)) != hipSuccess) return e;
@@ -480,7 +482,7 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
 hipError_t enqueue_dense(const moe_config& c, const void* x, int T, const moe_weights* w, void* out, uint8_t* ws,
                          const WsLayout& L, const Route& R, hipStream_t stream, hipEvent_t* ev) {
   hipError_t e;
-  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess || (e = mark(1)) != hipSuccess) return e;   // no routing stage
   if (T == 0) {
     for (int i = 2; i <= MOE_NUM_STAGES; ++i)
@@ -532,7 +534,7 @@ const char* moe_status_string(moe_status s) {
   return "unknown status";
 }
 
-const char* moe_version(void) { return "moe355 1 gfx950"; }
+const char* moe_version(void) { return "moe355 2 gfx950"; }
 
 moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
   if (!out) return MOE_ERR_INVALID_ARGUMENT;
@@ -543,6 +545,8 @@ moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
   if (c.n_experts < 0 || c.n_experts > 256) return MOE_ERR_UNSUPPORTED;
   if (!config_dtypes_ok(c)) return MOE_ERR_UNSUPPORTED;
   if (c.has_router_bias != 0 && c.has_router_bias != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.has_norm != 0 && c.has_norm != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.has_norm && !(c.norm_eps >= 0.0f && c.norm_eps <= 3.4e38f)) return MOE_ERR_INVALID_ARGUMENT;
   if (c.max_tokens < 1 || c.max_tokens > (int64_t{1} << 30)) return MOE_ERR_SHAPE;
   if (c.n_experts == 0) {
     // a dense layer: the shared gated MLP alone, bf16 weights, widths that
@@ -590,8 +594,15 @@ moe_status moe_route(moe_plan_t plan, const void* x, int64_t T, const moe_weight
   if (!out) return MOE_ERR_INVALID_ARGUMENT;
   if ((st = check_routing(out)) != MOE_OK) return st;
   const WsLayout L = layout_for(plan->cfg, T);
-  const Route R = route_ptrs(static_cast<uint8_t*>(workspace), L, out);
-  const hipError_t e = enqueue_route(plan->cfg, x, static_cast<int>(T), w, R, stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const Route R = route_ptrs(ws, L, out);
+  hipError_t e = hipSuccess;
+  if (plan->cfg.has_norm) {
+    e = launch_rmsnorm(plan->cfg.x_dtype, x, w->norm_weight, static_cast<int>(T), plan->cfg.d, plan->cfg.norm_eps,
+                       ws + L.x_n, nullptr, nullptr, stream);
+    x = ws + L.x_n;
+  }
+  if (e == hipSuccess) e = enqueue_route(plan->cfg, x, static_cast<int>(T), w, R, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
 }
 
@@ -610,12 +621,31 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   const WsLayout L = layout_for(c, T);
   const Route R = route_ptrs(ws, L, routing_out);
   const int Ti = static_cast<int>(T);
+  const bool fp8 = c.w_dtype == MOE_E4M3;
+
+  // the RMSNorm runs first, inside the routing stage of the timed variant
+  // (its events[0] is recorded here and the schedules below skip theirs);
+  // for e4m3 weights it also writes x's e4m3 codes and scales
+  hipEvent_t evn[MOE_NUM_STAGES + 1];
+  if (c.has_norm && T > 0) {
+    if (ev) {
+      hipError_t e0 = hipEventRecord(ev[0], stream);
+      if (e0 != hipSuccess) return hip_fail(plan, e0);
+      evn[0] = nullptr;
+      for (int i = 1; i <= MOE_NUM_STAGES; ++i) evn[i] = ev[i];
+      ev = evn;
+    }
+    const hipError_t en =
+        launch_rmsnorm(c.x_dtype, x, w->norm_weight, Ti, c.d, c.norm_eps, ws + L.x_n, fp8 ? ws + L.xq : nullptr,
+                       fp8 ? reinterpret_cast<float*>(ws + L.sx) : nullptr, stream);
+    if (en != hipSuccess) return hip_fail(plan, en);
+    x = ws + L.x_n;
+  }
   if (c.n_experts == 0) {
     const hipError_t e = enqueue_dense(c, x, Ti, w, out, ws, L, R, stream, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
   }
   const bool dec = use_decode(c, T);
-  const bool fp8 = c.w_dtype == MOE_E4M3;
   // the prefill kernels address activations with 32-bit byte offsets
   const int64_t kmax = std::max(std::max(c.d, c.f), c.f_shared);
   const bool offsets32 = T * kmax * 2 < (int64_t{1} << 31);
@@ -641,7 +671,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     e = enqueue_bf16_prefill(c, x, Ti, w, out, ws, L, R, aux, stream, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
   }
-  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return hip_fail(plan, e);
   e = enqueue_route(c, x, Ti, w, R, stream);
   if (e != hipSuccess) return hip_fail(plan, e);
@@ -657,7 +687,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   if (fp8) {
     uint8_t* xq = ws + L.xq;
     sx = reinterpret_cast<float*>(ws + L.sx);
-    if ((e = launch_quant_x(static_cast<const uint16_t*>(x), Ti, c.d, xq, sx, stream)) != hipSuccess)
+    if (!c.has_norm && (e = launch_quant_x(static_cast<const uint16_t*>(x), Ti, c.d, xq, sx, stream)) != hipSuccess)
       return hip_fail(plan, e);
     a_x = xq;
     amax_r = reinterpret_cast<uint32_t*>(ws + L.amax_r);

@@ -9,6 +9,8 @@
 // Active Parameters Diverge"); the gate is the sigmoid of the chosen logit,
 // applied to the routed expert's input (KerasFormers "Llama 4", section
 // "What is unusual about the block").
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -16,26 +18,22 @@ namespace moe {
 
 // ---------------------------------------------------------------- e4m3
 
-// float -> OCP e4m3fn code, round to nearest even, saturating at +-448.
-// Written from the format definition (4 significant bits, exponent bias 7,
-// subnormal quantum 2^-9, largest finite 448 = code 0x7E).
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0.015625f) {                     // below 2^-6: subnormal grid of 2^-9
-    const float q = rintf(a * 512.0f);     // exact scaling, RNE; q in [0, 8]
-    return sign | static_cast<uint32_t>(q);
-  }
-  const uint32_t ua = __float_as_uint(a);
-  int e = static_cast<int>(ua >> 23) - 127;
-  const uint32_t m = ua & 0x7FFFFFu;
-  const uint32_t r = m + 0x7FFFFu + ((m >> 20) & 1u);  // drop 20 mantissa bits, ties to even
-  e += static_cast<int>(r >> 23);
-  const uint32_t mant = (r >> 20) & 7u;
-  if (e > 8 || (e == 8 && mant == 7u)) return sign | 0x7Eu;
-  return sign | (static_cast<uint32_t>(e + 7) << 3) | mant;
+// Two floats -> two OCP e4m3fn codes (low byte = a), round to nearest even,
+// with gfx950's conversion instruction (its fp8 format is OCP E4M3, bias 7,
+// largest finite 448).  Inputs are clamped to +-448 first, so values past
+// the largest finite code saturate to it instead of becoming NaN.  On every
+// float of magnitude below 448 + 256 ulps, and for both signs, the
+// instruction gives the codes that the format definition does (4
+// significant bits, subnormal quantum 2^-9, ties to even): an exhaustive
+// comparison against an integer implementation of that definition found no
+// difference.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  return e4m3x2(a, b) | (e4m3x2(c, d) << 16);
 }
 
 // ---------------------------------------------------------------- router
@@ -191,15 +189,199 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* x, int T, 
   for (int k = lane * 8; k < d; k += 64 * 8) {
     const uint4 v = *reinterpret_cast<const uint4*>(row + k);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t lo = 0, hi = 0;
+    float q[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      lo |= f32_to_e4m3(__uint_as_float(w[i] << 16) / s) << (16 * i);
-      lo |= f32_to_e4m3(__uint_as_float(w[i] & 0xFFFF0000u) / s) << (16 * i + 8);
-      hi |= f32_to_e4m3(__uint_as_float(w[i + 2] << 16) / s) << (16 * i);
-      hi |= f32_to_e4m3(__uint_as_float(w[i + 2] & 0xFFFF0000u) / s) << (16 * i + 8);
+    for (int i = 0; i < 4; ++i) {
+      q[2 * i] = __uint_as_float(w[i] << 16) / s;
+      q[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) / s;
     }
-    *reinterpret_cast<uint2*>(qrow + k) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(qrow + k) = make_uint2(e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7]));
+  }
+}
+
+// RMSNorm of the block's input rows, the normalisation that precedes the
+// feed-forward block (llm-architectures-explained "Llama 4 Maverick", table
+// "Every architecture field": RMSNorm, placed before the MLP; KerasFormers
+// "Llama 4", Llama4Model arguments: norm_eps = 1e-5):
+//   xn[t, j] = x[t, j] * r_t * w[j],  r_t = 1 / sqrt(mean_j x[t, j]^2 + eps),
+// rounded once (RNE) to x's dtype; the block then reads xn in place of x.
+// The rounded rows are those of the exact value (to ties closer than ~1e-15
+// relative), so the router's argmax and the e4m3 codes downstream are
+// decided on the same rows as an exact computation would give:
+//   - the sum of squares and r_t are fp64 (squares of bf16 / fp32 values
+//     are exact in fp64);
+//   - bf16 rows: y = (x * fp32(r_t)) * w in fp32 is within 2 fp32 ulps of
+//     the exact value, which settles the bf16 rounding unless y's low 16
+//     bits lie within 4 of the halfway pattern 0x8000; those elements (about
+//     1 in 8000) are recomputed in fp64 and rounded to odd in fp32 before
+//     the bf16 rounding (no double-rounding error);
+//   - fp32 rows: fp64 throughout, one rounding to fp32.
+// With QUANT (bf16 rows feeding e4m3 weights) the same pass also writes xn's
+// per-token e4m3 codes and scales (s = fp32 max|xn_t| / 448, code =
+// e4m3(xn / s) with an IEEE fp32 division), so the normalised rows are not
+// read back for the quantisation.  One wave per row.
+
+// fp64 -> fp32 rounded to odd (truncate, then set the last bit if inexact):
+// a later RNE to bf16 (8 significant bits <= 24 - 2) is then correctly
+// rounded from the fp64 value.
+__device__ __forceinline__ float f64_to_f32_odd(double y) {
+  const float f = __double2float_rz(y);
+  return static_cast<double>(f) == y ? f : __uint_as_float(__float_as_uint(f) | 1u);
+}
+
+template <int XDT, bool QUANT, int NCH>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void* w, int T, int d, float eps,
+                                                      void* xn, uint8_t* xq, float* sx) {
+  static_assert(XDT == DT_BF16 || !QUANT, "e4m3 codes come from bf16 rows");
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  constexpr int V = XDT == DT_BF16 ? 8 : 4;   // elements per 16-byte chunk
+  constexpr int ES = XDT == DT_BF16 ? 2 : 4;  // bytes per element
+  // NCH chunks per lane are held in registers (the launcher picks the
+  // smallest instance that holds the row, 16 at most: fewer registers, more
+  // rows in flight): a row of up to 64 * V * NCH elements is loaded once,
+  // all its loads in flight together.  Longer rows are walked in groups of
+  // NCH chunks per lane: the sum of squares reads them once, the output
+  // pass again (from L2); with QUANT the output pass of a long row also
+  // recomputes its values after the max pass.
+  const int step = 64 * V;
+  const int nch = (d + step - 1) / step;
+  const bool resident = nch <= NCH;
+  const uint8_t* xrow = static_cast<const uint8_t*>(x) + static_cast<int64_t>(t) * d * ES;
+  const uint8_t* wrow = static_cast<const uint8_t*>(w);
+  // x and the gain (the same for every row: an L1 / L2 hit) are loaded
+  // together, so the gain's latency hides behind x's
+  uint4 xr[NCH], wr[NCH];
+  auto valid = [&](int g0, int c) { return g0 + c < nch && (g0 + c) * step + lane * V < d; };
+  auto load_group = [&](int g0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (valid(g0, c)) {
+        const int64_t k = (g0 + c) * step + lane * V;
+        xr[c] = *reinterpret_cast<const uint4*>(xrow + k * ES);
+        wr[c] = *reinterpret_cast<const uint4*>(wrow + k * ES);
+      }
+  };
+  auto unpack = [](const uint4& q, float (&v)[V]) {
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+    if constexpr (XDT == DT_BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(u[i] << 16);
+        v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(u[i]);
+    }
+  };
+
+  // pass 1: sum of squares (fp64)
+  double ss = 0.0;
+  for (int g0 = 0; g0 < nch; g0 += NCH) {
+    load_group(g0);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (valid(g0, c)) {
+        float v[V];
+        unpack(xr[c], v);
+#pragma unroll
+        for (int i = 0; i < V; ++i) ss = fma(static_cast<double>(v[i]), static_cast<double>(v[i]), ss);
+      }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m, 64);
+  const double r = 1.0 / sqrt(ss / static_cast<double>(d) + static_cast<double>(eps));
+  const float r32 = static_cast<float>(r);
+
+  // the normalised values of chunk c, as stored (rounded once to the row dtype)
+  auto normed = [&](int c, float (&y)[V]) {
+    float v[V], wv[V];
+    unpack(xr[c], v);
+    unpack(wr[c], wv);
+    if constexpr (XDT == DT_BF16) {
+      float yf[V];
+      bool near = false;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        yf[i] = (v[i] * r32) * wv[i];
+        near |= ((__float_as_uint(yf[i]) & 0xFFFFu) - 0x7FFCu) <= 8u;
+      }
+      if (near) {   // some value within 4 of the bf16 halfway pattern: decide those in fp64
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+          if (((__float_as_uint(yf[i]) & 0xFFFFu) - 0x7FFCu) <= 8u)
+            yf[i] = f64_to_f32_odd(static_cast<double>(v[i]) * r * static_cast<double>(wv[i]));
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) y[i] = __uint_as_float(static_cast<uint32_t>(f32_to_bf16(yf[i])) << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+        y[i] = static_cast<float>(static_cast<double>(v[i]) * r * static_cast<double>(wv[i]));
+    }
+  };
+  auto pack_bf16 = [](const float (&y)[V]) -> uint4 {
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (__float_as_uint(y[2 * i]) >> 16) | (__float_as_uint(y[2 * i + 1]) & 0xFFFF0000u);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  auto out_index = [&](int g0, int c) { return static_cast<int64_t>(t) * d + (g0 + c) * step + lane * V; };
+
+  if constexpr (!QUANT) {
+    // pass 2: the normalised rows
+    for (int g0 = 0; g0 < nch; g0 += NCH) {
+      if (!resident) load_group(g0);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (!valid(g0, c)) continue;
+        float y[V];
+        normed(c, y);
+        if constexpr (XDT == DT_BF16)
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(xn) + out_index(g0, c)) = pack_bf16(y);
+        else
+          *reinterpret_cast<float4*>(static_cast<float*>(xn) + out_index(g0, c)) = make_float4(y[0], y[1], y[2], y[3]);
+      }
+    }
+  } else {
+    // pass 2: the normalised rows and their largest magnitude; a resident
+    // row keeps its bf16 values in place of x for the codes
+    float amax = 0.f;
+    for (int g0 = 0; g0 < nch; g0 += NCH) {
+      if (!resident) load_group(g0);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (!valid(g0, c)) continue;
+        float y[V];
+        normed(c, y);
+#pragma unroll
+        for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(y[i]));
+        const uint4 yb = pack_bf16(y);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(xn) + out_index(g0, c)) = yb;
+        if (resident) xr[c] = yb;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (lane == 0) sx[t] = s;
+    // pass 3: e4m3 codes of the normalised rows
+    for (int g0 = 0; g0 < nch; g0 += NCH) {
+      if (!resident) load_group(g0);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (!valid(g0, c)) continue;
+        float y[V];
+        if (resident) unpack(xr[c], y);
+        else normed(c, y);
+#pragma unroll
+        for (int i = 0; i < V; ++i) y[i] = y[i] / s;
+        *reinterpret_cast<uint2*>(xq + out_index(g0, c)) =
+            make_uint2(e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7]));
+      }
+    }
   }
 }
 
@@ -217,10 +399,8 @@ __global__ __launch_bounds__(256) void quant_h_kernel(const float* h, const uint
   const float* src = h + static_cast<int64_t>(r) * n + k;
   const float4 v0 = *reinterpret_cast<const float4*>(src);
   const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-  const uint32_t lo = f32_to_e4m3(v0.x / s) | (f32_to_e4m3(v0.y / s) << 8) | (f32_to_e4m3(v0.z / s) << 16) |
-                      (f32_to_e4m3(v0.w / s) << 24);
-  const uint32_t hi = f32_to_e4m3(v1.x / s) | (f32_to_e4m3(v1.y / s) << 8) | (f32_to_e4m3(v1.z / s) << 16) |
-                      (f32_to_e4m3(v1.w / s) << 24);
+  const uint32_t lo = e4m3x4(v0.x / s, v0.y / s, v0.z / s, v0.w / s);
+  const uint32_t hi = e4m3x4(v1.x / s, v1.y / s, v1.z / s, v1.w / s);
   *reinterpret_cast<uint2*>(hq + static_cast<int64_t>(r) * n + k) = make_uint2(lo, hi);
 }
 
@@ -466,6 +646,30 @@ hipError_t launch_perm(const int32_t* idx, const int32_t* base, const int32_t* o
 
 hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* sx, hipStream_t s) {
   hipLaunchKernelGGL(quant_x_kernel, dim3((T + 3) / 4), dim3(256), 0, s, x, T, d, xq, sx);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int x_dtype, const void* x, const void* w, int T, int d, float eps, void* xn,
+                          uint8_t* xq, float* sx, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (d % (x_dtype == DT_BF16 ? 8 : 4) != 0) return hipErrorInvalidValue;
+  if (x_dtype != DT_BF16 && (x_dtype != DT_F32 || xq)) return hipErrorInvalidValue;
+  const dim3 grid((T + 3) / 4);
+  const int nch = (d + 64 * (x_dtype == DT_BF16 ? 8 : 4) - 1) / (64 * (x_dtype == DT_BF16 ? 8 : 4));
+  auto go = [&](auto nch_c) {
+    constexpr int N = decltype(nch_c)::value;
+    if (x_dtype == DT_BF16 && xq)
+      hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, true, N>), grid, dim3(256), 0, s, x, w, T, d, eps, xn, xq, sx);
+    else if (x_dtype == DT_BF16)
+      hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, false, N>), grid, dim3(256), 0, s, x, w, T, d, eps, xn, xq, sx);
+    else
+      hipLaunchKernelGGL((rmsnorm_kernel<DT_F32, false, N>), grid, dim3(256), 0, s, x, w, T, d, eps, xn, xq, sx);
+  };
+  if (nch <= 2) go(std::integral_constant<int, 2>{});
+  else if (nch <= 4) go(std::integral_constant<int, 4>{});
+  else if (nch <= 8) go(std::integral_constant<int, 8>{});
+  else if (nch <= 10) go(std::integral_constant<int, 10>{});   // 5120-wide bf16 rows
+  else go(std::integral_constant<int, 16>{});
   return hipGetLastError();
 }
 

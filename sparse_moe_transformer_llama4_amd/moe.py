@@ -14,7 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libmoe355.so")
 
-MOE_ABI_VERSION = 1
+MOE_ABI_VERSION = 2
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3}
 _TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.uint8}
@@ -40,13 +40,14 @@ class _Config(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_int32), ("d", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("f", ctypes.c_int32), ("f_shared", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("x_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("has_router_bias", ctypes.c_int32), ("max_tokens", ctypes.c_int64)]
+                ("has_router_bias", ctypes.c_int32), ("max_tokens", ctypes.c_int64),
+                ("has_norm", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
 
 
 class _Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "router_bias", "w_gate_up", "s_gate_up", "w_down", "s_down",
-        "ws_gate_up", "ss_gate_up", "ws_down", "ss_down")]
+        "ws_gate_up", "ss_gate_up", "ws_down", "ss_down", "norm_weight")]
 
 
 class _Routing(ctypes.Structure):
@@ -110,13 +111,17 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 class Plan:
-    """Owns a moe_plan_t.  Shapes: d, E, f, fs; dtypes as "f32" / "bf16" / "e4m3"."""
+    """Owns a moe_plan_t.  Shapes: d, E, f, fs; dtypes as "f32" / "bf16" / "e4m3".
+    norm_eps (a float) puts the RMSNorm in front of the block; the weights
+    dict then carries "norm_weight" ([d], x dtype)."""
 
     def __init__(self, d: int, E: int, f: int, fs: int, x_dtype="bf16", w_dtype="bf16",
-                 out_dtype="f32", has_bias=False, max_tokens=65536, top_k=1):
+                 out_dtype="f32", has_bias=False, max_tokens=65536, top_k=1, norm_eps=None):
         lib = load_library()
         self.cfg = _Config(MOE_ABI_VERSION, d, E, f, fs, top_k, _DT[x_dtype], _DT[w_dtype], _DT[out_dtype],
-                           int(bool(has_bias)), max_tokens)
+                           int(bool(has_bias)), max_tokens, int(norm_eps is not None),
+                           0.0 if norm_eps is None else float(norm_eps))
+        self.norm_eps = norm_eps
         self.d, self.E, self.f, self.fs = d, E, f, fs
         self.x_dtype, self.w_dtype, self.out_dtype = x_dtype, w_dtype, out_dtype
         self.has_bias = bool(has_bias)
@@ -128,7 +133,8 @@ class Plan:
     @staticmethod
     def for_shape(shape, max_tokens=None) -> "Plan":
         return Plan(shape.d, shape.E, shape.f, shape.fs, shape.x_dtype, shape.w_dtype, shape.out_dtype,
-                    shape.has_bias, max_tokens or max(shape.T, 1))
+                    shape.has_bias, max_tokens or max(shape.T, 1),
+                    norm_eps=getattr(shape, "norm_eps", None))
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -158,7 +164,7 @@ def moe_workspace_size(plan: Plan, T: int) -> int:
 def _weights(w: dict) -> _Weights:
     return _Weights(*[_ptr(w.get(k)) for k in (
         "w_router", "router_bias", "w_gate_up", "s_gate_up", "w_down", "s_down",
-        "ws_gate_up", "ss_gate_up", "ws_down", "ss_down")])
+        "ws_gate_up", "ss_gate_up", "ws_down", "ss_down", "norm_weight")])
 
 
 def new_routing(plan: Plan, T: int, device) -> dict:
@@ -191,6 +197,10 @@ def _check_inputs(plan: Plan, x: torch.Tensor, w: dict):
     _check_tensor(x, "x", _TORCH_DT[_DT[plan.x_dtype]])
     if x.dim() != 2 or x.shape[1] != plan.d:
         raise ValueError(f"x must be [T, {plan.d}]")
+    if plan.norm_eps is not None:
+        _check_tensor(w["norm_weight"], "norm_weight", _TORCH_DT[_DT[plan.x_dtype]])
+        if tuple(w["norm_weight"].shape) != (plan.d,):
+            raise ValueError("norm_weight shape")
     if plan.E == 0:          # a dense layer: no router
         return
     _check_tensor(w["w_router"], "w_router", _TORCH_DT[_DT[plan.x_dtype]])

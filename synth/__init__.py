@@ -22,6 +22,11 @@ Generator (counter-based, identical on CPU and GPU):
 fp8 weights (OCP e4m3fn) are drawn in fp32 the same way and quantised per
 output column of the [K, N] layout: scale = amax over K / 448 (fp32), code =
 torch's float8_e4m3fn cast of clamp(w / scale, -448, 448).
+
+Workloads with the RMSNorm in front of the block (norm_eps set) also draw its
+gain, w[j] = 1 + 0.1 * Q (fp32, then rounded to x's dtype), and give every
+token row its own scale, x[t, :] *= 0.25 + |Q_t| (fp32, from a stream of its
+own), so that rows differ in RMS as the residual stream's rows do.
 """
 from __future__ import annotations
 
@@ -35,7 +40,7 @@ import torch
 __all__ = [
     "MoEShape", "CONFIGS", "TEST_SHAPES", "get_config", "mix32_int",
     "normal_fp32", "gen_x", "gen_router", "gen_bias", "gen_expert",
-    "gen_shared", "make_inputs", "DTYPES",
+    "gen_shared", "gen_norm_weight", "make_inputs", "DTYPES",
 ]
 
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}
@@ -62,6 +67,7 @@ class MoEShape:
     seed: int = 0
     x_std: float = 1.0
     w_std: float = 0.02
+    norm_eps: Optional[float] = None   # RMSNorm in front of the block (None = none)
 
     @property
     def has_bias(self) -> bool:
@@ -92,6 +98,12 @@ EXTRA_CONFIGS = {
                                             fs=16384, seed=5),
     "maverick_dense_decode_bf16": MoEShape("maverick_dense_decode_bf16", T=32, d=5120, E=0, f=0,
                                            fs=16384, seed=6),
+    # the MoE layer with the RMSNorm that precedes it (eps 1e-5)
+    "scout_prefill_bf16_rmsnorm": MoEShape("scout_prefill_bf16_rmsnorm", T=4096, d=5120, E=16, f=8192,
+                                           fs=8192, seed=7, norm_eps=1e-5),
+    "maverick_prefill_fp8_rmsnorm": MoEShape("maverick_prefill_fp8_rmsnorm", T=16384, d=5120, E=128,
+                                             f=8192, fs=8192, w_dtype="e4m3", out_dtype="bf16", seed=8,
+                                             norm_eps=1e-5),
 }
 
 # Smaller shapes for element-by-element parity: several tiles in every
@@ -145,7 +157,7 @@ _C1 = 0x7FEB352D
 _C2 = 0x846CA68B
 
 STREAMS = {"x": 1, "w_router": 2, "bias": 3, "w_gate_up": 4, "w_down": 5,
-           "ws_gate_up": 6, "ws_down": 7}
+           "ws_gate_up": 6, "ws_down": 7, "norm_weight": 8, "x_row_scale": 9}
 
 
 def mix32_int(x: int) -> int:
@@ -236,8 +248,19 @@ def gen_x(cfg: MoEShape, device="cpu", rows: Optional[slice] = None) -> torch.Te
     """Token activations x [T, d] in cfg.x_dtype (rows: optional row slice)."""
     r0, r1 = (0, cfg.T) if rows is None else (rows.start or 0, rows.stop)
     key = stream_key(cfg.seed, "x")
-    v = normal_fp32(key, r0 * cfg.d, (r1 - r0) * cfg.d, cfg.x_std, device)
-    return _round_to(v, cfg.x_dtype).view(r1 - r0, cfg.d)
+    v = normal_fp32(key, r0 * cfg.d, (r1 - r0) * cfg.d, cfg.x_std, device).view(r1 - r0, cfg.d)
+    if cfg.norm_eps is not None:   # per-row scales 0.25 + |Q_t|
+        q = normal_fp32(stream_key(cfg.seed, "x_row_scale"), r0, r1 - r0, 1.0, device)
+        v = v * (q.abs() + torch.tensor(0.25, dtype=torch.float32, device=v.device))[:, None]
+    return _round_to(v, cfg.x_dtype)
+
+
+def gen_norm_weight(cfg: MoEShape, device="cpu") -> Optional[torch.Tensor]:
+    """RMSNorm gain [d] in cfg.x_dtype, 1 + 0.1 * Q (None without a norm)."""
+    if cfg.norm_eps is None:
+        return None
+    v = normal_fp32(stream_key(cfg.seed, "norm_weight"), 0, cfg.d, 0.1, device)
+    return _round_to(v + torch.tensor(1.0, dtype=torch.float32, device=v.device), cfg.x_dtype)
 
 
 def gen_router(cfg: MoEShape, device="cpu") -> torch.Tensor:
@@ -314,7 +337,8 @@ def make_inputs(cfg: MoEShape, device="cpu") -> dict:
         wsgu, ssgu, wsd, ssd = gen_shared(cfg, dev)
         return {"x": gen_x(cfg, dev), "w_router": None, "router_bias": None, "w_gate_up": None, "w_down": None,
                 "s_gate_up": None, "s_down": None,
-                "ws_gate_up": wsgu, "ss_gate_up": ssgu, "ws_down": wsd, "ss_down": ssd}
+                "ws_gate_up": wsgu, "ss_gate_up": ssgu, "ws_down": wsd, "ss_down": ssd,
+                "norm_weight": gen_norm_weight(cfg, dev)}
     out = {
         "x": gen_x(cfg, dev),
         "w_router": gen_router(cfg, dev),
@@ -322,6 +346,7 @@ def make_inputs(cfg: MoEShape, device="cpu") -> dict:
         "w_gate_up": torch.empty((E, d, 2 * f), dtype=wdt, device=dev),
         "w_down": torch.empty((E, f, d), dtype=wdt, device=dev),
         "s_gate_up": None, "s_down": None, "ss_gate_up": None, "ss_down": None,
+        "norm_weight": gen_norm_weight(cfg, dev),
     }
     if cfg.w_dtype == "e4m3":
         out["s_gate_up"] = torch.empty((E, 2 * f), dtype=torch.float32, device=dev)

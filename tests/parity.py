@@ -61,21 +61,35 @@ def output_error(cfg, out_gpu, ref):
     return float(np.max(np.maximum(np.abs(g - ref) - slack, 0.0)) / rms)
 
 
+def norm_eps32(cfg) -> float:
+    """The configured RMSNorm epsilon as the library holds it (an fp32 value)."""
+    return float(np.float32(cfg.norm_eps))
+
+
+def block_input(cfg, inp_cpu: dict, rows=None):
+    """What the block's steps read: x, or its RMSNorm when the workload has one."""
+    x = inp_cpu["x"] if rows is None else inp_cpu["x"][rows]
+    if getattr(cfg, "norm_eps", None) is None:
+        return x
+    return block.rmsnorm(x, inp_cpu["norm_weight"], norm_eps32(cfg), cfg.x_dtype)
+
+
 def check_forward(cfg, inp_cpu: dict, out_gpu, routing, tol=None):
     w = block.Weights.from_dict(inp_cpu)
     wr, b = w.router()
-    r = block.route(inp_cpu["x"], wr, b)
+    x = block_input(cfg, inp_cpu)
+    r = block.route(x, wr, b)
     idx = check_routing(cfg, r, routing)
     gate = block.sigmoid(r.logits[np.arange(len(idx)), idx])
-    ref = block.combine(inp_cpu["x"], idx, gate, w, cfg.f, cfg.fs, cfg.w_dtype)
+    ref = block.combine(x, idx, gate, w, cfg.f, cfg.fs, cfg.w_dtype)
     err = output_error(cfg, out_gpu, ref)
     assert err <= (tol or TOL[cfg.w_dtype]), f"{cfg.name}: max|err|/RMS = {err:.3e}"
     if cfg.w_dtype == "e4m3":
-        check_fp8_accuracy(cfg, inp_cpu, out_gpu, ref, idx, gate, w)
+        check_fp8_accuracy(cfg, x, out_gpu, ref, idx, gate, w)
     return err, r
 
 
-def check_fp8_accuracy(cfg, inp_cpu, out_gpu, ref, idx, gate, w):
+def check_fp8_accuracy(cfg, x, out_gpu, ref, idx, gate, w):
     """fp8 extra checks.  The fp8 MFMA sums its 128 products with less than
     fp32 precision, so rare e4m3 codes of h land one step away from the
     oracle's; the RMS-level deviation must stay small and the GPU must be as
@@ -83,7 +97,7 @@ def check_fp8_accuracy(cfg, inp_cpu, out_gpu, ref, idx, gate, w):
     g = out_gpu.detach().cpu().double().numpy()
     rms = np.sqrt(np.mean(ref * ref))
     assert np.sqrt(np.mean((g - ref) ** 2)) / rms <= 5e-3
-    exact = block.combine(inp_cpu["x"], idx, gate, w, cfg.f, cfg.fs, "f32")
+    exact = block.combine(x, idx, gate, w, cfg.f, cfg.fs, "f32")
     e_gpu = np.sqrt(np.mean((g - exact) ** 2))
     e_orc = np.sqrt(np.mean((ref - exact) ** 2))
     assert e_gpu <= 1.05 * e_orc + 1e-3 * rms

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def _cfg(**kw):
-    base = dict(abi_version=1, d=256, n_experts=4, f=512, f_shared=512, top_k=1, x_dtype=1, w_dtype=1,
+    base = dict(abi_version=moe.MOE_ABI_VERSION, d=256, n_experts=4, f=512, f_shared=512, top_k=1, x_dtype=1, w_dtype=1,
                 out_dtype=0, has_router_bias=0, max_tokens=64)
     base.update(kw)
     return moe._Config(**base)
@@ -58,9 +58,19 @@ def _plan(**kw):
     ({"x_dtype": 0}, UNSUPPORTED),
     ({"w_dtype": 2, "out_dtype": 0}, UNSUPPORTED),
     ({"w_dtype": 2, "out_dtype": 1, "d": 192}, UNSUPPORTED),
-    ({"abi_version": 2}, INVALID),
+    ({"abi_version": 1}, INVALID),
+    ({"abi_version": 3}, INVALID),
     ({"has_router_bias": 3}, INVALID),
     ({"max_tokens": 0}, SHAPE),
+    # the RMSNorm in front of the block
+    ({"has_norm": 1, "norm_eps": 1e-5}, OK),
+    ({"has_norm": 1, "norm_eps": 0.0, "x_dtype": 0, "w_dtype": 0, "out_dtype": 0}, OK),
+    ({"has_norm": 1, "norm_eps": 1e-5, "w_dtype": 2, "out_dtype": 1}, OK),
+    ({"has_norm": 1, "norm_eps": 1e-5, "n_experts": 0, "f": 0}, OK),
+    ({"has_norm": 1, "norm_eps": -1e-5}, INVALID),
+    ({"has_norm": 1, "norm_eps": float("nan")}, INVALID),
+    ({"has_norm": 1, "norm_eps": float("inf")}, INVALID),
+    ({"has_norm": 2, "norm_eps": 1e-5}, INVALID),
     # a dense layer (no routed experts): bf16, f == 0, no bias, widths % 128
     ({"n_experts": 0, "f": 0}, OK),
     ({"n_experts": 0, "f": 0, "out_dtype": 1}, OK),
@@ -97,7 +107,7 @@ def test_workspace_size_grows_with_tokens():
 
 
 def _weights(p=0x10000):
-    return moe._Weights(p, None, p, None, p, None, p, None, p, None)
+    return moe._Weights(p, None, p, None, p, None, p, None, p, None, None)
 
 
 def test_forward_rejects_before_enqueue():
@@ -162,3 +172,28 @@ def test_fp8_requires_scales_and_bias_when_declared():
 def test_status_strings():
     for s in (OK, INVALID, UNSUPPORTED, SHAPE, WORKSPACE, -5):
         assert moe.moe_status_string(s)
+
+
+def test_norm_requires_its_weight():
+    """A plan with the RMSNorm needs norm_weight (16-byte aligned) in every
+    entry point that reads x, and room for the normalised rows."""
+    lib = moe.load_library()
+    n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
+    st, h0 = _plan(max_tokens=64)
+    st1, h = _plan(max_tokens=64, has_norm=1, norm_eps=1e-5)
+    assert st == OK and st1 == OK
+    lib.moe_workspace_size(h0, 64, ctypes.byref(n0))
+    lib.moe_workspace_size(h, 64, ctypes.byref(n1))
+    assert n1.value >= n0.value + 64 * 256 * 2        # + T x d bf16 rows
+    P = 0x10000
+    r = moe._Routing(P, P, P, P, P)
+    for nw, want in ((None, INVALID), (P + 2, INVALID)):
+        w = _weights(P)
+        w.norm_weight = nw
+        assert lib.moe_forward(h, P, 64, ctypes.byref(w), P, None, P, n1.value, None) == want
+        assert lib.moe_route(h, P, 64, ctypes.byref(w), ctypes.byref(r), P, n1.value, None) == want
+    w = _weights(P)
+    w.norm_weight = P
+    assert lib.moe_forward(h, P, 64, ctypes.byref(w), P, None, P, n0.value, None) == WORKSPACE
+    lib.moe_plan_destroy(h0)
+    lib.moe_plan_destroy(h)

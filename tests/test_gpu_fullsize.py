@@ -13,7 +13,7 @@ import torch
 
 import synth
 from oracle import block
-from parity import TOL, check_routing, output_error
+from parity import TOL, block_input, check_routing, output_error
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,8 @@ def test_generator_gpu_equals_cpu(gpu):
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "scout_decode_bf16", "scout_prefill_bf16",
-                                  "maverick_prefill_bf16", "maverick_prefill_fp8"])
+                                  "maverick_prefill_bf16", "maverick_prefill_fp8",
+                                  "scout_prefill_bf16_rmsnorm", "maverick_prefill_fp8_rmsnorm"])
 def test_fullsize_sampled(gpu, name):
     from sparse_moe_transformer_llama4_amd import moe
     cfg = synth.get_config(name)
@@ -56,7 +57,9 @@ def test_fullsize_sampled(gpu, name):
     torch.cuda.empty_cache()
 
     print(f"[full] {name}: oracle routing on all {cfg.T} tokens", flush=True)
-    x = synth.gen_x(cfg, "cpu")
+    # the block's input: x, or its RMSNorm (computed row by row, so the
+    # sampled rows below are rows of the same array)
+    x = block_input(cfg, {"x": synth.gen_x(cfg, "cpu"), "norm_weight": synth.gen_norm_weight(cfg, "cpu")})
     r = block.route(x, synth.gen_router(cfg, "cpu"), synth.gen_bias(cfg))
     idx = check_routing(cfg, r, routing)
 

@@ -7,7 +7,7 @@ import torch
 
 import synth
 from oracle import block
-from parity import check_forward, run_gpu, to_device, output_error
+from parity import block_input, check_forward, check_routing, run_gpu, to_device, output_error
 
 pytestmark = pytest.mark.gpu
 
@@ -267,3 +267,68 @@ def test_dense_layer_matches_oracle(gpu, shape, T, out_dtype):
     assert err <= TOL["bf16"]
     with pytest.raises(Exception):
         moe.moe_forward(p, g["x"], g, workspace=ws, routing=moe.new_routing(p, T, gpu))
+
+
+# ------------------------------------------------------------ RMSNorm in front of the block
+
+# rows longer than the norm kernel keeps in registers (8192 bf16 / 4096 fp32
+# values) take its multi-pass path
+_LONG = dict(E=2, f=128, fs=128)
+NORM_CASES = [("small_bf16", None, 1e-5, {}), ("small_bf16", 65, 0.5, {}), ("small_fp32", None, 1e-5, {}),
+              ("small_fp8", None, 1e-5, {}), ("small_bf16_out16", None, 1e-5, {}),
+              ("decode_like_bf16", 33, 1e-5, {}), ("decode_like_bf16", 1, 1e-5, {}),
+              ("small_bf16_tall", None, 1e-5, {}), ("small_dense_bf16", 33, 1e-5, {}),
+              ("small_dense_bf16", 300, 1e-5, {}),
+              ("small_bf16", 40, 1e-5, dict(d=8704, **_LONG)), ("small_fp32", 20, 1e-5, dict(d=4160, **_LONG)),
+              ("small_fp8", 40, 1e-5, dict(d=8320, **_LONG))]
+
+
+@pytest.mark.parametrize("name,T,eps,over", NORM_CASES)
+def test_rmsnorm_block_matches_oracle(gpu, name, T, eps, over):
+    # out = block(RMSNorm(x)) on every schedule (fp32, bf16 decode / prefill
+    # with the side stream, e4m3 with the fused quantisation, dense layers);
+    # x itself is left unchanged
+    from parity import TOL
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = dataclasses.replace(synth.get_config(name), norm_eps=eps, name=f"{name}_norm", **over)
+    if T is not None:
+        cfg = dataclasses.replace(cfg, T=T)
+    print(f"[parity] rmsnorm {cfg.name} T={cfg.T} d={cfg.d} eps={eps}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    p = _plan(cfg)
+    if cfg.E == 0:
+        ws = torch.full((max(moe.moe_workspace_size(p, cfg.T), 256),), 0xFF, dtype=torch.uint8, device=gpu)
+        out = moe.moe_forward(p, g["x"], g, workspace=ws)
+        torch.cuda.synchronize()
+        ref = block.dense(block_input(cfg, inp), block.Weights.from_dict(inp), cfg.fs, cfg.w_dtype)
+        err = output_error(cfg, out, ref)
+        assert err <= TOL[cfg.w_dtype], err
+    else:
+        out, routing = run_gpu(p, g["x"], g)
+        err, _ = check_forward(cfg, inp, out, routing)
+    print(f"[parity] rmsnorm {cfg.name} max|err|/RMS = {err:.3e}", flush=True)
+    assert torch.equal(g["x"].cpu(), inp["x"])
+
+
+def test_rmsnorm_route_only_and_timed_variant(gpu):
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = dataclasses.replace(synth.get_config("small_bf16_tall"), norm_eps=1e-5, name="tall_norm")
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    p = _plan(cfg)
+    r = moe.moe_route(p, g["x"], g)
+    torch.cuda.synchronize()
+    w = block.Weights.from_dict(inp)
+    check_routing(cfg, block.route(block_input(cfg, inp), *w.router()), r)
+    # the stage-timed variant (serial schedule, the norm inside the routing
+    # stage) gives the same bits as moe_forward
+    ws = torch.empty(moe.moe_workspace_size(p, cfg.T), dtype=torch.uint8, device=gpu)
+    out = moe.moe_forward(p, g["x"], g, workspace=ws)
+    ev = moe.StageEvents()
+    out_t = torch.empty_like(out)
+    moe.moe_forward_timed(p, g["x"], g, ev, out=out_t, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_t)
+    ms = ev.durations_ms()
+    assert all(v >= 0 for v in ms) and ms[0] > 0

@@ -73,3 +73,26 @@ def test_e4m3_ties_to_even():
     # 1 + 3/16 halfway between 1.125 and 1.25: ties to 1.25
     v = np.array([1.0625, 1.1875, 2 ** -10, 3 * 2 ** -10], dtype=np.float32)
     np.testing.assert_array_equal(numerics.e4m3_round(v), [1.0, 1.25, 0.0, 2 ** -8])
+
+
+def test_round_f64_to_is_a_single_rounding():
+    # bf16: ulp 2^-7 at 1.0.  Exact ties go to even; a value just above a tie
+    # rounds up although its float32 rounding is the tie itself (a float32
+    # step in between would round it down to 1.0)
+    u = 2.0 ** -7
+    cases = [(1.0 + u / 2, 1.0), (1.0 + 1.5 * u, 1.0 + 2 * u), (1.0 + u / 2 + 2.0 ** -40, 1.0 + u),
+             (-(1.0 + u / 2 + 2.0 ** -40), -(1.0 + u)), (3.0, 3.0), (0.0, 0.0)]
+    got = numerics.round_f64_to(np.array([c[0] for c in cases]), "bf16")
+    np.testing.assert_array_equal(got, [c[1] for c in cases])
+    # fp32: ulp 2^-23 at 1.0
+    u = 2.0 ** -23
+    cases = [(1.0 + u / 2, 1.0), (1.0 + 1.5 * u, 1.0 + 2 * u), (1.0 + u / 2 + 2.0 ** -50, 1.0 + u)]
+    got = numerics.round_f64_to(np.array([c[0] for c in cases]), "f32")
+    np.testing.assert_array_equal(got, [c[1] for c in cases])
+    # agrees with numpy's own float64 -> float32 conversion (one RNE rounding)
+    v = np.random.default_rng(3).standard_normal(200_000) * 10.0 ** np.random.default_rng(4).integers(-30, 30, 200_000)
+    np.testing.assert_array_equal(numerics.round_f64_to(v, "f32"), v.astype(np.float32).astype(np.float64))
+    # and with torch's float32 -> bf16 cast where the input is already a float32
+    w = np.random.default_rng(5).standard_normal(200_000).astype(np.float32)
+    np.testing.assert_array_equal(numerics.round_f64_to(w.astype(np.float64), "bf16"),
+                                  torch.from_numpy(w).to(torch.bfloat16).double().numpy())

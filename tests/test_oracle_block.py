@@ -246,3 +246,58 @@ def test_e4m3_activation_quantisation_per_token():
             assert s[t] == np.float32(amax) / np.float32(448)
             codes = torch.from_numpy(np.clip(v[t] / s[t], -448, 448).astype(np.float32)).to(torch.float8_e4m3fn)
             np.testing.assert_array_equal(q[t], codes.to(torch.float64).numpy() * np.float64(s[t]))
+
+
+# ------------------------------------------------------------ RMSNorm (step 0)
+
+def test_rmsnorm_worked_example():
+    # x = (3, 4): mean square 12.5, root 5 / sqrt(2); xn = (3, 4) * sqrt(2) / 5
+    xn = block.rmsnorm(np.array([[3.0, 4.0]]), np.array([1.0, 1.0]), 0.0, "f32")
+    np.testing.assert_allclose(xn[0], [0.848528137423857, 1.131370849898476], rtol=2 ** -24)
+    # a gain scales each feature; eps sits under the root with the mean square
+    xn = block.rmsnorm(np.array([[3.0, 4.0]]), np.array([2.0, -0.5]), 3.5, "f32")
+    np.testing.assert_allclose(xn[0], [2 * 3 / 4.0, -0.5 * 4 / 4.0], rtol=2 ** -24)
+
+
+def test_rmsnorm_constant_rows_and_gain_per_feature():
+    # constant row c: xn[j] = c / sqrt(c^2 + eps) * w[j], w indexed by feature
+    w = np.array([1.0, 2.0, 3.0, 4.0])
+    x = np.array([[0.01] * 4, [-2.0] * 4, [5.0] * 4])
+    xn = block.rmsnorm(x, w, 1e-4, "f32")
+    for t, c in enumerate((0.01, -2.0, 5.0)):
+        np.testing.assert_allclose(xn[t], c / np.sqrt(c * c + 1e-4) * w, rtol=2 ** -23)
+
+
+def test_rmsnorm_unit_mean_square_and_scale_invariance():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((6, 40)) * np.array([0.01, 0.3, 1, 4, 50, 1e3])[:, None]
+    xn = block.rmsnorm(x, np.ones(40), 0.0, "f32")
+    np.testing.assert_allclose(np.mean(xn * xn, axis=1), 1.0, rtol=1e-6)   # each row, not each column
+    # powers of two commute with every step: bit-identical output
+    for k in (-20, -3, 5, 30):
+        np.testing.assert_array_equal(block.rmsnorm(x * 2.0 ** k, np.ones(40), 0.0, "f32"), xn)
+    # with eps > 0 the mean square of the output is ms / (ms + eps) < 1
+    ms = np.mean(x * x, axis=1)
+    xe = block.rmsnorm(x, np.ones(40), 0.5, "f32")
+    np.testing.assert_allclose(np.mean(xe * xe, axis=1), ms / (ms + 0.5), rtol=1e-6)
+    # a zero row stays zero when eps > 0
+    assert (block.rmsnorm(np.zeros((1, 8)), np.ones(8), 1e-5, "bf16") == 0).all()
+
+
+def test_rmsnorm_brute_force_and_bf16_rounding():
+    # pure-Python loops (math.fsum, math.sqrt) and the struct-based bf16
+    # rounding of oracle.brute against block.rmsnorm
+    import math
+    from oracle import brute
+    rng = np.random.default_rng(11)
+    x = torch.from_numpy(rng.standard_normal((5, 64)) * 3).to(torch.bfloat16)
+    w = torch.from_numpy(1 + 0.1 * rng.standard_normal(64)).to(torch.bfloat16)
+    eps = float(np.float32(1e-5))
+    got = block.rmsnorm(x, w, eps, "bf16")
+    xs, ws = x.double().tolist(), w.double().tolist()
+    for t in range(5):
+        r = 1.0 / math.sqrt(math.fsum(v * v for v in xs[t]) / 64 + eps)
+        exact = [xs[t][j] * r * ws[j] for j in range(64)]
+        # exact values are irrational: no float32-level tie, so brute's
+        # float32-then-bf16 route equals a single rounding here
+        assert got[t].tolist() == [brute._bf16(v) for v in exact]
