@@ -56,8 +56,8 @@ typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARGUMENT = -1, /* null / misaligned pointer, missing fp8 scale, bad abi_version */
   MOE_ERR_UNSUPPORTED = -2,      /* top_k != 1, d / f / f_shared not multiples of 64 (128 for
-                                    E4M3 weights), E outside [1,256], dtype combination not
-                                    implemented */
+                                    E4M3 and INT8 weights), E outside [1,256], dtype
+                                    combination not implemented */
   MOE_ERR_SHAPE = -3,            /* T < 0 or T > max_tokens */
   MOE_ERR_WORKSPACE = -4,        /* workspace smaller than moe_workspace_size */
   MOE_ERR_HIP = -5               /* a HIP launch failed; see moe_last_hip_error */
@@ -66,7 +66,8 @@ typedef enum moe_status {
 typedef enum moe_dtype {
   MOE_F32 = 0,
   MOE_BF16 = 1,
-  MOE_E4M3 = 2 /* OCP 8-bit float E4M3 "fn": max 448, no infinities; stored as uint8 codes */
+  MOE_E4M3 = 2, /* OCP 8-bit float E4M3 "fn": max 448, no infinities; stored as uint8 codes */
+  MOE_INT8 = 3  /* signed 8-bit integer weight codes (-127..127), with fp32 scales */
 } moe_dtype;
 
 /*
@@ -79,6 +80,18 @@ typedef enum moe_dtype {
  *   BF16 / BF16 / BF16   as above with the output rounded to bf16
  *   BF16 / E4M3 / BF16   router in bf16; x and h quantised to e4m3 per token;
  *                        e4m3 weights with one fp32 scale per output column
+ *   BF16 / INT8 / F32 or BF16
+ *                        weight-only int8 for decode (superteams.ai "Llama 4",
+ *                        section "The Llama 4 Herd"; aibase model card "Llama 4
+ *                        Maverick 17B 128E Instruct FP8", section
+ *                        "Quantization": Scout runs on one GPU with
+ *                        weights quantised to int4 on the fly; int8 halves
+ *                        the bytes a decode step streams): expert and
+ *                        shared weights as int8 codes
+ *                        with one fp32 scale per output column, dequantised
+ *                        in the weight-streaming GEMMs, bf16 activations and
+ *                        MFMA, h rounded to bf16; max_tokens <= 64
+ *                        (MOE_ERR_SHAPE otherwise), E >= 1
  *
  * n_experts == 0 configures a dense layer (llm-architectures-explained
  * "Llama 4 Maverick", table "Every architecture field": the layers between
@@ -101,10 +114,10 @@ typedef enum moe_dtype {
  */
 typedef struct moe_config {
   int32_t abi_version;     /* MOE_ABI_VERSION */
-  int32_t d;               /* model width, multiple of 64 (128 for E4M3 weights) */
+  int32_t d;               /* model width, multiple of 64 (128 for E4M3 / INT8 weights) */
   int32_t n_experts;       /* E, 1..256; 0 = a dense layer (see below) */
-  int32_t f;               /* routed expert width, multiple of 64 (128 for E4M3); 0 when E == 0 */
-  int32_t f_shared;        /* shared expert width, multiple of 64 (128 for E4M3) */
+  int32_t f;               /* routed expert width, multiple of 64 (128 for E4M3 / INT8); 0 when E == 0 */
+  int32_t f_shared;        /* shared expert width, multiple of 64 (128 for E4M3 / INT8) */
   int32_t top_k;           /* must be 1 */
   int32_t x_dtype;         /* moe_dtype of x and W_router */
   int32_t w_dtype;         /* moe_dtype of the expert and shared weights */
@@ -120,8 +133,8 @@ typedef struct moe_plan_s* moe_plan_t;
 /*
  * Weights: all resident in device memory (KerasFormers "Llama 4": all
  * experts stay resident).  Scale pointers are required when w_dtype is
- * E4M3 and ignored otherwise: one fp32 scale per output column n of the
- * [K, N] matrix, value = code * scale[n].
+ * E4M3 or INT8 and ignored otherwise: one fp32 scale per output column n of
+ * the [K, N] matrix, value = code * scale[n].
  */
 typedef struct moe_weights {
   const void* w_router;     /* [d, E]         x_dtype */

@@ -51,6 +51,8 @@ follow the data types of the workloads):
      (A bf16 intermediate is deliberately absent: a scale taken from a
      bf16-rounded row lets a one-ulp difference in the row's largest element
      re-round every code of that row.)
+  R1 (int8 weights, dequantised to code * column scale): as for bf16 -- the
+     activations stay bf16 and h is rounded to bf16.
   The output itself is returned unrounded in float64.
 """
 from __future__ import annotations
@@ -76,9 +78,15 @@ def to_f64(t) -> np.ndarray:
 
 
 def dequant_cols(codes, scale) -> np.ndarray:
-    """e4m3 codes [K, N] (uint8) with one fp32 scale per column N -> float64 values."""
+    """Weight codes [K, N] with one fp32 scale per column N -> float64 values:
+    e4m3 codes (uint8) decode to their e4m3 values, int8 codes are integers;
+    value = code value * scale[n]."""
     c = codes.numpy() if isinstance(codes, torch.Tensor) else np.asarray(codes)
     s = to_f64(scale)
+    if c.dtype == np.int8:
+        return c.astype(np.float64) * s[None, :]
+    if c.dtype != np.uint8:
+        raise TypeError(f"weight codes of dtype {c.dtype}")
     return e4m3_decode(c) * s[None, :]
 
 
@@ -178,7 +186,7 @@ def round_h(h: np.ndarray, mode: str) -> np.ndarray:
     """Rounding point R1 applied to SwiGLU outputs (rows = tokens)."""
     if mode == "f32":
         return h
-    if mode == "bf16":
+    if mode in ("bf16", "i8"):   # int8 weights: bf16 activations, h rounded like bf16
         return bf16_round(h.astype(np.float32))
     if mode == "e4m3":
         return quant_rows_e4m3(h.astype(np.float32))[0]

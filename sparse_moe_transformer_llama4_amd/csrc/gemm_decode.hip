@@ -530,6 +530,294 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------- int8 weights
+//
+// Weight-only int8 (codes q, one fp32 scale s per output column, weight =
+// q * s) on the same weight-streaming design, for all three GEMMs:
+//   * 256-byte weight rows per tile (down: 256 output columns; gate/up: 128
+//     gate + the matching 128 up columns), 32 K rows = 8 KB per stage, the
+//     same per-wave 4-deep ring and activation staging as the bf16 down
+//     tiles; 16-byte chunk c of LDS row r sits at c ^ (r & 15);
+//   * the 16x16x32 bf16 MFMA's B fragment comes from the 8-bit LDS transpose
+//     read: each group of 16 lanes reads an 8-row x 16-column block (lane s
+//     gives row s/2, columns 8 (s%2) .. +7) and lane s receives column s of
+//     the 8 rows, i.e. its 8 K values;
+//   * codes become bf16 exactly (|q| <= 127: at most 7 significant bits):
+//     int8 -> fp32, upper half;
+//   * the column scale multiplies the fp32 sums in the epilogue (exact
+//     algebra: sum_k x_k q_kn s_n = s_n sum_k x_k q_kn).
+constexpr int QBN = 256;               // int8 weight columns per tile
+constexpr int QBK = 32;                // K rows per stage
+constexpr int QWSTAGE = QBK * QBN;     // 8 KB of weights per stage
+constexpr int QINS = QWSTAGE / 1024;   // weight DMA instructions per stage per wave (8)
+constexpr int QFN = QBN / 16;          // weight fragments (16 columns each)
+constexpr int QPP = QBN + 16;          // floats per row of the partial-sum buffer (padded)
+
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// B fragment for tile columns col .. col+15 (col % 16 == 0): lane gets column
+// col + lane%16, K rows 8 (lane/16) .. +7 of the stage, as 8 int8 codes ...
+__device__ __forceinline__ i32x2 read_q_frag(const lds_u8* st, int col, int lane) {
+  const int s = lane & 15;
+  const int r = 8 * (lane >> 4) + (s >> 1);
+  const int pbyte = (((col >> 4) ^ (r & 15)) << 4) + 8 * (s & 1);
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(st + r * QBN + pbyte));
+}
+// ... and as bf16 (exact: int8 -> fp32 -> upper half)
+__device__ __forceinline__ bf16x8 q_to_bf16(i32x2 q) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int w = q[i >> 1];
+    const int sh = 16 * (i & 1);
+    const float lo = static_cast<float>(static_cast<int8_t>(w >> sh));
+    const float hi = static_cast<float>(static_cast<int8_t>(w >> (sh + 8)));
+    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  }
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+  const u32x4 v = {o[0], o[1], o[2], o[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int MODE, int FMMAX>
+__global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
+  constexpr bool GU = MODE == MODE_GATEUP;
+  constexpr int DBM = 16 * FMMAX;               // rows per tile
+  constexpr int ASTAGE = FMMAX * 1024;          // activation bytes per stage
+  constexpr int STAGE = QWSTAGE + ASTAGE;
+  constexpr int DNBUF = 4;
+  constexpr int LOADS = QINS + FMMAX;           // DMA instructions per stage per wave
+  constexpr int PART = 4 * DBM * QPP * 4;       // the four waves' partial sums
+  constexpr int RING = 4 * DNBUF * STAGE;
+  constexpr int SMEM = RING > PART + 8 * DBM ? RING : PART + 8 * DBM;   // + per-row tables after PART
+  constexpr int OUTC = GU ? QBN / 2 : QBN;      // output columns per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.E, T = p.T, K = p.K;
+
+  // ---- tile lookup: grid (row tile, column tile, K part), or (column tile,
+  // row tile) for tail launches.  Group E is the shared expert (GATEUP over
+  // the shared group alone, DOWN_SHARED) addressed without the tile table.
+  const int bi_m = p.tail_bm > 0 ? blockIdx.y : blockIdx.x;
+  const int bi_n = p.tail_bm > 0 ? blockIdx.x : blockIdx.y;
+  int g, m0;
+  if (MODE == MODE_DOWN_SHARED || (GU && p.group_lo == E)) {
+    g = E;
+    m0 = bi_m * DBM;
+    if (m0 >= T) return;
+  } else {
+    const int mt = bi_m + p.tiles[p.group_lo];
+    if (mt >= p.tiles[p.group_hi]) return;
+    int lo = p.group_lo, hi = p.group_hi - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    m0 = (mt - p.tiles[g]) * DBM;
+  }
+  const bool shared = g == E;
+  const int rows = shared ? T : p.offsets[g + 1] - p.offsets[g];
+  if (p.tail_bm > 0 && !shared) m0 += (rows / p.tail_bm) * p.tail_bm;   // tail launches
+  const int NH = (GU && shared) ? p.N_shared : p.N;   // output width of this GEMM
+  const int n0 = bi_n * OUTC;
+  if (n0 >= NH) return;
+  const int row_base = shared ? 0 : p.offsets[g];
+  const int ldb = GU ? 2 * NH : NH;                   // bytes per weight row
+  const int nvalid = min(DBM, rows - m0);
+  const int fm = (nvalid + 15) >> 4;                  // fragments with valid rows (uniform)
+
+  // per-row values loaded now so their latency hides behind the main loop:
+  // GATEUP routed rows: the token's gate; DOWN_ROUTED: the output row
+  float row_scale = 1.0f;
+  int row_out = 0;
+  if (tid < DBM) {
+    const int r = min(m0 + tid, rows - 1);
+    if (GU && !shared) row_scale = p.gate[p.perm[row_base + r]];
+    if (MODE == MODE_DOWN_ROUTED) row_out = p.perm[row_base + r];
+  }
+
+  // ---- this block's K range (DOWN_SHARED: split over blockIdx.z in
+  // 128-row units) and this wave's quarter of it
+  const int nsplit = gridDim.z;
+  const int units = K >> 7;
+  const int u0 = static_cast<int>(blockIdx.z) * units / nsplit;
+  const int u1 = (static_cast<int>(blockIdx.z) + 1) * units / nsplit;
+  const int ns = u1 - u0;                       // QBK-row stages per wave
+  const int k0 = u0 * 128 + wave * ns * QBK;
+
+  // weights: DMA instruction i fills K rows 4i .. 4i+3 of the stage; lane ->
+  // row 4i + lane/16, physical chunk lane%16 holding logical chunk
+  // c = (lane%16) ^ (row & 15) = 16 columns: down n0 + 16c; gate/up chunks
+  // 0..7 the gate columns n0 + 16c, 8..15 the up columns NH + n0 + 16 (c-8)
+  const uint8_t* wbase = static_cast<const uint8_t*>(shared ? p.B_shared : p.B) +
+                         (shared ? 0 : static_cast<int64_t>(g) * K * ldb);
+  int64_t w_off[QINS];
+#pragma unroll
+  for (int i = 0; i < QINS; ++i) {
+    const int kr = 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ (kr & 15);
+    const int oc = GU ? n0 + 16 * (c & 7) : n0 + 16 * c;       // output column of the chunk
+    const int gc = (GU && c >= 8) ? NH + oc : oc;              // weight column
+    w_off[i] = static_cast<int64_t>(k0 + kr) * ldb + (oc < NH ? gc : 0);
+  }
+  const int64_t w_kstride = static_cast<int64_t>(QBK) * ldb;
+
+  // activations: DMA instruction f fills rows 16f .. 16f+15 (64 B each) of
+  // the stage's activation block; lane -> row 16f + lane/4, slot lane%4,
+  // which holds logical chunk slot ^ ((row >> 1) & 3).  GATEUP reads x
+  // (routed rows gathered through perm), DOWN the h rows in group order.
+  const uint16_t* abase = static_cast<const uint16_t*>(shared ? p.A_shared : p.A);
+  int64_t a_off[FMMAX];
+#pragma unroll
+  for (int f = 0; f < FMMAX; ++f) {
+    const int r = min(m0 + 16 * f + (lane >> 2), rows - 1);
+    const int arow = (GU && !shared) ? p.perm[row_base + r] : row_base + r;
+    a_off[f] = static_cast<int64_t>(arow) * K + k0 + (((lane & 3) ^ ((lane >> 3) & 3)) * 8);
+  }
+
+  const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem)) +
+                        __builtin_amdgcn_readfirstlane(wave) * (DNBUF * STAGE);
+  const lds_u8* ring_p = (const lds_u8*)smem + wave * (DNBUF * STAGE);
+  const int a_rd = QWSTAGE + (lane & 15) * 64 + (((lane >> 4) ^ ((lane >> 1) & 3)) << 4);
+
+  f32x4 acc[FMMAX][QFN];
+#pragma unroll
+  for (int f = 0; f < FMMAX; ++f)
+#pragma unroll
+    for (int j = 0; j < QFN; ++j) acc[f][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#define Q8_ISSUE(st)                                                                           \
+  do {                                                                                         \
+    const int s_ = min((st), ns - 1);                                                          \
+    const uint32_t b_ = ring + static_cast<uint32_t>(((st) % DNBUF) * STAGE);                  \
+    _Pragma("unroll") for (int i = 0; i < QINS; ++i)                                           \
+      dma16_nt(wbase + w_off[i] + s_ * w_kstride, b_ + i * 1024);                              \
+    _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
+      dma16(abase + a_off[f] + s_ * QBK, b_ + QWSTAGE + f * 1024);                             \
+  } while (0)
+#define Q8_STEP(kt)                                                                            \
+  do {                                                                                         \
+    Q8_ISSUE((kt) + DNBUF - 1);                                                                \
+    wait_vmcnt<(DNBUF - 1) * LOADS>();                                                         \
+    const lds_u8* st_ = ring_p + ((kt) % DNBUF) * STAGE;                                       \
+    /* every LDS read of the stage in flight before the first use */                         \
+    i32x2 wq[QFN];                                                                             \
+    bf16x8 af[FMMAX];                                                                          \
+    _Pragma("unroll") for (int j = 0; j < QFN; ++j) wq[j] = read_q_frag(st_, j * 16, lane);    \
+    _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
+      af[f] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(st_ + a_rd + f * 1024); \
+    bf16x8 wf[QFN];                                                                            \
+    _Pragma("unroll") for (int j = 0; j < QFN; ++j) wf[j] = q_to_bf16(wq[j]);                  \
+    _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
+      if (f < fm)                                                                              \
+        _Pragma("unroll") for (int j = 0; j < QFN; ++j)                                        \
+          acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], wf[j], acc[f][j], 0, 0, 0); \
+    /* this stage's slot is refilled DNBUF-1 steps later: reads must be done */                \
+    __builtin_amdgcn_s_waitcnt(0xC07F);                                                        \
+  } while (0)
+
+#pragma unroll
+  for (int st = 0; st < DNBUF - 1; ++st) Q8_ISSUE(st);
+  for (int kt = 0; kt < ns; ++kt) Q8_STEP(kt);
+  wait_vmcnt<0>();
+#undef Q8_ISSUE
+#undef Q8_STEP
+
+  // ---- the four K-quarter partial sums through LDS ([row][QPP] fp32 per wave)
+  __syncthreads();
+  float* part = reinterpret_cast<float*>(smem);
+  const int lcol = lane & 15, rq = 4 * (lane >> 4);
+#pragma unroll
+  for (int f = 0; f < FMMAX; ++f) {
+    if (f < fm) {
+#pragma unroll
+      for (int j = 0; j < QFN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          part[(wave * DBM + 16 * f + rq + q) * QPP + j * 16 + lcol] = acc[f][j][q];
+    }
+  }
+  float* tab = reinterpret_cast<float*>(smem + PART);          // [DBM] gate scales
+  int* ot = reinterpret_cast<int*>(smem + PART + 4 * DBM);     // [DBM] output rows
+  if (tid < DBM) {
+    tab[tid] = row_scale;
+    ot[tid] = row_out;
+  }
+  __syncthreads();
+  auto total = [&](int r, int c) -> float {
+    return ((part[(0 * DBM + r) * QPP + c] + part[(1 * DBM + r) * QPP + c]) + part[(2 * DBM + r) * QPP + c]) +
+           part[(3 * DBM + r) * QPP + c];
+  };
+  const float* sbase = shared ? p.sB_shared : p.sB + static_cast<int64_t>(g) * ldb;
+
+  if constexpr (GU) {
+    // SwiGLU: h = SiLU(s_g acc_g t) * (s_u acc_u t), t = the token's gate on
+    // routed rows (1 on shared rows); thread -> one output column, rows in turn
+    const int c = tid % OUTC;
+    const int col = n0 + c;
+    const float sg = col < NH ? sbase[col] : 0.f;
+    const float su = col < NH ? sbase[NH + col] : 0.f;
+    uint16_t* C = static_cast<uint16_t*>(shared ? p.C_shared : p.C);
+    constexpr int NIT = DBM * OUTC / 256;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int r = (tid + 256 * it) / OUTC;
+      if (r >= nvalid || col >= NH) continue;
+      const float t = tab[r];
+      const float gv = total(r, c) * sg * t;
+      const float uv = total(r, c + OUTC) * su * t;
+      C[static_cast<int64_t>(row_base + m0 + r) * NH + col] = f32_to_bf16(silu_f(gv) * uv);
+    }
+  } else {
+    // down: thread -> one output column (tile column tid), rows in turn
+    const int c = tid;
+    const int col = n0 + c;
+    const float sc = col < NH ? sbase[col] : 0.f;
+    constexpr int NIT = DBM;
+    if constexpr (MODE == MODE_DOWN_SHARED) {
+      float* Cs = static_cast<float*>(p.C_shared) + static_cast<int64_t>(blockIdx.z) * T * NH;
+#pragma unroll 4
+      for (int r = 0; r < NIT; ++r)
+        if (r < nvalid && col < NH) Cs[static_cast<int64_t>(m0 + r) * NH + col] = total(r, c) * sc;
+    } else {
+      // the shared expert's output, y_parts K-split partials summed in order
+      const int nparts = !p.Y ? 0 : p.y_parts > 1 ? p.y_parts : 1;
+      const int64_t pstride = static_cast<int64_t>(T) * NH;
+#pragma unroll 4
+      for (int r = 0; r < NIT; ++r) {
+        if (r >= nvalid || col >= NH) continue;
+        const int64_t o = static_cast<int64_t>(ot[r]) * NH + col;
+        float y = 0.f;
+        for (int q = 0; q < nparts; ++q) y += p.Y[q * pstride + o];
+        const float v = nparts ? total(r, c) * sc + y : total(r, c) * sc;
+        if (p.out_bf16) static_cast<uint16_t*>(p.C)[o] = f32_to_bf16(v);
+        else static_cast<float*>(p.C)[o] = v;
+      }
+    }
+  }
+}
+
+template <int MODE, int FMMAX>
+hipError_t launch_q8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* tiles_all) {
+  constexpr int DBM = 16 * FMMAX;
+  GemmArgs a = a0;
+  a.tiles = tiles_all + bm_index(DBM) * (a.E + 2);
+  const int mt_tok = (T + DBM - 1) / DBM;
+  const bool shared_only = MODE == MODE_DOWN_SHARED || (MODE == MODE_GATEUP && a.group_lo == a.E);
+  if (MODE == MODE_GATEUP && !shared_only && a.group_hi > a.E) return hipErrorInvalidValue;   // one kind per launch
+  const int gm = shared_only ? mt_tok : mt_tok + a.E;
+  const int NH = (MODE == MODE_GATEUP && shared_only) ? a.N_shared : a.N;
+  const int gn = (NH + (MODE == MODE_GATEUP ? QBN / 2 : QBN) - 1) / (MODE == MODE_GATEUP ? QBN / 2 : QBN);
+  if (gm <= 0 || gn <= 0) return hipSuccess;
+  const int ks = (MODE == MODE_DOWN_SHARED && a.ksplit > 1) ? a.ksplit : 1;
+  if (a.K % 128 != 0 || a.K / 128 < ks || NH % 16 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_q8_kernel<MODE, FMMAX>), dim3(gm, gn, ks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int MODE, int FMMAX>
 hipError_t launch_dec(const GemmArgs& a0, int T, hipStream_t s, const int32_t* tiles_all) {
   constexpr int DBM = 16 * FMMAX;
@@ -600,6 +888,23 @@ hipError_t launch_gemm_decode_tail(int mode, const GemmArgs& a0, int bm_main, hi
 // rows32: 32-row tiles (for groups that may exceed 16 rows), else 16-row tiles.
 hipError_t launch_gemm_decode(int mode, bool rows32, const GemmArgs& a, int T, hipStream_t s,
                               const int32_t* tiles_all) {
+  if (a.w_int8) {
+    if (a.gu_part) return hipErrorInvalidValue;
+    if (rows32) {
+      switch (mode) {
+        case MODE_GATEUP: return launch_q8<MODE_GATEUP, 2>(a, T, s, tiles_all);
+        case MODE_DOWN_SHARED: return launch_q8<MODE_DOWN_SHARED, 2>(a, T, s, tiles_all);
+        case MODE_DOWN_ROUTED: return launch_q8<MODE_DOWN_ROUTED, 2>(a, T, s, tiles_all);
+      }
+    } else {
+      switch (mode) {
+        case MODE_GATEUP: return launch_q8<MODE_GATEUP, 1>(a, T, s, tiles_all);
+        case MODE_DOWN_SHARED: return launch_q8<MODE_DOWN_SHARED, 1>(a, T, s, tiles_all);
+        case MODE_DOWN_ROUTED: return launch_q8<MODE_DOWN_ROUTED, 1>(a, T, s, tiles_all);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   if (rows32) {
     switch (mode) {
       case MODE_GATEUP: return launch_dec_gateup<2>(a, T, s, tiles_all);

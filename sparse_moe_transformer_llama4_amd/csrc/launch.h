@@ -62,6 +62,8 @@ struct GemmArgs {
   int tail_bm;             // weight-streaming tail launches: rows of the groups' full main tiles (0 = none)
   float* gu_part;          // weight-streaming GATEUP: write fp32 pre-activation partials [ksplit][T][2 N] here
                            // instead of h (K split over ksplit workgroups; null = normal epilogue)
+  int w_int8;              // weight-streaming kernels: B / B_shared hold int8 codes, sB / sB_shared their fp32
+                           // column scales (a GATEUP launch covers the routed groups or the shared one, not both)
 };
 
 // Router in two launches: partial logits over K slices of d (the slice count

@@ -46,10 +46,14 @@ bool config_dtypes_ok(const moe_config& c) {
   if (c.x_dtype == MOE_BF16 && c.w_dtype == MOE_BF16 && (c.out_dtype == MOE_F32 || c.out_dtype == MOE_BF16))
     return true;
   if (c.x_dtype == MOE_BF16 && c.w_dtype == MOE_E4M3 && c.out_dtype == MOE_BF16) return true;
+  if (c.x_dtype == MOE_BF16 && c.w_dtype == MOE_INT8 && (c.out_dtype == MOE_F32 || c.out_dtype == MOE_BF16))
+    return true;
   return false;
 }
 
-int k_multiple(const moe_config& c) { return c.w_dtype == MOE_E4M3 ? 128 : 64; }
+bool scaled_weights(const moe_config& c) { return c.w_dtype == MOE_E4M3 || c.w_dtype == MOE_INT8; }
+
+int k_multiple(const moe_config& c) { return scaled_weights(c) ? 128 : 64; }
 
 constexpr int64_t kDecodeTokensMax = 64;
 // Token count from which the bf16 prefill tiling is used.
@@ -59,16 +63,17 @@ constexpr int64_t kPrefillTokens = 256;
 // would leave most CUs idle): the number of partial shared outputs, summed in
 // order by the routed down GEMM.  1 for every other path.
 int decode_y_parts(const moe_config& c, int64_t T) {
-  if (T > kDecodeTokensMax || c.w_dtype != MOE_BF16) return 1;
+  if (T > kDecodeTokensMax || (c.w_dtype != MOE_BF16 && c.w_dtype != MOE_INT8)) return 1;
   for (int s = 8; s > 1; s >>= 1)
     if (c.f_shared % (128 * s) == 0) return s;
   return 1;
 }
 
-// The weight-streaming decode tiling serves bf16 calls of at most 64 tokens.
+// The weight-streaming decode tiling serves bf16 calls of at most 64 tokens
+// and every int8 call (a plan with int8 weights takes at most 64 tokens).
 bool use_decode(const moe_config& c, int64_t T) {
-  return c.w_dtype == MOE_BF16 && T > 0 && T <= kDecodeTokensMax && decode_supported(c.d) &&
-         decode_supported(c.f) && decode_supported(c.f_shared);
+  return (c.w_dtype == MOE_BF16 || c.w_dtype == MOE_INT8) && T > 0 && T <= kDecodeTokensMax &&
+         decode_supported(c.d) && decode_supported(c.f) && decode_supported(c.f_shared);
 }
 
 // A dense layer's gate/up GEMM at decode sizes has one row tile per 128
@@ -104,7 +109,7 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   const size_t t = static_cast<size_t>(T);
   const size_t nb = (t + kRouteTokens - 1) / kRouteTokens;
   const bool fp8 = c.w_dtype == MOE_E4M3;
-  const size_t hsz = c.w_dtype == MOE_BF16 ? 2 : 4;  // e4m3: fp32 staging before quantisation
+  const size_t hsz = (c.w_dtype == MOE_BF16 || c.w_dtype == MOE_INT8) ? 2 : 4;  // e4m3: fp32 staging
   L.idx = take(t * 4);
   L.gate = take(t * 4);
   L.counts = take(E * 4);
@@ -157,7 +162,7 @@ moe_status check_expert_weights(const moe_config& c, const moe_weights* w) {
   const void* req[] = {w->ws_gate_up, w->ws_down, w->w_gate_up, w->w_down};
   for (int i = 0; i < (c.n_experts > 0 ? 4 : 2); ++i)    // a dense layer has no routed experts
     if (!req[i] || !aligned16(req[i])) return MOE_ERR_INVALID_ARGUMENT;
-  if (c.w_dtype == MOE_E4M3) {
+  if (scaled_weights(c)) {
     const void* sc[] = {w->s_gate_up, w->s_down, w->ss_gate_up, w->ss_down};
     for (const void* p : sc)
       if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
@@ -252,8 +257,9 @@ hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_we
 
 GemmArgs gateup_args(const moe_config& c, const moe_weights* w, uint8_t* ws, const WsLayout& L, const Route& R,
                      const void* a_x, float* sx, uint32_t* amax_r, uint32_t* amax_s, int T) {
-  const bool fp8 = c.w_dtype == MOE_E4M3;
+  const bool fp8 = scaled_weights(c);
   GemmArgs g{};
+  g.w_int8 = c.w_dtype == MOE_INT8;
   g.A = a_x;
   g.A_shared = a_x;
   g.B = w->w_gate_up;
@@ -279,8 +285,9 @@ GemmArgs gateup_args(const moe_config& c, const moe_weights* w, uint8_t* ws, con
 
 GemmArgs down_shared_args(const moe_config& c, const moe_weights* w, uint8_t* ws, const WsLayout& L,
                           const Route& R, const void* h_s, const float* sh_s, int T, int ksplit) {
-  const bool fp8 = c.w_dtype == MOE_E4M3;
+  const bool fp8 = scaled_weights(c);
   GemmArgs g{};
+  g.w_int8 = c.w_dtype == MOE_INT8;
   g.A_shared = h_s;
   g.B_shared = w->ws_down;
   g.sB_shared = fp8 ? w->ss_down : nullptr;
@@ -299,8 +306,9 @@ GemmArgs down_shared_args(const moe_config& c, const moe_weights* w, uint8_t* ws
 
 GemmArgs down_routed_args(const moe_config& c, const moe_weights* w, uint8_t* ws, const WsLayout& L,
                           const Route& R, const void* h_r, const float* sh_r, void* out, int T, int y_parts) {
-  const bool fp8 = c.w_dtype == MOE_E4M3;
+  const bool fp8 = scaled_weights(c);
   GemmArgs g{};
+  g.w_int8 = c.w_dtype == MOE_INT8;
   g.A = h_r;
   g.B = w->w_down;
   g.sB = fp8 ? w->s_down : nullptr;
@@ -558,6 +566,8 @@ moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
     const int km = k_multiple(c);
     if (c.d <= 0 || c.f <= 0 || c.f_shared <= 0 || c.d % km || c.f % km || c.f_shared % km)
       return MOE_ERR_UNSUPPORTED;
+    // int8 weights are a decode format: the weight-streaming tiles only
+    if (c.w_dtype == MOE_INT8 && c.max_tokens > kDecodeTokensMax) return MOE_ERR_SHAPE;
   }
   moe_plan_s* p = new (std::nothrow) moe_plan_s;
   if (!p) return MOE_ERR_INVALID_ARGUMENT;
@@ -703,6 +713,16 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     g1.group_lo = 0;
     g1.group_hi = c.n_experts + 1;
     if ((e = launch_gemm_fp8(MODE_GATEUP, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
+  } else if (dec && c.w_dtype == MOE_INT8) {
+    // int8 tiles: the routed groups, then the shared expert
+    g1.group_lo = 0;
+    g1.group_hi = c.n_experts;
+    if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles)) != hipSuccess)
+      return hip_fail(plan, e);
+    g1.group_lo = c.n_experts;
+    g1.group_hi = c.n_experts + 1;
+    if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles)) != hipSuccess)
+      return hip_fail(plan, e);
   } else if (dec) {
     // routed groups and the shared expert in one launch of 32-row tiles
     g1.group_lo = 0;

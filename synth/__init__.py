@@ -21,7 +21,8 @@ Generator (counter-based, identical on CPU and GPU):
 
 fp8 weights (OCP e4m3fn) are drawn in fp32 the same way and quantised per
 output column of the [K, N] layout: scale = amax over K / 448 (fp32), code =
-torch's float8_e4m3fn cast of clamp(w / scale, -448, 448).
+torch's float8_e4m3fn cast of clamp(w / scale, -448, 448).  int8 weights
+likewise: scale = amax over K / 127, code = round-half-even(w / scale).
 
 Workloads with the RMSNorm in front of the block (norm_eps set) also draw its
 gain, w[j] = 1 + 0.1 * Q (fp32, then rounded to x's dtype), and give every
@@ -43,7 +44,7 @@ __all__ = [
     "gen_shared", "gen_norm_weight", "make_inputs", "DTYPES",
 ]
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn, "i8": torch.int8}
 
 # ---------------------------------------------------------------- configs
 
@@ -58,7 +59,7 @@ class MoEShape:
     f: int                 # routed SwiGLU width
     fs: int                # shared SwiGLU width
     x_dtype: str = "bf16"  # activations and router weight dtype
-    w_dtype: str = "bf16"  # expert / shared weight dtype ("e4m3" = fp8 + fp32 scales)
+    w_dtype: str = "bf16"  # expert / shared weight dtype ("e4m3" = fp8, "i8" = int8, + fp32 scales)
     out_dtype: str = "f32"
     bias: str = "none"     # "none" | "cold" (4 experts at -30) | "zipf"
     n_cold: int = 4
@@ -101,6 +102,10 @@ EXTRA_CONFIGS = {
     # the MoE layer with the RMSNorm that precedes it (eps 1e-5)
     "scout_prefill_bf16_rmsnorm": MoEShape("scout_prefill_bf16_rmsnorm", T=4096, d=5120, E=16, f=8192,
                                            fs=8192, seed=7, norm_eps=1e-5),
+    # weight-only int8 decode on the Scout-shaped layer (the bf16 decode
+    # workload's seed and routing)
+    "scout_decode_int8": MoEShape("scout_decode_int8", T=32, d=5120, E=16, f=8192, fs=8192, w_dtype="i8",
+                                  bias="cold", seed=2),
     "maverick_prefill_fp8_rmsnorm": MoEShape("maverick_prefill_fp8_rmsnorm", T=16384, d=5120, E=128,
                                              f=8192, fs=8192, w_dtype="e4m3", out_dtype="bf16", seed=8,
                                              norm_eps=1e-5),
@@ -299,10 +304,22 @@ def gen_bias(cfg: MoEShape) -> Optional[torch.Tensor]:
     return torch.tensor(b, dtype=torch.float64).to(torch.float32)
 
 
+def _quant_cols_int8(w32: torch.Tensor):
+    """[K, N] fp32 -> (int8 codes [K, N] in -127..127, fp32 scale [N]):
+    scale = amax over K / 127, code = round-half-even(w / scale)."""
+    amax = w32.abs().amax(dim=0)
+    scale = amax / torch.tensor(127.0, dtype=torch.float32, device=w32.device)
+    scale = torch.where(amax > 0, scale, torch.ones_like(scale))
+    q = torch.round(w32 / scale).clamp_(-127.0, 127.0).to(torch.int8)
+    return q, scale
+
+
 def _gen_matrix(cfg: MoEShape, stream: str, expert: int, K: int, N: int, device):
     v = normal_fp32(stream_key(cfg.seed, stream, expert), 0, K * N, cfg.w_std, device).view(K, N)
     if cfg.w_dtype == "e4m3":
         return _quant_cols_e4m3(v)
+    if cfg.w_dtype == "i8":
+        return _quant_cols_int8(v)
     return _round_to(v, cfg.w_dtype), None
 
 
@@ -332,6 +349,7 @@ def make_inputs(cfg: MoEShape, device="cpu") -> dict:
     """
     dev = torch.device(device)
     wdt = torch.uint8 if cfg.w_dtype == "e4m3" else DTYPES[cfg.w_dtype]
+    scaled = cfg.w_dtype in ("e4m3", "i8")
     E, d, f, fs = cfg.E, cfg.d, cfg.f, cfg.fs
     if E == 0:   # a dense layer: the shared gated MLP alone
         wsgu, ssgu, wsd, ssd = gen_shared(cfg, dev)
@@ -348,7 +366,7 @@ def make_inputs(cfg: MoEShape, device="cpu") -> dict:
         "s_gate_up": None, "s_down": None, "ss_gate_up": None, "ss_down": None,
         "norm_weight": gen_norm_weight(cfg, dev),
     }
-    if cfg.w_dtype == "e4m3":
+    if scaled:
         out["s_gate_up"] = torch.empty((E, 2 * f), dtype=torch.float32, device=dev)
         out["s_down"] = torch.empty((E, d), dtype=torch.float32, device=dev)
     for e in range(E):

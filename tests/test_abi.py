@@ -62,6 +62,14 @@ def _plan(**kw):
     ({"abi_version": 3}, INVALID),
     ({"has_router_bias": 3}, INVALID),
     ({"max_tokens": 0}, SHAPE),
+    # weight-only int8: decode sizes, widths % 128, bf16 activations
+    ({"w_dtype": 3}, OK),
+    ({"w_dtype": 3, "out_dtype": 1}, OK),
+    ({"w_dtype": 3, "max_tokens": 65}, SHAPE),
+    ({"w_dtype": 3, "d": 192}, UNSUPPORTED),
+    ({"w_dtype": 3, "x_dtype": 0, "out_dtype": 0}, UNSUPPORTED),
+    ({"w_dtype": 3, "n_experts": 0, "f": 0}, UNSUPPORTED),
+    ({"w_dtype": 4}, UNSUPPORTED),
     # the RMSNorm in front of the block
     ({"has_norm": 1, "norm_eps": 1e-5}, OK),
     ({"has_norm": 1, "norm_eps": 0.0, "x_dtype": 0, "w_dtype": 0, "out_dtype": 0}, OK),
@@ -151,6 +159,19 @@ def test_dense_layer_rejects_before_enqueue():
     bad = moe._Weights(None, None, None, None, None, None, P, None, None, None)
     assert lib.moe_forward(h, P, 64, ctypes.byref(bad), P, None, P, n.value, None) == INVALID
     assert lib.moe_forward(h, P, 65, ctypes.byref(w), P, None, P, n.value, None) == SHAPE
+    lib.moe_plan_destroy(h)
+
+
+@pytest.mark.parametrize("wdt,odt", [(2, 1), (3, 0)])
+def test_scaled_weights_require_scales(wdt, odt):
+    lib = moe.load_library()
+    st, h = _plan(w_dtype=wdt, out_dtype=odt, max_tokens=8)
+    assert st == OK
+    n = ctypes.c_size_t()
+    lib.moe_workspace_size(h, 8, ctypes.byref(n))
+    P = 0x10000
+    w = _weights(P)
+    assert lib.moe_forward(h, P, 8, ctypes.byref(w), P, None, P, n.value, None) == INVALID
     lib.moe_plan_destroy(h)
 
 

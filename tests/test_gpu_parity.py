@@ -332,3 +332,63 @@ def test_rmsnorm_route_only_and_timed_variant(gpu):
     assert torch.equal(out, out_t)
     ms = ev.durations_ms()
     assert all(v >= 0 for v in ms) and ms[0] > 0
+
+
+# ------------------------------------------------------------ weight-only int8 (decode)
+
+def _int8(name="decode_like_bf16", **kw):
+    return dataclasses.replace(synth.get_config(name), w_dtype="i8", name=f"{name}_i8", **kw)
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 31, 32, 33, 64])
+def test_int8_decode_matches_oracle(gpu, T):
+    cfg = _int8(T=T)
+    print(f"[parity] int8 decode T={T}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    err, _ = check_forward(cfg, inp, out, routing)
+    print(f"[parity] int8 decode T={T} max|err|/RMS = {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("over", [dict(out_dtype="bf16"), dict(d=640, f=384, fs=896, T=40),
+                                  dict(norm_eps=1e-5, T=24)])
+def test_int8_decode_shapes_and_options(gpu, over):
+    # bf16 output; widths that leave partial 256-column tiles (d = 640) and
+    # 128-column gate/up tiles (f = 384, fs = 896); the RMSNorm in front
+    cfg = _int8(**over)
+    print(f"[parity] int8 {over}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    check_forward(cfg, inp, out, routing)
+
+
+def test_int8_one_hot_and_idle_scales_nan(gpu):
+    # 40 tokens to one expert (three 16-row down tiles of one group); every
+    # other expert's codes random and scales NaN: nothing of theirs is read
+    cfg = _int8(T=40, bias="cold", n_cold=0)
+    inp = synth.make_inputs(cfg)
+    inp["router_bias"] = torch.full((cfg.E,), -60.0)
+    inp["router_bias"][3] = 60.0
+    g = to_device(inp, gpu)
+    for e in range(cfg.E):
+        if e != 3:
+            g["s_gate_up"][e].fill_(float("nan")); g["s_down"][e].fill_(float("nan"))
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    assert int(routing["counts"][3]) == cfg.T
+    check_forward(cfg, inp, out, routing)
+
+
+def test_int8_side_stream_matches_serial_schedule(gpu):
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = _int8(T=33)
+    p = _plan(cfg)
+    w = to_device(synth.make_inputs(cfg), gpu)
+    ws = torch.empty(moe.moe_workspace_size(p, cfg.T), dtype=torch.uint8, device=gpu)
+    out = moe.moe_forward(p, w["x"], w, workspace=ws)
+    ev = moe.StageEvents()
+    out_t = torch.empty_like(out)
+    moe.moe_forward_timed(p, w["x"], w, ev, out=out_t, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_t)

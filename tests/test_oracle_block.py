@@ -13,7 +13,7 @@ import synth
 def _tiny(T, d, E, f, fs, mode, seed, bias=None):
     cfg = synth.MoEShape("t", T=T, d=d, E=E, f=f, fs=fs,
                          x_dtype="f32" if mode == "f32" else "bf16",
-                         w_dtype={"f32": "f32", "bf16": "bf16", "e4m3": "e4m3"}[mode],
+                         w_dtype={"f32": "f32", "bf16": "bf16", "e4m3": "e4m3", "i8": "i8"}[mode],
                          out_dtype="f32", seed=seed, w_std=0.3)
     inp = synth.make_inputs(cfg)
     if bias is not None:
@@ -26,17 +26,23 @@ def _lists(inp, E):
     ex = [w.expert(e) for e in range(E)]
     sh = w.shared()
     L = lambda a: a.tolist()
+
+    def deq(a, s):
+        # int8 codes dequantised here with torch (not through oracle.block)
+        if s is not None and a.dtype == torch.int8:
+            return (a.double() * s.double()[None, :]).numpy()
+        return block.weight_f64(a, s)
     return dict(
         x=L(block.to_f64(inp["x"])), wr=L(block.to_f64(inp["w_router"])),
         bias=None if inp["router_bias"] is None else L(block.to_f64(inp["router_bias"])),
-        w_gate_up=[L(block.weight_f64(a, s)) for a, s, _, _ in ex],
-        w_down=[L(block.weight_f64(c, sd)) for _, _, c, sd in ex],
-        ws_gate_up=L(block.weight_f64(sh[0], sh[1])), ws_down=L(block.weight_f64(sh[2], sh[3])))
+        w_gate_up=[L(deq(a, s)) for a, s, _, _ in ex],
+        w_down=[L(deq(c, sd)) for _, _, c, sd in ex],
+        ws_gate_up=L(deq(sh[0], sh[1])), ws_down=L(deq(sh[2], sh[3])))
 
 
 CASES = [(0, 8, 4, 8, 8, "f32"), (1, 8, 1, 4, 4, "f32"), (7, 16, 3, 8, 4, "f32"),
          (16, 8, 5, 4, 8, "f32"), (9, 16, 4, 8, 8, "bf16"), (12, 16, 2, 8, 16, "bf16"),
-         (8, 16, 4, 8, 8, "e4m3"), (11, 8, 3, 4, 8, "e4m3")]
+         (8, 16, 4, 8, 8, "e4m3"), (11, 8, 3, 4, 8, "e4m3"), (10, 16, 4, 8, 8, "i8"), (6, 8, 2, 4, 16, "i8")]
 
 
 @pytest.mark.parametrize("T,d,E,f,fs,mode", CASES)
@@ -301,3 +307,15 @@ def test_rmsnorm_brute_force_and_bf16_rounding():
         # exact values are irrational: no float32-level tie, so brute's
         # float32-then-bf16 route equals a single rounding here
         assert got[t].tolist() == [brute._bf16(v) for v in exact]
+
+
+def test_int8_weights_dequantise_to_code_times_column_scale():
+    codes = torch.tensor([[-127, 0, 5], [127, -1, 64]], dtype=torch.int8)
+    scale = torch.tensor([0.5, 2.0, 0.125], dtype=torch.float32)
+    got = block.dequant_cols(codes, scale)
+    np.testing.assert_array_equal(got, [[-63.5, 0.0, 0.625], [63.5, -2.0, 8.0]])
+    # e4m3 codes (uint8) of the same bits decode differently: the dtype decides
+    e4 = block.dequant_cols(codes.view(torch.uint8), torch.ones(3))
+    assert not np.array_equal(e4, codes.double().numpy())
+    with pytest.raises(TypeError):
+        block.dequant_cols(codes.to(torch.int16), scale)

@@ -94,3 +94,13 @@ def test_configs_are_the_five_workloads():
         (64, 256, 4, 512, 512), (4096, 5120, 16, 8192, 8192), (32, 5120, 16, 8192, 8192),
         (8192, 5120, 128, 8192, 8192), (16384, 5120, 128, 8192, 8192)]
     assert c["maverick_prefill_fp8"].w_dtype == "e4m3" and c["maverick_prefill_fp8"].out_dtype == "bf16"
+
+
+def test_int8_weights_round_trip_within_half_a_step():
+    cfg = synth.MoEShape("q8", T=4, d=256, E=2, f=128, fs=128, w_dtype="i8", seed=9)
+    inp = synth.make_inputs(cfg)
+    assert inp["w_gate_up"].dtype == torch.int8 and inp["s_gate_up"].shape == (2, 256)
+    w32 = synth.normal_fp32(synth.stream_key(cfg.seed, "w_gate_up", 1), 0, 256 * 256, cfg.w_std).view(256, 256)
+    q, s = inp["w_gate_up"][1].double(), inp["s_gate_up"][1].double()
+    assert (q.abs() <= 127).all() and (q.abs().amax(dim=0) == 127).all()     # each column reaches +-127
+    assert ((q * s - w32.double()).abs() <= s / 2 * (1 + 1e-6)).all()
