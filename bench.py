@@ -31,13 +31,15 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"bf16": 2516.6e12, "e4m3": 5033.2e12, "f32": 157.3e12}   # dense MFMA, FLOP/s
+# dense MFMA peak by weight dtype, FLOP/s (int8 weights are converted to
+# bf16 and multiplied on the bf16 MFMA)
+PEAK = {"bf16": 2516.6e12, "e4m3": 5033.2e12, "f32": 157.3e12, "i8": 2516.6e12}
 HBM_PEAK = 8.0e12                                                 # bytes/s
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def esize(dt: str) -> int:
-    return {"f32": 4, "bf16": 2, "e4m3": 1}[dt]
+    return {"f32": 4, "bf16": 2, "e4m3": 1, "i8": 1}[dt]
 
 
 def stage_work(cfg, counts):
@@ -47,7 +49,7 @@ def stage_work(cfg, counts):
     hb = 4 if cfg.w_dtype == "f32" else 2
     ob = esize(cfg.out_dtype)
     touched = sum(1 for c in counts if c > 0)
-    sc = 4 if cfg.w_dtype == "e4m3" else 0     # fp32 column scales per weight column
+    sc = 4 if cfg.w_dtype in ("e4m3", "i8") else 0     # fp32 column scales per weight column
     xin = 1 if cfg.w_dtype == "e4m3" else xb   # gate/up reads the e4m3 copy of x
     # RMSNorm in front of the block: x read, the normalised rows written (and
     # their e4m3 codes + scales for e4m3 weights), the gain read
@@ -68,7 +70,7 @@ def block_work(cfg, counts):
     """Whole-block algorithmic FLOPs and bytes (touched weights + x + out)."""
     T, d, E, f, fs = cfg.T, cfg.d, cfg.E, cfg.f, cfg.fs
     wb = esize(cfg.w_dtype)
-    sc = 4 if cfg.w_dtype == "e4m3" else 0
+    sc = 4 if cfg.w_dtype in ("e4m3", "i8") else 0
     touched = sum(1 for c in counts if c > 0)
     flops = 2 * T * (d * E + 3 * d * f + 3 * d * fs)
     byts = (touched * (3 * d * f * wb + (2 * f + d) * sc) + 3 * d * fs * wb + (2 * fs + d) * sc
@@ -117,6 +119,8 @@ def main():
     ap.add_argument("--config", default="scout_prefill_bf16")
     ap.add_argument("--cpu-sample", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the core-clock sampling bursts (for profiler runs that count calls)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (reference for rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE scaling) and exit")
@@ -189,7 +193,7 @@ def main():
         for _ in range(8):
             moe.moe_forward(plan, g["x"], g, out=out, routing=routing, workspace=ws)
         _t.cuda.synchronize()
-    clock_mhz = sample_clock_mhz(_burst)
+    clock_mhz = None if args.no_clock else sample_clock_mhz(_burst)
 
     per_stage = [ev.durations_ms() for ev in events]
     avg = [sum(s[i] for s in per_stage) / len(per_stage) for i in range(moe.MOE_NUM_STAGES)]
