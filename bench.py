@@ -45,6 +45,7 @@ def esize(dt: str) -> int:
 def stage_work(cfg, counts):
     """Algorithmic (FLOPs, bytes) per launch of each stage."""
     T, d, E, f, fs = cfg.T, cfg.d, cfg.E, cfg.f, cfg.fs
+    Tr = T * cfg.top_k                          # routed rows: k picks per token
     xb, wb = esize(cfg.x_dtype), esize(cfg.w_dtype)
     hb = 4 if cfg.w_dtype == "f32" else 2
     ob = esize(cfg.out_dtype)
@@ -58,11 +59,12 @@ def stage_work(cfg, counts):
         norm = 2 * T * d * xb + d * xb + ((T * d + 4 * T) if cfg.w_dtype == "e4m3" else 0)
     return {
         "route": (2 * T * d * E, T * d * xb + d * E * xb + (4 * E if cfg.has_bias else 0) + T * 8 + norm),
-        "gate_up": (4 * T * d * (f + fs),
+        "gate_up": (4 * d * (Tr * f + T * fs),
                     touched * (d * 2 * f * wb + 2 * f * sc) + d * 2 * fs * wb + 2 * fs * sc
-                    + T * d * xin + T * (f + fs) * hb),
+                    + T * d * xin + (Tr * f + T * fs) * hb),
         "down_shared": (2 * T * fs * d, fs * d * wb + d * sc + T * fs * hb + T * d * 4),
-        "down_routed": (2 * T * f * d, touched * (f * d * wb + d * sc) + T * f * hb + T * d * 4 + T * d * ob),
+        "down_routed": (2 * Tr * f * d, touched * (f * d * wb + d * sc) + Tr * f * hb + T * d * 4 + T * d * ob
+                        + (2 * Tr * d * 4 if cfg.top_k > 1 else 0)),
     }
 
 
@@ -72,7 +74,7 @@ def block_work(cfg, counts):
     wb = esize(cfg.w_dtype)
     sc = 4 if cfg.w_dtype in ("e4m3", "i8") else 0
     touched = sum(1 for c in counts if c > 0)
-    flops = 2 * T * (d * E + 3 * d * f + 3 * d * fs)
+    flops = 2 * T * (d * E + 3 * d * f * cfg.top_k + 3 * d * fs)
     byts = (touched * (3 * d * f * wb + (2 * f + d) * sc) + 3 * d * fs * wb + (2 * fs + d) * sc
             + d * E * esize(cfg.x_dtype) + T * d * esize(cfg.x_dtype) + T * d * esize(cfg.out_dtype))
     return flops, byts
@@ -103,7 +105,7 @@ def cpu_baseline(cfg, g, sample):
         out = block.dense(xs, w, cfg.fs, cfg.w_dtype)
         what = "dense gated MLP"
     else:
-        out, r = block.forward(xs, w, cfg.f, cfg.fs, cfg.w_dtype)
+        out, r = block.forward(xs, w, cfg.f, cfg.fs, cfg.w_dtype, top_k=cfg.top_k)
         what = (f"routing + every touched expert + shared), {int(np.count_nonzero(r.counts))} experts touched")
     dt = time.perf_counter() - t0
     norm = "RMSNorm + " if nw is not None else ""
@@ -241,7 +243,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "f": cfg.f, "f_shared": cfg.fs,
                    "x_dtype": cfg.x_dtype, "w_dtype": cfg.w_dtype, "out_dtype": cfg.out_dtype,
                    "routing": cfg.bias, "experts_touched": sum(1 for c in counts if c > 0),
-                   "rmsnorm_eps": cfg.norm_eps},
+                   "rmsnorm_eps": cfg.norm_eps, "top_k": cfg.top_k},
         "block_tflops": F / t / 1e12,
         "block_gbps": B / t / 1e9,
         "mfma_frac": F / t / peak_f,

@@ -30,6 +30,14 @@ Steps, in the order the pages give them:
 6. Combine: out = shared(x) + routed (superteams.ai routing sketch; the
    other experts contribute nothing).
 
+With k experts per token (torchtune llama4_decoder, Parameters:
+experts_per_token, whose docstring names 2 as its default; Llama 4 itself
+uses 1) steps 2-4 run for each of the token's k largest logits (lower
+expert index first among equal logits), each pick with the sigmoid of its
+own logit as the gate on its input, and step 6 adds the k routed outputs to
+the shared one.  No softmax or renormalisation over the picks: the plain
+generalisation of the top-1 gate.
+
 Optional step 0, the RMSNorm in front of the block (llm-architectures-explained
 "Llama 4 Maverick", table "Every architecture field": RMSNorm before the MLP;
 KerasFormers "Llama 4", Llama4Model arguments: norm_eps 1e-5): each row is
@@ -154,6 +162,33 @@ def routing_record(idx: np.ndarray, E: int):
     return counts, offsets, perm, inv
 
 
+def topk(logits: np.ndarray, k: int):
+    """The k largest logits of each row, best first, the lower expert index
+    first among equal logits; margin = the smallest gap between consecutive
+    values among the k + 1 largest (the k largest when E == k; inf for
+    k == E == 1).  k = 1 gives top1()."""
+    T, E = logits.shape
+    order = np.lexsort((np.broadcast_to(np.arange(E), (T, E)), -logits), axis=-1)
+    idx = order[:, :k].astype(np.int64)
+    top = np.take_along_axis(logits, order[:, :min(k + 1, E)], axis=1)
+    gaps = top[:, :-1] - top[:, 1:]
+    margin = gaps.min(axis=1) if gaps.shape[1] else np.full(T, np.inf)
+    return idx, margin
+
+
+def route_topk(x, wr, bias, k: int) -> Routing:
+    """Routing with k experts per token (the block generalised: each of the
+    token's k picks is an expert of the top-1 kind, with its own sigmoid gate
+    on its input; the routed outputs add up).  idx and gate are [T, k]; the
+    record groups the T * k slots (slot t * k + j = token t's j-th pick) by
+    expert, ascending slot order within a group."""
+    lg = router_logits(x, wr, bias)
+    idx, margin = topk(lg, k)
+    gate = sigmoid(np.take_along_axis(lg, idx, axis=1))
+    counts, offsets, perm, inv = routing_record(idx.reshape(-1), lg.shape[1])
+    return Routing(lg, idx, gate, margin, counts, offsets, perm, inv)
+
+
 def route(x, wr, bias=None) -> Routing:
     lg = router_logits(x, wr, bias)
     idx, margin = top1(lg)
@@ -252,6 +287,21 @@ def combine(x, idx: np.ndarray, gate: np.ndarray, w: Weights, f: int, fs: int,
     return out
 
 
+def combine_topk(x, idx: np.ndarray, gate: np.ndarray, w: Weights, f: int, fs: int,
+                 mode: str) -> np.ndarray:
+    """out[t] = shared(x[t]) + sum_j expert_{idx[t,j]}(gate[t,j] * x[t]), idx and
+    gate [T, k] (a token's picks are distinct experts)."""
+    xin, _ = expert_input(x, mode)
+    wsgu, ssgu, wsd, ssd = w.shared()
+    out = swiglu_mlp(xin, weight_f64(wsgu, ssgu), weight_f64(wsd, ssd), fs, mode)
+    for e in np.unique(idx):
+        rows, cols = np.nonzero(idx == e)
+        wgu, sgu, wd, sd = w.expert(int(e))
+        out[rows] += swiglu_mlp(xin[rows], weight_f64(wgu, sgu), weight_f64(wd, sd), f, mode,
+                                row_scale=gate[rows, cols])
+    return out
+
+
 def dense(x, w: Weights, fs: int, mode: str) -> np.ndarray:
     """A dense layer (llm-architectures-explained "Llama 4 Maverick", table
     "Every architecture field": the non-MoE layers' FFN is a gated MLP of
@@ -263,9 +313,12 @@ def dense(x, w: Weights, fs: int, mode: str) -> np.ndarray:
     return swiglu_mlp(xin, weight_f64(wsgu, ssgu), weight_f64(wsd, ssd), fs, mode)
 
 
-def forward(x, w: Weights, f: int, fs: int, mode: str):
+def forward(x, w: Weights, f: int, fs: int, mode: str, top_k: int = 1):
     """Whole block: returns (out float64 [T, d], Routing)."""
     wr, b = w.router()
+    if top_k > 1:
+        r = route_topk(x, wr, b, top_k)
+        return combine_topk(x, r.idx, r.gate, w, f, fs, mode), r
     r = route(x, wr, b)
     out = combine(x, r.idx, r.gate, w, f, fs, mode)
     return out, r

@@ -67,10 +67,11 @@ def _swiglu_mlp(u, wgu, wd, width, mode, scale=1.0):
     return _matvec(h, wd)
 
 
-def forward(x, wr, bias, w_gate_up, w_down, ws_gate_up, ws_down, f, fs, mode="f32"):
+def forward(x, wr, bias, w_gate_up, w_down, ws_gate_up, ws_down, f, fs, mode="f32", top_k=1):
     """All arguments are nested Python lists of floats (weights already dequantised).
 
-    Returns (out [T][d], idx [T], gate [T]).
+    Returns (out [T][d], idx [T], gate [T]); with top_k > 1 idx and gate hold
+    one list of the token's picks (best first) per token.
     """
     T = len(x)
     E = len(wr[0]) if wr else 0
@@ -84,6 +85,21 @@ def forward(x, wr, bias, w_gate_up, w_down, ws_gate_up, ws_down, f, fs, mode="f3
             for j in range(d):
                 acc += row[j] * wr[j][e]
             logits.append(acc + (bias[e] if bias is not None else 0.0))
+        if top_k > 1:
+            # every expert densely, then keep the top_k by (larger logit, lower index)
+            picks = sorted(range(E), key=lambda e: (-logits[e], e))[:top_k]
+            gs = [1.0 / (1.0 + math.exp(-logits[e])) for e in picks]
+            xin = _quant_row(row)[0] if mode == "e4m3" else row
+            dense = [_swiglu_mlp(xin, w_gate_up[e], w_down[e], f, mode,
+                                 scale=1.0 / (1.0 + math.exp(-logits[e]))) for e in range(E)]
+            shared = _swiglu_mlp(xin, ws_gate_up, ws_down, fs, mode)
+            o = list(shared)
+            for e in picks:
+                o = [o[n] + dense[e][n] for n in range(d)]
+            outs.append(o)
+            idxs.append(picks)
+            gates.append(gs)
+            continue
         best = 0
         for e in range(1, E):
             if logits[e] > logits[best]:

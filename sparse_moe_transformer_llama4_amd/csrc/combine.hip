@@ -32,6 +32,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const f32x4* r, const f32x
   }
 }
 
+// The same with k routed picks per token (slot rows t*k + j of r, written
+// once each by the routed down GEMM): out[t] = y[t] (its partials in order)
+// + r[t*k] + r[t*k + 1] + ... + r[t*k + k - 1], in fp32, in this order.
+__global__ __launch_bounds__(256) void combine_topk_kernel(const f32x4* r, int k, const f32x4* y, int parts,
+                                                           void* out, int64_t n4, int d4, int out_bf16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4; i += stride) {
+    const int64_t t = i / d4;
+    const int64_t c = i - t * d4;
+    f32x4 v = y[i];
+    for (int q = 1; q < parts; ++q) v += y[q * n4 + i];
+    for (int j = 0; j < k; ++j) v += r[(t * k + j) * d4 + c];
+    if (out_bf16) {
+      const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+      const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+      reinterpret_cast<uint2*>(out)[i] = make_uint2(lo, hi);
+    } else {
+      reinterpret_cast<f32x4*>(out)[i] = v;
+    }
+  }
+}
+
 // SwiGLU over summed K-split partials of the gate/up GEMM (the same SiLU and
 // products as the gate/up epilogue): thread -> 4 consecutive columns.
 __global__ __launch_bounds__(256) void swiglu_parts_kernel(const float* gu, int parts, int T, int N, uint16_t* h) {
@@ -76,6 +98,18 @@ hipError_t launch_combine(const float* r, const float* y, int parts, void* out, 
   const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
   hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                      reinterpret_cast<const f32x4*>(r), reinterpret_cast<const f32x4*>(y), parts, out, n4, out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_topk(const float* r, int k, const float* y, int parts, void* out, int T, int d,
+                               int out_bf16, hipStream_t s) {
+  if (d % 4 != 0 || parts < 1 || k < 1) return hipErrorInvalidValue;
+  const int64_t n4 = static_cast<int64_t>(T) * (d / 4);
+  if (n4 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(combine_topk_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     reinterpret_cast<const f32x4*>(r), k, reinterpret_cast<const f32x4*>(y), parts, out, n4, d / 4,
+                     out_bf16);
   return hipGetLastError();
 }
 

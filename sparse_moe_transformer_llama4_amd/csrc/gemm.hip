@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     int64_t arow;
     const uint8_t* base;
     if constexpr (GATEUP) {
-      arow = shared ? r : p.perm[row_base + r];
+      arow = shared ? r : slot_token(p.perm[row_base + r], p.top_k);
       base = reinterpret_cast<const uint8_t*>(shared ? p.A_shared : p.A);
     } else if constexpr (MODE == MODE_DOWN_SHARED) {
       arow = r;
@@ -248,8 +248,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
         const int r = m0 + wm * (BM / WM) + i * 16 + rq + q;
         const bool valid = r < rows;
         const int orow = row_base + min(r, rows - 1);        // output row (permuted order for routed)
-        const int tok = shared ? min(r, rows - 1) : p.perm[orow];
-        float scale = shared ? 1.0f : p.gate[tok];
+        const int slot = shared ? min(r, rows - 1) : p.perm[orow];
+        const int tok = shared ? slot : slot_token(slot, p.top_k);
+        float scale = shared ? 1.0f : p.gate[slot];
         if constexpr (DT == DT_E4M3) scale *= (shared ? p.sA_shared : p.sA)[tok];
         float rmax = 0.f;
 #pragma unroll
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
           if constexpr (MODE == MODE_DOWN_SHARED) {
             reinterpret_cast<float*>(p.C_shared)[o] = v;
           } else {
-            v += p.Y[o];
+            if (p.Y) v += p.Y[o];
             if (p.out_bf16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16(v);
             else reinterpret_cast<float*>(p.C)[o] = v;
           }
@@ -330,8 +331,10 @@ static hipError_t launch_one(const GemmArgs& a0, int grid_m_tokens, hipStream_t 
     gm = mt_tok;
     nmax = a.N;
   } else {
-    // sum over routed groups of ceil(n_g / BM) <= ceil(T / BM) + E; the shared group adds ceil(T / BM)
-    gm = (has_routed ? mt_tok + a.E : 0) + (has_shared ? mt_tok : 0);
+    // sum over routed groups of ceil(n_g / BM) <= ceil(T k / BM) + E (T k routed rows); the shared
+    // group adds ceil(T / BM)
+    const int mt_r = (grid_m_tokens * (a.top_k > 1 ? a.top_k : 1) + BM - 1) / BM;
+    gm = (has_routed ? mt_r + a.E : 0) + (has_shared ? mt_tok : 0);
     nmax = a.N;
     if (MODE == MODE_GATEUP) nmax = max(has_routed ? a.N : 0, has_shared ? a.N_shared : 0);
   }

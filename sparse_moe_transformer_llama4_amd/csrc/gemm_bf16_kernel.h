@@ -182,7 +182,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(GemmArgs p) 
     const int c = (lane & 3) ^ ((tr >> 1) & 3);                  // logical 16-byte chunk
     const int r = min(m0 + tr, rows - 1);
     int arow;
-    if constexpr (GATEUP) arow = shared ? r : p.perm[row_base + r];
+    if constexpr (GATEUP) arow = shared ? r : slot_token(p.perm[row_base + r], p.top_k);
     else if constexpr (MODE == MODE_DOWN_SHARED) arow = r;
     else arow = row_base + r;
     a_voff[i] = (static_cast<uint32_t>(arow) * static_cast<uint32_t>(K) + c * 8) * 2;
@@ -513,8 +513,10 @@ hipError_t launch_v2(const GemmArgs& a0, int T, hipStream_t s, const int32_t* ti
     gm = (T + BM - 1) / BM;
     nmax = a.N;
   } else {
-    // sum over routed groups of ceil(n_g / BM) <= ceil(T / BM) + E; the shared group adds ceil(T / BM)
-    gm = (has_routed ? (T + BM - 1) / BM + a.E : 0) + (has_shared ? (T + BM - 1) / BM : 0);
+    // sum over routed groups of ceil(n_g / BM) <= ceil(T k / BM) + E (T k routed rows); the shared
+    // group adds ceil(T / BM)
+    const int Tr = T * (a.top_k > 1 ? a.top_k : 1);
+    gm = (has_routed ? (Tr + BM - 1) / BM + a.E : 0) + (has_shared ? (T + BM - 1) / BM : 0);
     nmax = a.N;
     if (MODE == MODE_GATEUP) nmax = max(has_routed ? a.N : 0, has_shared ? a.N_shared : 0);
   }

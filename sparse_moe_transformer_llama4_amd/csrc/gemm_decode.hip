@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_gateup_kernel(GemmArgs p) 
   {
     const int ar = lane >> 1;
     const int r = min(m0 + ar, rows - 1);
-    const int arow = shared ? r : p.perm[row_base + r];
+    const int arow = shared ? r : slot_token(p.perm[row_base + r], p.top_k);
     a_off = static_cast<int64_t>(arow) * K + k0 + (((lane & 1) ^ ((ar >> 3) & 1)) * 8);
   }
 
@@ -674,7 +674,7 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
 #pragma unroll
   for (int f = 0; f < FMMAX; ++f) {
     const int r = min(m0 + 16 * f + (lane >> 2), rows - 1);
-    const int arow = (GU && !shared) ? p.perm[row_base + r] : row_base + r;
+    const int arow = (GU && !shared) ? slot_token(p.perm[row_base + r], p.top_k) : row_base + r;
     a_off[f] = static_cast<int64_t>(arow) * K + k0 + (((lane & 3) ^ ((lane >> 3) & 3)) * 8);
   }
 
@@ -808,7 +808,8 @@ hipError_t launch_q8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* ti
   const int mt_tok = (T + DBM - 1) / DBM;
   const bool shared_only = MODE == MODE_DOWN_SHARED || (MODE == MODE_GATEUP && a.group_lo == a.E);
   if (MODE == MODE_GATEUP && !shared_only && a.group_hi > a.E) return hipErrorInvalidValue;   // one kind per launch
-  const int gm = shared_only ? mt_tok : mt_tok + a.E;
+  const int mt_r = (T * (a.top_k > 1 ? a.top_k : 1) + DBM - 1) / DBM;   // routed rows are slots
+  const int gm = shared_only ? mt_tok : mt_r + a.E;
   const int NH = (MODE == MODE_GATEUP && shared_only) ? a.N_shared : a.N;
   const int gn = (NH + (MODE == MODE_GATEUP ? QBN / 2 : QBN) - 1) / (MODE == MODE_GATEUP ? QBN / 2 : QBN);
   if (gm <= 0 || gn <= 0) return hipSuccess;
@@ -824,7 +825,8 @@ hipError_t launch_dec(const GemmArgs& a0, int T, hipStream_t s, const int32_t* t
   GemmArgs a = a0;
   a.tiles = tiles_all + bm_index(DBM) * (a.E + 2);
   const int mt_tok = (T + DBM - 1) / DBM;
-  const int gm = MODE == MODE_DOWN_SHARED ? mt_tok : mt_tok + a.E;
+  const int mt_r = (T * (a.top_k > 1 ? a.top_k : 1) + DBM - 1) / DBM;   // routed rows are slots
+  const int gm = MODE == MODE_DOWN_SHARED ? mt_tok : mt_r + a.E;
   if (gm <= 0) return hipSuccess;
   const int gn = (a.N + DBN - 1) / DBN;
   const int ks = (MODE == MODE_DOWN_SHARED && a.ksplit > 1) ? a.ksplit : 1;
@@ -841,7 +843,8 @@ hipError_t launch_dec_gateup(const GemmArgs& a0, int T, hipStream_t s, const int
   const bool has_routed = a.group_lo < a.E;
   const bool has_shared = a.group_hi > a.E;
   const int mt_tok = (T + DBM - 1) / DBM;
-  const int gm = (has_routed ? mt_tok + a.E : 0) + (has_shared ? mt_tok : 0);
+  const int mt_r = (T * (a.top_k > 1 ? a.top_k : 1) + DBM - 1) / DBM;   // routed rows are slots
+  const int gm = (has_routed ? mt_r + a.E : 0) + (has_shared ? mt_tok : 0);
   const int nmax = std::max(has_routed ? a.N : 0, has_shared ? a.N_shared : 0);
   const int gn = (nmax + GBNH - 1) / GBNH;
   if (gm <= 0 || gn <= 0) return hipSuccess;

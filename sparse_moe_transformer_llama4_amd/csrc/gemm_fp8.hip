@@ -131,8 +131,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
   if (tid < BM) {
     const int r = min(m0 + tid, rows - 1);
     if constexpr (GATEUP) {
-      const int tok = shared ? r : p.perm[row_base + r];
-      row_scale = (shared ? 1.0f : p.gate[tok]) * (shared ? p.sA_shared : p.sA)[tok];
+      const int slot = shared ? r : p.perm[row_base + r];
+      row_scale = (shared ? 1.0f : p.gate[slot]) * (shared ? p.sA_shared : p.sA)[shared ? slot : slot_token(slot, p.top_k)];
     } else if constexpr (MODE == MODE_DOWN_SHARED) {
       row_scale = p.sA_shared[r];
     } else {
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
     const int c = (lane & 7) ^ a_swz(tr & 15);
     const int r = min(m0 + tr, rows - 1);
     int arow;
-    if constexpr (GATEUP) arow = shared ? r : p.perm[row_base + r];
+    if constexpr (GATEUP) arow = shared ? r : slot_token(p.perm[row_base + r], p.top_k);
     else if constexpr (MODE == MODE_DOWN_SHARED) arow = r;
     else arow = row_base + r;
     a_voff[i] = static_cast<uint32_t>(arow) * static_cast<uint32_t>(K) + c * 16;
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
         else orow[u] = m0 + r;
         y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (MODE == MODE_DOWN_ROUTED)
-          if (m0 + r < rows && n0 + cc * 4 < NH)
+          if (p.Y && m0 + r < rows && n0 + cc * 4 < NH)
             y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
       }
 #pragma unroll
@@ -451,7 +451,8 @@ hipError_t launch_f8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* ti
   if constexpr (MODE == MODE_DOWN_SHARED) {
     gm = (T + BM - 1) / BM;
   } else {
-    gm = (has_routed ? (T + BM - 1) / BM + a.E : 0) + (has_shared ? (T + BM - 1) / BM : 0);
+    const int Tr = T * (a.top_k > 1 ? a.top_k : 1);   // routed rows (slots)
+    gm = (has_routed ? (Tr + BM - 1) / BM + a.E : 0) + (has_shared ? (T + BM - 1) / BM : 0);
     if (MODE == MODE_GATEUP) nmax = max(has_routed ? a.N : 0, has_shared ? a.N_shared : 0);
   }
   if (gm <= 0) return hipSuccess;

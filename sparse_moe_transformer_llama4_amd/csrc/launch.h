@@ -11,10 +11,17 @@ struct RouterArgs {
   const void* wr;     // [d][E] x dtype
   const float* bias;  // [E] or nullptr
   int T, d, E;
-  int32_t* idx;       // [T]
-  float* gate;        // [T]
-  int32_t* hist;      // [nblocks][E]
+  int32_t* idx;       // [T * k]: slot t*k + j = the token's j-th pick
+  float* gate;        // [T * k]
+  int32_t* hist;      // [nblocks][E] picks (slots) per block of kRouteTokens tokens
+  int k;              // experts per token, 1 .. kMaxTopK
 };
+
+// Largest number of experts per token.
+constexpr int kMaxTopK = 8;
+
+// The token a routing slot belongs to (slot = token * k + rank).
+__host__ __device__ inline int slot_token(int slot, int k) { return k > 1 ? slot / k : slot; }
 
 struct ScanArgs {
   int32_t* hist;  // [nblocks][E], replaced by per-block bases
@@ -60,6 +67,8 @@ struct GemmArgs {
                            // necessarily equal counts (ksplit <= K/128); GATEUP: ksplit must divide K/64
   int y_parts;             // decode DOWN_ROUTED: Y holds this many partials, summed in order (0 = 1)
   int tail_bm;             // weight-streaming tail launches: rows of the groups' full main tiles (0 = none)
+  int top_k;               // experts per token (0 / 1 = one): routed rows are slots, the routed gate/up
+                           // reads x row slot_token(perm[.], top_k), grids cover T * top_k routed rows
   float* gu_part;          // weight-streaming GATEUP: write fp32 pre-activation partials [ksplit][T][2 N] here
                            // instead of h (K split over ksplit workgroups; null = normal epilogue)
   int w_int8;              // weight-streaming kernels: B / B_shared hold int8 codes, sB / sB_shared their fp32
@@ -76,7 +85,7 @@ hipError_t launch_router(const RouterArgs& a, int x_dtype, float* part, hipStrea
 hipError_t launch_route_small(const RouterArgs& a, int x_dtype, float* part, int32_t* counts, int32_t* offsets,
                               int32_t* tiles, int32_t* perm, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
-hipError_t launch_perm(const int32_t* idx, const int32_t* base, const int32_t* offsets, int T, int E,
+hipError_t launch_perm(const int32_t* idx, const int32_t* base, const int32_t* offsets, int T, int E, int k,
                        int32_t* perm, hipStream_t s);
 // The fixed-order finish of launch_router over `nsplit` partial logit slices
 // (used with nsplit = 1 when the logits come from the prefill GEMM).
@@ -95,6 +104,9 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 // sum of a dense layer's K-split partials.
 hipError_t launch_combine(const float* r, const float* y, int parts, void* out, int64_t n, int out_bf16,
                           hipStream_t s);
+// out[t] = y[t] (+ its partials in order) + r[t*k] + ... + r[t*k + k - 1] (fp32; r: [T*k][d] slot rows)
+hipError_t launch_combine_topk(const float* r, int k, const float* y, int parts, void* out, int T, int d,
+                               int out_bf16, hipStream_t s);
 // h[t][c] = bf16(SiLU(g) * u), g = sum over the parts of gu[q][t][c], u of
 // gu[q][t][N + c], in order (parts of a K-split gate/up GEMM; N % 4 == 0).
 hipError_t launch_swiglu_parts(const float* gu, int parts, int T, int N, uint16_t* h, hipStream_t s);

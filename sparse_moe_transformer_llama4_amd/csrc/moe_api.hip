@@ -110,27 +110,29 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   const size_t nb = (t + kRouteTokens - 1) / kRouteTokens;
   const bool fp8 = c.w_dtype == MOE_E4M3;
   const size_t hsz = (c.w_dtype == MOE_BF16 || c.w_dtype == MOE_INT8) ? 2 : 4;  // e4m3: fp32 staging
-  L.idx = take(t * 4);
-  L.gate = take(t * 4);
+  const size_t ts = t * static_cast<size_t>(c.top_k > 1 ? c.top_k : 1);   // routing slots (routed rows)
+  L.idx = take(ts * 4);
+  L.gate = take(ts * 4);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
-  L.perm = take(t * 4);
+  L.perm = take(ts * 4);
   L.hist = take(nb * E * 4);
   L.logits = take(static_cast<size_t>(router_splits(static_cast<int>(T), c.d, c.x_dtype)) * t * E * 4);
   L.tiles = take(kNumTables * (E + 2) * 4);
-  L.h_r = take(t * c.f * hsz);
+  L.h_r = take(ts * c.f * hsz);
   L.h_s = take(t * c.f_shared * hsz);
   L.y_s = take(t * c.d * 4 * static_cast<size_t>(std::max(decode_y_parts(c, T), dense_down_parts(c, T))));
-  if (c.w_dtype == MOE_BF16 && T >= kPrefillTokens) L.r_out = take(t * c.d * 4);
+  if (c.top_k > 1) L.r_out = take(ts * c.d * 4);   // routed output by slot, summed per token by the combine
+  else if (c.w_dtype == MOE_BF16 && T >= kPrefillTokens) L.r_out = take(t * c.d * 4);
   if (dense_gateup_parts(c, T) > 1)
     L.gu_part = take(static_cast<size_t>(dense_gateup_parts(c, T)) * t * 2 * c.f_shared * 4);
   if (c.has_norm) L.x_n = take(t * c.d * (c.x_dtype == MOE_F32 ? 4 : 2));
   if (fp8) {
-    L.hq_r = take(t * c.f);
+    L.hq_r = take(ts * c.f);
     L.hq_s = take(t * c.f_shared);
-    L.sh_r = take(t * 4);
+    L.sh_r = take(ts * 4);
     L.sh_s = take(t * 4);
-    L.amax_r = take(t * 4);
+    L.amax_r = take(ts * 4);
     L.amax_s = take(t * 4);
     L.xq = take(t * c.d);
     L.sx = take(t * 4);
@@ -223,7 +225,7 @@ hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_we
                          hipStream_t s) {
   hipError_t e;
   RouterArgs ra{x, w->w_router, c.has_router_bias ? w->router_bias : nullptr, T, c.d, c.n_experts,
-                R.idx, R.gate, R.hist};
+                R.idx, R.gate, R.hist, c.top_k};
   if (T > 0 && T <= kRouteTokens)
     return launch_route_small(ra, c.x_dtype, R.logits, R.counts, R.offsets, R.tiles, R.perm, s);
   // Prefill-sized bf16 calls with E a multiple of 64: the logits x·W_router
@@ -251,7 +253,7 @@ hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_we
   }
   ScanArgs sa{R.hist, (T + kRouteTokens - 1) / kRouteTokens, c.n_experts, T, R.counts, R.offsets, R.tiles};
   if ((e = launch_scan(sa, s)) != hipSuccess) return e;
-  if (T > 0 && (e = launch_perm(R.idx, R.hist, R.offsets, T, c.n_experts, R.perm, s)) != hipSuccess) return e;
+  if (T > 0 && (e = launch_perm(R.idx, R.hist, R.offsets, T, c.n_experts, c.top_k, R.perm, s)) != hipSuccess) return e;
   return hipSuccess;
 }
 
@@ -260,6 +262,7 @@ GemmArgs gateup_args(const moe_config& c, const moe_weights* w, uint8_t* ws, con
   const bool fp8 = scaled_weights(c);
   GemmArgs g{};
   g.w_int8 = c.w_dtype == MOE_INT8;
+  g.top_k = c.top_k;
   g.A = a_x;
   g.A_shared = a_x;
   g.B = w->w_gate_up;
@@ -325,7 +328,26 @@ GemmArgs down_routed_args(const moe_config& c, const moe_weights* w, uint8_t* ws
   g.out_bf16 = c.out_dtype == MOE_BF16;
   g.group_lo = 0;
   g.group_hi = c.n_experts;
+  g.top_k = c.top_k;
+  if (c.top_k > 1) {
+    // k picks per token: one fp32 row per slot, summed per token by
+    // finish_topk (one writer per row, no atomics)
+    g.C = ws + L.r_out;
+    g.Y = nullptr;
+    g.out_bf16 = 0;
+  }
   return g;
+}
+
+// k > 1: out[t] = y_s[t] (its `parts` partials in order) + the token's k slot
+// rows of r_out, in pick order.  Nothing to do for k = 1 (the routed down
+// epilogue or the combine has written out).
+hipError_t finish_topk(const moe_config& c, uint8_t* ws, const WsLayout& L, int T, int parts, void* out,
+                       hipStream_t s) {
+  if (c.top_k <= 1) return hipSuccess;
+  return launch_combine_topk(reinterpret_cast<const float*>(ws + L.r_out), c.top_k,
+                             reinterpret_cast<const float*>(ws + L.y_s), parts, out, T, c.d,
+                             c.out_dtype == MOE_BF16, s);
 }
 
 // The plan's side stream of the calling device (created on first use), or
@@ -386,7 +408,8 @@ hipError_t enqueue_decode_overlapped(const moe_config& c, const void* x, int T, 
   if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, T, stream, R.tiles)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(stream, aux.join, 0)) != hipSuccess) return e;
   const GemmArgs g3 = down_routed_args(c, w, ws, L, R, ws + L.h_r, nullptr, out, T, ys);
-  return launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, T, stream, R.tiles);
+  if ((e = launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, T, stream, R.tiles)) != hipSuccess) return e;
+  return finish_topk(c, ws, L, T, ys, out, stream);
 }
 
 // bf16 prefill.  Routed groups: main tiles of bm_r rows (gate/up) and bm_d
@@ -409,8 +432,9 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
                                 hipStream_t stream, hipEvent_t* ev) {
   hipError_t e;
   const int E = c.n_experts;
-  const int bm_r = routed_tile_rows(T, E);
-  const int bm_d = down_tile_rows(T, E, c.d, bm_r);
+  const int64_t Tr = static_cast<int64_t>(T) * c.top_k;   // routed rows (slots)
+  const int bm_r = routed_tile_rows(Tr, E);
+  const int bm_d = down_tile_rows(Tr, E, c.d, bm_r);
   const int bm_sd = down_tile_rows(T, 1, c.d, 256);
   const bool tails = decode_supported(c.d) && decode_supported(c.f);
   const int32_t* tiles_main = tails ? R.tiles + kNumBM * (E + 2) : R.tiles;
@@ -462,6 +486,7 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
     if ((e = hipStreamWaitEvent(stream, aux->shared, 0)) != hipSuccess) return e;
     if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3m, T, stream, tiles_main)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(stream, aux->join, 0)) != hipSuccess) return e;
+    if (c.top_k > 1) return finish_topk(c, ws, L, T, 1, out, stream);
     return launch_combine(reinterpret_cast<const float*>(ws + L.r_out), reinterpret_cast<const float*>(ws + L.y_s), 1,
                           out, static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream);
   }
@@ -478,6 +503,7 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
   if ((e = mark(3)) != hipSuccess) return e;
   if (tails && (e = launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3, bm_d, stream, R.tiles)) != hipSuccess) return e;
   if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3, T, stream, tiles_main)) != hipSuccess) return e;
+  if ((e = finish_topk(c, ws, L, T, 1, out, stream)) != hipSuccess) return e;
   return mark(4);
 }
 
@@ -549,7 +575,9 @@ moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
   *out = nullptr;
   if (!cfg || cfg->abi_version != MOE_ABI_VERSION) return MOE_ERR_INVALID_ARGUMENT;
   const moe_config& c = *cfg;
-  if (c.top_k != 1) return MOE_ERR_UNSUPPORTED;
+  if (c.top_k < 1 || c.top_k > kMaxTopK || (c.n_experts > 0 && c.top_k > c.n_experts) ||
+      (c.n_experts == 0 && c.top_k != 1))
+    return MOE_ERR_UNSUPPORTED;
   if (c.n_experts < 0 || c.n_experts > 256) return MOE_ERR_UNSUPPORTED;
   if (!config_dtypes_ok(c)) return MOE_ERR_UNSUPPORTED;
   if (c.has_router_bias != 0 && c.has_router_bias != 1) return MOE_ERR_INVALID_ARGUMENT;
@@ -658,7 +686,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   const bool dec = use_decode(c, T);
   // the prefill kernels address activations with 32-bit byte offsets
   const int64_t kmax = std::max(std::max(c.d, c.f), c.f_shared);
-  const bool offsets32 = T * kmax * 2 < (int64_t{1} << 31);
+  const bool offsets32 = T * c.top_k * kmax * 2 < (int64_t{1} << 31);   // routed rows: T k slots
   const bool v2 = c.w_dtype == MOE_BF16 && T >= kPrefillTokens && offsets32 && bf16_v2_supported(c.d, c.f, c.f_shared) &&
                   bf16_v2_supported(c.f, c.d, c.d) && bf16_v2_supported(c.f_shared, c.d, c.d);
   const bool f8 = fp8 && T >= kPrefillTokens && offsets32;
@@ -702,7 +730,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     a_x = xq;
     amax_r = reinterpret_cast<uint32_t*>(ws + L.amax_r);
     amax_s = reinterpret_cast<uint32_t*>(ws + L.amax_s);
-    if ((e = launch_fill_u32(amax_r, T, 0u, stream)) != hipSuccess) return hip_fail(plan, e);
+    if ((e = launch_fill_u32(amax_r, T * c.top_k, 0u, stream)) != hipSuccess) return hip_fail(plan, e);   // slot rows
     if ((e = launch_fill_u32(amax_s, T, 0u, stream)) != hipSuccess) return hip_fail(plan, e);
   }
   if ((e = mark(1)) != hipSuccess) return hip_fail(plan, e);
@@ -742,7 +770,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   if (fp8) {
     sh_r = reinterpret_cast<float*>(ws + L.sh_r);
     sh_s = reinterpret_cast<float*>(ws + L.sh_s);
-    if ((e = launch_quant_h(reinterpret_cast<const float*>(ws + L.h_r), amax_r, Ti, c.f, ws + L.hq_r, sh_r,
+    if ((e = launch_quant_h(reinterpret_cast<const float*>(ws + L.h_r), amax_r, Ti * c.top_k, c.f, ws + L.hq_r, sh_r,
                             stream)) != hipSuccess)
       return hip_fail(plan, e);
     if ((e = launch_quant_h(reinterpret_cast<const float*>(ws + L.h_s), amax_s, Ti, c.f_shared, ws + L.hq_s,
@@ -765,6 +793,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
       : dec ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
             : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
+  if ((e = finish_topk(c, ws, L, Ti, ys, out, stream)) != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(4)) != hipSuccess) return hip_fail(plan, e);
   return MOE_OK;
 }

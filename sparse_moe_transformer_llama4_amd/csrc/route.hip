@@ -136,28 +136,66 @@ __global__ __launch_bounds__(256) void router_partial_kernel(RouterArgs a, int k
   }
 }
 
-// Sum of the K-slice partials in slice order (deterministic), bias, top-1
-// with ties to the lowest index, sigmoid gate, and the per-workgroup expert
-// histogram (64 tokens per workgroup, the blocking the permutation uses).
+// The k largest logits of a token, best first; among equal logits the lower
+// expert index ranks first (experts arrive in ascending order: a new logit
+// must exceed a kept one to pass it, a displaced one moves down one rank).
+// k = 1 is the argmax with ties to the lowest index.
+struct TopK {
+  float v[kMaxTopK];
+  int i[kMaxTopK];
+};
+__device__ __forceinline__ void topk_init(TopK& b) {
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    b.v[j] = -INFINITY;
+    b.i[j] = 0x7fffffff;
+  }
+}
+__device__ __forceinline__ void topk_push(TopK& b, float x, int e, int k) {
+  float cv = x;
+  int ci = e;
+  bool moving = false;   // cv is a displaced entry (ranked ahead of the rest)
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k && (moving || cv > b.v[j])) {
+      const float tv = b.v[j];
+      const int ti = b.i[j];
+      b.v[j] = cv;
+      b.i[j] = ci;
+      cv = tv;
+      ci = ti;
+      moving = true;
+    }
+  }
+}
+
+// Sum of the K-slice partials in slice order (deterministic), bias, top-k
+// (lowest index among equal logits), sigmoid gate of each pick, and the
+// per-workgroup histogram of picks (64 tokens per workgroup, the blocking
+// the permutation uses).  Token t's j-th pick is slot t * k + j.
 __global__ __launch_bounds__(64) void router_finish_kernel(RouterArgs a, int nsplit, const float* part) {
   __shared__ int hist[256];
-  const int E = a.E, T = a.T;
+  const int E = a.E, T = a.T, k = a.k;
   for (int e = threadIdx.x; e < E; e += 64) hist[e] = 0;
   __syncthreads();
   const int t = blockIdx.x * kRouteTokens + threadIdx.x;
   if (t < T) {
-    float best = -INFINITY;
-    int bi = 0x7fffffff;
+    TopK b;
+    topk_init(b);
     for (int e = 0; e < E; ++e) {
       float v = 0.f;
       for (int s = 0; s < nsplit; ++s) v += part[(static_cast<int64_t>(s) * T + t) * E + e];
       if (a.bias) v += a.bias[e];
-      if (v > best) { best = v; bi = e; }
+      topk_push(b, v, e, k);
     }
-    bi = min(bi, E - 1);  // only reachable with non-finite logits (outside the contract)
-    a.idx[t] = bi;
-    a.gate[t] = 1.0f / (1.0f + expf(-best));
-    atomicAdd(&hist[bi], 1);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= k) break;
+      const int bi = min(b.i[j], E - 1);   // only reachable with non-finite logits (outside the contract)
+      a.idx[static_cast<int64_t>(t) * k + j] = bi;
+      a.gate[static_cast<int64_t>(t) * k + j] = 1.0f / (1.0f + expf(-b.v[j]));
+      atomicAdd(&hist[bi], 1);
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 64) a.hist[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
@@ -521,10 +559,10 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouterArgs a, int nspl
                                                           int32_t* counts, int32_t* offsets, int32_t* tiles,
                                                           int32_t* perm) {
   __shared__ int cnt_s[256];
-  __shared__ int ids[kRouteTokens];
+  __shared__ int ids[kRouteTokens * kMaxTopK];
   __shared__ int sm[(1 + kNumTables) * 4];
   __shared__ float lg[kRouteTokens * 256];
-  const int tid = threadIdx.x, E = a.E, T = a.T;
+  const int tid = threadIdx.x, E = a.E, T = a.T, k = a.k;
   cnt_s[tid] = 0;
   // logits of every (token, expert) pair, the K-slice partials summed in
   // slice order; the loads of a pair are issued together (a dependent chain
@@ -546,17 +584,18 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouterArgs a, int nspl
   }
   __syncthreads();
   if (tid < T) {
-    float best = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int e = 0; e < E; ++e) {
-      const float v = lg[tid * E + e];
-      if (v > best) { best = v; bi = e; }
+    TopK b;
+    topk_init(b);
+    for (int e = 0; e < E; ++e) topk_push(b, lg[tid * E + e], e, k);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= k) break;
+      const int bi = min(b.i[j], E - 1);   // only reachable with non-finite logits (outside the contract)
+      a.idx[tid * k + j] = bi;
+      a.gate[tid * k + j] = 1.0f / (1.0f + expf(-b.v[j]));
+      ids[tid * k + j] = bi;
+      atomicAdd(&cnt_s[bi], 1);
     }
-    bi = min(bi, E - 1);  // only reachable with non-finite logits (outside the contract)
-    a.idx[tid] = bi;
-    a.gate[tid] = 1.0f / (1.0f + expf(-best));
-    ids[tid] = bi;
-    atomicAdd(&cnt_s[bi], 1);
   }
   __syncthreads();
   offsets_and_tiles(tid < E ? cnt_s[tid] : 0, E, T, counts, offsets, tiles, sm);
@@ -564,28 +603,33 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouterArgs a, int nspl
   __syncthreads();
   if (tid < E) off_s[tid] = offsets[tid];
   __syncthreads();
-  if (tid < T) {
-    const int e = ids[tid];
+  // stable position of every slot (slots in ascending order within a group)
+  for (int sl = tid; sl < T * k; sl += 256) {
+    const int e = ids[sl];
     int rank = 0;
-    for (int j = 0; j < tid; ++j) rank += ids[j] == e;
-    perm[off_s[e] + rank] = tid;
+    for (int j = 0; j < sl; ++j) rank += ids[j] == e;
+    perm[off_s[e] + rank] = sl;
   }
 }
 
-// Stable position of every token: perm[offsets[e] + base[b][e] + rank] = t,
-// where rank counts earlier tokens of the same workgroup routed to the same
-// expert.
+// Stable position of every slot: perm[offsets[e] + base[b][e] + rank] = slot,
+// where rank counts earlier slots of the same workgroup (64 tokens, their
+// k picks each) routed to the same expert.
 __global__ __launch_bounds__(64) void perm_kernel(const int32_t* idx, const int32_t* base,
-                                                  const int32_t* offsets, int T, int E, int32_t* perm) {
-  __shared__ int ids[kRouteTokens];
+                                                  const int32_t* offsets, int T, int E, int k, int32_t* perm) {
+  __shared__ int ids[kRouteTokens * kMaxTopK];
   const int t = blockIdx.x * kRouteTokens + threadIdx.x;
-  ids[threadIdx.x] = t < T ? idx[t] : -1;
+  for (int j = 0; j < k; ++j)
+    ids[threadIdx.x * k + j] = t < T ? idx[static_cast<int64_t>(t) * k + j] : -1;
   __syncthreads();
   if (t >= T) return;
-  const int e = ids[threadIdx.x];
-  int rank = 0;
-  for (int j = 0; j < static_cast<int>(threadIdx.x); ++j) rank += ids[j] == e;
-  perm[offsets[e] + base[static_cast<int64_t>(blockIdx.x) * E + e] + rank] = t;
+  for (int j = 0; j < k; ++j) {
+    const int ls = threadIdx.x * k + j;
+    const int e = ids[ls];
+    int rank = 0;
+    for (int l = 0; l < ls; ++l) rank += ids[l] == e;
+    perm[offsets[e] + base[static_cast<int64_t>(blockIdx.x) * E + e] + rank] = t * k + j;
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -637,10 +681,11 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_perm(const int32_t* idx, const int32_t* base, const int32_t* offsets, int T, int E,
+hipError_t launch_perm(const int32_t* idx, const int32_t* base, const int32_t* offsets, int T, int E, int k,
                        int32_t* perm, hipStream_t s) {
+  if (k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
   hipLaunchKernelGGL(perm_kernel, dim3((T + kRouteTokens - 1) / kRouteTokens), dim3(kRouteTokens), 0, s, idx, base,
-                     offsets, T, E, perm);
+                     offsets, T, E, k, perm);
   return hipGetLastError();
 }
 

@@ -122,6 +122,7 @@ class Plan:
                            int(bool(has_bias)), max_tokens, int(norm_eps is not None),
                            0.0 if norm_eps is None else float(norm_eps))
         self.norm_eps = norm_eps
+        self.top_k = top_k
         self.d, self.E, self.f, self.fs = d, E, f, fs
         self.x_dtype, self.w_dtype, self.out_dtype = x_dtype, w_dtype, out_dtype
         self.has_bias = bool(has_bias)
@@ -133,7 +134,7 @@ class Plan:
     @staticmethod
     def for_shape(shape, max_tokens=None) -> "Plan":
         return Plan(shape.d, shape.E, shape.f, shape.fs, shape.x_dtype, shape.w_dtype, shape.out_dtype,
-                    shape.has_bias, max_tokens or max(shape.T, 1),
+                    shape.has_bias, max_tokens or max(shape.T, 1), top_k=getattr(shape, "top_k", 1),
                     norm_eps=getattr(shape, "norm_eps", None))
 
     def __del__(self):
@@ -168,10 +169,13 @@ def _weights(w: dict) -> _Weights:
 
 
 def new_routing(plan: Plan, T: int, device) -> dict:
+    """Routing record buffers: expert_idx / gate / perm hold T * top_k slots
+    (slot t * k + j = token t's j-th pick)."""
     z = lambda n, dt: torch.empty(max(n, 1), dtype=dt, device=device)
-    return {"expert_idx": z(T, torch.int32), "gate": z(T, torch.float32),
+    S = T * plan.top_k
+    return {"expert_idx": z(S, torch.int32), "gate": z(S, torch.float32),
             "counts": z(plan.E, torch.int32), "offsets": z(plan.E + 1, torch.int32),
-            "perm": z(T, torch.int32)}
+            "perm": z(S, torch.int32)}
 
 
 def _routing(r: Optional[dict]):

@@ -69,6 +69,7 @@ class MoEShape:
     x_std: float = 1.0
     w_std: float = 0.02
     norm_eps: Optional[float] = None   # RMSNorm in front of the block (None = none)
+    top_k: int = 1         # experts per token
 
     @property
     def has_bias(self) -> bool:
@@ -106,6 +107,11 @@ EXTRA_CONFIGS = {
     # workload's seed and routing)
     "scout_decode_int8": MoEShape("scout_decode_int8", T=32, d=5120, E=16, f=8192, fs=8192, w_dtype="i8",
                                   bias="cold", seed=2),
+    # two experts per token on the Scout-shaped layer (prefill and decode)
+    "scout_prefill_bf16_top2": MoEShape("scout_prefill_bf16_top2", T=4096, d=5120, E=16, f=8192, fs=8192,
+                                        seed=9, top_k=2),
+    "scout_decode_bf16_top2": MoEShape("scout_decode_bf16_top2", T=32, d=5120, E=16, f=8192, fs=8192,
+                                       seed=10, top_k=2),
     "maverick_prefill_fp8_rmsnorm": MoEShape("maverick_prefill_fp8_rmsnorm", T=16384, d=5120, E=128,
                                              f=8192, fs=8192, w_dtype="e4m3", out_dtype="bf16", seed=8,
                                              norm_eps=1e-5),

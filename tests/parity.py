@@ -29,9 +29,39 @@ def run_gpu(plan, x, w, poison_ws=True, T=None):
     return out, routing
 
 
+def check_routing_topk(cfg, r_or: block.Routing, routing: dict):
+    """k experts per token: the GPU's [T, k] picks (slot t*k + j) must equal
+    the oracle's, in order, on every token whose margin (smallest gap among
+    its k + 1 largest logits) exceeds 1e-3; elsewhere they must be a valid
+    top-k up to 1e-3.  The record over the T*k slots must be the one the
+    GPU's own picks give, and the oracle's when no token is near a tie."""
+    T, E, k = r_or.idx.shape[0], cfg.E, cfg.top_k
+    idx = routing["expert_idx"][:T * k].cpu().numpy().astype(np.int64).reshape(T, k)
+    assert ((idx >= 0) & (idx < E)).all()
+    assert all(len(set(row)) == k for row in idx.tolist())          # distinct picks
+    counts, offsets, perm, _ = block.routing_record(idx.reshape(-1), E)
+    np.testing.assert_array_equal(routing["counts"][:E].cpu().numpy(), counts)
+    np.testing.assert_array_equal(routing["offsets"][:E + 1].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(routing["perm"][:T * k].cpu().numpy(), perm)
+    far = r_or.margin > block.NEAR_TIE
+    np.testing.assert_array_equal(idx[far], r_or.idx[far])
+    lg = r_or.logits
+    picked = np.take_along_axis(lg, idx, axis=1)
+    kth = np.sort(lg, axis=1)[:, ::-1][:, k - 1]
+    assert (picked >= kth[:, None] - block.NEAR_TIE).all()             # a top-k up to the tolerance
+    assert (np.diff(picked, axis=1) <= block.NEAR_TIE).all()           # best first
+    if far.all():
+        np.testing.assert_array_equal(perm, r_or.perm)
+    gate = routing["gate"][:T * k].cpu().double().numpy().reshape(T, k)
+    np.testing.assert_allclose(gate, block.sigmoid(picked), rtol=0, atol=2e-6)
+    return idx
+
+
 def check_routing(cfg, r_or: block.Routing, routing: dict, rows=None):
     """Bit-exact routing rules: GPU record self-consistent, and equal to the
     oracle on every token whose top-2 margin exceeds 1e-3."""
+    if getattr(cfg, "top_k", 1) > 1:
+        return check_routing_topk(cfg, r_or, routing)
     T, E = len(r_or.idx), cfg.E
     idx = routing["expert_idx"][:T].cpu().numpy().astype(np.int64)
     assert ((idx >= 0) & (idx < E)).all()
@@ -78,6 +108,16 @@ def check_forward(cfg, inp_cpu: dict, out_gpu, routing, tol=None):
     w = block.Weights.from_dict(inp_cpu)
     wr, b = w.router()
     x = block_input(cfg, inp_cpu)
+    k = getattr(cfg, "top_k", 1)
+    if k > 1:
+        # the oracle's output on the GPU's picks (near-ties may pick either)
+        r = block.route_topk(x, wr, b, k)
+        idx = check_routing(cfg, r, routing)
+        gate = block.sigmoid(np.take_along_axis(r.logits, idx, axis=1))
+        ref = block.combine_topk(x, idx, gate, w, cfg.f, cfg.fs, cfg.w_dtype)
+        err = output_error(cfg, out_gpu, ref)
+        assert err <= (tol or TOL[cfg.w_dtype]), f"{cfg.name}: max|err|/RMS = {err:.3e}"
+        return err, r
     r = block.route(x, wr, b)
     idx = check_routing(cfg, r, routing)
     gate = block.sigmoid(r.logits[np.arange(len(idx)), idx])

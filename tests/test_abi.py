@@ -49,7 +49,13 @@ def _plan(**kw):
     ({"x_dtype": 0, "w_dtype": 0, "out_dtype": 0}, OK),
     ({"out_dtype": 1}, OK),
     ({"w_dtype": 2, "out_dtype": 1}, OK),
-    ({"top_k": 2}, UNSUPPORTED),
+    ({"top_k": 2}, OK),
+    ({"top_k": 4}, OK),                      # every expert
+    ({"top_k": 5}, UNSUPPORTED),             # more picks than experts
+    ({"top_k": 0}, UNSUPPORTED),
+    ({"top_k": 9, "n_experts": 16}, UNSUPPORTED),
+    ({"top_k": 8, "n_experts": 16}, OK),
+    ({"top_k": 2, "n_experts": 0, "f": 0}, UNSUPPORTED),
     ({"d": 96}, UNSUPPORTED),
     ({"f": 100}, UNSUPPORTED),
     ({"f_shared": 0}, UNSUPPORTED),
@@ -218,3 +224,15 @@ def test_norm_requires_its_weight():
     assert lib.moe_forward(h, P, 64, ctypes.byref(w), P, None, P, n0.value, None) == WORKSPACE
     lib.moe_plan_destroy(h0)
     lib.moe_plan_destroy(h)
+
+
+def test_workspace_grows_with_top_k():
+    lib = moe.load_library()
+    sizes = []
+    for k in (1, 2, 4):
+        st, h = _plan(max_tokens=100, top_k=k)
+        n = ctypes.c_size_t()
+        assert lib.moe_workspace_size(h, 100, ctypes.byref(n)) == OK
+        sizes.append(n.value)
+        lib.moe_plan_destroy(h)
+    assert sizes[0] < sizes[1] < sizes[2]

@@ -112,3 +112,43 @@ def test_fullsize_dense_sampled(gpu, name):
     print(f"[full] {name}: sampled max|err|/RMS = {err:.3e}", flush=True)
     assert err <= TOL[cfg.w_dtype]
     assert torch.isfinite(out_cpu.float()).all()
+
+
+@pytest.mark.parametrize("name", ["scout_decode_bf16_top2", "scout_prefill_bf16_top2"])
+def test_fullsize_topk_sampled(gpu, name):
+    # two experts per token at the Scout shape: routing on every token, the
+    # output on sampled tokens (those of the hottest expert and of token 0's
+    # first pick), the oracle evaluated on the GPU's picks
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = synth.get_config(name)
+    print(f"[full] {name}: generating on GPU", flush=True)
+    g = synth.make_inputs(cfg, gpu)
+    plan = moe.Plan.for_shape(cfg)
+    routing = moe.new_routing(plan, cfg.T, gpu)
+    ws = torch.full((moe.moe_workspace_size(plan, cfg.T),), 0xFF, dtype=torch.uint8, device=gpu)
+    out = moe.moe_forward(plan, g["x"], g, routing=routing, workspace=ws)
+    torch.cuda.synchronize()
+    out_cpu = out.cpu()
+    routing = {k: v.cpu() for k, v in routing.items()}
+    del g, ws, out
+    gc.collect()
+    torch.cuda.empty_cache()
+
+    x = synth.gen_x(cfg, "cpu")
+    r = block.route_topk(x, synth.gen_router(cfg, "cpu"), synth.gen_bias(cfg), cfg.top_k)
+    idx = check_routing(cfg, r, routing)
+    counts = np.bincount(idx.reshape(-1), minlength=cfg.E)
+    hot = int(np.argmax(counts))
+    grp = np.nonzero((idx == hot).any(axis=1))[0]
+    toks = np.array(sorted({0, int(grp[0]), int(grp[len(grp) // 2]), int(grp[-1])}))
+    experts = sorted(set(idx[toks].reshape(-1).tolist()))
+    print(f"[full] {name}: oracle output on tokens {toks.tolist()} (experts {experts})", flush=True)
+    cache = {e: synth.gen_expert(cfg, e, "cpu") for e in experts}
+    shared = synth.gen_shared(cfg, "cpu")
+    w = block.Weights(lambda: None, lambda e: cache[e], lambda: shared)
+    gate = block.sigmoid(np.take_along_axis(r.logits[toks], idx[toks], axis=1))
+    ref = block.combine_topk(x[toks], idx[toks], gate, w, cfg.f, cfg.fs, cfg.w_dtype)
+    err = output_error(cfg, out_cpu[toks], ref)
+    print(f"[full] {name}: sampled max|err|/RMS = {err:.3e}", flush=True)
+    assert err <= TOL[cfg.w_dtype]
+    assert torch.isfinite(out_cpu.float()).all()

@@ -392,3 +392,63 @@ def test_int8_side_stream_matches_serial_schedule(gpu):
     moe.moe_forward_timed(p, w["x"], w, ev, out=out_t, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out, out_t)
+
+
+# ------------------------------------------------------------ k experts per token
+
+TOPK_CASES = [("decode_like_bf16", 33, 2), ("decode_like_bf16", 1, 4), ("decode_like_bf16", 64, 2),
+              ("small_bf16", None, 2), ("small_bf16", None, 8), ("small_bf16_tall", None, 2),
+              ("small_fp32", None, 3), ("small_fp8", None, 2), ("small_bf16_out16", None, 2),
+              ("small_bf16_split", None, 3)]
+
+
+@pytest.mark.parametrize("name,T,k", TOPK_CASES)
+def test_topk_matches_oracle(gpu, name, T, k):
+    # every schedule (decode with the side stream, bf16 prefill with tails and
+    # the merged down launch, fp32, fp8) with k picks per token
+    cfg = dataclasses.replace(synth.get_config(name), top_k=k, name=f"{name}_k{k}")
+    if T is not None:
+        cfg = dataclasses.replace(cfg, T=T)
+    print(f"[parity] top-{k} {cfg.name} T={cfg.T}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    err, _ = check_forward(cfg, inp, out, routing)
+    print(f"[parity] top-{k} {cfg.name} max|err|/RMS = {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("over", [dict(w_dtype="i8", T=33), dict(norm_eps=1e-5, T=40)])
+def test_topk_int8_and_rmsnorm(gpu, over):
+    cfg = dataclasses.replace(synth.get_config("decode_like_bf16"), top_k=2, name="dec_k2", **over)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    check_forward(cfg, inp, out, routing)
+
+
+@pytest.mark.parametrize("name,T", [("decode_like_bf16", 33), ("small_bf16_tall", None)])
+def test_topk_side_stream_matches_serial_schedule(gpu, name, T):
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = dataclasses.replace(synth.get_config(name), top_k=2)
+    if T is not None:
+        cfg = dataclasses.replace(cfg, T=T)
+    p = _plan(cfg)
+    w = to_device(synth.make_inputs(cfg), gpu)
+    ws = torch.empty(moe.moe_workspace_size(p, cfg.T), dtype=torch.uint8, device=gpu)
+    out = moe.moe_forward(p, w["x"], w, workspace=ws)
+    ev = moe.StageEvents()
+    out_t = torch.empty_like(out)
+    moe.moe_forward_timed(p, w["x"], w, ev, out=out_t, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_t)
+
+
+def test_topk_route_only(gpu):
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = dataclasses.replace(synth.get_config("small_bf16_bias"), top_k=3)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    r = moe.moe_route(_plan(cfg), g["x"], g)
+    torch.cuda.synchronize()
+    w = block.Weights.from_dict(inp)
+    check_routing(cfg, block.route_topk(inp["x"], *w.router(), 3), r)

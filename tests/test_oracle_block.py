@@ -319,3 +319,67 @@ def test_int8_weights_dequantise_to_code_times_column_scale():
     assert not np.array_equal(e4, codes.double().numpy())
     with pytest.raises(TypeError):
         block.dequant_cols(codes.to(torch.int16), scale)
+
+
+# ------------------------------------------------------------ k experts per token
+
+@pytest.mark.parametrize("T,d,E,f,fs,mode,k", [(9, 16, 4, 8, 8, "bf16", 2), (7, 8, 5, 4, 8, "f32", 3),
+                                                (6, 16, 4, 8, 8, "e4m3", 2), (5, 16, 3, 8, 8, "i8", 3),
+                                                (8, 8, 4, 4, 4, "f32", 4)])
+def test_topk_matches_brute_force(T, d, E, f, fs, mode, k):
+    cfg, inp = _tiny(T, d, E, f, fs, mode, seed=T * 17 + E + k)
+    w = block.Weights.from_dict(inp)
+    out, r = block.forward(inp["x"], w, f, fs, mode, top_k=k)
+    lists = _lists(inp, E)
+    bo, bidx, bgate = brute.forward(lists["x"], lists["wr"], lists["bias"], lists["w_gate_up"],
+                                    lists["w_down"], lists["ws_gate_up"], lists["ws_down"], f, fs, mode, top_k=k)
+    np.testing.assert_array_equal(r.idx, np.array(bidx))
+    np.testing.assert_allclose(r.gate, np.array(bgate), rtol=1e-14)
+    bo = np.array(bo)
+    assert np.max(np.abs(out - bo)) <= 1e-12 * np.sqrt(np.mean(bo * bo))
+    # the record groups the T k slots by expert, ascending within a group
+    assert r.counts.sum() == T * k and (np.diff(r.offsets) == r.counts).all()
+    flat = r.idx.reshape(-1)
+    for e in range(E):
+        grp = r.perm[r.offsets[e]:r.offsets[e + 1]]
+        assert (flat[grp] == e).all() and (np.diff(grp) > 0).all()
+
+
+def test_topk_order_ties_and_margin():
+    lg = np.array([[1.0, 3.0, 3.0, 2.0], [0.5, 0.5, 0.5, 0.5], [4.0, 1.0, 2.0, 3.0]])
+    idx, margin = block.topk(lg, 2)
+    np.testing.assert_array_equal(idx, [[1, 2], [0, 1], [0, 3]])   # equal logits: lower index first
+    np.testing.assert_array_equal(margin, [0.0, 0.0, 1.0])
+    idx3, m3 = block.topk(lg, 3)
+    np.testing.assert_array_equal(idx3, [[1, 2, 3], [0, 1, 2], [0, 3, 2]])
+    idx4, m4 = block.topk(lg, 4)   # k == E: gaps among all four
+    np.testing.assert_array_equal(idx4[2], [0, 3, 2, 1])
+    assert m4[2] == 1.0
+    # k = 1 is top1
+    rng = np.random.default_rng(3)
+    lg = rng.standard_normal((50, 7))
+    i1, m1 = block.topk(lg, 1)
+    t1, tm = block.top1(lg)
+    np.testing.assert_array_equal(i1[:, 0], t1)
+    np.testing.assert_array_equal(m1, tm)
+
+
+def test_topk_with_every_expert_is_order_free():
+    # k = E: every expert fires on every token with its own gate, so relabelling
+    # the experts (router columns and weights together) leaves the output as is
+    cfg, inp = _tiny(6, 16, 4, 8, 8, "f32", seed=5)
+    w = block.Weights.from_dict(inp)
+    out, r = block.forward(inp["x"], w, 8, 8, "f32", top_k=4)
+    assert (r.counts == 6).all()
+    p = [2, 0, 3, 1]
+    inp2 = dict(inp)
+    inp2["w_router"] = inp["w_router"][:, p]
+    inp2["w_gate_up"] = inp["w_gate_up"][p]
+    inp2["w_down"] = inp["w_down"][p]
+    out2, _ = block.forward(inp2["x"], block.Weights.from_dict(inp2), 8, 8, "f32", top_k=4)
+    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-12 * np.abs(out).max())
+    # and it equals the shared expert plus every expert on its gated input
+    lg = block.router_logits(inp["x"], inp["w_router"])
+    g = block.sigmoid(lg)
+    ref = block.combine_topk(inp["x"], np.tile(np.arange(4), (6, 1)), g, w, 8, 8, "f32")
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12 * np.abs(out).max())
