@@ -16,6 +16,13 @@
  *   SwiGLU_W(u) = (SiLU(u Wg) * (u Wu)) Wd,  SiLU(z) = z / (1 + exp(-z)),
  *                Wg / Wu = columns [0,f) / [f,2f) of W_gate_up.
  *
+ * With top_k = k > 1 (torchtune llama4_decoder, Parameters:
+ * experts_per_token; Llama 4 itself routes one expert per token) the token's
+ * k largest logits are its picks e_0..e_{k-1}, best first, the lower index
+ * first among equal logits; pick j is routing slot t*k + j with gate
+ * g_j = 1 / (1 + exp(-logit[t,e_j])), and
+ *   out[t] = shared(t) + sum_j SwiGLU_{e_j}(g_j * x[t]).
+ *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer (HBM) owned by the caller;
  *     the library never allocates, frees or keeps device memory.  Scratch
@@ -55,7 +62,7 @@ extern "C" {
 typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARGUMENT = -1, /* null / misaligned pointer, missing fp8 scale, bad abi_version */
-  MOE_ERR_UNSUPPORTED = -2,      /* top_k != 1, d / f / f_shared not multiples of 64 (128 for
+  MOE_ERR_UNSUPPORTED = -2,      /* top_k outside [1, min(E, 8)], d / f / f_shared not multiples of 64 (128 for
                                     E4M3 and INT8 weights), E outside [1,256], dtype
                                     combination not implemented */
   MOE_ERR_SHAPE = -3,            /* T < 0 or T > max_tokens */
@@ -118,7 +125,7 @@ typedef struct moe_config {
   int32_t n_experts;       /* E, 1..256; 0 = a dense layer (see below) */
   int32_t f;               /* routed expert width, multiple of 64 (128 for E4M3 / INT8); 0 when E == 0 */
   int32_t f_shared;        /* shared expert width, multiple of 64 (128 for E4M3 / INT8) */
-  int32_t top_k;           /* must be 1 */
+  int32_t top_k;           /* experts per token, 1..min(E, 8) (1 for a dense layer) */
   int32_t x_dtype;         /* moe_dtype of x and W_router */
   int32_t w_dtype;         /* moe_dtype of the expert and shared weights */
   int32_t out_dtype;       /* moe_dtype of out */
@@ -151,19 +158,20 @@ typedef struct moe_weights {
 } moe_weights;
 
 /*
- * Routing record (device buffers owned by the caller).
- *   expert_idx[t] = e*(t);  gate[t] = g(t) (fp32, from the fp32 logit);
- *   counts[e] = #tokens routed to e;  offsets[0] = 0,
+ * Routing record (device buffers owned by the caller), over the T * top_k
+ * routing slots (slot t * k + j = token t's j-th pick; slot = token for k = 1):
+ *   expert_idx[s] = the slot's expert;  gate[s] = its gate (fp32, from the
+ *   fp32 logit);  counts[e] = #slots routed to e;  offsets[0] = 0,
  *   offsets[e+1] = offsets[e] + counts[e];
- *   perm[offsets[e] + r] = the r-th smallest token index routed to e
- *   (a stable grouping of tokens by expert).
+ *   perm[offsets[e] + r] = the r-th smallest slot routed to e
+ *   (a stable grouping of slots by expert).
  */
 typedef struct moe_routing {
-  int32_t* expert_idx; /* [T] */
-  float* gate;         /* [T] */
+  int32_t* expert_idx; /* [T * top_k] */
+  float* gate;         /* [T * top_k] */
   int32_t* counts;     /* [E] */
   int32_t* offsets;    /* [E + 1] */
-  int32_t* perm;       /* [T] */
+  int32_t* perm;       /* [T * top_k] */
 } moe_routing;
 
 /* Validate `cfg` and create a host-side plan (no device call is made; the
@@ -180,7 +188,7 @@ void moe_plan_destroy(moe_plan_t plan);
 moe_status moe_workspace_size(moe_plan_t plan, int64_t T, size_t* bytes);
 
 /*
- * Router, top-1, gate and the stable expert grouping only (superteams.ai
+ * Router, top-1 (top-k), gate and the stable expert grouping only (superteams.ai
  * "Llama 4", routing sketch: one logit per expert, argmax).  Fills every
  * pointer of *out.  T == 0 zeroes counts and offsets and enqueues nothing else.
  */
@@ -201,7 +209,7 @@ moe_status moe_forward(moe_plan_t plan, const void* x, int64_t T, const moe_weig
 /*
  * moe_forward with stage timing: records events[0..MOE_NUM_STAGES] on
  * `stream` at the stage boundaries
- *   [0] routing (RMSNorm if configured, router GEMM, top-1, gate, scan, permutation;
+ *   [0] routing (RMSNorm if configured, router GEMM, top-k, gate, scan, permutation;
  *       e4m3: x quantisation)
  *   [1] grouped gate/up GEMM with the SwiGLU epilogue (routed groups + shared)
  *   [2] shared-expert down GEMM (e4m3: preceded by h quantisation)
