@@ -33,13 +33,13 @@ sys.path.insert(0, ROOT)
 
 # dense MFMA peak by weight dtype, FLOP/s (int8 weights are converted to
 # bf16 and multiplied on the bf16 MFMA)
-PEAK = {"bf16": 2516.6e12, "e4m3": 5033.2e12, "f32": 157.3e12, "i8": 2516.6e12}
+PEAK = {"bf16": 2516.6e12, "e4m3": 5033.2e12, "f32": 157.3e12, "i8": 2516.6e12, "i4": 2516.6e12}
 HBM_PEAK = 8.0e12                                                 # bytes/s
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def esize(dt: str) -> int:
-    return {"f32": 4, "bf16": 2, "e4m3": 1, "i8": 1}[dt]
+    return {"f32": 4, "bf16": 2, "e4m3": 1, "i8": 1, "i4": 0.5}[dt]
 
 
 def stage_work(cfg, counts):
@@ -50,7 +50,7 @@ def stage_work(cfg, counts):
     hb = 4 if cfg.w_dtype == "f32" else 2
     ob = esize(cfg.out_dtype)
     touched = sum(1 for c in counts if c > 0)
-    sc = 4 if cfg.w_dtype in ("e4m3", "i8") else 0     # fp32 column scales per weight column
+    sc = 4 if cfg.w_dtype in ("e4m3", "i8", "i4") else 0     # fp32 column scales per weight column
     xin = 1 if cfg.w_dtype == "e4m3" else xb   # gate/up reads the e4m3 copy of x
     # RMSNorm in front of the block: x read, the normalised rows written (and
     # their e4m3 codes + scales for e4m3 weights), the gain read
@@ -72,7 +72,7 @@ def block_work(cfg, counts):
     """Whole-block algorithmic FLOPs and bytes (touched weights + x + out)."""
     T, d, E, f, fs = cfg.T, cfg.d, cfg.E, cfg.f, cfg.fs
     wb = esize(cfg.w_dtype)
-    sc = 4 if cfg.w_dtype in ("e4m3", "i8") else 0
+    sc = 4 if cfg.w_dtype in ("e4m3", "i8", "i4") else 0
     touched = sum(1 for c in counts if c > 0)
     flops = 2 * T * (d * E + 3 * d * f * cfg.top_k + 3 * d * fs)
     byts = (touched * (3 * d * f * wb + (2 * f + d) * sc) + 3 * d * fs * wb + (2 * fs + d) * sc

@@ -74,7 +74,8 @@ typedef enum moe_dtype {
   MOE_F32 = 0,
   MOE_BF16 = 1,
   MOE_E4M3 = 2, /* OCP 8-bit float E4M3 "fn": max 448, no infinities; stored as uint8 codes */
-  MOE_INT8 = 3  /* signed 8-bit integer weight codes (-127..127), with fp32 scales */
+  MOE_INT8 = 3, /* signed 8-bit integer weight codes (-127..127), with fp32 scales */
+  MOE_INT4 = 4  /* signed 4-bit weight codes (-7..7), two per byte along K, with fp32 scales */
 } moe_dtype;
 
 /*
@@ -99,6 +100,11 @@ typedef enum moe_dtype {
  *                        in the weight-streaming GEMMs, bf16 activations and
  *                        MFMA, h rounded to bf16; max_tokens <= 64
  *                        (MOE_ERR_SHAPE otherwise), E >= 1
+ *   BF16 / INT4 / F32 or BF16
+ *                        the same with int4 codes: a [K, N] matrix is stored
+ *                        as [K/2, N] bytes, byte (i, n) = code(2i, n) in the
+ *                        low nibble, code(2i+1, n) in the high one (two's
+ *                        complement); d, f, f_shared multiples of 256
  *
  * n_experts == 0 configures a dense layer (llm-architectures-explained
  * "Llama 4 Maverick", table "Every architecture field": the layers between

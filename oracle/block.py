@@ -59,8 +59,8 @@ follow the data types of the workloads):
      (A bf16 intermediate is deliberately absent: a scale taken from a
      bf16-rounded row lets a one-ulp difference in the row's largest element
      re-round every code of that row.)
-  R1 (int8 weights, dequantised to code * column scale): as for bf16 -- the
-     activations stay bf16 and h is rounded to bf16.
+  R1 (int8 and int4 weights, dequantised to code * column scale): as for
+     bf16 -- the activations stay bf16 and h is rounded to bf16.
   The output itself is returned unrounded in float64.
 """
 from __future__ import annotations
@@ -85,12 +85,27 @@ def to_f64(t) -> np.ndarray:
     return np.asarray(t, dtype=np.float64)
 
 
-def dequant_cols(codes, scale) -> np.ndarray:
+def unpack_int4(packed) -> np.ndarray:
+    """[K/2, N] bytes, byte (i, n) = code(2i, n) in the low nibble and
+    code(2i+1, n) in the high one (two's complement) -> int codes [K, N]."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    lo, hi = b & 15, b >> 4
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty((2 * b.shape[0], b.shape[1]), dtype=np.int64)
+    out[0::2], out[1::2] = lo, hi
+    return out
+
+
+def dequant_cols(codes, scale, fmt=None) -> np.ndarray:
     """Weight codes [K, N] with one fp32 scale per column N -> float64 values:
-    e4m3 codes (uint8) decode to their e4m3 values, int8 codes are integers;
-    value = code value * scale[n]."""
+    e4m3 codes (uint8) decode to their e4m3 values, int8 codes are integers,
+    int4 codes (fmt "i4") come packed two per byte along K; value = code
+    value * scale[n]."""
     c = codes.numpy() if isinstance(codes, torch.Tensor) else np.asarray(codes)
     s = to_f64(scale)
+    if fmt == "i4":
+        return unpack_int4(c).astype(np.float64) * s[None, :]
     if c.dtype == np.int8:
         return c.astype(np.float64) * s[None, :]
     if c.dtype != np.uint8:
@@ -98,10 +113,10 @@ def dequant_cols(codes, scale) -> np.ndarray:
     return e4m3_decode(c) * s[None, :]
 
 
-def weight_f64(w, scale=None) -> np.ndarray:
+def weight_f64(w, scale=None, fmt=None) -> np.ndarray:
     if scale is None:
         return to_f64(w)
-    return dequant_cols(w, scale)
+    return dequant_cols(w, scale, fmt)
 
 
 # ------------------------------------------------------------ routing
@@ -221,7 +236,7 @@ def round_h(h: np.ndarray, mode: str) -> np.ndarray:
     """Rounding point R1 applied to SwiGLU outputs (rows = tokens)."""
     if mode == "f32":
         return h
-    if mode in ("bf16", "i8"):   # int8 weights: bf16 activations, h rounded like bf16
+    if mode in ("bf16", "i8", "i4"):   # int8 / int4 weights: bf16 activations, h rounded like bf16
         return bf16_round(h.astype(np.float32))
     if mode == "e4m3":
         return quant_rows_e4m3(h.astype(np.float32))[0]
@@ -277,11 +292,11 @@ def combine(x, idx: np.ndarray, gate: np.ndarray, w: Weights, f: int, fs: int,
     xin, _ = expert_input(x, mode)
     T = xin.shape[0]
     wsgu, ssgu, wsd, ssd = w.shared()
-    out = swiglu_mlp(xin, weight_f64(wsgu, ssgu), weight_f64(wsd, ssd), fs, mode)
+    out = swiglu_mlp(xin, weight_f64(wsgu, ssgu, mode), weight_f64(wsd, ssd, mode), fs, mode)
     for e in np.unique(idx):
         rows = np.nonzero(idx == e)[0]
         wgu, sgu, wd, sd = w.expert(int(e))
-        out[rows] += swiglu_mlp(xin[rows], weight_f64(wgu, sgu), weight_f64(wd, sd), f, mode,
+        out[rows] += swiglu_mlp(xin[rows], weight_f64(wgu, sgu, mode), weight_f64(wd, sd, mode), f, mode,
                                 row_scale=gate[rows])
     assert out.shape[0] == T
     return out
@@ -293,11 +308,11 @@ def combine_topk(x, idx: np.ndarray, gate: np.ndarray, w: Weights, f: int, fs: i
     gate [T, k] (a token's picks are distinct experts)."""
     xin, _ = expert_input(x, mode)
     wsgu, ssgu, wsd, ssd = w.shared()
-    out = swiglu_mlp(xin, weight_f64(wsgu, ssgu), weight_f64(wsd, ssd), fs, mode)
+    out = swiglu_mlp(xin, weight_f64(wsgu, ssgu, mode), weight_f64(wsd, ssd, mode), fs, mode)
     for e in np.unique(idx):
         rows, cols = np.nonzero(idx == e)
         wgu, sgu, wd, sd = w.expert(int(e))
-        out[rows] += swiglu_mlp(xin[rows], weight_f64(wgu, sgu), weight_f64(wd, sd), f, mode,
+        out[rows] += swiglu_mlp(xin[rows], weight_f64(wgu, sgu, mode), weight_f64(wd, sd, mode), f, mode,
                                 row_scale=gate[rows, cols])
     return out
 
@@ -310,7 +325,7 @@ def dense(x, w: Weights, fs: int, mode: str) -> np.ndarray:
     token."""
     xin, _ = expert_input(x, mode)
     wsgu, ssgu, wsd, ssd = w.shared()
-    return swiglu_mlp(xin, weight_f64(wsgu, ssgu), weight_f64(wsd, ssd), fs, mode)
+    return swiglu_mlp(xin, weight_f64(wsgu, ssgu, mode), weight_f64(wsd, ssd, mode), fs, mode)
 
 
 def forward(x, w: Weights, f: int, fs: int, mode: str, top_k: int = 1):

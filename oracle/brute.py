@@ -60,7 +60,7 @@ def _swiglu_mlp(u, wgu, wd, width, mode, scale=1.0):
     for j in range(width):
         z = a[j]
         h.append(z / (1.0 + math.exp(-z)) * a[width + j])
-    if mode in ("bf16", "i8"):
+    if mode in ("bf16", "i8", "i4"):
         h = [_bf16(v) for v in h]
     if mode == "e4m3":
         h, _ = _quant_row([_f32(v) for v in h])

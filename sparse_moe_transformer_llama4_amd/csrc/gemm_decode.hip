@@ -546,7 +546,14 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
 //     int8 -> fp32, upper half;
 //   * the column scale multiplies the fp32 sums in the epilogue (exact
 //     algebra: sum_k x_k q_kn s_n = s_n sum_k x_k q_kn).
-constexpr int QBN = 256;               // int8 weight columns per tile
+// int4 (QB = 4): two codes per byte along K (byte (k/2, n) holds rows k, k+1
+// of column n, the even row in the low nibble, two's complement), so the
+// same 256-byte rows and transpose reads carry 64 K rows per stage: a lane's
+// 8 bytes are 16 consecutive K values of its column, the B operands of two
+// MFMA steps (K rows 16g .. 16g+7 and 16g+8 .. 16g+15 of lane group g), and
+// the activation stage holds 64 K values per row, read as the matching
+// contiguous 16-byte chunks 2g and 2g + 1.
+constexpr int QBN = 256;               // weight bytes per tile row (int8: columns)
 constexpr int QBK = 32;                // K rows per stage
 constexpr int QWSTAGE = QBK * QBN;     // 8 KB of weights per stage
 constexpr int QINS = QWSTAGE / 1024;   // weight DMA instructions per stage per wave (8)
@@ -557,7 +564,8 @@ typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 // B fragment for tile columns col .. col+15 (col % 16 == 0): lane gets column
-// col + lane%16, K rows 8 (lane/16) .. +7 of the stage, as 8 int8 codes ...
+// col + lane%16, byte rows 8 (lane/16) .. +7 of the stage (int8: 8 codes;
+// int4: 16 codes) ...
 __device__ __forceinline__ i32x2 read_q_frag(const lds_u8* st, int col, int lane) {
   const int s = lane & 15;
   const int r = 8 * (lane >> 4) + (s >> 1);
@@ -579,15 +587,33 @@ __device__ __forceinline__ bf16x8 q_to_bf16(i32x2 q) {
   const u32x4 v = {o[0], o[1], o[2], o[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
+// ... and, int4, the 8 codes of word w (K rows 8 in order: byte j holds rows
+// 2j (low nibble) and 2j + 1) as bf16
+__device__ __forceinline__ bf16x8 q4_to_bf16(int w) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = static_cast<float>((w << (28 - 8 * i)) >> 28);
+    const float hi = static_cast<float>((w << (24 - 8 * i)) >> 28);
+    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  }
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+  const u32x4 v = {o[0], o[1], o[2], o[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
 
-template <int MODE, int FMMAX>
+template <int MODE, int FMMAX, int QB>
 __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
+  static_assert(QB == 8 || QB == 4, "int8 or int4 codes");
   constexpr bool GU = MODE == MODE_GATEUP;
+  constexpr int KPS = QB == 8 ? QBK : 2 * QBK;  // K rows per stage
   constexpr int DBM = 16 * FMMAX;               // rows per tile
-  constexpr int ASTAGE = FMMAX * 1024;          // activation bytes per stage
+  constexpr int AROW = KPS * 2;                 // activation bytes per row per stage (64 / 128)
+  constexpr int AINS = 16 * AROW / 1024;        // activation DMA instructions per fragment (1 / 2)
+  constexpr int ASTAGE = FMMAX * 16 * AROW;     // activation bytes per stage
   constexpr int STAGE = QWSTAGE + ASTAGE;
-  constexpr int DNBUF = 4;
-  constexpr int LOADS = QINS + FMMAX;           // DMA instructions per stage per wave
+  constexpr int DNBUF = 4 * 4 * STAGE <= 160 * 1024 ? 4 : 3;   // per-wave ring depth within 160 KB
+  constexpr int LOADS = QINS + FMMAX * AINS;    // DMA instructions per stage per wave
   constexpr int PART = 4 * DBM * QPP * 4;       // the four waves' partial sums
   constexpr int RING = 4 * DNBUF * STAGE;
   constexpr int SMEM = RING > PART + 8 * DBM ? RING : PART + 8 * DBM;   // + per-row tables after PART
@@ -639,21 +665,23 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
     if (MODE == MODE_DOWN_ROUTED) row_out = p.perm[row_base + r];
   }
 
-  // ---- this block's K range (DOWN_SHARED: split over blockIdx.z in
-  // 128-row units) and this wave's quarter of it
+  // ---- this block's K range (DOWN_SHARED: split over blockIdx.z in units
+  // of 4 stages) and this wave's quarter of it
   const int nsplit = gridDim.z;
-  const int units = K >> 7;
+  const int units = K / (4 * KPS);
   const int u0 = static_cast<int>(blockIdx.z) * units / nsplit;
   const int u1 = (static_cast<int>(blockIdx.z) + 1) * units / nsplit;
-  const int ns = u1 - u0;                       // QBK-row stages per wave
-  const int k0 = u0 * 128 + wave * ns * QBK;
+  const int ns = u1 - u0;                       // stages per wave
+  const int k0 = u0 * 4 * KPS + wave * ns * KPS;
 
   // weights: DMA instruction i fills K rows 4i .. 4i+3 of the stage; lane ->
   // row 4i + lane/16, physical chunk lane%16 holding logical chunk
   // c = (lane%16) ^ (row & 15) = 16 columns: down n0 + 16c; gate/up chunks
   // 0..7 the gate columns n0 + 16c, 8..15 the up columns NH + n0 + 16 (c-8)
+  // (int4: byte rows are pairs of K rows)
+  const int kb0 = QB == 8 ? k0 : k0 / 2;         // first byte row of this wave
   const uint8_t* wbase = static_cast<const uint8_t*>(shared ? p.B_shared : p.B) +
-                         (shared ? 0 : static_cast<int64_t>(g) * K * ldb);
+                         (shared ? 0 : static_cast<int64_t>(g) * (QB == 8 ? K : K / 2) * ldb);
   int64_t w_off[QINS];
 #pragma unroll
   for (int i = 0; i < QINS; ++i) {
@@ -661,27 +689,39 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
     const int c = (lane & 15) ^ (kr & 15);
     const int oc = GU ? n0 + 16 * (c & 7) : n0 + 16 * c;       // output column of the chunk
     const int gc = (GU && c >= 8) ? NH + oc : oc;              // weight column
-    w_off[i] = static_cast<int64_t>(k0 + kr) * ldb + (oc < NH ? gc : 0);
+    w_off[i] = static_cast<int64_t>(kb0 + kr) * ldb + (oc < NH ? gc : 0);
   }
   const int64_t w_kstride = static_cast<int64_t>(QBK) * ldb;
 
-  // activations: DMA instruction f fills rows 16f .. 16f+15 (64 B each) of
-  // the stage's activation block; lane -> row 16f + lane/4, slot lane%4,
-  // which holds logical chunk slot ^ ((row >> 1) & 3).  GATEUP reads x
-  // (routed rows gathered through perm), DOWN the h rows in group order.
+  // activations, AROW bytes per row and stage.  int8: DMA instruction f
+  // fills rows 16f .. 16f+15 (64 B each); lane -> row 16f + lane/4, slot
+  // lane%4 holding logical chunk slot ^ ((row >> 1) & 3).  int4: instructions
+  // 2f, 2f+1 fill rows 16f + 8i + lane/8 (128 B each), slot lane%8 holding
+  // logical chunk slot ^ (row & 7).  GATEUP reads x (routed rows gathered
+  // through perm), DOWN the h rows in group order.
   const uint16_t* abase = static_cast<const uint16_t*>(shared ? p.A_shared : p.A);
-  int64_t a_off[FMMAX];
+  int64_t a_off[FMMAX * AINS];
 #pragma unroll
-  for (int f = 0; f < FMMAX; ++f) {
-    const int r = min(m0 + 16 * f + (lane >> 2), rows - 1);
-    const int arow = (GU && !shared) ? slot_token(p.perm[row_base + r], p.top_k) : row_base + r;
-    a_off[f] = static_cast<int64_t>(arow) * K + k0 + (((lane & 3) ^ ((lane >> 3) & 3)) * 8);
-  }
+  for (int f = 0; f < FMMAX; ++f)
+#pragma unroll
+    for (int i = 0; i < AINS; ++i) {
+      const int tr = QB == 8 ? (lane >> 2) : 8 * i + (lane >> 3);     // row within the fragment
+      const int slot = QB == 8 ? (lane & 3) : (lane & 7);
+      const int lc = QB == 8 ? (slot ^ ((tr >> 1) & 3)) : (slot ^ (tr & 7));
+      const int r = min(m0 + 16 * f + tr, rows - 1);
+      const int arow = (GU && !shared) ? slot_token(p.perm[row_base + r], p.top_k) : row_base + r;
+      a_off[f * AINS + i] = static_cast<int64_t>(arow) * K + k0 + lc * 8;
+    }
 
   const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem)) +
                         __builtin_amdgcn_readfirstlane(wave) * (DNBUF * STAGE);
   const lds_u8* ring_p = (const lds_u8*)smem + wave * (DNBUF * STAGE);
-  const int a_rd = QWSTAGE + (lane & 15) * 64 + (((lane >> 4) ^ ((lane >> 1) & 3)) << 4);
+  // A fragment of a step: row lane%16, K chunk lane/16 (int8) or chunk
+  // 2 (lane/16) + step (int4), at its swizzled slot
+  const int am = lane & 15, ag = lane >> 4;
+  const int a_rd = QB == 8 ? QWSTAGE + am * 64 + ((ag ^ ((am >> 1) & 3)) << 4)
+                           : QWSTAGE + am * 128 + (((2 * ag) ^ (am & 7)) << 4);
+  const int a_rd1 = QWSTAGE + am * 128 + (((2 * ag + 1) ^ (am & 7)) << 4);   // int4 second step
 
   f32x4 acc[FMMAX][QFN];
 #pragma unroll
@@ -695,8 +735,8 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
     const uint32_t b_ = ring + static_cast<uint32_t>(((st) % DNBUF) * STAGE);                  \
     _Pragma("unroll") for (int i = 0; i < QINS; ++i)                                           \
       dma16_nt(wbase + w_off[i] + s_ * w_kstride, b_ + i * 1024);                              \
-    _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
-      dma16(abase + a_off[f] + s_ * QBK, b_ + QWSTAGE + f * 1024);                             \
+    _Pragma("unroll") for (int f = 0; f < FMMAX * AINS; ++f)                                   \
+      dma16(abase + a_off[f] + s_ * KPS, b_ + QWSTAGE + f * 1024);                             \
   } while (0)
 #define Q8_STEP(kt)                                                                            \
   do {                                                                                         \
@@ -705,16 +745,39 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
     const lds_u8* st_ = ring_p + ((kt) % DNBUF) * STAGE;                                       \
     /* every LDS read of the stage in flight before the first use */                         \
     i32x2 wq[QFN];                                                                             \
-    bf16x8 af[FMMAX];                                                                          \
+    bf16x8 af[FMMAX], af1[FMMAX];                                                              \
     _Pragma("unroll") for (int j = 0; j < QFN; ++j) wq[j] = read_q_frag(st_, j * 16, lane);    \
-    _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
-      af[f] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(st_ + a_rd + f * 1024); \
-    bf16x8 wf[QFN];                                                                            \
-    _Pragma("unroll") for (int j = 0; j < QFN; ++j) wf[j] = q_to_bf16(wq[j]);                  \
-    _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                          \
-      if (f < fm)                                                                              \
-        _Pragma("unroll") for (int j = 0; j < QFN; ++j)                                        \
-          acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], wf[j], acc[f][j], 0, 0, 0); \
+    _Pragma("unroll") for (int f = 0; f < FMMAX; ++f) {                                        \
+      af[f] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(st_ + a_rd + f * 16 * AROW); \
+      if constexpr (QB == 4)                                                                   \
+        af1[f] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(st_ + a_rd1 + f * 16 * AROW); \
+    }                                                                                          \
+    if constexpr (QB == 8) {                                                                   \
+      bf16x8 wf[QFN];                                                                          \
+      _Pragma("unroll") for (int j = 0; j < QFN; ++j) wf[j] = q_to_bf16(wq[j]);                \
+      _Pragma("unroll") for (int f = 0; f < FMMAX; ++f)                                        \
+        if (f < fm)                                                                            \
+          _Pragma("unroll") for (int j = 0; j < QFN; ++j)                                      \
+            acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], wf[j], acc[f][j], 0, 0, 0); \
+    } else {                                                                                   \
+      /* codes converted per fragment (transient registers); one branch on */                 \
+      /* the valid row fragments, outside the fragment loop */                                \
+      if (FMMAX > 1 && fm > 1) {                                                               \
+        _Pragma("unroll") for (int j = 0; j < QFN; ++j) {                                      \
+          const bf16x8 w0 = q4_to_bf16(wq[j][0]), w1 = q4_to_bf16(wq[j][1]);                   \
+          _Pragma("unroll") for (int f = 0; f < FMMAX; ++f) {                                  \
+            acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], w0, acc[f][j], 0, 0, 0); \
+            acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af1[f], w1, acc[f][j], 0, 0, 0); \
+          }                                                                                    \
+        }                                                                                      \
+      } else {                                                                                 \
+        _Pragma("unroll") for (int j = 0; j < QFN; ++j) {                                      \
+          const bf16x8 w0 = q4_to_bf16(wq[j][0]), w1 = q4_to_bf16(wq[j][1]);                   \
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], w0, acc[0][j], 0, 0, 0);  \
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af1[0], w1, acc[0][j], 0, 0, 0); \
+        }                                                                                      \
+      }                                                                                        \
+    }                                                                                          \
     /* this stage's slot is refilled DNBUF-1 steps later: reads must be done */                \
     __builtin_amdgcn_s_waitcnt(0xC07F);                                                        \
   } while (0)
@@ -800,7 +863,7 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
   }
 }
 
-template <int MODE, int FMMAX>
+template <int MODE, int FMMAX, int QB>
 hipError_t launch_q8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* tiles_all) {
   constexpr int DBM = 16 * FMMAX;
   GemmArgs a = a0;
@@ -814,8 +877,9 @@ hipError_t launch_q8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* ti
   const int gn = (NH + (MODE == MODE_GATEUP ? QBN / 2 : QBN) - 1) / (MODE == MODE_GATEUP ? QBN / 2 : QBN);
   if (gm <= 0 || gn <= 0) return hipSuccess;
   const int ks = (MODE == MODE_DOWN_SHARED && a.ksplit > 1) ? a.ksplit : 1;
-  if (a.K % 128 != 0 || a.K / 128 < ks || NH % 16 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_q8_kernel<MODE, FMMAX>), dim3(gm, gn, ks), dim3(256), 0, s, a);
+  constexpr int unit = QB == 8 ? 128 : 256;   // K rows of 4 waves' stages
+  if (a.K % unit != 0 || a.K / unit < ks || NH % 16 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_q8_kernel<MODE, FMMAX, QB>), dim3(gm, gn, ks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -892,20 +956,24 @@ hipError_t launch_gemm_decode_tail(int mode, const GemmArgs& a0, int bm_main, hi
 hipError_t launch_gemm_decode(int mode, bool rows32, const GemmArgs& a, int T, hipStream_t s,
                               const int32_t* tiles_all) {
   if (a.w_int8) {
-    if (a.gu_part) return hipErrorInvalidValue;
-    if (rows32) {
-      switch (mode) {
-        case MODE_GATEUP: return launch_q8<MODE_GATEUP, 2>(a, T, s, tiles_all);
-        case MODE_DOWN_SHARED: return launch_q8<MODE_DOWN_SHARED, 2>(a, T, s, tiles_all);
-        case MODE_DOWN_ROUTED: return launch_q8<MODE_DOWN_ROUTED, 2>(a, T, s, tiles_all);
-      }
-    } else {
-      switch (mode) {
-        case MODE_GATEUP: return launch_q8<MODE_GATEUP, 1>(a, T, s, tiles_all);
-        case MODE_DOWN_SHARED: return launch_q8<MODE_DOWN_SHARED, 1>(a, T, s, tiles_all);
-        case MODE_DOWN_ROUTED: return launch_q8<MODE_DOWN_ROUTED, 1>(a, T, s, tiles_all);
-      }
+    if (a.gu_part || (a.w_int8 != 8 && a.w_int8 != 4)) return hipErrorInvalidValue;
+    const bool q4 = a.w_int8 == 4;
+#define Q8_DISPATCH(FM)                                                                        \
+    switch (mode) {                                                                            \
+      case MODE_GATEUP:                                                                        \
+        return q4 ? launch_q8<MODE_GATEUP, 1, 4>(a, T, s, tiles_all) : launch_q8<MODE_GATEUP, FM, 8>(a, T, s, tiles_all); \
+      case MODE_DOWN_SHARED:                                                                   \
+        return q4 ? launch_q8<MODE_DOWN_SHARED, 1, 4>(a, T, s, tiles_all)                      \
+                  : launch_q8<MODE_DOWN_SHARED, FM, 8>(a, T, s, tiles_all);                    \
+      case MODE_DOWN_ROUTED:                                                                   \
+        return q4 ? launch_q8<MODE_DOWN_ROUTED, 1, 4>(a, T, s, tiles_all)                      \
+                  : launch_q8<MODE_DOWN_ROUTED, FM, 8>(a, T, s, tiles_all);                    \
     }
+    // int4 takes 16-row tiles only: a 32-row int4 tile needs more registers
+    // than a wave has (its spills cost more than re-streaming the weights of
+    // the few groups with more than 16 rows)
+    if (rows32 && !q4) { Q8_DISPATCH(2) } else { Q8_DISPATCH(1) }
+#undef Q8_DISPATCH
     return hipErrorInvalidValue;
   }
   if (rows32) {

@@ -71,8 +71,9 @@ struct GemmArgs {
                            // reads x row slot_token(perm[.], top_k), grids cover T * top_k routed rows
   float* gu_part;          // weight-streaming GATEUP: write fp32 pre-activation partials [ksplit][T][2 N] here
                            // instead of h (K split over ksplit workgroups; null = normal epilogue)
-  int w_int8;              // weight-streaming kernels: B / B_shared hold int8 codes, sB / sB_shared their fp32
-                           // column scales (a GATEUP launch covers the routed groups or the shared one, not both)
+  int w_int8;              // weight-streaming kernels: 8 = B / B_shared hold int8 codes, 4 = int4 codes packed two
+                           // per byte along K (low nibble = even row), sB / sB_shared their fp32 column scales
+                           // (a GATEUP launch covers the routed groups or the shared one, not both); 0 = none
 };
 
 // Router in two launches: partial logits over K slices of d (the slice count

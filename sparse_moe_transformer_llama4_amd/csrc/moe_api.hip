@@ -46,14 +46,19 @@ bool config_dtypes_ok(const moe_config& c) {
   if (c.x_dtype == MOE_BF16 && c.w_dtype == MOE_BF16 && (c.out_dtype == MOE_F32 || c.out_dtype == MOE_BF16))
     return true;
   if (c.x_dtype == MOE_BF16 && c.w_dtype == MOE_E4M3 && c.out_dtype == MOE_BF16) return true;
-  if (c.x_dtype == MOE_BF16 && c.w_dtype == MOE_INT8 && (c.out_dtype == MOE_F32 || c.out_dtype == MOE_BF16))
+  if (c.x_dtype == MOE_BF16 && (c.w_dtype == MOE_INT8 || c.w_dtype == MOE_INT4) &&
+      (c.out_dtype == MOE_F32 || c.out_dtype == MOE_BF16))
     return true;
   return false;
 }
 
-bool scaled_weights(const moe_config& c) { return c.w_dtype == MOE_E4M3 || c.w_dtype == MOE_INT8; }
+bool scaled_weights(const moe_config& c) {
+  return c.w_dtype == MOE_E4M3 || c.w_dtype == MOE_INT8 || c.w_dtype == MOE_INT4;
+}
+bool int_weights(const moe_config& c) { return c.w_dtype == MOE_INT8 || c.w_dtype == MOE_INT4; }
 
-int k_multiple(const moe_config& c) { return scaled_weights(c) ? 128 : 64; }
+// int4: 4 waves x 64 K rows per stage of the weight-streaming tiles
+int k_multiple(const moe_config& c) { return c.w_dtype == MOE_INT4 ? 256 : scaled_weights(c) ? 128 : 64; }
 
 constexpr int64_t kDecodeTokensMax = 64;
 // Token count from which the bf16 prefill tiling is used.
@@ -63,16 +68,17 @@ constexpr int64_t kPrefillTokens = 256;
 // would leave most CUs idle): the number of partial shared outputs, summed in
 // order by the routed down GEMM.  1 for every other path.
 int decode_y_parts(const moe_config& c, int64_t T) {
-  if (T > kDecodeTokensMax || (c.w_dtype != MOE_BF16 && c.w_dtype != MOE_INT8)) return 1;
+  if (T > kDecodeTokensMax || (c.w_dtype != MOE_BF16 && !int_weights(c))) return 1;
+  const int unit = c.w_dtype == MOE_INT4 ? 256 : 128;   // K rows per part at least (4 waves' stages)
   for (int s = 8; s > 1; s >>= 1)
-    if (c.f_shared % (128 * s) == 0) return s;
+    if (c.f_shared % (unit * s) == 0) return s;
   return 1;
 }
 
 // The weight-streaming decode tiling serves bf16 calls of at most 64 tokens
 // and every int8 call (a plan with int8 weights takes at most 64 tokens).
 bool use_decode(const moe_config& c, int64_t T) {
-  return (c.w_dtype == MOE_BF16 || c.w_dtype == MOE_INT8) && T > 0 && T <= kDecodeTokensMax &&
+  return (c.w_dtype == MOE_BF16 || int_weights(c)) && T > 0 && T <= kDecodeTokensMax &&
          decode_supported(c.d) && decode_supported(c.f) && decode_supported(c.f_shared);
 }
 
@@ -109,7 +115,7 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   const size_t t = static_cast<size_t>(T);
   const size_t nb = (t + kRouteTokens - 1) / kRouteTokens;
   const bool fp8 = c.w_dtype == MOE_E4M3;
-  const size_t hsz = (c.w_dtype == MOE_BF16 || c.w_dtype == MOE_INT8) ? 2 : 4;  // e4m3: fp32 staging
+  const size_t hsz = (c.w_dtype == MOE_BF16 || int_weights(c)) ? 2 : 4;  // e4m3: fp32 staging
   const size_t ts = t * static_cast<size_t>(c.top_k > 1 ? c.top_k : 1);   // routing slots (routed rows)
   L.idx = take(ts * 4);
   L.gate = take(ts * 4);
@@ -261,7 +267,7 @@ GemmArgs gateup_args(const moe_config& c, const moe_weights* w, uint8_t* ws, con
                      const void* a_x, float* sx, uint32_t* amax_r, uint32_t* amax_s, int T) {
   const bool fp8 = scaled_weights(c);
   GemmArgs g{};
-  g.w_int8 = c.w_dtype == MOE_INT8;
+  g.w_int8 = c.w_dtype == MOE_INT8 ? 8 : c.w_dtype == MOE_INT4 ? 4 : 0;
   g.top_k = c.top_k;
   g.A = a_x;
   g.A_shared = a_x;
@@ -290,7 +296,7 @@ GemmArgs down_shared_args(const moe_config& c, const moe_weights* w, uint8_t* ws
                           const Route& R, const void* h_s, const float* sh_s, int T, int ksplit) {
   const bool fp8 = scaled_weights(c);
   GemmArgs g{};
-  g.w_int8 = c.w_dtype == MOE_INT8;
+  g.w_int8 = c.w_dtype == MOE_INT8 ? 8 : c.w_dtype == MOE_INT4 ? 4 : 0;
   g.A_shared = h_s;
   g.B_shared = w->ws_down;
   g.sB_shared = fp8 ? w->ss_down : nullptr;
@@ -311,7 +317,7 @@ GemmArgs down_routed_args(const moe_config& c, const moe_weights* w, uint8_t* ws
                           const Route& R, const void* h_r, const float* sh_r, void* out, int T, int y_parts) {
   const bool fp8 = scaled_weights(c);
   GemmArgs g{};
-  g.w_int8 = c.w_dtype == MOE_INT8;
+  g.w_int8 = c.w_dtype == MOE_INT8 ? 8 : c.w_dtype == MOE_INT4 ? 4 : 0;
   g.A = h_r;
   g.B = w->w_down;
   g.sB = fp8 ? w->s_down : nullptr;
@@ -594,8 +600,8 @@ moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
     const int km = k_multiple(c);
     if (c.d <= 0 || c.f <= 0 || c.f_shared <= 0 || c.d % km || c.f % km || c.f_shared % km)
       return MOE_ERR_UNSUPPORTED;
-    // int8 weights are a decode format: the weight-streaming tiles only
-    if (c.w_dtype == MOE_INT8 && c.max_tokens > kDecodeTokensMax) return MOE_ERR_SHAPE;
+    // int8 / int4 weights are decode formats: the weight-streaming tiles only
+    if (int_weights(c) && c.max_tokens > kDecodeTokensMax) return MOE_ERR_SHAPE;
   }
   moe_plan_s* p = new (std::nothrow) moe_plan_s;
   if (!p) return MOE_ERR_INVALID_ARGUMENT;
@@ -741,8 +747,8 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     g1.group_lo = 0;
     g1.group_hi = c.n_experts + 1;
     if ((e = launch_gemm_fp8(MODE_GATEUP, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
-  } else if (dec && c.w_dtype == MOE_INT8) {
-    // int8 tiles: the routed groups, then the shared expert
+  } else if (dec && int_weights(c)) {
+    // int8 / int4 tiles: the routed groups, then the shared expert
     g1.group_lo = 0;
     g1.group_hi = c.n_experts;
     if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles)) != hipSuccess)

@@ -15,9 +15,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libmoe355.so")
 
 MOE_ABI_VERSION = 2
-MOE_F32, MOE_BF16, MOE_E4M3, MOE_INT8 = 0, 1, 2, 3
-_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3, "i8": MOE_INT8}
-_TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.uint8, MOE_INT8: torch.int8}
+MOE_F32, MOE_BF16, MOE_E4M3, MOE_INT8, MOE_INT4 = 0, 1, 2, 3, 4
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3, "i8": MOE_INT8, "i4": MOE_INT4}
+# int4 codes travel packed, two per byte along K
+_TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.uint8, MOE_INT8: torch.int8,
+             MOE_INT4: torch.uint8}
 
 # names declared in include/moe.h
 symbols = ("moe_plan", "moe_plan_destroy", "moe_workspace_size", "moe_route", "moe_forward",

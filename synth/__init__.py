@@ -22,7 +22,8 @@ Generator (counter-based, identical on CPU and GPU):
 fp8 weights (OCP e4m3fn) are drawn in fp32 the same way and quantised per
 output column of the [K, N] layout: scale = amax over K / 448 (fp32), code =
 torch's float8_e4m3fn cast of clamp(w / scale, -448, 448).  int8 weights
-likewise: scale = amax over K / 127, code = round-half-even(w / scale).
+likewise: scale = amax over K / 127, code = round-half-even(w / scale); int4
+with 7 in place of 127, two codes per byte along K (low nibble = even row).
 
 Workloads with the RMSNorm in front of the block (norm_eps set) also draw its
 gain, w[j] = 1 + 0.1 * Q (fp32, then rounded to x's dtype), and give every
@@ -44,7 +45,8 @@ __all__ = [
     "gen_shared", "gen_norm_weight", "make_inputs", "DTYPES",
 ]
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn, "i8": torch.int8}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn, "i8": torch.int8,
+          "i4": torch.uint8}
 
 # ---------------------------------------------------------------- configs
 
@@ -103,6 +105,8 @@ EXTRA_CONFIGS = {
     # the MoE layer with the RMSNorm that precedes it (eps 1e-5)
     "scout_prefill_bf16_rmsnorm": MoEShape("scout_prefill_bf16_rmsnorm", T=4096, d=5120, E=16, f=8192,
                                            fs=8192, seed=7, norm_eps=1e-5),
+    "scout_decode_int4": MoEShape("scout_decode_int4", T=32, d=5120, E=16, f=8192, fs=8192, w_dtype="i4",
+                                  bias="cold", seed=2),
     # weight-only int8 decode on the Scout-shaped layer (the bf16 decode
     # workload's seed and routing)
     "scout_decode_int8": MoEShape("scout_decode_int8", T=32, d=5120, E=16, f=8192, fs=8192, w_dtype="i8",
@@ -320,12 +324,26 @@ def _quant_cols_int8(w32: torch.Tensor):
     return q, scale
 
 
+def _quant_cols_int4(w32: torch.Tensor):
+    """[K, N] fp32 -> (int4 codes packed along K as uint8 [K/2, N], fp32 scale [N]):
+    scale = amax over K / 7, code = round-half-even(w / scale) in -7..7, byte
+    (i, n) = code(2i, n) & 15 | (code(2i+1, n) & 15) << 4."""
+    amax = w32.abs().amax(dim=0)
+    scale = amax / torch.tensor(7.0, dtype=torch.float32, device=w32.device)
+    scale = torch.where(amax > 0, scale, torch.ones_like(scale))
+    q = torch.round(w32 / scale).clamp_(-7.0, 7.0).to(torch.int32)
+    packed = (q[0::2] & 15) | ((q[1::2] & 15) << 4)
+    return packed.to(torch.uint8), scale
+
+
 def _gen_matrix(cfg: MoEShape, stream: str, expert: int, K: int, N: int, device):
     v = normal_fp32(stream_key(cfg.seed, stream, expert), 0, K * N, cfg.w_std, device).view(K, N)
     if cfg.w_dtype == "e4m3":
         return _quant_cols_e4m3(v)
     if cfg.w_dtype == "i8":
         return _quant_cols_int8(v)
+    if cfg.w_dtype == "i4":
+        return _quant_cols_int4(v)
     return _round_to(v, cfg.w_dtype), None
 
 
@@ -355,7 +373,8 @@ def make_inputs(cfg: MoEShape, device="cpu") -> dict:
     """
     dev = torch.device(device)
     wdt = torch.uint8 if cfg.w_dtype == "e4m3" else DTYPES[cfg.w_dtype]
-    scaled = cfg.w_dtype in ("e4m3", "i8")
+    scaled = cfg.w_dtype in ("e4m3", "i8", "i4")
+    kd = 2 if cfg.w_dtype == "i4" else 1       # int4: two K rows per byte row
     E, d, f, fs = cfg.E, cfg.d, cfg.f, cfg.fs
     if E == 0:   # a dense layer: the shared gated MLP alone
         wsgu, ssgu, wsd, ssd = gen_shared(cfg, dev)
@@ -367,8 +386,8 @@ def make_inputs(cfg: MoEShape, device="cpu") -> dict:
         "x": gen_x(cfg, dev),
         "w_router": gen_router(cfg, dev),
         "router_bias": None if not cfg.has_bias else gen_bias(cfg).to(dev),
-        "w_gate_up": torch.empty((E, d, 2 * f), dtype=wdt, device=dev),
-        "w_down": torch.empty((E, f, d), dtype=wdt, device=dev),
+        "w_gate_up": torch.empty((E, d // kd, 2 * f), dtype=wdt, device=dev),
+        "w_down": torch.empty((E, f // kd, d), dtype=wdt, device=dev),
         "s_gate_up": None, "s_down": None, "ss_gate_up": None, "ss_down": None,
         "norm_weight": gen_norm_weight(cfg, dev),
     }

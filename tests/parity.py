@@ -8,7 +8,7 @@ import torch
 import synth
 from oracle import block
 
-TOL = {"f32": 1e-4, "bf16": 1e-2, "e4m3": 5e-2, "i8": 1e-2}
+TOL = {"f32": 1e-4, "bf16": 1e-2, "e4m3": 5e-2, "i8": 1e-2, "i4": 1e-2}
 
 
 def to_device(inp: dict, device) -> dict:

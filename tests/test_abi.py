@@ -75,7 +75,10 @@ def _plan(**kw):
     ({"w_dtype": 3, "d": 192}, UNSUPPORTED),
     ({"w_dtype": 3, "x_dtype": 0, "out_dtype": 0}, UNSUPPORTED),
     ({"w_dtype": 3, "n_experts": 0, "f": 0}, UNSUPPORTED),
-    ({"w_dtype": 4}, UNSUPPORTED),
+    ({"w_dtype": 4, "d": 256, "f": 512, "f_shared": 512}, OK),   # int4: widths % 256
+    ({"w_dtype": 4, "d": 384}, UNSUPPORTED),
+    ({"w_dtype": 4, "max_tokens": 65}, SHAPE),
+    ({"w_dtype": 5}, UNSUPPORTED),
     # the RMSNorm in front of the block
     ({"has_norm": 1, "norm_eps": 1e-5}, OK),
     ({"has_norm": 1, "norm_eps": 0.0, "x_dtype": 0, "w_dtype": 0, "out_dtype": 0}, OK),
@@ -168,7 +171,7 @@ def test_dense_layer_rejects_before_enqueue():
     lib.moe_plan_destroy(h)
 
 
-@pytest.mark.parametrize("wdt,odt", [(2, 1), (3, 0)])
+@pytest.mark.parametrize("wdt,odt", [(2, 1), (3, 0), (4, 0)])
 def test_scaled_weights_require_scales(wdt, odt):
     lib = moe.load_library()
     st, h = _plan(w_dtype=wdt, out_dtype=odt, max_tokens=8)

@@ -40,7 +40,7 @@ def test_generator_gpu_equals_cpu(gpu):
 @pytest.mark.parametrize("name", ["tiny_fp32", "scout_decode_bf16", "scout_prefill_bf16",
                                   "maverick_prefill_bf16", "maverick_prefill_fp8",
                                   "scout_prefill_bf16_rmsnorm", "maverick_prefill_fp8_rmsnorm",
-                                  "scout_decode_int8"])
+                                  "scout_decode_int8", "scout_decode_int4"])
 def test_fullsize_sampled(gpu, name):
     from sparse_moe_transformer_llama4_amd import moe
     cfg = synth.get_config(name)

@@ -452,3 +452,61 @@ def test_topk_route_only(gpu):
     torch.cuda.synchronize()
     w = block.Weights.from_dict(inp)
     check_routing(cfg, block.route_topk(inp["x"], *w.router(), 3), r)
+
+
+# ------------------------------------------------------------ weight-only int4 (decode)
+
+def _int4(name="decode_like_bf16", **kw):
+    return dataclasses.replace(synth.get_config(name), w_dtype="i4", name=f"{name}_i4", **kw)
+
+
+@pytest.mark.parametrize("T", [1, 2, 16, 17, 33, 64])
+def test_int4_decode_matches_oracle(gpu, T):
+    cfg = _int4(T=T)
+    print(f"[parity] int4 decode T={T}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    err, _ = check_forward(cfg, inp, out, routing)
+    print(f"[parity] int4 decode T={T} max|err|/RMS = {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("over", [dict(out_dtype="bf16"), dict(d=768, f=512, fs=1280, T=40),
+                                  dict(norm_eps=1e-5, T=24), dict(top_k=2, T=33)])
+def test_int4_decode_shapes_and_options(gpu, over):
+    # bf16 output; widths with a partial 256-column tile (d = 768) and
+    # 128-column gate/up tiles (fs = 1280); the RMSNorm; two experts per token
+    cfg = _int4(**over)
+    print(f"[parity] int4 {over}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    check_forward(cfg, inp, out, routing)
+
+
+def test_int4_one_hot_and_idle_scales_nan(gpu):
+    cfg = _int4(T=40, bias="cold", n_cold=0)
+    inp = synth.make_inputs(cfg)
+    inp["router_bias"] = torch.full((cfg.E,), -60.0)
+    inp["router_bias"][7] = 60.0
+    g = to_device(inp, gpu)
+    for e in range(cfg.E):
+        if e != 7:
+            g["s_gate_up"][e].fill_(float("nan")); g["s_down"][e].fill_(float("nan"))
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    assert int(routing["counts"][7]) == cfg.T
+    check_forward(cfg, inp, out, routing)
+
+
+def test_int4_side_stream_matches_serial_schedule(gpu):
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = _int4(T=33)
+    p = _plan(cfg)
+    w = to_device(synth.make_inputs(cfg), gpu)
+    ws = torch.empty(moe.moe_workspace_size(p, cfg.T), dtype=torch.uint8, device=gpu)
+    out = moe.moe_forward(p, w["x"], w, workspace=ws)
+    ev = moe.StageEvents()
+    out_t = torch.empty_like(out)
+    moe.moe_forward_timed(p, w["x"], w, ev, out=out_t, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_t)

@@ -13,7 +13,7 @@ import synth
 def _tiny(T, d, E, f, fs, mode, seed, bias=None):
     cfg = synth.MoEShape("t", T=T, d=d, E=E, f=f, fs=fs,
                          x_dtype="f32" if mode == "f32" else "bf16",
-                         w_dtype={"f32": "f32", "bf16": "bf16", "e4m3": "e4m3", "i8": "i8"}[mode],
+                         w_dtype={"f32": "f32", "bf16": "bf16", "e4m3": "e4m3", "i8": "i8", "i4": "i4"}[mode],
                          out_dtype="f32", seed=seed, w_std=0.3)
     inp = synth.make_inputs(cfg)
     if bias is not None:
@@ -21,16 +21,22 @@ def _tiny(T, d, E, f, fs, mode, seed, bias=None):
     return cfg, inp
 
 
-def _lists(inp, E):
+def _lists(inp, E, mode=None):
     w = block.Weights.from_dict(inp)
     ex = [w.expert(e) for e in range(E)]
     sh = w.shared()
     L = lambda a: a.tolist()
 
     def deq(a, s):
-        # int8 codes dequantised here with torch (not through oracle.block)
+        # int8 / int4 codes dequantised here with torch (not through oracle.block)
         if s is not None and a.dtype == torch.int8:
             return (a.double() * s.double()[None, :]).numpy()
+        if s is not None and mode == "i4":
+            b = a.to(torch.int32)
+            lo = (b & 15) - 16 * ((b & 15) >= 8).to(torch.int32)
+            hi = (b >> 4) - 16 * ((b >> 4) >= 8).to(torch.int32)
+            q = torch.stack([lo, hi], dim=1).reshape(2 * b.shape[0], b.shape[1])
+            return (q.double() * s.double()[None, :]).numpy()
         return block.weight_f64(a, s)
     return dict(
         x=L(block.to_f64(inp["x"])), wr=L(block.to_f64(inp["w_router"])),
@@ -42,7 +48,8 @@ def _lists(inp, E):
 
 CASES = [(0, 8, 4, 8, 8, "f32"), (1, 8, 1, 4, 4, "f32"), (7, 16, 3, 8, 4, "f32"),
          (16, 8, 5, 4, 8, "f32"), (9, 16, 4, 8, 8, "bf16"), (12, 16, 2, 8, 16, "bf16"),
-         (8, 16, 4, 8, 8, "e4m3"), (11, 8, 3, 4, 8, "e4m3"), (10, 16, 4, 8, 8, "i8"), (6, 8, 2, 4, 16, "i8")]
+         (8, 16, 4, 8, 8, "e4m3"), (11, 8, 3, 4, 8, "e4m3"), (10, 16, 4, 8, 8, "i8"), (6, 8, 2, 4, 16, "i8"),
+         (9, 16, 3, 8, 8, "i4"), (5, 8, 4, 4, 16, "i4")]
 
 
 @pytest.mark.parametrize("T,d,E,f,fs,mode", CASES)
@@ -50,7 +57,7 @@ def test_oracle_matches_brute_force(T, d, E, f, fs, mode):
     cfg, inp = _tiny(T, d, E, f, fs, mode, seed=T * 31 + E)
     w = block.Weights.from_dict(inp)
     out, r = block.forward(inp["x"], w, f, fs, mode)
-    lists = _lists(inp, E)
+    lists = _lists(inp, E, mode)
     bo, bidx, bgate = brute.forward(lists["x"], lists["wr"], lists["bias"], lists["w_gate_up"],
                                     lists["w_down"], lists["ws_gate_up"], lists["ws_down"], f, fs, mode)
     assert out.shape == (T, d)
@@ -325,12 +332,13 @@ def test_int8_weights_dequantise_to_code_times_column_scale():
 
 @pytest.mark.parametrize("T,d,E,f,fs,mode,k", [(9, 16, 4, 8, 8, "bf16", 2), (7, 8, 5, 4, 8, "f32", 3),
                                                 (6, 16, 4, 8, 8, "e4m3", 2), (5, 16, 3, 8, 8, "i8", 3),
+                                                (6, 16, 4, 8, 8, "i4", 2),
                                                 (8, 8, 4, 4, 4, "f32", 4)])
 def test_topk_matches_brute_force(T, d, E, f, fs, mode, k):
     cfg, inp = _tiny(T, d, E, f, fs, mode, seed=T * 17 + E + k)
     w = block.Weights.from_dict(inp)
     out, r = block.forward(inp["x"], w, f, fs, mode, top_k=k)
-    lists = _lists(inp, E)
+    lists = _lists(inp, E, mode)
     bo, bidx, bgate = brute.forward(lists["x"], lists["wr"], lists["bias"], lists["w_gate_up"],
                                     lists["w_down"], lists["ws_gate_up"], lists["ws_down"], f, fs, mode, top_k=k)
     np.testing.assert_array_equal(r.idx, np.array(bidx))
@@ -383,3 +391,11 @@ def test_topk_with_every_expert_is_order_free():
     g = block.sigmoid(lg)
     ref = block.combine_topk(inp["x"], np.tile(np.arange(4), (6, 1)), g, w, 8, 8, "f32")
     np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12 * np.abs(out).max())
+
+
+def test_int4_codes_unpack_two_per_byte_along_k():
+    # byte (i, n): low nibble = code(2i, n), high nibble = code(2i+1, n), two's complement
+    packed = np.array([[0x7F, 0x89], [0x10, 0xF0]], dtype=np.uint8)
+    np.testing.assert_array_equal(block.unpack_int4(packed), [[-1, -7], [7, -8], [0, 0], [1, -1]])
+    got = block.dequant_cols(torch.from_numpy(packed), torch.tensor([0.5, 2.0]), "i4")
+    np.testing.assert_array_equal(got, [[-0.5, -14.0], [3.5, -16.0], [0.0, 0.0], [0.5, -2.0]])

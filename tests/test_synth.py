@@ -104,3 +104,18 @@ def test_int8_weights_round_trip_within_half_a_step():
     q, s = inp["w_gate_up"][1].double(), inp["s_gate_up"][1].double()
     assert (q.abs() <= 127).all() and (q.abs().amax(dim=0) == 127).all()     # each column reaches +-127
     assert ((q * s - w32.double()).abs() <= s / 2 * (1 + 1e-6)).all()
+
+
+def test_int4_weights_pack_two_codes_per_byte_within_half_a_step():
+    cfg = synth.MoEShape("q4", T=4, d=256, E=2, f=128, fs=128, w_dtype="i4", seed=9)
+    inp = synth.make_inputs(cfg)
+    assert inp["w_gate_up"].dtype == torch.uint8 and tuple(inp["w_gate_up"].shape) == (2, 128, 256)
+    assert tuple(inp["w_down"].shape) == (2, 64, 256) and tuple(inp["ws_gate_up"].shape) == (128, 256)
+    w32 = synth.normal_fp32(synth.stream_key(cfg.seed, "w_gate_up", 1), 0, 256 * 256, cfg.w_std).view(256, 256)
+    b = inp["w_gate_up"][1].to(torch.int32)
+    lo = (b & 15) - 16 * ((b & 15) >= 8).to(torch.int32)
+    hi = (b >> 4) - 16 * ((b >> 4) >= 8).to(torch.int32)
+    q = torch.stack([lo, hi], dim=1).reshape(256, 256).double()
+    s = inp["s_gate_up"][1].double()
+    assert (q.abs() <= 7).all() and (q.abs().amax(dim=0) == 7).all()
+    assert ((q * s - w32.double()).abs() <= s / 2 * (1 + 1e-6)).all()
