@@ -588,15 +588,18 @@ __device__ __forceinline__ bf16x8 q_to_bf16(i32x2 q) {
   return __builtin_bit_cast(bf16x8, v);
 }
 // ... and, int4, the 8 codes of word w (K rows 8 in order: byte j holds rows
-// 2j (low nibble) and 2j + 1) as bf16
-__device__ __forceinline__ bf16x8 q4_to_bf16(int w) {
+// 2j (low nibble) and 2j + 1) as the bf16 values 136 + q, exactly: flipping
+// each nibble's top bit turns the two's-complement code q into u = q + 8 in
+// 0..15, and 0x4300 | u is the bf16 pattern of 128 + u.  Two AND/OR
+// operations per pair of codes; the kernel removes the offset 136 * sum_k x_k
+// once per row after the K loop.
+__device__ __forceinline__ bf16x8 q4_to_bf16_off(int w) {
+  const uint32_t b = static_cast<uint32_t>(w) ^ 0x88888888u;
   uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = static_cast<float>((w << (28 - 8 * i)) >> 28);
-    const float hi = static_cast<float>((w << (24 - 8 * i)) >> 28);
-    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-  }
+  o[0] = 0x43004300u | (b & 0xFu) | ((b & 0xF0u) << 12);
+  o[1] = 0x43004300u | ((b >> 8) & 0xFu) | ((b & 0xF000u) << 4);
+  o[2] = 0x43004300u | ((b >> 16) & 0xFu) | ((b >> 4) & 0xF0000u);
+  o[3] = 0x43004300u | ((b >> 24) & 0xFu) | ((b >> 12) & 0xF0000u);
   typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
   const u32x4 v = {o[0], o[1], o[2], o[3]};
   return __builtin_bit_cast(bf16x8, v);
@@ -604,7 +607,7 @@ __device__ __forceinline__ bf16x8 q4_to_bf16(int w) {
 
 template <int MODE, int FMMAX, int QB>
 __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
-  static_assert(QB == 8 || QB == 4, "int8 or int4 codes");
+  static_assert(QB == 8 || (QB == 4 && FMMAX == 1), "int8 codes, or int4 codes on 16-row tiles");
   constexpr bool GU = MODE == MODE_GATEUP;
   constexpr int KPS = QB == 8 ? QBK : 2 * QBK;  // K rows per stage
   constexpr int DBM = 16 * FMMAX;               // rows per tile
@@ -616,7 +619,8 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
   constexpr int LOADS = QINS + FMMAX * AINS;    // DMA instructions per stage per wave
   constexpr int PART = 4 * DBM * QPP * 4;       // the four waves' partial sums
   constexpr int RING = 4 * DNBUF * STAGE;
-  constexpr int SMEM = RING > PART + 8 * DBM ? RING : PART + 8 * DBM;   // + per-row tables after PART
+  constexpr int TABS = 8 * DBM + (QB == 4 ? 4 * 5 * DBM : 0);   // per-row tables after PART (+ int4 row sums)
+  constexpr int SMEM = RING > PART + TABS ? RING : PART + TABS;
   constexpr int OUTC = GU ? QBN / 2 : QBN;      // output columns per tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
@@ -728,6 +732,11 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
   for (int f = 0; f < FMMAX; ++f)
 #pragma unroll
     for (int j = 0; j < QFN; ++j) acc[f][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // int4: sum_k x[row][k] of this wave's K range, from one MFMA per step
+  // against a fragment of ones (every column of the result is the row sum)
+  f32x4 accx = f32x4{0.f, 0.f, 0.f, 0.f};
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
 #define Q8_ISSUE(st)                                                                           \
   do {                                                                                         \
@@ -760,22 +769,13 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
           _Pragma("unroll") for (int j = 0; j < QFN; ++j)                                      \
             acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], wf[j], acc[f][j], 0, 0, 0); \
     } else {                                                                                   \
-      /* codes converted per fragment (transient registers); one branch on */                 \
-      /* the valid row fragments, outside the fragment loop */                                \
-      if (FMMAX > 1 && fm > 1) {                                                               \
-        _Pragma("unroll") for (int j = 0; j < QFN; ++j) {                                      \
-          const bf16x8 w0 = q4_to_bf16(wq[j][0]), w1 = q4_to_bf16(wq[j][1]);                   \
-          _Pragma("unroll") for (int f = 0; f < FMMAX; ++f) {                                  \
-            acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], w0, acc[f][j], 0, 0, 0); \
-            acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af1[f], w1, acc[f][j], 0, 0, 0); \
-          }                                                                                    \
-        }                                                                                      \
-      } else {                                                                                 \
-        _Pragma("unroll") for (int j = 0; j < QFN; ++j) {                                      \
-          const bf16x8 w0 = q4_to_bf16(wq[j][0]), w1 = q4_to_bf16(wq[j][1]);                   \
-          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], w0, acc[0][j], 0, 0, 0);  \
-          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af1[0], w1, acc[0][j], 0, 0, 0); \
-        }                                                                                      \
+      /* codes converted per fragment (transient registers), 16-row tiles */                  \
+      accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], ones, accx, 0, 0, 0);              \
+      accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af1[0], ones, accx, 0, 0, 0);             \
+      _Pragma("unroll") for (int j = 0; j < QFN; ++j) {                                        \
+        const bf16x8 w0 = q4_to_bf16_off(wq[j][0]), w1 = q4_to_bf16_off(wq[j][1]);             \
+        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], w0, acc[0][j], 0, 0, 0);    \
+        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af1[0], w1, acc[0][j], 0, 0, 0);   \
       }                                                                                        \
     }                                                                                          \
     /* this stage's slot is refilled DNBUF-1 steps later: reads must be done */                \
@@ -805,14 +805,25 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
   }
   float* tab = reinterpret_cast<float*>(smem + PART);          // [DBM] gate scales
   int* ot = reinterpret_cast<int*>(smem + PART + 4 * DBM);     // [DBM] output rows
+  float* xw = reinterpret_cast<float*>(smem + PART + 8 * DBM); // int4: [4 waves][DBM] row sums, then [DBM] total
   if (tid < DBM) {
     tab[tid] = row_scale;
     ot[tid] = row_out;
   }
+  if constexpr (QB == 4) {
+    if (lcol == 0 && fm > 0)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xw[wave * DBM + rq + q] = accx[q];
+    __syncthreads();
+    if (tid < DBM) xw[4 * DBM + tid] = 136.0f * (((xw[tid] + xw[DBM + tid]) + xw[2 * DBM + tid]) + xw[3 * DBM + tid]);
+  }
   __syncthreads();
+  // the K-quarter sums in wave order (int4: less the code offset 136 sum_k x_k)
   auto total = [&](int r, int c) -> float {
-    return ((part[(0 * DBM + r) * QPP + c] + part[(1 * DBM + r) * QPP + c]) + part[(2 * DBM + r) * QPP + c]) +
-           part[(3 * DBM + r) * QPP + c];
+    const float v = ((part[(0 * DBM + r) * QPP + c] + part[(1 * DBM + r) * QPP + c]) + part[(2 * DBM + r) * QPP + c]) +
+                    part[(3 * DBM + r) * QPP + c];
+    if constexpr (QB == 4) return v - xw[4 * DBM + r];
+    return v;
   };
   const float* sbase = shared ? p.sB_shared : p.sB + static_cast<int64_t>(g) * ldb;
 
