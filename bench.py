@@ -109,7 +109,20 @@ def cpu_baseline(cfg, g, sample):
         what = (f"routing + every touched expert + shared), {int(np.count_nonzero(r.counts))} experts touched")
     dt = time.perf_counter() - t0
     norm = "RMSNorm + " if nw is not None else ""
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfgd = np.show_config(mode="dicts")
+        blas = cfgd.get("Build Dependencies", {}).get("blas", {}).get("name")
+    except Exception:   # numpy without the dict form
+        pass
     return {"value": sample / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas, "torch_threads": torch.get_num_threads(),
             "sample": f"first {sample} of {cfg.T} tokens, full fp64 block ({norm}{what}, {dt:.1f} s"}
 
 
@@ -121,6 +134,11 @@ def main():
     ap.add_argument("--config", default="scout_prefill_bf16")
     ap.add_argument("--cpu-sample", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weight-sets", type=int, default=None,
+                    help="independent copies of the weights the timed calls rotate over (default: 2 for "
+                         "decode-sized calls, so every call streams its weights from HBM, else 1)")
+    ap.add_argument("--latency-samples", type=int, default=None,
+                    help="calls timed one by one with events for the median / p90 (default 50 prefill, 200 decode)")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the core-clock sampling bursts (for profiler runs that count calls)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -151,6 +169,11 @@ def main():
     cfg = synth.get_config(args.config)
     print(f"[bench] generating {cfg.name} on {dev}", file=sys.stderr, flush=True)
     g = synth.make_inputs(cfg, dev)
+    # decode-sized calls rotate over independent weight copies (each far
+    # larger than the 256 MB last-level cache), so no call finds the previous
+    # call's weights in a cache
+    nsets = args.weight_sets or (2 if cfg.T <= 64 else 1)
+    gsets = [g] + [{k: (v if (v is None or k == "x") else v.clone()) for k, v in g.items()} for _ in range(nsets - 1)]
     torch.cuda.synchronize()
     plan = moe.Plan.for_shape(cfg)
     ws = torch.empty(max(moe.moe_workspace_size(plan, cfg.T), 256), dtype=torch.uint8, device=dev)
@@ -171,7 +194,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        moe.moe_forward(plan, g["x"], g, out=out, routing=routing, workspace=ws)
+        gk = gsets[k % nsets]
+        moe.moe_forward(plan, gk["x"], gk, out=out, routing=routing, workspace=ws)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
@@ -183,9 +207,23 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for k in range(args.steps):
-        moe.moe_forward_timed(plan, g["x"], g, events[k], out, ws, routing)
+        gk = gsets[k % nsets]
+        moe.moe_forward_timed(plan, gk["x"], gk, events[k], out, ws, routing)
     torch.cuda.synchronize()
     ms_timed = (time.perf_counter() - t1) / args.steps * 1e3
+
+    # per-call times (events on the caller's stream around each call): median, p90
+    nlat = args.latency_samples or (200 if cfg.T <= 64 else 50)
+    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nlat)]
+    for k, (e0, e1) in enumerate(ev_pairs):
+        gk = gsets[k % nsets]
+        e0.record()
+        moe.moe_forward(plan, gk["x"], gk, out=out, routing=routing, workspace=ws)
+        e1.record()
+    torch.cuda.synchronize()
+    lat = sorted(e0.elapsed_time(e1) for e0, e1 in ev_pairs)
+    ms_median = lat[len(lat) // 2]
+    ms_p90 = lat[min(len(lat) - 1, int(0.9 * len(lat)))]
 
     # core clock under this load (outside the timed regions): the MFMA peak
     # is quoted at 2.4 GHz, and the chip runs slower under heavy MFMA use
@@ -235,6 +273,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms,
         "ms_per_step_stage_timed": ms_timed,
+        "ms_median": ms_median,
+        "ms_p90": ms_p90,
+        "latency_samples": nlat,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -243,7 +284,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "f": cfg.f, "f_shared": cfg.fs,
                    "x_dtype": cfg.x_dtype, "w_dtype": cfg.w_dtype, "out_dtype": cfg.out_dtype,
                    "routing": cfg.bias, "experts_touched": sum(1 for c in counts if c > 0),
-                   "rmsnorm_eps": cfg.norm_eps, "top_k": cfg.top_k},
+                   "rmsnorm_eps": cfg.norm_eps, "top_k": cfg.top_k, "weight_sets": nsets},
         "block_tflops": F / t / 1e12,
         "block_gbps": B / t / 1e9,
         "mfma_frac": F / t / peak_f,
