@@ -136,7 +136,7 @@ typedef struct moe_config {
   int32_t w_dtype;         /* moe_dtype of the expert and shared weights */
   int32_t out_dtype;       /* moe_dtype of out */
   int32_t has_router_bias; /* 0 / 1 */
-  int64_t max_tokens;      /* largest T accepted by this plan (>= 1) */
+  int64_t max_tokens;      /* largest T accepted by this plan, 1..2^30, max_tokens * top_k < 2^31 */
   int32_t has_norm;        /* 0 / 1: the block starts with the RMSNorm below */
   float norm_eps;          /* RMSNorm epsilon (1e-5 in Llama 4), finite and >= 0; read when has_norm */
 } moe_config;

@@ -593,6 +593,7 @@ moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
   if (c.has_norm != 0 && c.has_norm != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c.has_norm && !(c.norm_eps >= 0.0f && c.norm_eps <= 3.4e38f)) return MOE_ERR_INVALID_ARGUMENT;
   if (c.max_tokens < 1 || c.max_tokens > (int64_t{1} << 30)) return MOE_ERR_SHAPE;
+  if (c.max_tokens * c.top_k >= (int64_t{1} << 31)) return MOE_ERR_SHAPE;   // routing slots are int32
   if (c.n_experts == 0) {
     // a dense layer: the shared gated MLP alone, bf16 weights, widths that
     // the weight-streaming and prefill tilings both take

@@ -55,6 +55,8 @@ def _plan(**kw):
     ({"top_k": 0}, UNSUPPORTED),
     ({"top_k": 9, "n_experts": 16}, UNSUPPORTED),
     ({"top_k": 8, "n_experts": 16}, OK),
+    ({"top_k": 8, "n_experts": 16, "max_tokens": 1 << 28}, SHAPE),     # 2^31 routing slots
+    ({"top_k": 7, "n_experts": 16, "max_tokens": 1 << 28}, OK),
     ({"top_k": 2, "n_experts": 0, "f": 0}, UNSUPPORTED),
     ({"d": 96}, UNSUPPORTED),
     ({"f": 100}, UNSUPPORTED),
