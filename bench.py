@@ -349,12 +349,18 @@ def sample_clock_mhz(run, seconds=0.5):
 
 
 def _kernel_source_hash() -> str:
+    """Hash of the library's code (comments and whitespace left out): the
+    recorded traffic is valid while this matches the hash stored with it."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_moe_transformer_llama4_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            src = open(os.path.join(csrc, f)).read()
+            src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+            src = re.sub(r"//[^\n]*", " ", src)
+            h.update(f.encode() + b"\0" + " ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,7 +10,10 @@ Contents
   numerics  bf16 and OCP e4m3fn rounding written from the format definitions
   block     the block itself in fp64 (router, top-1, sigmoid gate on the
             input, routed + shared SwiGLU experts, combine) with the
-            rounding points of the reduced-precision variants emulated
+            rounding points of the reduced-precision variants emulated;
+            the optional RMSNorm in front, k experts per token, dense
+            layers (no routed experts), and int8 / int4 / e4m3 weight codes
+            dequantised with their column scales
   brute     pure-Python loops that evaluate every expert densely, then select
   arith     the pages' parameter / FLOP / KV-cache arithmetic
 

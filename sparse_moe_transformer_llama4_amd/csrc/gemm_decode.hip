@@ -1,4 +1,6 @@
-// bf16 grouped GEMMs for decode-sized token counts (gfx950).
+// Weight-streaming grouped GEMMs for decode-sized token counts (gfx950):
+// bf16 weights (also the routed tails of bf16 prefill and dense decode),
+// and int8 / int4 weight codes (gemm_q8_kernel, further below).
 //
 // With a few tokens per expert the block is a weight stream: every touched
 // expert's W_gate_up and W_down are read once from HBM and each weight is
