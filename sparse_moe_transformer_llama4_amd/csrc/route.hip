@@ -273,7 +273,6 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
   static_assert(XDT == DT_BF16 || !QUANT, "e4m3 codes come from bf16 rows");
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
   constexpr int V = XDT == DT_BF16 ? 8 : 4;   // elements per 16-byte chunk
   constexpr int ES = XDT == DT_BF16 ? 2 : 4;  // bytes per element
   // NCH chunks per lane are held in registers (the launcher picks the
@@ -288,18 +287,25 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
   const bool resident = nch <= NCH;
   const uint8_t* xrow = static_cast<const uint8_t*>(x) + static_cast<int64_t>(t) * d * ES;
   const uint8_t* wrow = static_cast<const uint8_t*>(w);
-  // x and the gain (the same for every row: an L1 / L2 hit) are loaded
-  // together, so the gain's latency hides behind x's
-  uint4 xr[NCH], wr[NCH];
+  // the gain, the same for every row: staged in LDS once per workgroup for
+  // a resident row (chunk c of lane l at c * 64 + l), so the registers hold
+  // x alone and more rows are in flight
+  __shared__ uint4 wl[NCH * 64];
+  if (resident)
+    for (int i = threadIdx.x; i < nch * 64; i += 256)
+      if (i * V < d) wl[i] = *reinterpret_cast<const uint4*>(wrow + static_cast<int64_t>(i) * V * ES);
+  __syncthreads();
+  if (t >= T) return;
+  uint4 xr[NCH];
   auto valid = [&](int g0, int c) { return g0 + c < nch && (g0 + c) * step + lane * V < d; };
   auto load_group = [&](int g0) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
-      if (valid(g0, c)) {
-        const int64_t k = (g0 + c) * step + lane * V;
-        xr[c] = *reinterpret_cast<const uint4*>(xrow + k * ES);
-        wr[c] = *reinterpret_cast<const uint4*>(wrow + k * ES);
-      }
+      if (valid(g0, c)) xr[c] = *reinterpret_cast<const uint4*>(xrow + static_cast<int64_t>((g0 + c) * step + lane * V) * ES);
+  };
+  auto wchunk = [&](int g0, int c) -> uint4 {
+    if (resident) return wl[c * 64 + lane];
+    return *reinterpret_cast<const uint4*>(wrow + static_cast<int64_t>((g0 + c) * step + lane * V) * ES);
   };
   auto unpack = [](const uint4& q, float (&v)[V]) {
     const uint32_t u[4] = {q.x, q.y, q.z, q.w};
@@ -315,8 +321,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
     }
   };
 
-  // pass 1: sum of squares (fp64)
-  double ss = 0.0;
+  // pass 1: sum of squares (fp64; four independent partial sums per lane
+  // keep the dependent FMA chains short)
+  double ssp[4] = {0.0, 0.0, 0.0, 0.0};
   for (int g0 = 0; g0 < nch; g0 += NCH) {
     load_group(g0);
 #pragma unroll
@@ -325,19 +332,21 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
         float v[V];
         unpack(xr[c], v);
 #pragma unroll
-        for (int i = 0; i < V; ++i) ss = fma(static_cast<double>(v[i]), static_cast<double>(v[i]), ss);
+        for (int i = 0; i < V; ++i)
+          ssp[i & 3] = fma(static_cast<double>(v[i]), static_cast<double>(v[i]), ssp[i & 3]);
       }
   }
+  double ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m, 64);
   const double r = 1.0 / sqrt(ss / static_cast<double>(d) + static_cast<double>(eps));
   const float r32 = static_cast<float>(r);
 
   // the normalised values of chunk c, as stored (rounded once to the row dtype)
-  auto normed = [&](int c, float (&y)[V]) {
+  auto normed = [&](int g0, int c, float (&y)[V]) {
     float v[V], wv[V];
     unpack(xr[c], v);
-    unpack(wr[c], wv);
+    unpack(wchunk(g0, c), wv);
     if constexpr (XDT == DT_BF16) {
       float yf[V];
       bool near = false;
@@ -376,7 +385,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
       for (int c = 0; c < NCH; ++c) {
         if (!valid(g0, c)) continue;
         float y[V];
-        normed(c, y);
+        normed(g0, c, y);
         if constexpr (XDT == DT_BF16)
           *reinterpret_cast<uint4*>(static_cast<uint16_t*>(xn) + out_index(g0, c)) = pack_bf16(y);
         else
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
       for (int c = 0; c < NCH; ++c) {
         if (!valid(g0, c)) continue;
         float y[V];
-        normed(c, y);
+        normed(g0, c, y);
 #pragma unroll
         for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(y[i]));
         const uint4 yb = pack_bf16(y);
@@ -413,7 +422,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
         if (!valid(g0, c)) continue;
         float y[V];
         if (resident) unpack(xr[c], y);
-        else normed(c, y);
+        else normed(g0, c, y);
 #pragma unroll
         for (int i = 0; i < V; ++i) y[i] = y[i] / s;
         *reinterpret_cast<uint2*>(xq + out_index(g0, c)) =
