@@ -138,7 +138,8 @@ def main():
                     help="independent copies of the weights the timed calls rotate over (default: 2 for "
                          "decode-sized calls, so every call streams its weights from HBM, else 1)")
     ap.add_argument("--latency-samples", type=int, default=None,
-                    help="calls timed one by one with events for the median / p90 (default 50 prefill, 200 decode)")
+                    help="calls timed one by one with events for the median / p90 (default 50 prefill, "
+                         "200 decode; 0 skips them, e.g. for profiler runs that count calls)")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the core-clock sampling bursts (for profiler runs that count calls)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -213,7 +214,7 @@ def main():
     ms_timed = (time.perf_counter() - t1) / args.steps * 1e3
 
     # per-call times (events on the caller's stream around each call): median, p90
-    nlat = args.latency_samples or (200 if cfg.T <= 64 else 50)
+    nlat = args.latency_samples if args.latency_samples is not None else (200 if cfg.T <= 64 else 50)
     ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nlat)]
     for k, (e0, e1) in enumerate(ev_pairs):
         gk = gsets[k % nsets]
@@ -222,8 +223,8 @@ def main():
         e1.record()
     torch.cuda.synchronize()
     lat = sorted(e0.elapsed_time(e1) for e0, e1 in ev_pairs)
-    ms_median = lat[len(lat) // 2]
-    ms_p90 = lat[min(len(lat) - 1, int(0.9 * len(lat)))]
+    ms_median = lat[len(lat) // 2] if lat else None
+    ms_p90 = lat[min(len(lat) - 1, int(0.9 * len(lat)))] if lat else None
 
     # core clock under this load (outside the timed regions): the MFMA peak
     # is quoted at 2.4 GHz, and the chip runs slower under heavy MFMA use
