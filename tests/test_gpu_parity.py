@@ -208,14 +208,22 @@ def test_side_stream_matches_serial_schedule(gpu, name, T):
     check_forward(cfg, inp, out, routing)
 
 
-@pytest.mark.parametrize("name", ["small_fp32", "small_fp8", "decode_like_bf16", "small_bf16_tall"])
-def test_graph_capture_replays_match_eager(gpu, name):
+GRAPH_CASES = [("small_fp32", {}), ("small_fp8", {}), ("decode_like_bf16", {}), ("small_bf16_tall", {}),
+               ("decode_like_bf16", dict(w_dtype="i8", T=33)), ("decode_like_bf16", dict(w_dtype="i4", T=33)),
+               ("decode_like_bf16", dict(top_k=2, T=33)), ("small_bf16_tall", dict(top_k=2)),
+               ("small_bf16_tall", dict(norm_eps=1e-5)), ("small_fp8", dict(norm_eps=1e-5, top_k=2)),
+               ("small_dense_bf16", dict(T=40)), ("small_dense_bf16", dict(T=300))]
+
+
+@pytest.mark.parametrize("name,over", GRAPH_CASES)
+def test_graph_capture_replays_match_eager(gpu, name, over):
     # moe_forward captured into a HIP graph (its side stream forks from and
     # joins the capturing stream) replays to the eager result, with eager
-    # work on the GPU between the replays
+    # work on the GPU between the replays: every schedule, including int8 /
+    # int4 weights, k picks per token, the RMSNorm in front and dense layers
     from sparse_moe_transformer_llama4_amd import moe
-    cfg = synth.get_config(name)
-    print(f"[parity] graph capture {name}", flush=True)
+    cfg = dataclasses.replace(synth.get_config(name), **over)
+    print(f"[parity] graph capture {name} {over}", flush=True)
     g = to_device(synth.make_inputs(cfg), gpu)
     p = _plan(cfg)
     ws = torch.empty(max(moe.moe_workspace_size(p, cfg.T), 256), dtype=torch.uint8, device=gpu)
