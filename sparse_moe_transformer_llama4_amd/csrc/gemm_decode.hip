@@ -589,22 +589,32 @@ __device__ __forceinline__ bf16x8 q_to_bf16(i32x2 q) {
   const u32x4 v = {o[0], o[1], o[2], o[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
-// ... and, int4, the 8 codes of word w (K rows 8 in order: byte j holds rows
-// 2j (low nibble) and 2j + 1) as the bf16 values 136 + q, exactly: flipping
-// each nibble's top bit turns the two's-complement code q into u = q + 8 in
-// 0..15, and 0x4300 | u is the bf16 pattern of 128 + u.  Two AND/OR
-// operations per pair of codes; the kernel removes the offset 136 * sum_k x_k
-// once per row after the K loop.
+// ... and, int4, the 8 codes of word w (K rows 0..7: byte j holds rows 2j
+// (low nibble) and 2j + 1) as the bf16 values 136 + q, exactly, in the K
+// order 0 2 4 6 1 3 5 7: flipping each nibble's top bit turns the
+// two's-complement code q into u = q + 8 in 0..15, and the bf16 pattern
+// 0x43 | u (high byte 0x43, low byte u) is 128 + u.  The even rows' nibbles,
+// masked, are bytes 0..3 of one word and the odd rows' of another; a byte
+// permute then pairs two of them with 0x43 bytes per output dword (eight
+// operations for eight codes).  The A fragment is put in the same K order
+// (a4_order); the kernel removes the offset 136 * sum_k x_k once per row
+// after the K loop.
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4q;
 __device__ __forceinline__ bf16x8 q4_to_bf16_off(int w) {
   const uint32_t b = static_cast<uint32_t>(w) ^ 0x88888888u;
-  uint32_t o[4];
-  o[0] = 0x43004300u | (b & 0xFu) | ((b & 0xF0u) << 12);
-  o[1] = 0x43004300u | ((b >> 8) & 0xFu) | ((b & 0xF000u) << 4);
-  o[2] = 0x43004300u | ((b >> 16) & 0xFu) | ((b >> 4) & 0xF0000u);
-  o[3] = 0x43004300u | ((b >> 24) & 0xFu) | ((b >> 12) & 0xF0000u);
-  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-  const u32x4 v = {o[0], o[1], o[2], o[3]};
-  return __builtin_bit_cast(bf16x8, v);
+  const uint32_t ev = b & 0x0F0F0F0Fu, od = (b >> 4) & 0x0F0F0F0Fu;
+  constexpr uint32_t kHi = 0x43434343u;
+  const u32x4q o = {__builtin_amdgcn_perm(kHi, ev, 0x04010400u), __builtin_amdgcn_perm(kHi, ev, 0x04030402u),
+                    __builtin_amdgcn_perm(kHi, od, 0x04010400u), __builtin_amdgcn_perm(kHi, od, 0x04030402u)};
+  return __builtin_bit_cast(bf16x8, o);
+}
+// A fragment of K rows 0..7 (in order, two per dword) -> K order 0 2 4 6
+// 1 3 5 7: the low halves of dwords 0, 1, then 2, 3, then the high halves
+__device__ __forceinline__ bf16x8 a4_order(bf16x8 a) {
+  const u32x4q v = __builtin_bit_cast(u32x4q, a);
+  const u32x4q r = {__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+                    __builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 template <int MODE, int FMMAX, int QB>
@@ -772,12 +782,17 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
             acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], wf[j], acc[f][j], 0, 0, 0); \
     } else {                                                                                   \
       /* codes converted per fragment (transient registers), 16-row tiles */                  \
+      af[0] = a4_order(af[0]);                                                                 \
+      af1[0] = a4_order(af1[0]);                                                               \
       accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], ones, accx, 0, 0, 0);              \
       accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af1[0], ones, accx, 0, 0, 0);             \
+      /* one fragment at a time: converted just before its two MFMAs (the    */                \
+      /* scheduler would otherwise convert all 32 words first and keep them) */                \
       _Pragma("unroll") for (int j = 0; j < QFN; ++j) {                                        \
         const bf16x8 w0 = q4_to_bf16_off(wq[j][0]), w1 = q4_to_bf16_off(wq[j][1]);             \
         acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], w0, acc[0][j], 0, 0, 0);    \
         acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af1[0], w1, acc[0][j], 0, 0, 0);   \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
       }                                                                                        \
     }                                                                                          \
     /* this stage's slot is refilled DNBUF-1 steps later: reads must be done */                \

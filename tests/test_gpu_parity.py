@@ -31,6 +31,19 @@ def test_forward_matches_oracle(gpu, name):
     print(f"[parity] {name} max|err|/RMS = {err:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("name,over", [("small_bf16", dict(d=2560)), ("small_bf16_tall", dict(d=2304)),
+                                       ("small_fp8", dict(d=2560)), ("small_bf16_tall", dict(d=2560, top_k=2))])
+def test_down_ntiles_not_multiple_of_8(gpu, name, over):
+    # down GEMMs with 9 or 10 column tiles: the tiles are shared out over
+    # the XCDs in equal contiguous runs of the row-major tile list
+    cfg = dataclasses.replace(synth.get_config(name), name=f"{name}_d{over['d']}", **over)
+    print(f"[parity] {cfg.name} T={cfg.T} d={cfg.d} {cfg.w_dtype} k={cfg.top_k}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    check_forward(cfg, inp, out, routing)
+
+
 @pytest.mark.parametrize("name", ["small_bf16", "small_fp32", "small_fp8"])
 def test_deterministic(gpu, name):
     cfg = synth.get_config(name)
