@@ -9,11 +9,12 @@ namespace moe {
 
 constexpr int kWave = 64;
 
-// Tile heights the device-side scheduler publishes tile tables for.
-constexpr int kNumBM = 5;
-__host__ __device__ constexpr int bm_of(int i) { return 16 << i; }  // 16, 32, 64, 128, 256
+// Tile heights the device-side scheduler publishes tile tables for: 16, 32,
+// 64, 128, 256, and 160 (the e4m3 gate/up tiles for groups of ~100..160 rows).
+constexpr int kNumBM = 6;
+__host__ __device__ constexpr int bm_of(int i) { return i < 5 ? 16 << i : 160; }
 __host__ __device__ constexpr int bm_index(int bm) {
-  return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : 4;
+  return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : bm == 256 ? 4 : 5;
 }
 
 // Tile tables published by the routing stage, each [E + 2] int32 (entry g =

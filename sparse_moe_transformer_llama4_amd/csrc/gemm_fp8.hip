@@ -37,17 +37,13 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-constexpr int BM = 128, BN = 256, WM = 2, WN = 2;
+constexpr int BN = 256, WM = 2, WN = 2;
 constexpr int BK = 128;                  // K bytes per stage = one MFMA step
 constexpr int NBUF = 3;
 constexpr int A_ROWB = BK;               // 128 B per A row
 constexpr int B_ROWB = BN;               // 256 B per weight row
-constexpr int A_STAGE = BM * A_ROWB;     // 16 KB
 constexpr int B_STAGE = BK * B_ROWB;     // 32 KB
-constexpr int A_INS = A_STAGE / 1024 / 4;
 constexpr int B_INS = B_STAGE / 1024 / 4;
-constexpr int LOADS = A_INS + B_INS;
-constexpr int FM = BM / WM / 16;         // 4
 constexpr int FN = BN / WN / 16;         // 8
 
 // Chunk permutation of an A row (see the header comment): XOR of 5, 7 and 1
@@ -71,10 +67,18 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 }
 
 
-template <int MODE>
+// BM = 128 or 160 rows (the 160-row gate/up tile takes a group of up to 160
+// rows whole where 128-row tiles would add a second, nearly empty tile)
+template <int MODE, int BM>
 __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
   constexpr bool GATEUP = MODE == MODE_GATEUP;
   constexpr int BNH = GATEUP ? BN / 2 : BN;
+  constexpr int A_STAGE = BM * A_ROWB;   // 16 / 20 KB
+  constexpr int A_INS = A_STAGE / 1024 / 4;
+  constexpr int LOADS = A_INS + B_INS;
+  constexpr int FM = BM / WM / 16;       // 4 / 5
+  static_assert((BM == 128 || BM == 160) && A_INS * 4 * 1024 == A_STAGE, "tile rows");
+  static_assert(NBUF * (A_STAGE + B_STAGE) <= 160 * 1024, "ring fits the LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * (A_STAGE + B_STAGE)];
   lds_u8* const As = (lds_u8*)(smem);
   lds_u8* const Bs = As + NBUF * A_STAGE;
@@ -230,10 +234,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
 #define F8_DMA_B(i, st, SL)                                                                    \
   dma16(b_src + static_cast<int64_t>(min((st), nk - 1)) * b_kstep, b_voff[i], b_lds0 + (SL) * B_STAGE + (i) * 1024)
 
-  // Operands in registers: all of a stage's fragments double-buffered.
+  // Operands in registers: all of a stage's fragments double-buffered; the
+  // 160-row tile (ASB) keeps one set of A fragments, each refilled with the
+  // next stage's fragment right after its last MFMA of the stage (the
+  // registers of a second set would not fit beside its 160 accumulators).
+  constexpr bool ASB = BM == 160;
   i32x8 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
+  i32x8 (&fa_odd)[FM] = ASB ? fa0 : fa1;
   constexpr int NMF = FM * FN;
-  constexpr int NOPS = FM + FN + A_INS + B_INS;
+  constexpr int NOPS = (ASB ? 0 : FM) + FN + A_INS + B_INS;   // spread through the MFMA stream
   // One stage (step kt + R, slot R % NBUF free, operands FA/FB): the MFMA
   // stream starts right after the previous barrier; the reads of the next
   // stage's fragments and then the DMA of stage kt + R + NBUF into the free
@@ -246,12 +255,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
     _Pragma("unroll") for (int m_ = 0; m_ < NMF; ++m_) {                                       \
       acc[m_ / FN][m_ % FN] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(               \
           FA[m_ / FN], FB[m_ % FN], acc[m_ / FN][m_ % FN], 0, 0, 0, 127, 0, 127);              \
+      if constexpr (ASB)                                                                       \
+        if (m_ % FN == FN - 1) F8_AREAD(FA, m_ / FN, nsl_);                                    \
       _Pragma("unroll") for (int o_ = 0; o_ < NOPS; ++o_) {                                    \
         if (o_ * NMF / NOPS == m_) {                                                           \
-          if (o_ < FM) F8_AREAD(FA2, o_, nsl_);                                                \
-          else if (o_ < FM + FN) F8_BREAD(FB2, o_ - FM, nsl_);                                 \
-          else if (o_ < FM + FN + A_INS) F8_DMA_A(o_ - FM - FN, sd_, sl_);                     \
-          else F8_DMA_B(o_ - FM - FN - A_INS, sd_, sl_);                                       \
+          const int u_ = o_ + (ASB ? FM : 0);                                                  \
+          if (u_ < FM) F8_AREAD(FA2, u_, nsl_);                                                \
+          else if (u_ < FM + FN) F8_BREAD(FB2, u_ - FM, nsl_);                                 \
+          else if (u_ < FM + FN + A_INS) F8_DMA_A(u_ - FM - FN, sd_, sl_);                     \
+          else F8_DMA_B(u_ - FM - FN - A_INS, sd_, sl_);                                       \
         }                                                                                      \
       }                                                                                        \
       __builtin_amdgcn_sched_barrier(0);                                                       \
@@ -288,22 +300,22 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
-    F8_STEP(0, fa0, fb0, fa1, fb1);
-    F8_STEP(1, fa1, fb1, fa0, fb0);
-    F8_STEP(2, fa0, fb0, fa1, fb1);
-    F8_STEP(3, fa1, fb1, fa0, fb0);
-    F8_STEP(4, fa0, fb0, fa1, fb1);
-    F8_STEP(5, fa1, fb1, fa0, fb0);
+    F8_STEP(0, fa0, fb0, fa_odd, fb1);
+    F8_STEP(1, fa_odd, fb1, fa0, fb0);
+    F8_STEP(2, fa0, fb0, fa_odd, fb1);
+    F8_STEP(3, fa_odd, fb1, fa0, fb0);
+    F8_STEP(4, fa0, fb0, fa_odd, fb1);
+    F8_STEP(5, fa_odd, fb1, fa0, fb0);
   }
   if (kt < nk) {
-    F8_STEP(0, fa0, fb0, fa1, fb1);
+    F8_STEP(0, fa0, fb0, fa_odd, fb1);
     if (kt + 1 < nk) {
-      F8_STEP(1, fa1, fb1, fa0, fb0);
+      F8_STEP(1, fa_odd, fb1, fa0, fb0);
       if (kt + 2 < nk) {
-        F8_STEP(2, fa0, fb0, fa1, fb1);
+        F8_STEP(2, fa0, fb0, fa_odd, fb1);
         if (kt + 3 < nk) {
-          F8_STEP(3, fa1, fb1, fa0, fb0);
-          if (kt + 4 < nk) F8_STEP(4, fa0, fb0, fa1, fb1);
+          F8_STEP(3, fa_odd, fb1, fa0, fb0);
+          if (kt + 4 < nk) F8_STEP(4, fa0, fb0, fa_odd, fb1);
         }
       }
     }
@@ -347,13 +359,14 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
   // memory sees 16-byte row chunks instead of scattered 4-byte stores.
   typedef __attribute__((address_space(3))) float lds_f32;
   typedef __attribute__((address_space(3))) int lds_i32;
-  lds_u8* const stage = As + 1024;
+  constexpr int TABB = (8 * BM + 1023) / 1024 * 1024;   // the two row tables, rounded to 1 KB
+  lds_u8* const stage = As + TABB;
   if constexpr (GATEUP) {
     // h tile [BM][BNH] fp32 (row pitch HP bytes), then 16-byte chunks with the
     // per-row max |h| reduced over the lanes that share a row
     constexpr int HF = FN / 2;
     constexpr int HP = BNH * 4 + 16;
-    static_assert(1024 + BM * HP <= NBUF * (A_STAGE + B_STAGE), "h staging fits the ring");
+    static_assert(TABB + BM * HP <= NBUF * (A_STAGE + B_STAGE), "h staging fits the ring");
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
@@ -385,62 +398,71 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
       if (cc == 0 && m0 + r < rows) atomicMax(&amax[row_base + m0 + r], __float_as_uint(m));
     }
   } else {
-    // scaled fp32 tile [BM][BN] (row pitch FPB bytes), then 16-byte chunks:
+    // scaled fp32 tile [PR][BN] (row pitch FPB bytes) in passes of PR rows
+    // (160-row tiles: two passes, one per wave row), then 16-byte chunks:
     // shared down stores them; routed down adds the shared expert's output,
-    // loaded for 16 chunks at a time before they are stored
+    // loaded for NB chunks at a time before they are stored
     constexpr int FPB = BN * 4 + 16;
-    static_assert(1024 + BM * FPB <= NBUF * (A_STAGE + B_STAGE), "fp32 staging fits the ring");
+    constexpr int PR = TABB + BM * FPB <= NBUF * (A_STAGE + B_STAGE) ? BM : BM / WM;
+    static_assert(TABB + PR * FPB <= NBUF * (A_STAGE + B_STAGE), "fp32 staging fits the ring");
     constexpr int CPR = BN / 4;
-    constexpr int NB = 16;
-    static_assert((BM * CPR) % (256 * NB) == 0, "whole batches");
+    constexpr int NB = (PR * CPR) % (256 * 16) == 0 ? 16 : 10;
+    static_assert((PR * CPR) % (256 * NB) == 0, "whole batches");
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
+    for (int pass = 0; pass < BM / PR; ++pass) {
+      if (pass > 0) __syncthreads();      // the previous pass's chunks are read
+      if (PR == BM || wm == pass) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rt = wrow + i * 16 + q;
+        for (int i = 0; i < FM; ++i) {
+          const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          *(lds_f32*)(stage + rt * FPB + (wn * BNW + j * 16 + lcol) * 4) = acc[i][j][q] * sc[q] * csc[j];
+          for (int q = 0; q < 4; ++q) {
+            const int rp = wrow + i * 16 + q - pass * PR;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              *(lds_f32*)(stage + rp * FPB + (wn * BNW + j * 16 + lcol) * 4) = acc[i][j][q] * sc[q] * csc[j];
+          }
+        }
       }
-    }
-    __syncthreads();
-    for (int k0 = tid; k0 < BM * CPR; k0 += 256 * NB) {
-      f32x4 y[NB];
-      int orow[NB];
+      __syncthreads();
+      for (int k0 = tid; k0 < PR * CPR; k0 += 256 * NB) {
+        f32x4 y[NB];
+        int orow[NB];
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int k = k0 + u * 256;
-        const int r = k / CPR, cc = k - r * CPR;
-        if constexpr (MODE == MODE_DOWN_ROUTED) orow[u] = reinterpret_cast<const lds_i32*>(As)[BM + r];
-        else orow[u] = m0 + r;
-        y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (MODE == MODE_DOWN_ROUTED)
-          if (p.Y && m0 + r < rows && n0 + cc * 4 < NH)
-            y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
-      }
+        for (int u = 0; u < NB; ++u) {
+          const int k = k0 + u * 256;
+          const int r = k / CPR, cc = k - r * CPR;
+          const int rt = pass * PR + r;
+          if constexpr (MODE == MODE_DOWN_ROUTED) orow[u] = reinterpret_cast<const lds_i32*>(As)[BM + rt];
+          else orow[u] = m0 + rt;
+          y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (MODE == MODE_DOWN_ROUTED)
+            if (p.Y && m0 + rt < rows && n0 + cc * 4 < NH)
+              y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
+        }
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int k = k0 + u * 256;
-        const int r = k / CPR, cc = k - r * CPR;
-        if (m0 + r >= rows || n0 + cc * 4 >= NH) continue;
-        const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
-        const int64_t o = static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4;
-        if constexpr (MODE == MODE_DOWN_SHARED) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + o) = v;
-        } else if (p.out_bf16) {
-          const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-          const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + o) = v;
+        for (int u = 0; u < NB; ++u) {
+          const int k = k0 + u * 256;
+          const int r = k / CPR, cc = k - r * CPR;
+          if (m0 + pass * PR + r >= rows || n0 + cc * 4 >= NH) continue;
+          const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
+          const int64_t o = static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4;
+          if constexpr (MODE == MODE_DOWN_SHARED) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + o) = v;
+          } else if (p.out_bf16) {
+            const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+            const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + o) = v;
+          }
         }
       }
     }
   }
 }
 
-template <int MODE>
+template <int MODE, int BM>
 hipError_t launch_f8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* tiles_all) {
   GemmArgs a = a0;
   a.tiles = tiles_all + bm_index(BM) * (a.E + 2);
@@ -459,17 +481,20 @@ hipError_t launch_f8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* ti
   const int gn = (nmax + BNH - 1) / BNH;
   a.n_tiles = gn;
   const int64_t nblk = gn >= 8 ? 8 * static_cast<int64_t>(gm) * ((gn + 7) / 8) : static_cast<int64_t>(gm) * gn;
-  hipLaunchKernelGGL((gemm_fp8_kernel<MODE>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_fp8_kernel<MODE, BM>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_fp8(int mode, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all) {
+hipError_t launch_gemm_fp8(int mode, int bm, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all) {
+  if (bm == 160 && mode == MODE_GATEUP) return launch_f8<MODE_GATEUP, 160>(a, T, s, tiles_all);
+  if (bm == 160 && mode == MODE_DOWN_ROUTED) return launch_f8<MODE_DOWN_ROUTED, 160>(a, T, s, tiles_all);
+  if (bm != 128) return hipErrorInvalidValue;
   switch (mode) {
-    case MODE_GATEUP: return launch_f8<MODE_GATEUP>(a, T, s, tiles_all);
-    case MODE_DOWN_SHARED: return launch_f8<MODE_DOWN_SHARED>(a, T, s, tiles_all);
-    case MODE_DOWN_ROUTED: return launch_f8<MODE_DOWN_ROUTED>(a, T, s, tiles_all);
+    case MODE_GATEUP: return launch_f8<MODE_GATEUP, 128>(a, T, s, tiles_all);
+    case MODE_DOWN_SHARED: return launch_f8<MODE_DOWN_SHARED, 128>(a, T, s, tiles_all);
+    case MODE_DOWN_ROUTED: return launch_f8<MODE_DOWN_ROUTED, 128>(a, T, s, tiles_all);
   }
   return hipErrorInvalidValue;
 }

@@ -124,8 +124,9 @@ hipError_t launch_gemm_bf16_v2(int mode, int bm, const GemmArgs& a, int T, hipSt
 // The 256-row tiles of launch_gemm_bf16_v2 (separate unit: AGPR-form MFMAs).
 hipError_t launch_gemm_bf16_tall(int mode, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all);
 
-// fp8 prefill tiling (128 x 256 tiles, K 128 per stage; K multiple of 128).
-hipError_t launch_gemm_fp8(int mode, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all);
+// fp8 prefill tiling (bm x 256 tiles, K 128 per stage; K multiple of 128):
+// bm = 128, or 160 for MODE_GATEUP and MODE_DOWN_ROUTED.
+hipError_t launch_gemm_fp8(int mode, int bm, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all);
 
 // bf16 weight-streaming tiling for decode-sized T (16- or 32-row tiles, K
 // split over the 4 waves; K must be a multiple of 128).  Gate/up tiles are 128

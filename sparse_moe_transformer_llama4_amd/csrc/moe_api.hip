@@ -214,6 +214,15 @@ int routed_tile_rows(int64_t T, int E) {
   return mean >= 192 ? 256 : 128;
 }
 
+// e4m3 tile height of the gate/up and routed down GEMMs: 160 rows when the
+// mean routed group holds 96..136 rows (one 160-row tile then takes nearly
+// every group whole, where 128-row tiles add a second, nearly empty tile to
+// each group above 128 rows), else 128.
+int fp8_routed_rows(int64_t Tr, int E) {
+  const int64_t mean = E > 0 ? Tr / E : 0;
+  return mean >= 96 && mean <= 136 ? 160 : 128;
+}
+
 // Tile height for a down GEMM (N = d columns in 256-wide tiles) over `rows`
 // tokens in `groups` groups: 256-row tiles when they still give at least
 // ~1.5 rounds of workgroups over the GPU's 256 CUs, else 128 (fewer idle CUs
@@ -750,7 +759,8 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   if (f8) {
     g1.group_lo = 0;
     g1.group_hi = c.n_experts + 1;
-    if ((e = launch_gemm_fp8(MODE_GATEUP, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
+    const int bm = fp8_routed_rows(static_cast<int64_t>(Ti) * c.top_k, c.n_experts);
+    if ((e = launch_gemm_fp8(MODE_GATEUP, bm, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
   } else if (dec && int_weights(c)) {
     // int8 / int4 tiles: the routed groups, then the shared expert
     g1.group_lo = 0;
@@ -792,14 +802,15 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
 
   const int ys = dec ? decode_y_parts(c, T) : 1;
   const GemmArgs g2 = down_shared_args(c, w, ws, L, R, h_s, sh_s, Ti, ys);
-  e = f8    ? launch_gemm_fp8(MODE_DOWN_SHARED, g2, Ti, stream, R.tiles)
+  e = f8    ? launch_gemm_fp8(MODE_DOWN_SHARED, 128, g2, Ti, stream, R.tiles)
       : dec ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
             : launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(plan, e);
 
   const GemmArgs g3 = down_routed_args(c, w, ws, L, R, h_r, sh_r, out, Ti, ys);
-  e = f8    ? launch_gemm_fp8(MODE_DOWN_ROUTED, g3, Ti, stream, R.tiles)
+  e = f8    ? launch_gemm_fp8(MODE_DOWN_ROUTED, fp8_routed_rows(static_cast<int64_t>(Ti) * c.top_k, c.n_experts), g3,
+                              Ti, stream, R.tiles)
       : dec ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
             : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
   if (e != hipSuccess) return hip_fail(plan, e);

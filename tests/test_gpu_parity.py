@@ -44,6 +44,31 @@ def test_down_ntiles_not_multiple_of_8(gpu, name, over):
     check_forward(cfg, inp, out, routing)
 
 
+FP8_160_CASES = [dict(T=1000), dict(T=800, out_dtype="bf16"), dict(T=500, top_k=2), dict(T=1000, norm_eps=1e-5),
+                 dict(T=1000, bias="cold", n_cold=0, hot=3)]
+
+
+@pytest.mark.parametrize("over", FP8_160_CASES)
+def test_fp8_gateup_160_row_tiles(gpu, over):
+    # e4m3 with 100..125 routed rows per expert: the gate/up GEMM takes
+    # 160-row tiles (one per group, or several for a hot expert); the down
+    # GEMMs keep 128-row tiles
+    over = dict(over)
+    hot = over.pop("hot", None)
+    cfg = dataclasses.replace(synth.get_config("small_fp8"), name="fp8_160", **over)
+    print(f"[parity] fp8 160-row gate/up {over} hot={hot}", flush=True)
+    inp = synth.make_inputs(cfg)
+    if hot is not None:
+        inp["router_bias"] = torch.full((cfg.E,), -60.0)
+        inp["router_bias"][hot] = 60.0
+    g = to_device(inp, gpu)
+    out, routing = run_gpu(_plan(cfg), g["x"], g)
+    if hot is not None:
+        assert int(routing["counts"][hot]) == cfg.T
+    err, _ = check_forward(cfg, inp, out, routing)
+    print(f"[parity] fp8 160-row max|err|/RMS = {err:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("name", ["small_bf16", "small_fp32", "small_fp8"])
 def test_deterministic(gpu, name):
     cfg = synth.get_config(name)
@@ -225,7 +250,8 @@ GRAPH_CASES = [("small_fp32", {}), ("small_fp8", {}), ("decode_like_bf16", {}), 
                ("decode_like_bf16", dict(w_dtype="i8", T=33)), ("decode_like_bf16", dict(w_dtype="i4", T=33)),
                ("decode_like_bf16", dict(top_k=2, T=33)), ("small_bf16_tall", dict(top_k=2)),
                ("small_bf16_tall", dict(norm_eps=1e-5)), ("small_fp8", dict(norm_eps=1e-5, top_k=2)),
-               ("small_dense_bf16", dict(T=40)), ("small_dense_bf16", dict(T=300))]
+               ("small_dense_bf16", dict(T=40)), ("small_dense_bf16", dict(T=300)),
+               ("small_fp8", dict(T=1000))]
 
 
 @pytest.mark.parametrize("name,over", GRAPH_CASES)
