@@ -142,6 +142,9 @@ def main():
                          "200 decode; 0 skips them, e.g. for profiler runs that count calls)")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the core-clock sampling bursts (for profiler runs that count calls)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="time the library bf16 GEMM (torch.matmul, hipBLASLt) on the workload's dense shared-expert "
+                         "shapes, for comparison with the block's own GEMM kernels, and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (reference for rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE scaling) and exit")
@@ -156,6 +159,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}))
+        return
+    if args.library_gemm:
+        import synth
+        print(json.dumps(library_gemm(synth.get_config(args.config))))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the block is measured at one "
@@ -347,6 +354,34 @@ def sample_clock_mhz(run, seconds=0.5):
         return None
     samples = samples[len(samples) // 5:]          # skip the ramp-up
     return sum(samples) / len(samples) if samples else None
+
+
+def library_gemm(cfg, iters: int = 30) -> dict:
+    """The library's bf16 GEMM (torch.matmul on contiguous operands) on the
+    shared expert's two GEMM shapes, [T, d] x [d, 2 fs] and [T, fs] x [fs, d]:
+    a reference point for the MFMA fraction, not part of the block."""
+    import torch
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(0)
+    out = []
+    for m, k, n in ((cfg.T, cfg.d, 2 * cfg.fs), (cfg.T, cfg.fs, cfg.d)):
+        a = (torch.randn(m, k, device=dev, generator=gen) * 0.05).to(torch.bfloat16).contiguous()
+        b = (torch.randn(k, n, device=dev, generator=gen) * 0.05).to(torch.bfloat16).contiguous()
+        for _ in range(5):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(iters):
+            torch.matmul(a, b)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / iters
+        tf = 2.0 * m * k * n / (ms * 1e-3) / 1e12
+        out.append({"m": m, "k": k, "n": n, "us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                    "frac": round(tf * 1e12 / PEAK["bf16"], 4)})
+        del a, b
+    return {"library_gemm": out, "config": cfg.name, "library": "torch.matmul (hipBLASLt), bf16"}
 
 
 def _kernel_source_hash() -> str:
