@@ -119,8 +119,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(GemmArgs p) 
     const int x = lid & 7, local = lid >> 3;
     const int nt_lo = (x * gn) >> 3, w = (((x + 1) * gn) >> 3) - nt_lo;
     if (local >= nmt * w) return;
-    mt_rel = local / w;
-    nt = nt_lo + (local - mt_rel * w);
+    if (w > 8 && w % 8 == 0) {
+      // a wide range (d_ff = 16384: 16 N-tiles per XCD) is walked in blocks
+      // of 8 N-tiles, so the workgroups running together cover ~4 M-tiles x 8
+      // weight panels rather than 2 x 16 (fewer distinct panel slices per stage)
+      const int blk = local / (nmt * 8), in = local - blk * (nmt * 8);
+      mt_rel = in >> 3;
+      nt = nt_lo + blk * 8 + (in & 7);
+    } else {
+      mt_rel = local / w;
+      nt = nt_lo + (local - mt_rel * w);
+    }
   } else {
     if (lid >= nmt * gn) return;
     mt_rel = lid / gn;
