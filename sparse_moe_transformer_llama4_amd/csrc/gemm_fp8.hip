@@ -92,7 +92,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
   const int gn = p.n_tiles;
   const int lid = blockIdx.x;
   int mt_rel, nt;
-  if (gn >= 8) {
+  if (gn >= 8 && gn % 8 != 0 && gn % 4 == 0) {
+    // N-tiles a multiple of 4 but not of 8 (the down GEMMs: d / 256 = 20):
+    // 4 N-ranges x 2 M-halves, one rectangle per XCD (as in the bf16 kernels)
+    const int x = lid & 7, local = lid >> 3;
+    const int w = gn >> 2, m_lo = ((x >> 2) * nmt) >> 1, m_hi = (((x >> 2) + 1) * nmt) >> 1;
+    if (local >= (m_hi - m_lo) * w) return;
+    mt_rel = m_lo + local / w;
+    nt = (x & 3) * w + (local - (local / w) * w);
+  } else if (gn >= 8) {
     const int x = lid & 7, local = lid >> 3;
     const int nt_lo = (x * gn) >> 3, w = (((x + 1) * gn) >> 3) - nt_lo;
     if (local >= nmt * w) return;
@@ -480,7 +488,9 @@ hipError_t launch_f8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* ti
   if (gm <= 0) return hipSuccess;
   const int gn = (nmax + BNH - 1) / BNH;
   a.n_tiles = gn;
-  const int64_t nblk = gn >= 8 ? 8 * static_cast<int64_t>(gm) * ((gn + 7) / 8) : static_cast<int64_t>(gm) * gn;
+  const int64_t nblk = (gn >= 8 && gn % 8 != 0 && gn % 4 == 0) ? 8 * static_cast<int64_t>((gm + 1) / 2) * (gn / 4)
+                       : gn >= 8 ? 8 * static_cast<int64_t>(gm) * ((gn + 7) / 8)
+                                 : static_cast<int64_t>(gm) * gn;
   hipLaunchKernelGGL((gemm_fp8_kernel<MODE, BM>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -32,10 +32,12 @@ def test_forward_matches_oracle(gpu, name):
 
 
 @pytest.mark.parametrize("name,over", [("small_bf16", dict(d=2560)), ("small_bf16_tall", dict(d=2304)),
-                                       ("small_fp8", dict(d=2560)), ("small_bf16_tall", dict(d=2560, top_k=2))])
+                                       ("small_fp8", dict(d=2560)), ("small_bf16_tall", dict(d=2560, top_k=2)),
+                                       ("small_bf16_tall", dict(d=3072)), ("small_fp8", dict(d=3072, T=1000)),
+                                       ("small_bf16", dict(d=3072, top_k=3))])
 def test_down_ntiles_not_multiple_of_8(gpu, name, over):
-    # down GEMMs with 9 or 10 column tiles: the tiles are shared out over
-    # the XCDs in equal contiguous runs of the row-major tile list
+    # down GEMMs with 9, 10 or 12 column tiles: whole column tiles per XCD
+    # (9, 10), or (12) 4 column ranges x 2 row halves, one per XCD
     cfg = dataclasses.replace(synth.get_config(name), name=f"{name}_d{over['d']}", **over)
     print(f"[parity] {cfg.name} T={cfg.T} d={cfg.d} {cfg.w_dtype} k={cfg.top_k}", flush=True)
     inp = synth.make_inputs(cfg)
