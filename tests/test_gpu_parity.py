@@ -205,7 +205,8 @@ def test_decode_path_one_hot_and_idle_nan(gpu):
 
 
 @pytest.mark.parametrize("name,T", [("decode_like_bf16", 33), ("small_bf16_split", None),
-                                    ("small_bf16_tall", None), ("wide_bf16_tall", None)])
+                                    ("small_bf16_tall", None), ("wide_bf16_tall", None),
+                                    ("small_fp8", None), ("small_fp8", 1000)])
 def test_side_stream_matches_serial_schedule(gpu, name, T):
     # Decode-sized bf16 calls run the shared expert's GEMMs, and bf16 prefill
     # calls the shared expert and the routed groups' tails, on a side stream.  Same kernels and arguments as the serial schedule
