@@ -6,19 +6,25 @@ with the SwiGLU epilogue (routed + shared), shared down GEMM, routed down
 GEMM with un-permute + combine.  Inputs are generated on the GPU by the
 seeded generator before timing and stay resident in HBM.
 
-Prints ONE JSON line (rank 0, N = 1):
+Prints ONE JSON line (rank 0, N = 1) for the headline workload (default:
+the Maverick-shaped fp8 prefill layer, T = 16384, the largest of the
+workloads), with the other single-GPU workloads under "per_config":
   value       tokens/s of the whole block (timed moe_forward calls)
-  roofline    the dominant stage (largest average duration, timed with HIP
-              events recorded by the library on its stream over a second
-              timed region of moe_forward_timed calls, which run the stages in
-              order on one stream) against the MFMA or HBM roofline, using
-              algorithmic FLOPs / bytes of that stage
+  kernels     every launch of the call, timed with HIP events the library
+              records around each launch on the stream it goes to
+              (moe_forward_traced: the same schedule and streams as
+              moe_forward), with its algorithmic FLOPs / bytes and the
+              fraction of its roofline
+  roofline    the launch with the largest average duration (the dominant
+              kernel) against the MFMA or HBM roofline, with the HBM bytes
+              the rocprofv3 counters measured for it (profiles/traffic.json)
   clock_mhz   mean core clock during ~0.5 s of further moe_forward calls
-              (sysfs pp_dpm_sclk), and the MFMA fractions against the peak at
-              that clock (the quoted peaks assume 2.4 GHz)
-  cpu_baseline  the fp64 CPU oracle timed on a bounded token sample
+              (sysfs pp_dpm_sclk); MFMA fractions at that clock beside the
+              nominal ones (the quoted peaks assume 2.4 GHz)
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+                       [--per-config NAMES | --no-per-config]
 """
 from __future__ import annotations
 
@@ -31,41 +37,95 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# dense MFMA peak by weight dtype, FLOP/s (int8 weights are converted to
-# bf16 and multiplied on the bf16 MFMA)
+METRIC = "MoE-layer tokens/s + % MFMA peak (prefill), % HBM BW (decode)"
+HEADLINE = "maverick_prefill_fp8"
+PER_CONFIG = ("scout_prefill_bf16", "scout_decode_bf16", "maverick_prefill_bf16")
+
+# dense MFMA peak by weight dtype, FLOP/s (int8 / int4 weights are converted
+# to bf16 and multiplied on the bf16 MFMA)
 PEAK = {"bf16": 2516.6e12, "e4m3": 5033.2e12, "f32": 157.3e12, "i8": 2516.6e12, "i4": 2516.6e12}
 HBM_PEAK = 8.0e12                                                 # bytes/s
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def esize(dt: str) -> int:
+def esize(dt: str) -> float:
     return {"f32": 4, "bf16": 2, "e4m3": 1, "i8": 1, "i4": 0.5}[dt]
 
 
-def stage_work(cfg, counts):
-    """Algorithmic (FLOPs, bytes) per launch of each stage."""
+# ---------------------------------------------------------------- algorithmic work
+
+def split_rows(n: int, bm: int, part: int) -> int:
+    """Rows of a group of n rows that a launch covers: part 0 all of them;
+    part 1 the main tiles (a last 1..32 rows past the group's full bm-row
+    tiles are left to the tail tiles, so a group of at most 32 rows is all
+    tail); part 2 those tail rows alone."""
+    if part == 0 or not bm:
+        return n
+    r = n % bm
+    tail = r if 1 <= r <= 32 else 0
+    return n - tail if part == 1 else tail
+
+
+def launch_work(cfg, counts, rec):
+    """Algorithmic (FLOPs, bytes) of one launch of the call.  Bytes: the
+    weights (+ column scales) of the experts the launch touches, read once,
+    plus its activation rows read and its output rows written once."""
+    name, _side, bm, groups, part = rec[:5]
     T, d, E, f, fs = cfg.T, cfg.d, cfg.E, cfg.f, cfg.fs
-    Tr = T * cfg.top_k                          # routed rows: k picks per token
-    xb, wb = esize(cfg.x_dtype), esize(cfg.w_dtype)
-    hb = 4 if cfg.w_dtype == "f32" else 2
-    ob = esize(cfg.out_dtype)
-    touched = sum(1 for c in counts if c > 0)
-    sc = 4 if cfg.w_dtype in ("e4m3", "i8", "i4") else 0     # fp32 column scales per weight column
-    xin = 1 if cfg.w_dtype == "e4m3" else xb   # gate/up reads the e4m3 copy of x
-    # RMSNorm in front of the block: x read, the normalised rows written (and
-    # their e4m3 codes + scales for e4m3 weights), the gain read
-    norm = 0
-    if cfg.norm_eps is not None:
-        norm = 2 * T * d * xb + d * xb + ((T * d + 4 * T) if cfg.w_dtype == "e4m3" else 0)
-    return {
-        "route": (2 * T * d * E, T * d * xb + d * E * xb + (4 * E if cfg.has_bias else 0) + T * 8 + norm),
-        "gate_up": (4 * d * (Tr * f + T * fs),
-                    touched * (d * 2 * f * wb + 2 * f * sc) + d * 2 * fs * wb + 2 * fs * sc
-                    + T * d * xin + (Tr * f + T * fs) * hb),
-        "down_shared": (2 * T * fs * d, fs * d * wb + d * sc + T * fs * hb + T * d * 4),
-        "down_routed": (2 * Tr * f * d, touched * (f * d * wb + d * sc) + Tr * f * hb + T * d * 4 + T * d * ob
-                        + (2 * Tr * d * 4 if cfg.top_k > 1 else 0)),
-    }
+    k = cfg.top_k
+    xb, wb, ob = esize(cfg.x_dtype), esize(cfg.w_dtype), esize(cfg.out_dtype)
+    sc = 4 if cfg.w_dtype in ("e4m3", "i8", "i4") else 0
+    fp8 = cfg.w_dtype == "e4m3"
+    xin = 1 if fp8 else xb                    # the gate/up reads x's e4m3 codes
+    hout = 4 if cfg.w_dtype in ("f32", "e4m3") else 2   # h as the gate/up writes it (e4m3: fp32 staging)
+    hin = 1 if fp8 else hout                  # h as the down GEMMs read it (e4m3: its codes)
+    rows = [split_rows(int(n), bm, part) for n in counts]
+    R = sum(rows)
+    touched = sum(1 for r in rows if r > 0)
+    routed = groups in (0, 2)
+    shared = groups in (1, 2)
+    F = B = 0
+    if name == "gateup":
+        if routed:
+            F += 4 * d * f * R
+            B += touched * (d * 2 * f * wb + 2 * f * sc) + R * d * xin + R * f * hout + R * 4
+        if shared:
+            F += 4 * d * fs * T
+            B += d * 2 * fs * wb + 2 * fs * sc + T * d * xin + T * fs * hout
+    elif name == "down_shared":
+        F = 2 * T * fs * d
+        B = fs * d * wb + d * sc + T * fs * hin + T * d * 4
+    elif name in ("down_routed", "down_routed_r"):
+        F = 2 * R * f * d
+        B = touched * (f * d * wb + d * sc) + R * f * hin
+        if name == "down_routed_r" or k > 1:
+            B += R * d * 4                    # fp32 rows into the workspace
+        else:
+            B += T * d * 4 + T * d * ob       # adds the shared output, writes out
+        if shared:
+            F += 2 * T * fs * d
+            B += fs * d * wb + T * fs * hin + T * d * 4
+    elif name in ("router", "router_gemm", "route_small"):
+        F = 2 * T * d * E
+        B = T * d * xb + d * E * xb
+    elif name == "router_finish":
+        B = T * E * 4 + T * k * 8
+    elif name in ("scan", "perm", "fill"):
+        B = T * k * 8
+    elif name == "rmsnorm":
+        B = 2 * T * d * xb + d * xb + ((T * d + 4 * T) if fp8 else 0)
+    elif name == "quant_x":
+        B = T * d * xb + T * d + 4 * T
+    elif name == "quant_h":
+        r_, n_ = (R, f) if groups == 0 else (T, fs)
+        B = r_ * n_ * 4 + r_ * n_ + r_ * 8
+    elif name == "combine":
+        B = 2 * T * d * 4 + T * d * ob
+    elif name == "combine_topk":
+        B = T * k * d * 4 + T * d * 4 + T * d * ob
+    elif name == "swiglu_parts":
+        B = T * 2 * fs * 4 + T * fs * 2
+    return F, B
 
 
 def block_work(cfg, counts):
@@ -80,35 +140,80 @@ def block_work(cfg, counts):
     return flops, byts
 
 
-def cpu_baseline(cfg, g, sample):
-    """Time the fp64 oracle on the first `sample` tokens (weights copied per expert)."""
+def launch_key(rec) -> str:
+    """Stable name of a launch: kernel[routed|shared|both, all|main|tail, tile rows]."""
+    name, side, bm, groups, part = rec[:5]
+    g = {0: "routed", 1: "shared", 2: "routed+shared"}.get(groups)
+    p = {0: "", 1: ",main", 2: ",tail"}[part]
+    inner = f"{g}{p},bm{bm}" if g else ""
+    return f"{name}[{inner}]" if inner else name
+
+
+def roofline_of(cfg, F, B, ms):
+    t = ms * 1e-3
+    peak_f = PEAK[cfg.w_dtype]
+    if F > 0 and F / B >= peak_f / HBM_PEAK:
+        return {"bound": "mfma", "achieved": F / t / 1e12, "peak": peak_f / 1e12, "unit": "TFLOP/s",
+                "frac": F / t / peak_f}
+    return {"bound": "hbm", "achieved": B / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": B / t / HBM_PEAK}
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(cfg, g, routing_counts):
+    """Time the fp64 oracle (as it stands) on the host cores.
+
+    Small workloads run whole.  The Maverick-shaped ones (128 experts) run on
+    a stratified sample: the oracle routes all T tokens, then evaluates the
+    experts of 16 of the 128 groups (every 8th group in order of size, so hot
+    and cold groups are both in it) on their tokens, with the shared expert
+    on the same tokens.  The weights are copied to host memory before the
+    clock starts.  The figure is scaled per token: the whole workload would
+    take t_route + t_experts * T / n_sample."""
     import numpy as np
     import torch
     from oracle import block
 
-    xs = g["x"][:sample].cpu()
+    x = g["x"].cpu()
     nw = None if g.get("norm_weight") is None else g["norm_weight"].cpu()
+    if cfg.E == 0:
+        return cpu_baseline_dense(cfg, g, x)
+    router = (g["w_router"].cpu(), None if g["router_bias"] is None else g["router_bias"].cpu())
+    counts = np.asarray(routing_counts)
+    if cfg.E > 16:
+        order = np.argsort(-counts, kind="stable")
+        experts = [int(e) for e in order[::8] if counts[e] > 0]
+    else:
+        experts = [int(e) for e in np.nonzero(counts)[0]]
 
-    def ex(e):
-        s = g["s_gate_up"]
-        sd = g["s_down"]
+    def host(e):
+        s, sd = g.get("s_gate_up"), g.get("s_down")
         return (g["w_gate_up"][e].cpu(), None if s is None else s[e].cpu(),
                 g["w_down"][e].cpu(), None if sd is None else sd[e].cpu())
-
+    cache = {e: host(e) for e in experts}
     shared = tuple(None if g[k] is None else g[k].cpu() for k in ("ws_gate_up", "ss_gate_up", "ws_down", "ss_down"))
-    router = (g["w_router"].cpu(), None if g["router_bias"] is None else g["router_bias"].cpu())
-    w = block.Weights(lambda: router, ex, lambda: shared)
+    w = block.Weights(lambda: router, lambda e: cache[e], lambda: shared)
+
     t0 = time.perf_counter()
-    if nw is not None:
-        xs = block.rmsnorm(xs, nw, float(np.float32(cfg.norm_eps)), cfg.x_dtype)
-    if cfg.E == 0:
-        out = block.dense(xs, w, cfg.fs, cfg.w_dtype)
-        what = "dense gated MLP"
+    xs = block.rmsnorm(x, nw, float(np.float32(cfg.norm_eps)), cfg.x_dtype) if nw is not None else x
+    if cfg.top_k > 1:
+        r = block.route_topk(xs, *router, cfg.top_k)
+        idx = r.idx
     else:
-        out, r = block.forward(xs, w, cfg.f, cfg.fs, cfg.w_dtype, top_k=cfg.top_k)
-        what = (f"routing + every touched expert + shared), {int(np.count_nonzero(r.counts))} experts touched")
-    dt = time.perf_counter() - t0
-    norm = "RMSNorm + " if nw is not None else ""
+        r = block.route(xs, *router)
+        idx = r.idx[:, None]
+    t_route = time.perf_counter() - t0
+    # the tokens all of whose picks fall in the sampled groups (all tokens
+    # when every non-empty group is sampled)
+    toks = np.nonzero(np.isin(idx, experts).all(axis=1))[0]
+    t1 = time.perf_counter()
+    sub = idx[toks]
+    gate = block.sigmoid(np.take_along_axis(r.logits[toks], sub, axis=1))
+    block.combine_topk(xs[toks], sub, gate, w, cfg.f, cfg.fs, cfg.w_dtype)
+    t_exp = time.perf_counter() - t1
+    n = len(toks)
+    whole = n == cfg.T
+    t_est = t_route + t_exp * (cfg.T / max(n, 1))
     cpu_model = None
     try:
         with open("/proc/cpuinfo") as fh:
@@ -117,13 +222,156 @@ def cpu_baseline(cfg, g, sample):
         pass
     blas = None
     try:
-        cfgd = np.show_config(mode="dicts")
-        blas = cfgd.get("Build Dependencies", {}).get("blas", {}).get("name")
+        blas = np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {}).get("name")
     except Exception:   # numpy without the dict form
         pass
-    return {"value": sample / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "cpu_model": cpu_model, "blas": blas, "torch_threads": torch.get_num_threads(),
-            "sample": f"first {sample} of {cfg.T} tokens, full fp64 block ({norm}{what}, {dt:.1f} s"}
+    if whole:
+        sample = (f"all {cfg.T} tokens, full fp64 block ({'RMSNorm + ' if nw is not None else ''}routing + "
+                  f"{len(experts)} touched experts + shared), {t_route + t_exp:.1f} s")
+    else:
+        sample = (f"per-token-scaled stratified sample: oracle routing of all {cfg.T} tokens ({t_route:.1f} s), "
+                  f"then the {n} tokens of {len(experts)} of the {cfg.E} expert groups (every 8th by size, "
+                  f"{int(counts[experts].min())}..{int(counts[experts].max())} tokens each) through their "
+                  f"experts and the shared expert ({t_exp:.1f} s); tokens/s = T / (t_route + t_experts * T / "
+                  f"{n})")
+    return {"value": cfg.T / t_est, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": sample, "cpu_model": cpu_model, "blas": blas, "torch_threads": torch.get_num_threads()}
+
+
+def cpu_baseline_dense(cfg, g, x, sample=512):
+    """A dense layer: the oracle's gated MLP on the first `sample` tokens."""
+    import numpy as np
+    import torch
+    from oracle import block
+    shared = tuple(None if g[k] is None else g[k].cpu() for k in ("ws_gate_up", "ss_gate_up", "ws_down", "ss_down"))
+    w = block.Weights(lambda: None, lambda e: None, lambda: shared)
+    n = min(cfg.T, sample)
+    t0 = time.perf_counter()
+    block.dense(x[:n], w, cfg.fs, cfg.w_dtype)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens through the fp64 dense gated MLP, {dt:.1f} s",
+            "torch_threads": torch.get_num_threads(), "blas": None, "cpu_model": None}
+
+
+# ---------------------------------------------------------------- one workload
+
+def run_config(cfg, steps, warmup, nsets=None, latency_samples=None, clock=True, detail=True):
+    import torch
+    import synth
+    from sparse_moe_transformer_llama4_amd import moe
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] {cfg.name}: generating inputs on {dev}", file=sys.stderr, flush=True)
+    g = synth.make_inputs(cfg, dev)
+    # decode-sized calls rotate over independent weight copies (each far
+    # larger than the 256 MB last-level cache), so no call finds the previous
+    # call's weights in a cache
+    nsets = nsets or (2 if cfg.T <= 64 else 1)
+    gsets = [g] + [{k: (v if (v is None or k == "x") else v.clone()) for k, v in g.items()} for _ in range(nsets - 1)]
+    torch.cuda.synchronize()
+    plan = moe.Plan.for_shape(cfg)
+    ws = torch.empty(max(moe.moe_workspace_size(plan, cfg.T), 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.T, cfg.d), dtype=moe._TORCH_DT[moe._DT[cfg.out_dtype]], device=dev)
+    routing = moe.new_routing(plan, cfg.T, dev) if cfg.E > 0 else None   # a dense layer routes nothing
+    lev = [moe.LaunchEvents() for _ in range(steps)]
+    warm_ev = moe.LaunchEvents()
+
+    print(f"[bench] {cfg.name}: warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        moe.moe_forward(plan, g["x"], g, out=out, routing=routing, workspace=ws)
+        moe.moe_forward_traced(plan, g["x"], g, warm_ev, out, ws, routing)
+    torch.cuda.synchronize()
+    counts = routing["counts"].cpu().tolist() if routing is not None else []
+
+    # timed region 1: the library call itself (tokens/s)
+    print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        gk = gsets[k % nsets]
+        moe.moe_forward(plan, gk["x"], gk, out=out, routing=routing, workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+
+    # timed region 2: the same calls with an event pair around every launch
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in range(steps):
+        gk = gsets[k % nsets]
+        moe.moe_forward_traced(plan, gk["x"], gk, lev[k], out, ws, routing)
+    torch.cuda.synchronize()
+    ms_traced = (time.perf_counter() - t1) / steps * 1e3
+
+    # per-call times (events on the caller's stream around each call): median, p90
+    nlat = latency_samples if latency_samples is not None else (200 if cfg.T <= 64 else 50)
+    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nlat)]
+    for k, (e0, e1) in enumerate(ev_pairs):
+        gk = gsets[k % nsets]
+        e0.record()
+        moe.moe_forward(plan, gk["x"], gk, out=out, routing=routing, workspace=ws)
+        e1.record()
+    torch.cuda.synchronize()
+    lat = sorted(e0.elapsed_time(e1) for e0, e1 in ev_pairs)
+
+    def _burst():
+        for _ in range(8):
+            moe.moe_forward(plan, g["x"], g, out=out, routing=routing, workspace=ws)
+        torch.cuda.synchronize()
+    clock_mhz = sample_clock_mhz(_burst) if clock else None
+
+    # per-launch durations, averaged over the traced steps (the schedule is
+    # the same every call)
+    per = [ev.launches() for ev in lev]
+    kernels = []
+    for i, rec in enumerate(per[0]):
+        avg = sum(p[i][5] for p in per) / len(per)
+        F, B = launch_work(cfg, counts, rec)
+        roof = roofline_of(cfg, F, B, avg)
+        kernels.append({"launch": i, "kernel": launch_key(rec), "stream": "side" if rec[1] else "main",
+                        "ms": avg, "gflop": F / 1e9, "gbytes": B / 1e9, "tflops": F / (avg * 1e-3) / 1e12,
+                        "gbps": B / (avg * 1e-3) / 1e9, "bound": roof["bound"], "frac": roof["frac"]})
+    dom = max(kernels, key=lambda kk: kk["ms"])
+    F, B = launch_work(cfg, counts, per[0][dom["launch"]])
+    roof = roofline_of(cfg, F, B, dom["ms"])
+    roof["kernel"] = dom["kernel"]
+    roof["ms"] = dom["ms"]
+    roof["clock_mhz"] = clock_mhz
+    roof["frac_at_clock"] = roof["frac"] * 2400.0 / clock_mhz if clock_mhz and roof["bound"] == "mfma" else None
+    roof["traffic"] = stored_traffic(cfg.name, dom["kernel"])
+
+    Fb, Bb = block_work(cfg, counts)
+    t = ms * 1e-3
+    peak_f = PEAK[cfg.w_dtype]
+    res = {
+        "value": cfg.T / t, "unit": "tokens/s", "ms_per_step": ms, "ms_per_step_traced": ms_traced,
+        "ms_median": lat[len(lat) // 2] if lat else None,
+        "ms_p90": lat[min(len(lat) - 1, int(0.9 * len(lat)))] if lat else None,
+        "latency_samples": nlat,
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "f": cfg.f, "f_shared": cfg.fs,
+                   "x_dtype": cfg.x_dtype, "w_dtype": cfg.w_dtype, "out_dtype": cfg.out_dtype,
+                   "routing": cfg.bias, "experts_touched": sum(1 for c in counts if c > 0),
+                   "rmsnorm_eps": cfg.norm_eps, "top_k": cfg.top_k, "weight_sets": nsets},
+        "block_tflops": Fb / t / 1e12, "block_gbps": Bb / t / 1e9,
+        "mfma_frac": Fb / t / peak_f, "hbm_frac": Bb / t / HBM_PEAK,
+        "clock_mhz": clock_mhz,
+        "mfma_frac_at_clock": Fb / t / peak_f * 2400.0 / clock_mhz if clock_mhz else None,
+        "roofline": roof,
+        "kernels": kernels if detail else [{k_: v for k_, v in kk.items() if k_ in ("kernel", "stream", "ms", "bound",
+                                                                                    "frac")} for kk in kernels],
+    }
+    return res, g, counts
+
+
+def stored_traffic(workload, kernel):
+    """HBM bytes per launch measured by the rocprofv3 counters for this
+    workload's kernel, while the library source is unchanged since."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    tr = json.load(open(PROFILE_TRAFFIC)).get(workload, {}).get(kernel)
+    if tr and tr.get("source_hash") == _kernel_source_hash():
+        return tr["bytes"]
+    return None
 
 
 def main():
@@ -131,8 +379,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="scout_prefill_bf16")
-    ap.add_argument("--cpu-sample", type=int, default=None)
+    ap.add_argument("--config", default=HEADLINE)
+    ap.add_argument("--per-config", default=None,
+                    help="comma-separated workloads reported under per_config (default: the other single-GPU "
+                         "workloads when --config is the headline one, none otherwise)")
+    ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weight-sets", type=int, default=None,
                     help="independent copies of the weights the timed calls rotate over (default: 2 for "
@@ -149,6 +400,11 @@ def main():
                     help="only run a device-to-device copy of MIB MiB (reference for rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE scaling) and exit")
     args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the block is measured at one "
+                                   "GPU's share with no collectives (how it would shard is design only); "
+                                   "--gpus must be 1"}))
+        sys.exit(2)
     if args.calibrate_copy:
         import torch
         n = args.calibrate_copy << 20
@@ -160,154 +416,67 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}))
         return
+    import synth
     if args.library_gemm:
-        import synth
         print(json.dumps(library_gemm(synth.get_config(args.config))))
         return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the block is measured at one "
-                                   "GPU's share with no collectives; --gpus must be 1"}))
-        sys.exit(2)
 
+    import gc
     import torch
-    import synth
-    from sparse_moe_transformer_llama4_amd import moe
-
-    dev = torch.device("cuda:0")
     cfg = synth.get_config(args.config)
-    print(f"[bench] generating {cfg.name} on {dev}", file=sys.stderr, flush=True)
-    g = synth.make_inputs(cfg, dev)
-    # decode-sized calls rotate over independent weight copies (each far
-    # larger than the 256 MB last-level cache), so no call finds the previous
-    # call's weights in a cache
-    nsets = args.weight_sets or (2 if cfg.T <= 64 else 1)
-    gsets = [g] + [{k: (v if (v is None or k == "x") else v.clone()) for k, v in g.items()} for _ in range(nsets - 1)]
-    torch.cuda.synchronize()
-    plan = moe.Plan.for_shape(cfg)
-    ws = torch.empty(max(moe.moe_workspace_size(plan, cfg.T), 256), dtype=torch.uint8, device=dev)
-    out = torch.empty((cfg.T, cfg.d), dtype=moe._TORCH_DT[moe._DT[cfg.out_dtype]], device=dev)
-    routing = moe.new_routing(plan, cfg.T, dev) if cfg.E > 0 else None   # a dense layer routes nothing
-    events = [moe.StageEvents() for _ in range(args.steps)]
-    warm_ev = moe.StageEvents()
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        moe.moe_forward(plan, g["x"], g, out=out, routing=routing, workspace=ws)
-        moe.moe_forward_timed(plan, g["x"], g, warm_ev, out, ws, routing)
-    torch.cuda.synchronize()
-    counts = routing["counts"].cpu().tolist() if routing is not None else []
-
-    # timed region 1: the library call itself (tokens/s)
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        gk = gsets[k % nsets]
-        moe.moe_forward(plan, gk["x"], gk, out=out, routing=routing, workspace=ws)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = elapsed / args.steps * 1e3
-
-    # timed region 2: the same call with HIP events at the stage boundaries
-    # (stages in order on one stream; decode-sized calls otherwise overlap the
-    # shared expert with the routing and the routed gate/up on a side stream)
-    print(f"[bench] timing {args.steps} stage-timed steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for k in range(args.steps):
-        gk = gsets[k % nsets]
-        moe.moe_forward_timed(plan, gk["x"], gk, events[k], out, ws, routing)
-    torch.cuda.synchronize()
-    ms_timed = (time.perf_counter() - t1) / args.steps * 1e3
-
-    # per-call times (events on the caller's stream around each call): median, p90
-    nlat = args.latency_samples if args.latency_samples is not None else (200 if cfg.T <= 64 else 50)
-    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nlat)]
-    for k, (e0, e1) in enumerate(ev_pairs):
-        gk = gsets[k % nsets]
-        e0.record()
-        moe.moe_forward(plan, gk["x"], gk, out=out, routing=routing, workspace=ws)
-        e1.record()
-    torch.cuda.synchronize()
-    lat = sorted(e0.elapsed_time(e1) for e0, e1 in ev_pairs)
-    ms_median = lat[len(lat) // 2] if lat else None
-    ms_p90 = lat[min(len(lat) - 1, int(0.9 * len(lat)))] if lat else None
-
-    # core clock under this load (outside the timed regions): the MFMA peak
-    # is quoted at 2.4 GHz, and the chip runs slower under heavy MFMA use
-    import torch as _t
-
-    def _burst():
-        for _ in range(8):
-            moe.moe_forward(plan, g["x"], g, out=out, routing=routing, workspace=ws)
-        _t.cuda.synchronize()
-    clock_mhz = None if args.no_clock else sample_clock_mhz(_burst)
-
-    per_stage = [ev.durations_ms() for ev in events]
-    avg = [sum(s[i] for s in per_stage) / len(per_stage) for i in range(moe.MOE_NUM_STAGES)]
-    stage_ms = dict(zip(moe.STAGES, avg))
-    work = stage_work(cfg, counts)
-    dom = max(stage_ms, key=stage_ms.get)
-    fl, by = work[dom]
-    peak_f = PEAK[cfg.w_dtype]
-    ridge = peak_f / HBM_PEAK
-    t_dom = stage_ms[dom] * 1e-3
-    if fl / by >= ridge:
-        roof = {"bound": "mfma", "achieved": fl / t_dom / 1e12, "peak": peak_f / 1e12, "unit": "TFLOP/s"}
+    res, g, counts = run_config(cfg, args.steps, args.warmup, args.weight_sets, args.latency_samples,
+                                clock=not args.no_clock)
+    if not args.no_cpu_baseline:
+        print(f"[bench] {cfg.name}: cpu oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, g, counts)
     else:
-        roof = {"bound": "hbm", "achieved": by / t_dom / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    # second column: against the MFMA peak at the clock sustained under this load
-    roof["clock_mhz"] = clock_mhz
-    roof["frac_at_clock"] = (roof["frac"] * 2400.0 / clock_mhz
-                             if clock_mhz and roof["bound"] == "mfma" else None)
-    roof["kernel"] = dom
-    roof["ms"] = stage_ms[dom]
-    traffic = None
-    if os.path.exists(PROFILE_TRAFFIC):
-        tr = json.load(open(PROFILE_TRAFFIC)).get(cfg.name, {}).get(dom)
-        if tr and tr.get("source_hash") == _kernel_source_hash():
-            traffic = tr["bytes"]
-    roof["traffic"] = traffic
+        res["cpu_baseline"] = None
+    del g
+    gc.collect()
+    torch.cuda.empty_cache()
 
-    F, B = block_work(cfg, counts)
-    t = ms * 1e-3
+    if args.no_per_config:
+        names = []
+    elif args.per_config is not None:
+        names = [n for n in args.per_config.split(",") if n]
+    else:
+        names = list(PER_CONFIG) if args.config == HEADLINE else []
+    per_config = {cfg.name: {k: res[k] for k in ("value", "ms_per_step", "ms_median", "mfma_frac", "hbm_frac")}
+                  | {"roofline": {k: res["roofline"][k] for k in ("kernel", "bound", "frac", "ms")},
+                     "cpu_baseline": res["cpu_baseline"] and res["cpu_baseline"]["value"]}}
+    for name in names:
+        c = synth.get_config(name)
+        r, g, cnt = run_config(c, max(5, args.steps // 2), args.warmup, latency_samples=20 if c.T > 64 else 100,
+                               clock=False, detail=False)
+        entry = {k: r[k] for k in ("value", "ms_per_step", "ms_median", "mfma_frac", "hbm_frac")}
+        entry["dtype"] = c.w_dtype
+        entry["roofline"] = {k: r["roofline"][k] for k in ("kernel", "bound", "frac", "ms", "traffic")}
+        entry["kernels"] = r["kernels"]
+        if not args.no_cpu_baseline:
+            print(f"[bench] {c.name}: cpu oracle", file=sys.stderr, flush=True)
+            cb = cpu_baseline(c, g, cnt)
+            entry["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        per_config[name] = entry
+        del g
+        gc.collect()
+        torch.cuda.empty_cache()
+
     result = {
-        "metric": "MoE-layer tokens/s + % MFMA peak (prefill), % HBM BW (decode)",
-        "value": cfg.T / t,
+        "metric": METRIC,
+        "value": res["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
-        "ms_per_step_stage_timed": ms_timed,
-        "ms_median": ms_median,
-        "ms_p90": ms_p90,
-        "latency_samples": nlat,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.w_dtype,
         "data": "synthetic (seeded counter-based generator, random-init weights)",
-        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "f": cfg.f, "f_shared": cfg.fs,
-                   "x_dtype": cfg.x_dtype, "w_dtype": cfg.w_dtype, "out_dtype": cfg.out_dtype,
-                   "routing": cfg.bias, "experts_touched": sum(1 for c in counts if c > 0),
-                   "rmsnorm_eps": cfg.norm_eps, "top_k": cfg.top_k, "weight_sets": nsets},
-        "block_tflops": F / t / 1e12,
-        "block_gbps": B / t / 1e9,
-        "mfma_frac": F / t / peak_f,
-        "clock_mhz": clock_mhz,
-        "mfma_frac_at_clock": F / t / peak_f * 2400.0 / clock_mhz if clock_mhz else None,
-        "hbm_frac": B / t / HBM_PEAK,
-        "stage_ms": stage_ms,
-        "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        sample = args.cpu_sample or min(cfg.T, 4096 if cfg.E <= 16 else 512)
-        print(f"[bench] cpu oracle on {sample} tokens", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, g, sample)
-    else:
-        result["cpu_baseline"] = None
+    result.update({k: v for k, v in res.items() if k not in ("value", "unit", "ms_per_step")})
+    result["per_config"] = per_config
     print(json.dumps(result), flush=True)
 
 

@@ -230,6 +230,35 @@ moe_status moe_forward_timed(moe_plan_t plan, const void* x, int64_t T, const mo
                              void* out, moe_routing* routing_out, void* workspace,
                              size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
 
+/*
+ * moe_forward with per-launch timing, for measuring each kernel inside the
+ * schedule moe_forward runs (side stream included).  Every kernel launch of
+ * the call is bracketed by events[2 i] and events[2 i + 1], recorded on the
+ * stream that launch goes to, so hipEventElapsedTime(events[2 i],
+ * events[2 i + 1]) is launch i's duration; launches[i] describes it and
+ * *n_launches receives the count.  The events are created by the caller
+ * (2 * max_launches of them); max_launches must be at least
+ * MOE_MAX_LAUNCHES (MOE_ERR_INVALID_ARGUMENT otherwise, before anything is
+ * enqueued).  The extra events are the only difference from moe_forward:
+ * same kernels, arguments, streams and results.
+ */
+#define MOE_MAX_LAUNCHES 32
+typedef struct moe_launch_record {
+  const char* kernel;  /* static name: "gateup", "down_shared", "down_routed" (un-permute + add the shared output),
+                          "down_routed_r" (routed rows into the fp32 workspace), "router", "router_gemm",
+                          "router_finish", "route_small", "scan", "perm", "rmsnorm", "quant_x", "quant_h",
+                          "fill", "combine", "combine_topk", "swiglu_parts" */
+  int32_t side_stream; /* 1: the plan's side stream; 0: the caller's stream */
+  int32_t tile_rows;   /* rows per tile of a GEMM launch (0 otherwise) */
+  int32_t groups;      /* GEMMs and quant_h: 0 routed groups, 1 shared expert, 2 both; -1 otherwise */
+  int32_t part;        /* routed GEMMs: 0 all rows; 1 the main tiles (a group's last 1..32 rows past its last
+                          full tile_rows tile are left out); 2 those last rows alone */
+} moe_launch_record;
+moe_status moe_forward_traced(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
+                              moe_routing* routing_out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, hipEvent_t* events, int32_t max_launches,
+                              moe_launch_record* launches, int32_t* n_launches);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status s);
 

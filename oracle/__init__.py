@@ -19,7 +19,8 @@ Contents
 
 What the block computes is taken from: the KerasFormers "Llama 4" page,
 section "What is unusual about the block" (top-1 of 16 / 128 experts, a
-sigmoid gate on the scaled input, a shared MLP alongside the experts); the
+routed expert's input multiplied by the sigmoid of its logit, a shared MLP
+alongside the experts); the
 superteams.ai glossary "Llama 4", section "Mixture of Experts: Why Total and
 Active Parameters Diverge" (one logit per expert, argmax, the shared
 expert's output plus the routed expert's output, the other experts idle);

@@ -16,7 +16,8 @@ Steps, in the order the pages give them:
    architecture field", ffns.moe.active = 1).
 3. Gate: g = sigmoid(l[t, e*]) of the selected logit, applied to the
    token's input of the routed expert only (KerasFormers "Llama 4", "What is
-   unusual about the block": routed with a sigmoid gate on the scaled input).
+   unusual about the block": the chosen expert receives the token multiplied
+   by the sigmoid of its logit).
    No softmax, no renormalisation.  Because the expert's first layer is
    linear, g * (x W) = (g x) W; the oracle uses the former.
 4. Routed expert e*: SwiGLU MLP, h = SiLU(u Wg) * (u Wu), y = h Wd, with

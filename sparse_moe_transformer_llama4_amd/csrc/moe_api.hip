@@ -23,6 +23,7 @@ struct AuxStream {
   hipEvent_t fork = nullptr, join = nullptr;  // side stream starts after / main stream resumes after
   hipEvent_t routed = nullptr;                // routing done (main stream)
   hipEvent_t shared = nullptr;                // shared expert's output done (side stream)
+  hipEvent_t gateup = nullptr;                // routed main gate/up tiles done (main stream)
 };
 constexpr int kMaxDevices = 16;
 
@@ -40,6 +41,43 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-launch events of moe_forward_traced: while a traced call is enqueued
+// on this thread, every launch below is bracketed by two events recorded on
+// the stream the launch goes to.  Null (no tracing) for every other call.
+struct Trace {
+  hipEvent_t* ev;          // [2 * cap]
+  moe_launch_record* rec;  // [cap]
+  int cap, n;
+  hipStream_t caller;
+  hipError_t err;
+};
+thread_local Trace* g_trace = nullptr;
+
+void trace_begin(const char* name, int tile_rows, int groups, int part, hipStream_t s) {
+  Trace* t = g_trace;
+  if (!t) return;
+  if (t->n >= t->cap) {
+    if (t->err == hipSuccess) t->err = hipErrorInvalidValue;
+    return;
+  }
+  t->rec[t->n] = moe_launch_record{name, s != t->caller ? 1 : 0, tile_rows, groups, part};
+  const hipError_t e = hipEventRecord(t->ev[2 * t->n], s);
+  if (e != hipSuccess && t->err == hipSuccess) t->err = e;
+}
+
+hipError_t trace_end(hipStream_t s, hipError_t call) {
+  Trace* t = g_trace;
+  if (!t || t->n >= t->cap) return call;
+  const hipError_t e = hipEventRecord(t->ev[2 * t->n + 1], s);
+  ++t->n;
+  return call != hipSuccess ? call : e;
+}
+
+// groups: 0 routed, 1 shared, 2 both, -1 not a GEMM; part: 0 all rows,
+// 1 the main tiles (tails left out), 2 the tails alone
+#define TRACED(name, rows, groups, part, s, call) \
+  (trace_begin((name), (rows), (groups), (part), (s)), trace_end((s), (call)))
 
 bool config_dtypes_ok(const moe_config& c) {
   if (c.x_dtype == MOE_F32 && c.w_dtype == MOE_F32 && c.out_dtype == MOE_F32) return true;
@@ -242,7 +280,7 @@ hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_we
   RouterArgs ra{x, w->w_router, c.has_router_bias ? w->router_bias : nullptr, T, c.d, c.n_experts,
                 R.idx, R.gate, R.hist, c.top_k};
   if (T > 0 && T <= kRouteTokens)
-    return launch_route_small(ra, c.x_dtype, R.logits, R.counts, R.offsets, R.tiles, R.perm, s);
+    return TRACED("route_small", 0, -1, 0, s, launch_route_small(ra, c.x_dtype, R.logits, R.counts, R.offsets, R.tiles, R.perm, s));
   // Prefill-sized bf16 calls with E a multiple of 64: the logits x·W_router
   // come from the pipelined bf16 GEMM (its fp32 [T][N] mode), then the
   // fixed-order finish; otherwise the dedicated router kernels.
@@ -261,14 +299,17 @@ hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_we
     g.C_shared = R.logits;
     g.group_lo = c.n_experts;
     g.group_hi = c.n_experts + 1;
-    if ((e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, 64, g, T, s, R.tiles)) != hipSuccess) return e;
-    if ((e = launch_router_finish(ra, 1, R.logits, s)) != hipSuccess) return e;
+    if ((e = TRACED("router_gemm", 64, -1, 0, s, launch_gemm_bf16_v2(MODE_DOWN_SHARED, 64, g, T, s, R.tiles))) != hipSuccess)
+      return e;
+    if ((e = TRACED("router_finish", 0, -1, 0, s, launch_router_finish(ra, 1, R.logits, s))) != hipSuccess) return e;
   } else if (T > 0) {
-    if ((e = launch_router(ra, c.x_dtype, R.logits, s)) != hipSuccess) return e;
+    if ((e = TRACED("router", 0, -1, 0, s, launch_router(ra, c.x_dtype, R.logits, s))) != hipSuccess) return e;
   }
   ScanArgs sa{R.hist, (T + kRouteTokens - 1) / kRouteTokens, c.n_experts, T, R.counts, R.offsets, R.tiles};
-  if ((e = launch_scan(sa, s)) != hipSuccess) return e;
-  if (T > 0 && (e = launch_perm(R.idx, R.hist, R.offsets, T, c.n_experts, c.top_k, R.perm, s)) != hipSuccess) return e;
+  if ((e = TRACED("scan", 0, -1, 0, s, launch_scan(sa, s))) != hipSuccess) return e;
+  if (T > 0 && (e = TRACED("perm", 0, -1, 0, s, launch_perm(R.idx, R.hist, R.offsets, T, c.n_experts, c.top_k, R.perm, s))) !=
+                   hipSuccess)
+    return e;
   return hipSuccess;
 }
 
@@ -360,9 +401,10 @@ GemmArgs down_routed_args(const moe_config& c, const moe_weights* w, uint8_t* ws
 hipError_t finish_topk(const moe_config& c, uint8_t* ws, const WsLayout& L, int T, int parts, void* out,
                        hipStream_t s) {
   if (c.top_k <= 1) return hipSuccess;
-  return launch_combine_topk(reinterpret_cast<const float*>(ws + L.r_out), c.top_k,
-                             reinterpret_cast<const float*>(ws + L.y_s), parts, out, T, c.d,
-                             c.out_dtype == MOE_BF16, s);
+  return TRACED("combine_topk", 0, -1, 0, s,
+                launch_combine_topk(reinterpret_cast<const float*>(ws + L.r_out), c.top_k,
+                                    reinterpret_cast<const float*>(ws + L.y_s), parts, out, T, c.d,
+                                    c.out_dtype == MOE_BF16, s));
 }
 
 // The plan's side stream of the calling device (created on first use), or
@@ -378,7 +420,7 @@ const AuxStream* aux_for(moe_plan_t plan, hipStream_t stream, hipError_t* err) {
   AuxStream& a = plan->aux[cur];
   if (!a.stream) {
     hipStream_t st = nullptr;
-    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
     if ((*err = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return nullptr;
     for (hipEvent_t& x : ev) {
       if ((*err = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) {
@@ -393,6 +435,7 @@ const AuxStream* aux_for(moe_plan_t plan, hipStream_t stream, hipError_t* err) {
     a.join = ev[1];
     a.routed = ev[2];
     a.shared = ev[3];
+    a.gateup = ev[4];
   }
   return &a;
 }
@@ -412,18 +455,25 @@ hipError_t enqueue_decode_overlapped(const moe_config& c, const void* x, int T, 
   GemmArgs g1 = gateup_args(c, w, ws, L, R, x, nullptr, nullptr, nullptr, T);
   g1.group_lo = c.n_experts;
   g1.group_hi = c.n_experts + 1;
-  if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, T, aux.stream, R.tiles)) != hipSuccess) return e;
+  if ((e = TRACED("gateup", 32, 1, 0, aux.stream, launch_gemm_decode(MODE_GATEUP, true, g1, T, aux.stream, R.tiles))) !=
+      hipSuccess)
+    return e;
   const GemmArgs g2 = down_shared_args(c, w, ws, L, R, ws + L.h_s, nullptr, T, ys);
-  if ((e = launch_gemm_decode(MODE_DOWN_SHARED, true, g2, T, aux.stream, R.tiles)) != hipSuccess) return e;
+  if ((e = TRACED("down_shared", 32, 1, 0, aux.stream,
+                  launch_gemm_decode(MODE_DOWN_SHARED, true, g2, T, aux.stream, R.tiles))) != hipSuccess)
+    return e;
   if ((e = hipEventRecord(aux.join, aux.stream)) != hipSuccess) return e;
 
   if ((e = enqueue_route(c, x, T, w, R, stream)) != hipSuccess) return e;
   g1.group_lo = 0;
   g1.group_hi = c.n_experts;
-  if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, T, stream, R.tiles)) != hipSuccess) return e;
+  if ((e = TRACED("gateup", 32, 0, 0, stream, launch_gemm_decode(MODE_GATEUP, true, g1, T, stream, R.tiles))) != hipSuccess)
+    return e;
   if ((e = hipStreamWaitEvent(stream, aux.join, 0)) != hipSuccess) return e;
   const GemmArgs g3 = down_routed_args(c, w, ws, L, R, ws + L.h_r, nullptr, out, T, ys);
-  if ((e = launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, T, stream, R.tiles)) != hipSuccess) return e;
+  if ((e = TRACED("down_routed", 16, 0, 0, stream, launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, T, stream, R.tiles))) !=
+      hipSuccess)
+    return e;
   return finish_topk(c, ws, L, T, ys, out, stream);
 }
 
@@ -433,7 +483,8 @@ hipError_t enqueue_decode_overlapped(const moe_config& c, const void* x, int T, 
 // tokens) on the 32-row weight-streaming tiles over table_tail.  With a side
 // stream:
 //   side: shared gate/up -> (h_s done) -> [routing done] -> tail gate/up ->
-//         tail down (into r_out) -> (join)
+//         [main gate/up done, only when bm_d < bm_r] -> tail down (into
+//         r_out) -> (join)
 //   main: routing -> routed main gate/up -> [h_s done] -> one down launch:
 //         routed main tiles (into r_out) + shared tiles (into y_s) ->
 //         [join] -> combine out = r_out + y_s
@@ -486,38 +537,73 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
     }
     if ((e = hipEventRecord(aux->fork, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(a, aux->fork, 0)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, T, a, R.tiles)) != hipSuccess) return e;
-    if (!merge_down && (e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, 256, g2, T, a, R.tiles)) != hipSuccess) return e;
+    if ((e = TRACED("gateup", 256, 1, 0, a, launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, T, a, R.tiles))) != hipSuccess) return e;
+    if (!merge_down &&
+        (e = TRACED("down_shared", 256, 1, 0, a, launch_gemm_bf16_v2(MODE_DOWN_SHARED, 256, g2, T, a, R.tiles))) != hipSuccess)
+      return e;
     if ((e = hipEventRecord(aux->shared, a)) != hipSuccess) return e;
     if ((e = enqueue_route(c, x, T, w, R, stream)) != hipSuccess) return e;
     if (tails) {
       if ((e = hipEventRecord(aux->routed, stream)) != hipSuccess) return e;
       if ((e = hipStreamWaitEvent(a, aux->routed, 0)) != hipSuccess) return e;
-      if ((e = launch_gemm_decode_tail(MODE_GATEUP, g1, bm_r, a, R.tiles)) != hipSuccess) return e;
-      if ((e = launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3r, bm_d, a, R.tiles)) != hipSuccess) return e;
+      if ((e = TRACED("gateup", bm_r, 0, 2, a, launch_gemm_decode_tail(MODE_GATEUP, g1, bm_r, a, R.tiles))) != hipSuccess)
+        return e;
+    }
+    if ((e = TRACED("gateup", bm_r, 0, tails ? 1 : 0, stream,
+                    launch_gemm_bf16_v2(MODE_GATEUP, bm_r, g1, T, stream, tiles_main))) != hipSuccess)
+      return e;
+    if (tails) {
+      // With bm_d < bm_r the down tails are not the gate/up tails: a group
+      // of n rows with n % bm_r in bm_d+1 .. bm_d+32 has its last n % bm_d
+      // rows of h_r written by a main gate/up tile on `stream`, so the tail
+      // down GEMM waits for the main gate/up launch.  With bm_d == bm_r the
+      // down tails read exactly the rows the tail gate/up wrote on this side
+      // stream.  (bm_d <= bm_r always; for bm_r = 256, bm_d = 128 the gate/up
+      // tails are a subset of the down tails, so the main down tiles never
+      // read a row the side stream writes.)
+      if (bm_d != bm_r) {
+        if ((e = hipEventRecord(aux->gateup, stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(a, aux->gateup, 0)) != hipSuccess) return e;
+      }
+      if ((e = TRACED("down_routed_r", bm_d, 0, 2, a, launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3r, bm_d, a, R.tiles))) !=
+          hipSuccess)
+        return e;
     }
     if ((e = hipEventRecord(aux->join, a)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_r, g1, T, stream, tiles_main)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(stream, aux->shared, 0)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3m, T, stream, tiles_main)) != hipSuccess) return e;
+    if ((e = TRACED("down_routed_r", bm_d, merge_down ? 2 : 0, tails ? 1 : 0, stream,
+                    launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3m, T, stream, tiles_main))) != hipSuccess)
+      return e;
     if ((e = hipStreamWaitEvent(stream, aux->join, 0)) != hipSuccess) return e;
     if (c.top_k > 1) return finish_topk(c, ws, L, T, 1, out, stream);
-    return launch_combine(reinterpret_cast<const float*>(ws + L.r_out), reinterpret_cast<const float*>(ws + L.y_s), 1,
-                          out, static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream);
+    return TRACED("combine", 0, -1, 0, stream,
+                  launch_combine(reinterpret_cast<const float*>(ws + L.r_out), reinterpret_cast<const float*>(ws + L.y_s),
+                                 1, out, static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream));
   }
 
   auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return e;
   if ((e = enqueue_route(c, x, T, w, R, stream)) != hipSuccess) return e;
   if ((e = mark(1)) != hipSuccess) return e;
-  if (tails && (e = launch_gemm_decode_tail(MODE_GATEUP, g1, bm_r, stream, R.tiles)) != hipSuccess) return e;
-  if ((e = launch_gemm_bf16_v2(MODE_GATEUP, bm_r, g1, T, stream, tiles_main)) != hipSuccess) return e;
-  if ((e = launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, T, stream, R.tiles)) != hipSuccess) return e;
+  if (tails && (e = TRACED("gateup", bm_r, 0, 2, stream, launch_gemm_decode_tail(MODE_GATEUP, g1, bm_r, stream, R.tiles))) !=
+                   hipSuccess)
+    return e;
+  if ((e = TRACED("gateup", bm_r, 0, tails ? 1 : 0, stream,
+                  launch_gemm_bf16_v2(MODE_GATEUP, bm_r, g1, T, stream, tiles_main))) != hipSuccess)
+    return e;
+  if ((e = TRACED("gateup", 256, 1, 0, stream, launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, T, stream, R.tiles))) != hipSuccess)
+    return e;
   if ((e = mark(2)) != hipSuccess) return e;
-  if ((e = launch_gemm_bf16_v2(MODE_DOWN_SHARED, bm_sd, g2, T, stream, R.tiles)) != hipSuccess) return e;
+  if ((e = TRACED("down_shared", bm_sd, 1, 0, stream, launch_gemm_bf16_v2(MODE_DOWN_SHARED, bm_sd, g2, T, stream, R.tiles))) !=
+      hipSuccess)
+    return e;
   if ((e = mark(3)) != hipSuccess) return e;
-  if (tails && (e = launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3, bm_d, stream, R.tiles)) != hipSuccess) return e;
-  if ((e = launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3, T, stream, tiles_main)) != hipSuccess) return e;
+  if (tails && (e = TRACED("down_routed", bm_d, 0, 2, stream, launch_gemm_decode_tail(MODE_DOWN_ROUTED, g3, bm_d, stream, R.tiles))) !=
+                   hipSuccess)
+    return e;
+  if ((e = TRACED("down_routed", bm_d, 0, tails ? 1 : 0, stream,
+                  launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3, T, stream, tiles_main))) != hipSuccess)
+    return e;
   if ((e = finish_topk(c, ws, L, T, 1, out, stream)) != hipSuccess) return e;
   return mark(4);
 }
@@ -547,11 +633,12 @@ hipError_t enqueue_dense(const moe_config& c, const void* x, int T, const moe_we
     g1.gu_part = reinterpret_cast<float*>(ws + L.gu_part);
     g1.ksplit = gp;
   }
-  e = small ? launch_gemm_decode(MODE_GATEUP, true, g1, T, stream, R.tiles)
-            : launch_gemm_bf16_v2(MODE_GATEUP, 256, g1, T, stream, R.tiles);
+  e = small ? TRACED("gateup", 32, 1, 0, stream, launch_gemm_decode(MODE_GATEUP, true, g1, T, stream, R.tiles))
+            : TRACED("gateup", 256, 1, 0, stream, launch_gemm_bf16_v2(MODE_GATEUP, 256, g1, T, stream, R.tiles));
   if (e == hipSuccess && gp > 1)
-    e = launch_swiglu_parts(reinterpret_cast<const float*>(ws + L.gu_part), gp, T, c.f_shared,
-                            reinterpret_cast<uint16_t*>(ws + L.h_s), stream);
+    e = TRACED("swiglu_parts", 0, -1, 0, stream,
+               launch_swiglu_parts(reinterpret_cast<const float*>(ws + L.gu_part), gp, T, c.f_shared,
+                                   reinterpret_cast<uint16_t*>(ws + L.h_s), stream));
   if (e != hipSuccess || (e = mark(2)) != hipSuccess) return e;
   const int parts = small ? dense_down_parts(c, T) : 1;
   GemmArgs g2 = down_shared_args(c, w, ws, L, R, ws + L.h_s, nullptr, T, parts);
@@ -560,12 +647,14 @@ hipError_t enqueue_dense(const moe_config& c, const void* x, int T, const moe_we
   // prefill down tiles of 128 rows: on the Maverick-shaped layer (T = 8192,
   // d = 5120) 1280 of them fill 5 rounds of the 256 CUs where 640 256-row
   // tiles fill 2.5 (measured 1.55 -> 1.39 ms; 128-row gate/up tiles lost)
-  e = small ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, T, stream, R.tiles)
-            : launch_gemm_bf16_v2(MODE_DOWN_SHARED, 128, g2, T, stream, R.tiles);
+  e = small ? TRACED("down_shared", 32, 1, 0, stream, launch_gemm_decode(MODE_DOWN_SHARED, true, g2, T, stream, R.tiles))
+            : TRACED("down_shared", 128, 1, 0, stream,
+                     launch_gemm_bf16_v2(MODE_DOWN_SHARED, 128, g2, T, stream, R.tiles));
   if (e != hipSuccess || (e = mark(3)) != hipSuccess) return e;
   if (!direct &&
-      (e = launch_combine(nullptr, reinterpret_cast<const float*>(ws + L.y_s), parts, out,
-                          static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream)) != hipSuccess)
+      (e = TRACED("combine", 0, -1, 0, stream,
+                  launch_combine(nullptr, reinterpret_cast<const float*>(ws + L.y_s), parts, out,
+                                 static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream))) != hipSuccess)
     return e;
   return mark(4);
 }
@@ -627,7 +716,7 @@ moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
 void moe_plan_destroy(moe_plan_t plan) {
   if (!plan) return;
   for (AuxStream& a : plan->aux) {
-    for (hipEvent_t ev : {a.fork, a.join, a.routed, a.shared})
+    for (hipEvent_t ev : {a.fork, a.join, a.routed, a.shared, a.gateup})
       if (ev) (void)hipEventDestroy(ev);
     if (a.stream) (void)hipStreamDestroy(a.stream);
   }
@@ -655,8 +744,9 @@ moe_status moe_route(moe_plan_t plan, const void* x, int64_t T, const moe_weight
   const Route R = route_ptrs(ws, L, out);
   hipError_t e = hipSuccess;
   if (plan->cfg.has_norm) {
-    e = launch_rmsnorm(plan->cfg.x_dtype, x, w->norm_weight, static_cast<int>(T), plan->cfg.d, plan->cfg.norm_eps,
-                       ws + L.x_n, nullptr, nullptr, stream);
+    e = TRACED("rmsnorm", 0, -1, 0, stream,
+               launch_rmsnorm(plan->cfg.x_dtype, x, w->norm_weight, static_cast<int>(T), plan->cfg.d,
+                              plan->cfg.norm_eps, ws + L.x_n, nullptr, nullptr, stream));
     x = ws + L.x_n;
   }
   if (e == hipSuccess) e = enqueue_route(plan->cfg, x, static_cast<int>(T), w, R, stream);
@@ -693,8 +783,9 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
       ev = evn;
     }
     const hipError_t en =
-        launch_rmsnorm(c.x_dtype, x, w->norm_weight, Ti, c.d, c.norm_eps, ws + L.x_n, fp8 ? ws + L.xq : nullptr,
-                       fp8 ? reinterpret_cast<float*>(ws + L.sx) : nullptr, stream);
+        TRACED("rmsnorm", 0, -1, 0, stream,
+               launch_rmsnorm(c.x_dtype, x, w->norm_weight, Ti, c.d, c.norm_eps, ws + L.x_n, fp8 ? ws + L.xq : nullptr,
+                              fp8 ? reinterpret_cast<float*>(ws + L.sx) : nullptr, stream));
     if (en != hipSuccess) return hip_fail(plan, en);
     x = ws + L.x_n;
   }
@@ -744,13 +835,15 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   if (fp8) {
     uint8_t* xq = ws + L.xq;
     sx = reinterpret_cast<float*>(ws + L.sx);
-    if (!c.has_norm && (e = launch_quant_x(static_cast<const uint16_t*>(x), Ti, c.d, xq, sx, stream)) != hipSuccess)
+    if (!c.has_norm && (e = TRACED("quant_x", 0, -1, 0, stream,
+                                   launch_quant_x(static_cast<const uint16_t*>(x), Ti, c.d, xq, sx, stream))) != hipSuccess)
       return hip_fail(plan, e);
     a_x = xq;
     amax_r = reinterpret_cast<uint32_t*>(ws + L.amax_r);
     amax_s = reinterpret_cast<uint32_t*>(ws + L.amax_s);
-    if ((e = launch_fill_u32(amax_r, T * c.top_k, 0u, stream)) != hipSuccess) return hip_fail(plan, e);   // slot rows
-    if ((e = launch_fill_u32(amax_s, T, 0u, stream)) != hipSuccess) return hip_fail(plan, e);
+    if ((e = TRACED("fill", 0, -1, 0, stream, launch_fill_u32(amax_r, T * c.top_k, 0u, stream))) != hipSuccess)   // slot rows
+      return hip_fail(plan, e);
+    if ((e = TRACED("fill", 0, -1, 0, stream, launch_fill_u32(amax_s, T, 0u, stream))) != hipSuccess) return hip_fail(plan, e);
   }
   if ((e = mark(1)) != hipSuccess) return hip_fail(plan, e);
 
@@ -760,27 +853,29 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     g1.group_lo = 0;
     g1.group_hi = c.n_experts + 1;
     const int bm = fp8_routed_rows(static_cast<int64_t>(Ti) * c.top_k, c.n_experts);
-    if ((e = launch_gemm_fp8(MODE_GATEUP, bm, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
+    if ((e = TRACED("gateup", bm, 2, 0, stream, launch_gemm_fp8(MODE_GATEUP, bm, g1, Ti, stream, R.tiles))) != hipSuccess)
+      return hip_fail(plan, e);
   } else if (dec && int_weights(c)) {
     // int8 / int4 tiles: the routed groups, then the shared expert
     g1.group_lo = 0;
     g1.group_hi = c.n_experts;
-    if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles)) != hipSuccess)
+    if ((e = TRACED("gateup", 32, 0, 0, stream, launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles))) != hipSuccess)
       return hip_fail(plan, e);
     g1.group_lo = c.n_experts;
     g1.group_hi = c.n_experts + 1;
-    if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles)) != hipSuccess)
+    if ((e = TRACED("gateup", 32, 1, 0, stream, launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles))) != hipSuccess)
       return hip_fail(plan, e);
   } else if (dec) {
     // routed groups and the shared expert in one launch of 32-row tiles
     g1.group_lo = 0;
     g1.group_hi = c.n_experts + 1;
-    if ((e = launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles)) != hipSuccess)
+    if ((e = TRACED("gateup", 32, 2, 0, stream, launch_gemm_decode(MODE_GATEUP, true, g1, Ti, stream, R.tiles))) != hipSuccess)
       return hip_fail(plan, e);
   } else {
     g1.group_lo = 0;
     g1.group_hi = c.n_experts + 1;
-    if ((e = launch_gemm(MODE_GATEUP, c.w_dtype, g1, Ti, stream, R.tiles)) != hipSuccess) return hip_fail(plan, e);
+    if ((e = TRACED("gateup", 0, 2, 0, stream, launch_gemm(MODE_GATEUP, c.w_dtype, g1, Ti, stream, R.tiles))) != hipSuccess)
+      return hip_fail(plan, e);
   }
   if ((e = mark(2)) != hipSuccess) return hip_fail(plan, e);
 
@@ -790,11 +885,13 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   if (fp8) {
     sh_r = reinterpret_cast<float*>(ws + L.sh_r);
     sh_s = reinterpret_cast<float*>(ws + L.sh_s);
-    if ((e = launch_quant_h(reinterpret_cast<const float*>(ws + L.h_r), amax_r, Ti * c.top_k, c.f, ws + L.hq_r, sh_r,
-                            stream)) != hipSuccess)
+    if ((e = TRACED("quant_h", 0, 0, 0, stream,
+                    launch_quant_h(reinterpret_cast<const float*>(ws + L.h_r), amax_r, Ti * c.top_k, c.f, ws + L.hq_r,
+                                   sh_r, stream))) != hipSuccess)
       return hip_fail(plan, e);
-    if ((e = launch_quant_h(reinterpret_cast<const float*>(ws + L.h_s), amax_s, Ti, c.f_shared, ws + L.hq_s,
-                            sh_s, stream)) != hipSuccess)
+    if ((e = TRACED("quant_h", 0, 1, 0, stream,
+                    launch_quant_h(reinterpret_cast<const float*>(ws + L.h_s), amax_s, Ti, c.f_shared, ws + L.hq_s,
+                                   sh_s, stream))) != hipSuccess)
       return hip_fail(plan, e);
     h_r = ws + L.hq_r;
     h_s = ws + L.hq_s;
@@ -802,17 +899,17 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
 
   const int ys = dec ? decode_y_parts(c, T) : 1;
   const GemmArgs g2 = down_shared_args(c, w, ws, L, R, h_s, sh_s, Ti, ys);
-  e = f8    ? launch_gemm_fp8(MODE_DOWN_SHARED, 128, g2, Ti, stream, R.tiles)
-      : dec ? launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles)
-            : launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles);
+  e = f8    ? TRACED("down_shared", 128, 1, 0, stream, launch_gemm_fp8(MODE_DOWN_SHARED, 128, g2, Ti, stream, R.tiles))
+      : dec ? TRACED("down_shared", 32, 1, 0, stream, launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles))
+            : TRACED("down_shared", 0, 1, 0, stream, launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles));
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(plan, e);
 
   const GemmArgs g3 = down_routed_args(c, w, ws, L, R, h_r, sh_r, out, Ti, ys);
-  e = f8    ? launch_gemm_fp8(MODE_DOWN_ROUTED, fp8_routed_rows(static_cast<int64_t>(Ti) * c.top_k, c.n_experts), g3,
-                              Ti, stream, R.tiles)
-      : dec ? launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles)
-            : launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles);
+  const int bm_f8 = fp8_routed_rows(static_cast<int64_t>(Ti) * c.top_k, c.n_experts);
+  e = f8    ? TRACED("down_routed", bm_f8, 0, 0, stream, launch_gemm_fp8(MODE_DOWN_ROUTED, bm_f8, g3, Ti, stream, R.tiles))
+      : dec ? TRACED("down_routed", 16, 0, 0, stream, launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles))
+            : TRACED("down_routed", 0, 0, 0, stream, launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles));
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = finish_topk(c, ws, L, Ti, ys, out, stream)) != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(4)) != hipSuccess) return hip_fail(plan, e);
@@ -830,6 +927,22 @@ moe_status moe_forward_timed(moe_plan_t plan, const void* x, int64_t T, const mo
                              hipStream_t stream, hipEvent_t* events) {
   if (!events) return MOE_ERR_INVALID_ARGUMENT;
   return forward_impl(plan, x, T, w, out, routing_out, workspace, workspace_bytes, stream, events);
+}
+
+moe_status moe_forward_traced(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
+                              moe_routing* routing_out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, hipEvent_t* events, int32_t max_launches,
+                              moe_launch_record* launches, int32_t* n_launches) {
+  if (!events || !launches || !n_launches || max_launches < MOE_MAX_LAUNCHES) return MOE_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 2 * max_launches; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARGUMENT;
+  Trace t{events, launches, max_launches, 0, stream, hipSuccess};
+  g_trace = &t;
+  moe_status st = forward_impl(plan, x, T, w, out, routing_out, workspace, workspace_bytes, stream, nullptr);
+  g_trace = nullptr;
+  *n_launches = t.n;
+  if (st == MOE_OK && t.err != hipSuccess) st = hip_fail(plan, t.err);
+  return st;
 }
 
 }  // extern "C"

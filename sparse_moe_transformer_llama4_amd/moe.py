@@ -23,8 +23,9 @@ _TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.u
 
 # names declared in include/moe.h
 symbols = ("moe_plan", "moe_plan_destroy", "moe_workspace_size", "moe_route", "moe_forward",
-           "moe_forward_timed", "moe_status_string", "moe_last_hip_error", "moe_version")
+           "moe_forward_timed", "moe_forward_traced", "moe_status_string", "moe_last_hip_error", "moe_version")
 MOE_NUM_STAGES = 4
+MOE_MAX_LAUNCHES = 32
 STAGES = ("route", "gate_up", "down_shared", "down_routed")
 
 
@@ -56,6 +57,11 @@ class _Routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("expert_idx", "gate", "counts", "offsets", "perm")]
 
 
+class _LaunchRecord(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("side_stream", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
+                ("groups", ctypes.c_int32), ("part", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -82,6 +88,10 @@ def load_library(path: str = LIB_PATH):
     lib.moe_forward_timed.argtypes = [P, P, I64, ctypes.POINTER(_Weights), P, ctypes.POINTER(_Routing), P, SZ,
                                       P, ctypes.POINTER(P)]
     lib.moe_forward_timed.restype = ctypes.c_int
+    lib.moe_forward_traced.argtypes = [P, P, I64, ctypes.POINTER(_Weights), P, ctypes.POINTER(_Routing), P, SZ,
+                                       P, ctypes.POINTER(P), ctypes.c_int32, ctypes.POINTER(_LaunchRecord),
+                                       ctypes.POINTER(ctypes.c_int32)]
+    lib.moe_forward_traced.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_hip_error.argtypes = [P]
@@ -214,12 +224,62 @@ def _check_inputs(plan: Plan, x: torch.Tensor, w: dict):
         raise ValueError("w_router shape")
 
 
+def _check_shape(t: torch.Tensor, name: str, dtype, shape):
+    _check_tensor(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: need shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_weights(plan: Plan, w: dict):
+    """Expert and shared weights (and their fp32 column scales) against the
+    plan: the C ABI receives bare pointers, so a wrongly shaped tensor would
+    otherwise be read out of bounds on the device."""
+    wdt = _TORCH_DT[_DT[plan.w_dtype]]
+    kd = 2 if plan.w_dtype == "i4" else 1          # int4: two K rows per byte row
+    E, d, f, fs = plan.E, plan.d, plan.f, plan.fs
+    mats = {"ws_gate_up": (d // kd, 2 * fs), "ws_down": (fs // kd, d)}
+    scales = {"ss_gate_up": (2 * fs,), "ss_down": (d,)}
+    if E > 0:
+        mats.update(w_gate_up=(E, d // kd, 2 * f), w_down=(E, f // kd, d))
+        scales.update(s_gate_up=(E, 2 * f), s_down=(E, d))
+    for k, shp in mats.items():
+        if w.get(k) is None:
+            raise ValueError(f"{k} is required")
+        _check_shape(w[k], k, wdt, shp)
+    if plan.w_dtype in ("e4m3", "i8", "i4"):
+        for k, shp in scales.items():
+            if w.get(k) is None:
+                raise ValueError(f"{k} is required for {plan.w_dtype} weights")
+            _check_shape(w[k], k, torch.float32, shp)
+    if E > 0 and plan.has_bias:
+        if w.get("router_bias") is None:
+            raise ValueError("router_bias is required by this plan")
+        _check_shape(w["router_bias"], "router_bias", torch.float32, (E,))
+
+
+def _check_routing_buffers(plan: Plan, T: int, routing: Optional[dict]):
+    if routing is None:
+        return
+    S = T * plan.top_k
+    need = {"expert_idx": (S, torch.int32), "gate": (S, torch.float32), "perm": (S, torch.int32),
+            "counts": (plan.E, torch.int32), "offsets": (plan.E + 1, torch.int32)}
+    for k, (n, dt) in need.items():
+        _check_tensor(routing[k], k, dt)
+        if routing[k].numel() < n:
+            raise ValueError(f"routing[{k!r}] holds {routing[k].numel()} values, needs {n}")
+
+
 def moe_route(plan: Plan, x: torch.Tensor, w: dict, routing: Optional[dict] = None,
               workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Router + top-1 + gate + stable expert grouping; returns the routing dict."""
     _check_inputs(plan, x, w)
     T = x.shape[0]
+    if plan.E > 0 and plan.has_bias:
+        if w.get("router_bias") is None:
+            raise ValueError("router_bias is required by this plan")
+        _check_shape(w["router_bias"], "router_bias", torch.float32, (plan.E,))
     routing = routing or new_routing(plan, T, x.device)
+    _check_routing_buffers(plan, T, routing)
     ws = _workspace(plan, T, workspace, x.device)
     r = _routing(routing)
     st = load_library().moe_route(plan.handle, _ptr(x), T, ctypes.byref(_weights(w)), ctypes.byref(r),
@@ -234,13 +294,12 @@ def moe_forward(plan: Plan, x: torch.Tensor, w: dict, out: Optional[torch.Tensor
                 stream=None) -> torch.Tensor:
     """The whole block: out = shared(x) + routed(x)."""
     _check_inputs(plan, x, w)
+    _check_weights(plan, w)
     T = x.shape[0]
-    wdt = _TORCH_DT[_DT[plan.w_dtype]]
-    for k in ("w_gate_up", "w_down", "ws_gate_up", "ws_down") if plan.E > 0 else ("ws_gate_up", "ws_down"):
-        _check_tensor(w[k], k, wdt)
     if out is None:
         out = torch.empty((T, plan.d), dtype=_TORCH_DT[_DT[plan.out_dtype]], device=x.device)
-    _check_tensor(out, "out", _TORCH_DT[_DT[plan.out_dtype]])
+    _check_shape(out, "out", _TORCH_DT[_DT[plan.out_dtype]], (T, plan.d))
+    _check_routing_buffers(plan, T, routing)
     ws = _workspace(plan, T, workspace, x.device)
     r = _routing(routing)
     st = load_library().moe_forward(plan.handle, _ptr(x), T, ctypes.byref(_weights(w)), _ptr(out),
@@ -306,11 +365,71 @@ class StageEvents:
 def moe_forward_timed(plan: Plan, x: torch.Tensor, w: dict, events: StageEvents, out: torch.Tensor,
                       workspace: torch.Tensor, routing: Optional[dict] = None, stream=None) -> torch.Tensor:
     """moe_forward that records `events` at the stage boundaries."""
+    _check_inputs(plan, x, w)
+    _check_weights(plan, w)
     T = x.shape[0]
+    _check_shape(out, "out", _TORCH_DT[_DT[plan.out_dtype]], (T, plan.d))
+    _check_routing_buffers(plan, T, routing)
     r = _routing(routing)
     st = load_library().moe_forward_timed(plan.handle, _ptr(x), T, ctypes.byref(_weights(w)), _ptr(out),
                                           ctypes.byref(r) if r is not None else None, _ptr(workspace),
                                           workspace.numel(), _stream(stream), events.ev)
     if st != 0:
         raise plan._err(st, "moe_forward_timed")
+    return out
+
+
+class LaunchEvents:
+    """2 * MOE_MAX_LAUNCHES hipEvents and the launch records of one
+    moe_forward_traced call."""
+
+    def __init__(self):
+        h = _hip_runtime()
+        self.n = 2 * MOE_MAX_LAUNCHES
+        self.ev = (ctypes.c_void_p * self.n)()
+        for i in range(self.n):
+            e = ctypes.c_void_p()
+            if h.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev[i] = e
+        self.rec = (_LaunchRecord * MOE_MAX_LAUNCHES)()
+        self.count = ctypes.c_int32(0)
+        self.h = h
+
+    def launches(self):
+        """[(kernel, side_stream, tile_rows, groups, part, ms)] of the last
+        recorded call (synchronises on each launch's end event)."""
+        out = []
+        for i in range(self.count.value):
+            self.h.hipEventSynchronize(self.ev[2 * i + 1])
+            ms = ctypes.c_float()
+            self.h.hipEventElapsedTime(ctypes.byref(ms), self.ev[2 * i], self.ev[2 * i + 1])
+            r = self.rec[i]
+            out.append((r.kernel.decode(), r.side_stream, r.tile_rows, r.groups, r.part, ms.value))
+        return out
+
+    def __del__(self):
+        ev, h = getattr(self, "ev", None), getattr(self, "h", None)
+        if ev is None or h is None:
+            return
+        for i in range(getattr(self, "n", 0)):
+            if ev[i]:
+                h.hipEventDestroy(ev[i])
+
+
+def moe_forward_traced(plan: Plan, x: torch.Tensor, w: dict, events: LaunchEvents, out: torch.Tensor,
+                       workspace: torch.Tensor, routing: Optional[dict] = None, stream=None) -> torch.Tensor:
+    """moe_forward (same schedule and streams) with an event pair around every kernel launch."""
+    _check_inputs(plan, x, w)
+    _check_weights(plan, w)
+    T = x.shape[0]
+    _check_shape(out, "out", _TORCH_DT[_DT[plan.out_dtype]], (T, plan.d))
+    _check_routing_buffers(plan, T, routing)
+    r = _routing(routing)
+    st = load_library().moe_forward_traced(plan.handle, _ptr(x), T, ctypes.byref(_weights(w)), _ptr(out),
+                                           ctypes.byref(r) if r is not None else None, _ptr(workspace),
+                                           workspace.numel(), _stream(stream), events.ev, MOE_MAX_LAUNCHES,
+                                           events.rec, ctypes.byref(events.count))
+    if st != 0:
+        raise plan._err(st, "moe_forward_traced")
     return out

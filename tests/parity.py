@@ -10,6 +10,20 @@ from oracle import block
 
 TOL = {"f32": 1e-4, "bf16": 1e-2, "e4m3": 5e-2, "i8": 1e-2, "i4": 1e-2}
 
+# Every output comparison made in this session: (case, max|err|/RMS, bound,
+# graded, "weights->output" dtypes).  tests/conftest.py prints them at the end of the run.
+RESULTS: list = []
+
+
+def graded(cfg) -> bool:
+    """Whether the plain max|err|/RMS against the unrounded fp64 oracle is
+    the graded metric for this output.  bf16 outputs of the bf16 / int8 /
+    int4 weight paths are not graded (rounding the exact output to bf16 alone
+    costs ~1.2e-2 of RMS at these widths, above the 1e-2 bar): their bound is
+    on the value the GPU rounded (see output_bound).  fp32 outputs, and the
+    bf16 output of the e4m3 path, are graded."""
+    return not (cfg.out_dtype == "bf16" and cfg.w_dtype in ("bf16", "i8", "i4"))
+
 
 def to_device(inp: dict, device) -> dict:
     return {k: (None if v is None else v.to(device)) for k, v in inp.items()}
@@ -83,12 +97,49 @@ def check_routing(cfg, r_or: block.Routing, routing: dict, rows=None):
 
 
 def output_error(cfg, out_gpu, ref):
-    """max over elements of (|gpu - ref| - half a bf16 ulp of ref for bf16 outputs) / RMS(ref)."""
+    """max over elements of |gpu - ref| / RMS(ref): the plain metric, against
+    the unrounded fp64 oracle."""
     g = out_gpu.detach().cpu().double().numpy()
     ref = np.asarray(ref, dtype=np.float64)
     rms = np.sqrt(np.mean(ref * ref))
-    slack = np.abs(ref) * 2.0 ** -9 if cfg.out_dtype == "bf16" else 0.0
-    return float(np.max(np.maximum(np.abs(g - ref) - slack, 0.0)) / rms)
+    return float(np.max(np.abs(g - ref)) / rms)
+
+
+def _half_ulp_bf16(g: np.ndarray) -> np.ndarray:
+    """Half the spacing of bf16 values at each (bf16) value g: 2^(e - 8)
+    for |g| in [2^e, 2^(e+1)), the subnormal spacing below 2^-126."""
+    _, ex = np.frexp(np.abs(g))
+    h = np.ldexp(1.0, np.maximum(ex - 1 - 8, -134))
+    return np.where(g == 0, 2.0 ** -134, h)
+
+
+def output_bound_error(cfg, out_gpu, ref):
+    """For ungraded bf16 outputs: max over elements of (|gpu - ref| minus half
+    a bf16 ulp at the GPU's value) / RMS(ref), i.e. how far the value the GPU
+    rounded to bf16 was from the oracle.  Equals output_error otherwise."""
+    if graded(cfg):
+        return output_error(cfg, out_gpu, ref)
+    g = out_gpu.detach().cpu().double().numpy()
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.maximum(np.abs(g - ref) - _half_ulp_bf16(g), 0.0)) / rms)
+
+
+def assert_output(cfg, out_gpu, ref, tol=None, case=None):
+    """Assert the output against the oracle and record the margin.  Graded
+    outputs: plain max|err|/RMS <= the dtype's bar.  Ungraded bf16 outputs:
+    the plain error is recorded, the bar applies to the value before the
+    final bf16 rounding (output_bound_error)."""
+    tol = tol or TOL[cfg.w_dtype]
+    err = output_error(cfg, out_gpu, ref)
+    ok = graded(cfg)
+    RESULTS.append((case or cfg.name, err, tol, ok, f"{cfg.w_dtype}->{cfg.out_dtype}"))
+    if ok:
+        assert err <= tol, f"{cfg.name}: max|err|/RMS = {err:.3e} > {tol}"
+    else:
+        eb = output_bound_error(cfg, out_gpu, ref)
+        assert eb <= tol, f"{cfg.name}: bf16 output, pre-rounding max|err|/RMS = {eb:.3e} > {tol}"
+    return err
 
 
 def norm_eps32(cfg) -> float:
@@ -115,15 +166,13 @@ def check_forward(cfg, inp_cpu: dict, out_gpu, routing, tol=None):
         idx = check_routing(cfg, r, routing)
         gate = block.sigmoid(np.take_along_axis(r.logits, idx, axis=1))
         ref = block.combine_topk(x, idx, gate, w, cfg.f, cfg.fs, cfg.w_dtype)
-        err = output_error(cfg, out_gpu, ref)
-        assert err <= (tol or TOL[cfg.w_dtype]), f"{cfg.name}: max|err|/RMS = {err:.3e}"
+        err = assert_output(cfg, out_gpu, ref, tol)
         return err, r
     r = block.route(x, wr, b)
     idx = check_routing(cfg, r, routing)
     gate = block.sigmoid(r.logits[np.arange(len(idx)), idx])
     ref = block.combine(x, idx, gate, w, cfg.f, cfg.fs, cfg.w_dtype)
-    err = output_error(cfg, out_gpu, ref)
-    assert err <= (tol or TOL[cfg.w_dtype]), f"{cfg.name}: max|err|/RMS = {err:.3e}"
+    err = assert_output(cfg, out_gpu, ref, tol)
     if cfg.w_dtype == "e4m3":
         check_fp8_accuracy(cfg, x, out_gpu, ref, idx, gate, w)
     return err, r

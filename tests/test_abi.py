@@ -154,6 +154,33 @@ def test_forward_rejects_before_enqueue():
     lib.moe_plan_destroy(h)
 
 
+def test_traced_forward_rejects_before_enqueue():
+    """moe_forward_traced: too few event slots, missing events or records,
+    and every check of moe_forward, all before any HIP call."""
+    lib = moe.load_library()
+    st, h = _plan(max_tokens=64)
+    n = ctypes.c_size_t()
+    lib.moe_workspace_size(h, 64, ctypes.byref(n))
+    P = 0x10000
+    w = _weights(P)
+    M = moe.MOE_MAX_LAUNCHES
+    ev = (ctypes.c_void_p * (2 * M))(*([P] * (2 * M)))
+    rec = (moe._LaunchRecord * M)()
+    cnt = ctypes.c_int32(-1)
+
+    def trc(T, evs, m, recs, count):
+        return lib.moe_forward_traced(h, P, T, ctypes.byref(w), P, None, P, n.value, None, evs, m, recs, count)
+    assert trc(64, ev, M - 1, rec, ctypes.byref(cnt)) == INVALID
+    assert trc(64, None, M, rec, ctypes.byref(cnt)) == INVALID
+    assert trc(64, ev, M, None, ctypes.byref(cnt)) == INVALID
+    assert trc(64, ev, M, rec, None) == INVALID
+    ev_null = (ctypes.c_void_p * (2 * M))(*([P] * (2 * M - 1) + [None]))
+    assert trc(64, ev_null, M, rec, ctypes.byref(cnt)) == INVALID
+    assert trc(65, ev, M, rec, ctypes.byref(cnt)) == SHAPE
+    assert cnt.value == 0                       # nothing was launched
+    lib.moe_plan_destroy(h)
+
+
 def test_dense_layer_rejects_before_enqueue():
     """A dense plan (n_experts == 0): no routing entry point, no routing record,
     the shared weights required, the router and routed weights not."""

@@ -7,7 +7,7 @@ import torch
 
 import synth
 from oracle import block
-from parity import block_input, check_forward, check_routing, run_gpu, to_device, output_error
+from parity import assert_output, block_input, check_forward, check_routing, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -164,6 +164,39 @@ def test_single_expert(gpu):
     check_forward(cfg, inp, out, routing)
 
 
+@pytest.mark.parametrize("case", ["w_down_swapped", "int4_unpacked", "scale_shape", "scale_missing",
+                                  "bias_missing", "out_shape", "routing_short"])
+def test_binding_rejects_wrong_shapes_before_the_call(gpu, case):
+    # the C ABI takes bare pointers; the binding checks every tensor's shape
+    # and dtype against the plan and raises before the library is called
+    from sparse_moe_transformer_llama4_amd import moe
+    name = {"int4_unpacked": "decode_like_bf16", "scale_shape": "small_fp8", "scale_missing": "small_fp8",
+            "bias_missing": "small_bf16_bias"}.get(case, "small_bf16")
+    cfg = synth.get_config(name)
+    if case == "int4_unpacked":
+        cfg = dataclasses.replace(cfg, w_dtype="i4")
+    g = to_device(synth.make_inputs(cfg), gpu)
+    p = _plan(cfg)
+    out = None
+    routing = None
+    if case == "w_down_swapped":
+        g["w_down"] = g["w_down"].transpose(1, 2).contiguous()      # [E, d, f] instead of [E, f, d]
+    elif case == "int4_unpacked":
+        g["w_gate_up"] = torch.zeros((cfg.E, cfg.d, 2 * cfg.f), dtype=torch.uint8, device=gpu)
+    elif case == "scale_shape":
+        g["s_down"] = g["s_down"][:, :-1].contiguous()
+    elif case == "scale_missing":
+        g["ss_down"] = None
+    elif case == "bias_missing":
+        g["router_bias"] = None
+    elif case == "out_shape":
+        out = torch.empty((cfg.T, cfg.d + 8), dtype=torch.float32, device=gpu)
+    elif case == "routing_short":
+        routing = moe.new_routing(p, cfg.T - 1, gpu)
+    with pytest.raises(ValueError):
+        moe.moe_forward(p, g["x"], g, out=out, routing=routing)
+
+
 def test_route_only_entry_point(gpu):
     from sparse_moe_transformer_llama4_amd import moe
     cfg = synth.get_config("small_bf16_bias")
@@ -249,6 +282,57 @@ def test_side_stream_matches_serial_schedule(gpu, name, T):
     check_forward(cfg, inp, out, routing)
 
 
+def _assign_groups(inp, sizes, lift=4.0):
+    """Route token t to a chosen expert: logits = x[:, :E] through an identity
+    router block, with x[t, e] = lift for the chosen e and 0 for the others
+    (margin = lift, gate = sigmoid(lift)).  Group sizes are exactly `sizes`."""
+    E = len(sizes)
+    T = inp["x"].shape[0]
+    assert sum(sizes) == T
+    assign = torch.repeat_interleave(torch.arange(E), torch.tensor(sizes))
+    assign = assign[torch.randperm(T, generator=torch.Generator().manual_seed(5))]
+    x = inp["x"].clone()
+    x[:, :E] = 0
+    x[torch.arange(T), assign] = lift
+    inp["x"] = x.to(inp["x"].dtype)
+    wr = torch.zeros_like(inp["w_router"])
+    wr[torch.arange(E), torch.arange(E)] = 1
+    inp["w_router"] = wr
+    return assign
+
+
+def test_side_stream_down_tails_wait_for_main_gateup(gpu):
+    # 256-row gate/up tiles with 128-row down tiles (2200 tokens over 8
+    # experts at d = 512): groups of 400, 150 and 386 rows end (n % 256 in
+    # 129..160) in a down tail whose h rows a main gate/up tile writes.  The
+    # side stream's tail down must wait for the main gate/up launch: compare
+    # the two-stream schedule bit for bit with the serial one on a poisoned
+    # workspace, several calls in a row, and the result with the oracle
+    from sparse_moe_transformer_llama4_amd import moe
+    cfg = synth.get_config("small_bf16_tall")
+    sizes = [400, 150, 386, 280, 260, 300, 224, 200]
+    inp = synth.make_inputs(cfg)
+    assign = _assign_groups(inp, sizes)
+    g = to_device(inp, gpu)
+    p = _plan(cfg)
+    ws = torch.empty(moe.moe_workspace_size(p, cfg.T), dtype=torch.uint8, device=gpu)
+    ev = moe.StageEvents()
+    ref = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device=gpu)
+    ws.fill_(0xFF)
+    moe.moe_forward_timed(p, g["x"], g, ev, out=ref, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        ws.fill_(0xFF)
+        out = torch.full_like(ref, float("nan"))
+        routing = moe.new_routing(p, cfg.T, gpu)
+        moe.moe_forward(p, g["x"], g, out=out, routing=routing, workspace=ws)
+        torch.cuda.synchronize()
+        assert routing["counts"].cpu().tolist() == sizes
+        assert torch.equal(out, ref), f"call {rep}: two-stream schedule differs from the serial one"
+    assert (routing["expert_idx"].cpu().long() == assign).all()
+    check_forward(cfg, inp, out, routing)
+
+
 GRAPH_CASES = [("small_fp32", {}), ("small_fp8", {}), ("decode_like_bf16", {}), ("small_bf16_tall", {}),
                ("decode_like_bf16", dict(w_dtype="i8", T=33)), ("decode_like_bf16", dict(w_dtype="i4", T=33)),
                ("decode_like_bf16", dict(top_k=2, T=33)), ("small_bf16_tall", dict(top_k=2)),
@@ -312,9 +396,8 @@ def test_dense_layer_matches_oracle(gpu, shape, T, out_dtype):
     out = moe.moe_forward(p, g["x"], g, workspace=ws)
     torch.cuda.synchronize()
     ref = block.dense(inp["x"], block.Weights.from_dict(inp), cfg.fs, cfg.w_dtype)
-    err = output_error(cfg, out, ref)
+    err = assert_output(cfg, out, ref, TOL["bf16"])
     print(f"[parity] dense T={T} max|err|/RMS = {err:.3e}", flush=True)
-    assert err <= TOL["bf16"]
     with pytest.raises(Exception):
         moe.moe_forward(p, g["x"], g, workspace=ws, routing=moe.new_routing(p, T, gpu))
 
@@ -352,8 +435,7 @@ def test_rmsnorm_block_matches_oracle(gpu, name, T, eps, over):
         out = moe.moe_forward(p, g["x"], g, workspace=ws)
         torch.cuda.synchronize()
         ref = block.dense(block_input(cfg, inp), block.Weights.from_dict(inp), cfg.fs, cfg.w_dtype)
-        err = output_error(cfg, out, ref)
-        assert err <= TOL[cfg.w_dtype], err
+        err = assert_output(cfg, out, ref)
     else:
         out, routing = run_gpu(p, g["x"], g)
         err, _ = check_forward(cfg, inp, out, routing)
