@@ -259,6 +259,26 @@ moe_status moe_forward_traced(moe_plan_t plan, const void* x, int64_t T, const m
                               hipStream_t stream, hipEvent_t* events, int32_t max_launches,
                               moe_launch_record* launches, int32_t* n_launches);
 
+/*
+ * moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same block, with no workspace argument.  Its scratch space is a device
+ * array of MOE_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; calls whose workspace (moe_workspace_size) exceeds it return
+ * MOE_ERR_WORKSPACE before anything is enqueued -- with d = 5120 and
+ * f = f_shared = 8192 that admits decode-sized calls (T <= 64).  The call
+ * runs every stage on `stream` alone (no side stream), in the stage order of
+ * moe_forward_timed, so its results equal moe_forward's bit for bit.  It calls
+ * no hipMalloc / hipFree; the first call on a device looks up that device's
+ * scratch address once (hipGetSymbolAddress).  Every call on one GPU shares
+ * that GPU's scratch array, which keeps the last call's contents (nothing
+ * relies on its initial contents): calls that overlap in time on one GPU
+ * (two streams, two threads, two plans) race.
+ */
+#define MOE_SCRATCH_BYTES (32u << 20)
+moe_status moe_forward_noalloc(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
+                               moe_routing* routing_out, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status s);
 

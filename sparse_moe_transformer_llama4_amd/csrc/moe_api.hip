@@ -755,7 +755,7 @@ moe_status moe_route(moe_plan_t plan, const void* x, int64_t T, const moe_weight
 
 static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
                                moe_routing* routing_out, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream, hipEvent_t* ev) {
+                               hipStream_t stream, hipEvent_t* ev, bool serial = false) {
   moe_status st = check_common(plan, x, T, w, workspace, workspace_bytes);
   if (st != MOE_OK) return st;
   const moe_config& c = plan->cfg;
@@ -803,10 +803,10 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   hipError_t e;
 
   // decode-sized and bf16 prefill calls use the plan's side stream (not the
-  // stage-timed variant, which keeps every stage on `stream`)
+  // stage-timed variant or a serial call, which keep every stage on `stream`)
   std::unique_lock<std::mutex> lock(plan->mu, std::defer_lock);
   const AuxStream* aux = nullptr;
-  if (!ev && T > 0 && (dec || v2)) {
+  if (!ev && !serial && T > 0 && (dec || v2)) {
     lock.lock();
     aux = aux_for(plan, stream, &e);
     if (e != hipSuccess) return hip_fail(plan, e);
@@ -927,6 +927,48 @@ moe_status moe_forward_timed(moe_plan_t plan, const void* x, int64_t T, const mo
                              hipStream_t stream, hipEvent_t* events) {
   if (!events) return MOE_ERR_INVALID_ARGUMENT;
   return forward_impl(plan, x, T, w, out, routing_out, workspace, workspace_bytes, stream, events);
+}
+
+}  // extern "C"
+
+// Device scratch of moe_forward_noalloc: one copy per GPU, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (in host
+// code the name is a host-side stand-in, not a device address): each
+// device's address comes from hipGetSymbolAddress once, with that device
+// current, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[MOE_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward_noalloc(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
+                               moe_routing* routing_out, hipStream_t stream) {
+  if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  if (T < 0 || T > plan->cfg.max_tokens) return MOE_ERR_SHAPE;
+  const size_t need = layout_for(plan->cfg, T).total;
+  if (need > MOE_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(plan, e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  void* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        g_scratch_ptr[dev] = nullptr;
+        return hip_fail(plan, e);
+      }
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  // serial schedule on `stream` alone: no side stream to create
+  return forward_impl(plan, x, T, w, out, routing_out, ptr, MOE_SCRATCH_BYTES, stream, nullptr, true);
 }
 
 moe_status moe_forward_traced(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,

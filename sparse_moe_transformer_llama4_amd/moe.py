@@ -23,7 +23,9 @@ _TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.u
 
 # names declared in include/moe.h
 symbols = ("moe_plan", "moe_plan_destroy", "moe_workspace_size", "moe_route", "moe_forward",
-           "moe_forward_timed", "moe_forward_traced", "moe_status_string", "moe_last_hip_error", "moe_version")
+           "moe_forward_timed", "moe_forward_traced", "moe_forward_noalloc", "moe_status_string",
+           "moe_last_hip_error", "moe_version")
+MOE_SCRATCH_BYTES = 32 << 20
 MOE_NUM_STAGES = 4
 MOE_MAX_LAUNCHES = 32
 STAGES = ("route", "gate_up", "down_shared", "down_routed")
@@ -92,6 +94,8 @@ def load_library(path: str = LIB_PATH):
                                        P, ctypes.POINTER(P), ctypes.c_int32, ctypes.POINTER(_LaunchRecord),
                                        ctypes.POINTER(ctypes.c_int32)]
     lib.moe_forward_traced.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [P, P, I64, ctypes.POINTER(_Weights), P, ctypes.POINTER(_Routing), P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_hip_error.argtypes = [P]
@@ -307,6 +311,24 @@ def moe_forward(plan: Plan, x: torch.Tensor, w: dict, out: Optional[torch.Tensor
                                     _stream(stream))
     if st != 0:
         raise plan._err(st, "moe_forward")
+    return out
+
+
+def moe_forward_noalloc(plan: Plan, x: torch.Tensor, w: dict, out: torch.Tensor,
+                        routing: Optional[dict] = None, stream=None) -> torch.Tensor:
+    """The whole block with the library's own device scratch instead of a
+    workspace (no allocation anywhere; the caller passes inputs and outputs).
+    Calls that overlap in time on one GPU share that scratch and race."""
+    _check_inputs(plan, x, w)
+    _check_weights(plan, w)
+    T = x.shape[0]
+    _check_shape(out, "out", _TORCH_DT[_DT[plan.out_dtype]], (T, plan.d))
+    _check_routing_buffers(plan, T, routing)
+    r = _routing(routing)
+    st = load_library().moe_forward_noalloc(plan.handle, _ptr(x), T, ctypes.byref(_weights(w)), _ptr(out),
+                                            ctypes.byref(r) if r is not None else None, _stream(stream))
+    if st != 0:
+        raise plan._err(st, "moe_forward_noalloc")
     return out
 
 
