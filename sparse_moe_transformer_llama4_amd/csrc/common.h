@@ -56,6 +56,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Two floats -> two OCP e4m3fn codes (low byte = a), round to nearest even,
+// with gfx950's conversion instruction (its fp8 format is OCP E4M3, bias 7,
+// largest finite 448).  Inputs are clamped to +-448 first, so values past
+// the largest finite code saturate to it instead of becoming NaN.  On every
+// float of magnitude below 448 + 256 ulps, and for both signs, the
+// instruction gives the codes that the format definition does (4
+// significant bits, subnormal quantum 2^-9, ties to even): an exhaustive
+// comparison against an integer implementation of that definition found no
+// difference.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  return e4m3x2(a, b) | (e4m3x2(c, d) << 16);
+}
+
+// fp64 -> fp32 rounded to odd (truncate, then set the last bit if inexact):
+// a later RNE to bf16 (8 significant bits <= 24 - 2) is then correctly
+// rounded from the fp64 value.
+__device__ __forceinline__ float f64_to_f32_odd(double y) {
+  const float f = __double2float_rz(y);
+  return static_cast<double>(f) == y ? f : __uint_as_float(__float_as_uint(f) | 1u);
+}
+
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
@@ -76,6 +102,7 @@ struct WsLayout {
   size_t r_out;                             // fp32 [T][d] routed output before the combine (bf16 prefill)
   size_t gu_part;                           // fp32 [parts][T][2 fs] gate/up partials (dense decode)
   size_t x_n;                               // x's rows after the RMSNorm (x dtype), when the block has one
+  size_t wr_pack;                           // W_router packed into MFMA B fragments (RMSNorm fused with the router)
   size_t xq, sx;                            // e4m3 x codes [T][d] and fp32 scales [T] (e4m3 only)
   size_t total;
 };

@@ -96,6 +96,18 @@ hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* s
 // (bf16 only) also xn's per-token e4m3 codes and scales.
 hipError_t launch_rmsnorm(int x_dtype, const void* x, const void* w, int T, int d, float eps, void* xn,
                           uint8_t* xq, float* sx, hipStream_t s);
+// The RMSNorm fused with the router GEMM (bf16 x, d a multiple of 128 up to
+// 5120, 1 <= E <= 256): packs W_router into wr_pack (norm_route_pack_bytes),
+// then writes xn (and, with xq / sx non-null, xn's e4m3 codes and per-token
+// scales) and the fp32 logits [T][E] without the bias.
+bool norm_route_supported(int x_dtype, int d, int E);
+size_t norm_route_pack_bytes(int d, int E);
+hipError_t launch_norm_route(const void* x, const void* w, int T, int d, int E, float eps, const void* wr,
+                             void* wr_pack, void* xn, uint8_t* xq, float* sx, float* logits, hipStream_t s);
+// T <= 64 with the logits [T][E] already computed: top-k, gate, counts,
+// offsets, tile tables and the permutation in one workgroup.
+hipError_t launch_route_small_finish(const RouterArgs& a, const float* logits, int32_t* counts, int32_t* offsets,
+                                     int32_t* tiles, int32_t* perm, hipStream_t s);
 hipError_t launch_quant_h(const float* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
                           float* sh, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);

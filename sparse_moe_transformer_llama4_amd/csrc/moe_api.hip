@@ -141,6 +141,12 @@ int dense_down_parts(const moe_config& c, int64_t T) {
   return static_cast<int>(ks);
 }
 
+// The RMSNorm runs inside the router kernel (one read of x for both) when
+// the block has a router and the fused kernel takes the shape.
+bool fused_norm_route(const moe_config& c) {
+  return c.has_norm && c.n_experts > 0 && norm_route_supported(c.x_dtype, c.d, c.n_experts);
+}
+
 WsLayout layout_for(const moe_config& c, int64_t T) {
   WsLayout L{};
   size_t off = 0;
@@ -171,6 +177,7 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   if (dense_gateup_parts(c, T) > 1)
     L.gu_part = take(static_cast<size_t>(dense_gateup_parts(c, T)) * t * 2 * c.f_shared * 4);
   if (c.has_norm) L.x_n = take(t * c.d * (c.x_dtype == MOE_F32 ? 4 : 2));
+  if (fused_norm_route(c)) L.wr_pack = take(norm_route_pack_bytes(c.d, c.n_experts));
   if (fp8) {
     L.hq_r = take(ts * c.f);
     L.hq_s = take(t * c.f_shared);
@@ -227,6 +234,7 @@ moe_status check_routing(const moe_routing* r) {
 struct Route {
   int32_t *idx, *counts, *offsets, *perm, *hist, *tiles;
   float *gate, *logits;
+  bool logits_ready;   // logits [T][E] (no bias) already written by the fused RMSNorm + router kernel
 };
 
 Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
@@ -239,6 +247,7 @@ Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
   o.hist = reinterpret_cast<int32_t*>(ws + L.hist);
   o.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   o.logits = reinterpret_cast<float*>(ws + L.logits);
+  o.logits_ready = false;
   return o;
 }
 
@@ -280,14 +289,20 @@ hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_we
   RouterArgs ra{x, w->w_router, c.has_router_bias ? w->router_bias : nullptr, T, c.d, c.n_experts,
                 R.idx, R.gate, R.hist, c.top_k};
   if (T > 0 && T <= kRouteTokens)
-    return TRACED("route_small", 0, -1, 0, s, launch_route_small(ra, c.x_dtype, R.logits, R.counts, R.offsets, R.tiles, R.perm, s));
+    return R.logits_ready
+               ? TRACED("route_small", 0, -1, 0, s,
+                        launch_route_small_finish(ra, R.logits, R.counts, R.offsets, R.tiles, R.perm, s))
+               : TRACED("route_small", 0, -1, 0, s,
+                        launch_route_small(ra, c.x_dtype, R.logits, R.counts, R.offsets, R.tiles, R.perm, s));
   // Prefill-sized bf16 calls with E a multiple of 64: the logits x·W_router
   // come from the pipelined bf16 GEMM (its fp32 [T][N] mode), then the
   // fixed-order finish; otherwise the dedicated router kernels.
   const bool gemm_router = c.x_dtype == MOE_BF16 && T >= kPrefillTokens && c.n_experts % 64 == 0 &&
                            bf16_v2_supported(c.d, c.n_experts, c.n_experts) &&
                            static_cast<int64_t>(T) * c.d * 2 < (int64_t{1} << 31);
-  if (T > 0 && gemm_router) {
+  if (T > 0 && R.logits_ready) {
+    if ((e = TRACED("router_finish", 0, -1, 0, s, launch_router_finish(ra, 1, R.logits, s))) != hipSuccess) return e;
+  } else if (T > 0 && gemm_router) {
     GemmArgs g{};
     g.A_shared = x;
     g.B_shared = w->w_router;
@@ -741,12 +756,19 @@ moe_status moe_route(moe_plan_t plan, const void* x, int64_t T, const moe_weight
   if ((st = check_routing(out)) != MOE_OK) return st;
   const WsLayout L = layout_for(plan->cfg, T);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const Route R = route_ptrs(ws, L, out);
+  Route R = route_ptrs(ws, L, out);
   hipError_t e = hipSuccess;
-  if (plan->cfg.has_norm) {
+  const moe_config& c = plan->cfg;
+  if (c.has_norm && fused_norm_route(c)) {
+    e = TRACED("norm_route", 0, -1, 0, stream,
+               launch_norm_route(x, w->norm_weight, static_cast<int>(T), c.d, c.n_experts, c.norm_eps, w->w_router,
+                                 ws + L.wr_pack, ws + L.x_n, nullptr, nullptr, R.logits, stream));
+    x = ws + L.x_n;
+    R.logits_ready = T > 0;
+  } else if (c.has_norm) {
     e = TRACED("rmsnorm", 0, -1, 0, stream,
-               launch_rmsnorm(plan->cfg.x_dtype, x, w->norm_weight, static_cast<int>(T), plan->cfg.d,
-                              plan->cfg.norm_eps, ws + L.x_n, nullptr, nullptr, stream));
+               launch_rmsnorm(c.x_dtype, x, w->norm_weight, static_cast<int>(T), c.d, c.norm_eps, ws + L.x_n,
+                              nullptr, nullptr, stream));
     x = ws + L.x_n;
   }
   if (e == hipSuccess) e = enqueue_route(plan->cfg, x, static_cast<int>(T), w, R, stream);
@@ -766,13 +788,16 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const WsLayout L = layout_for(c, T);
-  const Route R = route_ptrs(ws, L, routing_out);
+  Route R = route_ptrs(ws, L, routing_out);
   const int Ti = static_cast<int>(T);
   const bool fp8 = c.w_dtype == MOE_E4M3;
 
   // the RMSNorm runs first, inside the routing stage of the timed variant
   // (its events[0] is recorded here and the schedules below skip theirs);
-  // for e4m3 weights it also writes x's e4m3 codes and scales
+  // for e4m3 weights it also writes x's e4m3 codes and scales.  When the
+  // block has a router and the shape allows, the norm and the router GEMM
+  // are one kernel (x read once; the routing stage then starts from the
+  // logits)
   hipEvent_t evn[MOE_NUM_STAGES + 1];
   if (c.has_norm && T > 0) {
     if (ev) {
@@ -782,12 +807,18 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
       for (int i = 1; i <= MOE_NUM_STAGES; ++i) evn[i] = ev[i];
       ev = evn;
     }
+    uint8_t* xq = fp8 ? ws + L.xq : nullptr;
+    float* sx = fp8 ? reinterpret_cast<float*>(ws + L.sx) : nullptr;
     const hipError_t en =
-        TRACED("rmsnorm", 0, -1, 0, stream,
-               launch_rmsnorm(c.x_dtype, x, w->norm_weight, Ti, c.d, c.norm_eps, ws + L.x_n, fp8 ? ws + L.xq : nullptr,
-                              fp8 ? reinterpret_cast<float*>(ws + L.sx) : nullptr, stream));
+        fused_norm_route(c)
+            ? TRACED("norm_route", 0, -1, 0, stream,
+                     launch_norm_route(x, w->norm_weight, Ti, c.d, c.n_experts, c.norm_eps, w->w_router,
+                                       ws + L.wr_pack, ws + L.x_n, xq, sx, R.logits, stream))
+            : TRACED("rmsnorm", 0, -1, 0, stream,
+                     launch_rmsnorm(c.x_dtype, x, w->norm_weight, Ti, c.d, c.norm_eps, ws + L.x_n, xq, sx, stream));
     if (en != hipSuccess) return hip_fail(plan, en);
     x = ws + L.x_n;
+    R.logits_ready = fused_norm_route(c);
   }
   if (c.n_experts == 0) {
     const hipError_t e = enqueue_dense(c, x, Ti, w, out, ws, L, R, stream, ev);

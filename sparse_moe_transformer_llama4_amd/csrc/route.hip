@@ -18,24 +18,6 @@ namespace moe {
 
 // ---------------------------------------------------------------- e4m3
 
-// Two floats -> two OCP e4m3fn codes (low byte = a), round to nearest even,
-// with gfx950's conversion instruction (its fp8 format is OCP E4M3, bias 7,
-// largest finite 448).  Inputs are clamped to +-448 first, so values past
-// the largest finite code saturate to it instead of becoming NaN.  On every
-// float of magnitude below 448 + 256 ulps, and for both signs, the
-// instruction gives the codes that the format definition does (4
-// significant bits, subnormal quantum 2^-9, ties to even): an exhaustive
-// comparison against an integer implementation of that definition found no
-// difference.
-__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
-  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
-}
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  return e4m3x2(a, b) | (e4m3x2(c, d) << 16);
-}
-
 // ---------------------------------------------------------------- router
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short r_s16x4;
@@ -258,14 +240,6 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* x, int T, 
 // per-token e4m3 codes and scales (s = fp32 max|xn_t| / 448, code =
 // e4m3(xn / s) with an IEEE fp32 division), so the normalised rows are not
 // read back for the quantisation.  One wave per row.
-
-// fp64 -> fp32 rounded to odd (truncate, then set the last bit if inexact):
-// a later RNE to bf16 (8 significant bits <= 24 - 2) is then correctly
-// rounded from the fp64 value.
-__device__ __forceinline__ float f64_to_f32_odd(double y) {
-  const float f = __double2float_rz(y);
-  return static_cast<double>(f) == y ? f : __uint_as_float(__float_as_uint(f) | 1u);
-}
 
 template <int XDT, bool QUANT, int NCH>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void* w, int T, int d, float eps,
@@ -682,6 +656,12 @@ hipError_t launch_route_small(const RouterArgs& a, int x_dtype, float* part, int
   hipError_t e = launch_partials(a, x_dtype, part, ns, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(256), 0, s, a, ns, part, counts, offsets, tiles, perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_small_finish(const RouterArgs& a, const float* logits, int32_t* counts, int32_t* offsets,
+                                     int32_t* tiles, int32_t* perm, hipStream_t s) {
+  hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(256), 0, s, a, 1, logits, counts, offsets, tiles, perm);
   return hipGetLastError();
 }
 

@@ -404,7 +404,10 @@ def test_dense_layer_matches_oracle(gpu, shape, T, out_dtype):
 
 # ------------------------------------------------------------ RMSNorm in front of the block
 
-# rows longer than the norm kernel keeps in registers (8192 bf16 / 4096 fp32
+# bf16 blocks with a router and d a multiple of 128 up to 5120 take the norm
+# fused with the router GEMM (E = 8, 16, 20, 32 experts; decode and prefill
+# sizes); fp32 rows, dense layers and wider rows the stand-alone norm kernel,
+# whose rows longer than it keeps in registers (8192 bf16 / 4096 fp32
 # values) take its multi-pass path
 _LONG = dict(E=2, f=128, fs=128)
 NORM_CASES = [("small_bf16", None, 1e-5, {}), ("small_bf16", 65, 0.5, {}), ("small_fp32", None, 1e-5, {}),
@@ -412,6 +415,7 @@ NORM_CASES = [("small_bf16", None, 1e-5, {}), ("small_bf16", 65, 0.5, {}), ("sma
               ("decode_like_bf16", 33, 1e-5, {}), ("decode_like_bf16", 1, 1e-5, {}),
               ("small_bf16_tall", None, 1e-5, {}), ("small_dense_bf16", 33, 1e-5, {}),
               ("small_dense_bf16", 300, 1e-5, {}),
+              ("small_bf16", 300, 1e-5, dict(E=20)), ("small_bf16_split", None, 1e-5, {}),
               ("small_bf16", 40, 1e-5, dict(d=8704, **_LONG)), ("small_fp32", 20, 1e-5, dict(d=4160, **_LONG)),
               ("small_fp8", 40, 1e-5, dict(d=8320, **_LONG))]
 

@@ -96,3 +96,38 @@ def test_round_f64_to_is_a_single_rounding():
     w = np.random.default_rng(5).standard_normal(200_000).astype(np.float32)
     np.testing.assert_array_equal(numerics.round_f64_to(w.astype(np.float64), "bf16"),
                                   torch.from_numpy(w).to(torch.bfloat16).double().numpy())
+
+
+def test_e4m3_row_scale_from_bf16_rows_is_unstable():
+    """Why the per-token e4m3 quantisation of h takes its scale from the fp32
+    row (block.quant_rows_e4m3 on float32 values) and not from a bf16-rounded
+    copy: two computations of h that differ by 2^-16 relative in the row's
+    largest element (within what two correct fp32 GEMMs may differ by) must
+    give nearly the same codes.  With the row max sitting on a bf16 halfway
+    point, the bf16 copy moves the max by a whole bf16 ulp (2^-8), which
+    shifts every code's argument by that much and re-rounds about one code in
+    sixteen; from the fp32 row the scale moves by 2^-15 and only a handful of
+    codes change.  Uses the oracle only."""
+    from oracle import block
+    rng = np.random.default_rng(3)
+    n = 8192
+    h = (rng.standard_normal(n) * 0.25).astype(np.float32)
+    h = np.clip(h, -0.99, 0.99).astype(np.float32)
+    mid = np.float32(1.0 + 2.0 ** -8)                 # halfway between bf16 values 1 and 1 + 2^-7
+    lo, hi = h.copy(), h.copy()
+    lo[0] = np.float32(mid * (1 - 2.0 ** -16))
+    hi[0] = np.float32(mid * (1 + 2.0 ** -16))
+
+    def codes(rows):
+        q, s = block.quant_rows_e4m3(rows)
+        return q / s[:, None]
+
+    # from bf16-rounded rows
+    b_lo = numerics.bf16_round(lo).astype(np.float32)[None, :]
+    b_hi = numerics.bf16_round(hi).astype(np.float32)[None, :]
+    assert b_lo[0, 0] != b_hi[0, 0]                   # the max moved by a bf16 ulp
+    frac_bf16 = np.mean(codes(b_lo)[0, 1:] != codes(b_hi)[0, 1:])
+    # from the fp32 rows (the reading the oracle and the kernels use)
+    frac_f32 = np.mean(codes(lo[None, :])[0, 1:] != codes(hi[None, :])[0, 1:])
+    assert frac_bf16 > 0.03, frac_bf16
+    assert frac_f32 < 0.002, frac_f32
