@@ -58,7 +58,11 @@ def split_rows(n: int, bm: int, part: int) -> int:
     """Rows of a group of n rows that a launch covers: part 0 all of them;
     part 1 the main tiles (a last 1..32 rows past the group's full bm-row
     tiles are left to the tail tiles, so a group of at most 32 rows is all
-    tail); part 2 those tail rows alone."""
+    tail); part 2 those tail rows alone; part 3 all of them if the group's
+    size class is bm (1..32 rows: 32, 33..128: 128, more: 256), else none."""
+    if part == 3:
+        cls = 0 if n <= 0 else 32 if n <= 32 else 128 if n <= 128 else 256
+        return n if cls == bm else 0
     if part == 0 or not bm:
         return n
     r = n % bm
@@ -144,7 +148,7 @@ def launch_key(rec) -> str:
     """Stable name of a launch: kernel[routed|shared|both, all|main|tail, tile rows]."""
     name, side, bm, groups, part = rec[:5]
     g = {0: "routed", 1: "shared", 2: "routed+shared"}.get(groups)
-    p = {0: "", 1: ",main", 2: ",tail"}[part]
+    p = {0: "", 1: ",main", 2: ",tail", 3: ",class"}[part]
     inner = f"{g}{p},bm{bm}" if g else ""
     return f"{name}[{inner}]" if inner else name
 
@@ -399,7 +403,23 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (reference for rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE scaling) and exit")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR OUT [PATTERN]",
+                    help="condense a rocprofv3 --pmc CSV directory into one line per dispatch of the kernels whose "
+                         "name matches PATTERN (default: the library's) and exit")
+    ap.add_argument("--record-traffic", nargs=7,
+                    metavar=("KERNEL_KEY", "SYMBOL", "FETCH_SUMMARY", "WRITE_SUMMARY", "COPY_FETCH_SUMMARY",
+                             "COPY_WRITE_SUMMARY", "COPY_MIB"),
+                    help="store the HBM bytes per launch of --config's launch KERNEL_KEY (kernel symbol SYMBOL) "
+                         "from --pmc-summary files of FETCH_SIZE and WRITE_SIZE runs, scaled by a --calibrate-copy "
+                         "run's, in profiles/traffic.json, and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(f"{pmc_summary(*args.pmc_summary)} dispatches")
+        return
+    if args.record_traffic:
+        key, sym, fs, ws_, cfs, cws, mib = args.record_traffic
+        print(json.dumps(record_traffic(args.config, key, sym, fs, ws_, cfs, cws, int(mib) << 20)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the block is measured at one "
                                    "GPU's share with no collectives (how it would shard is design only); "
@@ -478,6 +498,70 @@ def main():
     result.update({k: v for k, v in res.items() if k not in ("value", "unit", "ms_per_step")})
     result["per_config"] = per_config
     print(json.dumps(result), flush=True)
+
+
+def pmc_summary(d: str, out: str, pattern: str = "moe::") -> int:
+    """Condense a rocprofv3 --pmc CSV output directory into one line per
+    dispatch of a kernel whose name matches `pattern` (a regular expression;
+    by default the library's kernels, not the input generator's):
+    'id|kernel|grid|counter=value,...' (per-dispatch values, summed over the
+    counter's instances)."""
+    import csv
+    import glob
+    import re
+    rx = re.compile(pattern)
+    rows = {}
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if not rx.search(r.get("Kernel_Name", "")):
+                    continue
+                key = (int(r.get("Dispatch_Id", 0) or 0), r.get("Kernel_Name", ""), r.get("Grid_Size", ""))
+                ent = rows.setdefault(key, {})
+                ent[r["Counter_Name"]] = ent.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    with open(out, "w") as fh:
+        for (did, name, grid), ent in sorted(rows.items()):
+            fh.write(f"{did}|{name}|{grid}|" + ",".join(f"{k}={v:.6g}" for k, v in sorted(ent.items())) + "\n")
+    return len(rows)
+
+
+def _read_pmc_summary(path: str):
+    out = []
+    for line in open(path):
+        did, name, grid, vals = line.rstrip("\n").split("|", 3)
+        out.append((int(did), name, grid, {k: float(v) for k, v in (kv.split("=") for kv in vals.split(",") if kv)}))
+    return out
+
+
+def record_traffic(workload: str, kernel: str, symbol: str, fetch_sum: str, write_sum: str, copy_fetch_sum: str,
+                   copy_write_sum: str, copy_bytes: int) -> dict:
+    """HBM bytes per launch of one kernel from two counter runs (FETCH_SIZE,
+    then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+    reads for a device-to-device copy of copy_bytes (its dispatches are the
+    ones whose name mentions 'copy' or 'elementwise'); stored in
+    profiles/traffic.json under the workload and the launch's key, with the
+    library source hash it is valid for."""
+    def per_dispatch(path, counter, match):
+        v = [c[counter] for _, name, _, c in _read_pmc_summary(path) if match(name) and counter in c]
+        if not v:
+            raise SystemExit(f"no dispatch of {symbol if match is not copy_match else 'the copy'} with {counter} in {path}")
+        return sum(v) / len(v), len(v)
+    copy_match = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
+    kmatch = lambda n: symbol in n
+    cf, _ = per_dispatch(copy_fetch_sum, "FETCH_SIZE", copy_match)
+    cw, _ = per_dispatch(copy_write_sum, "WRITE_SIZE", copy_match)
+    kf, nf = per_dispatch(fetch_sum, "FETCH_SIZE", kmatch)
+    kw, nw = per_dispatch(write_sum, "WRITE_SIZE", kmatch)
+    sf, sw = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    ent = {"bytes": (kf * sf + kw * sw) * 1024.0, "fetch_bytes": kf * sf * 1024.0, "write_bytes": kw * sw * 1024.0,
+           "source_hash": _kernel_source_hash(),
+           "note": f"{symbol}: FETCH_SIZE x {sf:.3f} ({nf} dispatches) + WRITE_SIZE x {sw:.3f} ({nw}), factors from a "
+                   f"{copy_bytes >> 20} MiB device-to-device copy"}
+    data = json.load(open(PROFILE_TRAFFIC)) if os.path.exists(PROFILE_TRAFFIC) else {}
+    data.setdefault(workload, {})[kernel] = ent
+    with open(PROFILE_TRAFFIC, "w") as fh:
+        json.dump(data, fh, indent=1)
+    return ent
 
 
 def sample_clock_mhz(run, seconds=0.5):

@@ -252,7 +252,8 @@ typedef struct moe_launch_record {
   int32_t tile_rows;   /* rows per tile of a GEMM launch (0 otherwise) */
   int32_t groups;      /* GEMMs and quant_h: 0 routed groups, 1 shared expert, 2 both; -1 otherwise */
   int32_t part;        /* routed GEMMs: 0 all rows; 1 the main tiles (a group's last 1..32 rows past its last
-                          full tile_rows tile are left out); 2 those last rows alone */
+                          full tile_rows tile are left out); 2 those last rows alone; 3 the groups whose size
+                          class is tile_rows (1..32 rows: 32, 33..128: 128, more: 256), whole */
 } moe_launch_record;
 moe_status moe_forward_traced(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
                               moe_routing* routing_out, void* workspace, size_t workspace_bytes,

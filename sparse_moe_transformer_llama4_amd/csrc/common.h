@@ -27,11 +27,24 @@ __host__ __device__ constexpr int bm_index(int bm) {
 //                   bm * floor(n / bm) .. n - 1; no shared group).
 // A group of 1..kTailRows tokens is all tail.  Tails are weight streams: they
 // take the 32-row weight-streaming tiles while the MFMA tiles do the rest.
+//   table_class(bm): every routed group in one tile height chosen by its size
+//                   (class_tiles below), so that each group's weights are
+//                   streamed by one set of tiles: groups of 1..kTailRows rows
+//                   in the kTailRows table (weight-streaming tiles, row 0),
+//                   kTailRows+1..128 rows in the 128 table (one tile),
+//                   larger groups in the 256 table; no shared group.
 constexpr int kTailRows = 32;
-constexpr int kNumTables = 3 * kNumBM;
+constexpr int kNumTables = 4 * kNumBM;
 __host__ __device__ constexpr int table_all(int bm) { return bm_index(bm); }
 __host__ __device__ constexpr int table_main(int bm) { return kNumBM + bm_index(bm); }
 __host__ __device__ constexpr int table_tail(int bm) { return 2 * kNumBM + bm_index(bm); }
+__host__ __device__ constexpr int table_class(int bm) { return 3 * kNumBM + bm_index(bm); }
+__host__ __device__ constexpr int class_tiles(int n, int bm) {
+  return n <= 0 ? 0
+         : n <= kTailRows ? (bm == kTailRows ? 1 : 0)
+         : n <= 128       ? (bm == 128 ? 1 : 0)
+                          : (bm == 256 ? (n + 255) / 256 : 0);
+}
 
 // Tokens handled by one router workgroup (4 waves x 16 tokens).
 constexpr int kRouteTokens = 64;

@@ -957,8 +957,9 @@ hipError_t launch_gemm_decode_tail(int mode, const GemmArgs& a0, int bm_main, hi
                                    const int32_t* tiles_all) {
   static_assert(kTailRows == 32, "tails are single 32-row tiles");
   GemmArgs a = a0;
-  a.tiles = tiles_all + table_tail(bm_main) * (a.E + 2);
-  a.tail_bm = bm_main;
+  // bm_main == 0: the groups of at most kTailRows rows (class table), whole
+  a.tiles = tiles_all + (bm_main > 0 ? table_tail(bm_main) : table_class(kTailRows)) * (a.E + 2);
+  a.tail_bm = bm_main > 0 ? bm_main : (1 << 30);
   a.group_lo = 0;
   a.group_hi = a.E;
   // one tail tile per group at most.  Grid (column tile, row tile), column

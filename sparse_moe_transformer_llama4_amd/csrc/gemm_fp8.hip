@@ -470,6 +470,411 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------- 256 x 256 tiles
+//
+// The same three GEMMs on 256 x 256 workgroup tiles, for MFMA-bound work (the
+// shared expert's gate/up and down GEMMs): each of the 4 waves owns a
+// 128 x 128 accumulator block of 16 v_mfma_scale_f32_32x32x64_f8f6f4
+// fragments (256 AGPRs), which reads 2/3 of the LDS bytes per FLOP that the
+// 64 x 128 (or 80 x 128) blocks of the tiles above read, and half the L2
+// bytes.  K = 64 bytes per stage (16 KB of A + 16 KB of weights) in a 5-deep
+// ring, the whole LDS: four stages (~2 us of MFMA work) in flight, for
+// operands that come from the last-level cache rather than L2.
+//   * A rows (64 B): 16-byte chunk c of row r at c ^ ((r >> 1) & 3) ^
+//     ((r >> 4) & 1); a lane's operand is 32 K bytes of one row (two
+//     ds_read_b128).  The bf16 tiles' c ^ ((r >> 1) & 3) left a 2-way bank
+//     conflict here (lanes 0-31 read 32 rows at one chunk, where the bf16
+//     fragment reads 16 rows at two chunks): SQ_LDS_BANK_CONFLICT measured
+//     29-31 % of the LDS-active cycles with it, 0 with the extra term;
+//   * weight rows (256 B): chunk c of row r at c ^ (2 (r & 7)).  A byte
+//     transpose read serves two 16-lane groups that read the same 8 K rows
+//     at the adjacent column chunks 2m and 2m + 1; with this swizzle the
+//     first lands on chunks {2m ^ even} and the second on {2m + 1 ^ even},
+//     disjoint halves of the banks;
+//   * 32 x 32 accumulator layout: lane l holds column l % 32 of rows
+//     8 (i / 4) + 4 (l / 32) + i % 4, i = 0..15.
+__device__ __forceinline__ int tall_a_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 4) & 1); }
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(GemmArgs p) {
+  typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+  constexpr int BM = 256;
+  constexpr bool GATEUP = MODE == MODE_GATEUP;
+  constexpr int BNH = GATEUP ? BN / 2 : BN;
+  constexpr int TK = 64;                         // K bytes per stage
+  constexpr int TNBUF = 5;
+  constexpr int TA_ROWB = TK;
+  constexpr int TA_STAGE = BM * TA_ROWB;         // 16 KB
+  constexpr int TB_STAGE = TK * BN;              // 16 KB
+  constexpr int TA_INS = TA_STAGE / 1024 / 4;    // 1 KB DMA instructions per wave per stage
+  constexpr int TB_INS = TB_STAGE / 1024 / 4;
+  constexpr int TLOADS = TA_INS + TB_INS;
+  constexpr int FM = 4, FN = 4;                  // 32 x 32 fragments per wave
+  static_assert(TNBUF * (TA_STAGE + TB_STAGE) <= 160 * 1024, "ring fits the LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[TNBUF * (TA_STAGE + TB_STAGE)];
+  lds_u8* const As = (lds_u8*)(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int E = p.E, T = p.T, K = p.K;
+
+  // ---- XCD-aware tile lookup (as in the tiles above)
+  const int nmt = (MODE == MODE_DOWN_SHARED) ? (T + BM - 1) / BM : p.tiles[p.group_hi] - p.tiles[p.group_lo];
+  const int gn = p.n_tiles;
+  const int lid = blockIdx.x;
+  int mt_rel, nt;
+  if (gn >= 8 && gn % 8 != 0 && gn % 4 == 0) {
+    const int x = lid & 7, local = lid >> 3;
+    const int w = gn >> 2, m_lo = ((x >> 2) * nmt) >> 1, m_hi = (((x >> 2) + 1) * nmt) >> 1;
+    if (local >= (m_hi - m_lo) * w) return;
+    mt_rel = m_lo + local / w;
+    nt = (x & 3) * w + (local - (local / w) * w);
+  } else if (gn >= 8) {
+    const int x = lid & 7, local = lid >> 3;
+    const int nt_lo = (x * gn) >> 3, w = (((x + 1) * gn) >> 3) - nt_lo;
+    if (local >= nmt * w) return;
+    mt_rel = local / w;
+    nt = nt_lo + (local - mt_rel * w);
+  } else {
+    if (lid >= nmt * gn) return;
+    mt_rel = lid / gn;
+    nt = lid - mt_rel * gn;
+  }
+  int g, m0, rows;
+  if constexpr (MODE == MODE_DOWN_SHARED) {
+    g = 0;
+    m0 = mt_rel * BM;
+    rows = T;
+  } else {
+    const int mt = mt_rel + p.tiles[p.group_lo];
+    int lo = p.group_lo, hi = p.group_hi - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    m0 = (mt - p.tiles[g]) * BM;
+    rows = (g == E) ? T : p.offsets[g + 1] - p.offsets[g];
+  }
+  const bool shared = (MODE == MODE_DOWN_SHARED) || (GATEUP && g == E);
+  const int NH = (GATEUP && shared) ? p.N_shared : p.N;
+  const int n0 = nt * BNH;
+  if (n0 >= NH) return;
+  const int row_base = shared ? 0 : p.offsets[g];
+  const int ldb = GATEUP ? 2 * NH : NH;
+
+  // per-row metadata for the epilogue, one tile row per thread
+  float row_scale = 1.0f;
+  int row_out = 0;
+  {
+    const int r = min(m0 + tid, rows - 1);
+    if constexpr (GATEUP) {
+      const int slot = shared ? r : p.perm[row_base + r];
+      row_scale = (shared ? 1.0f : p.gate[slot]) * (shared ? p.sA_shared : p.sA)[shared ? slot : slot_token(slot, p.top_k)];
+    } else if constexpr (MODE == MODE_DOWN_SHARED) {
+      row_scale = p.sA_shared[r];
+    } else {
+      row_scale = p.sA[row_base + r];
+      row_out = p.perm[row_base + r];
+    }
+  }
+
+  // ---- DMA sources.  A: instruction i of wave w fills tile rows
+  // 16 (w TA_INS + i) + lane / 4, the lane fetching the chunk its slot holds.
+  const uint8_t* a_src;
+  if constexpr (GATEUP) a_src = reinterpret_cast<const uint8_t*>(shared ? p.A_shared : p.A);
+  else if constexpr (MODE == MODE_DOWN_SHARED) a_src = reinterpret_cast<const uint8_t*>(p.A_shared);
+  else a_src = reinterpret_cast<const uint8_t*>(p.A);
+  uint32_t a_voff[TA_INS];   // (the caller guarantees T * K < 2^31)
+#pragma unroll
+  for (int i = 0; i < TA_INS; ++i) {
+    const int tr = 16 * (wave * TA_INS + i) + (lane >> 2);
+    const int c = (lane & 3) ^ tall_a_swz(tr);
+    const int r = min(m0 + tr, rows - 1);
+    int arow;
+    if constexpr (GATEUP) arow = shared ? r : slot_token(p.perm[row_base + r], p.top_k);
+    else if constexpr (MODE == MODE_DOWN_SHARED) arow = r;
+    else arow = row_base + r;
+    a_voff[i] = static_cast<uint32_t>(arow) * static_cast<uint32_t>(K) + c * 16;
+  }
+  // weights: instruction i of wave w fills K rows 4 (w TB_INS + i) + lane / 16
+  const uint8_t* b_src = reinterpret_cast<const uint8_t*>(shared ? p.B_shared : p.B) +
+                         (shared ? 0 : static_cast<int64_t>(g) * K * ldb);
+  uint32_t b_voff[TB_INS];
+#pragma unroll
+  for (int i = 0; i < TB_INS; ++i) {
+    const int kr = 4 * (wave * TB_INS + i) + (lane >> 4);
+    const int c = (lane & 15) ^ (2 * (kr & 7));
+    const int lc = c * 16;
+    int gc;
+    if constexpr (GATEUP) gc = lc < BNH ? n0 + lc : NH + n0 + (lc - BNH);
+    else gc = n0 + lc;
+    const bool ok = n0 + (GATEUP ? lc % BNH : lc) < NH;
+    b_voff[i] = static_cast<uint32_t>(kr * ldb + (ok ? gc : 0));   // clamped columns are never stored
+  }
+  const int64_t b_kstep = static_cast<int64_t>(TK) * ldb;
+  const int nk = K / TK;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // ---- LDS read addresses
+  const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(As));
+  const int l32 = lane & 31, kh = lane >> 5;
+  // A fragment i of slot sl: row wm 128 + 32 i + l32, logical chunks 2 kh and
+  // 2 kh + 1 (the row's (r >> 1) & 3 equals (l32 >> 1) & 3)
+  const int aswz = tall_a_swz(l32);   // (bits 0..4 of the row: the fragment base is a multiple of 32)
+  const uint32_t a_rd0 = ring + (wm * 128 + l32) * TA_ROWB + (((2 * kh) ^ aswz) << 4);
+  const uint32_t a_rd1 = ring + (wm * 128 + l32) * TA_ROWB + (((2 * kh + 1) ^ aswz) << 4);
+  // weight fragment j: 32 columns; lane group gg = lane / 16 reads the 16
+  // columns 16 (gg & 1) of it at K rows 32 (gg >> 1) + 8 q + s / 2, bytes
+  // 8 (s & 1) of the chunk, s = lane % 16; four reads (q) give 32 K bytes
+  uint32_t b_rd[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int gg = lane >> 4, s = lane & 15;
+    int col;
+    if constexpr (GATEUP) col = (j < FN / 2 ? 0 : BNH) + wn * (BNH / 2) + (j % (FN / 2)) * 32 + 16 * (gg & 1);
+    else col = wn * (BN / 2) + j * 32 + 16 * (gg & 1);
+    const int kr = 32 * (gg >> 1) + (s >> 1);
+    b_rd[j] = ring + TNBUF * TA_STAGE + kr * BN + (((col >> 4) ^ (2 * (kr & 7))) << 4) + 8 * (s & 1);
+  }
+  typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+#define T8_AREAD(FA, i, SL)                                                                    \
+  do {                                                                                         \
+    const i32x4 lo_ = *(const lds_i32x4*)((const lds_u8*)(uintptr_t)a_rd0 + (SL) * TA_STAGE + (i) * 32 * TA_ROWB); \
+    const i32x4 hi_ = *(const lds_i32x4*)((const lds_u8*)(uintptr_t)a_rd1 + (SL) * TA_STAGE + (i) * 32 * TA_ROWB); \
+    FA[i] = i32x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};             \
+  } while (0)
+#define T8_BREAD(FB, j, SL)                                                                    \
+  do {                                                                                         \
+    const lds_u8* q_ = (const lds_u8*)(uintptr_t)b_rd[j] + (SL) * TB_STAGE;                    \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                            \
+      const i32x2 v_ = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(q_ + 8 * q * BN));  \
+      FB[j][2 * q] = v_[0];                                                                    \
+      FB[j][2 * q + 1] = v_[1];                                                                \
+    }                                                                                          \
+  } while (0)
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t a_lds0 = ring + wave_u * (TA_INS * 1024);
+  const uint32_t b_lds0 = ring + TNBUF * TA_STAGE + wave_u * (TB_INS * 1024);
+#define T8_DMA_A(i, st, SL)                                                                    \
+  dma16(a_src + static_cast<int64_t>(min((st), nk - 1)) * TK, a_voff[i], a_lds0 + (SL) * TA_STAGE + (i) * 1024)
+#define T8_DMA_B(i, st, SL)                                                                    \
+  dma16(b_src + static_cast<int64_t>(min((st), nk - 1)) * b_kstep, b_voff[i], b_lds0 + (SL) * TB_STAGE + (i) * 1024)
+
+  i32x8 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
+  constexpr int NMF = FM * FN;
+  constexpr int NOPS = FM + FN + TA_INS + TB_INS;
+#define T8_STEP(R, FA, FB, FA2, FB2)                                                           \
+  do {                                                                                         \
+    constexpr int sl_ = (R) % TNBUF, nsl_ = ((R) + 1) % TNBUF;                                 \
+    const int sd_ = kt + (R) + TNBUF;                                                          \
+    _Pragma("unroll") for (int m_ = 0; m_ < NMF; ++m_) {                                       \
+      acc[m_ / FN][m_ % FN] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
+          FA[m_ / FN], FB[m_ % FN], acc[m_ / FN][m_ % FN], 0, 0, 0, 127, 0, 127);              \
+      _Pragma("unroll") for (int o_ = 0; o_ < NOPS; ++o_) {                                    \
+        if (o_ * NMF / NOPS == m_) {                                                           \
+          if (o_ < FM) T8_AREAD(FA2, o_, nsl_);                                                \
+          else if (o_ < FM + FN) T8_BREAD(FB2, o_ - FM, nsl_);                                 \
+          else if (o_ < FM + FN + TA_INS) T8_DMA_A(o_ - FM - FN, sd_, sl_);                    \
+          else T8_DMA_B(o_ - FM - FN - TA_INS, sd_, sl_);                                      \
+        }                                                                                      \
+      }                                                                                        \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+    }                                                                                          \
+    wait_vmcnt<(TNBUF - 2) * TLOADS>();                                                        \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                                       \
+    __builtin_amdgcn_s_barrier();                                                              \
+  } while (0)
+
+  // prologue: stages 0 .. TNBUF-1 in flight; 0 and 1 landed and published;
+  // stage 0's fragments in registers and its slot released
+#pragma unroll
+  for (int st = 0; st < TNBUF; ++st) {
+#pragma unroll
+    for (int i = 0; i < TA_INS; ++i) T8_DMA_A(i, st, st);
+#pragma unroll
+    for (int i = 0; i < TB_INS; ++i) T8_DMA_B(i, st, st);
+  }
+  wait_vmcnt<(TNBUF - 2) * TLOADS>();
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int i = 0; i < FM; ++i) T8_AREAD(fa0, i, 0);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) T8_BREAD(fb0, j, 0);
+  __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */
+  __builtin_amdgcn_s_barrier();
+  // unrolled by 10 = ring depth x register parity (slots and buffers
+  // compile-time); accumulators pinned to AGPRs at each iteration
+#define T8_STEPR(R)                                                                            \
+  do {                                                                                         \
+    if constexpr ((R) % 2 == 0) T8_STEP((R), fa0, fb0, fa1, fb1);                              \
+    else T8_STEP((R), fa1, fb1, fa0, fb0);                                                     \
+  } while (0)
+  int kt = 0;
+  for (; kt + 10 <= nk; kt += 10) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+    T8_STEPR(0); T8_STEPR(1); T8_STEPR(2); T8_STEPR(3); T8_STEPR(4);
+    T8_STEPR(5); T8_STEPR(6); T8_STEPR(7); T8_STEPR(8); T8_STEPR(9);
+  }
+  const int left = nk - kt;   // 0 .. 9
+  if (left > 0) { T8_STEPR(0);
+  if (left > 1) { T8_STEPR(1);
+  if (left > 2) { T8_STEPR(2);
+  if (left > 3) { T8_STEPR(3);
+  if (left > 4) { T8_STEPR(4);
+  if (left > 5) { T8_STEPR(5);
+  if (left > 6) { T8_STEPR(6);
+  if (left > 7) { T8_STEPR(7);
+  if (left > 8) { T8_STEPR(8); } } } } } } } } }
+  wait_vmcnt<0>();
+#undef T8_STEPR
+#undef T8_AREAD
+#undef T8_BREAD
+#undef T8_DMA_A
+#undef T8_DMA_B
+#undef T8_STEP
+
+  // ---- epilogue.  Column scales first, the row tables through LDS, then the
+  // tile through LDS so that global memory sees 16-byte row chunks.
+  const int lcol = lane & 31;
+  float csc[FN];
+  {
+    const float* sB = GATEUP ? (shared ? p.sB_shared : p.sB + static_cast<int64_t>(g) * 2 * NH)
+                             : (MODE == MODE_DOWN_ROUTED ? p.sB + static_cast<int64_t>(g) * NH : p.sB_shared);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int jj = GATEUP ? j % (FN / 2) : j;
+      const int col = n0 + wn * (BNH / 2) + jj * 32 + lcol;
+      csc[j] = col < NH ? sB[(GATEUP && j >= FN / 2 ? NH : 0) + col] : 0.0f;
+    }
+  }
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  typedef __attribute__((address_space(3))) float lds_f32;
+  typedef __attribute__((address_space(3))) int lds_i32;
+  __syncthreads();
+  reinterpret_cast<lds_f32*>(As)[tid] = row_scale;
+  reinterpret_cast<lds_i32*>(As)[BM + tid] = row_out;
+  __syncthreads();
+  constexpr int TABB = 8 * BM;            // the two row tables
+  lds_u8* const stage = As + TABB;
+  // tile row of accumulator element e of fragment row i: wm 128 + 32 i +
+  // 8 (e / 4) + 4 kh + e % 4
+  const int wrow = wm * 128 + 4 * kh;
+  if constexpr (GATEUP) {
+    // h tile [256][128] fp32 (row pitch HP), then 16-byte chunks with the
+    // per-row max |h| reduced over the 32 lanes that share a row
+    constexpr int HP = BNH * 4 + 16;
+    static_assert(TABB + BM * HP <= TNBUF * (TA_STAGE + TB_STAGE), "h staging fits the ring");
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int rt0 = wrow + 32 * i + 8 * b;
+        const f32x4 sc = *(const lds_f32x4*)(As + 4 * rt0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int j = 0; j < FN / 2; ++j) {
+            const float gv = acc[i][j][4 * b + q] * sc[q] * csc[j];
+            const float uv = acc[i][j + FN / 2][4 * b + q] * sc[q] * csc[j + FN / 2];
+            *(lds_f32*)(stage + (rt0 + q) * HP + (wn * (BNH / 2) + j * 32 + lcol) * 4) = silu_f(gv) * uv;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CPR = BNH / 4;          // 32 chunks per row
+    float* C = reinterpret_cast<float*>(shared ? p.C_shared : p.C);
+    uint32_t* amax = shared ? p.amax_shared : p.amax;
+    for (int k = tid; k < BM * CPR; k += 256) {
+      const int r = k / CPR, cc = k - r * CPR;
+      const int col = n0 + cc * 4;
+      const bool ok = m0 + r < rows && col < NH;
+      const f32x4 v = *(const lds_f32x4*)(stage + r * HP + cc * 16);
+      float m = ok ? fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))) : 0.f;
+#pragma unroll
+      for (int sh = 1; sh < 32; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
+      if (ok) *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row_base + m0 + r) * NH + col) = v;
+      if (cc == 0 && m0 + r < rows) atomicMax(&amax[row_base + m0 + r], __float_as_uint(m));
+    }
+  } else {
+    // scaled fp32 tile in two passes of 128 rows (one per wave row), then
+    // 16-byte chunks: shared down stores them; routed down adds the shared
+    // expert's output, loaded for NB chunks at a time before they are stored
+    constexpr int FPB = BN * 4 + 16;
+    constexpr int PR = BM / 2;
+    static_assert(TABB + PR * FPB <= TNBUF * (TA_STAGE + TB_STAGE), "fp32 staging fits the ring");
+    constexpr int CPR = BN / 4;
+    constexpr int NB = 16;
+    static_assert((PR * CPR) % (256 * NB) == 0, "whole batches");
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass > 0) __syncthreads();      // the previous pass's chunks are read
+      if (wm == pass) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int rt0 = wrow + 32 * i + 8 * b;
+            const f32x4 sc = *(const lds_f32x4*)(As + 4 * rt0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int rp = rt0 + q - pass * PR;
+#pragma unroll
+              for (int j = 0; j < FN; ++j)
+                *(lds_f32*)(stage + rp * FPB + (wn * (BN / 2) + j * 32 + lcol) * 4) = acc[i][j][4 * b + q] * sc[q] * csc[j];
+            }
+          }
+        }
+      }
+      __syncthreads();
+      for (int k0 = tid; k0 < PR * CPR; k0 += 256 * NB) {
+        f32x4 y[NB];
+        int orow[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int k = k0 + u * 256;
+          const int r = k / CPR, cc = k - r * CPR;
+          const int rt = pass * PR + r;
+          if constexpr (MODE == MODE_DOWN_ROUTED) orow[u] = reinterpret_cast<const lds_i32*>(As)[BM + rt];
+          else orow[u] = m0 + rt;
+          y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (MODE == MODE_DOWN_ROUTED)
+            if (p.Y && m0 + rt < rows && n0 + cc * 4 < NH)
+              y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int k = k0 + u * 256;
+          const int r = k / CPR, cc = k - r * CPR;
+          if (m0 + pass * PR + r >= rows || n0 + cc * 4 >= NH) continue;
+          const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
+          const int64_t o = static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4;
+          if constexpr (MODE == MODE_DOWN_SHARED) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + o) = v;
+          } else if (p.out_bf16) {
+            const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+            const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + o) = v;
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int MODE, int BM>
 hipError_t launch_f8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* tiles_all) {
   GemmArgs a = a0;
@@ -491,13 +896,24 @@ hipError_t launch_f8(const GemmArgs& a0, int T, hipStream_t s, const int32_t* ti
   const int64_t nblk = (gn >= 8 && gn % 8 != 0 && gn % 4 == 0) ? 8 * static_cast<int64_t>((gm + 1) / 2) * (gn / 4)
                        : gn >= 8 ? 8 * static_cast<int64_t>(gm) * ((gn + 7) / 8)
                                  : static_cast<int64_t>(gm) * gn;
-  hipLaunchKernelGGL((gemm_fp8_kernel<MODE, BM>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, a);
+  if constexpr (BM == 256)
+    hipLaunchKernelGGL((gemm_fp8_tall_kernel<MODE>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_fp8_kernel<MODE, BM>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_fp8(int mode, int bm, const GemmArgs& a, int T, hipStream_t s, const int32_t* tiles_all) {
+  if (bm == 256) {
+    switch (mode) {
+      case MODE_GATEUP: return launch_f8<MODE_GATEUP, 256>(a, T, s, tiles_all);
+      case MODE_DOWN_SHARED: return launch_f8<MODE_DOWN_SHARED, 256>(a, T, s, tiles_all);
+      case MODE_DOWN_ROUTED: return launch_f8<MODE_DOWN_ROUTED, 256>(a, T, s, tiles_all);
+    }
+    return hipErrorInvalidValue;
+  }
   if (bm == 160 && mode == MODE_GATEUP) return launch_f8<MODE_GATEUP, 160>(a, T, s, tiles_all);
   if (bm == 160 && mode == MODE_DOWN_ROUTED) return launch_f8<MODE_DOWN_ROUTED, 160>(a, T, s, tiles_all);
   if (bm != 128) return hipErrorInvalidValue;

@@ -97,9 +97,11 @@ hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* s
 hipError_t launch_rmsnorm(int x_dtype, const void* x, const void* w, int T, int d, float eps, void* xn,
                           uint8_t* xq, float* sx, hipStream_t s);
 // The RMSNorm fused with the router GEMM (bf16 x, d a multiple of 128 up to
-// 5120, 1 <= E <= 256): packs W_router into wr_pack (norm_route_pack_bytes),
+// 5120, 1 <= E <= 128): packs W_router into wr_pack (norm_route_pack_bytes),
 // then writes xn (and, with xq / sx non-null, xn's e4m3 codes and per-token
-// scales) and the fp32 logits [T][E] without the bias.
+// scales) and the fp32 logits [T][E] without the bias.  With w == nullptr
+// there is no norm: x's own e4m3 codes and scales (xq, sx required) and its
+// logits, xn unused.
 bool norm_route_supported(int x_dtype, int d, int E);
 size_t norm_route_pack_bytes(int d, int E);
 hipError_t launch_norm_route(const void* x, const void* w, int T, int d, int E, float eps, const void* wr,
@@ -152,6 +154,7 @@ hipError_t launch_gemm_decode(int mode, bool rows32, const GemmArgs& a, int T, h
 // full bm_main-row tiles) on the weight-streaming tiles: MODE_GATEUP (SwiGLU
 // epilogue) or MODE_DOWN_ROUTED (un-permute + combine with the y_parts shared
 // partials).  The rest is left to launches over table_main(bm_main).
+// bm_main == 0 takes the groups of at most 32 rows whole (table_class(32)).
 hipError_t launch_gemm_decode_tail(int mode, const GemmArgs& a, int bm_main, hipStream_t s,
                                    const int32_t* tiles_all);
 

@@ -142,9 +142,16 @@ int dense_down_parts(const moe_config& c, int64_t T) {
 }
 
 // The RMSNorm runs inside the router kernel (one read of x for both) when
-// the block has a router and the fused kernel takes the shape.
+// the block has a router of at most 32 experts and the fused kernel takes the
+// shape; with e4m3 weights and no norm the same kernel quantises x while it
+// computes the logits (again one read of x).  Every 16 rows of the fused
+// kernel read the whole router weight from L2: at 128 experts (1.3 MB at
+// d = 5120) that traffic made it slower than the stand-alone norm and router
+// GEMM (measured on the Maverick-shaped fp8 layer: 0.43 against 0.18 ms with
+// the norm, 0.18 against 0.13 ms without).
 bool fused_norm_route(const moe_config& c) {
-  return c.has_norm && c.n_experts > 0 && norm_route_supported(c.x_dtype, c.d, c.n_experts);
+  return (c.has_norm || c.w_dtype == MOE_E4M3) && c.n_experts > 0 && c.n_experts <= 32 &&
+         norm_route_supported(c.x_dtype, c.d, c.n_experts);
 }
 
 WsLayout layout_for(const moe_config& c, int64_t T) {
@@ -492,6 +499,87 @@ hipError_t enqueue_decode_overlapped(const moe_config& c, const void* x, int T, 
   return finish_topk(c, ws, L, T, ys, out, stream);
 }
 
+// bf16 prefill over the class tables (see enqueue_bf16_prefill).  With a
+// side stream:
+//   side: shared gate/up -> shared down (into y_s) -> (shared done) ->
+//         [routing done] -> gate/up and down of the groups of <= 32 rows
+//         (into r_out) -> (join)
+//   main: routing -> gate/up of the 33..128-row groups (128-row tiles) and of
+//         the larger ones (256-row tiles) -> their down GEMMs (into r_out) ->
+//         [join] -> combine out = r_out + y_s
+// Each group's rows are written (h_r, r_out) by launches of one stream only.
+// Without a side stream the same GEMMs run in stage order on `stream`, the
+// routed down epilogues adding y_s themselves.
+hipError_t enqueue_bf16_prefill_classes(const moe_config& c, int T, const moe_weights* w, void* out, uint8_t* ws,
+                                        const WsLayout& L, const Route& R, const GemmArgs& g1, const GemmArgs& gs,
+                                        const GemmArgs& g2, const GemmArgs& g3, const AuxStream* aux,
+                                        hipStream_t stream, hipEvent_t* ev) {
+  hipError_t e;
+  const int E = c.n_experts;
+  const int32_t* tiles_class = R.tiles + 3 * kNumBM * (E + 2);   // the class tables, indexed by tile height
+  const int bm_sd = down_tile_rows(T, 1, c.d, 256);
+  auto gateup_small = [&](hipStream_t s) {
+    return TRACED("gateup", 32, 0, 3, s, launch_gemm_decode_tail(MODE_GATEUP, g1, 0, s, R.tiles));
+  };
+  auto gateup_mid_big = [&](hipStream_t s) {
+    hipError_t r = TRACED("gateup", 128, 0, 3, s, launch_gemm_bf16_v2(MODE_GATEUP, 128, g1, T, s, tiles_class));
+    if (r == hipSuccess) r = TRACED("gateup", 256, 0, 3, s, launch_gemm_bf16_v2(MODE_GATEUP, 256, g1, T, s, tiles_class));
+    return r;
+  };
+  auto down_small = [&](const GemmArgs& g, const char* name, hipStream_t s) {
+    return TRACED(name, 32, 0, 3, s, launch_gemm_decode_tail(MODE_DOWN_ROUTED, g, 0, s, R.tiles));
+  };
+  auto down_mid_big = [&](const GemmArgs& g, const char* name, hipStream_t s) {
+    hipError_t r = TRACED(name, 128, 0, 3, s, launch_gemm_bf16_v2(MODE_DOWN_ROUTED, 128, g, T, s, tiles_class));
+    if (r == hipSuccess) r = TRACED(name, 256, 0, 3, s, launch_gemm_bf16_v2(MODE_DOWN_ROUTED, 256, g, T, s, tiles_class));
+    return r;
+  };
+  if (aux) {
+    const hipStream_t a = aux->stream;
+    GemmArgs g3r = g3;   // routed rows into r_out (fp32, token order); the combine adds y_s
+    g3r.C = ws + L.r_out;
+    g3r.Y = nullptr;
+    g3r.out_bf16 = 0;
+    if ((e = hipEventRecord(aux->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(a, aux->fork, 0)) != hipSuccess) return e;
+    if ((e = TRACED("gateup", 256, 1, 0, a, launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, T, a, R.tiles))) != hipSuccess)
+      return e;
+    if ((e = TRACED("down_shared", bm_sd, 1, 0, a, launch_gemm_bf16_v2(MODE_DOWN_SHARED, bm_sd, g2, T, a, R.tiles))) !=
+        hipSuccess)
+      return e;
+    if ((e = hipEventRecord(aux->shared, a)) != hipSuccess) return e;
+    if ((e = enqueue_route(c, g1.A, T, w, R, stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(aux->routed, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(a, aux->routed, 0)) != hipSuccess) return e;
+    if ((e = gateup_small(a)) != hipSuccess || (e = down_small(g3r, "down_routed_r", a)) != hipSuccess) return e;
+    if ((e = hipEventRecord(aux->join, a)) != hipSuccess) return e;
+    if ((e = gateup_mid_big(stream)) != hipSuccess || (e = down_mid_big(g3r, "down_routed_r", stream)) != hipSuccess)
+      return e;
+    if ((e = hipStreamWaitEvent(stream, aux->join, 0)) != hipSuccess) return e;
+    if (c.top_k > 1) return finish_topk(c, ws, L, T, 1, out, stream);
+    return TRACED("combine", 0, -1, 0, stream,
+                  launch_combine(reinterpret_cast<const float*>(ws + L.r_out), reinterpret_cast<const float*>(ws + L.y_s),
+                                 1, out, static_cast<int64_t>(T) * c.d, c.out_dtype == MOE_BF16, stream));
+  }
+  auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  if ((e = mark(0)) != hipSuccess) return e;
+  if ((e = enqueue_route(c, g1.A, T, w, R, stream)) != hipSuccess) return e;
+  if ((e = mark(1)) != hipSuccess) return e;
+  if ((e = gateup_small(stream)) != hipSuccess || (e = gateup_mid_big(stream)) != hipSuccess) return e;
+  if ((e = TRACED("gateup", 256, 1, 0, stream, launch_gemm_bf16_v2(MODE_GATEUP, 256, gs, T, stream, R.tiles))) !=
+      hipSuccess)
+    return e;
+  if ((e = mark(2)) != hipSuccess) return e;
+  if ((e = TRACED("down_shared", bm_sd, 1, 0, stream, launch_gemm_bf16_v2(MODE_DOWN_SHARED, bm_sd, g2, T, stream,
+                                                                           R.tiles))) != hipSuccess)
+    return e;
+  if ((e = mark(3)) != hipSuccess) return e;
+  if ((e = down_small(g3, "down_routed", stream)) != hipSuccess || (e = down_mid_big(g3, "down_routed", stream)) != hipSuccess)
+    return e;
+  if ((e = finish_topk(c, ws, L, T, 1, out, stream)) != hipSuccess) return e;
+  return mark(4);
+}
+
 // bf16 prefill.  Routed groups: main tiles of bm_r rows (gate/up) and bm_d
 // rows (down) on the MFMA kernels over table_main; the tails (the 1..32 rows
 // past a group's last full main tile, or all of a group of at most 32
@@ -527,6 +615,13 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
   g1.group_hi = E;
   const GemmArgs g2 = down_shared_args(c, w, ws, L, R, ws + L.h_s, nullptr, T, 1);
   const GemmArgs g3 = down_routed_args(c, w, ws, L, R, ws + L.h_r, nullptr, out, T, 1);
+  // Groups averaging under 192 rows (the Maverick-shaped layer: 13..647 rows
+  // over 128 experts) stream nearly all their weights from HBM; each group
+  // then takes one tile height by its size (the class tables), so that its
+  // weights are read by one set of tiles: 1..32 rows on the weight-streaming
+  // tiles, 33..128 rows on one 128-row tile, more on 256-row tiles.  (With
+  // the main / tail split a group of 129..160 rows read its weights twice.)
+  if (tails && bm_r == 128) return enqueue_bf16_prefill_classes(c, T, w, out, ws, L, R, g1, gs, g2, g3, aux, stream, ev);
 
   if (aux) {
     const hipStream_t a = aux->stream;
@@ -619,6 +714,80 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
   if ((e = TRACED("down_routed", bm_d, 0, tails ? 1 : 0, stream,
                   launch_gemm_bf16_v2(MODE_DOWN_ROUTED, bm_d, g3, T, stream, tiles_main))) != hipSuccess)
     return e;
+  if ((e = finish_topk(c, ws, L, T, 1, out, stream)) != hipSuccess) return e;
+  return mark(4);
+}
+
+// e4m3 prefill (T >= 256).  The routed groups' gate/up and down GEMMs take
+// bm_r-row tiles (160 when the mean group holds 96..136 rows, so one tile
+// takes a group whole; else 128): they stream each expert's weights once
+// from HBM.  The shared expert's gate/up and down GEMMs are MFMA-bound and
+// take the 256 x 256 tiles.  h is quantised per row to e4m3 between the two
+// GEMMs of each expert (from its fp32 values and the row max the gate/up
+// epilogue gathered), and the routed down epilogue adds the shared output.
+// With a side stream the shared expert's three launches run there, next to
+// the routed gate/up:
+//   side: [fork] shared gate/up -> quantise h_s -> shared down -> (done)
+//   main: routed gate/up -> quantise h_r -> [done] -> routed down
+// Without one (the stage-timed variant) the same launches run in stage
+// order on `stream`; the results are the same bit for bit.
+hipError_t enqueue_fp8_prefill(const moe_config& c, const moe_weights* w, void* out, uint8_t* ws, const WsLayout& L,
+                               const Route& R, const void* xq, float* sx, uint32_t* amax_r, uint32_t* amax_s, int T,
+                               const AuxStream* aux, hipStream_t stream, hipEvent_t* ev) {
+  hipError_t e;
+  auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  const int E = c.n_experts;
+  const int bm_r = fp8_routed_rows(static_cast<int64_t>(T) * c.top_k, E);
+  GemmArgs g1 = gateup_args(c, w, ws, L, R, xq, sx, amax_r, amax_s, T);
+  GemmArgs gs = g1;
+  gs.group_lo = E;
+  gs.group_hi = E + 1;
+  g1.group_lo = 0;
+  g1.group_hi = E;
+  float* sh_r = reinterpret_cast<float*>(ws + L.sh_r);
+  float* sh_s = reinterpret_cast<float*>(ws + L.sh_s);
+  const GemmArgs g2 = down_shared_args(c, w, ws, L, R, ws + L.hq_s, sh_s, T, 1);
+  const GemmArgs g3 = down_routed_args(c, w, ws, L, R, ws + L.hq_r, sh_r, out, T, 1);
+  auto routed_gateup = [&](hipStream_t s) {
+    return TRACED("gateup", bm_r, 0, 0, s, launch_gemm_fp8(MODE_GATEUP, bm_r, g1, T, s, R.tiles));
+  };
+  auto shared_gateup = [&](hipStream_t s) {
+    return TRACED("gateup", 256, 1, 0, s, launch_gemm_fp8(MODE_GATEUP, 256, gs, T, s, R.tiles));
+  };
+  auto quant_r = [&](hipStream_t s) {
+    return TRACED("quant_h", 0, 0, 0, s,
+                  launch_quant_h(reinterpret_cast<const float*>(ws + L.h_r), amax_r, T * c.top_k, c.f, ws + L.hq_r,
+                                 sh_r, s));
+  };
+  auto quant_s = [&](hipStream_t s) {
+    return TRACED("quant_h", 0, 1, 0, s,
+                  launch_quant_h(reinterpret_cast<const float*>(ws + L.h_s), amax_s, T, c.f_shared, ws + L.hq_s, sh_s,
+                                 s));
+  };
+  auto shared_down = [&](hipStream_t s) {
+    return TRACED("down_shared", 256, 1, 0, s, launch_gemm_fp8(MODE_DOWN_SHARED, 256, g2, T, s, R.tiles));
+  };
+  auto routed_down = [&](hipStream_t s) {
+    return TRACED("down_routed", bm_r, 0, 0, s, launch_gemm_fp8(MODE_DOWN_ROUTED, bm_r, g3, T, s, R.tiles));
+  };
+  if (aux) {
+    const hipStream_t a = aux->stream;
+    if ((e = hipEventRecord(aux->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(a, aux->fork, 0)) != hipSuccess) return e;
+    if ((e = shared_gateup(a)) != hipSuccess || (e = quant_s(a)) != hipSuccess || (e = shared_down(a)) != hipSuccess)
+      return e;
+    if ((e = hipEventRecord(aux->shared, a)) != hipSuccess) return e;
+    if ((e = routed_gateup(stream)) != hipSuccess || (e = quant_r(stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, aux->shared, 0)) != hipSuccess) return e;
+    if ((e = routed_down(stream)) != hipSuccess) return e;
+    return finish_topk(c, ws, L, T, 1, out, stream);
+  }
+  if ((e = routed_gateup(stream)) != hipSuccess || (e = shared_gateup(stream)) != hipSuccess) return e;
+  if ((e = mark(2)) != hipSuccess) return e;
+  if ((e = quant_r(stream)) != hipSuccess || (e = quant_s(stream)) != hipSuccess || (e = shared_down(stream)) != hipSuccess)
+    return e;
+  if ((e = mark(3)) != hipSuccess) return e;
+  if ((e = routed_down(stream)) != hipSuccess) return e;
   if ((e = finish_topk(c, ws, L, T, 1, out, stream)) != hipSuccess) return e;
   return mark(4);
 }
@@ -759,6 +928,7 @@ moe_status moe_route(moe_plan_t plan, const void* x, int64_t T, const moe_weight
   Route R = route_ptrs(ws, L, out);
   hipError_t e = hipSuccess;
   const moe_config& c = plan->cfg;
+  // (routing alone needs no e4m3 codes: the fused kernel only with the norm)
   if (c.has_norm && fused_norm_route(c)) {
     e = TRACED("norm_route", 0, -1, 0, stream,
                launch_norm_route(x, w->norm_weight, static_cast<int>(T), c.d, c.n_experts, c.norm_eps, w->w_router,
@@ -799,7 +969,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   // are one kernel (x read once; the routing stage then starts from the
   // logits)
   hipEvent_t evn[MOE_NUM_STAGES + 1];
-  if (c.has_norm && T > 0) {
+  if ((c.has_norm || fused_norm_route(c)) && T > 0) {
     if (ev) {
       hipError_t e0 = hipEventRecord(ev[0], stream);
       if (e0 != hipSuccess) return hip_fail(plan, e0);
@@ -811,13 +981,14 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     float* sx = fp8 ? reinterpret_cast<float*>(ws + L.sx) : nullptr;
     const hipError_t en =
         fused_norm_route(c)
-            ? TRACED("norm_route", 0, -1, 0, stream,
-                     launch_norm_route(x, w->norm_weight, Ti, c.d, c.n_experts, c.norm_eps, w->w_router,
-                                       ws + L.wr_pack, ws + L.x_n, xq, sx, R.logits, stream))
+            ? TRACED(c.has_norm ? "norm_route" : "route_quant", 0, -1, 0, stream,
+                     launch_norm_route(x, c.has_norm ? w->norm_weight : nullptr, Ti, c.d, c.n_experts, c.norm_eps,
+                                       w->w_router, ws + L.wr_pack, c.has_norm ? ws + L.x_n : nullptr, xq, sx,
+                                       R.logits, stream))
             : TRACED("rmsnorm", 0, -1, 0, stream,
                      launch_rmsnorm(c.x_dtype, x, w->norm_weight, Ti, c.d, c.norm_eps, ws + L.x_n, xq, sx, stream));
     if (en != hipSuccess) return hip_fail(plan, en);
-    x = ws + L.x_n;
+    if (c.has_norm) x = ws + L.x_n;
     R.logits_ready = fused_norm_route(c);
   }
   if (c.n_experts == 0) {
@@ -837,7 +1008,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   // stage-timed variant or a serial call, which keep every stage on `stream`)
   std::unique_lock<std::mutex> lock(plan->mu, std::defer_lock);
   const AuxStream* aux = nullptr;
-  if (!ev && !serial && T > 0 && (dec || v2)) {
+  if (!ev && !serial && T > 0 && (dec || v2 || f8)) {
     lock.lock();
     aux = aux_for(plan, stream, &e);
     if (e != hipSuccess) return hip_fail(plan, e);
@@ -866,7 +1037,7 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
   if (fp8) {
     uint8_t* xq = ws + L.xq;
     sx = reinterpret_cast<float*>(ws + L.sx);
-    if (!c.has_norm && (e = TRACED("quant_x", 0, -1, 0, stream,
+    if (!c.has_norm && !R.logits_ready && (e = TRACED("quant_x", 0, -1, 0, stream,
                                    launch_quant_x(static_cast<const uint16_t*>(x), Ti, c.d, xq, sx, stream))) != hipSuccess)
       return hip_fail(plan, e);
     a_x = xq;
@@ -877,16 +1048,14 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
     if ((e = TRACED("fill", 0, -1, 0, stream, launch_fill_u32(amax_s, T, 0u, stream))) != hipSuccess) return hip_fail(plan, e);
   }
   if ((e = mark(1)) != hipSuccess) return hip_fail(plan, e);
+  if (f8) {
+    e = enqueue_fp8_prefill(c, w, out, ws, L, R, a_x, sx, amax_r, amax_s, Ti, aux, stream, ev);
+    return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
+  }
 
   // gate/up (routed groups + shared group) with the SwiGLU epilogue
   GemmArgs g1 = gateup_args(c, w, ws, L, R, a_x, sx, amax_r, amax_s, Ti);
-  if (f8) {
-    g1.group_lo = 0;
-    g1.group_hi = c.n_experts + 1;
-    const int bm = fp8_routed_rows(static_cast<int64_t>(Ti) * c.top_k, c.n_experts);
-    if ((e = TRACED("gateup", bm, 2, 0, stream, launch_gemm_fp8(MODE_GATEUP, bm, g1, Ti, stream, R.tiles))) != hipSuccess)
-      return hip_fail(plan, e);
-  } else if (dec && int_weights(c)) {
+  if (dec && int_weights(c)) {
     // int8 / int4 tiles: the routed groups, then the shared expert
     g1.group_lo = 0;
     g1.group_hi = c.n_experts;
@@ -930,17 +1099,14 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
 
   const int ys = dec ? decode_y_parts(c, T) : 1;
   const GemmArgs g2 = down_shared_args(c, w, ws, L, R, h_s, sh_s, Ti, ys);
-  e = f8    ? TRACED("down_shared", 128, 1, 0, stream, launch_gemm_fp8(MODE_DOWN_SHARED, 128, g2, Ti, stream, R.tiles))
-      : dec ? TRACED("down_shared", 32, 1, 0, stream, launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles))
-            : TRACED("down_shared", 0, 1, 0, stream, launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles));
+  e = dec ? TRACED("down_shared", 32, 1, 0, stream, launch_gemm_decode(MODE_DOWN_SHARED, true, g2, Ti, stream, R.tiles))
+          : TRACED("down_shared", 0, 1, 0, stream, launch_gemm(MODE_DOWN_SHARED, c.w_dtype, g2, Ti, stream, R.tiles));
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(plan, e);
 
   const GemmArgs g3 = down_routed_args(c, w, ws, L, R, h_r, sh_r, out, Ti, ys);
-  const int bm_f8 = fp8_routed_rows(static_cast<int64_t>(Ti) * c.top_k, c.n_experts);
-  e = f8    ? TRACED("down_routed", bm_f8, 0, 0, stream, launch_gemm_fp8(MODE_DOWN_ROUTED, bm_f8, g3, Ti, stream, R.tiles))
-      : dec ? TRACED("down_routed", 16, 0, 0, stream, launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles))
-            : TRACED("down_routed", 0, 0, 0, stream, launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles));
+  e = dec ? TRACED("down_routed", 16, 0, 0, stream, launch_gemm_decode(MODE_DOWN_ROUTED, false, g3, Ti, stream, R.tiles))
+          : TRACED("down_routed", 0, 0, 0, stream, launch_gemm(MODE_DOWN_ROUTED, c.w_dtype, g3, Ti, stream, R.tiles));
   if (e != hipSuccess) return hip_fail(plan, e);
   if ((e = finish_topk(c, ws, L, Ti, ys, out, stream)) != hipSuccess) return hip_fail(plan, e);
   if ((e = mark(4)) != hipSuccess) return hip_fail(plan, e);

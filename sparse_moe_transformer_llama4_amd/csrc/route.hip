@@ -484,6 +484,7 @@ __device__ void offsets_and_tiles(int cnt, int E, int T, int32_t* counts, int32_
     v[1 + i] = (cnt + bm - 1) / bm;
     v[1 + kNumBM + i] = tail ? cnt / bm : (cnt + bm - 1) / bm;
     v[1 + 2 * kNumBM + i] = tail ? 1 : 0;
+    v[1 + 3 * kNumBM + i] = class_tiles(cnt, bm);
   }
   block_exclusive_scan<1 + kNumTables>(v, tot, sm);
   if (e < E) {
@@ -496,7 +497,7 @@ __device__ void offsets_and_tiles(int cnt, int E, int T, int32_t* counts, int32_
     offsets[E] = tot[0];
 #pragma unroll
     for (int i = 0; i < kNumTables; ++i) {
-      const int shared = i >= 2 * kNumBM ? 0 : (T + bm_of(i % kNumBM) - 1) / bm_of(i % kNumBM);
+      const int shared = i >= 2 * kNumBM ? 0 : (T + bm_of(i % kNumBM) - 1) / bm_of(i % kNumBM);   // tail, class: none
       tiles[i * (E + 2) + E] = tot[1 + i];   // the shared group follows the routed ones
       tiles[i * (E + 2) + E + 1] = tot[1 + i] + shared;
     }

@@ -333,6 +333,44 @@ def test_side_stream_down_tails_wait_for_main_gateup(gpu):
     check_forward(cfg, inp, out, routing)
 
 
+@pytest.mark.parametrize("k", [1, 2])
+def test_class_tiles_every_size_class(gpu, k):
+    # groups averaging under 192 rows take one tile height each by size
+    # (1..32 rows: weight-streaming tiles, 33..128: one 128-row tile, more:
+    # 256-row tiles): groups of 20, 40, 100, 128, 129, 200, 300 and 583 rows
+    # (1500 tokens over 8 experts at d = 512); with k = 2 the picks spread
+    # over the same classes.  Two-stream vs serial schedule bit for bit on a
+    # poisoned workspace, and the oracle
+    from sparse_moe_transformer_llama4_amd import moe
+    # (k = 2: 750 tokens whose picks give groups of 260, 30, 60, 100, 150,
+    # 220, 280 and 400 slots, 187.5 on average)
+    sizes = [20, 40, 100, 128, 129, 200, 300, 583] if k == 1 else [10, 20, 40, 60, 90, 130, 150, 250]
+    cfg = dataclasses.replace(synth.get_config("small_bf16_tall"), T=sum(sizes), top_k=k, name=f"classes_k{k}")
+    inp = synth.make_inputs(cfg)
+    assign = _assign_groups(inp, sizes)
+    if k == 2:   # second pick: the next expert (its logit lifted to half the first's)
+        x = inp["x"]
+        x[torch.arange(cfg.T), (assign + 1) % cfg.E] = 2.0
+        inp["x"] = x
+    g = to_device(inp, gpu)
+    p = _plan(cfg)
+    ws = torch.empty(moe.moe_workspace_size(p, cfg.T), dtype=torch.uint8, device=gpu)
+    ws.fill_(0xFF)
+    ref = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device=gpu)
+    moe.moe_forward_timed(p, g["x"], g, moe.StageEvents(), out=ref, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ws.fill_(0xFF)
+        out = torch.full_like(ref, float("nan"))
+        routing = moe.new_routing(p, cfg.T, gpu)
+        moe.moe_forward(p, g["x"], g, out=out, routing=routing, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"call {rep}: two-stream schedule differs from the serial one"
+    if k == 1:
+        assert routing["counts"].cpu().tolist() == sizes
+    check_forward(cfg, inp, out, routing)
+
+
 GRAPH_CASES = [("small_fp32", {}), ("small_fp8", {}), ("decode_like_bf16", {}), ("small_bf16_tall", {}),
                ("decode_like_bf16", dict(w_dtype="i8", T=33)), ("decode_like_bf16", dict(w_dtype="i4", T=33)),
                ("decode_like_bf16", dict(top_k=2, T=33)), ("small_bf16_tall", dict(top_k=2)),
