@@ -373,7 +373,7 @@ def stored_traffic(workload, kernel):
     if not os.path.exists(PROFILE_TRAFFIC):
         return None
     tr = json.load(open(PROFILE_TRAFFIC)).get(workload, {}).get(kernel)
-    if tr and tr.get("source_hash") == _kernel_source_hash():
+    if tr and "symbol" in tr and tr.get("source_hash") == _kernel_source_hash(tr["symbol"]):
         return tr["bytes"]
     return None
 
@@ -412,7 +412,15 @@ def main():
                     help="store the HBM bytes per launch of --config's launch KERNEL_KEY (kernel symbol SYMBOL) "
                          "from --pmc-summary files of FETCH_SIZE and WRITE_SIZE runs, scaled by a --calibrate-copy "
                          "run's, in profiles/traffic.json, and exit")
+    ap.add_argument("--trace-summary", nargs=4, metavar=("DIR", "OUT", "WARMUP", "STEPS"),
+                    help="write a markdown summary of a rocprofv3 --kernel-trace --stats CSV directory of a bench.py "
+                         "run made with --latency-samples 0 --no-clock and these --warmup / --steps (the library's "
+                         "kernels: the --stats rows, then one call of timed region 1 launch by launch) and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        d, out, w, k = args.trace_summary
+        print(f"{trace_summary(d, out, int(w), int(k))} library dispatches")
+        return
     if args.pmc_summary:
         print(f"{pmc_summary(*args.pmc_summary)} dispatches")
         return
@@ -428,7 +436,9 @@ def main():
     if args.calibrate_copy:
         import torch
         n = args.calibrate_copy << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        # no fill: the copies are the only kernels, so the counters' copy
+        # dispatches are exactly these
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
         b = torch.empty_like(a)
         torch.cuda.synchronize()
         for _ in range(3):
@@ -525,6 +535,109 @@ def pmc_summary(d: str, out: str, pattern: str = "moe::") -> int:
     return len(rows)
 
 
+KERNEL_ROLES = {
+    "norm_route_kernel": "RMSNorm and/or e4m3 codes of x, and the router logits, per 16 rows",
+    "wr_pack_kernel": "router weight into the fused kernel's layout",
+    "rmsnorm_kernel": "RMSNorm of x (and its e4m3 codes)",
+    "quant_x_kernel": "e4m3 codes and row scales of x",
+    "quant_h_kernel": "e4m3 codes and row scales of h",
+    "router_partial_kernel": "router logits, K-split partial sums",
+    "router_finish_kernel": "top-k, gate, expert histograms",
+    "route_small_kernel": "router for a few tokens: logits, top-k, counts, tables",
+    "scan_kernel": "expert offsets and tile tables",
+    "perm_kernel": "stable permutation of the routed rows",
+    "combine_kernel": "out = routed rows + shared rows",
+    "combine_topk_kernel": "out = gate-weighted routed rows + shared rows (top-k > 1)",
+    "swiglu_parts_kernel": "SwiGLU of summed K-split gate/up partials",
+    "fill_u32_kernel": "zero the per-row max |h|",
+    "gemm_fp8_kernel": "e4m3 scaled-MFMA GEMM <MODE, tile rows>, 256 columns",
+    "gemm_fp8_tall_kernel": "e4m3 scaled-MFMA GEMM <MODE>, 256 x 256 tiles",
+    "gemm_bf16_kernel": "bf16 MFMA GEMM <MODE, tile rows, wave rows, wave columns>",
+    "gemm_kernel": "bf16 MFMA GEMM (router logits / generic)",
+    "gemm_decode_kernel": "weight-streaming GEMM for <= 32-row groups <MODE, 16-row fragments>",
+    "gemm_decode_gateup_kernel": "weight-streaming gate/up + SwiGLU for <= 32-row groups",
+    "gemm_q8_kernel": "int8 / int4 weight-streaming GEMM <MODE, 16-row fragments, code bits>",
+}
+MODE_NAMES = {"0": "gate/up + SwiGLU", "1": "shared down", "2": "routed down"}
+
+
+def _short_kernel(name: str) -> str:
+    """'void moe::(anonymous namespace)::f<1, 2>(Args)' -> 'f<1, 2>'."""
+    n = name.strip()
+    if n.startswith("void "):
+        n = n[5:]
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):   # the argument list is the first top-level '('
+        if ch in "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not n[i:].startswith("(anonymous namespace)"):
+            cut = i
+            break
+    n = n[:cut]
+    return n.replace("(anonymous namespace)::", "").replace("moe::", "")
+
+
+def _kernel_role(short: str) -> str:
+    base = short.split("<")[0]
+    role = KERNEL_ROLES.get(base, "")
+    if short.startswith("gemm_bf16_kernel<1, 64,"):
+        return "router logits (N = E) or a shared down of <= 64 rows: " + role
+    if base.startswith("gemm_") and "<" in short:
+        mode = short.split("<")[1].split(",")[0].split(">")[0].strip()
+        if mode in MODE_NAMES and base != "gemm_kernel":
+            role = f"{MODE_NAMES[mode]}: {role}"
+    return role
+
+
+def trace_summary(d: str, out: str, warmup: int, steps: int) -> int:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats CSV directory
+    of one bench.py run (--latency-samples 0 --no-clock, so the library is
+    called 2*warmup + 2*steps times: warm-up pairs of moe_forward and
+    moe_forward_traced, then `steps` of each).  Lists the --stats rows of the
+    library's kernels, then the launches of the last moe_forward call of
+    timed region 1 with their queue, start and end."""
+    import csv
+    import glob
+    stats = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if "moe::" in r["Name"]:
+                stats.append(r)
+    trace = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if "moe::" in r["Kernel_Name"]:
+                trace.append(r)
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    calls = 2 * warmup + 2 * steps
+    if not trace or len(trace) % calls:
+        raise SystemExit(f"{len(trace)} library dispatches do not split into {calls} calls")
+    per = len(trace) // calls
+    lines = ["| kernel | role | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        k = _short_kernel(r["Name"])
+        lines.append(f"| `{k}` | {_kernel_role(k)} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    call = trace[(2 * warmup + steps - 1) * per:(2 * warmup + steps) * per]
+    t0 = min(int(r["Start_Timestamp"]) for r in call)
+    t1 = max(int(r["End_Timestamp"]) for r in call)
+    qkey = "Stream_Id" if "Stream_Id" in call[0] else "Queue_Id"
+    main_q = call[0][qkey]
+    lines += ["", f"Launches of one `moe_forward` call (the last of timed region 1): {(t1 - t0) / 1e3:.1f} us "
+                  f"from the first start to the last end; 'main' is the queue of the call's first launch.", "",
+              "| kernel | queue | start us | end us | us |", "|---|---|---|---|---|"]
+    for r in call:
+        a, b = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        k = _short_kernel(r["Kernel_Name"])
+        q = "main" if r[qkey] == main_q else "side"
+        lines.append(f"| `{k}` | {q} | {(a - t0) / 1e3:.1f} | {(b - t0) / 1e3:.1f} | {(b - a) / 1e3:.1f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return len(trace)
+
+
 def _read_pmc_summary(path: str):
     out = []
     for line in open(path):
@@ -541,21 +654,34 @@ def record_traffic(workload: str, kernel: str, symbol: str, fetch_sum: str, writ
     ones whose name mentions 'copy' or 'elementwise'); stored in
     profiles/traffic.json under the workload and the launch's key, with the
     library source hash it is valid for."""
-    def per_dispatch(path, counter, match):
+    # SYMBOL#i/m: of the dispatches whose name contains SYMBOL, in dispatch
+    # order, those at positions i, i + m, i + 2m ... (the launch's place among
+    # m launches of that kernel in one call)
+    sel_i, sel_m = 0, 1
+    if "#" in symbol:
+        symbol, sel = symbol.split("#")
+        sel_i, sel_m = (int(v) for v in sel.split("/"))
+
+    def per_dispatch(path, counter, match, pick=True):
         v = [c[counter] for _, name, _, c in _read_pmc_summary(path) if match(name) and counter in c]
+        if pick:
+            if len(v) % sel_m:
+                raise SystemExit(f"{len(v)} dispatches of {symbol} in {path} are not calls of {sel_m}")
+            v = v[sel_i::sel_m]
         if not v:
             raise SystemExit(f"no dispatch of {symbol if match is not copy_match else 'the copy'} with {counter} in {path}")
         return sum(v) / len(v), len(v)
     copy_match = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
     kmatch = lambda n: symbol in n
-    cf, _ = per_dispatch(copy_fetch_sum, "FETCH_SIZE", copy_match)
-    cw, _ = per_dispatch(copy_write_sum, "WRITE_SIZE", copy_match)
+    cf, _ = per_dispatch(copy_fetch_sum, "FETCH_SIZE", copy_match, False)
+    cw, _ = per_dispatch(copy_write_sum, "WRITE_SIZE", copy_match, False)
     kf, nf = per_dispatch(fetch_sum, "FETCH_SIZE", kmatch)
     kw, nw = per_dispatch(write_sum, "WRITE_SIZE", kmatch)
     sf, sw = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
     ent = {"bytes": (kf * sf + kw * sw) * 1024.0, "fetch_bytes": kf * sf * 1024.0, "write_bytes": kw * sw * 1024.0,
-           "source_hash": _kernel_source_hash(),
-           "note": f"{symbol}: FETCH_SIZE x {sf:.3f} ({nf} dispatches) + WRITE_SIZE x {sw:.3f} ({nw}), factors from a "
+           "symbol": symbol, "source_hash": _kernel_source_hash(symbol),
+           "note": f"{symbol} (dispatch {sel_i} of every {sel_m}): FETCH_SIZE x {sf:.3f} ({nf} dispatches) + "
+                   f"WRITE_SIZE x {sw:.3f} ({nw}), factors from a "
                    f"{copy_bytes >> 20} MiB device-to-device copy"}
     data = json.load(open(PROFILE_TRAFFIC)) if os.path.exists(PROFILE_TRAFFIC) else {}
     data.setdefault(workload, {})[kernel] = ent
@@ -637,16 +763,21 @@ def library_gemm(cfg, iters: int = 30) -> dict:
     return {"library_gemm": out, "config": cfg.name, "library": "torch.matmul (hipBLASLt), bf16"}
 
 
-def _kernel_source_hash() -> str:
-    """Hash of the library's code (comments and whitespace left out): the
+def _kernel_source_hash(symbol: str) -> str:
+    """Hash of the code of the kernel `symbol` names (its function name, the
+    part before any template arguments): every header of the library and each
+    unit that mentions that name, comments and whitespace left out.  The
     recorded traffic is valid while this matches the hash stored with it."""
     import hashlib
     import re
+    base = symbol.split("<")[0].strip()
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_moe_transformer_llama4_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h")):
             src = open(os.path.join(csrc, f)).read()
+            if f.endswith(".hip") and not re.search(r"\b" + re.escape(base) + r"\b", src):
+                continue
             src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
             src = re.sub(r"//[^\n]*", " ", src)
             h.update(f.encode() + b"\0" + " ".join(src.split()).encode())
