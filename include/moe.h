@@ -67,7 +67,8 @@ typedef enum moe_status {
                                     combination not implemented */
   MOE_ERR_SHAPE = -3,            /* T < 0 or T > max_tokens */
   MOE_ERR_WORKSPACE = -4,        /* workspace smaller than moe_workspace_size */
-  MOE_ERR_HIP = -5               /* a HIP launch failed; see moe_last_hip_error */
+  MOE_ERR_HIP = -5,              /* a HIP launch failed; see moe_last_hip_error */
+  MOE_ERR_CHECK = -6             /* debug builds only: a device-side check failed; see moe_debug_flags */
 } moe_status;
 
 typedef enum moe_dtype {
@@ -288,6 +289,22 @@ int moe_last_hip_error(moe_plan_t plan);
 
 /* Library identity, e.g. "moe355 2 gfx950". */
 const char* moe_version(void);
+
+/*
+ * Debug builds (libmoe355_debug.so, compiled with -DMOE_DEBUG) check on the
+ * device, before any grouped GEMM uses them, the invariants of the routing
+ * (expert indices in [0, E), group offsets consistent with the counts, perm
+ * holding every slot once, grouped by expert in slot order, tile tables
+ * non-decreasing from 0), and in every grouped GEMM that its tile lies inside
+ * its group.  A failed check skips the work it guards (no out-of-bounds
+ * access follows) and the call, which in debug builds waits for its stream
+ * before returning, returns MOE_ERR_CHECK.  This returns the check bits of
+ * the last call that failed (bit 0 expert index, 1 offsets / counts, 2 perm,
+ * 3 tile tables, 4 a GEMM tile outside its group), then clears them when
+ * `clear` is non-zero; release builds return -1 and make no device call.
+ * Not for graph capture (the debug calls synchronise).
+ */
+int32_t moe_debug_flags(int32_t clear);
 
 #ifdef __cplusplus
 }

@@ -1,7 +1,10 @@
 """Build libmoe355.so (the C-ABI library) from csrc/*.hip for gfx950 with hipcc.
 
-Usage: python -m sparse_moe_transformer_llama4_amd.build   (or build() from Python)
-The library lands in sparse_moe_transformer_llama4_amd/_lib/ (in-tree).
+Usage: python -m sparse_moe_transformer_llama4_amd.build [--debug]   (or build() from Python)
+The library lands in sparse_moe_transformer_llama4_amd/_lib/ (in-tree); with
+--debug (build(debug=True)) the same sources compiled with -DMOE_DEBUG land in
+_lib/libmoe355_debug.so: device-side checks of the routing and of every GEMM
+tile, reported as MOE_ERR_CHECK (include/moe.h, moe_debug_flags).
 """
 from __future__ import annotations
 
@@ -15,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libmoe355.so")
+DEBUG_LIB = os.path.join(LIBDIR, "libmoe355_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -47,22 +51,25 @@ def _compile(src: str, objdir: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    objdir = os.path.join(LIBDIR, "obj")
+def build(verbose: bool = False, extra=(), debug: bool = False) -> str:
+    objdir = os.path.join(LIBDIR, "obj_debug" if debug else "obj")
+    lib = DEBUG_LIB if debug else LIB
+    extra = list(extra) + (["-DMOE_DEBUG"] if debug else [])
     os.makedirs(objdir, exist_ok=True)
     srcs = sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, objdir, list(extra)), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, objdir, extra), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra=sys.argv[1:])
+    args = sys.argv[1:]
+    build(verbose=True, extra=[a for a in args if a != "--debug"], debug="--debug" in args)

@@ -117,6 +117,7 @@ struct WsLayout {
   size_t x_n;                               // x's rows after the RMSNorm (x dtype), when the block has one
   size_t wr_pack;                           // W_router packed into MFMA B fragments (RMSNorm fused with the router)
   size_t xq, sx;                            // e4m3 x codes [T][d] and fp32 scales [T] (e4m3 only)
+  size_t dbg;                               // uint32 check flags (debug builds; allocated in every build)
   size_t total;
 };
 

@@ -115,6 +115,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   const int NH = (GATEUP && shared) ? p.N_shared : p.N;   // output width of this group
   const int n0 = blockIdx.y * BNH;
   if (n0 >= NH) return;
+  if (!shared && !MOE_DCHECK_TILE(p, g, m0, rows)) return;   // debug builds: the tile is in its group
   const int row_base = shared ? 0 : p.offsets[g];          // first row of the group (permuted order)
   const int ldb = GATEUP ? 2 * NH : NH;                     // weight row length (elements)
 

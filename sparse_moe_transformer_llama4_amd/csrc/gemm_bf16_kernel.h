@@ -168,6 +168,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(GemmArgs p) 
   const int NH = (GATEUP && shared) ? p.N_shared : p.N;
   const int n0 = nt * BNH;
   if (n0 >= NH) return;
+  if (!shared && !MOE_DCHECK_TILE(p, g, m0, rows)) return;   // debug builds: the tile is in its group
   const int row_base = shared ? 0 : p.offsets[g];
   const int ldb = GATEUP ? 2 * NH : NH;
 

@@ -150,6 +150,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_gateup_kernel(GemmArgs p) 
   const int NH = shared ? p.N_shared : p.N;
   const int n0 = bi_n * GBNH;
   if (n0 >= NH) return;
+  if (!shared && !MOE_DCHECK_TILE(p, g, m0, rows)) return;   // debug builds: the tile is in its group
   const int row_base = shared ? 0 : p.offsets[g];
   const int ldb = 2 * NH;
   const int nvalid = min(DBM, rows - m0);
@@ -362,6 +363,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(GemmArgs p) {
   const int NH = p.N;
   const int n0 = bi_n * DBN;
   if (n0 >= NH) return;
+  if (!shared && !MOE_DCHECK_TILE(p, g, m0, rows)) return;   // debug builds: the tile is in its group
   const int row_base = shared ? 0 : p.offsets[g];
   const int ldb = NH;
   const int nvalid = min(DBM, rows - m0);
@@ -666,6 +668,7 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
   const int NH = (GU && shared) ? p.N_shared : p.N;   // output width of this GEMM
   const int n0 = bi_n * OUTC;
   if (n0 >= NH) return;
+  if (!shared && !MOE_DCHECK_TILE(p, g, m0, rows)) return;   // debug builds: the tile is in its group
   const int row_base = shared ? 0 : p.offsets[g];
   const int ldb = GU ? 2 * NH : NH;                   // bytes per weight row
   const int nvalid = min(DBM, rows - m0);

@@ -6,6 +6,30 @@
 
 namespace moe {
 
+// Debug builds (-DMOE_DEBUG): device-side checks of the structure a kernel
+// derives addresses from (routing indices, group offsets, tile tables).  A
+// failed check sets bit `bit` of *flags (a word of the workspace the host
+// reads after the call) and the caller then skips the work it guards, so a
+// broken invariant becomes an error code instead of an out-of-bounds access.
+// Release builds compile every check to `true`.
+enum DebugBit {
+  kDbgIdx = 0,      // an expert index outside [0, E)
+  kDbgOffsets = 1,  // offsets / counts inconsistent (offsets[0] != 0, decreasing, offsets[E] != T k)
+  kDbgPerm = 2,     // perm entry outside [0, T k), in another expert's group, or out of slot order
+  kDbgTiles = 3,    // a tile table not starting at 0 or decreasing
+  kDbgTile = 4,     // a GEMM tile outside its group's rows
+};
+#ifdef MOE_DEBUG
+__device__ __forceinline__ bool dbg_check(uint32_t* flags, bool ok, int bit) {
+  if (!ok && flags) atomicOr(flags, 1u << bit);
+  return ok;
+}
+#define MOE_DCHECK(flags, cond, bit) ::moe::dbg_check((flags), (cond), (bit))
+#else
+__host__ __device__ constexpr bool dbg_pass() { return true; }
+#define MOE_DCHECK(flags, cond, bit) ::moe::dbg_pass()
+#endif
+
 struct RouterArgs {
   const void* x;      // [T][d] x dtype
   const void* wr;     // [d][E] x dtype
@@ -74,7 +98,17 @@ struct GemmArgs {
   int w_int8;              // weight-streaming kernels: 8 = B / B_shared hold int8 codes, 4 = int4 codes packed two
                            // per byte along K (low nibble = even row), sB / sB_shared their fp32 column scales
                            // (a GATEUP launch covers the routed groups or the shared one, not both); 0 = none
+  uint32_t* dbg;           // debug builds: the check flags (MOE_DCHECK); unused otherwise
 };
+
+// A tile (group g, first row m0 of the group's `rows`) lies inside its
+// group: the check every grouped GEMM makes after its tile lookup in debug
+// builds (group E, the shared expert, has T rows and no offsets).
+#define MOE_DCHECK_TILE(p, g, m0, rows)                                                                 \
+  MOE_DCHECK((p).dbg,                                                                                   \
+             (g) >= 0 && (g) <= (p).E && (m0) >= 0 && (m0) < (rows) &&                                  \
+                 ((g) == (p).E || ((p).offsets[g] >= 0 && (p).offsets[g] + (rows) <= (p).offsets[(p).E])), \
+             kDbgTile)
 
 // Router in two launches: partial logits over K slices of d (the slice count
 // grows for few tokens so the GPU fills), then a fixed-order sum + top-1 +
@@ -113,6 +147,18 @@ hipError_t launch_route_small_finish(const RouterArgs& a, const float* logits, i
 hipError_t launch_quant_h(const float* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
                           float* sh, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+// Debug builds: check every routing invariant the GEMMs rely on (expert
+// indices, offsets against counts, perm grouped by expert in slot order,
+// tile tables non-decreasing from 0) and record failures in *flags; then, if
+// any flag is set, zero the tile tables so that no grouped GEMM tile runs on
+// the broken routing.  S = T * k routed slots; tables: kNumTables rows of
+// E + 2 entries.
+hipError_t launch_validate_routing(const int32_t* idx, const int32_t* counts, const int32_t* offsets,
+                                   const int32_t* perm, int32_t* tiles, int S, int E, uint32_t* flags,
+                                   hipStream_t s);
+// Debug builds, tests of the check path: overwrite perm[0] with perm[S - 1]
+// (an in-range slot in the wrong place) before the validation runs.
+hipError_t launch_debug_break_perm(int32_t* perm, int S, hipStream_t s);
 // out = r + y[0] + y[1] + ... + y[parts-1] element by element, in that order
 // (n fp32 values per array, n % 4 == 0; r may be null), stored as bf16 when
 // out_bf16: the combine of the two down GEMMs when they run unordered, and the

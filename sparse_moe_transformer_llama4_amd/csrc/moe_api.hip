@@ -6,6 +6,8 @@
 // calls run the shared expert's two GEMMs on a side stream forked from and
 // joined back into the caller's stream.
 #include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -195,6 +197,7 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
     L.xq = take(t * c.d);
     L.sx = take(t * 4);
   }
+  L.dbg = take(4);
   L.total = off;
   return L;
 }
@@ -242,6 +245,7 @@ struct Route {
   int32_t *idx, *counts, *offsets, *perm, *hist, *tiles;
   float *gate, *logits;
   bool logits_ready;   // logits [T][E] (no bias) already written by the fused RMSNorm + router kernel
+  uint32_t* dbg;       // the debug builds' check flags (workspace)
 };
 
 Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
@@ -255,6 +259,7 @@ Route route_ptrs(uint8_t* ws, const WsLayout& L, const moe_routing* r) {
   o.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   o.logits = reinterpret_cast<float*>(ws + L.logits);
   o.logits_ready = false;
+  o.dbg = reinterpret_cast<uint32_t*>(ws + L.dbg);
   return o;
 }
 
@@ -289,18 +294,61 @@ int down_tile_rows(int64_t rows, int groups, int d, int bm_max) {
   return bm_max >= 128 ? 128 : bm_max;
 }
 
+// Debug builds (-DMOE_DEBUG) check the routing on the device before any
+// grouped GEMM reads it (launch_validate_routing: on a failure the tile
+// tables are zeroed, so no GEMM tile runs) and the GEMMs check each tile
+// against its group; every call clears the flag word first and, at its end,
+// waits for its stream and returns MOE_ERR_CHECK if a check failed.  With
+// MOE_DEBUG_BREAK_PERM=1 in the environment a debug build first moves one
+// in-range slot of perm to a wrong position (for tests of that path).
+// Release builds do none of this.
+#ifdef MOE_DEBUG
+constexpr bool kDebugBuild = true;
+#else
+constexpr bool kDebugBuild = false;
+#endif
+std::atomic<uint32_t> g_debug_flags{0};   // flags of the last call that failed a check
+
+hipError_t debug_validate_route(const moe_config& c, int T, const Route& R, hipStream_t s) {
+  if (!kDebugBuild || T <= 0) return hipSuccess;
+  const int S = T * c.top_k;
+  const char* brk = std::getenv("MOE_DEBUG_BREAK_PERM");
+  hipError_t e = hipSuccess;
+  if (brk && brk[0] == '1') e = launch_debug_break_perm(R.perm, S, s);
+  if (e == hipSuccess) e = launch_validate_routing(R.idx, R.counts, R.offsets, R.perm, R.tiles, S, c.n_experts, R.dbg, s);
+  return e;
+}
+
+// (flags == nullptr: a call without tokens, whose workspace may be null)
+hipError_t debug_begin(uint32_t* flags, hipStream_t s) {
+  return kDebugBuild && flags ? launch_fill_u32(flags, 1, 0u, s) : hipSuccess;
+}
+
+moe_status debug_end(moe_plan_t plan, moe_status st, const uint32_t* flags, hipStream_t s) {
+  if (!kDebugBuild || !flags || st != MOE_OK) return st;
+  uint32_t v = 0;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(&v, flags, sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(plan, e);
+  if (v == 0u) return MOE_OK;
+  g_debug_flags.store(v);
+  return MOE_ERR_CHECK;
+}
+
 // Router + scan + permutation.
 hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_weights* w, const Route& R,
                          hipStream_t s) {
   hipError_t e;
   RouterArgs ra{x, w->w_router, c.has_router_bias ? w->router_bias : nullptr, T, c.d, c.n_experts,
                 R.idx, R.gate, R.hist, c.top_k};
-  if (T > 0 && T <= kRouteTokens)
-    return R.logits_ready
-               ? TRACED("route_small", 0, -1, 0, s,
-                        launch_route_small_finish(ra, R.logits, R.counts, R.offsets, R.tiles, R.perm, s))
-               : TRACED("route_small", 0, -1, 0, s,
-                        launch_route_small(ra, c.x_dtype, R.logits, R.counts, R.offsets, R.tiles, R.perm, s));
+  if (T > 0 && T <= kRouteTokens) {
+    e = R.logits_ready
+            ? TRACED("route_small", 0, -1, 0, s,
+                     launch_route_small_finish(ra, R.logits, R.counts, R.offsets, R.tiles, R.perm, s))
+            : TRACED("route_small", 0, -1, 0, s,
+                     launch_route_small(ra, c.x_dtype, R.logits, R.counts, R.offsets, R.tiles, R.perm, s));
+    return e != hipSuccess ? e : debug_validate_route(c, T, R, s);
+  }
   // Prefill-sized bf16 calls with E a multiple of 64: the logits x·W_router
   // come from the pipelined bf16 GEMM (its fp32 [T][N] mode), then the
   // fixed-order finish; otherwise the dedicated router kernels.
@@ -321,6 +369,7 @@ hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_we
     g.C_shared = R.logits;
     g.group_lo = c.n_experts;
     g.group_hi = c.n_experts + 1;
+    g.dbg = R.dbg;
     if ((e = TRACED("router_gemm", 64, -1, 0, s, launch_gemm_bf16_v2(MODE_DOWN_SHARED, 64, g, T, s, R.tiles))) != hipSuccess)
       return e;
     if ((e = TRACED("router_finish", 0, -1, 0, s, launch_router_finish(ra, 1, R.logits, s))) != hipSuccess) return e;
@@ -332,7 +381,7 @@ hipError_t enqueue_route(const moe_config& c, const void* x, int T, const moe_we
   if (T > 0 && (e = TRACED("perm", 0, -1, 0, s, launch_perm(R.idx, R.hist, R.offsets, T, c.n_experts, c.top_k, R.perm, s))) !=
                    hipSuccess)
     return e;
-  return hipSuccess;
+  return debug_validate_route(c, T, R, s);
 }
 
 GemmArgs gateup_args(const moe_config& c, const moe_weights* w, uint8_t* ws, const WsLayout& L, const Route& R,
@@ -355,6 +404,7 @@ GemmArgs gateup_args(const moe_config& c, const moe_weights* w, uint8_t* ws, con
   g.T = T;
   g.E = c.n_experts;
   g.offsets = R.offsets;
+  g.dbg = R.dbg;
   g.perm = R.perm;
   g.gate = R.gate;
   g.C = ws + L.h_r;
@@ -378,6 +428,7 @@ GemmArgs down_shared_args(const moe_config& c, const moe_weights* w, uint8_t* ws
   g.T = T;
   g.E = c.n_experts;
   g.offsets = R.offsets;
+  g.dbg = R.dbg;
   g.C_shared = reinterpret_cast<float*>(ws + L.y_s);
   g.ksplit = ksplit;
   g.group_lo = c.n_experts;
@@ -399,6 +450,7 @@ GemmArgs down_routed_args(const moe_config& c, const moe_weights* w, uint8_t* ws
   g.T = T;
   g.E = c.n_experts;
   g.offsets = R.offsets;
+  g.dbg = R.dbg;
   g.perm = R.perm;
   g.C = out;
   g.Y = reinterpret_cast<const float*>(ws + L.y_s);
@@ -855,11 +907,17 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_SHAPE: return "token count out of range";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP error";
+    case MOE_ERR_CHECK: return "device-side check failed (debug build)";
   }
   return "unknown status";
 }
 
-const char* moe_version(void) { return "moe355 2 gfx950"; }
+const char* moe_version(void) { return kDebugBuild ? "moe355 2 gfx950 debug" : "moe355 2 gfx950"; }
+
+int32_t moe_debug_flags(int32_t clear) {
+  if (!kDebugBuild) return -1;
+  return static_cast<int32_t>(clear ? g_debug_flags.exchange(0u) : g_debug_flags.load());
+}
 
 moe_status moe_plan(const moe_config* cfg, moe_plan_t* out) {
   if (!out) return MOE_ERR_INVALID_ARGUMENT;
@@ -926,10 +984,12 @@ moe_status moe_route(moe_plan_t plan, const void* x, int64_t T, const moe_weight
   const WsLayout L = layout_for(plan->cfg, T);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   Route R = route_ptrs(ws, L, out);
-  hipError_t e = hipSuccess;
+  uint32_t* const dbg = T > 0 ? R.dbg : nullptr;
+  hipError_t e = debug_begin(dbg, stream);
   const moe_config& c = plan->cfg;
   // (routing alone needs no e4m3 codes: the fused kernel only with the norm)
-  if (c.has_norm && fused_norm_route(c)) {
+  if (e != hipSuccess) {
+  } else if (c.has_norm && fused_norm_route(c)) {
     e = TRACED("norm_route", 0, -1, 0, stream,
                launch_norm_route(x, w->norm_weight, static_cast<int>(T), c.d, c.n_experts, c.norm_eps, w->w_router,
                                  ws + L.wr_pack, ws + L.x_n, nullptr, nullptr, R.logits, stream));
@@ -942,8 +1002,12 @@ moe_status moe_route(moe_plan_t plan, const void* x, int64_t T, const moe_weight
     x = ws + L.x_n;
   }
   if (e == hipSuccess) e = enqueue_route(plan->cfg, x, static_cast<int>(T), w, R, stream);
-  return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
+  return debug_end(plan, e == hipSuccess ? MOE_OK : hip_fail(plan, e), dbg, stream);
 }
+
+static moe_status forward_enqueue(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
+                                  uint8_t* ws, const WsLayout& L, Route R, hipStream_t stream, hipEvent_t* ev,
+                                  bool serial);
 
 static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
                                moe_routing* routing_out, void* workspace, size_t workspace_bytes,
@@ -958,7 +1022,18 @@ static moe_status forward_impl(moe_plan_t plan, const void* x, int64_t T, const 
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const WsLayout L = layout_for(c, T);
-  Route R = route_ptrs(ws, L, routing_out);
+  const Route R = route_ptrs(ws, L, routing_out);
+  uint32_t* const dbg = T > 0 ? R.dbg : nullptr;
+  const hipError_t e = debug_begin(dbg, stream);
+  if (e != hipSuccess) return hip_fail(plan, e);
+  return debug_end(plan, forward_enqueue(plan, x, T, w, out, ws, L, R, stream, ev, serial), dbg, stream);
+}
+
+// The schedules of one forward call (arguments already checked).
+static moe_status forward_enqueue(moe_plan_t plan, const void* x, int64_t T, const moe_weights* w, void* out,
+                                  uint8_t* ws, const WsLayout& L, Route R, hipStream_t stream, hipEvent_t* ev,
+                                  bool serial) {
+  const moe_config& c = plan->cfg;
   const int Ti = static_cast<int>(T);
   const bool fp8 = c.w_dtype == MOE_E4M3;
 

@@ -616,7 +616,89 @@ __global__ __launch_bounds__(64) void perm_kernel(const int32_t* idx, const int3
   }
 }
 
+#ifdef MOE_DEBUG
+// Debug builds: the routing invariants the grouped GEMMs rely on, one thread
+// per routed slot position i (plus the offsets and tile tables in block 0):
+//   * idx[i] in [0, E);
+//   * offsets[0] = 0, offsets[e + 1] - offsets[e] = counts[e] >= 0,
+//     offsets[E] = S;
+//   * perm[i] in [0, S), the slot of an expert-g pick for every position i of
+//     group g, and slots increasing inside a group (the stable order; with the
+//     two conditions before, perm is then a permutation of the S slots);
+//   * every tile table starts at 0 and does not decrease.
+// Positions are placed in groups by a search over offsets clamped to [0, E),
+// so broken offsets cannot send a read out of bounds.
+__global__ __launch_bounds__(256) void validate_routing_kernel(const int32_t* idx, const int32_t* counts,
+                                                               const int32_t* offsets, const int32_t* perm,
+                                                               const int32_t* tiles, int S, int E,
+                                                               uint32_t* flags) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < S) {
+    const int e = idx[i];
+    MOE_DCHECK(flags, e >= 0 && e < E, kDbgIdx);
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offsets[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int sl = perm[i];
+    if (MOE_DCHECK(flags, sl >= 0 && sl < S, kDbgPerm)) {
+      MOE_DCHECK(flags, idx[sl] == lo, kDbgPerm);
+      if (i + 1 < S && i + 1 < offsets[lo + 1]) MOE_DCHECK(flags, perm[i + 1] > sl, kDbgPerm);
+    }
+  }
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < E; e += 256)
+      MOE_DCHECK(flags, counts[e] >= 0 && offsets[e + 1] - offsets[e] == counts[e], kDbgOffsets);
+    if (threadIdx.x == 0) MOE_DCHECK(flags, offsets[0] == 0 && offsets[E] == S, kDbgOffsets);
+    for (int j = threadIdx.x; j < kNumTables * (E + 1); j += 256) {
+      const int t = j / (E + 1), g = j - t * (E + 1);
+      MOE_DCHECK(flags, tiles[t * (E + 2) + g + 1] >= tiles[t * (E + 2) + g], kDbgTiles);
+    }
+    for (int t = threadIdx.x; t < kNumTables; t += 256) MOE_DCHECK(flags, tiles[t * (E + 2)] == 0, kDbgTiles);
+  }
+}
+
+// After the validation (same stream): with any flag set, every tile table
+// becomes all zeros, so the grouped GEMMs find no tiles.
+__global__ __launch_bounds__(256) void neutralize_tables_kernel(int32_t* tiles, int n, const uint32_t* flags) {
+  if (*flags == 0u) return;
+  for (int j = threadIdx.x; j < n; j += 256) tiles[j] = 0;
+}
+
+__global__ void debug_break_perm_kernel(int32_t* perm, int S) {
+  if (threadIdx.x == 0 && S > 1) perm[0] = perm[S - 1];
+}
+#endif  // MOE_DEBUG
+
 // ---------------------------------------------------------------- launchers
+
+// (release builds: no-ops)
+hipError_t launch_validate_routing(const int32_t* idx, const int32_t* counts, const int32_t* offsets,
+                                   const int32_t* perm, int32_t* tiles, int S, int E, uint32_t* flags,
+                                   hipStream_t s) {
+#ifndef MOE_DEBUG
+  return hipSuccess;
+#else
+  if (S <= 0 || E <= 0) return hipSuccess;
+  hipLaunchKernelGGL(validate_routing_kernel, dim3((S + 255) / 256), dim3(256), 0, s, idx, counts, offsets, perm,
+                     tiles, S, E, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(neutralize_tables_kernel, dim3(1), dim3(256), 0, s, tiles, kNumTables * (E + 2),
+                     static_cast<const uint32_t*>(flags));
+  return hipGetLastError();
+#endif
+}
+
+hipError_t launch_debug_break_perm(int32_t* perm, int S, hipStream_t s) {
+#ifndef MOE_DEBUG
+  return hipSuccess;
+#else
+  hipLaunchKernelGGL(debug_break_perm_kernel, dim3(1), dim3(64), 0, s, perm, S);
+  return hipGetLastError();
+#endif
+}
 
 int router_splits(int T, int d, int x_dtype) {
   const int kc = x_dtype == DT_BF16 ? 64 : 32;

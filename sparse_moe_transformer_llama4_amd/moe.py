@@ -5,6 +5,7 @@ fallback: if the library is missing or a call fails, this module raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -13,6 +14,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libmoe355.so")
+# the same library with the device-side checks (build.py --debug)
+DEBUG_LIB_PATH = os.path.join(_HERE, "_lib", "libmoe355_debug.so")
 
 MOE_ABI_VERSION = 2
 MOE_F32, MOE_BF16, MOE_E4M3, MOE_INT8, MOE_INT4 = 0, 1, 2, 3, 4
@@ -24,7 +27,8 @@ _TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.u
 # names declared in include/moe.h
 symbols = ("moe_plan", "moe_plan_destroy", "moe_workspace_size", "moe_route", "moe_forward",
            "moe_forward_timed", "moe_forward_traced", "moe_forward_noalloc", "moe_status_string",
-           "moe_last_hip_error", "moe_version")
+           "moe_last_hip_error", "moe_version", "moe_debug_flags")
+MOE_ERR_CHECK = -6
 MOE_SCRATCH_BYTES = 32 << 20
 MOE_NUM_STAGES = 4
 MOE_MAX_LAUNCHES = 32
@@ -102,8 +106,30 @@ def load_library(path: str = LIB_PATH):
     lib.moe_last_hip_error.restype = ctypes.c_int
     lib.moe_version.argtypes = []
     lib.moe_version.restype = ctypes.c_char_p
+    lib.moe_debug_flags.argtypes = [ctypes.c_int32]
+    lib.moe_debug_flags.restype = ctypes.c_int32
     _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route this module's calls to the library at `path` (e.g. DEBUG_LIB_PATH)
+    inside the block; plans created inside belong to that library and must
+    not be used after it."""
+    global _lib
+    saved = _lib
+    _lib = None
+    try:
+        yield load_library(path)
+    finally:
+        _lib = saved
+
+
+def moe_debug_flags(clear: bool = False) -> int:
+    """Check bits of the last call that failed a device-side check (debug
+    builds; -1 from a release build)."""
+    return int(load_library().moe_debug_flags(int(bool(clear))))
 
 
 def moe_status_string(status: int) -> str:
@@ -143,6 +169,7 @@ class Plan:
         self.x_dtype, self.w_dtype, self.out_dtype = x_dtype, w_dtype, out_dtype
         self.has_bias = bool(has_bias)
         self.handle = ctypes.c_void_p()
+        self._lib = lib
         st = lib.moe_plan(ctypes.byref(self.cfg), ctypes.byref(self.handle))
         if st != 0:
             raise MoeError(st, "moe_plan")
@@ -155,8 +182,9 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value and _lib is not None:
-            _lib.moe_plan_destroy(h)
+        lib = getattr(self, "_lib", None)
+        if h is not None and h.value and lib is not None:
+            lib.moe_plan_destroy(h)
             self.handle = None
 
     def _err(self, st, what):

@@ -229,8 +229,41 @@ def test_fp8_requires_scales_and_bias_when_declared():
 
 
 def test_status_strings():
-    for s in (OK, INVALID, UNSUPPORTED, SHAPE, WORKSPACE, -5):
-        assert moe.moe_status_string(s)
+    for s in (OK, INVALID, UNSUPPORTED, SHAPE, WORKSPACE, -5, moe.MOE_ERR_CHECK):
+        assert moe.moe_status_string(s) != "unknown status"
+
+
+def test_release_build_has_no_debug_checks():
+    """moe_debug_flags answers -1 in a release build without touching a GPU."""
+    assert moe.moe_debug_flags() == -1
+    assert moe.moe_debug_flags(clear=True) == -1
+    assert "debug" not in moe.moe_version()
+
+
+@pytest.mark.skipif(not os.path.exists(moe.DEBUG_LIB_PATH), reason="debug library not built (build.py --debug)")
+def test_debug_library_exports_the_same_entry_points():
+    """The -DMOE_DEBUG build is the same ABI: every declared symbol, the same
+    host-side argument checks (made before any enqueue, so no GPU is needed)."""
+    with moe.using_library(moe.DEBUG_LIB_PATH) as lib:
+        for n in declared_functions():
+            assert hasattr(lib, n), n
+        assert moe.moe_version().endswith("debug")
+        st, h = _plan(top_k=5)
+        assert st == UNSUPPORTED
+        st, h = _plan()
+        assert st == OK
+        n = ctypes.c_size_t()
+        assert lib.moe_workspace_size(h, 64, ctypes.byref(n)) == OK
+        P = 0x10000
+        w = _weights(P)
+        fwd = lambda x, T, w_, out, ws, wsb: lib.moe_forward(h, x, T, ctypes.byref(w_) if w_ else None, out, None,
+                                                             ws, wsb, None)
+        assert fwd(P, 65, w, P, P, n.value) == SHAPE
+        assert fwd(P, 64, w, P, P, n.value - 1) == WORKSPACE
+        assert fwd(P + 4, 64, w, P, P, n.value) == INVALID
+        assert fwd(P, 64, None, P, P, n.value) == INVALID
+        lib.moe_plan_destroy(h)
+    assert "debug" not in moe.moe_version()
 
 
 def test_norm_requires_its_weight():
