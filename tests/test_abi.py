@@ -17,7 +17,7 @@ OK, INVALID, UNSUPPORTED, SHAPE, WORKSPACE = 0, -1, -2, -3, -4
 def declared_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", txt)))
 
 
 def test_library_exports_every_declared_symbol():
