@@ -96,7 +96,10 @@ __device__ __forceinline__ float f64_to_f32_odd(double y) {
 }
 
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU z / (1 + e^-z) with the hardware reciprocal (v_rcp_f32, 1 ulp) in
+// place of the IEEE divide sequence: about 5 VALU instructions per element
+// instead of 15, in epilogues during which the matrix pipe idles.
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ------------------------------------------------------------------ workspace
 

@@ -34,6 +34,7 @@ namespace moe {
 namespace {
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
@@ -64,6 +65,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
                : "memory", "m0");
+}
+
+// Maximum of v over the 16 lanes of its DPP row (lanes 16 r .. 16 r + 15),
+// returned in every lane of the row: lane pairs, quad pairs, the two quads of
+// each half, the two halves (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror; every source lane is in the row).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
 }
 
 
@@ -362,49 +375,72 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
   if (tid < BM) {
     reinterpret_cast<__attribute__((address_space(3))) float*>(As)[tid] = row_scale;
     reinterpret_cast<__attribute__((address_space(3))) int*>(As)[BM + tid] = row_out;
+    reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(As)[2 * BM + tid] = 0u;
   }
   __syncthreads();
-  // The tile goes through LDS (after the 1 KB of row tables) so that global
-  // memory sees 16-byte row chunks instead of scattered 4-byte stores.
+  // The tile goes through LDS (after the row tables) so that global memory
+  // sees 16-byte row chunks instead of scattered 4-byte stores.
   typedef __attribute__((address_space(3))) float lds_f32;
   typedef __attribute__((address_space(3))) int lds_i32;
-  constexpr int TABB = (8 * BM + 1023) / 1024 * 1024;   // the two row tables, rounded to 1 KB
+  constexpr int TABB = (12 * BM + 1023) / 1024 * 1024;  // three row tables, rounded to 1 KB
   lds_u8* const stage = As + TABB;
   if constexpr (GATEUP) {
-    // h tile [BM][BNH] fp32 (row pitch HP bytes), then 16-byte chunks with the
-    // per-row max |h| reduced over the lanes that share a row
+    // h tile [BM][BNH] fp32 (row pitch HP bytes) and each row's max |h|: over
+    // this lane's HF columns, then over the 16 lanes of the row (DPP), then
+    // over the two waves of the row (LDS atomic max on the bit patterns of
+    // non-negative floats); then 16-byte chunks to global memory and one
+    // atomic per row.  Columns past NH hold h = 0 (zero column scales).
     constexpr int HF = FN / 2;
     constexpr int HP = BNH * 4 + 16;
     static_assert(TABB + BM * HP <= NBUF * (A_STAGE + B_STAGE), "h staging fits the ring");
+    float mx[FM][4];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const f32x4 sc = *(const lds_f32x4*)(As + 4 * (wrow + 16 * i));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rt = wrow + i * 16 + q;
+        float m = 0.f;
 #pragma unroll
         for (int j = 0; j < HF; ++j) {
           const float gv = acc[i][j][q] * sc[q] * csc[j];
           const float uv = acc[i][j + HF][q] * sc[q] * csc[j + HF];
-          *(lds_f32*)(stage + rt * HP + (wn * BNW + j * 16 + lcol) * 4) = silu_f(gv) * uv;
+          const float h = silu_f(gv) * uv;
+          *(lds_f32*)(stage + rt * HP + (wn * BNW + j * 16 + lcol) * 4) = h;
+          m = fmaxf(m, fabsf(h));
         }
+        mx[i][q] = row16_max(m);
       }
+    }
+    if (lcol == 15) {
+      uint32_t* const rmax = reinterpret_cast<uint32_t*>(smem) + 2 * BM;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) atomicMax(rmax + wrow + i * 16 + q, __float_as_uint(mx[i][q]));
     }
     __syncthreads();
     constexpr int CPR = BNH / 4;          // 16-byte chunks per row (32)
-    static_assert(CPR == 32 && (BM * CPR) % 256 == 0, "a row's chunks are 32 consecutive lanes");
+    static_assert((BM * CPR) % 256 == 0, "whole passes");
     float* C = reinterpret_cast<float*>(shared ? p.C_shared : p.C);
     uint32_t* amax = shared ? p.amax_shared : p.amax;
-    for (int k = tid; k < BM * CPR; k += 256) {
-      const int r = k / CPR, cc = k - r * CPR;
-      const int col = n0 + cc * 4;
-      const bool ok = m0 + r < rows && col < NH;
-      const f32x4 v = *(const lds_f32x4*)(stage + r * HP + cc * 16);
-      float m = ok ? fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))) : 0.f;
+    if (tid < BM && m0 + tid < rows)
+      atomicMax(&amax[row_base + m0 + tid], reinterpret_cast<const lds_u32*>(As)[2 * BM + tid]);
+    // thread: chunk tid % 32 of rows tid / 32 + 8 u, NU rows read before any is stored
+    constexpr int NPASS = BM * CPR / 256, NU = NPASS % 8 == 0 ? 8 : 5;
+    static_assert(CPR == 32 && NPASS % NU == 0, "whole batches of rows");
+    const int cc = tid & 31, col = n0 + cc * 4;
 #pragma unroll
-      for (int sh = 1; sh < 32; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
-      if (ok) *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row_base + m0 + r) * NH + col) = v;
-      if (cc == 0 && m0 + r < rows) atomicMax(&amax[row_base + m0 + r], __float_as_uint(m));
+    for (int u0 = 0; u0 < NPASS; u0 += NU) {
+      f32x4 v[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) v[u] = *(const lds_f32x4*)(stage + ((tid >> 5) + 8 * (u0 + u)) * HP + cc * 16);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int r = (tid >> 5) + 8 * (u0 + u);
+        if (m0 + r < rows && col < NH)
+          *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row_base + m0 + r) * NH + col) = v[u];
+      }
     }
   } else {
     // scaled fp32 tile [PR][BN] (row pitch FPB bytes) in passes of PR rows
@@ -766,48 +802,69 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(GemmArgs p) {
   __syncthreads();
   reinterpret_cast<lds_f32*>(As)[tid] = row_scale;
   reinterpret_cast<lds_i32*>(As)[BM + tid] = row_out;
+  reinterpret_cast<lds_u32*>(As)[2 * BM + tid] = 0u;
   __syncthreads();
-  constexpr int TABB = 8 * BM;            // the two row tables
+  constexpr int TABB = 12 * BM;           // the three row tables
   lds_u8* const stage = As + TABB;
   // tile row of accumulator element e of fragment row i: wm 128 + 32 i +
   // 8 (e / 4) + 4 kh + e % 4
   const int wrow = wm * 128 + 4 * kh;
   if constexpr (GATEUP) {
-    // h tile [256][128] fp32 (row pitch HP), then 16-byte chunks with the
-    // per-row max |h| reduced over the 32 lanes that share a row
+    // h tile [256][128] fp32 (row pitch HP) and each row's max |h|: over this
+    // lane's two columns, over the 16 lanes of its DPP row (DPP), then over
+    // the two DPP rows and two waves that share the tile row (LDS atomic max
+    // on the bit patterns of non-negative floats); then 16-byte chunks to
+    // global memory and one atomic per row.  Columns past NH hold h = 0.
     constexpr int HP = BNH * 4 + 16;
     static_assert(TABB + BM * HP <= TNBUF * (TA_STAGE + TB_STAGE), "h staging fits the ring");
+    uint32_t* const rmax = reinterpret_cast<uint32_t*>(smem) + 2 * BM;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      float mx[4][4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int rt0 = wrow + 32 * i + 8 * b;
         const f32x4 sc = *(const lds_f32x4*)(As + 4 * rt0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          float m = 0.f;
 #pragma unroll
           for (int j = 0; j < FN / 2; ++j) {
             const float gv = acc[i][j][4 * b + q] * sc[q] * csc[j];
             const float uv = acc[i][j + FN / 2][4 * b + q] * sc[q] * csc[j + FN / 2];
-            *(lds_f32*)(stage + (rt0 + q) * HP + (wn * (BNH / 2) + j * 32 + lcol) * 4) = silu_f(gv) * uv;
+            const float h = silu_f(gv) * uv;
+            *(lds_f32*)(stage + (rt0 + q) * HP + (wn * (BNH / 2) + j * 32 + lcol) * 4) = h;
+            m = fmaxf(m, fabsf(h));
           }
+          mx[b][q] = row16_max(m);
         }
+      }
+      if ((lane & 15) == 15) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) atomicMax(rmax + wrow + 32 * i + 8 * b + q, __float_as_uint(mx[b][q]));
       }
     }
     __syncthreads();
     constexpr int CPR = BNH / 4;          // 32 chunks per row
     float* C = reinterpret_cast<float*>(shared ? p.C_shared : p.C);
     uint32_t* amax = shared ? p.amax_shared : p.amax;
-    for (int k = tid; k < BM * CPR; k += 256) {
-      const int r = k / CPR, cc = k - r * CPR;
-      const int col = n0 + cc * 4;
-      const bool ok = m0 + r < rows && col < NH;
-      const f32x4 v = *(const lds_f32x4*)(stage + r * HP + cc * 16);
-      float m = ok ? fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))) : 0.f;
+    if (m0 + tid < rows) atomicMax(&amax[row_base + m0 + tid], reinterpret_cast<const lds_u32*>(As)[2 * BM + tid]);
+    // thread: chunk tid % 32 of rows tid / 32 + 8 u, 8 rows read before any is stored
+    static_assert(CPR == 32, "a row's chunks are 32 consecutive threads");
+    const int cc = tid & 31, col = n0 + cc * 4;
 #pragma unroll
-      for (int sh = 1; sh < 32; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
-      if (ok) *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row_base + m0 + r) * NH + col) = v;
-      if (cc == 0 && m0 + r < rows) atomicMax(&amax[row_base + m0 + r], __float_as_uint(m));
+    for (int u0 = 0; u0 < BM / 8; u0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *(const lds_f32x4*)(stage + ((tid >> 5) + 8 * (u0 + u)) * HP + cc * 16);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = (tid >> 5) + 8 * (u0 + u);
+        if (m0 + r < rows && col < NH)
+          *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row_base + m0 + r) * NH + col) = v[u];
+      }
     }
   } else {
     // scaled fp32 tile in two passes of 128 rows (one per wave row), then
