@@ -99,7 +99,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(GemmArgs p) 
   lds_u8* const As = (lds_u8*)(smem);
   lds_u8* const Bs = As + NBUF * A_STAGE;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
   const int wm = wave / WN, wn = wave % WN;
   const int E = p.E, T = p.T, K = p.K;
 
@@ -495,6 +496,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(GemmArgs p) 
             if (ok && p.Y && !shared)
               y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
         }
+        // the batch's loads have landed before its first store: the stores
+        // are conditional, and a wait the compiler placed after one of them
+        // would also wait for the stores before it (one round trip each)
+        wait_vmcnt<0>();
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
           const int k = k0 + u * NT;

@@ -96,7 +96,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
   lds_u8* const As = (lds_u8*)(smem);
   lds_u8* const Bs = As + NBUF * A_STAGE;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
   const int wm = wave / WN, wn = wave % WN;
   const int E = p.E, T = p.T, K = p.K;
 
@@ -445,16 +446,33 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
   } else {
     // scaled fp32 tile [PR][BN] (row pitch FPB bytes) in passes of PR rows
     // (160-row tiles: two passes, one per wave row), then 16-byte chunks:
-    // shared down stores them; routed down adds the shared expert's output,
-    // loaded for NB chunks at a time before they are stored
+    // shared down stores them; routed down adds the shared expert's output.
+    // Thread: chunk tid % 64 of pass rows tid / 64 + 4 u.  The routed down
+    // loads its chunks of that output for the pass before the pass's staging
+    // writes, so their latency overlaps the staging, and before the pass's
+    // stores: a load issued after a store would make its wait cover the
+    // store's round trip too.
     constexpr int FPB = BN * 4 + 16;
     constexpr int PR = TABB + BM * FPB <= NBUF * (A_STAGE + B_STAGE) ? BM : BM / WM;
     static_assert(TABB + PR * FPB <= NBUF * (A_STAGE + B_STAGE), "fp32 staging fits the ring");
     constexpr int CPR = BN / 4;
-    constexpr int NB = (PR * CPR) % (256 * 16) == 0 ? 16 : 10;
-    static_assert((PR * CPR) % (256 * NB) == 0, "whole batches");
+    constexpr int NPR = PR * CPR / 256;   // chunks per thread and pass (20 / 32)
+    static_assert(CPR == 64 && (PR * CPR) % 256 == 0, "rows of 64 chunks, whole passes");
+    const int cc = tid & 63, col = n0 + cc * 4;
+    const lds_i32* const orows = reinterpret_cast<const lds_i32*>(As) + BM;
 #pragma unroll
     for (int pass = 0; pass < BM / PR; ++pass) {
+      // (unconditional loads: the rows past the group repeat its last
+      // token, a column past NH reads column 0; neither is stored)
+      f32x4 y[MODE == MODE_DOWN_ROUTED ? NPR : 1];
+      if constexpr (MODE == MODE_DOWN_ROUTED) {
+        const int ycol = col < NH ? col : 0;
+#pragma unroll
+        for (int u = 0; u < NPR; ++u) {
+          y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (p.Y) y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orows[pass * PR + (tid >> 6) + 4 * u]) * NH + ycol);
+        }
+      }
       if (pass > 0) __syncthreads();      // the previous pass's chunks are read
       if (PR == BM || wm == pass) {
 #pragma unroll
@@ -470,37 +488,38 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
         }
       }
       __syncthreads();
-      for (int k0 = tid; k0 < PR * CPR; k0 += 256 * NB) {
-        f32x4 y[NB];
-        int orow[NB];
+      // every load of this pass has landed before the first store: the
+      // stores are conditional, and a wait placed by the compiler after one
+      // of them would also wait for the stores before it
+      wait_vmcnt<0>();
+      if constexpr (MODE == MODE_DOWN_ROUTED) {
+        if (p.out_bf16) {
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-          const int k = k0 + u * 256;
-          const int r = k / CPR, cc = k - r * CPR;
-          const int rt = pass * PR + r;
-          if constexpr (MODE == MODE_DOWN_ROUTED) orow[u] = reinterpret_cast<const lds_i32*>(As)[BM + rt];
-          else orow[u] = m0 + rt;
-          y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if constexpr (MODE == MODE_DOWN_ROUTED)
-            if (p.Y && m0 + rt < rows && n0 + cc * 4 < NH)
-              y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
-        }
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-          const int k = k0 + u * 256;
-          const int r = k / CPR, cc = k - r * CPR;
-          if (m0 + pass * PR + r >= rows || n0 + cc * 4 >= NH) continue;
-          const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
-          const int64_t o = static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4;
-          if constexpr (MODE == MODE_DOWN_SHARED) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + o) = v;
-          } else if (p.out_bf16) {
+          for (int u = 0; u < NPR; ++u) {
+            const int r = (tid >> 6) + 4 * u, rt = pass * PR + r;
+            if (m0 + rt >= rows || col >= NH) continue;
+            const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
             const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
             const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = make_uint2(lo, hi);
-          } else {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + o) = v;
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + static_cast<int64_t>(orows[rt]) * NH + col) =
+                make_uint2(lo, hi);
           }
+        } else {
+#pragma unroll
+          for (int u = 0; u < NPR; ++u) {
+            const int r = (tid >> 6) + 4 * u, rt = pass * PR + r;
+            if (m0 + rt >= rows || col >= NH) continue;
+            const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + static_cast<int64_t>(orows[rt]) * NH + col) = v;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NPR; ++u) {
+          const int r = (tid >> 6) + 4 * u, rt = pass * PR + r;
+          if (m0 + rt >= rows || col >= NH) continue;
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + static_cast<int64_t>(m0 + rt) * NH + col) =
+              *(const lds_f32x4*)(stage + r * FPB + cc * 16);
         }
       }
     }
@@ -551,7 +570,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[TNBUF * (TA_STAGE + TB_STAGE)];
   lds_u8* const As = (lds_u8*)(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
   const int wm = wave >> 1, wn = wave & 1;
   const int E = p.E, T = p.T, K = p.K;
 
@@ -869,15 +889,31 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(GemmArgs p) {
   } else {
     // scaled fp32 tile in two passes of 128 rows (one per wave row), then
     // 16-byte chunks: shared down stores them; routed down adds the shared
-    // expert's output, loaded for NB chunks at a time before they are stored
+    // expert's output.  Thread: chunk tid % 64 of pass rows tid / 64 + 4 u.
+    // The routed down loads its 32 chunks of that output for the pass before
+    // the pass's staging writes (unconditionally: the rows past the group
+    // repeat its last token, a column past NH reads column 0; neither is
+    // stored) and waits for them before the first store, as in the tiles
+    // above.
     constexpr int FPB = BN * 4 + 16;
     constexpr int PR = BM / 2;
     static_assert(TABB + PR * FPB <= TNBUF * (TA_STAGE + TB_STAGE), "fp32 staging fits the ring");
     constexpr int CPR = BN / 4;
-    constexpr int NB = 16;
-    static_assert((PR * CPR) % (256 * NB) == 0, "whole batches");
+    constexpr int NPR = PR * CPR / 256;   // 32
+    static_assert(CPR == 64 && (PR * CPR) % 256 == 0, "rows of 64 chunks, whole passes");
+    const int cc = tid & 63, col = n0 + cc * 4;
+    const lds_i32* const orows = reinterpret_cast<const lds_i32*>(As) + BM;
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
+      f32x4 y[MODE == MODE_DOWN_ROUTED ? NPR : 1];
+      if constexpr (MODE == MODE_DOWN_ROUTED) {
+        const int ycol = col < NH ? col : 0;
+#pragma unroll
+        for (int u = 0; u < NPR; ++u) {
+          y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (p.Y) y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orows[pass * PR + (tid >> 6) + 4 * u]) * NH + ycol);
+        }
+      }
       if (pass > 0) __syncthreads();      // the previous pass's chunks are read
       if (wm == pass) {
 #pragma unroll
@@ -897,37 +933,35 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(GemmArgs p) {
         }
       }
       __syncthreads();
-      for (int k0 = tid; k0 < PR * CPR; k0 += 256 * NB) {
-        f32x4 y[NB];
-        int orow[NB];
+      wait_vmcnt<0>();
+      if constexpr (MODE == MODE_DOWN_ROUTED) {
+        if (p.out_bf16) {
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-          const int k = k0 + u * 256;
-          const int r = k / CPR, cc = k - r * CPR;
-          const int rt = pass * PR + r;
-          if constexpr (MODE == MODE_DOWN_ROUTED) orow[u] = reinterpret_cast<const lds_i32*>(As)[BM + rt];
-          else orow[u] = m0 + rt;
-          y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if constexpr (MODE == MODE_DOWN_ROUTED)
-            if (p.Y && m0 + rt < rows && n0 + cc * 4 < NH)
-              y[u] = *reinterpret_cast<const f32x4*>(p.Y + static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4);
-        }
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-          const int k = k0 + u * 256;
-          const int r = k / CPR, cc = k - r * CPR;
-          if (m0 + pass * PR + r >= rows || n0 + cc * 4 >= NH) continue;
-          const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
-          const int64_t o = static_cast<int64_t>(orow[u]) * NH + n0 + cc * 4;
-          if constexpr (MODE == MODE_DOWN_SHARED) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + o) = v;
-          } else if (p.out_bf16) {
+          for (int u = 0; u < NPR; ++u) {
+            const int r = (tid >> 6) + 4 * u, rt = pass * PR + r;
+            if (m0 + rt >= rows || col >= NH) continue;
+            const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
             const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
             const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = make_uint2(lo, hi);
-          } else {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + o) = v;
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + static_cast<int64_t>(orows[rt]) * NH + col) =
+                make_uint2(lo, hi);
           }
+        } else {
+#pragma unroll
+          for (int u = 0; u < NPR; ++u) {
+            const int r = (tid >> 6) + 4 * u, rt = pass * PR + r;
+            if (m0 + rt >= rows || col >= NH) continue;
+            const f32x4 v = *(const lds_f32x4*)(stage + r * FPB + cc * 16) + y[u];
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + static_cast<int64_t>(orows[rt]) * NH + col) = v;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NPR; ++u) {
+          const int r = (tid >> 6) + 4 * u, rt = pass * PR + r;
+          if (m0 + rt >= rows || col >= NH) continue;
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C_shared) + static_cast<int64_t>(m0 + rt) * NH + col) =
+              *(const lds_f32x4*)(stage + r * FPB + cc * 16);
         }
       }
     }
