@@ -575,8 +575,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(GemmArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int E = p.E, T = p.T, K = p.K;
 
-  // ---- XCD-aware tile lookup (as in the tiles above)
-  const int nmt = (MODE == MODE_DOWN_SHARED) ? (T + BM - 1) / BM : p.tiles[p.group_hi] - p.tiles[p.group_lo];
+  // ---- XCD-aware tile lookup (as in the tiles above).  A launch of the
+  // shared group alone (group_lo == E) reads no tile tables, so it can run
+  // before the routing has written them.
+  const bool shared_only = MODE != MODE_DOWN_SHARED && p.group_lo == E;
+  const int nmt = (MODE == MODE_DOWN_SHARED || shared_only) ? (T + BM - 1) / BM
+                                                            : p.tiles[p.group_hi] - p.tiles[p.group_lo];
   const int gn = p.n_tiles;
   const int lid = blockIdx.x;
   int mt_rel, nt;
@@ -600,6 +604,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(GemmArgs p) {
   int g, m0, rows;
   if constexpr (MODE == MODE_DOWN_SHARED) {
     g = 0;
+    m0 = mt_rel * BM;
+    rows = T;
+  } else if (shared_only) {
+    g = E;
     m0 = mt_rel * BM;
     rows = T;
   } else {

@@ -785,7 +785,8 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
 // order on `stream`; the results are the same bit for bit.
 hipError_t enqueue_fp8_prefill(const moe_config& c, const moe_weights* w, void* out, uint8_t* ws, const WsLayout& L,
                                const Route& R, const void* xq, float* sx, uint32_t* amax_r, uint32_t* amax_s, int T,
-                               const AuxStream* aux, hipStream_t stream, hipEvent_t* ev) {
+                               const AuxStream* aux, hipStream_t stream, hipEvent_t* ev, bool shared_only = false,
+                               bool shared_enqueued = false) {
   hipError_t e;
   auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], stream) : hipSuccess; };
   const int E = c.n_experts;
@@ -824,11 +825,14 @@ hipError_t enqueue_fp8_prefill(const moe_config& c, const moe_weights* w, void* 
   };
   if (aux) {
     const hipStream_t a = aux->stream;
-    if ((e = hipEventRecord(aux->fork, stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(a, aux->fork, 0)) != hipSuccess) return e;
-    if ((e = shared_gateup(a)) != hipSuccess || (e = quant_s(a)) != hipSuccess || (e = shared_down(a)) != hipSuccess)
-      return e;
-    if ((e = hipEventRecord(aux->shared, a)) != hipSuccess) return e;
+    if (!shared_enqueued) {
+      if ((e = hipEventRecord(aux->fork, stream)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(a, aux->fork, 0)) != hipSuccess) return e;
+      if ((e = shared_gateup(a)) != hipSuccess || (e = quant_s(a)) != hipSuccess || (e = shared_down(a)) != hipSuccess)
+        return e;
+      if ((e = hipEventRecord(aux->shared, a)) != hipSuccess) return e;
+    }
+    if (shared_only) return hipSuccess;
     if ((e = routed_gateup(stream)) != hipSuccess || (e = quant_r(stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(stream, aux->shared, 0)) != hipSuccess) return e;
     if ((e = routed_down(stream)) != hipSuccess) return e;
@@ -1097,6 +1101,26 @@ static moe_status forward_enqueue(moe_plan_t plan, const void* x, int64_t T, con
     return e == hipSuccess ? MOE_OK : hip_fail(plan, e);
   }
   auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  // e4m3 prefill on two streams, x quantised by its own kernel: the shared
+  // expert reads only x's codes, so its launches (which address the shared
+  // group without tile tables) go to the side stream before the routing
+  if (f8 && aux && !c.has_norm && !R.logits_ready) {
+    uint8_t* xq = ws + L.xq;
+    float* sx = reinterpret_cast<float*>(ws + L.sx);
+    uint32_t* amax_r = reinterpret_cast<uint32_t*>(ws + L.amax_r);
+    uint32_t* amax_s = reinterpret_cast<uint32_t*>(ws + L.amax_s);
+    if ((e = TRACED("quant_x", 0, -1, 0, stream,
+                    launch_quant_x(static_cast<const uint16_t*>(x), Ti, c.d, xq, sx, stream))) != hipSuccess ||
+        (e = TRACED("fill", 0, -1, 0, stream, launch_fill_u32(amax_s, T, 0u, stream))) != hipSuccess ||
+        (e = TRACED("fill", 0, -1, 0, stream, launch_fill_u32(amax_r, T * c.top_k, 0u, stream))) != hipSuccess ||
+        (e = enqueue_fp8_prefill(c, w, out, ws, L, R, xq, sx, amax_r, amax_s, Ti, aux, stream, nullptr, true)) !=
+            hipSuccess ||
+        (e = enqueue_route(c, x, Ti, w, R, stream)) != hipSuccess ||
+        (e = enqueue_fp8_prefill(c, w, out, ws, L, R, xq, sx, amax_r, amax_s, Ti, aux, stream, nullptr, false, true)) !=
+            hipSuccess)
+      return hip_fail(plan, e);
+    return MOE_OK;
+  }
   if ((e = mark(0)) != hipSuccess) return hip_fail(plan, e);
   e = enqueue_route(c, x, Ti, w, R, stream);
   if (e != hipSuccess) return hip_fail(plan, e);
