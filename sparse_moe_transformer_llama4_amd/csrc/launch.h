@@ -125,7 +125,10 @@ hipError_t launch_perm(const int32_t* idx, const int32_t* base, const int32_t* o
 // The fixed-order finish of launch_router over `nsplit` partial logit slices
 // (used with nsplit = 1 when the logits come from the prefill GEMM).
 hipError_t launch_router_finish(const RouterArgs& a, int nsplit, const float* part, hipStream_t s);
-hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* sx, hipStream_t s);
+// Per-token e4m3 codes and scales of bf16 x; with zero_a /
+// zero_b also zero_a[t] = 0 and zero_b[t * kb + j] = 0 for j < kb.
+hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* sx, hipStream_t s,
+                          uint32_t* zero_a = nullptr, uint32_t* zero_b = nullptr, int kb = 0);
 // RMSNorm of x's rows into xn (x's dtype, DT_BF16 or DT_F32); with xq / sx
 // (bf16 only) also xn's per-token e4m3 codes and scales.
 hipError_t launch_rmsnorm(int x_dtype, const void* x, const void* w, int T, int d, float eps, void* xn,

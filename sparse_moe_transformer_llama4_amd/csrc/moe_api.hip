@@ -1110,9 +1110,8 @@ static moe_status forward_enqueue(moe_plan_t plan, const void* x, int64_t T, con
     uint32_t* amax_r = reinterpret_cast<uint32_t*>(ws + L.amax_r);
     uint32_t* amax_s = reinterpret_cast<uint32_t*>(ws + L.amax_s);
     if ((e = TRACED("quant_x", 0, -1, 0, stream,
-                    launch_quant_x(static_cast<const uint16_t*>(x), Ti, c.d, xq, sx, stream))) != hipSuccess ||
-        (e = TRACED("fill", 0, -1, 0, stream, launch_fill_u32(amax_s, T, 0u, stream))) != hipSuccess ||
-        (e = TRACED("fill", 0, -1, 0, stream, launch_fill_u32(amax_r, T * c.top_k, 0u, stream))) != hipSuccess ||
+                    launch_quant_x(static_cast<const uint16_t*>(x), Ti, c.d, xq, sx, stream, amax_s, amax_r,
+                                   c.top_k))) != hipSuccess ||
         (e = enqueue_fp8_prefill(c, w, out, ws, L, R, xq, sx, amax_r, amax_s, Ti, aux, stream, nullptr, true)) !=
             hipSuccess ||
         (e = enqueue_route(c, x, Ti, w, R, stream)) != hipSuccess ||

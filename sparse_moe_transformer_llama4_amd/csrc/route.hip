@@ -184,17 +184,61 @@ __global__ __launch_bounds__(64) void router_finish_kernel(RouterArgs a, int nsp
 }
 
 // Per-token e4m3 quantisation of x (bf16): s = fp32(max|x_t|) / 448 (1 for
-// a zero row), code = e4m3(x / s).  One wave per token row.
-__global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* x, int T, int d, uint8_t* xq,
-                                                      float* sx) {
+// a zero row), code = e4m3(x / s).  One wave per token row, the row held in
+// registers between the max and the quantisation when d <= 64 * 8 * NC
+// (NC > 0), else read twice (NC = 0).  With
+// zero_a / zero_b non-null it also clears the row's entries of the two max
+// |h| arrays the gate/up epilogues accumulate into: zero_a[t] and
+// zero_b[t * kb + j], j < kb.
+template <int NC>
+__global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* x, int T, int d, uint8_t* xq, float* sx,
+                                                      uint32_t* zero_a, uint32_t* zero_b, int kb) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  if (zero_a && lane == 0) zero_a[t] = 0u;
+  if (zero_b && lane < kb) zero_b[static_cast<int64_t>(t) * kb + lane] = 0u;
   const uint16_t* row = x + static_cast<int64_t>(t) * d;
+  uint8_t* qrow = xq + static_cast<int64_t>(t) * d;
+  if constexpr (NC == 0) {
+    float amax = 0.f;
+    for (int k = lane * 8; k < d; k += 64 * 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + k);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (lane == 0) sx[t] = s;
+    for (int k = lane * 8; k < d; k += 64 * 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + k);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        q[2 * i] = __uint_as_float(w[i] << 16) / s;
+        q[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) / s;
+      }
+      *reinterpret_cast<uint2*>(qrow + k) = make_uint2(e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7]));
+    }
+    return;
+  }
+  constexpr int NR = NC > 0 ? NC : 1;
+  uint4 v[NR];
+#pragma unroll
+  for (int c = 0; c < NR; ++c) {
+    const int k = (lane + 64 * c) * 8;
+    v[c] = k < d ? *reinterpret_cast<const uint4*>(row + k) : make_uint4(0u, 0u, 0u, 0u);
+  }
   float amax = 0.f;
-  for (int k = lane * 8; k < d; k += 64 * 8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(row + k);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int c = 0; c < NR; ++c) {
+    const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
@@ -205,10 +249,11 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* x, int T, 
   for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
   const float s = amax > 0.f ? amax / 448.0f : 1.0f;
   if (lane == 0) sx[t] = s;
-  uint8_t* qrow = xq + static_cast<int64_t>(t) * d;
-  for (int k = lane * 8; k < d; k += 64 * 8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(row + k);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int c = 0; c < NR; ++c) {
+    const int k = (lane + 64 * c) * 8;
+    if (k >= d) continue;
+    const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
     float q[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -761,8 +806,18 @@ hipError_t launch_perm(const int32_t* idx, const int32_t* base, const int32_t* o
   return hipGetLastError();
 }
 
-hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* sx, hipStream_t s) {
-  hipLaunchKernelGGL(quant_x_kernel, dim3((T + 3) / 4), dim3(256), 0, s, x, T, d, xq, sx);
+hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, float* sx, hipStream_t s, uint32_t* zero_a,
+                          uint32_t* zero_b, int kb) {
+  if (kb < 0 || kb > 64) return hipErrorInvalidValue;
+  const dim3 g((T + 3) / 4);
+  if (d <= 64 * 8 * 4)
+    hipLaunchKernelGGL(quant_x_kernel<4>, g, dim3(256), 0, s, x, T, d, xq, sx, zero_a, zero_b, kb);
+  else if (d <= 64 * 8 * 10)
+    hipLaunchKernelGGL(quant_x_kernel<10>, g, dim3(256), 0, s, x, T, d, xq, sx, zero_a, zero_b, kb);
+  else if (d <= 64 * 8 * 16)
+    hipLaunchKernelGGL(quant_x_kernel<16>, g, dim3(256), 0, s, x, T, d, xq, sx, zero_a, zero_b, kb);
+  else
+    hipLaunchKernelGGL(quant_x_kernel<0>, g, dim3(256), 0, s, x, T, d, xq, sx, zero_a, zero_b, kb);
   return hipGetLastError();
 }
 
