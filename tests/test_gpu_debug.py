@@ -20,11 +20,11 @@ needs_debug = pytest.mark.skipif(not os.path.exists(moe.DEBUG_LIB_PATH),
                                  reason="debug library not built (build.py --debug)")
 
 # one case per schedule: fp32 prefill, bf16 prefill (main / tail tiles, size
-# classes), e4m3 prefill, decode, two picks per token, a dense layer, the
-# RMSNorm in front
+# classes), e4m3 prefill (and with more than 32 experts, forked before the
+# routing), decode, two picks per token, a dense layer, the RMSNorm in front
 CASES = [("tiny_fp32", {}), ("small_bf16", {}), ("small_bf16_split", {}), ("small_bf16_tall", {}),
          ("small_fp8", {}), ("decode_like_bf16", {}), ("small_bf16", {"top_k": 2}), ("small_dense_bf16", {}),
-         ("small_bf16", {"norm_eps": 1e-5})]
+         ("small_bf16", {"norm_eps": 1e-5}), ("small_fp8", {"E": 40})]
 
 
 def _forward(cfg, w, dev):

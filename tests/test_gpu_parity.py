@@ -239,12 +239,16 @@ def test_decode_path_one_hot_and_idle_nan(gpu):
     check_forward(cfg, inp, out, routing)
 
 
-@pytest.mark.parametrize("name,T", [("decode_like_bf16", 33), ("small_bf16_split", None),
-                                    ("small_bf16_tall", None), ("wide_bf16_tall", None),
-                                    ("small_fp8", None), ("small_fp8", 1000)])
-def test_side_stream_matches_serial_schedule(gpu, name, T):
-    # Decode-sized bf16 calls run the shared expert's GEMMs, and bf16 prefill
-    # calls the shared expert and the routed groups' tails, on a side stream.  Same kernels and arguments as the serial schedule
+@pytest.mark.parametrize("name,T,over", [("decode_like_bf16", 33, {}), ("small_bf16_split", None, {}),
+                                         ("small_bf16_tall", None, {}), ("wide_bf16_tall", None, {}),
+                                         ("small_fp8", None, {}), ("small_fp8", 1000, {}),
+                                         ("small_fp8", None, dict(E=40)), ("small_fp8", 1000, dict(E=64))])
+def test_side_stream_matches_serial_schedule(gpu, name, T, over):
+    # Decode-sized bf16 calls run the shared expert's GEMMs, and prefill calls
+    # the shared expert (and, bf16, the routed groups' tails) on a side
+    # stream; e4m3 prefill with more than 32 experts (x quantised by its own
+    # kernel, E = 40: router kernels, E = 64: router GEMM) forks before the
+    # routing, its shared launches reading no tile tables.  Same kernels and arguments as the serial schedule
     # (moe_forward_timed): results must be identical bit for bit, also for
     # back-to-back calls with different inputs on a non-default stream,
     # sharing one workspace, with no host synchronisation in between (each
@@ -253,6 +257,8 @@ def test_side_stream_matches_serial_schedule(gpu, name, T):
     cfg = synth.get_config(name)
     if T is not None:
         cfg = dataclasses.replace(cfg, T=T, name=f"{name}_T{T}")
+    if over:
+        cfg = dataclasses.replace(cfg, name=f"{cfg.name}_E{over['E']}", **over)
     print(f"[parity] side stream {cfg.name}", flush=True)
     p = _plan(cfg)
     w = to_device(synth.make_inputs(cfg), gpu)
@@ -378,7 +384,7 @@ GRAPH_CASES = [("small_fp32", {}), ("small_fp8", {}), ("decode_like_bf16", {}), 
                ("decode_like_bf16", dict(top_k=2, T=33)), ("small_bf16_tall", dict(top_k=2)),
                ("small_bf16_tall", dict(norm_eps=1e-5)), ("small_fp8", dict(norm_eps=1e-5, top_k=2)),
                ("small_dense_bf16", dict(T=40)), ("small_dense_bf16", dict(T=300)),
-               ("small_fp8", dict(T=1000))]
+               ("small_fp8", dict(T=1000)), ("small_fp8", dict(E=40))]
 
 
 @pytest.mark.parametrize("name,over", GRAPH_CASES)
