@@ -29,8 +29,9 @@
  *     space is the caller's workspace, sized by moe_workspace_size.
  *   - All work is enqueued asynchronously on `stream` (hipStream_t; NULL =
  *     the default stream).  No host synchronisation, no device-to-host copy.
- *     moe_forward also uses a side stream for decode-sized bf16 calls
- *     (T <= 64) and for bf16 prefill-sized calls (T >= 256).  The plan
+ *     moe_forward also uses a side stream for decode-sized calls (T <= 64)
+ *     with bf16, int8 or int4 weights and for prefill-sized calls (T >= 256)
+ *     with bf16 or e4m3 weights.  The plan
  *     creates it for the current device on first use (non-blocking, default
  *     priority): it waits for `stream` before its first kernel and `stream`
  *     waits for it before the call's last kernel, so for the caller the whole
