@@ -155,21 +155,67 @@ __device__ __forceinline__ void topk_push(TopK& b, float x, int e, int k) {
 // (lowest index among equal logits), sigmoid gate of each pick, and the
 // per-workgroup histogram of picks (64 tokens per workgroup, the blocking
 // the permutation uses).  Token t's j-th pick is slot t * k + j.
-__global__ __launch_bounds__(64) void router_finish_kernel(RouterArgs a, int nsplit, const float* part) {
+// The workgroup's 64 x E logits are first staged in LDS by coalesced loads,
+// several in flight per thread (one thread walking its token's row with
+// dependent global loads took ~60 us per workgroup at E = 128).  Wave q then
+// ranks quarter q of every token's experts, and wave 0 pushes the other
+// quarters' rankings, best first and in quarter order, into its own: every
+// entry of a later quarter has a higher index than those of the earlier
+// ones, so among equal logits the lower index stays ahead, and the result is
+// the ranking of the whole row.
+constexpr int kFinishPitch = 257;   // floats per staged row: the 64 lanes of a wave read distinct banks
+__global__ __launch_bounds__(256) void router_finish_kernel(RouterArgs a, int nsplit, const float* part) {
+  __shared__ float lg[kRouteTokens * kFinishPitch];
+  __shared__ float qv[3][kRouteTokens][kMaxTopK];
+  __shared__ int qi[3][kRouteTokens][kMaxTopK];
   __shared__ int hist[256];
+  const int tid = threadIdx.x;
   const int E = a.E, T = a.T, k = a.k;
-  for (int e = threadIdx.x; e < E; e += 64) hist[e] = 0;
-  __syncthreads();
-  const int t = blockIdx.x * kRouteTokens + threadIdx.x;
-  if (t < T) {
-    TopK b;
-    topk_init(b);
-    for (int e = 0; e < E; ++e) {
-      float v = 0.f;
-      for (int s = 0; s < nsplit; ++s) v += part[(static_cast<int64_t>(s) * T + t) * E + e];
-      if (a.bias) v += a.bias[e];
-      topk_push(b, v, e, k);
+  const int t0 = blockIdx.x * kRouteTokens;
+  const int nt = min(kRouteTokens, T - t0);
+  const int n = nt * E;   // this block's logits: part[s][t0 * E + i], i < n
+  hist[tid] = 0;
+  for (int i0 = tid; i0 < n; i0 += 4 * 256) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nsplit; ++s) {
+      const float* ps = part + (static_cast<int64_t>(s) * T + t0) * E;
+      float x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = i0 + 256 * u < n ? ps[i0 + 256 * u] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] += x[u];
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 256 * u;
+      if (i < n) {
+        const int r = i / E, e = i - r * E;
+        float y = v[u];
+        if (a.bias) y += a.bias[e];
+        lg[r * kFinishPitch + e] = y;
+      }
+    }
+  }
+  __syncthreads();
+  const int q = tid >> 6, r = tid & 63;
+  const int seg = (E + 3) >> 2;
+  const int e0 = min(E, q * seg), e1 = min(E, e0 + seg);
+  TopK b;
+  topk_init(b);
+  if (r < nt)
+    for (int e = e0; e < e1; ++e) topk_push(b, lg[r * kFinishPitch + e], e, k);
+  if (q > 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      qv[q - 1][r][j] = b.v[j];
+      qi[q - 1][r][j] = b.i[j];
+    }
+  }
+  __syncthreads();
+  if (q == 0 && r < nt) {
+    for (int qq = 0; qq < 3; ++qq)
+      for (int j = 0; j < k; ++j) topk_push(b, qv[qq][r][j], qi[qq][r][j], k);
+    const int t = t0 + r;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j >= k) break;
@@ -180,7 +226,7 @@ __global__ __launch_bounds__(64) void router_finish_kernel(RouterArgs a, int nsp
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 64) a.hist[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
+  if (tid < E) a.hist[static_cast<int64_t>(blockIdx.x) * E + tid] = hist[tid];
 }
 
 // Per-token e4m3 quantisation of x (bf16): s = fp32(max|x_t|) / 448 (1 for
@@ -765,7 +811,7 @@ static hipError_t launch_partials(const RouterArgs& a, int x_dtype, float* part,
 
 hipError_t launch_router_finish(const RouterArgs& a, int nsplit, const float* part, hipStream_t s) {
   const int nb = (a.T + kRouteTokens - 1) / kRouteTokens;
-  hipLaunchKernelGGL(router_finish_kernel, dim3(nb), dim3(kRouteTokens), 0, s, a, nsplit, part);
+  hipLaunchKernelGGL(router_finish_kernel, dim3(nb), dim3(256), 0, s, a, nsplit, part);
   return hipGetLastError();
 }
 
@@ -774,7 +820,7 @@ hipError_t launch_router(const RouterArgs& a, int x_dtype, float* part, hipStrea
   const int ns = router_splits(a.T, a.d, x_dtype);
   hipError_t e = launch_partials(a, x_dtype, part, ns, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(router_finish_kernel, dim3(nb), dim3(kRouteTokens), 0, s, a, ns, part);
+  hipLaunchKernelGGL(router_finish_kernel, dim3(nb), dim3(256), 0, s, a, ns, part);
   return hipGetLastError();
 }
 
