@@ -30,11 +30,18 @@ FLAGS = [
 ]
 
 
-# Per-unit code generation.  The 64- and 128-row bf16 GEMM tiles keep their
-# accumulators in VGPRs (VGPR-form MFMAs): with the AGPR form the register
-# allocator copied them between registers on every main-loop iteration.
+# Per-unit code generation.  The 64- and 128-row bf16 GEMM tiles, the
+# weight-streaming decode kernels, the router partials and the fp32 MFMA
+# GEMMs keep their accumulators in VGPRs (VGPR-form MFMAs): with the AGPR form
+# the register allocator copied them between registers, and in the decode
+# kernels parked other values in AGPRs, inside the main loops.  The 256-row
+# tiles need both register files (with the VGPR form they spill).
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 UNIT_FLAGS = {
-    "gemm_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "gemm_bf16.hip": _VGPR_FORM,
+    "gemm_decode.hip": _VGPR_FORM,
+    "route.hip": _VGPR_FORM,
+    "gemm.hip": _VGPR_FORM,
 }
 
 
