@@ -81,7 +81,7 @@ def launch_work(cfg, counts, rec):
     sc = 4 if cfg.w_dtype in ("e4m3", "i8", "i4") else 0
     fp8 = cfg.w_dtype == "e4m3"
     xin = 1 if fp8 else xb                    # the gate/up reads x's e4m3 codes
-    hout = 4 if cfg.w_dtype in ("f32", "e4m3") else 2   # h as the gate/up writes it (e4m3: fp32 staging)
+    hout = {"f32": 4, "e4m3": 3}.get(cfg.w_dtype, 2)   # h as the gate/up writes it (bf16; e4m3: 24 bits)
     hin = 1 if fp8 else hout                  # h as the down GEMMs read it (e4m3: its codes)
     rows = [split_rows(int(n), bm, part) for n in counts]
     R = sum(rows)
@@ -122,7 +122,7 @@ def launch_work(cfg, counts, rec):
         B = T * d * xb + T * d + 4 * T
     elif name == "quant_h":
         r_, n_ = (R, f) if groups == 0 else (T, fs)
-        B = r_ * n_ * 4 + r_ * n_ + r_ * 8
+        B = r_ * n_ * 3 + r_ * n_ + r_ * 8      # 24-bit h in, e4m3 codes and the row scale out
     elif name == "combine":
         B = 2 * T * d * 4 + T * d * ob
     elif name == "combine_topk":

@@ -110,7 +110,8 @@ struct WsLayout {
   size_t hist;                              // int32 [nblocks_route][E] -> per-block bases
   size_t logits;                            // fp32 [router splits][T][E] partial router logits
   size_t tiles;                             // int32 [kNumTables][E + 2] tile tables
-  size_t h_r, h_s;                          // SwiGLU outputs (bf16 / f32; bf16 staging for e4m3)
+  size_t h_r, h_s;                          // SwiGLU outputs (bf16 / f32; e4m3: bits 31..16 of fp32 h)
+  size_t h_r_lo, h_s_lo;                    // e4m3 only: bits 15..8 of fp32 h, one byte per element
   size_t hq_r, hq_s;                        // e4m3 codes of h (e4m3 only)
   size_t sh_r, sh_s;                        // per-row fp32 scales of h (e4m3 only)
   size_t amax_r, amax_s;                    // per-row max |h| as uint bits (e4m3 only)

@@ -269,9 +269,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
             const int64_t o = static_cast<int64_t>(orow) * NH + col;
             if constexpr (DT == DT_BF16) {
               reinterpret_cast<uint16_t*>(C)[o] = f32_to_bf16(h);
-            } else {
-              // fp32 h; e4m3 rows are quantised afterwards from these values
+            } else if constexpr (DT == DT_F32) {
               reinterpret_cast<float*>(C)[o] = h;
+            } else {
+              // 24-bit h (the fp32 pattern rounded at bit 8: bits 31..16,
+              // then 15..8); e4m3 rows are quantised afterwards from these
+              // values, with the scale from the max of the fp32 values
+              const uint32_t hb = __float_as_uint(h) + 0x80u;
+              reinterpret_cast<uint16_t*>(C)[o] = static_cast<uint16_t>(hb >> 16);
+              (shared ? p.C_shared_lo : p.C_lo)[o] = static_cast<uint8_t>(hb >> 8);
               rmax = fmaxf(rmax, fabsf(h));
             }
           }

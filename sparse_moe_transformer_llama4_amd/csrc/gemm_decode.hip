@@ -585,7 +585,8 @@ __device__ __forceinline__ bf16x8 q_to_bf16(i32x2 q) {
     const int sh = 16 * (i & 1);
     const float lo = static_cast<float>(static_cast<int8_t>(w >> sh));
     const float hi = static_cast<float>(static_cast<int8_t>(w >> (sh + 8)));
-    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    // the upper halves of both (one byte permute): lo's in bits 0..15, hi's above
+    o[i] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
   }
   typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
   const u32x4 v = {o[0], o[1], o[2], o[3]};

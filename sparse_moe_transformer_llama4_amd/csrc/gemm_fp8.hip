@@ -80,6 +80,20 @@ __device__ __forceinline__ float row16_max(float v) {
 }
 
 
+// Four fp32 h values in the 24-bit form the quantisation pass reads: each
+// value's bit pattern rounded at bit 8 (half a unit added to the magnitude,
+// the low 8 bits then dropped), bits 31..16 (four uint16, in order) to `hi`,
+// bits 15..8 (four bytes) to `lo`.
+__device__ __forceinline__ void store_h24(uint16_t* hi, uint8_t* lo, f32x4 v) {
+  const uint32_t b0 = __float_as_uint(v[0]) + 0x80u, b1 = __float_as_uint(v[1]) + 0x80u,
+                 b2 = __float_as_uint(v[2]) + 0x80u, b3 = __float_as_uint(v[3]) + 0x80u;
+  *reinterpret_cast<uint2*>(hi) = make_uint2(__builtin_amdgcn_perm(b1, b0, 0x07060302u),
+                                             __builtin_amdgcn_perm(b3, b2, 0x07060302u));
+  *reinterpret_cast<uint32_t*>(lo) =
+      __builtin_amdgcn_perm(__builtin_amdgcn_perm(b3, b2, 0x00000501u), __builtin_amdgcn_perm(b1, b0, 0x00000501u),
+                            0x05040100u);
+}
+
 // BM = 128 or 160 rows (the 160-row gate/up tile takes a group of up to 160
 // rows whole where 128-row tiles would add a second, nearly empty tile)
 template <int MODE, int BM>
@@ -389,8 +403,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
     // h tile [BM][BNH] fp32 (row pitch HP bytes) and each row's max |h|: over
     // this lane's HF columns, then over the 16 lanes of the row (DPP), then
     // over the two waves of the row (LDS atomic max on the bit patterns of
-    // non-negative floats); then 16-byte chunks to global memory and one
-    // atomic per row.  Columns past NH hold h = 0 (zero column scales).
+    // non-negative floats); then rows to global memory in 24 bits (the max
+    // is that of the fp32 values) and one atomic per row.  Columns past NH
+    // hold h = 0 (zero column scales).
     constexpr int HF = FN / 2;
     constexpr int HP = BNH * 4 + 16;
     static_assert(TABB + BM * HP <= NBUF * (A_STAGE + B_STAGE), "h staging fits the ring");
@@ -421,13 +436,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
         for (int q = 0; q < 4; ++q) atomicMax(rmax + wrow + i * 16 + q, __float_as_uint(mx[i][q]));
     }
     __syncthreads();
-    constexpr int CPR = BNH / 4;          // 16-byte chunks per row (32)
+    constexpr int CPR = BNH / 4;          // 4-column chunks per row (32)
     static_assert((BM * CPR) % 256 == 0, "whole passes");
-    float* C = reinterpret_cast<float*>(shared ? p.C_shared : p.C);
+    uint16_t* C = reinterpret_cast<uint16_t*>(shared ? p.C_shared : p.C);
+    uint8_t* Clo = shared ? p.C_shared_lo : p.C_lo;
     uint32_t* amax = shared ? p.amax_shared : p.amax;
     if (tid < BM && m0 + tid < rows)
       atomicMax(&amax[row_base + m0 + tid], reinterpret_cast<const lds_u32*>(As)[2 * BM + tid]);
-    // thread: chunk tid % 32 of rows tid / 32 + 8 u, NU rows read before any is stored
+    // thread: chunk tid % 32 of rows tid / 32 + 8 u, NU rows read before any
+    // is stored; each chunk leaves in the 24-bit form (8 + 4 bytes)
     constexpr int NPASS = BM * CPR / 256, NU = NPASS % 8 == 0 ? 8 : 5;
     static_assert(CPR == 32 && NPASS % NU == 0, "whole batches of rows");
     const int cc = tid & 31, col = n0 + cc * 4;
@@ -439,8 +456,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs p) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int r = (tid >> 5) + 8 * (u0 + u);
-        if (m0 + r < rows && col < NH)
-          *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row_base + m0 + r) * NH + col) = v[u];
+        if (m0 + r < rows && col < NH) {
+          const int64_t o = static_cast<int64_t>(row_base + m0 + r) * NH + col;
+          store_h24(C + o, Clo + o, v[u]);
+        }
       }
     }
   } else {
@@ -841,8 +860,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(GemmArgs p) {
     // h tile [256][128] fp32 (row pitch HP) and each row's max |h|: over this
     // lane's two columns, over the 16 lanes of its DPP row (DPP), then over
     // the two DPP rows and two waves that share the tile row (LDS atomic max
-    // on the bit patterns of non-negative floats); then 16-byte chunks to
-    // global memory and one atomic per row.  Columns past NH hold h = 0.
+    // on the bit patterns of non-negative floats); then rows to global memory
+    // in 24 bits (the max is that of the fp32 values) and one atomic per row.
+    // Columns past NH hold h = 0.
     constexpr int HP = BNH * 4 + 16;
     static_assert(TABB + BM * HP <= TNBUF * (TA_STAGE + TB_STAGE), "h staging fits the ring");
     uint32_t* const rmax = reinterpret_cast<uint32_t*>(smem) + 2 * BM;
@@ -875,11 +895,13 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(GemmArgs p) {
       }
     }
     __syncthreads();
-    constexpr int CPR = BNH / 4;          // 32 chunks per row
-    float* C = reinterpret_cast<float*>(shared ? p.C_shared : p.C);
+    constexpr int CPR = BNH / 4;          // 32 chunks of 4 columns per row
+    uint16_t* C = reinterpret_cast<uint16_t*>(shared ? p.C_shared : p.C);
+    uint8_t* Clo = shared ? p.C_shared_lo : p.C_lo;
     uint32_t* amax = shared ? p.amax_shared : p.amax;
     if (m0 + tid < rows) atomicMax(&amax[row_base + m0 + tid], reinterpret_cast<const lds_u32*>(As)[2 * BM + tid]);
-    // thread: chunk tid % 32 of rows tid / 32 + 8 u, 8 rows read before any is stored
+    // thread: chunk tid % 32 of rows tid / 32 + 8 u, 8 rows read before any
+    // is stored; each chunk leaves in the 24-bit form (8 + 4 bytes)
     static_assert(CPR == 32, "a row's chunks are 32 consecutive threads");
     const int cc = tid & 31, col = n0 + cc * 4;
 #pragma unroll
@@ -890,8 +912,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(GemmArgs p) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int r = (tid >> 5) + 8 * (u0 + u);
-        if (m0 + r < rows && col < NH)
-          *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row_base + m0 + r) * NH + col) = v[u];
+        if (m0 + r < rows && col < NH) {
+          const int64_t o = static_cast<int64_t>(row_base + m0 + r) * NH + col;
+          store_h24(C + o, Clo + o, v[u]);
+        }
       }
     }
   } else {

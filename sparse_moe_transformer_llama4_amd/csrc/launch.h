@@ -80,6 +80,8 @@ struct GemmArgs {
   const float* gate;     // [T] by token
   void* C;               // GATEUP: h_r [T][f]; DOWN_ROUTED: out [T][d]; DOWN_SHARED: y_s
   void* C_shared;        // GATEUP: h_s [T][fs]
+  uint8_t* C_lo;         // e4m3 GATEUP: h is stored in 24 bits (each fp32 pattern rounded at bit 8), bits
+  uint8_t* C_shared_lo;  // 31..16 in C (uint16) and bits 15..8 here (one byte per element, same indexing)
   const float* Y;        // DOWN_ROUTED: y_s [T][d]
   uint32_t* amax;        // e4m3 GATEUP: per-row max |h| bits (routed rows)
   uint32_t* amax_shared;
@@ -147,8 +149,8 @@ hipError_t launch_norm_route(const void* x, const void* w, int T, int d, int E, 
 // offsets, tile tables and the permutation in one workgroup.
 hipError_t launch_route_small_finish(const RouterArgs& a, const float* logits, int32_t* counts, int32_t* offsets,
                                      int32_t* tiles, int32_t* perm, hipStream_t s);
-hipError_t launch_quant_h(const float* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
-                          float* sh, hipStream_t s);
+hipError_t launch_quant_h(const uint16_t* h, const uint8_t* h_lo, const uint32_t* amax, int rows, int n,
+                          uint8_t* hq, float* sh, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 // Debug builds: check every routing invariant the GEMMs rely on (expert
 // indices, offsets against counts, perm grouped by expert in slot order,

@@ -168,7 +168,9 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   const size_t t = static_cast<size_t>(T);
   const size_t nb = (t + kRouteTokens - 1) / kRouteTokens;
   const bool fp8 = c.w_dtype == MOE_E4M3;
-  const size_t hsz = (c.w_dtype == MOE_BF16 || int_weights(c)) ? 2 : 4;  // e4m3: fp32 staging
+  // h: fp32 for fp32 weights, else bf16; e4m3: 24 bits in two planes (the
+  // upper 16 bits of the fp32 value here, the next 8 in h_r_lo / h_s_lo)
+  const size_t hsz = c.w_dtype == MOE_F32 ? 4 : 2;
   const size_t ts = t * static_cast<size_t>(c.top_k > 1 ? c.top_k : 1);   // routing slots (routed rows)
   L.idx = take(ts * 4);
   L.gate = take(ts * 4);
@@ -188,6 +190,8 @@ WsLayout layout_for(const moe_config& c, int64_t T) {
   if (c.has_norm) L.x_n = take(t * c.d * (c.x_dtype == MOE_F32 ? 4 : 2));
   if (fused_norm_route(c)) L.wr_pack = take(norm_route_pack_bytes(c.d, c.n_experts));
   if (fp8) {
+    L.h_r_lo = take(ts * c.f);
+    L.h_s_lo = take(t * c.f_shared);
     L.hq_r = take(ts * c.f);
     L.hq_s = take(t * c.f_shared);
     L.sh_r = take(ts * 4);
@@ -409,6 +413,10 @@ GemmArgs gateup_args(const moe_config& c, const moe_weights* w, uint8_t* ws, con
   g.gate = R.gate;
   g.C = ws + L.h_r;
   g.C_shared = ws + L.h_s;
+  if (fp8) {
+    g.C_lo = ws + L.h_r_lo;
+    g.C_shared_lo = ws + L.h_s_lo;
+  }
   g.amax = amax_r;
   g.amax_shared = amax_s;
   return g;
@@ -775,8 +783,9 @@ hipError_t enqueue_bf16_prefill(const moe_config& c, const void* x, int T, const
 // takes a group whole; else 128): they stream each expert's weights once
 // from HBM.  The shared expert's gate/up and down GEMMs are MFMA-bound and
 // take the 256 x 256 tiles.  h is quantised per row to e4m3 between the two
-// GEMMs of each expert (from its fp32 values and the row max the gate/up
-// epilogue gathered), and the routed down epilogue adds the shared output.
+// GEMMs of each expert (from the 24-bit h the gate/up epilogue stores, with
+// the scale from the max of the fp32 values it gathered), and the routed down
+// epilogue adds the shared output.
 // With a side stream the shared expert's three launches run there, next to
 // the routed gate/up:
 //   side: [fork] shared gate/up -> quantise h_s -> shared down -> (done)
@@ -809,12 +818,12 @@ hipError_t enqueue_fp8_prefill(const moe_config& c, const moe_weights* w, void* 
   };
   auto quant_r = [&](hipStream_t s) {
     return TRACED("quant_h", 0, 0, 0, s,
-                  launch_quant_h(reinterpret_cast<const float*>(ws + L.h_r), amax_r, T * c.top_k, c.f, ws + L.hq_r,
+                  launch_quant_h(reinterpret_cast<const uint16_t*>(ws + L.h_r), ws + L.h_r_lo, amax_r, T * c.top_k, c.f, ws + L.hq_r,
                                  sh_r, s));
   };
   auto quant_s = [&](hipStream_t s) {
     return TRACED("quant_h", 0, 1, 0, s,
-                  launch_quant_h(reinterpret_cast<const float*>(ws + L.h_s), amax_s, T, c.f_shared, ws + L.hq_s, sh_s,
+                  launch_quant_h(reinterpret_cast<const uint16_t*>(ws + L.h_s), ws + L.h_s_lo, amax_s, T, c.f_shared, ws + L.hq_s, sh_s,
                                  s));
   };
   auto shared_down = [&](hipStream_t s) {
@@ -1184,11 +1193,11 @@ static moe_status forward_enqueue(moe_plan_t plan, const void* x, int64_t T, con
     sh_r = reinterpret_cast<float*>(ws + L.sh_r);
     sh_s = reinterpret_cast<float*>(ws + L.sh_s);
     if ((e = TRACED("quant_h", 0, 0, 0, stream,
-                    launch_quant_h(reinterpret_cast<const float*>(ws + L.h_r), amax_r, Ti * c.top_k, c.f, ws + L.hq_r,
+                    launch_quant_h(reinterpret_cast<const uint16_t*>(ws + L.h_r), ws + L.h_r_lo, amax_r, Ti * c.top_k, c.f, ws + L.hq_r,
                                    sh_r, stream))) != hipSuccess)
       return hip_fail(plan, e);
     if ((e = TRACED("quant_h", 0, 1, 0, stream,
-                    launch_quant_h(reinterpret_cast<const float*>(ws + L.h_s), amax_s, Ti, c.f_shared, ws + L.hq_s,
+                    launch_quant_h(reinterpret_cast<const uint16_t*>(ws + L.h_s), ws + L.h_s_lo, amax_s, Ti, c.f_shared, ws + L.hq_s,
                                    sh_s, stream))) != hipSuccess)
       return hip_fail(plan, e);
     h_r = ws + L.hq_r;

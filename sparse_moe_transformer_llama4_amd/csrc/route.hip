@@ -497,10 +497,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
   }
 }
 
-// Per-row e4m3 quantisation of fp32 h rows with a precomputed row max:
-// s = max|h| / 448 (1 for a zero row), code = e4m3(h / s).
-__global__ __launch_bounds__(256) void quant_h_kernel(const float* h, const uint32_t* amax, int rows,
-                                                      int n, uint8_t* hq, float* sh) {
+// Per-row e4m3 quantisation of h with the row max the gate/up epilogues
+// gathered from its fp32 values: s = max|h| / 448 (1 for a zero row), code =
+// e4m3(h / s).  h arrives in 24 bits (each fp32 pattern rounded at bit 8:
+// bits 31..16 in `h`, bits 15..8 in `h_lo`), a relative change of at most
+// 2^-16, below the fp8 MFMA's own accumulation error.
+__global__ __launch_bounds__(256) void quant_h_kernel(const uint16_t* h, const uint8_t* h_lo, const uint32_t* amax,
+                                                      int rows, int n, uint8_t* hq, float* sh) {
   const int r = blockIdx.x;
   if (r >= rows) return;
   const float am = __uint_as_float(amax[r]);
@@ -508,12 +511,19 @@ __global__ __launch_bounds__(256) void quant_h_kernel(const float* h, const uint
   if (blockIdx.y == 0 && threadIdx.x == 0) sh[r] = s;
   const int k = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (k >= n) return;
-  const float* src = h + static_cast<int64_t>(r) * n + k;
-  const float4 v0 = *reinterpret_cast<const float4*>(src);
-  const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-  const uint32_t lo = e4m3x4(v0.x / s, v0.y / s, v0.z / s, v0.w / s);
-  const uint32_t hi = e4m3x4(v1.x / s, v1.y / s, v1.z / s, v1.w / s);
-  *reinterpret_cast<uint2*>(hq + static_cast<int64_t>(r) * n + k) = make_uint2(lo, hi);
+  const int64_t o = static_cast<int64_t>(r) * n + k;
+  const uint4 v = *reinterpret_cast<const uint4*>(h + o);
+  const uint2 b = *reinterpret_cast<const uint2*>(h_lo + o);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t lb[2] = {b.x, b.y};
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t hi = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    const uint32_t lo = (lb[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    y[i] = __uint_as_float((hi << 16) | (lo << 8)) / s;
+  }
+  *reinterpret_cast<uint2*>(hq + o) = make_uint2(e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7]));
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
@@ -891,9 +901,9 @@ hipError_t launch_rmsnorm(int x_dtype, const void* x, const void* w, int T, int 
   return hipGetLastError();
 }
 
-hipError_t launch_quant_h(const float* h, const uint32_t* amax, int rows, int n, uint8_t* hq,
-                          float* sh, hipStream_t s) {
-  hipLaunchKernelGGL(quant_h_kernel, dim3(rows, (n + 2047) / 2048), dim3(256), 0, s, h, amax, rows, n,
+hipError_t launch_quant_h(const uint16_t* h, const uint8_t* h_lo, const uint32_t* amax, int rows, int n,
+                          uint8_t* hq, float* sh, hipStream_t s) {
+  hipLaunchKernelGGL(quant_h_kernel, dim3(rows, (n + 2047) / 2048), dim3(256), 0, s, h, h_lo, amax, rows, n,
                      hq, sh);
   return hipGetLastError();
 }
