@@ -64,6 +64,17 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
 __device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_base), "v"(g) : "memory", "m0");
 }
+// Scalar-base forms (the int8 / int4 tiles): `sbase` is wave-uniform (an
+// SGPR pair) and each lane adds its own 32-bit byte offset, so advancing
+// along K is a scalar add per stage and no lane computes a 64-bit address.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_s_nt(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ bf16x8 read_w_frag(const lds_u8* st, int kb, int col, int lane) {
   const int s = lane & 15;
@@ -604,8 +615,10 @@ __device__ __forceinline__ bf16x8 q_to_bf16(i32x2 q) {
 // after the K loop.
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4q;
 __device__ __forceinline__ bf16x8 q4_to_bf16_off(int w) {
-  const uint32_t b = static_cast<uint32_t>(w) ^ 0x88888888u;
-  const uint32_t ev = b & 0x0F0F0F0Fu, od = (b >> 4) & 0x0F0F0F0Fu;
+  // (mask, then flip each nibble's top bit: one three-input bit operation for
+  // the even nibbles, a shift and one for the odd ones)
+  const uint32_t b = static_cast<uint32_t>(w);
+  const uint32_t ev = (b & 0x0F0F0F0Fu) ^ 0x08080808u, od = ((b >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
   constexpr uint32_t kHi = 0x43434343u;
   const u32x4q o = {__builtin_amdgcn_perm(kHi, ev, 0x04010400u), __builtin_amdgcn_perm(kHi, ev, 0x04030402u),
                     __builtin_amdgcn_perm(kHi, od, 0x04010400u), __builtin_amdgcn_perm(kHi, od, 0x04030402u)};
@@ -692,7 +705,7 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
   const int u0 = static_cast<int>(blockIdx.z) * units / nsplit;
   const int u1 = (static_cast<int>(blockIdx.z) + 1) * units / nsplit;
   const int ns = u1 - u0;                       // stages per wave
-  const int k0 = u0 * 4 * KPS + wave * ns * KPS;
+  const int k0 = u0 * 4 * KPS + __builtin_amdgcn_readfirstlane(wave) * ns * KPS;   // wave-uniform
 
   // weights: DMA instruction i fills K rows 4i .. 4i+3 of the stage; lane ->
   // row 4i + lane/16, physical chunk lane%16 holding logical chunk
@@ -700,16 +713,19 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
   // 0..7 the gate columns n0 + 16c, 8..15 the up columns NH + n0 + 16 (c-8)
   // (int4: byte rows are pairs of K rows)
   const int kb0 = QB == 8 ? k0 : k0 / 2;         // first byte row of this wave
+  // scalar base: the group's weights from this wave's first byte row; lane
+  // offsets within a stage (< QBK + 1 rows) stay in 32 bits
   const uint8_t* wbase = static_cast<const uint8_t*>(shared ? p.B_shared : p.B) +
-                         (shared ? 0 : static_cast<int64_t>(g) * (QB == 8 ? K : K / 2) * ldb);
-  int64_t w_off[QINS];
+                         (shared ? 0 : static_cast<int64_t>(g) * (QB == 8 ? K : K / 2) * ldb) +
+                         static_cast<int64_t>(kb0) * ldb;
+  uint32_t w_off[QINS];
 #pragma unroll
   for (int i = 0; i < QINS; ++i) {
     const int kr = 4 * i + (lane >> 4);
     const int c = (lane & 15) ^ (kr & 15);
     const int oc = GU ? n0 + 16 * (c & 7) : n0 + 16 * c;       // output column of the chunk
     const int gc = (GU && c >= 8) ? NH + oc : oc;              // weight column
-    w_off[i] = static_cast<int64_t>(kb0 + kr) * ldb + (oc < NH ? gc : 0);
+    w_off[i] = static_cast<uint32_t>(kr * ldb + (oc < NH ? gc : 0));
   }
   const int64_t w_kstride = static_cast<int64_t>(QBK) * ldb;
 
@@ -719,8 +735,10 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
   // 2f, 2f+1 fill rows 16f + 8i + lane/8 (128 B each), slot lane%8 holding
   // logical chunk slot ^ (row & 7).  GATEUP reads x (routed rows gathered
   // through perm), DOWN the h rows in group order.
-  const uint16_t* abase = static_cast<const uint16_t*>(shared ? p.A_shared : p.A);
-  int64_t a_off[FMMAX * AINS];
+  // (scalar base: the A matrix from this wave's first K column; lane byte
+  // offsets row * 2K + 2 (chunk * 8), at most 64 * top_k rows)
+  const uint8_t* abase = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(shared ? p.A_shared : p.A) + k0);
+  uint32_t a_off[FMMAX * AINS];
 #pragma unroll
   for (int f = 0; f < FMMAX; ++f)
 #pragma unroll
@@ -730,7 +748,7 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
       const int lc = QB == 8 ? (slot ^ ((tr >> 1) & 3)) : (slot ^ (tr & 7));
       const int r = min(m0 + 16 * f + tr, rows - 1);
       const int arow = (GU && !shared) ? slot_token(p.perm[row_base + r], p.top_k) : row_base + r;
-      a_off[f * AINS + i] = static_cast<int64_t>(arow) * K + k0 + lc * 8;
+      a_off[f * AINS + i] = static_cast<uint32_t>((static_cast<int64_t>(arow) * K + lc * 8) * 2);
     }
 
   const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem)) +
@@ -758,10 +776,12 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs p) {
   do {                                                                                         \
     const int s_ = min((st), ns - 1);                                                          \
     const uint32_t b_ = ring + static_cast<uint32_t>(((st) % DNBUF) * STAGE);                  \
+    const uint8_t* const wst_ = wbase + s_ * w_kstride;                                        \
+    const uint8_t* const ast_ = abase + s_ * (KPS * 2);                                        \
     _Pragma("unroll") for (int i = 0; i < QINS; ++i)                                           \
-      dma16_nt(wbase + w_off[i] + s_ * w_kstride, b_ + i * 1024);                              \
+      dma16_s_nt(wst_, w_off[i], b_ + i * 1024);                                               \
     _Pragma("unroll") for (int f = 0; f < FMMAX * AINS; ++f)                                   \
-      dma16(abase + a_off[f] + s_ * KPS, b_ + QWSTAGE + f * 1024);                             \
+      dma16_s(ast_, a_off[f], b_ + QWSTAGE + f * 1024);                                        \
   } while (0)
 #define Q8_STEP(kt)                                                                            \
   do {                                                                                         \
