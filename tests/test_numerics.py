@@ -140,8 +140,8 @@ def test_e4m3_codes_from_24bit_h_match_fp32_but_not_from_bf16():
     a code differs from the one of the fp32 value only where h lies within
     2^-16 of an e4m3 rounding boundary; from bf16 values (2^-9) a few percent
     of the codes move, each then a whole e4m3 step away from the oracle's
-    (R-14 quantises the fp32 h).  SwiGLU-shaped rows; the oracle's e4m3 and
-    bf16 rounding only."""
+    (the oracle quantises the fp32 h).  SwiGLU-shaped rows; the oracle's e4m3
+    and bf16 rounding only."""
     rng = np.random.default_rng(5)
     a = rng.standard_normal((64, 8192))
     b = rng.standard_normal((64, 8192))
